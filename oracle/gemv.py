@@ -1,0 +1,88 @@
+"""The GEMV the fused kernels must reproduce, by its plain definition.
+
+TEST INFRASTRUCTURE ONLY (see ``oracle/__init__.py``).
+
+hipEngine 0.3.0, "Core principles": every fused composite has an unfused chain
+that is the correctness baseline.  Here the unfused chain is: dequantize every
+weight exactly (``dequant64``), convert the activations exactly to float64,
+and take the float64 product  y64[b, r] = sum_k W[r, k] * x[b, k].
+
+x is [batch, cols] and y is [batch, rows], the layout of the C ABI.
+
+Tolerance definitions (the GPU accumulates in float32, so its sums are not
+unique; only these bounds are):
+
+* normwise relative error per batch row b:
+      max_r |y[b, r] - y64[b, r]| / max_r |y64[b, r]|
+  gated at 2e-3 for the GEMVs.
+* elementwise a-priori bound, valid for any float32 summation order when the
+  weights and activations enter exactly:
+      |y - y64| <= gamma_{K+1} * sum_k |W[r, k] x[b, k]|,
+      gamma_n = n u / (1 - n u),  u = 2^-24
+  (Higham, "Accuracy and Stability of Numerical Algorithms", section 3.1).
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from .formats import dequant64, row_slice
+from .fp import bf16_bits_to_f64, fp16_bits_to_f64
+
+
+def x_to_f64(x, x_dtype: str) -> np.ndarray:
+    """Exact float64 value of activations given as f32 / f16 arrays or bf16 bits."""
+    x = np.asarray(x)
+    if x_dtype == "f32":
+        if x.dtype != np.float32:
+            raise TypeError("f32 activations must be float32")
+        return x.astype(np.float64)
+    if x_dtype == "f16":
+        if x.dtype != np.float16:
+            raise TypeError("f16 activations must be float16")
+        return fp16_bits_to_f64(x.view(np.uint16))
+    if x_dtype == "bf16":
+        if x.dtype != np.uint16:
+            raise TypeError("bf16 activations are passed as uint16 bit patterns")
+        return bf16_bits_to_f64(x)
+    raise ValueError(f"unknown activation dtype {x_dtype!r}")
+
+
+def gemv64(fmt: str, data, rows: int, cols: int, x, x_dtype: str,
+           row_chunk: int = 4096) -> np.ndarray:
+    """y64 = x64 @ W64^T, float64 [batch, rows]; W decoded in row chunks."""
+    x64 = x_to_f64(x, x_dtype).reshape(-1, cols)
+    y = np.empty((x64.shape[0], rows), np.float64)
+    for r0 in range(0, rows, row_chunk):
+        r1 = min(rows, r0 + row_chunk)
+        w = dequant64(fmt, row_slice(fmt, data, rows, cols, r0, r1), r1 - r0, cols)
+        y[:, r0:r1] = x64 @ w.T
+    return y
+
+
+def gemv64_rows(fmt: str, data, rows: int, cols: int, x, x_dtype: str,
+                row_ids) -> np.ndarray:
+    """y64 restricted to the given rows: float64 [batch, len(row_ids)]."""
+    x64 = x_to_f64(x, x_dtype).reshape(-1, cols)
+    ids = np.asarray(row_ids, np.int64)
+    w = np.stack([dequant64(fmt, row_slice(fmt, data, rows, cols, int(r), int(r) + 1), 1, cols)[0]
+                  for r in ids])
+    return x64 @ w.T
+
+
+def normwise_rel_err(y, y64) -> np.ndarray:
+    """Per batch row: max_r |y - y64| / max_r |y64| (float64)."""
+    y = np.asarray(y, np.float64).reshape(np.shape(y64))
+    y64 = np.asarray(y64, np.float64)
+    num = np.max(np.abs(y - y64), axis=-1)
+    den = np.max(np.abs(y64), axis=-1)
+    return num / np.where(den == 0, 1.0, den)
+
+
+def elementwise_bound(fmt: str, data, rows: int, cols: int, x, x_dtype: str) -> np.ndarray:
+    """gamma_{K+1} * |W| |x|, float64 [batch, rows]."""
+    u = 2.0 ** -24
+    n = cols + 1
+    gamma = n * u / (1 - n * u)
+    x64 = np.abs(x_to_f64(x, x_dtype).reshape(-1, cols))
+    w = np.abs(dequant64(fmt, data, rows, cols))
+    return gamma * (x64 @ w.T)

@@ -1,0 +1,265 @@
+"""Pins that tie the CPU oracle to facts outside itself.
+
+Each ``pin_*`` function raises (AssertionError or another exception) when the
+oracle disagrees with:
+
+* the hand-computed golden blocks in tests/golden/ (layout readings of the VTE
+  feature list and of the INT4 group-128 description in the datastack.it
+  summary of "annotated-llm-runtime");
+* IEEE-754 decoding of fp16/bf16 (checked over every finite bit pattern against
+  numpy's own float16 / float32 types);
+* closed forms: float32 dequantization is the exact value rounded once and does
+  not depend on the order of the products; x = e_k extracts column k exactly;
+* invariants: zero scale -> zero weights, weights affine in the code with slope
+  d*sc, the zero point of each format;
+* brute force: the float64 GEMV against an exact rational sum;
+* the byte counts of the decode workloads (34, 144 and 210 bytes per block).
+
+They are plain functions so tests/test_oracle_mutants.py can run them against
+an oracle with a planted mistake and check that some pin catches it.
+"""
+from fractions import Fraction
+
+import numpy as np
+
+import oracle
+from golden_io import all_names, load
+from synth import gen_weights, gen_x, rng
+
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+
+
+# -- encodings ----------------------------------------------------------------
+def pin_fp16_decode():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 10) & 0x1F) != 0x1F
+    got = oracle.fp16_bits_to_f64(bits[finite])
+    ref = bits[finite].view(np.float16).astype(np.float64)
+    assert np.array_equal(got, ref)
+    assert np.array_equal(np.signbit(got), np.signbit(ref))
+    # a few values fixed by the binary16 definition itself
+    table = {0x3C00: 1.0, 0x3800: 0.5, 0x0001: 2.0 ** -24, 0x03FF: 1023 * 2.0 ** -24,
+             0x0400: 2.0 ** -14, 0x7BFF: 65504.0, 0xC000: -2.0, 0x3555: 0.333251953125}
+    for b, v in table.items():
+        assert oracle.fp16_bits_to_f64(np.uint16(b)) == v
+
+
+def pin_bf16_decode():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    got = oracle.bf16_bits_to_f64(bits[finite])
+    ref = (bits[finite].astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    assert np.array_equal(got, ref)
+    assert oracle.bf16_bits_to_f64(np.uint16(0x3F80)) == 1.0
+    assert oracle.bf16_bits_to_f64(np.uint16(0x0001)) == 2.0 ** -133
+
+
+def pin_bf16_rne():
+    g = rng(7)
+    x = g.standard_normal(20000).astype(np.float32)
+    # exact ties: low half 0x8000 with even and odd kept bits
+    tie_bits = (g.integers(0, 1 << 15, 2000).astype(np.uint32) << 16) | 0x8000
+    x = np.concatenate([x, tie_bits.view(np.float32)[np.isfinite(tie_bits.view(np.float32))]])
+    got = oracle.f32_to_bf16_bits_rne(x).astype(np.uint32)
+    u = x.view(np.uint32)
+    lo = u >> 16                                   # truncation toward zero (magnitude)
+    hi = lo + 1
+    xv = x.astype(np.float64)
+    vlo = (lo << 16).view(np.float32).astype(np.float64)
+    vhi = (hi << 16).view(np.float32).astype(np.float64)
+    dlo, dhi = np.abs(xv - vlo), np.abs(vhi - xv)
+    want = np.where(dlo < dhi, lo, np.where(dhi < dlo, hi, np.where(lo % 2 == 0, lo, hi)))
+    assert np.array_equal(got, want)
+
+
+# -- golden blocks ------------------------------------------------------------
+def pin_golden(name):
+    g = load(name)
+    fmt, rows, cols = g["fmt"], g["rows"], g["cols"]
+    assert g["data"].size == oracle.packed_size(fmt, rows, cols), name
+    w = oracle.dequant64(fmt, g["data"], rows, cols)
+    bad = np.argwhere(w != g["w"])
+    assert bad.size == 0, f"{name}: first mismatch at {bad[:4].tolist()}"
+    ones = np.ones((1, cols), np.float32)
+    y = oracle.gemv64(fmt, g["data"], rows, cols, ones, "f32")
+    for r, v in g["row_sums"]:
+        assert y[0, r] == v, f"{name}: row {r} sum {y[0, r]} != {v}"
+    # re-packing the decoded fields must give back the same bytes
+    f = oracle.unpack(fmt, g["data"], rows, cols)
+    assert np.array_equal(oracle.pack(fmt, f, rows, cols), g["data"]), name
+
+
+def pin_packed_sizes():
+    # bytes per block quoted with the decode workloads: Q8_0 34 B, Q4_K 144 B, Q6_K 210 B
+    assert oracle.packed_size("q8_0", 1, 32) == 34
+    assert oracle.packed_size("q4_k", 1, 256) == 144
+    assert oracle.packed_size("q6_k", 1, 256) == 210
+    assert oracle.packed_size("int4_g128", 1, 128) == 64 + 2
+    assert oracle.packed_size("q8_0", 1536, 1536) == 2_506_752
+    assert oracle.packed_size("q4_k", 18944, 3584) == 38_191_104
+    assert oracle.packed_size("q4_k", 3584, 18944) == 38_191_104
+    assert oracle.packed_size("q6_k", 152064, 3584) == 447_068_160
+    assert oracle.packed_size("int4_g128", 18944, 3584) == 35_008_512
+
+
+# -- helpers to build fields with chosen scales --------------------------------
+def _fields(fmt, rows, cols, seed, scale_bits=None):
+    f = gen_weights(fmt, rows, cols, seed)
+    if scale_bits is not None:
+        key = "s_bits" if fmt == "int4_g128" else "d_bits"
+        f[key] = np.broadcast_to(np.asarray(scale_bits, np.uint16), f[key].shape).copy()
+        if fmt == "q4_k":
+            f["dmin_bits"] = f[key][:, ::-1].copy()
+    return f
+
+
+def _scale64(fmt, f):
+    key = "s_bits" if fmt == "int4_g128" else "d_bits"
+    return oracle.fp16_bits_to_f64(f[key])
+
+
+EXTREME_SCALES = [0x0001, 0x03FF, 0x0400, 0x3C00, 0x7BFF, 0xBC00, 0x8001, 0x1234]
+
+
+def pin_roundtrip(fmt):
+    rows, cols = 3, 2 * oracle.QK[fmt]
+    for seed in range(3):
+        f = _fields(fmt, rows, cols, 50 + seed)
+        data = oracle.pack(fmt, f, rows, cols)
+        back = oracle.unpack(fmt, data, rows, cols)
+        for k, v in f.items():
+            assert np.array_equal(np.asarray(back[k]).reshape(np.shape(v)), v), (fmt, k)
+    # extreme codes
+    f = _fields(fmt, rows, cols, 9)
+    lo_hi = {"q8_0": ("q", -128, 127), "q4_k": ("u", 0, 15), "q6_k": ("q", 0, 63),
+             "int4_g128": ("q", -8, 7)}[fmt]
+    key, lo, hi = lo_hi
+    f[key][:, ::2] = lo
+    f[key][:, 1::2] = hi
+    if fmt == "q4_k":
+        f["sc"][...] = 63
+        f["m"][:, :, ::2] = 0
+    back = oracle.unpack(fmt, oracle.pack(fmt, f, rows, cols), rows, cols)
+    for k, v in f.items():
+        assert np.array_equal(np.asarray(back[k]).reshape(np.shape(v)), v), (fmt, k)
+
+
+def pin_single_rounding(fmt):
+    """float32 dequant = exact value rounded once, whatever the product order."""
+    rows, cols = 4, 2 * oracle.QK[fmt]
+    for i, sb in enumerate([None] + EXTREME_SCALES):
+        f = _fields(fmt, rows, cols, 100 + i, sb)
+        data = oracle.pack(fmt, f, rows, cols)
+        w64 = oracle.dequant64(fmt, data, rows, cols)
+        w32 = oracle.dequant32(fmt, data, rows, cols)
+        assert np.array_equal(w32, w64.astype(np.float32))
+        if fmt != "q4_k":
+            assert np.array_equal(w32.astype(np.float64), w64), "product must be exact in float32"
+            continue
+        # Q4_K: the two products are exact in float32, so any order gives the same result.
+        nb = cols // 256
+        d = oracle.fp16_bits_to_f64(f["d_bits"]).astype(np.float32)[:, :, None, None]
+        dm = oracle.fp16_bits_to_f64(f["dmin_bits"]).astype(np.float32)[:, :, None, None]
+        sc = f["sc"].astype(np.float32)[:, :, :, None]
+        m = f["m"].astype(np.float32)[:, :, :, None]
+        u = f["u"].astype(np.float32).reshape(rows, nb, 8, 32)
+        order1 = (d * sc) * u - dm * m
+        order2 = d * (sc * u) - m * dm
+        assert np.array_equal(order1.reshape(rows, cols), w32)
+        assert np.array_equal(order2.reshape(rows, cols), w32)
+
+
+def pin_zero_scale(fmt):
+    rows, cols = 2, 2 * oracle.QK[fmt]
+    f = _fields(fmt, rows, cols, 200, 0x0000)
+    if fmt == "q4_k":
+        f["dmin_bits"][...] = 0
+    w = oracle.dequant64(fmt, oracle.pack(fmt, f, rows, cols), rows, cols)
+    assert np.all(w == 0)
+    if fmt == "q4_k":  # d = 0 leaves only the min term
+        f["dmin_bits"][...] = 0x3C00
+        w = oracle.dequant64(fmt, oracle.pack(fmt, f, rows, cols), rows, cols)
+        want = -np.repeat(f["m"].astype(np.float64).reshape(rows, -1), 32, axis=1)
+        assert np.array_equal(w, want)
+
+
+def pin_affine_in_code(fmt):
+    """All codes equal to c: w(c+1) - w(c) = d*sc exactly; the format's zero point gives 0."""
+    rows, cols = 2, oracle.QK[fmt]
+    f = _fields(fmt, rows, cols, 300)
+    key = {"q8_0": "q", "q4_k": "u", "q6_k": "q", "int4_g128": "q"}[fmt]
+    rng_c = {"q8_0": range(-128, 127), "q4_k": range(0, 15), "q6_k": range(0, 63),
+             "int4_g128": range(-8, 7)}[fmt]
+    zero = {"q8_0": 0, "q6_k": 32, "int4_g128": 0}
+    prev = None
+    d = _scale64(fmt, f)[:, 0]
+    if fmt == "q4_k":
+        slope = np.repeat(d[:, None] * f["sc"][:, 0, :].astype(np.float64), 32, axis=1)
+    elif fmt == "q6_k":
+        slope = np.repeat(d[:, None] * f["sc"][:, 0, :].astype(np.float64), 16, axis=1)
+    else:
+        slope = np.repeat(d[:, None], cols, axis=1)
+    for c in rng_c:
+        f[key][...] = c
+        w = oracle.dequant64(fmt, oracle.pack(fmt, f, rows, cols), rows, cols)
+        if prev is not None:
+            assert np.array_equal(w - prev, slope), (fmt, c)
+        if fmt in zero and c == zero[fmt]:
+            assert np.all(w == 0), (fmt, c)
+        if fmt == "q4_k" and c == 0:
+            dmin = oracle.fp16_bits_to_f64(f["dmin_bits"])[:, 0]
+            want = -np.repeat(dmin[:, None] * f["m"][:, 0, :].astype(np.float64), 32, axis=1)
+            assert np.array_equal(w, want)
+        prev = w
+
+
+def pin_gemv_bruteforce(fmt):
+    """Tiny non-square GEMVs: float64 result vs exact rational sum; x = e_k -> column k."""
+    for rows, nblk, batch in [(3, 1, 1), (5, 2, 2), (8, 1, 3)]:
+        cols = nblk * oracle.QK[fmt]
+        f = _fields(fmt, rows, cols, 400 + rows)
+        data = oracle.pack(fmt, f, rows, cols)
+        for xd in ("f32", "f16", "bf16"):
+            x = gen_x(batch, cols, xd, 500 + rows)
+            y = oracle.gemv64(fmt, data, rows, cols, x, xd)
+            assert y.shape == (batch, rows)
+            w = oracle.dequant64(fmt, data, rows, cols)
+            x64 = oracle.x_to_f64(x, xd)
+            for b in range(batch):
+                for r in range(rows):
+                    exact = sum(Fraction(float(w[r, k])) * Fraction(float(x64[b, k]))
+                                for k in range(cols))
+                    assert abs(Fraction(float(y[b, r])) - exact) <= abs(exact) * Fraction(1, 10 ** 13) + Fraction(1, 10 ** 300)
+        w = oracle.dequant64(fmt, data, rows, cols)
+        for k in (0, cols // 2 + 1, cols - 1):
+            e = np.zeros((1, cols), np.float32)
+            e[0, k] = 1.0
+            y = oracle.gemv64(fmt, data, rows, cols, e, "f32")
+            assert np.array_equal(y[0], w[:, k])
+        # sampled-row path equals the full path (up to float64 summation order)
+        ids = [rows - 1, 0]
+        x = gen_x(2, cols, "f32", 9)
+        assert np.allclose(oracle.gemv64_rows(fmt, data, rows, cols, x, "f32", ids),
+                           oracle.gemv64(fmt, data, rows, cols, x, "f32")[:, ids],
+                           rtol=1e-13, atol=0)
+
+
+ALL_PINS = (
+    [("fp16_decode", pin_fp16_decode, ()), ("bf16_decode", pin_bf16_decode, ()),
+     ("bf16_rne", pin_bf16_rne, ()), ("packed_sizes", pin_packed_sizes, ())]
+    + [(f"golden[{n}]", pin_golden, (n,)) for n in all_names()]
+    + [(f"{p.__name__[4:]}[{fmt}]", p, (fmt,)) for fmt in FMTS
+       for p in (pin_roundtrip, pin_single_rounding, pin_zero_scale, pin_affine_in_code,
+                 pin_gemv_bruteforce)]
+)
+
+
+def failing_pins():
+    """Names of the pins that fail against the oracle as currently loaded."""
+    bad = []
+    for name, fn, args in ALL_PINS:
+        try:
+            fn(*args)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            bad.append(name)
+    return bad
