@@ -1,0 +1,206 @@
+// C ABI of libqmv: argument validation, status codes and kernel dispatch.
+//
+// Validation happens before any HIP call, so every error code except
+// QMV_ERR_HIP can be produced and tested on a machine without a GPU.
+// Unsupported combinations are refused, never routed to another path
+// (hipEngine 0.3.0, "Quickstart": unsupported registry combinations fail
+// rather than fall back; hipfire, "Implementation requirements for
+// multi-weight Q8 WMMA dispatch": check dtypes and that K is a whole number
+// of blocks so no kernel silently drops a tail).
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <hip/hip_runtime.h>
+
+#include "api_internal.h"
+#include "launch.h"
+
+namespace qmv {
+
+static thread_local char g_last_error[512];
+
+int32_t fail(int32_t status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int32_t ok() {
+  g_last_error[0] = '\0';
+  return QMV_OK;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static int32_t from_hip(hipError_t e, const char* what) {
+  if (e == hipSuccess) return ok();
+  return fail(QMV_ERR_HIP, "%s: %s (%d)", what, hipGetErrorString(e), static_cast<int>(e));
+}
+
+// Largest cols a single GEMV launch supports: 16 waves along K.
+static int64_t gemv_max_cols(int32_t fmt) {
+  switch (fmt) {
+    case QMV_Q8_0: return 16 * 64 * 32;
+    case QMV_Q4_K: return 16 * 16 * 256;
+    case QMV_Q6_K: return 16 * 16 * 256;
+    case QMV_INT4_G128: return 16 * 64 * 64;
+    default: return 0;
+  }
+}
+
+static int32_t check_weights(const qmv_weights* W) {
+  if (!W) return fail(QMV_ERR_NULL, "weights descriptor is NULL");
+  if (!W->data) return fail(QMV_ERR_NULL, "weights data pointer is NULL");
+  if (qmv_block_size(W->fmt) == 0) return fail(QMV_ERR_FORMAT, "unknown format %d", W->fmt);
+  const uint64_t need = qmv_packed_size(W->fmt, W->rows, W->cols);
+  if (need == 0)
+    return fail(QMV_ERR_SHAPE, "bad weight shape %lld x %lld for format %d", (long long)W->rows,
+                (long long)W->cols, W->fmt);
+  if (W->nbytes != need)
+    return fail(QMV_ERR_SIZE, "weights hold %llu bytes, format needs %llu",
+                (unsigned long long)W->nbytes, (unsigned long long)need);
+  const uint64_t soff = W->fmt == QMV_INT4_G128 ? static_cast<uint64_t>(W->rows * W->cols / 2) : 0;
+  if (W->scales_offset != soff)
+    return fail(QMV_ERR_FORMAT, "scales_offset %llu, expected %llu",
+                (unsigned long long)W->scales_offset, (unsigned long long)soff);
+  if (!aligned16(W->data)) return fail(QMV_ERR_ALIGN, "weights data not 16-byte aligned");
+  if (W->rows > INT32_MAX || W->cols > INT32_MAX || W->rows * W->cols > (int64_t{1} << 40))
+    return fail(QMV_ERR_UNSUPPORTED, "weight tensor too large");
+  return QMV_OK;
+}
+
+}  // namespace qmv
+
+using qmv::fail;
+
+extern "C" {
+
+int32_t qmv_block_size(int32_t fmt) {
+  switch (fmt) {
+    case QMV_Q8_0: return 32;
+    case QMV_Q4_K: return 256;
+    case QMV_Q6_K: return 256;
+    case QMV_INT4_G128: return 128;
+    default: return 0;
+  }
+}
+
+uint64_t qmv_packed_size(int32_t fmt, int64_t rows, int64_t cols) {
+  const int32_t qk = qmv_block_size(fmt);
+  if (qk == 0 || rows < 1 || cols < 1 || cols % qk != 0) return 0;
+  if (rows > (int64_t{1} << 40) / cols) return 0;
+  const uint64_t nblk = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / qk);
+  switch (fmt) {
+    case QMV_Q8_0: return nblk * 34;
+    case QMV_Q4_K: return nblk * 144;
+    case QMV_Q6_K: return nblk * 210;
+    default: return static_cast<uint64_t>(rows) * cols / 2 + nblk * 2;
+  }
+}
+
+int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols, const void* dev_packed,
+                           uint64_t nbytes, qmv_weights* out) {
+  if (!out) return fail(QMV_ERR_NULL, "output descriptor is NULL");
+  if (!dev_packed) return fail(QMV_ERR_NULL, "packed data pointer is NULL");
+  if (qmv_block_size(fmt) == 0) return fail(QMV_ERR_FORMAT, "unknown format %d", fmt);
+  const uint64_t need = qmv_packed_size(fmt, rows, cols);
+  if (need == 0)
+    return fail(QMV_ERR_SHAPE, "bad shape %lld x %lld (cols must be a positive multiple of %d)",
+                (long long)rows, (long long)cols, qmv_block_size(fmt));
+  if (nbytes != need)
+    return fail(QMV_ERR_SIZE, "got %llu bytes, format needs %llu", (unsigned long long)nbytes,
+                (unsigned long long)need);
+  if ((reinterpret_cast<uintptr_t>(dev_packed) & 15u) != 0)
+    return fail(QMV_ERR_ALIGN, "packed data not 16-byte aligned");
+  qmv_weights w;
+  w.fmt = fmt;
+  w.reserved = 0;
+  w.rows = rows;
+  w.cols = cols;
+  w.data = dev_packed;
+  w.nbytes = nbytes;
+  w.scales_offset = fmt == QMV_INT4_G128 ? static_cast<uint64_t>(rows * cols / 2) : 0;
+  *out = w;
+  return qmv::ok();
+}
+
+int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x, int32_t x_dtype, float* y,
+                 int64_t rows, int64_t cols, int64_t batch, void* stream) {
+  int32_t st = qmv::check_weights(W);
+  if (st != QMV_OK) return st;
+  if (!x || !y) return fail(QMV_ERR_NULL, "x or y is NULL");
+  if (fmt != W->fmt || rows != W->rows || cols != W->cols)
+    return fail(QMV_ERR_FORMAT, "call (fmt %d, %lld x %lld) disagrees with weights (fmt %d, %lld x %lld)",
+                fmt, (long long)rows, (long long)cols, W->fmt, (long long)W->rows,
+                (long long)W->cols);
+  if (batch < 1) return fail(QMV_ERR_SHAPE, "batch %lld < 1", (long long)batch);
+  if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16)
+    return fail(QMV_ERR_UNSUPPORTED, "activation dtype %d", x_dtype);
+  if (!qmv::aligned16(x) || !qmv::aligned16(y))
+    return fail(QMV_ERR_ALIGN, "x or y not 16-byte aligned");
+  if (batch > qmv::kMaxBatch)
+    return fail(QMV_ERR_UNSUPPORTED, "batch %lld above %lld", (long long)batch,
+                (long long)qmv::kMaxBatch);
+  if (cols > qmv::gemv_max_cols(fmt))
+    return fail(QMV_ERR_UNSUPPORTED, "cols %lld above the GEMV limit %lld for format %d",
+                (long long)cols, (long long)qmv::gemv_max_cols(fmt), fmt);
+  qmv::GemvArgs a{W, x, x_dtype, y, batch, static_cast<hipStream_t>(stream)};
+  hipError_t e;
+  switch (fmt) {
+    case QMV_Q8_0: e = qmv::gemv_q8_0(a); break;
+    case QMV_Q4_K: e = qmv::gemv_q4_k(a); break;
+    case QMV_Q6_K: e = qmv::gemv_q6_k(a); break;
+    default: e = qmv::gemv_int4_g128(a); break;
+  }
+  return qmv::from_hip(e, "qmv_gemv launch");
+}
+
+int32_t qmv_dequant(const qmv_weights* W, void* out, int32_t out_dtype, void* stream) {
+  int32_t st = qmv::check_weights(W);
+  if (st != QMV_OK) return st;
+  if (!out) return fail(QMV_ERR_NULL, "output is NULL");
+  if (out_dtype != QMV_F32 && out_dtype != QMV_F16 && out_dtype != QMV_BF16)
+    return fail(QMV_ERR_UNSUPPORTED, "output dtype %d", out_dtype);
+  if (!qmv::aligned16(out)) return fail(QMV_ERR_ALIGN, "output not 16-byte aligned");
+  return qmv::from_hip(qmv::dequant(*W, out, out_dtype, static_cast<hipStream_t>(stream)),
+                       "qmv_dequant launch");
+}
+
+int64_t qmv_probe_read_outputs(uint64_t nbytes) { return qmv::probe_read_blocks(nbytes); }
+
+int32_t qmv_probe_read(const void* src, uint64_t nbytes, float* out, void* stream) {
+  if (!src || !out) return fail(QMV_ERR_NULL, "probe: NULL pointer");
+  if (nbytes % 16 != 0) return fail(QMV_ERR_SIZE, "probe: nbytes not a multiple of 16");
+  if (!qmv::aligned16(src) || !qmv::aligned16(out)) return fail(QMV_ERR_ALIGN, "probe: misaligned");
+  return qmv::from_hip(qmv::probe_read(src, nbytes, out, static_cast<hipStream_t>(stream)),
+                       "qmv_probe_read launch");
+}
+
+int32_t qmv_probe_copy(const void* src, void* dst, uint64_t nbytes, void* stream) {
+  if (!src || !dst) return fail(QMV_ERR_NULL, "probe: NULL pointer");
+  if (nbytes % 16 != 0) return fail(QMV_ERR_SIZE, "probe: nbytes not a multiple of 16");
+  if (!qmv::aligned16(src) || !qmv::aligned16(dst)) return fail(QMV_ERR_ALIGN, "probe: misaligned");
+  return qmv::from_hip(qmv::probe_copy(src, dst, nbytes, static_cast<hipStream_t>(stream)),
+                       "qmv_probe_copy launch");
+}
+
+const char* qmv_status_string(int32_t status) {
+  switch (status) {
+    case QMV_OK: return "ok";
+    case QMV_ERR_NULL: return "null pointer";
+    case QMV_ERR_FORMAT: return "format or descriptor mismatch";
+    case QMV_ERR_SHAPE: return "bad shape";
+    case QMV_ERR_ALIGN: return "pointer not 16-byte aligned";
+    case QMV_ERR_SIZE: return "byte count mismatch";
+    case QMV_ERR_UNSUPPORTED: return "unsupported combination";
+    case QMV_ERR_RANGE: return "value out of range";
+    case QMV_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* qmv_last_error(void) { return qmv::g_last_error; }
+
+}  // extern "C"

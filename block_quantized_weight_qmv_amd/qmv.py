@@ -1,0 +1,223 @@
+"""Python binding of libqmv.so: the C ABI of include/qmv.h, one function per entry point.
+
+Argument marshalling only.  Device buffers are torch tensors (or raw integer
+device pointers); every computation runs in the library's HIP kernels.  If the
+library is not built, the first call raises: there is no fallback path.
+
+torch is imported before the library is loaded so that libqmv.so binds to the
+HIP runtime torch already mapped (both use the soname libamdhip64.so.7), which
+makes torch's hipStream_t values valid inside the library.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libqmv.so")
+
+FMT = {"q8_0": 1, "q4_k": 2, "q6_k": 3, "int4_g128": 4}
+DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
+
+QMV_OK = 0
+STATUS = {0: "QMV_OK", -1: "QMV_ERR_NULL", -2: "QMV_ERR_FORMAT", -3: "QMV_ERR_SHAPE",
+          -4: "QMV_ERR_ALIGN", -5: "QMV_ERR_SIZE", -6: "QMV_ERR_UNSUPPORTED",
+          -7: "QMV_ERR_RANGE", -8: "QMV_ERR_HIP"}
+
+
+class QmvError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        super().__init__(f"{STATUS.get(status, status)}: {detail}")
+
+
+class QmvWeights(ctypes.Structure):
+    """Mirror of struct qmv_weights."""
+    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+                ("data", ctypes.c_void_p), ("nbytes", ctypes.c_uint64),
+                ("scales_offset", ctypes.c_uint64)]
+
+
+_lib = None
+
+_i32, _i64, _u64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
+_SIGS = {
+    "qmv_block_size": (_i32, [_i32]),
+    "qmv_packed_size": (_u64, [_i32, _i64, _i64]),
+    "qmv_pack_q8_0": (_i32, [_p, _p, _i64, _i64, _p, _u64]),
+    "qmv_pack_q4_k": (_i32, [_p, _p, _p, _p, _p, _i64, _i64, _p, _u64]),
+    "qmv_pack_q6_k": (_i32, [_p, _p, _p, _i64, _i64, _p, _u64]),
+    "qmv_pack_int4_g128": (_i32, [_p, _p, _i64, _i64, _p, _u64]),
+    "qmv_create_weights": (_i32, [_i32, _i64, _i64, _p, _u64, ctypes.POINTER(QmvWeights)]),
+    "qmv_gemv": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
+    "qmv_dequant": (_i32, [ctypes.POINTER(QmvWeights), _p, _i32, _p]),
+    "qmv_probe_read_outputs": (_i64, [_u64]),
+    "qmv_probe_read": (_i32, [_p, _u64, _p, _p]),
+    "qmv_probe_copy": (_i32, [_p, _p, _u64, _p]),
+    "qmv_status_string": (ctypes.c_char_p, [_i32]),
+    "qmv_last_error": (ctypes.c_char_p, []),
+}
+EXPORTED = tuple(_SIGS)
+
+
+def lib() -> ctypes.CDLL:
+    """Load libqmv.so (once).  Raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m block_quantized_weight_qmv_amd.build`")
+        try:
+            import torch  # noqa: F401  (maps torch's HIP runtime first)
+        except ImportError:
+            pass
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(status: int) -> None:
+    if status != QMV_OK:
+        raise QmvError(status, (lib().qmv_last_error() or b"").decode())
+
+
+def _ptr(a):
+    """Device or host address of a torch tensor, numpy array, int or None."""
+    if a is None:
+        return None
+    if isinstance(a, int):
+        return a
+    if isinstance(a, np.ndarray):
+        return a.ctypes.data
+    return a.data_ptr()
+
+
+def _stream(stream, *tensors):
+    if stream is not None:
+        return stream if isinstance(stream, int) else stream.cuda_stream
+    for t in tensors:
+        if hasattr(t, "is_cuda") and t.is_cuda:
+            import torch
+            return torch.cuda.current_stream(t.device).cuda_stream
+    return None
+
+
+def _fmt(fmt) -> int:
+    return FMT[fmt] if isinstance(fmt, str) else int(fmt)
+
+
+def _dtype(dt) -> int:
+    if isinstance(dt, str):
+        return DTYPE[dt]
+    if isinstance(dt, int):
+        return dt
+    import torch
+    return {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2}[dt]
+
+
+# -- entry points -------------------------------------------------------------
+def qmv_block_size(fmt) -> int:
+    return lib().qmv_block_size(_fmt(fmt))
+
+
+def qmv_packed_size(fmt, rows: int, cols: int) -> int:
+    return lib().qmv_packed_size(_fmt(fmt), rows, cols)
+
+
+def _pack_out(fmt, rows, cols):
+    n = qmv_packed_size(fmt, rows, cols)
+    if n == 0:
+        raise QmvError(-3, f"bad shape {rows}x{cols} for {fmt}")
+    return np.empty(n, np.uint8)
+
+
+def _c(a, dtype):
+    return np.ascontiguousarray(a, dtype=dtype)
+
+
+def qmv_pack_q8_0(d_bits, q, rows: int, cols: int) -> np.ndarray:
+    d, qq, out = _c(d_bits, np.uint16), _c(q, np.int8), _pack_out("q8_0", rows, cols)
+    _check(lib().qmv_pack_q8_0(_ptr(d), _ptr(qq), rows, cols, _ptr(out), out.size))
+    return out
+
+
+def qmv_pack_q4_k(d_bits, dmin_bits, sc6, m6, q4, rows: int, cols: int) -> np.ndarray:
+    d, dm = _c(d_bits, np.uint16), _c(dmin_bits, np.uint16)
+    sc, m, q = _c(sc6, np.uint8), _c(m6, np.uint8), _c(q4, np.uint8)
+    out = _pack_out("q4_k", rows, cols)
+    _check(lib().qmv_pack_q4_k(_ptr(d), _ptr(dm), _ptr(sc), _ptr(m), _ptr(q), rows, cols,
+                               _ptr(out), out.size))
+    return out
+
+
+def qmv_pack_q6_k(d_bits, sc8, q6, rows: int, cols: int) -> np.ndarray:
+    d, sc, q = _c(d_bits, np.uint16), _c(sc8, np.int8), _c(q6, np.uint8)
+    out = _pack_out("q6_k", rows, cols)
+    _check(lib().qmv_pack_q6_k(_ptr(d), _ptr(sc), _ptr(q), rows, cols, _ptr(out), out.size))
+    return out
+
+
+def qmv_pack_int4_g128(s_bits, q, rows: int, cols: int) -> np.ndarray:
+    s, qq, out = _c(s_bits, np.uint16), _c(q, np.int8), _pack_out("int4_g128", rows, cols)
+    _check(lib().qmv_pack_int4_g128(_ptr(s), _ptr(qq), rows, cols, _ptr(out), out.size))
+    return out
+
+
+def pack_fields(fmt: str, fields: dict, rows: int, cols: int) -> np.ndarray:
+    """Call the packer of `fmt` with the field arrays named as in synth/."""
+    if fmt == "q8_0":
+        return qmv_pack_q8_0(fields["d_bits"], fields["q"], rows, cols)
+    if fmt == "q4_k":
+        return qmv_pack_q4_k(fields["d_bits"], fields["dmin_bits"], fields["sc"], fields["m"],
+                             fields["u"], rows, cols)
+    if fmt == "q6_k":
+        return qmv_pack_q6_k(fields["d_bits"], fields["sc"], fields["q"], rows, cols)
+    if fmt == "int4_g128":
+        return qmv_pack_int4_g128(fields["s_bits"], fields["q"], rows, cols)
+    raise ValueError(fmt)
+
+
+def qmv_create_weights(fmt, rows: int, cols: int, dev_packed, nbytes: int | None = None) -> QmvWeights:
+    """Descriptor for packed bytes already in device memory (a uint8 tensor or a pointer)."""
+    if nbytes is None:
+        nbytes = dev_packed.numel() * dev_packed.element_size()
+    w = QmvWeights()
+    _check(lib().qmv_create_weights(_fmt(fmt), rows, cols, _ptr(dev_packed), nbytes, ctypes.byref(w)))
+    return w
+
+
+def qmv_gemv(fmt, W: QmvWeights, x, x_dtype, y, rows: int, cols: int, batch: int,
+             stream=None) -> None:
+    _check(lib().qmv_gemv(_fmt(fmt), ctypes.byref(W), _ptr(x), _dtype(x_dtype), _ptr(y),
+                          rows, cols, batch, _stream(stream, x, y)))
+
+
+def qmv_dequant(W: QmvWeights, out, out_dtype, stream=None) -> None:
+    _check(lib().qmv_dequant(ctypes.byref(W), _ptr(out), _dtype(out_dtype), _stream(stream, out)))
+
+
+def qmv_probe_read_outputs(nbytes: int) -> int:
+    return lib().qmv_probe_read_outputs(nbytes)
+
+
+def qmv_probe_read(src, nbytes: int, out, stream=None) -> None:
+    _check(lib().qmv_probe_read(_ptr(src), nbytes, _ptr(out), _stream(stream, src, out)))
+
+
+def qmv_probe_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check(lib().qmv_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream, src, dst)))
+
+
+def qmv_status_string(status: int) -> str:
+    return lib().qmv_status_string(status).decode()
+
+
+def qmv_last_error() -> str:
+    return (lib().qmv_last_error() or b"").decode()

@@ -1,0 +1,175 @@
+/*
+ * qmv.h -- block-quantized weight dequantize-and-multiply on AMD gfx950.
+ *
+ * C ABI of libqmv.so.  Plain C types only: integers, sizes and pointers.
+ * Device pointers come from the caller (for example torch tensors'
+ * data_ptr()); the library allocates no memory, creates no stream and never
+ * synchronizes.  `stream` arguments are hipStream_t values passed as void*
+ * (NULL = the legacy default stream).
+ *
+ * Operation (what every entry point computes):
+ *   W is a rows x cols matrix stored as blocks of quantized codes plus
+ *   per-block scales, row-major, each row being cols / QK consecutive blocks.
+ *     - VTE (kyuubyn.github.io/VTE), feature list: Q4_K, Q6_K and Q8_0 blocks
+ *       are decoded byte for byte in llama.cpp's reference block layout.
+ *     - "Costruire un runtime di inference LLM da zero" (datastack.it),
+ *       "Tre bug che insegnano": the seven projections of each layer use
+ *       symmetric INT4 weights with one scale per group of 128, multiplied
+ *       against FP16 activations by a dedicated GEMV (an unpack of the 4-bit
+ *       codes feeding FP16 activations beat an INT8-activation dot product).
+ *   Byte maps (all fp16 little-endian IEEE binary16):
+ *     Q8_0 (QK 32, 34 B):  d fp16 | q[32] int8.             w_i = d*q_i
+ *     Q4_K (QK 256, 144 B): d fp16 | dmin fp16 | scales[12] (eight 6-bit
+ *         scales sc_j and mins m_j) | qs[128].  Weight t = 64c+32h+l uses
+ *         nibble h of qs[32c+l] and sub-block s = t/32:
+ *         w_t = d*sc_s*u - dmin*m_s.
+ *         j<4:  sc_j = scales[j]&63, m_j = scales[j+4]&63
+ *         j>=4: sc_j = (scales[j+4]&15) | (scales[j-4]>>6)<<4,
+ *               m_j  = (scales[j+4]>>4) | (scales[j]>>6)<<4
+ *     Q6_K (QK 256, 210 B): ql[128] | qh[64] | sc[16] int8 | d fp16.
+ *         Weight t = 128h+32g+l: low4 = nibble (g>>1) of ql[64h+32(g&1)+l],
+ *         high2 = bits 2g..2g+1 of qh[32h+l], q6 = low4 | high2<<4,
+ *         w_t = d*sc[t/16]*(q6-32).
+ *     INT4_G128 (QK 128): codes plane rows*cols/2 bytes, byte j of a row
+ *         holding u_{2j} (bits 0-3) and u_{2j+1} (bits 4-7), u = q+8; then a
+ *         scales plane of rows*(cols/128) fp16 at scales_offset = rows*cols/2.
+ *         w_k = s_{k/128}*(u_k-8).
+ *   GEMV: y[b][r] = sum_k W[r][k] * x[b][k], x [batch][cols] row-major,
+ *   y [batch][rows] fp32 row-major, overwritten.  Products and sums are
+ *   carried in fp32; activations are converted exactly to fp32 (f16 and
+ *   bf16 are subsets of fp32).
+ *
+ * Errors: every entry point returns a qmv_status.  Argument validation runs
+ * before any HIP call, so it needs no GPU.  After a launch, a failed
+ * hipGetLastError maps to QMV_ERR_HIP; qmv_last_error() then holds the HIP
+ * error text (thread-local).  Faults inside a kernel surface at the caller's
+ * next synchronization, as for any HIP kernel.  The library never prints and
+ * never aborts.
+ */
+#ifndef QMV_H
+#define QMV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  QMV_Q8_0 = 1,
+  QMV_Q4_K = 2,
+  QMV_Q6_K = 3,
+  QMV_INT4_G128 = 4
+};
+
+enum { QMV_F32 = 0, QMV_F16 = 1, QMV_BF16 = 2 };
+
+enum {
+  QMV_OK = 0,
+  QMV_ERR_NULL = -1,        /* a required pointer is NULL                    */
+  QMV_ERR_FORMAT = -2,      /* unknown format, or fmt/rows/cols disagree     */
+                            /* with the weights descriptor                   */
+  QMV_ERR_SHAPE = -3,       /* rows/cols/batch < 1, or cols % QK != 0        */
+  QMV_ERR_ALIGN = -4,       /* a device pointer is not 16-byte aligned       */
+  QMV_ERR_SIZE = -5,        /* a byte count differs from qmv_packed_size or  */
+                            /* an output buffer is too small                 */
+  QMV_ERR_UNSUPPORTED = -6, /* dtype combination not provided                */
+  QMV_ERR_RANGE = -7,       /* packer: a code or scale outside its range     */
+  QMV_ERR_HIP = -8          /* the HIP runtime reported an error             */
+};
+
+/* Descriptor of packed weights resident in device memory.  Plain data,
+ * caller-owned; it only points at the packed bytes, which must stay alive
+ * (and unmodified) until every enqueued call that reads them has finished. */
+typedef struct qmv_weights {
+  int32_t fmt;            /* QMV_Q8_0 .. QMV_INT4_G128                       */
+  int32_t reserved;       /* 0                                               */
+  int64_t rows, cols;     /* logical shape of W                              */
+  const void* data;       /* device pointer to the packed bytes (16 B aligned)*/
+  uint64_t nbytes;        /* == qmv_packed_size(fmt, rows, cols)             */
+  uint64_t scales_offset; /* INT4_G128: byte offset of the scales plane; 0   */
+                          /* for the block formats                           */
+} qmv_weights;
+
+/* Codes per block: 32, 256, 256, 128; 0 for an unknown format. */
+int32_t qmv_block_size(int32_t fmt);
+
+/* Bytes of a packed rows x cols tensor; 0 if fmt is unknown, rows or cols < 1
+ * or cols is not a multiple of the block size. */
+uint64_t qmv_packed_size(int32_t fmt, int64_t rows, int64_t cols);
+
+/* ---- Host block packer (host memory in and out, caller-owned) ----------
+ * Each packer writes the canonical bytes of the layouts above into `out`
+ * (out_bytes must be >= qmv_packed_size).  Codes are given per weight in
+ * natural [rows][cols] order; scales are fp16 bit patterns.  Range errors
+ * (QMV_ERR_RANGE) are detected before anything is written. */
+
+/* Q8_0: d_bits [rows][cols/32], q [rows][cols] (any int8). */
+int32_t qmv_pack_q8_0(const uint16_t* d_bits, const int8_t* q, int64_t rows,
+                      int64_t cols, uint8_t* out, uint64_t out_bytes);
+
+/* Q4_K: d_bits, dmin_bits [rows][cols/256]; sc6, m6 [rows][cols/256][8] each
+ * in 0..63; q4 [rows][cols] in 0..15. */
+int32_t qmv_pack_q4_k(const uint16_t* d_bits, const uint16_t* dmin_bits,
+                      const uint8_t* sc6, const uint8_t* m6, const uint8_t* q4,
+                      int64_t rows, int64_t cols, uint8_t* out,
+                      uint64_t out_bytes);
+
+/* Q6_K: d_bits [rows][cols/256]; sc8 [rows][cols/256][16] (any int8);
+ * q6 [rows][cols] in 0..63. */
+int32_t qmv_pack_q6_k(const uint16_t* d_bits, const int8_t* sc8,
+                      const uint8_t* q6, int64_t rows, int64_t cols,
+                      uint8_t* out, uint64_t out_bytes);
+
+/* INT4_G128: s_bits [rows][cols/128]; q [rows][cols] in -8..7. */
+int32_t qmv_pack_int4_g128(const uint16_t* s_bits, const int8_t* q,
+                           int64_t rows, int64_t cols, uint8_t* out,
+                           uint64_t out_bytes);
+
+/* Validate shape and size and fill *out.  No HIP call, no allocation.
+ * dev_packed must be 16-byte aligned (QMV_ERR_ALIGN) and nbytes must equal
+ * qmv_packed_size (QMV_ERR_SIZE). */
+int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
+                           const void* dev_packed, uint64_t nbytes,
+                           qmv_weights* out);
+
+/* y = W x for `batch` activation rows (the decode GEMV; see top of file).
+ * fmt, rows and cols must repeat the descriptor's (QMV_ERR_FORMAT otherwise),
+ * x is [batch][cols] of x_dtype (QMV_F32, QMV_F16 or QMV_BF16), y is
+ * [batch][rows] fp32; x and y device pointers, 16-byte aligned.  Enqueues on
+ * `stream` and returns; legal inside HIP stream capture.  For Q4_K with bf16
+ * activations and batch >= 64 the call runs the MFMA tile path. */
+int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,
+                 int32_t x_dtype, float* y, int64_t rows, int64_t cols,
+                 int64_t batch, void* stream);
+
+/* out = W as a dense [rows][cols] matrix of out_dtype (QMV_F32: the exact
+ * value rounded once to fp32, bit-exact; QMV_F16 / QMV_BF16: that fp32 value
+ * rounded to nearest-even).  out is a 16-byte aligned device pointer to
+ * rows*cols elements. */
+int32_t qmv_dequant(const qmv_weights* W, void* out, int32_t out_dtype,
+                    void* stream);
+
+/* Measurement kernels for the HBM roofline (not part of the GEMV path).
+ * qmv_probe_read streams nbytes (multiple of 16) from src with 128-bit loads
+ * and writes one fp32 per workgroup to out (out must hold
+ * qmv_probe_read_outputs(nbytes) floats).  qmv_probe_copy copies nbytes
+ * (multiple of 16) from src to dst with 128-bit loads and stores. */
+int64_t qmv_probe_read_outputs(uint64_t nbytes);
+int32_t qmv_probe_read(const void* src, uint64_t nbytes, float* out,
+                       void* stream);
+int32_t qmv_probe_copy(const void* src, void* dst, uint64_t nbytes,
+                       void* stream);
+
+/* Static text for a status code; "unknown status" otherwise. */
+const char* qmv_status_string(int32_t status);
+
+/* Details of the last error raised on the calling thread ("" if none). */
+const char* qmv_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMV_H */

@@ -1,0 +1,124 @@
+"""The C ABI without a GPU: library loads, exports what include/qmv.h declares,
+and every validation error is raised before any HIP call."""
+import os
+import re
+
+import numpy as np
+import pytest
+
+from block_quantized_weight_qmv_amd import qmv
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "qmv.h")
+
+FAKE = 0x7F0000000000  # a 16-byte aligned address; never dereferenced by these tests
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(qmv_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qmv.lib()
+    names = declared_functions()
+    assert len(names) >= 14
+    for n in names:
+        assert hasattr(lib, n), n
+    assert sorted(qmv.EXPORTED) == names
+
+
+def test_block_and_packed_sizes():
+    assert [qmv.qmv_block_size(f) for f in ("q8_0", "q4_k", "q6_k", "int4_g128")] == [32, 256, 256, 128]
+    assert qmv.qmv_block_size(0) == 0 and qmv.qmv_block_size(5) == 0
+    assert qmv.qmv_packed_size("q8_0", 1536, 1536) == 2_506_752
+    assert qmv.qmv_packed_size("q4_k", 18944, 3584) == 38_191_104
+    assert qmv.qmv_packed_size("q6_k", 152064, 3584) == 447_068_160
+    assert qmv.qmv_packed_size("int4_g128", 3584, 18944) == 35_008_512
+    for bad in [(0, 256), (1, 0), (1, 255), (-1, 256)]:
+        assert qmv.qmv_packed_size("q4_k", *bad) == 0
+
+
+def _desc(fmt="q4_k", rows=8, cols=512, ptr=FAKE):
+    return qmv.qmv_create_weights(fmt, rows, cols, ptr, qmv.qmv_packed_size(fmt, rows, cols))
+
+
+def _expect(status, fn, *args):
+    with pytest.raises(qmv.QmvError) as e:
+        fn(*args)
+    assert e.value.status == status, str(e.value)
+    assert qmv.qmv_last_error() != ""
+
+
+def test_create_weights_errors():
+    n = qmv.qmv_packed_size("q4_k", 8, 512)
+    _expect(-1, qmv.qmv_create_weights, "q4_k", 8, 512, None, n)
+    _expect(-2, qmv.qmv_create_weights, 9, 8, 512, FAKE, n)
+    _expect(-3, qmv.qmv_create_weights, "q4_k", 8, 500, FAKE, n)
+    _expect(-3, qmv.qmv_create_weights, "q4_k", 0, 512, FAKE, n)
+    _expect(-5, qmv.qmv_create_weights, "q4_k", 8, 512, FAKE, n + 1)
+    _expect(-4, qmv.qmv_create_weights, "q4_k", 8, 512, FAKE + 2, n)
+    w = _desc("int4_g128", 4, 256)
+    assert w.scales_offset == 4 * 256 // 2 and w.fmt == 4 and w.nbytes == 4 * 128 + 4 * 2 * 2
+    assert _desc().scales_offset == 0
+
+
+def test_gemv_validation_errors():
+    w = _desc()
+    g = qmv.qmv_gemv
+    _expect(-1, g, "q4_k", w, None, "f32", FAKE, 8, 512, 1)
+    _expect(-1, g, "q4_k", w, FAKE, "f32", None, 8, 512, 1)
+    _expect(-2, g, "q6_k", w, FAKE, "f32", FAKE, 8, 512, 1)     # fmt disagrees
+    _expect(-2, g, "q4_k", w, FAKE, "f32", FAKE, 9, 512, 1)     # rows disagree
+    _expect(-2, g, "q4_k", w, FAKE, "f32", FAKE, 8, 256, 1)     # cols disagree
+    _expect(-3, g, "q4_k", w, FAKE, "f32", FAKE, 8, 512, 0)     # batch < 1
+    _expect(-6, g, "q4_k", w, FAKE, 7, FAKE, 8, 512, 1)         # dtype
+    _expect(-4, g, "q4_k", w, FAKE + 4, "f32", FAKE, 8, 512, 1)
+    _expect(-4, g, "q4_k", w, FAKE, "f32", FAKE + 8, 8, 512, 1)
+    _expect(-6, g, "q4_k", w, FAKE, "f32", FAKE, 8, 512, 70000)  # batch above the limit
+    big = _desc("q4_k", 1, 256 * 300)
+    _expect(-6, g, "q4_k", big, FAKE, "f32", FAKE, 1, 256 * 300, 1)
+    # a tampered descriptor is caught
+    bad = _desc()
+    bad.nbytes += 144
+    _expect(-5, g, "q4_k", bad, FAKE, "f32", FAKE, 8, 512, 1)
+    bad = _desc()
+    bad.data = None
+    _expect(-1, g, "q4_k", bad, FAKE, "f32", FAKE, 8, 512, 1)
+    bad = _desc("int4_g128", 4, 256)
+    bad.scales_offset = 0
+    _expect(-2, g, "int4_g128", bad, FAKE, "f32", FAKE, 4, 256, 1)
+
+
+def test_dequant_and_probe_validation_errors():
+    w = _desc()
+    _expect(-1, qmv.qmv_dequant, w, None, "f32")
+    _expect(-6, qmv.qmv_dequant, w, FAKE, 5)
+    _expect(-4, qmv.qmv_dequant, w, FAKE + 2, "f32")
+    _expect(-5, qmv.qmv_probe_read, FAKE, 17, FAKE)
+    _expect(-4, qmv.qmv_probe_copy, FAKE + 1, FAKE, 16)
+    _expect(-1, qmv.qmv_probe_copy, None, FAKE, 16)
+    assert qmv.qmv_probe_read_outputs(1 << 30) >= 1
+
+
+def test_status_strings():
+    for s in range(-8, 1):
+        assert qmv.qmv_status_string(s) not in ("", "unknown status")
+    assert qmv.qmv_status_string(-99) == "unknown status"
+
+
+def test_hip_error_surfaces_without_a_gpu():
+    """A valid call on a machine with no GPU fails inside HIP -> QMV_ERR_HIP."""
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("a GPU is present: this test would launch with fake pointers")
+    w = _desc()
+    _expect(-8, qmv.qmv_gemv, "q4_k", w, FAKE, "f32", FAKE, 8, 512, 1)
+
+
+def test_single_hip_runtime_mapped():
+    import torch  # noqa: F401
+    qmv.lib()
+    maps = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
+    assert len(maps) == 1, maps

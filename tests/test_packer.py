@@ -1,0 +1,65 @@
+"""The library's host packer against the oracle's packer: byte-exact (CPU only)."""
+import numpy as np
+import pytest
+
+import oracle
+from block_quantized_weight_qmv_amd import qmv
+from golden_io import all_names, load
+from synth import gen_weights
+
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("rows,nblk", [(1, 1), (3, 2), (7, 5), (16, 14)])
+def test_random_fields_pack_identically(fmt, rows, nblk):
+    cols = nblk * oracle.QK[fmt]
+    f = gen_weights(fmt, rows, cols, seed=7000 + rows * 31 + nblk)
+    got = qmv.pack_fields(fmt, f, rows, cols)
+    want = oracle.pack(fmt, f, rows, cols)
+    assert got.dtype == np.uint8 and np.array_equal(got, want)
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_extreme_fields_pack_identically(fmt):
+    rows, cols = 4, 2 * oracle.QK[fmt]
+    f = gen_weights(fmt, rows, cols, seed=11)
+    key, lo, hi = {"q8_0": ("q", -128, 127), "q4_k": ("u", 0, 15), "q6_k": ("q", 0, 63),
+                   "int4_g128": ("q", -8, 7)}[fmt]
+    f[key][0::2] = lo
+    f[key][1::2] = hi
+    sk = "s_bits" if fmt == "int4_g128" else "d_bits"
+    f[sk][...] = np.array([0x0000, 0x0001, 0x7BFF, 0x8000][: f[sk].shape[1]] * 4, np.uint16)[: f[sk].size].reshape(f[sk].shape)
+    if fmt == "q4_k":
+        f["sc"][...] = 63
+        f["m"][0] = 0
+    if fmt == "q6_k":
+        f["sc"][0] = -128
+        f["sc"][1] = 127
+    assert np.array_equal(qmv.pack_fields(fmt, f, rows, cols), oracle.pack(fmt, f, rows, cols))
+
+
+@pytest.mark.parametrize("name", all_names())
+def test_golden_blocks_repack(name):
+    g = load(name)
+    f = oracle.unpack(g["fmt"], g["data"], g["rows"], g["cols"])
+    assert np.array_equal(qmv.pack_fields(g["fmt"], f, g["rows"], g["cols"]), g["data"])
+
+
+@pytest.mark.parametrize("fmt,field,value", [
+    ("q4_k", "u", 16), ("q4_k", "sc", 64), ("q4_k", "m", 64), ("q6_k", "q", 64),
+    ("int4_g128", "q", 8), ("int4_g128", "q", -9)])
+def test_range_errors(fmt, field, value):
+    rows, cols = 2, oracle.QK[fmt]
+    f = gen_weights(fmt, rows, cols, seed=3)
+    f[field] = f[field].astype(np.int16)
+    f[field].flat[5] = value
+    f[field] = f[field].astype(np.int8 if value < 0 or f[field].dtype == np.int8 else np.uint8)
+    with pytest.raises(qmv.QmvError) as e:
+        qmv.pack_fields(fmt, f, rows, cols)
+    assert e.value.status == -7
+
+
+def test_packer_shape_errors():
+    with pytest.raises(qmv.QmvError):
+        qmv.qmv_pack_q8_0(np.zeros(1, np.uint16), np.zeros(33, np.int8), 1, 33)
