@@ -8,10 +8,14 @@ down 3584x18944 -- with fp32 activations ~ N(0, 1), seeded synthetic weights
 timed region starts.  Distinct copies of the layer (>= 1.25 GiB in total) are
 cycled so that the 256 MB Infinity Cache cannot serve repeated reads.
 
+The step issues the layer's GEMVs in decode order, one launch per group of
+projections that read the same activation (qmv_gemv_multi): [q, k, v], [o],
+[gate, up], [down].  `--separate` issues one qmv_gemv per matrix instead.
+
 Output: one JSON line.  `value` is algorithmic bytes (packed weights + x + y)
 per step divided by the measured time per step.  `roofline` covers the
-dominant kernel (most time per step), timed with HIP events recorded on the
-launch stream around each of its launches inside the timed region.
+dominant kernel (most bytes per step): a graph of the same K steps restricted
+to that kernel's launches, replayed between HIP events on the replay stream.
 `cpu_baseline` times the CPU oracle (float64 decode + dot) on a bounded sample
 of the same matrices.
 
@@ -42,16 +46,33 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(fmt: str, cols: int, x_dtype: str) -> str:
-    """Instantiation the library launches for this shape (mirrors the launcher's choice)."""
+def kernel_name(fmt: str, cols_list, x_dtype: str) -> str:
+    """Instantiation the library launches for matrices of these widths in one
+    launch (mirrors the launcher: waves per workgroup = max(4, widest K split))."""
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096}[fmt]
-    kw = -(-cols // per_wave)
-    threads = 64 * kw * (4 if kw == 1 else 1)
-    cfg = "4, 256" if threads <= 256 else ("4, 512" if threads <= 512 else "2, 1024")
+    waves = max([4] + [-(-c // per_wave) for c in cols_list])
+    cfg = "4, 256" if waves <= 4 else ("4, 512" if waves <= 8 else "2, 1024")
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
            "int4_g128": "Int4G128Policy"}[fmt]
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
     return f"gemv_kernel<qmv::{pol}, {xt}, {cfg}>"
+
+
+def decode_groups(names):
+    """Launch groups in decode order: consecutive projections that read the same
+    activation (q/k/v, gate/up) form one group; every other matrix is alone."""
+    shared = [("q", "k", "v"), ("gate", "up")]
+    groups, i = [], 0
+    while i < len(names):
+        for tup in shared:
+            if tuple(names[i:i + len(tup)]) == tup:
+                groups.append(list(range(i, i + len(tup))))
+                i += len(tup)
+                break
+        else:
+            groups.append([i])
+            i += 1
+    return groups
 
 
 def measured_traffic(kernel: str, workload: str):
@@ -113,6 +134,7 @@ def main() -> int:
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--separate", action="store_true", help="one launch per matrix")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -136,20 +158,34 @@ def main() -> int:
     xb = {"f32": 4, "f16": 2, "bf16": 2}[x_dtype]
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[x_dtype]
 
+    # -- launch groups: projections that read the same activation share a launch --
+    names = [n for n, _, _ in mats]
+    if args.separate:
+        groups = [[m] for m in range(len(mats))]
+    else:
+        groups = decode_groups(names)
+
     # -- inputs: synthesize, pack on the host with the library packer, upload ---
     fields_list, packed_dev, xs, xs_dev, ys = [], [], [], [], []
+    leader = {m: g[0] for g in groups for m in g}
     for i, (name, rows, cols) in enumerate(mats):
         f = gen_weights(fmt, rows, cols, weight_seed(args.config, i))
         fields_list.append(f)
         packed_dev.append(torch.from_numpy(qmv.pack_fields(fmt, f, rows, cols)).to(dev))
-        x = gen_x(batch, cols, x_dtype, x_seed(args.config, i))
-        xs.append(x)
-        xt = torch.from_numpy(x.view(np.int16) if x_dtype == "bf16" else x).to(dev)
-        xs_dev.append(xt.view(tdt) if x_dtype == "bf16" else xt)
+        if leader[i] == i:
+            x = gen_x(batch, cols, x_dtype, x_seed(args.config, i))
+            xt = torch.from_numpy(x.view(np.int16) if x_dtype == "bf16" else x).to(dev)
+            xs.append(x)
+            xs_dev.append(xt.view(tdt) if x_dtype == "bf16" else xt)
+        else:  # same activation as the group's first matrix
+            xs.append(xs[leader[i]])
+            xs_dev.append(xs_dev[leader[i]])
         ys.append(torch.empty(batch, rows, dtype=torch.float32, device=dev))
     step_w_bytes = sum(p.numel() for p in packed_dev)
-    step_bytes = sum(p.numel() + batch * c * xb + batch * r * 4
-                     for p, (_, r, c) in zip(packed_dev, mats))
+    # algorithmic bytes: packed weights, each activation once per launch, y
+    gbytes = [sum(packed_dev[m].numel() + batch * mats[m][1] * 4 for m in g)
+              + batch * mats[g[0]][2] * xb for g in groups]
+    step_bytes = sum(gbytes)
     copies = max(1, int(np.ceil(args.rotate_gib * 2 ** 30 / step_w_bytes)))
     descs = []  # descs[c][m]
     keep = []
@@ -165,55 +201,76 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
-    def launch(c, m):
-        _, rows, cols = mats[m]
-        qmv.qmv_gemv(fmt, descs[c][m], xs_dev[m], x_dtype, ys[m], rows, cols, batch, sp)
+    def launch(c, g, sptr):
+        if len(g) == 1:
+            m = g[0]
+            _, rows, cols = mats[m]
+            qmv.qmv_gemv(fmt, descs[c][m], xs_dev[m], x_dtype, ys[m], rows, cols, batch, sptr)
+        else:
+            qmv.qmv_gemv_multi(fmt, x_dtype, batch,
+                               [(descs[c][m], xs_dev[m], ys[m]) for m in g], sptr)
 
     # dominant kernel: the instantiation with the most algorithmic bytes per step
-    kname = {m: kernel_name(fmt, mats[m][2], x_dtype) for m in range(len(mats))}
+    kname = [kernel_name(fmt, [mats[m][2] for m in g], x_dtype) for g in groups]
     by_kernel = {}
-    for m in range(len(mats)):
-        by_kernel.setdefault(kname[m], []).append(m)
-    mbytes = [packed_dev[m].numel() + batch * mats[m][2] * xb + batch * mats[m][1] * 4
-              for m in range(len(mats))]
-    dom = max(by_kernel, key=lambda k: sum(mbytes[m] for m in by_kernel[k]))
-    dom_ms = set(by_kernel[dom])
+    for gi in range(len(groups)):
+        by_kernel.setdefault(kname[gi], []).append(gi)
+    dom = max(by_kernel, key=lambda k: sum(gbytes[gi] for gi in by_kernel[k]))
 
     for s in range(args.warmup):
-        for m in range(len(mats)):
-            launch(s % copies, m)
+        for g in groups:
+            launch(s % copies, g, sp)
     torch.cuda.synchronize()
 
-    # -- timed region ------------------------------------------------------------
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(mats) + 1)]
-          for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_start.record(stream)
-    for s in range(args.steps):
-        c = (args.warmup + s) % copies
-        ev[s][0].record(stream)
-        for m in range(len(mats)):
-            launch(c, m)
-            ev[s][m + 1].record(stream)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_start.elapsed_time(t_end)
+    # -- timed regions: HIP-graph replays ------------------------------------------
+    # Launching from Python costs more than these kernels run, so every timed
+    # region is captured once as a graph and replayed; events on the replay stream
+    # bracket the replay.  (1) K whole steps -> ms_per_step.  (2) per kernel
+    # instantiation, the same K steps restricted to that kernel's launches, so the
+    # rotation over weight copies and the launch order are unchanged -> its average
+    # launch duration (the duration plus the small gap between graph nodes).
+    cap = torch.cuda.Stream(dev)
+
+    def timed_graph(gis):
+        g = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=cap):
+            for s in range(args.steps):
+                c = (args.warmup + s) % copies
+                for gi in gis:
+                    launch(c, groups[gi], cap.cuda_stream)
+        g.replay()                    # untimed: first-touch costs
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        g.replay()                    # replays on the current stream
+        t1.record(stream)
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1)
+
+    total_ms = timed_graph(list(range(len(groups))))
     ms_per_step = total_ms / args.steps
-
-    per_launch_ms = np.array([[ev[s][m].elapsed_time(ev[s][m + 1]) for m in range(len(mats))]
-                              for s in range(args.steps)])
-    med_us = np.median(per_launch_ms, axis=0) * 1e3
-    detail = {mats[m][0]: {"shape": f"{mats[m][1]}x{mats[m][2]}", "bytes": int(mbytes[m]),
-                           "median_us": round(float(med_us[m]), 3),
-                           "GBps": round(mbytes[m] / (med_us[m] * 1e-6) / 1e9, 1)}
-              for m in range(len(mats))}
-    dom_time_s = per_launch_ms[:, sorted(dom_ms)].sum() / 1e3
-    dom_launches = args.steps * len(dom_ms)
-    dom_avg_us = dom_time_s / dom_launches * 1e6
-    dom_bytes_per_launch = sum(mbytes[m] for m in dom_ms) / len(dom_ms)
+    kern = {}
+    for k, gis in by_kernel.items():
+        el = timed_graph(gis)
+        kern[k] = {"launches": ["+".join(names[m] for m in groups[gi]) for gi in gis],
+                   "launches_per_step": len(gis),
+                   "avg_launch_us": round(el * 1e3 / (args.steps * len(gis)), 3),
+                   "bytes_per_launch": sum(gbytes[gi] for gi in gis) / len(gis)}
+        kern[k]["GBps"] = round(kern[k]["bytes_per_launch"] / (kern[k]["avg_launch_us"] * 1e-6) / 1e9, 1)
+    if not args.separate or len(groups) > 1:
+        per_launch = {}
+        for gi, g in enumerate(groups):
+            el = timed_graph([gi])
+            us = el * 1e3 / args.steps
+            per_launch["+".join(names[m] for m in g)] = {
+                "us": round(us, 3), "GBps": round(gbytes[gi] / (us * 1e-6) / 1e9, 1)}
+    else:
+        per_launch = None
+    dom_avg_us = kern[dom]["avg_launch_us"]
+    dom_bytes_per_launch = kern[dom]["bytes_per_launch"]
     achieved = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9
+    detail = kern
 
     # -- HBM read ceiling on this GPU (128-bit streaming read of 2 GiB) ----------------
     nb = 2 * 2 ** 30
@@ -248,16 +305,20 @@ def main() -> int:
         "data": "synthetic",
         "config": {"workload": workload, "format": fmt, "batch": batch, "x_dtype": x_dtype,
                    "matrices": {n: f"{r}x{c}" for n, r, c in mats},
+                   "launches": ["+".join(names[m] for m in g) for g in groups],
                    "bytes_per_step": int(step_bytes), "weight_copies": copies},
         "pct_of_peak": round(100 * value / PEAK_GBPS, 1),
         "us_per_gemv": round(ms_per_step * 1e3 / len(mats), 3),
-        "per_matrix": detail,
+        "per_kernel": detail,
+        "per_launch": per_launch,
         "read_ceiling_GBps": round(read_ceiling, 1),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
                      "traffic": measured_traffic(dom, workload),
                      "kernel": dom, "avg_launch_us": round(dom_avg_us, 3),
-                     "launches_per_step": len(dom_ms),
+                     "launches_per_step": len(by_kernel[dom]),
+                     "timing": "HIP events around a graph replay of the K steps restricted "
+                               "to this kernel's launches, on the replay stream",
                      "bytes_per_launch": round(dom_bytes_per_launch, 1)},
     }
     if not args.no_cpu_baseline:

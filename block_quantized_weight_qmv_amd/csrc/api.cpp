@@ -128,31 +128,59 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols, const void* 
 
 int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x, int32_t x_dtype, float* y,
                  int64_t rows, int64_t cols, int64_t batch, void* stream) {
-  int32_t st = qmv::check_weights(W);
-  if (st != QMV_OK) return st;
-  if (!x || !y) return fail(QMV_ERR_NULL, "x or y is NULL");
+  if (!W) return fail(QMV_ERR_NULL, "weights descriptor is NULL");
   if (fmt != W->fmt || rows != W->rows || cols != W->cols)
     return fail(QMV_ERR_FORMAT, "call (fmt %d, %lld x %lld) disagrees with weights (fmt %d, %lld x %lld)",
                 fmt, (long long)rows, (long long)cols, W->fmt, (long long)W->rows,
                 (long long)W->cols);
+  const qmv_gemv_item item{W, x, y};
+  return qmv_gemv_multi(fmt, x_dtype, batch, &item, 1, stream);
+}
+
+int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
+                       int32_t n, void* stream) {
+  if (!items) return fail(QMV_ERR_NULL, "items is NULL");
+  if (n < 1) return fail(QMV_ERR_SHAPE, "item count %d < 1", n);
+  if (n > qmv::kMaxItems)
+    return fail(QMV_ERR_UNSUPPORTED, "item count %d above %d", n, qmv::kMaxItems);
+  if (qmv_block_size(fmt) == 0) return fail(QMV_ERR_FORMAT, "unknown format %d", fmt);
   if (batch < 1) return fail(QMV_ERR_SHAPE, "batch %lld < 1", (long long)batch);
   if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16)
     return fail(QMV_ERR_UNSUPPORTED, "activation dtype %d", x_dtype);
-  if (!qmv::aligned16(x) || !qmv::aligned16(y))
-    return fail(QMV_ERR_ALIGN, "x or y not 16-byte aligned");
   if (batch > qmv::kMaxBatch)
     return fail(QMV_ERR_UNSUPPORTED, "batch %lld above %lld", (long long)batch,
                 (long long)qmv::kMaxBatch);
-  if (cols > qmv::gemv_max_cols(fmt))
-    return fail(QMV_ERR_UNSUPPORTED, "cols %lld above the GEMV limit %lld for format %d",
-                (long long)cols, (long long)qmv::gemv_max_cols(fmt), fmt);
-  qmv::GemvArgs a{W, x, x_dtype, y, batch, static_cast<hipStream_t>(stream)};
+  qmv::GemvCall calls[qmv::kMaxItems];
+  for (int i = 0; i < n; ++i) {
+    const qmv_gemv_item& it = items[i];
+    int32_t st = qmv::check_weights(it.W);
+    if (st != QMV_OK) return st;
+    if (it.W->fmt != fmt)
+      return fail(QMV_ERR_FORMAT, "item %d has format %d, launch format %d", i, it.W->fmt, fmt);
+    if (!it.x || !it.y) return fail(QMV_ERR_NULL, "item %d: x or y is NULL", i);
+    if (!qmv::aligned16(it.x) || !qmv::aligned16(it.y))
+      return fail(QMV_ERR_ALIGN, "item %d: x or y not 16-byte aligned", i);
+    if (it.W->cols > qmv::gemv_max_cols(fmt))
+      return fail(QMV_ERR_UNSUPPORTED, "item %d: cols %lld above the GEMV limit %lld", i,
+                  (long long)it.W->cols, (long long)qmv::gemv_max_cols(fmt));
+    calls[i] = qmv::GemvCall{it.W, it.x, it.y};
+  }
+  // Outputs must not overlap: each item's y is written by its own workgroups.
+  for (int i = 0; i < n; ++i)
+    for (int j = i + 1; j < n; ++j) {
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(items[i].y);
+      const uintptr_t a1 = a0 + static_cast<uintptr_t>(batch * items[i].W->rows) * 4;
+      const uintptr_t b0 = reinterpret_cast<uintptr_t>(items[j].y);
+      const uintptr_t b1 = b0 + static_cast<uintptr_t>(batch * items[j].W->rows) * 4;
+      if (a0 < b1 && b0 < a1) return fail(QMV_ERR_SHAPE, "outputs of items %d and %d overlap", i, j);
+    }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
   switch (fmt) {
-    case QMV_Q8_0: e = qmv::gemv_q8_0(a); break;
-    case QMV_Q4_K: e = qmv::gemv_q4_k(a); break;
-    case QMV_Q6_K: e = qmv::gemv_q6_k(a); break;
-    default: e = qmv::gemv_int4_g128(a); break;
+    case QMV_Q8_0: e = qmv::gemv_q8_0(calls, n, x_dtype, batch, s); break;
+    case QMV_Q4_K: e = qmv::gemv_q4_k(calls, n, x_dtype, batch, s); break;
+    case QMV_Q6_K: e = qmv::gemv_q6_k(calls, n, x_dtype, batch, s); break;
+    default: e = qmv::gemv_int4_g128(calls, n, x_dtype, batch, s); break;
   }
   return qmv::from_hip(e, "qmv_gemv launch");
 }

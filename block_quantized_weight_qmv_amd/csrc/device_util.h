@@ -20,93 +20,100 @@ __device__ __forceinline__ float bf16_to_f32(uint32_t bits) {
   return __uint_as_float(bits << 16);
 }
 
-// 16 bytes from an address with any alignment.  On gfx950 the compiler emits
-// one global_load_dwordx4 (unaligned global access is enabled for amdhsa).
-__device__ __forceinline__ uint4 load16_any(const uint8_t* p) {
-  uint4 v;
-  __builtin_memcpy(&v, p, 16);
-  return v;
+// Weight loads: plain 128-bit global loads.  (Measured on gfx950 with
+// block-shaped access patterns, the nontemporal hint lowered bandwidth.)
+__device__ __forceinline__ uint4 ld16(const uint8_t* p) {  // 16-byte aligned
+  return *reinterpret_cast<const uint4*>(p);
 }
 
-__device__ __forceinline__ uint2 load8_any(const uint8_t* p) {
-  uint2 v;
-  __builtin_memcpy(&v, p, 8);
-  return v;
+typedef uint32_t u32x4_a1 __attribute__((ext_vector_type(4), aligned(1)));
+typedef uint32_t u32x2_a1 __attribute__((ext_vector_type(2), aligned(1)));
+
+// Any alignment: on gfx950 the compiler emits one global_load_dwordx4
+// (unaligned global access is enabled for amdhsa).
+__device__ __forceinline__ uint4 ld16_any(const uint8_t* p) {
+  const u32x4_a1 v = *reinterpret_cast<const u32x4_a1*>(p);
+  return make_uint4(v.x, v.y, v.z, v.w);
 }
 
-__device__ __forceinline__ uint32_t load_u16(const uint8_t* p) {
-  uint16_t v;
-  __builtin_memcpy(&v, p, 2);
-  return v;
+__device__ __forceinline__ uint2 ld8_any(const uint8_t* p) {
+  const u32x2_a1 v = *reinterpret_cast<const u32x2_a1*>(p);
+  return make_uint2(v.x, v.y);
 }
 
-// N contiguous activations starting at a 16-byte aligned element, as fp32.
-template <int N>
-__device__ __forceinline__ void load_x(const float* p, float* out) {
-#pragma unroll
-  for (int i = 0; i < N; i += 4) {
-    const float4 v = *reinterpret_cast<const float4*>(p + i);
-    out[i] = v.x; out[i + 1] = v.y; out[i + 2] = v.z; out[i + 3] = v.w;
-  }
+__device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {  // 2-byte aligned
+  return *reinterpret_cast<const uint16_t*>(p);
 }
 
-template <int N>
-__device__ __forceinline__ void load_x(const _Float16* p, float* out) {
-#pragma unroll
-  for (int i = 0; i < N; i += 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p + i);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      out[i + 2 * k] = f16_to_f32(w[k] & 0xFFFFu);
-      out[i + 2 * k + 1] = f16_to_f32(w[k] >> 16);
-    }
-  }
+// Small integer codes as fp16 *subnormal* bit patterns.  A 16-bit half holding
+// an integer u < 1024 in its low bits is the fp16 value u * 2^-24, so
+//   fma(float(half), x, acc)
+// is exactly fma(u, x, acc) scaled by 2^-24 (one rounding either way; the
+// power-of-two scale is undone once per row).  The compiler folds the fp16
+// operand into v_fma_mix_f32 with op_sel, so two codes masked out of one
+// dword (bits 0-15 and 16-31) feed two FMAs with no conversion instruction.
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+constexpr float kTwo24 = 16777216.0f;
+
+__device__ __forceinline__ float fma_lo(uint32_t bits, float x, float acc) {
+  return fmaf(static_cast<float>(__builtin_bit_cast(h2_t, bits).x), x, acc);
+}
+__device__ __forceinline__ float fma_hi(uint32_t bits, float x, float acc) {
+  return fmaf(static_cast<float>(__builtin_bit_cast(h2_t, bits).y), x, acc);
 }
 
-template <int N>
-__device__ __forceinline__ void load_x(const bf16_t* p, float* out) {
-#pragma unroll
-  for (int i = 0; i < N; i += 8) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p + i);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      out[i + 2 * k] = __uint_as_float(w[k] << 16);
-      out[i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
-    }
-  }
-}
-
-// Byte b of a dword, converted to fp32 (v_cvt_f32_ubyte{0..3}).
+// Byte B of v as fp32 via v_cvt_f32_ubyte{B}.  The empty asm hides how v was
+// computed, which keeps the compiler from rewriting mask-then-convert into a
+// bitfield extract per byte.
 template <int B>
-__device__ __forceinline__ float ubyte(uint32_t v) {
+__device__ __forceinline__ float cvt_ubyte(uint32_t v) {
+  __asm__("" : "+v"(v));
   return static_cast<float>((v >> (8 * B)) & 0xFFu);
 }
 
-// Sum over the 64 lanes of a wave, returned to every lane.  Fixed order:
-// quad butterflies, half-row and row mirrors, then row broadcasts 15 and 31
-// (lane 63 ends with the total), read back with readlane.
-__device__ __forceinline__ float wave_sum(float v) {
-  int iv;
-  iv = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false);  // quad_perm 1,0,3,2
-  v += __int_as_float(iv);
-  iv = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false);  // quad_perm 2,3,0,1
-  v += __int_as_float(iv);
-  iv = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false); // row_half_mirror
-  v += __int_as_float(iv);
-  iv = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false); // row_mirror
-  v += __int_as_float(iv);
-  iv = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false); // row_bcast:15
-  v += __int_as_float(iv);
-  iv = __builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false); // row_bcast:31
-  v += __int_as_float(iv);
-  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 63));
+// Raw activation loads: N elements of XT starting at a 16-byte aligned element,
+// as N * sizeof(XT) / 16 uint4 words; converted later by x_to_f32 so that the
+// conversion does not force a wait before the weight loads are issued.
+template <int N, typename XT>
+__device__ __forceinline__ void load_x_raw(const XT* p, uint4* raw) {
+#pragma unroll
+  for (int i = 0; i < N * static_cast<int>(sizeof(XT)) / 16; ++i)
+    raw[i] = reinterpret_cast<const uint4*>(p)[i];
 }
 
-// Balanced contiguous partition of n items into parts: [begin, end) of part p.
-__device__ __forceinline__ int part_begin(int p, int n, int parts) {
-  return static_cast<int>((static_cast<int64_t>(p) * n) / parts);
+template <int N>
+__device__ __forceinline__ void x_to_f32(const uint4* raw, float* out, const float*) {
+#pragma unroll
+  for (int i = 0; i < N / 4; ++i) {
+    out[4 * i] = __uint_as_float(raw[i].x); out[4 * i + 1] = __uint_as_float(raw[i].y);
+    out[4 * i + 2] = __uint_as_float(raw[i].z); out[4 * i + 3] = __uint_as_float(raw[i].w);
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void x_to_f32(const uint4* raw, float* out, const _Float16*) {
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[8 * i + 2 * k] = f16_to_f32(w[k] & 0xFFFFu);
+      out[8 * i + 2 * k + 1] = f16_to_f32(w[k] >> 16);
+    }
+  }
+}
+
+template <int N>
+__device__ __forceinline__ void x_to_f32(const uint4* raw, float* out, const bf16_t*) {
+#pragma unroll
+  for (int i = 0; i < N / 8; ++i) {
+    const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      out[8 * i + 2 * k] = __uint_as_float(w[k] << 16);
+      out[8 * i + 2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+    }
+  }
 }
 
 }  // namespace qmv

@@ -6,95 +6,111 @@
 // u_{2j} in bits 0-3 and u_{2j+1} in bits 4-7 (u = q + 8), then an fp16 scales
 // plane [rows][cols/128].  w_k = s_{k/128} * (u_k - 8).
 //
-// Lane mapping: each lane owns 64 consecutive weights (32 code bytes, two
-// 16-byte loads, half of one group) plus that group's 2-byte scale; a wave
-// covers 4096 columns.  Per lane and row, in fp32:
-//   Se = sum u_even * x_even,  So = sum (16 u_odd) * x_odd
-//   partial = s * (Se + So/16 - 8 * X),  X = sum of the lane's 64 activations
+// Lane mapping: a wave covers 4096 columns = 2048 code bytes of a row.  Lane l
+// owns code bytes [16l, 16l+16) and [1024+16l, 1024+16l+16), so each of the two
+// 16-byte load instructions reads 1 KB of consecutive bytes, plus the fp16
+// scale of each half's group.  Per lane, half and row, fp32 (codes enter as
+// fp16 subnormals, see device_util.h):
+//   Se = sum u_even x_even 2^-24,  So = sum 16 u_odd x_odd 2^-24
+//   partial += s (2^24 (Se + So/16) - 8 X),  X = sum of the half's 32 activations
 #include "gemv_skeleton.h"
 
 namespace qmv {
 
 struct Int4G128Policy {
   static constexpr int kColsPerWave = 64 * 64;
-  struct Params {
-    const uint8_t* w;
-    uint64_t scales_offset;
-  };
+  static constexpr int kXElems = 64;
   struct XSlice {
-    float v[64];
-    float s;
+    float v[64];  // v[32h + k]: activation of column col[h] + k
+    float s[2];
   };
   struct Frag {
-    uint4 qa, qb;
-    uint32_t sbits;
+    uint4 q[2];
+    uint32_t sb[2];
   };
 
-  const uint8_t* codes;
-  const uint8_t* scales;
-  size_t code_row, scale_row;
-  int col0;
-  bool ok;
+  const uint8_t* codes[2];
+  const uint8_t* scales[2];
+  uint32_t code_row, scale_row;
+  int col[2];
+  bool okh[2];
 
-  __device__ Int4G128Policy(const Params& p, int cols, int kslot, int lane) {
-    col0 = kslot * kColsPerWave + 64 * lane;
-    ok = col0 < cols;
-    code_row = static_cast<size_t>(cols) / 2;
-    scale_row = static_cast<size_t>(cols / 128) * 2;
-    codes = p.w + col0 / 2;
-    scales = p.w + p.scales_offset + static_cast<size_t>(col0 / 128) * 2;
+  __device__ Int4G128Policy(const uint8_t* w, uint64_t scales_offset, int cols, int kslot,
+                            int lane) {
+    code_row = static_cast<uint32_t>(cols) / 2;
+    scale_row = static_cast<uint32_t>(cols / 128) * 2;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      int c = kslot * kColsPerWave + 2048 * h + 32 * lane;
+      okh[h] = c < cols;
+      if (!okh[h]) c = cols - 32;  // past the row end: read valid columns, x zeroed
+      col[h] = c;
+      codes[h] = w + c / 2;
+      scales[h] = w + scales_offset + static_cast<size_t>(c / 128) * 2;
+    }
   }
 
   template <typename XT>
-  __device__ void load_x(const XT* x, XSlice& s) const {
-    s.s = 0.f;
-    if (!ok) {
+  __device__ void load_x_raw(const XT* x, uint4* raw) const {
+    constexpr int kPer = 32 * static_cast<int>(sizeof(XT)) / 16;
+    qmv::load_x_raw<32>(x + col[0], raw);
+    qmv::load_x_raw<32>(x + col[1], raw + kPer);
+  }
+
+  template <typename XT>
+  __device__ void finish_x(const uint4* raw, XSlice& s) const {
+    x_to_f32<64>(raw, s.v, static_cast<const XT*>(nullptr));
 #pragma unroll
-      for (int i = 0; i < 64; ++i) s.v[i] = 0.f;
-      return;
+    for (int h = 0; h < 2; ++h) {
+      s.s[h] = 0.f;
+#pragma unroll
+      for (int k = 0; k < 32; ++k) {
+        s.v[32 * h + k] = okh[h] ? s.v[32 * h + k] : 0.f;
+        s.s[h] += s.v[32 * h + k];
+      }
     }
-    qmv::load_x<64>(x + col0, s.v);
-#pragma unroll
-    for (int i = 0; i < 64; ++i) s.s += s.v[i];
   }
 
   __device__ void load(int row, Frag& f) const {
-    const uint8_t* p = codes + static_cast<size_t>(row) * code_row;
-    f.qa = *reinterpret_cast<const uint4*>(p);
-    f.qb = *reinterpret_cast<const uint4*>(p + 16);
-    f.sbits = load_u16(scales + static_cast<size_t>(row) * scale_row);
-  }
-
-  __device__ static void zero(Frag& f) {
-    f.qa = make_uint4(0, 0, 0, 0);
-    f.qb = f.qa;
-    f.sbits = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      f.q[h] = ld16(codes[h] + static_cast<size_t>(row) * code_row);
+      f.sb[h] = ld_u16(scales[h] + static_cast<size_t>(row) * scale_row);
+    }
   }
 
   __device__ float dot(const Frag& f, const XSlice& s) const {
-    const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
-    float se = 0.f, so = 0.f;
+    float out = 0.f;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t lo = q[i] & 0x0F0F0F0Fu;  // u_{8i}, u_{8i+2}, u_{8i+4}, u_{8i+6}
-      const uint32_t hv = q[i] & 0xF0F0F0F0u;  // 16 u_{8i+1}, 16 u_{8i+3}, ...
-      se = fmaf(ubyte<0>(lo), s.v[8 * i + 0], se);
-      se = fmaf(ubyte<1>(lo), s.v[8 * i + 2], se);
-      se = fmaf(ubyte<2>(lo), s.v[8 * i + 4], se);
-      se = fmaf(ubyte<3>(lo), s.v[8 * i + 6], se);
-      so = fmaf(ubyte<0>(hv), s.v[8 * i + 1], so);
-      so = fmaf(ubyte<1>(hv), s.v[8 * i + 3], so);
-      so = fmaf(ubyte<2>(hv), s.v[8 * i + 5], so);
-      so = fmaf(ubyte<3>(hv), s.v[8 * i + 7], so);
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t q[4] = {f.q[h].x, f.q[h].y, f.q[h].z, f.q[h].w};
+      const float* v = s.v + 32 * h;
+      float se = 0.f, so = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        // dword i holds weights 8i..8i+7: byte b = u_{8i+2b} (low) | u_{8i+2b+1} (high)
+        const uint32_t w0 = q[i], w8 = q[i] >> 8;
+        const uint32_t a = w0 & 0x000F000Fu, b = w8 & 0x000F000Fu;  // u_{8i}, u_{8i+4} | u_{8i+2}, u_{8i+6}
+        const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;  // 16 u_{8i+1}, ... (odd weights)
+        const float* x = v + 8 * i;
+        se = fma_lo(a, x[0], se);
+        se = fma_lo(b, x[2], se);
+        se = fma_hi(a, x[4], se);
+        se = fma_hi(b, x[6], se);
+        so = fma_lo(e, x[1], so);
+        so = fma_lo(g, x[3], so);
+        so = fma_hi(e, x[5], so);
+        so = fma_hi(g, x[7], so);
+      }
+      const float t = fmaf(kTwo24, fmaf(so, 0.0625f, se), -8.f * s.s[h]);
+      out = fmaf(f16_to_f32(f.sb[h]), t, out);
     }
-    const float t = fmaf(so, 0.0625f, se);
-    return f16_to_f32(f.sbits) * fmaf(-8.f, s.s, t);
+    return out;
   }
 };
 
-hipError_t gemv_int4_g128(const GemvArgs& a) {
-  Int4G128Policy::Params prm{static_cast<const uint8_t*>(a.W->data), a.W->scales_offset};
-  return launch_gemv<Int4G128Policy>(a, prm);
+hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
+  return launch_gemv<Int4G128Policy>(calls, n, x_dtype, batch, s);
 }
 
 }  // namespace qmv

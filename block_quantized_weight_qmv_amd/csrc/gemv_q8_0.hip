@@ -7,17 +7,15 @@
 //
 // Lane mapping: one lane per block (32 weights); a wave covers 64 blocks
 // (2048 columns).  Codes are made unsigned by flipping bit 7 of every byte
-// (u = q + 128) so v_cvt_f32_ubyte applies; per lane and row, in fp32:
-//   partial = d * (sum u * x - 128 * X),  X = sum of the lane's 32 activations
+// (u = q + 128 < 1024) and enter the FMAs as fp16 subnormals (device_util.h):
+//   partial = d (2^24 sum u x 2^-24 - 128 X),  X = sum of the lane's activations
 #include "gemv_skeleton.h"
 
 namespace qmv {
 
 struct Q80Policy {
   static constexpr int kColsPerWave = 64 * 32;
-  struct Params {
-    const uint8_t* w;
-  };
+  static constexpr int kXElems = 32;
   struct XSlice {
     float v[32];
     float s;
@@ -28,43 +26,41 @@ struct Q80Policy {
   };
 
   const uint8_t* base;
-  size_t row_bytes;
+  uint32_t row_bytes;
   int col0;
   bool ok;
 
-  __device__ Q80Policy(const Params& p, int cols, int kslot, int lane) {
+  __device__ Q80Policy(const uint8_t* w, uint64_t, int cols, int kslot, int lane) {
     const int nb = cols / 32;
     const int j = kslot * 64 + lane;
     ok = j < nb;
-    row_bytes = static_cast<size_t>(nb) * 34;
-    base = p.w + static_cast<size_t>(j) * 34;
-    col0 = j * 32;
+    const int jc = ok ? j : nb - 1;  // lanes past the row end read a valid block
+    row_bytes = static_cast<uint32_t>(nb) * 34;
+    base = w + static_cast<size_t>(jc) * 34;
+    col0 = jc * 32;
   }
 
   template <typename XT>
-  __device__ void load_x(const XT* x, XSlice& s) const {
+  __device__ void load_x_raw(const XT* x, uint4* raw) const {
+    qmv::load_x_raw<32>(x + col0, raw);
+  }
+
+  template <typename XT>
+  __device__ void finish_x(const uint4* raw, XSlice& s) const {
+    x_to_f32<32>(raw, s.v, static_cast<const XT*>(nullptr));
     s.s = 0.f;
-    if (!ok) {
 #pragma unroll
-      for (int i = 0; i < 32; ++i) s.v[i] = 0.f;
-      return;
+    for (int i = 0; i < 32; ++i) {
+      s.v[i] = ok ? s.v[i] : 0.f;
+      s.s += s.v[i];
     }
-    qmv::load_x<32>(x + col0, s.v);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s.s += s.v[i];
   }
 
   __device__ void load(int row, Frag& f) const {
     const uint8_t* p = base + static_cast<size_t>(row) * row_bytes;
-    f.d = load_u16(p);
-    f.qa = load16_any(p + 2);
-    f.qb = load16_any(p + 18);
-  }
-
-  __device__ static void zero(Frag& f) {
-    f.qa = make_uint4(0, 0, 0, 0);
-    f.qb = f.qa;
-    f.d = 0;
+    f.d = ld_u16(p);
+    f.qa = ld16_any(p + 2);
+    f.qb = ld16_any(p + 18);
   }
 
   __device__ float dot(const Frag& f, const XSlice& s) const {
@@ -73,18 +69,18 @@ struct Q80Policy {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t u = q[i] ^ 0x80808080u;
-      acc = fmaf(ubyte<0>(u), s.v[4 * i + 0], acc);
-      acc = fmaf(ubyte<1>(u), s.v[4 * i + 1], acc);
-      acc = fmaf(ubyte<2>(u), s.v[4 * i + 2], acc);
-      acc = fmaf(ubyte<3>(u), s.v[4 * i + 3], acc);
+      const uint32_t a = u & 0x00FF00FFu, b = (u >> 8) & 0x00FF00FFu;  // codes 0,2 | 1,3
+      acc = fma_lo(a, s.v[4 * i + 0], acc);
+      acc = fma_lo(b, s.v[4 * i + 1], acc);
+      acc = fma_hi(a, s.v[4 * i + 2], acc);
+      acc = fma_hi(b, s.v[4 * i + 3], acc);
     }
-    return f16_to_f32(f.d) * fmaf(-128.f, s.s, acc);
+    return f16_to_f32(f.d) * fmaf(kTwo24, acc, -128.f * s.s);
   }
 };
 
-hipError_t gemv_q8_0(const GemvArgs& a) {
-  Q80Policy::Params prm{static_cast<const uint8_t*>(a.W->data)};
-  return launch_gemv<Q80Policy>(a, prm);
+hipError_t gemv_q8_0(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
+  return launch_gemv<Q80Policy>(calls, n, x_dtype, batch, s);
 }
 
 }  // namespace qmv

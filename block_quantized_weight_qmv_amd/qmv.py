@@ -41,6 +41,11 @@ class QmvWeights(ctypes.Structure):
                 ("scales_offset", ctypes.c_uint64)]
 
 
+class QmvGemvItem(ctypes.Structure):
+    """Mirror of struct qmv_gemv_item."""
+    _fields_ = [("W", ctypes.POINTER(QmvWeights)), ("x", ctypes.c_void_p), ("y", ctypes.c_void_p)]
+
+
 _lib = None
 
 _i32, _i64, _u64, _p = ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64, ctypes.c_void_p
@@ -53,6 +58,7 @@ _SIGS = {
     "qmv_pack_int4_g128": (_i32, [_p, _p, _i64, _i64, _p, _u64]),
     "qmv_create_weights": (_i32, [_i32, _i64, _i64, _p, _u64, ctypes.POINTER(QmvWeights)]),
     "qmv_gemv": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
+    "qmv_gemv_multi": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32, _p]),
     "qmv_dequant": (_i32, [ctypes.POINTER(QmvWeights), _p, _i32, _p]),
     "qmv_probe_read_outputs": (_i64, [_u64]),
     "qmv_probe_read": (_i32, [_p, _u64, _p, _p]),
@@ -197,6 +203,18 @@ def qmv_gemv(fmt, W: QmvWeights, x, x_dtype, y, rows: int, cols: int, batch: int
              stream=None) -> None:
     _check(lib().qmv_gemv(_fmt(fmt), ctypes.byref(W), _ptr(x), _dtype(x_dtype), _ptr(y),
                           rows, cols, batch, _stream(stream, x, y)))
+
+
+def qmv_gemv_multi(fmt, x_dtype, batch: int, items, stream=None) -> None:
+    """items: sequence of (QmvWeights, x, y) triples; one launch for all of them."""
+    arr = (QmvGemvItem * max(1, len(items)))()
+    for i, (W, x, y) in enumerate(items):
+        arr[i].W = ctypes.pointer(W)
+        arr[i].x = _ptr(x)
+        arr[i].y = _ptr(y)
+    tensors = [t for _, x, y in items for t in (x, y)]
+    _check(lib().qmv_gemv_multi(_fmt(fmt), _dtype(x_dtype), batch, arr, len(items),
+                                _stream(stream, *tensors)))
 
 
 def qmv_dequant(W: QmvWeights, out, out_dtype, stream=None) -> None:

@@ -144,6 +144,27 @@ int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,
                  int32_t x_dtype, float* y, int64_t rows, int64_t cols,
                  int64_t batch, void* stream);
 
+/* One matrix of a multi-matrix GEMV launch. */
+typedef struct qmv_gemv_item {
+  const qmv_weights* W; /* packed W_i (all items share the launch's format)  */
+  const void* x;        /* [batch][W->cols] activations of the launch's dtype */
+  float* y;             /* [batch][W->rows] fp32, overwritten                 */
+} qmv_gemv_item;
+
+/* y_i = W_i x_i for n (1..16) matrices in one launch: the matrices' rows are
+ * spread over one resident generation of workgroups, so small matrices share
+ * the ramp-up and tail of large ones.  Meant for the projections of a decode
+ * step that read the same activation (q/k/v, gate/up) -- the fused-QKV and
+ * multi-weight dispatch of hipfire ("Review hipfire prefill optimization
+ * levers"; "Implementation requirements for multi-weight Q8 WMMA dispatch":
+ * one dtype for every weight of a dispatch, K a whole number of blocks, and
+ * output tiles that never overlap).  Each item is validated as in qmv_gemv;
+ * the y ranges must be disjoint (QMV_ERR_SHAPE otherwise); every x and y is a
+ * 16-byte aligned device pointer.  Results equal n separate qmv_gemv calls
+ * up to float32 summation order. */
+int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch,
+                       const qmv_gemv_item* items, int32_t n, void* stream);
+
 /* out = W as a dense [rows][cols] matrix of out_dtype (QMV_F32: the exact
  * value rounded once to fp32, bit-exact; QMV_F16 / QMV_BF16: that fp32 value
  * rounded to nearest-even).  out is a 16-byte aligned device pointer to

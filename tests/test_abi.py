@@ -91,6 +91,24 @@ def test_gemv_validation_errors():
     _expect(-2, g, "int4_g128", bad, FAKE, "f32", FAKE, 4, 256, 1)
 
 
+def test_gemv_multi_validation_errors():
+    a, b = _desc(), _desc("q4_k", 16, 512)
+    m = qmv.qmv_gemv_multi
+    Y2 = FAKE + 4096
+    _expect(-3, m, "q4_k", "f32", 1, [])                                   # no items
+    _expect(-6, m, "q4_k", "f32", 1, [(a, FAKE, FAKE + 64 * i) for i in range(17)])
+    _expect(-2, m, "q6_k", "f32", 1, [(a, FAKE, FAKE)])                    # format differs
+    _expect(-2, m, 9, "f32", 1, [(a, FAKE, FAKE)])
+    _expect(-3, m, "q4_k", "f32", 1, [(a, FAKE, FAKE), (b, FAKE, FAKE + 16)])  # y overlap
+    _expect(-4, m, "q4_k", "f32", 1, [(a, FAKE, FAKE), (b, FAKE + 2, Y2)])
+    _expect(-1, m, "q4_k", "f32", 1, [(a, FAKE, FAKE), (b, None, Y2)])
+    _expect(-6, m, "q4_k", 3, 1, [(a, FAKE, FAKE)])
+    _expect(-3, m, "q4_k", "f32", 0, [(a, FAKE, FAKE)])
+    bad = _desc()
+    bad.nbytes = 1
+    _expect(-5, m, "q4_k", "f32", 1, [(a, FAKE, FAKE), (bad, FAKE, Y2)])
+
+
 def test_dequant_and_probe_validation_errors():
     w = _desc()
     _expect(-1, qmv.qmv_dequant, w, None, "f32")

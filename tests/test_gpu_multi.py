@@ -1,0 +1,109 @@
+"""qmv_gemv_multi on the GPU: several matrices in one launch.
+
+Each item is checked against the float64 oracle with the same normwise bound
+as qmv_gemv (2e-3), and against a separate qmv_gemv call of the same matrix
+(same per-row arithmetic, so the two agree to float32 rounding).  Items mix
+shapes with one and several waves along K, ragged row counts and shared or
+distinct activations; y buffers carry canaries between items.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from block_quantized_weight_qmv_amd import qmv
+from gpu_util import DEV, Weights, oracle_y, say, to_dev_x
+from synth import gen_x
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+# (rows, blocks per row) per item; the last item spans several waves along K
+ITEMS = {
+    "q8_0": [(67, 48), (5, 48), (130, 48), (33, 300)],
+    "q4_k": [(67, 14), (5, 14), (130, 14), (33, 40)],
+    "q6_k": [(67, 14), (5, 14), (130, 14), (33, 40)],
+    "int4_g128": [(67, 28), (5, 28), (130, 28), (33, 80)],
+}
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+@pytest.mark.parametrize("x_dtype", ["f32", "f16", "bf16"])
+def test_multi_matches_oracle_and_single_calls(fmt, x_dtype):
+    qk = oracle.QK[fmt]
+    batch = 2
+    ws, xs_np, xs, ys = [], [], [], []
+    # one flat y buffer with a canary gap of 16..19 floats after each item
+    # (each item's y starts 16-byte aligned)
+    sizes = [batch * r for r, _ in ITEMS[fmt]]
+    offs = np.cumsum([0] + [(s + 16 + 3) // 4 * 4 for s in sizes])
+    ybuf = torch.full((int(offs[-1]),), 7.25, dtype=torch.float32, device=DEV)
+    shared = None
+    for i, (rows, nblk) in enumerate(ITEMS[fmt]):
+        cols = nblk * qk
+        w = Weights(fmt, rows, cols, seed=900 + 7 * i)
+        if i in (0, 1, 2):  # q/k/v-style items read one activation
+            if shared is None:
+                shared = gen_x(batch, cols, x_dtype, seed=77)
+            x = shared
+        else:
+            x = gen_x(batch, cols, x_dtype, seed=78 + i)
+        ws.append(w)
+        xs_np.append(x)
+        xs.append(to_dev_x(x, x_dtype))
+        ys.append(ybuf[int(offs[i]):int(offs[i]) + sizes[i]])
+    say(f"multi {fmt} x {x_dtype}: " + ", ".join(f"{w.rows}x{w.cols}" for w in ws))
+    qmv.qmv_gemv_multi(fmt, x_dtype, batch, [(w.desc, x, y) for w, x, y in zip(ws, xs, ys)])
+    torch.cuda.synchronize()
+    host = ybuf.cpu().numpy()
+    for i, w in enumerate(ws):
+        gap = host[int(offs[i]) + sizes[i]:int(offs[i + 1])]
+        assert np.all(gap == 7.25), f"canary after item {i} overwritten"
+        y = host[int(offs[i]):int(offs[i]) + sizes[i]].reshape(batch, w.rows)
+        err = oracle.normwise_rel_err(y, oracle_y(w, xs_np[i], x_dtype))
+        say(f"  item {i} {w.rows}x{w.cols}: normwise err {err.max():.3e}")
+        assert np.all(err <= TOL), err
+        single = w.gemv(xs[i], x_dtype, batch).cpu().numpy()
+        np.testing.assert_allclose(y, single, rtol=1e-5, atol=1e-5 * np.abs(single).max())
+
+
+@pytest.mark.parametrize("fmt", FMTS)
+def test_multi_sixteen_items(fmt):
+    qk = oracle.QK[fmt]
+    nblk = {"q8_0": 40, "q4_k": 5, "q6_k": 5, "int4_g128": 10}[fmt]
+    cols = nblk * qk
+    ws = [Weights(fmt, 3 + 11 * i, cols, seed=500 + i) for i in range(16)]
+    x_np = gen_x(1, cols, "f32", seed=5)
+    x = to_dev_x(x_np, "f32")
+    ys = [torch.empty(1, w.rows, dtype=torch.float32, device=DEV) for w in ws]
+    say(f"multi16 {fmt} cols {cols}")
+    qmv.qmv_gemv_multi(fmt, "f32", 1, [(w.desc, x, y) for w, y in zip(ws, ys)])
+    for w, y in zip(ws, ys):
+        err = oracle.normwise_rel_err(y.cpu().numpy(), oracle_y(w, x_np, "f32"))
+        assert np.all(err <= TOL), err
+
+
+def test_multi_graph_replay_matches_eager():
+    fmt, x_dtype = "q4_k", "bf16"
+    ws = [Weights(fmt, r, 14 * 256, seed=40 + r) for r in (96, 16, 16)]
+    x_np = gen_x(1, 14 * 256, x_dtype, seed=9)
+    x = to_dev_x(x_np, x_dtype)
+    ys = [torch.zeros(1, w.rows, dtype=torch.float32, device=DEV) for w in ws]
+    items = [(w.desc, x, y) for w, y in zip(ws, ys)]
+    qmv.qmv_gemv_multi(fmt, x_dtype, 1, items)
+    torch.cuda.synchronize()
+    eager = [y.clone() for y in ys]
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            qmv.qmv_gemv_multi(fmt, x_dtype, 1, items, stream=s)
+    for rep in range(3):
+        for y in ys:
+            y.fill_(-1.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for y, e in zip(ys, eager):
+            assert torch.equal(y, e), f"replay {rep} differs"
