@@ -83,25 +83,26 @@ __device__ __forceinline__ void load_tile(const P& pol, typename P::Frag* f, int
   for (int r = 0; r < R; ++r) pol.load(min(row0 + r, r_last), f[r]);
 }
 
+// Reduce a tile and store its rows: to y when this wave covers all of K, else
+// this wave's K-slice sums to its LDS column `part` (indexed by row - r_begin).
 template <class P, int R>
 __device__ __forceinline__ void finish_tile(const P& pol, const typename P::Frag* f,
                                             const typename P::XSlice& xs, float* y, int row0,
-                                            int r_end, int kw, int lane, int wave, float* part) {
+                                            int r_begin, int r_end, int kw, int lane, float* part) {
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = pol.dot(f[r], xs);
   const float t = reduce_rows<R>(acc, lane);
-  if (kw == 1) {
-    if (lane < R && row0 + lane < r_end) y[row0 + lane] = t;
-  } else {
-    if (lane < R) part[wave * R + lane] = t;
-    __syncthreads();
-    if (wave == 0 && lane < R && row0 + lane < r_end) {
-      float s = 0.f;
-      for (int k = 0; k < kw; ++k) s += part[k * R + lane];
-      y[row0 + lane] = s;
-    }
-    __syncthreads();
+  if (lane < R && row0 + lane < r_end) {
+    // The LDS write is a relaxed atomic store (a plain ds_write) so that the
+    // compiler cannot merge the two stores into one generic-pointer store:
+    // a flat store counts against both wait counters, and the wait-count
+    // pass would then drain the weight prefetch at every tile.
+    if (kw == 1)
+      y[row0 + lane] = t;
+    else
+      __hip_atomic_store(part + (row0 - r_begin + lane), t, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
   }
 }
 
@@ -113,13 +114,14 @@ struct GemvItem {
   float* y;           // [batch][rows]
   int rows, cols;
   int kw;             // waves along K
-  int sets_per_wg;    // row sets per workgroup
+  int sets_per_wg;    // row sets per workgroup (kw waves each)
   int nsets, q, rem;  // rows = q * nsets + rem; set s has q + (s < rem) rows
   int wg_begin;       // first workgroup of this matrix
 };
 
 struct GemvLaunch {
   int n;
+  int part_stride;    // LDS floats per wave for K-split partial sums (>= rows of a set)
   GemvItem item[kMaxItems];
 };
 
@@ -146,7 +148,9 @@ gemv_kernel(const GemvLaunch args) {
   const int r_end = r_begin + m.q + (set < m.rem ? 1 : 0);
   const int r_last = r_end - 1;
 
-  __shared__ float part[(MAXT / 64) * R];
+  // K-split partial sums: one column of part_stride floats per wave.
+  extern __shared__ float part_lds[];
+  float* part = part_lds + wave * args.part_stride;
   const P pol(m.w, m.scales_offset, m.cols, kslot, lane);
 
   // Issue order: x slice, tile 0, tile 1; only then wait for x.
@@ -167,19 +171,50 @@ gemv_kernel(const GemvLaunch args) {
   // flight per wave.  An empty asm with a memory clobber keeps the loads in
   // program order without waiting for them (the weight pointer is
   // deliberately not __restrict__: a restrict-qualified read-only pointer
-  // lets the compiler move its loads across the clobber).
-  int r0 = r_begin;  // every set has at least one row
-  do {
-    finish_tile<P, R>(pol, fa, xs, y, r0, r_end, kw, lane, wave, part);
+  // lets the compiler move its loads across the clobber), and a scheduling
+  // barrier stops the next tile's arithmetic, which touches no memory, from
+  // being hoisted above them.
+  //
+  // The loop has a single exit, at its bottom.  A second exit between the two
+  // tiles reaches the loop header in the compiler's wait-count analysis on a
+  // path where only one tile was requested, and the merged state makes the
+  // first tile of every iteration wait for all outstanding loads, draining
+  // the prefetch.  So the pair loop runs while a third tile exists and the
+  // last one or two tiles are finished after it.
+  const int ntiles = (r_end - r_begin + R - 1) / R;
+  int r0 = r_begin;
+#pragma unroll 1
+  for (int t = 2; t < ntiles; t += 2) {
+    finish_tile<P, R>(pol, fa, xs, y, r0, r_begin, r_end, kw, lane, part);
     load_tile<P, R>(pol, fa, r0 + 2 * R, r_last);
     __asm__ __volatile__("" ::: "memory");
-    if (r0 + R >= r_end) break;
-    finish_tile<P, R>(pol, fb, xs, y, r0 + R, r_end, kw, lane, wave, part);
+    __builtin_amdgcn_sched_barrier(0);
+    finish_tile<P, R>(pol, fb, xs, y, r0 + R, r_begin, r_end, kw, lane, part);
     load_tile<P, R>(pol, fb, r0 + 3 * R, r_last);
     __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
     r0 += 2 * R;
-  } while (r0 < r_end);
+  }
+  finish_tile<P, R>(pol, fa, xs, y, r0, r_begin, r_end, kw, lane, part);
+  if (r0 + R < r_end) finish_tile<P, R>(pol, fb, xs, y, r0 + R, r_begin, r_end, kw, lane, part);
+
+  // K split: after one barrier, the kw waves of the set add the columns of
+  // their set in slot order, row by row (waves that left early count as
+  // arrived at a barrier).
+  if (kw > 1) {
+    __syncthreads();
+    const float* cols = part_lds + (wave - kslot) * args.part_stride;
+    for (int j = kslot * 64 + lane; j < r_end - r_begin; j += kw * 64) {
+      float v = cols[j];
+      for (int k = 1; k < kw; ++k) v += cols[k * args.part_stride + j];
+      y[r_begin + j] = v;
+    }
+  }
 }
+
+// Rows of a K-split set are capped so that the partial sums of a workgroup
+// (waves x rows floats) stay within 16 waves x kMaxPartStride x 4 bytes.
+constexpr int kMaxPartStride = 256;
 
 // Widest K split among the matrices of a launch.
 template <class P>
@@ -206,6 +241,7 @@ inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_wav
   if (rps < 1) rps = 1;
   int wg = 0;
   L->n = n;
+  L->part_stride = 0;
   for (int i = 0; i < n; ++i) {
     GemvItem& m = L->item[i];
     const qmv_weights* W = calls[i].W;
@@ -216,10 +252,16 @@ inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_wav
     m.rows = static_cast<int>(W->rows);
     m.cols = static_cast<int>(W->cols);
     m.kw = static_cast<int>((W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
-    m.sets_per_wg = m.kw == 1 ? waves : 1;  // a kw > 1 set shares its workgroup's barrier
-    m.nsets = static_cast<int>((m.rows + rps - 1) / rps);
+    m.sets_per_wg = waves / m.kw;
+    int64_t set_rows = rps;
+    if (m.kw > 1 && set_rows > kMaxPartStride) set_rows = kMaxPartStride;  // LDS of the partials
+    m.nsets = static_cast<int>((m.rows + set_rows - 1) / set_rows);
     m.q = m.rows / m.nsets;
     m.rem = m.rows % m.nsets;
+    if (m.kw > 1) {
+      const int need = m.q + (m.rem ? 1 : 0);
+      L->part_stride = need > L->part_stride ? need : L->part_stride;
+    }
     m.wg_begin = wg;
     wg += (m.nsets + m.sets_per_wg - 1) / m.sets_per_wg;
   }
@@ -246,14 +288,60 @@ inline int64_t resident_workgroups(K kernel, int block) {
   return cache[dev];
 }
 
+// Launch shape.  Waves stream their rows with two tiles in flight; the HBM
+// queue holds all of them, so a request waits about (bytes in flight) /
+// bandwidth.  Enough waves keep the memory busy and the SIMDs fed, but every
+// extra byte in flight lengthens the ramp-up before the first tiles arrive
+// and the tail after the last: measured on gfx950, two waves per SIMD at
+// most, at least one per SIMD, and at least kMinRowsPerWave rows per wave
+// (short-lived waves pay the activation load and the first-tile latency for
+// little work).
+#ifndef QMV_WAVES_PER_SIMD
+#define QMV_WAVES_PER_SIMD 2
+#endif
+#ifndef QMV_MIN_ROWS_PER_WAVE
+#define QMV_MIN_ROWS_PER_WAVE 8
+#endif
+constexpr int kMaxWavesPerSimd = QMV_WAVES_PER_SIMD;
+constexpr int kMinRowsPerWave = QMV_MIN_ROWS_PER_WAVE;
+
+inline int device_cus() {
+  static int cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
 template <class P, typename XT, int R, int MAXT>
 hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream) {
   auto kernel = gemv_kernel<P, XT, R, MAXT>;
   const int block = 64 * waves;
-  const int64_t target = resident_workgroups(kernel, block) * waves;
+  const int cus = device_cus();
+  int64_t wave_rows = 0;
+  for (int i = 0; i < n; ++i)
+    wave_rows += calls[i].W->rows * ((calls[i].W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
+  const int64_t resident = resident_workgroups(kernel, block) * waves;
+  int64_t target = wave_rows / kMinRowsPerWave;
+  if (target > static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd)
+    target = static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd;
+  if (target < static_cast<int64_t>(cus) * 4) target = static_cast<int64_t>(cus) * 4;
+  // whole workgroups per CU, so that no CU carries an extra one
+  int64_t per_cu = target / (static_cast<int64_t>(cus) * waves);
+  if (per_cu < 1) per_cu = 1;
+  target = per_cu * cus * waves;
+  if (target > resident) target = resident;
   GemvLaunch L;
   const int grid = plan_gemv<P>(calls, n, waves, target, &L);
-  hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(block), 0, stream, L);
+  const size_t lds = static_cast<size_t>(waves) * L.part_stride * sizeof(float);
+  hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(block), lds, stream,
+                     L);
   return hipGetLastError();
 }
 
@@ -262,9 +350,9 @@ hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStr
   const int kw = max_kw<P>(calls, n);
   if (kw > 16) return hipErrorInvalidValue;
   const int waves = kw < 4 ? 4 : kw;
-  if (waves <= 4) return launch_cfg<P, XT, 4, 256>(calls, n, waves, batch, stream);
-  if (waves <= 8) return launch_cfg<P, XT, 4, 512>(calls, n, waves, batch, stream);
-  return launch_cfg<P, XT, 2, 1024>(calls, n, waves, batch, stream);
+  if (waves <= 4) return launch_cfg<P, XT, 2, 256>(calls, n, waves, batch, stream);
+  if (waves <= 8) return launch_cfg<P, XT, 2, 512>(calls, n, waves, batch, stream);
+  return launch_cfg<P, XT, 1, 1024>(calls, n, waves, batch, stream);
 }
 
 template <class P>

@@ -196,6 +196,10 @@ def qmv_create_weights(fmt, rows: int, cols: int, dev_packed, nbytes: int | None
         nbytes = dev_packed.numel() * dev_packed.element_size()
     w = QmvWeights()
     _check(lib().qmv_create_weights(_fmt(fmt), rows, cols, _ptr(dev_packed), nbytes, ctypes.byref(w)))
+    # The descriptor holds a raw pointer: keep the tensor alive with it, or the
+    # caching allocator may hand its memory back to the driver (empty_cache(),
+    # which graph capture calls) while launches still read it.
+    w.owner = None if isinstance(dev_packed, int) else dev_packed
     return w
 
 
