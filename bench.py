@@ -51,11 +51,11 @@ def kernel_name(fmt: str, cols_list, x_dtype: str) -> str:
     launch (mirrors the launcher: waves per workgroup = max(4, widest K split))."""
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
-    cfg = "4, 256" if waves <= 4 else ("4, 512" if waves <= 8 else "2, 1024")
+    cfg = "2, 256" if waves <= 4 else ("2, 512" if waves <= 8 else "1, 1024")
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
            "int4_g128": "Int4G128Policy"}[fmt]
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
-    return f"gemv_kernel<qmv::{pol}, {xt}, {cfg}>"
+    return f"qmv::gemv_kernel<qmv::{pol}, {xt}, {cfg}>"
 
 
 def decode_groups(names):
@@ -135,6 +135,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true", help="one launch per matrix")
+    ap.add_argument("--eager-pass", action="store_true",
+                    help="only issue warmup + steps eagerly (no graphs, no timing): for counter runs")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -221,6 +223,15 @@ def main() -> int:
         for g in groups:
             launch(s % copies, g, sp)
     torch.cuda.synchronize()
+    if args.eager_pass:
+        for s in range(args.steps):
+            for g in groups:
+                launch((args.warmup + s) % copies, g, sp)
+        torch.cuda.synchronize()
+        print(json.dumps({"eager_pass": cfg["name"], "steps": args.steps, "warmup": args.warmup,
+                          "launches": ["+".join(names[m] for m in g) for g in groups],
+                          "kernels": kname}), flush=True)
+        return 0
 
     # -- timed regions: HIP-graph replays ------------------------------------------
     # Launching from Python costs more than these kernels run, so every timed
