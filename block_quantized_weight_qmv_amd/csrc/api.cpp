@@ -175,7 +175,14 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
       if (a0 < b1 && b0 < a1) return fail(QMV_ERR_SHAPE, "outputs of items %d and %d overlap", i, j);
     }
   const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
+  hipError_t e = hipSuccess;
+  // Q4_K with bf16 activations and a batch of at least kMfmaMinBatch rows is
+  // a dense contraction: the MFMA tile kernel, one launch per matrix.
+  if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
+    for (int i = 0; i < n && e == hipSuccess; ++i)
+      e = qmv::gemm_q4_k_bf16(*calls[i].W, calls[i].x, calls[i].y, batch, s);
+    return qmv::from_hip(e, "qmv_gemv (MFMA tiles) launch");
+  }
   switch (fmt) {
     case QMV_Q8_0: e = qmv::gemv_q8_0(calls, n, x_dtype, batch, s); break;
     case QMV_Q4_K: e = qmv::gemv_q4_k(calls, n, x_dtype, batch, s); break;

@@ -28,6 +28,12 @@ hipError_t gemv_q6_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, h
 hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                           hipStream_t s);
 
+// Batched Q4_K x bf16 on MFMA (gemm_q4_k_mfma.hip); the GEMV entry points use
+// it for batches of at least kMfmaMinBatch rows.
+constexpr int64_t kMfmaMinBatch = 64;
+hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
+                          hipStream_t s);
+
 hipError_t dequant(const qmv_weights& W, void* out, int out_dtype, hipStream_t s);
 
 int64_t probe_read_blocks(uint64_t nbytes);

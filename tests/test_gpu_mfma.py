@@ -1,0 +1,95 @@
+"""Batched Q4_K x bf16 on the MFMA tile path (qmv_gemv with batch >= 64).
+
+Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
+The weights enter the matrix cores as bf16 hi + lo of their exact fp32 value
+(16 significant bits), so results are not bitwise those of the fp32 GEMV;
+inputs whose products and sums are small integers are exact on both paths and
+are checked exactly.  Shapes cover ragged tiles in both dimensions (rows and
+batch not multiples of 64) and the full-size batched workload (18944 x 3584,
+M = 64 and 512) on sampled rows.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from gpu_util import DEV, Weights, oracle_y, say, to_dev_x
+from synth import CONFIGS, gen_weights, gen_x, weight_seed, x_seed
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-3
+
+
+@pytest.mark.parametrize("rows,nblk,batch", [(64, 1, 64), (67, 14, 64), (130, 3, 65), (33, 5, 100),
+                                             (200, 14, 128), (1, 2, 64)])
+def test_mfma_matches_oracle(rows, nblk, batch):
+    cols = nblk * 256
+    say(f"mfma q4_k {rows}x{cols} batch {batch}")
+    w = Weights("q4_k", rows, cols, seed=700 + rows + nblk)
+    x = gen_x(batch, cols, "bf16", seed=71 + batch)
+    y = torch.full((batch, rows), 3.5, dtype=torch.float32, device=DEV)
+    w.gemv(to_dev_x(x, "bf16"), "bf16", batch, y=y)
+    y = y.cpu().numpy()
+    err = oracle.normwise_rel_err(y, oracle_y(w, x, "bf16"))
+    say(f"  normwise err max {err.max():.3e}")
+    assert np.all(err <= TOL), err
+
+
+def test_mfma_integer_case_is_exact():
+    # d = dmin = 1 and x in {-1, 0, 1}: every product and partial sum is an
+    # integer below 2^24, and hi + lo represents every weight exactly.
+    rows, cols, batch = 96, 4 * 256, 64
+    f = gen_weights("q4_k", rows, cols, 5)
+    f["d_bits"][:] = 0x3C00
+    f["dmin_bits"][:] = 0x3C00
+    w = Weights("q4_k", rows, cols, fields=f)
+    g = np.random.Generator(np.random.PCG64(9))
+    xf = g.integers(-1, 2, size=(batch, cols)).astype(np.float32)
+    x = (xf.view(np.uint32) >> 16).astype(np.uint16)
+    y = w.gemv(to_dev_x(x, "bf16"), "bf16", batch).cpu().numpy()
+    y64 = oracle_y(w, x, "bf16")
+    assert np.abs(y64).max() < 2 ** 24
+    np.testing.assert_array_equal(y, y64.astype(np.float32))
+
+
+def test_mfma_deterministic_and_graph_replay():
+    rows, cols, batch = 256, 14 * 256, 64
+    w = Weights("q4_k", rows, cols, seed=11)
+    x = to_dev_x(gen_x(batch, cols, "bf16", seed=12), "bf16")
+    y1 = w.gemv(x, "bf16", batch)
+    y2 = w.gemv(x, "bf16", batch)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    s = torch.cuda.Stream()
+    yg = torch.zeros_like(y1)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            w.gemv(x, "bf16", batch, y=yg, stream=s)
+    for _ in range(3):
+        yg.fill_(-2.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y1)
+
+
+@pytest.mark.parametrize("batch", [64, 512])
+def test_full_size_batched_ffn_sampled_rows(batch):
+    cfg = CONFIGS[5]
+    _, rows, cols = cfg["mats"][0]
+    say(f"full-size mfma {rows}x{cols} batch {batch}")
+    w = Weights("q4_k", rows, cols, seed=weight_seed(5, 0))
+    x = gen_x(batch, cols, "bf16", x_seed(5, 0))
+    y = w.gemv(to_dev_x(x, "bf16"), "bf16", batch).cpu().numpy()
+    g = np.random.Generator(np.random.PCG64(batch))
+    ids = np.sort(g.choice(rows, size=48, replace=False))
+    ids[0], ids[-1] = 0, rows - 1
+    y64 = oracle_y(w, x, "bf16", ids)
+    err = oracle.normwise_rel_err(y[:, ids], y64)
+    say(f"  sampled normwise err max {err.max():.3e}")
+    assert np.all(err <= TOL)
+    assert np.all(np.isfinite(y))
+    del w
+    torch.cuda.empty_cache()
