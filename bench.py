@@ -51,7 +51,7 @@ def kernel_name(fmt: str, cols_list, x_dtype: str) -> str:
     launch (mirrors the launcher: waves per workgroup = max(4, widest K split))."""
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
-    cfg = "2, 256" if waves <= 4 else ("2, 512" if waves <= 8 else "1, 1024")
+    cfg = "2, 2, 256" if waves <= 4 else ("2, 2, 512" if waves <= 8 else "1, 2, 1024")
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
            "int4_g128": "Int4G128Policy"}[fmt]
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]

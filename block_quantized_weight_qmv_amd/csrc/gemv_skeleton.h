@@ -125,7 +125,7 @@ struct GemvLaunch {
   GemvItem item[kMaxItems];
 };
 
-template <class P, typename XT, int R, int MAXT>
+template <class P, typename XT, int R, int D, int MAXT>
 __global__ void __launch_bounds__(MAXT)
 gemv_kernel(const GemvLaunch args) {
   // This workgroup's matrix (wave-uniform scan over at most kMaxItems).
@@ -157,9 +157,9 @@ gemv_kernel(const GemvLaunch args) {
   uint4 raw[P::kXElems * sizeof(XT) / 16];
   pol.load_x_raw(x, raw);
   __builtin_amdgcn_sched_barrier(0);
-  typename P::Frag fa[R], fb[R];
-  load_tile<P, R>(pol, fa, r_begin, r_last);
-  load_tile<P, R>(pol, fb, r_begin + R, r_last);
+  typename P::Frag f[D][R];
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
   typename P::XSlice xs;
@@ -179,24 +179,24 @@ gemv_kernel(const GemvLaunch args) {
   // tiles reaches the loop header in the compiler's wait-count analysis on a
   // path where only one tile was requested, and the merged state makes the
   // first tile of every iteration wait for all outstanding loads, draining
-  // the prefetch.  So the pair loop runs while a third tile exists and the
-  // last one or two tiles are finished after it.
+  // the prefetch.  So the loop runs D tiles per iteration while a tile past
+  // them exists, and the last at most D tiles are finished after it.
   const int ntiles = (r_end - r_begin + R - 1) / R;
   int r0 = r_begin;
 #pragma unroll 1
-  for (int t = 2; t < ntiles; t += 2) {
-    finish_tile<P, R>(pol, fa, xs, y, r0, r_begin, r_end, kw, lane, part);
-    load_tile<P, R>(pol, fa, r0 + 2 * R, r_last);
-    __asm__ __volatile__("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    finish_tile<P, R>(pol, fb, xs, y, r0 + R, r_begin, r_end, kw, lane, part);
-    load_tile<P, R>(pol, fb, r0 + 3 * R, r_last);
-    __asm__ __volatile__("" ::: "memory");
-    __builtin_amdgcn_sched_barrier(0);
-    r0 += 2 * R;
+  for (int t = D; t < ntiles; t += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      finish_tile<P, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
+      load_tile<P, R>(pol, f[j], r0 + (j + D) * R, r_last);
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    r0 += D * R;
   }
-  finish_tile<P, R>(pol, fa, xs, y, r0, r_begin, r_end, kw, lane, part);
-  if (r0 + R < r_end) finish_tile<P, R>(pol, fb, xs, y, r0 + R, r_begin, r_end, kw, lane, part);
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (r0 + j * R < r_end) finish_tile<P, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
 
   // K split: after one barrier, the kw waves of the set add the columns of
   // their set in slot order, row by row (waves that left early count as
@@ -319,9 +319,10 @@ inline int device_cus() {
   return cache[dev];
 }
 
-template <class P, typename XT, int R, int MAXT>
-hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream) {
-  auto kernel = gemv_kernel<P, XT, R, MAXT>;
+template <class P, typename XT, int R, int D, int MAXT>
+hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream,
+                      int waves_per_simd) {
+  auto kernel = gemv_kernel<P, XT, R, D, MAXT>;
   const int block = 64 * waves;
   const int cus = device_cus();
   int64_t wave_rows = 0;
@@ -329,8 +330,8 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
     wave_rows += calls[i].W->rows * ((calls[i].W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
   const int64_t resident = resident_workgroups(kernel, block) * waves;
   int64_t target = wave_rows / kMinRowsPerWave;
-  if (target > static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd)
-    target = static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd;
+  if (target > static_cast<int64_t>(cus) * 4 * waves_per_simd)
+    target = static_cast<int64_t>(cus) * 4 * waves_per_simd;
   if (target < static_cast<int64_t>(cus) * 4) target = static_cast<int64_t>(cus) * 4;
   // whole workgroups per CU, so that no CU carries an extra one
   int64_t per_cu = target / (static_cast<int64_t>(cus) * waves);
@@ -350,9 +351,14 @@ hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStr
   const int kw = max_kw<P>(calls, n);
   if (kw > 16) return hipErrorInvalidValue;
   const int waves = kw < 4 ? 4 : kw;
-  if (waves <= 4) return launch_cfg<P, XT, 2, 256>(calls, n, waves, batch, stream);
-  if (waves <= 8) return launch_cfg<P, XT, 2, 512>(calls, n, waves, batch, stream);
-  return launch_cfg<P, XT, 1, 1024>(calls, n, waves, batch, stream);
+  // Two tiles in flight per wave, two waves per SIMD.  (Measured alternatives
+  // on the 7B layer shapes: one wave per SIMD with 3, 4, 6 or 8 tiles in
+  // flight, or two waves with 4, were no faster in total; the younger wave of
+  // a SIMD trails the older one under the oldest-first issue order, but a
+  // deeper single wave loses more on the small matrices and at steady state.)
+  if (waves <= 4) return launch_cfg<P, XT, 2, 2, 256>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+  if (waves <= 8) return launch_cfg<P, XT, 2, 2, 512>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+  return launch_cfg<P, XT, 1, 2, 1024>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
 }
 
 template <class P>
