@@ -176,8 +176,9 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     }
   const hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e = hipSuccess;
-  // Q4_K with bf16 activations and a batch of at least kMfmaMinBatch rows is
-  // a dense contraction: the MFMA tile kernel, one launch per matrix.
+  // Q4_K with bf16 activations and a batch of at least kMfmaMinBatch rows: the
+  // matrix-core kernel, one launch per matrix (the GEMV path would read the
+  // weights once per activation row).
   if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
     for (int i = 0; i < n && e == hipSuccess; ++i)
       e = qmv::gemm_q4_k_bf16(*calls[i].W, calls[i].x, calls[i].y, batch, s);

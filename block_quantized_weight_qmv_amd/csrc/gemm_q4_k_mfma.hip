@@ -1,53 +1,58 @@
 // Batched Q4_K multiply on the gfx950 matrix cores: Y[m][n] = sum_k X[m][k] W[n][k]
 // for bf16 activations X [M][K] and Q4_K weights W [N][K] (y layout [batch][rows]).
 //
-// Used when the batch makes the product a real dense contraction (M >= 64:
-// prefill chunks, speculative-decode verify).  The pages keep two kernel
-// families for this reason: hipEngine 0.3.0 ("Quickstart") pairs WMMA prefill
-// with GEMV decode, LLM170 runs speculative verify as a batched forward, and
-// hipfire's multi-weight WMMA dispatch rules (K a whole number of blocks, one
-// dtype per dispatch, disjoint output tiles) apply here unchanged.
+// Used once the batch makes the product a dense contraction (prefill chunks,
+// speculative-decode verify).  The pages keep two kernel families for this
+// reason: hipEngine 0.3.0 ("Quickstart") pairs WMMA prefill with GEMV decode,
+// LLM170 runs speculative verify as a batched forward, and hipfire's
+// multi-weight WMMA dispatch rules (K a whole number of blocks, one dtype per
+// dispatch, disjoint output tiles) apply unchanged.
 //
-// Per workgroup (4 waves) an output tile of 64 rows of W x 64 activation rows,
-// K stepped 64 weights at a time (one Q4_K sub-block pair):
-//   1. every thread decodes 16 weights of one W row to their exact fp32 value
-//      w = fma(d*sc, u, -dmin*m) (the one rounding of the format), then splits
-//      it into bf16 hi = RNE(w) and lo = RNE(w - hi): hi + lo carries 16
-//      significant bits (relative error <= 2^-17), so the bf16 products stay
-//      far inside the 2e-3 GEMV bound while X is used exactly as given;
-//   2. hi, lo and the X tile go to LDS (rows padded to 144 bytes so that the
-//      MFMA operand reads of 32 rows hit distinct banks);
-//   3. each wave runs v_mfma_f32_32x32x16_bf16 on its 32 x 32 block, twice per
-//      16-wide K slice (hi and lo), accumulating in fp32.
-// The next step's global loads are issued before the MFMA phase.
+// Factored form.  A Q4_K weight is d*sc_s*u - dmin*m_s with a 4-bit code u and
+// per-(row, sub-block) scales, so for every sub-block s of 32 weights
+//   sum_k W[n][k] X[m][k] = d sc_s (sum_k u X) - dmin m_s (sum_k X).
+// The code sum is a small-integer dot product that the matrix cores compute
+// exactly: the codes enter v_mfma_f32_16x16x32_bf16 as the bf16 value 128 + u
+// (bits 0x4300 | u, one AND-OR per two codes), X enters as given, and one
+// instruction covers one sub-block (K = 32).  With S = sum (128 + u) X and
+// Xs = sum X, the row's contribution is ds S - (128 ds + dm) Xs with
+// ds = d sc_s, dm = dmin m_s, applied in fp32 to the 16x16 result.  Nothing
+// is dequantized to memory, W is read once per tile of up to 64 batch rows,
+// and the products are exact (the 2e-3 GEMV bound is spent only on fp32
+// summation).
 //
-// Operand layouts of v_mfma_f32_32x32x16_bf16 (checked on the device): lane l
-// holds A[l % 32][8 (l / 32) + e] and B[8 (l / 32) + e][l % 32] for e = 0..7;
-// accumulator r of lane l is D[8 (r / 4) + 4 (l / 32) + r % 4][l % 32].
+// Workgroup: 4 waves, 64 rows of W (16 per wave), MT = 16 MB batch rows,
+// stepping one Q4_K block (256 K) at a time:
+//   * X's block for the tile is staged in LDS (double buffered, one barrier
+//     per block, its global loads issued two blocks ahead) with each group of
+//     8 columns permuted to the code order below, together with its 8
+//     sub-block sums;
+//   * each lane streams its row's header and 4 x 8 code bytes straight into
+//     registers (two blocks in flight) and builds the A operands there;
+//   * ds and 128 ds + dm of its 16 rows are exchanged through per-wave LDS.
+//
+// v_mfma_f32_16x16x32_bf16 (layout checked on the device): lane l holds
+// A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e = 0..7, and
+// accumulator r of lane l is D[4 (l / 16) + r][l % 16].  Code slot 8q + e of a
+// sub-block maps to weight 8q + (0, 2, 1, 3, 4, 6, 5, 7)[e], the order in which
+// masking one dword of code bytes yields bf16 pairs.
 #include "device_util.h"
 #include "launch.h"
 
 namespace qmv {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
-typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kTileN = 64, kTileM = 64, kTileK = 64;
-constexpr int kRowPad = kTileK + 8;  // bf16 per LDS row: 144 bytes
+constexpr int kXRow = 256 + 8;  // bf16 per staged X row (528 bytes)
 
-// fp32 -> bf16 bits, round to nearest even (finite inputs).
-__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
-  const uint32_t u = __float_as_uint(f);
-  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-}
-
-// 6-bit scale and min of sub-block s (0..7) from the 12 scale bytes, held in
-// the header dwords h1 (bytes 0-3), h2 (4-7), h3 (8-11).
+// 6-bit scale and min of sub-block s (0..7) from the header dwords holding
+// scales[0..3] (h1), [4..7] (h2) and [8..11] (h3).
 __device__ __forceinline__ void q4k_scale_min(uint32_t h1, uint32_t h2, uint32_t h3, int s,
                                               uint32_t& sc, uint32_t& mn) {
-  const uint64_t lo = (static_cast<uint64_t>(h2) << 32) | h1;  // scales[0..7]
   auto byte = [&](int i) -> uint32_t {
-    return i < 8 ? static_cast<uint32_t>(lo >> (8 * i)) & 0xFFu : (h3 >> (8 * (i - 8))) & 0xFFu;
+    const uint32_t word = i < 4 ? h1 : (i < 8 ? h2 : h3);
+    return (word >> (8 * (i & 3))) & 0xFFu;
   };
   if (s < 4) {
     sc = byte(s) & 63u;
@@ -58,97 +63,144 @@ __device__ __forceinline__ void q4k_scale_min(uint32_t h1, uint32_t h2, uint32_t
   }
 }
 
+// Two columns of a permuted 8-group: (x0, x2) and (x1, x3) from (x0, x1), (x2, x3).
+__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
+__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
+
+struct WRegs {
+  uint4 hd;     // block header of this lane's row
+  uint2 q[4];   // code bytes 32c + 8 (lane / 16) .. +7 of chunks c = 0..3
+};
+
+template <int MB>
 __global__ void __launch_bounds__(256)
-gemm_q4_k_bf16_kernel(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M,
-                      int m_tiles) {
-  __shared__ __attribute__((aligned(16))) uint16_t wh[kTileN][kRowPad];
-  __shared__ __attribute__((aligned(16))) uint16_t wl[kTileN][kRowPad];
-  __shared__ __attribute__((aligned(16))) uint16_t xs[kTileM][kRowPad];
+gemm_q4_k_bf16_kernel(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M) {
+  constexpr int MT = 16 * MB;
+  constexpr int kPairs = MT * 8;                 // (batch row, sub-block) sums per block
+  constexpr int kPairsPerThread = (kPairs + 255) / 256;
+  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][kXRow];
+  __shared__ __attribute__((aligned(16))) float xsum[2][8][MT];
+  __shared__ __attribute__((aligned(16))) float sds[4][8][16];   // ds per (wave, s, row)
+  __shared__ __attribute__((aligned(16))) float sdm[4][8][16];   // 128 ds + dm
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mt = static_cast<int>(blockIdx.x) % m_tiles, nt = static_cast<int>(blockIdx.x) / m_tiles;
-  const int n0 = nt * kTileN, m0 = mt * kTileM;
+  const int q = lane >> 4, l16 = lane & 15;
   const int nb = K / 256;
-  const size_t row_bytes = static_cast<size_t>(nb) * 144;
-  const int steps = nb * 4;
+  const int n0 = static_cast<int>(blockIdx.x) * 64 + wave * 16;
+  const int m0 = static_cast<int>(blockIdx.y) * MT;
+  const uint8_t* wrow = w + static_cast<size_t>(min(n0 + l16, N - 1)) * (static_cast<size_t>(nb) * 144);
 
-  // Decode assignment: W row r, 16 weights = half h (low / high nibbles) of
-  // qs bytes [32c + 16q, +16) of the step's chunk c.
-  const int r = tid >> 2, h = (tid >> 1) & 1, q = tid & 1;
-  const uint8_t* wrow = w + static_cast<size_t>(min(n0 + r, N - 1)) * row_bytes;
-  // X assignment: activation row xr, 16 consecutive elements of the step.
-  const int xr = tid >> 2, xk = 16 * (tid & 3);
-  const uint16_t* xrow = x + static_cast<size_t>(min(m0 + xr, M - 1)) * K + xk;
-
-  uint4 hd, qv, x0, x1;
-  auto load = [&](int step) {
-    const uint8_t* p = wrow + static_cast<size_t>(step >> 2) * 144;
-    hd = *reinterpret_cast<const uint4*>(p);
-    qv = *reinterpret_cast<const uint4*>(p + 16 + 32 * (step & 3) + 16 * q);
-    const uint16_t* px = xrow + step * kTileK;
-    x0 = *reinterpret_cast<const uint4*>(px);
-    x1 = *reinterpret_cast<const uint4*>(px + 8);
+  auto load_w = [&](int b, WRegs& r) {
+    const uint8_t* p = wrow + static_cast<size_t>(min(b, nb - 1)) * 144;
+    r.hd = *reinterpret_cast<const uint4*>(p);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint2*>(p + 16 + 32 * c + 8 * q);
+  };
+  // X staging: thread handles pairs (m, s) = (pi / 8, pi % 8): 32 columns.
+  uint4 xr[2][kPairsPerThread][4];  // X of the next two blocks in flight
+  auto load_x = [&](int b, int slot) {
+#pragma unroll
+    for (int t = 0; t < kPairsPerThread; ++t) {
+      const int pi = min(tid + 256 * t, kPairs - 1);
+      const int m = pi >> 3, s = pi & 7;
+      const uint16_t* p = x + static_cast<size_t>(min(m0 + m, M - 1)) * K +
+                          static_cast<size_t>(min(b, nb - 1)) * 256 + 32 * s;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) xr[slot][t][g] = reinterpret_cast<const uint4*>(p)[g];
+    }
+  };
+  auto stage_x = [&](int buf) {
+#pragma unroll
+    for (int t = 0; t < kPairsPerThread; ++t) {
+      const int pi = tid + 256 * t;
+      if (pi < kPairs) {
+        const int m = pi >> 3, s = pi & 7;
+        float sum = 0.f;
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const uint4 v = xr[buf][t][g];
+          const uint32_t d[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sum += __uint_as_float(d[i] << 16);
+            sum += __uint_as_float(d[i] & 0xFFFF0000u);
+          }
+          *reinterpret_cast<uint4*>(&xs[buf][m][32 * s + 8 * g]) =
+              make_uint4(lo_pair(v.x, v.y), hi_pair(v.x, v.y), lo_pair(v.z, v.w), hi_pair(v.z, v.w));
+        }
+        xsum[buf][s][m] = sum;
+      }
+    }
   };
 
-  // Output block of this wave: W rows [32 wn, +32) x activation rows [32 wm, +32).
-  const int wn = wave >> 1, wm = wave & 1;
-  f32x16_t acc = {};
+  f32x4_t acc[MB];
+#pragma unroll
+  for (int i = 0; i < MB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load(0);
-  for (int step = 0; step < steps; ++step) {
-    // 1-2: decode and stage this step's tiles.
+  auto step = [&](int b, const WRegs& r) {
+    const int buf = b & 1;
+    stage_x(buf);
+    __syncthreads();
+    load_x(b + 2, buf);
+    // Scales of this lane's row for sub-blocks 2q and 2q + 1.
     {
-      const int c = step & 3, s = 2 * c + h;
-      uint32_t sc, mn;
-      q4k_scale_min(hd.y, hd.z, hd.w, s, sc, mn);
-      const float ds = f16_to_f32(hd.x & 0xFFFFu) * static_cast<float>(sc);
-      const float dm = f16_to_f32(hd.x >> 16) * static_cast<float>(mn);
-      const uint32_t qw[4] = {qv.x, qv.y, qv.z, qv.w};
-      uint32_t hw[8], lw[8];
+      const float d = f16_to_f32(r.hd.x & 0xFFFFu), dmin = f16_to_f32(r.hd.x >> 16);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t byte = (qw[i >> 2] >> (8 * (i & 3))) & 0xFFu;
-        const uint32_t u = h ? (byte >> 4) : (byte & 15u);
-        const float v = fmaf(ds, static_cast<float>(u), -dm);
-        const uint32_t hb = f32_to_bf16_rne(v);
-        const uint32_t lb = f32_to_bf16_rne(v - __uint_as_float(hb << 16));
-        if (i & 1) {
-          hw[i >> 1] |= hb << 16;
-          lw[i >> 1] |= lb << 16;
-        } else {
-          hw[i >> 1] = hb;
-          lw[i >> 1] = lb;
-        }
+      for (int i = 0; i < 2; ++i) {
+        const int s = 2 * q + i;
+        uint32_t sc, mn;
+        q4k_scale_min(r.hd.y, r.hd.z, r.hd.w, s, sc, mn);
+        const float ds = d * static_cast<float>(sc);
+        sds[wave][s][l16] = ds;
+        sdm[wave][s][l16] = fmaf(128.f, ds, dmin * static_cast<float>(mn));
       }
-      const int col = 32 * h + 16 * q;
-      *reinterpret_cast<uint4*>(&wh[r][col]) = make_uint4(hw[0], hw[1], hw[2], hw[3]);
-      *reinterpret_cast<uint4*>(&wh[r][col + 8]) = make_uint4(hw[4], hw[5], hw[6], hw[7]);
-      *reinterpret_cast<uint4*>(&wl[r][col]) = make_uint4(lw[0], lw[1], lw[2], lw[3]);
-      *reinterpret_cast<uint4*>(&wl[r][col + 8]) = make_uint4(lw[4], lw[5], lw[6], lw[7]);
-      *reinterpret_cast<uint4*>(&xs[xr][xk]) = x0;
-      *reinterpret_cast<uint4*>(&xs[xr][xk + 8]) = x1;
     }
-    __syncthreads();
-    if (step + 1 < steps) load(step + 1);
-    // 3: four 16-wide K slices, hi and lo.
 #pragma unroll
-    for (int ks = 0; ks < kTileK / 16; ++ks) {
-      const int kk = 16 * ks + 8 * (lane >> 5);
-      const bf16x8_t a_hi = *reinterpret_cast<const bf16x8_t*>(&wh[32 * wn + (lane & 31)][kk]);
-      const bf16x8_t a_lo = *reinterpret_cast<const bf16x8_t*>(&wl[32 * wn + (lane & 31)][kk]);
-      const bf16x8_t b = *reinterpret_cast<const bf16x8_t*>(&xs[32 * wm + (lane & 31)][kk]);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_hi, b, acc, 0, 0, 0);
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_lo, b, acc, 0, 0, 0);
+    for (int s = 0; s < 8; ++s) {
+      const uint2 pc = r.q[s >> 1];
+      const uint32_t v0 = (s & 1) ? pc.x >> 4 : pc.x, v1 = (s & 1) ? pc.y >> 4 : pc.y;
+      const uint32_t a[4] = {(v0 & 0x000F000Fu) | 0x43004300u, ((v0 >> 8) & 0x000F000Fu) | 0x43004300u,
+                             (v1 & 0x000F000Fu) | 0x43004300u, ((v1 >> 8) & 0x000F000Fu) | 0x43004300u};
+      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a);
+      const f32x4_t ds4 = *reinterpret_cast<const f32x4_t*>(&sds[wave][s][4 * q]);
+      const f32x4_t dm4 = *reinterpret_cast<const f32x4_t*>(&sdm[wave][s][4 * q]);
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb) {
+        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(&xs[buf][16 * mb + l16][32 * s + 8 * q]);
+        const f32x4_t S =
+            __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const float xsv = xsum[buf][s][16 * mb + l16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(-dm4[i], xsv, fmaf(ds4[i], S[i], acc[mb][i]));
+      }
     }
-    __syncthreads();
-  }
+  };
 
-  const int m = m0 + 32 * wm + (lane & 31);
-  if (m < M) {
+  WRegs ra, rb;
+  load_w(0, ra);
+  load_w(1, rb);
+  load_x(0, 0);
+  load_x(1, 1);
+  int b = 0;
+#pragma unroll 1
+  for (; b + 2 < nb; b += 2) {
+    step(b, ra);
+    load_w(b + 2, ra);
+    step(b + 1, rb);
+    load_w(b + 3, rb);
+  }
+  step(b, ra);
+  if (b + 1 < nb) step(b + 1, rb);
+
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int n = n0 + 32 * wn + 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
-      if (n < N) y[static_cast<size_t>(m) * N + n] = acc[i];
+  for (int mb = 0; mb < MB; ++mb) {
+    const int m = m0 + 16 * mb + l16;
+    if (m < M) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 4 * q + i;
+        if (n < N) y[static_cast<size_t>(m) * N + n] = acc[mb][i];
+      }
     }
   }
 }
@@ -156,10 +208,20 @@ gemm_q4_k_bf16_kernel(const uint8_t* w, int N, int K, const uint16_t* x, float* 
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t stream) {
   const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols), M = static_cast<int>(batch);
-  const int m_tiles = (M + kTileM - 1) / kTileM, n_tiles = (N + kTileN - 1) / kTileN;
-  hipLaunchKernelGGL(gemm_q4_k_bf16_kernel, dim3(m_tiles * n_tiles), dim3(256), 0, stream,
-                     static_cast<const uint8_t*>(W.data), N, K, static_cast<const uint16_t*>(x), y,
-                     M, m_tiles);
+  const uint8_t* w = static_cast<const uint8_t*>(W.data);
+  const uint16_t* xb = static_cast<const uint16_t*>(x);
+  const unsigned n_tiles = static_cast<unsigned>((N + 63) / 64);
+  if (M <= 16) {
+    hipLaunchKernelGGL(gemm_q4_k_bf16_kernel<1>, dim3(n_tiles, 1), dim3(256), 0, stream, w, N, K, xb,
+                       y, M);
+  } else if (M <= 32) {
+    hipLaunchKernelGGL(gemm_q4_k_bf16_kernel<2>, dim3(n_tiles, 1), dim3(256), 0, stream, w, N, K, xb,
+                       y, M);
+  } else {
+    const unsigned m_tiles = static_cast<unsigned>((M + 63) / 64);
+    hipLaunchKernelGGL(gemm_q4_k_bf16_kernel<4>, dim3(n_tiles, m_tiles), dim3(256), 0, stream, w, N,
+                       K, xb, y, M);
+  }
   return hipGetLastError();
 }
 

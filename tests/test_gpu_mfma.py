@@ -1,12 +1,13 @@
-"""Batched Q4_K x bf16 on the MFMA tile path (qmv_gemv with batch >= 64).
+"""Batched Q4_K x bf16 on the matrix-core path (qmv_gemv with batch >= 3).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
-The weights enter the matrix cores as bf16 hi + lo of their exact fp32 value
-(16 significant bits), so results are not bitwise those of the fp32 GEMV;
-inputs whose products and sums are small integers are exact on both paths and
-are checked exactly.  Shapes cover ragged tiles in both dimensions (rows and
-batch not multiples of 64) and the full-size batched workload (18944 x 3584,
-M = 64 and 512) on sampled rows.
+The matrix cores take the 4-bit codes and the activations exactly and the
+sub-block scales are applied in fp32, so results are not bitwise those of the
+fp32 GEMV; inputs whose products and sums are small integers are exact on both
+paths and are checked exactly.  Shapes cover every batch tiling (batch tiles of
+16, 32 and 64 rows, ragged in rows and in batch, several tiles along the
+batch), the smallest batch routed here (3), and the full-size batched workload
+(18944 x 3584, M = 4, 16, 64 and 512) on sampled rows.
 """
 import numpy as np
 import pytest
@@ -22,7 +23,8 @@ TOL = 2e-3
 
 
 @pytest.mark.parametrize("rows,nblk,batch", [(64, 1, 64), (67, 14, 64), (130, 3, 65), (33, 5, 100),
-                                             (200, 14, 128), (1, 2, 64)])
+                                             (200, 14, 128), (1, 2, 64), (70, 3, 3), (67, 5, 4),
+                                             (96, 2, 16), (65, 3, 17), (40, 2, 32), (33, 4, 33)])
 def test_mfma_matches_oracle(rows, nblk, batch):
     cols = nblk * 256
     say(f"mfma q4_k {rows}x{cols} batch {batch}")
@@ -38,7 +40,7 @@ def test_mfma_matches_oracle(rows, nblk, batch):
 
 def test_mfma_integer_case_is_exact():
     # d = dmin = 1 and x in {-1, 0, 1}: every product and partial sum is an
-    # integer below 2^24, and hi + lo represents every weight exactly.
+    # integer below 2^24, so the fp32 result is exact on any summation order.
     rows, cols, batch = 96, 4 * 256, 64
     f = gen_weights("q4_k", rows, cols, 5)
     f["d_bits"][:] = 0x3C00
@@ -75,7 +77,7 @@ def test_mfma_deterministic_and_graph_replay():
         assert torch.equal(yg, y1)
 
 
-@pytest.mark.parametrize("batch", [64, 512])
+@pytest.mark.parametrize("batch", [4, 16, 64, 512])
 def test_full_size_batched_ffn_sampled_rows(batch):
     cfg = CONFIGS[5]
     _, rows, cols = cfg["mats"][0]
