@@ -10,6 +10,9 @@ Source of each layout:
   are GGUF's published block definitions as this library reads them (see the
   layout table in each function).  hipEngine 0.3.0, "GGUF Support", lists the
   same three types (plus Q5_K) as the tensor payload of a Q4_K_M file.
+* Q5_K -- hipEngine 0.3.0, "GGUF Support": 31% of the Q4_K_M tensor payload
+  (the MoE expert-down projections).  The page names the type only; the byte
+  map below is GGUF's published Q5_K block as this library reads it.
 * INT4_G128 -- "Costruire un runtime di inference LLM da zero" (datastack.it),
   "Tre bug che insegnano": symmetric INT4, one scale per 128 weights.  The
   page gives no byte layout; this library's reading is a codes plane followed
@@ -25,6 +28,7 @@ Field arrays ("fields") used by ``pack``/``unpack``:
   q4_k      d_bits u16[rows, nb], dmin_bits u16[rows, nb],
             sc u8[rows, nb, 8] (0..63), m u8[rows, nb, 8] (0..63),
             u u8[rows, cols] (0..15)
+  q5_k      d_bits, dmin_bits, sc, m as q4_k; u u8[rows, cols] (0..31)
   q6_k      d_bits u16[rows, nb], sc i8[rows, nb, 16], q u8[rows, cols] (0..63)
   int4_g128 s_bits u16[rows, cols/128], q i8[rows, cols] (-8..7)
 
@@ -36,9 +40,9 @@ import numpy as np
 
 from .fp import fp16_bits_to_f64
 
-FORMATS = ("q8_0", "q4_k", "q6_k", "int4_g128")
-QK = {"q8_0": 32, "q4_k": 256, "q6_k": 256, "int4_g128": 128}
-BLOCK_BYTES = {"q8_0": 34, "q4_k": 144, "q6_k": 210}
+FORMATS = ("q8_0", "q4_k", "q6_k", "int4_g128", "q5_k")
+QK = {"q8_0": 32, "q4_k": 256, "q6_k": 256, "int4_g128": 128, "q5_k": 256}
+BLOCK_BYTES = {"q8_0": 34, "q4_k": 144, "q6_k": 210, "q5_k": 176}
 
 
 def _check_shape(fmt: str, rows: int, cols: int) -> None:
@@ -276,16 +280,86 @@ def _dequant_int4_g128(f: dict, rows: int, cols: int) -> np.ndarray:
     return (s * q).reshape(rows, cols)
 
 
+# ----------------------------------------------------------------------------
+# Q5_K: 256 weights, 176 bytes, eight sub-blocks of 32.
+#   bytes [0, 2)    d, fp16;  bytes [2, 4) dmin, fp16
+#   bytes [4, 16)   scales[12]: the six-bit scales and mins, packed as in Q4_K
+#   bytes [16, 48)  qh[32]: bit 2c + h of qh[l] is the fifth code bit of weight
+#                   t = 64c + 32h + l
+#   bytes [48, 176) qs[128]: the low four code bits, arranged as Q4_K's qs
+#        (weight t = 64c + 32h + l takes nibble h of qs[32c + l])
+#   u = low | high << 4 (0..31),  sub-block s = 2c + h = t // 32
+#   w_t = d * sc_s * u - dmin * m_s
+# ----------------------------------------------------------------------------
+def q5_k_codes_to_bytes(u: np.ndarray):
+    """u[..., 256] (0..31) -> (qh[..., 32], qs[..., 128])."""
+    u = np.asarray(u, np.uint8)
+    qs = q4_k_codes_to_qs(u & 15)
+    hi = (u >> 4).reshape(u.shape[:-1] + (8, 32))                     # [s = 2c + h, l]
+    qh = np.zeros(u.shape[:-1] + (32,), np.uint8)
+    for s in range(8):
+        qh |= (hi[..., s, :] << s).astype(np.uint8)
+    return qh, qs
+
+
+def q5_k_bytes_to_codes(qh: np.ndarray, qs: np.ndarray) -> np.ndarray:
+    """(qh[..., 32], qs[..., 128]) -> u[..., 256] with weight t = 64c + 32h + l."""
+    low = q4_k_qs_to_codes(qs).reshape(qs.shape[:-1] + (8, 32))     # [s, l]
+    qh = np.asarray(qh, np.uint8)
+    high = np.stack([(qh >> s) & 1 for s in range(8)], axis=-2)      # [s, l]
+    return (low | (high << 4)).reshape(qs.shape[:-1] + (256,))
+
+
+def _pack_q5_k(f: dict, rows: int, cols: int) -> np.ndarray:
+    nb = cols // 256
+    blk = np.zeros((rows, nb, 176), np.uint8)
+    _put_le16(blk[:, :, 0:2], f["d_bits"])
+    _put_le16(blk[:, :, 2:4], f["dmin_bits"])
+    blk[:, :, 4:16] = q4_k_scales_to_bytes(f["sc"], f["m"])
+    qh, qs = q5_k_codes_to_bytes(np.asarray(f["u"]).reshape(rows, nb, 256))
+    blk[:, :, 16:48] = qh
+    blk[:, :, 48:176] = qs
+    return blk.reshape(-1)
+
+
+def _unpack_q5_k(data: np.ndarray, rows: int, cols: int) -> dict:
+    nb = cols // 256
+    blk = data.reshape(rows, nb, 176)
+    sc, m = q4_k_bytes_to_scales(blk[:, :, 4:16])
+    return {"d_bits": _le16(blk[:, :, 0], blk[:, :, 1]),
+            "dmin_bits": _le16(blk[:, :, 2], blk[:, :, 3]),
+            "sc": sc, "m": m,
+            "u": q5_k_bytes_to_codes(blk[:, :, 16:48], blk[:, :, 48:176]).reshape(rows, cols)}
+
+
+def _dequant_q5_k(f: dict, rows: int, cols: int) -> np.ndarray:
+    nb = cols // 256
+    d = fp16_bits_to_f64(f["d_bits"])[:, :, None, None]               # [r, b, 1, 1]
+    dmin = fp16_bits_to_f64(f["dmin_bits"])[:, :, None, None]
+    sc = f["sc"].astype(np.float64)[:, :, :, None]                    # [r, b, s, 1]
+    m = f["m"].astype(np.float64)[:, :, :, None]
+    u = f["u"].astype(np.float64).reshape(rows, nb, 8, 32)            # [r, b, s, l]
+    a = d * sc * u          # exact: at most 11 + 6 + 5 significant bits
+    b = dmin * m            # exact: at most 11 + 6 significant bits
+    w = a - b
+    bb = w - a              # TwoSum error term of a + (-b) must vanish
+    err = (a - (w - bb)) + (-b - bb)
+    if np.any(err != 0):
+        raise AssertionError("Q5_K weight not exact in float64")
+    return w.reshape(rows, cols)
+
+
 _PACK = {"q8_0": _pack_q8_0, "q4_k": _pack_q4_k, "q6_k": _pack_q6_k,
-         "int4_g128": _pack_int4_g128}
+         "int4_g128": _pack_int4_g128, "q5_k": _pack_q5_k}
 _UNPACK = {"q8_0": _unpack_q8_0, "q4_k": _unpack_q4_k, "q6_k": _unpack_q6_k,
-           "int4_g128": _unpack_int4_g128}
+           "int4_g128": _unpack_int4_g128, "q5_k": _unpack_q5_k}
 _DEQUANT = {"q8_0": _dequant_q8_0, "q4_k": _dequant_q4_k, "q6_k": _dequant_q6_k,
-            "int4_g128": _dequant_int4_g128}
+            "int4_g128": _dequant_int4_g128, "q5_k": _dequant_q5_k}
 
 _RANGES = {  # field -> (lo, hi) inclusive, for range validation of codes
     "q8_0": {"q": (-128, 127)},
     "q4_k": {"sc": (0, 63), "m": (0, 63), "u": (0, 15)},
+    "q5_k": {"sc": (0, 63), "m": (0, 63), "u": (0, 31)},
     "q6_k": {"sc": (-128, 127), "q": (0, 63)},
     "int4_g128": {"q": (-8, 7)},
 }
@@ -320,7 +394,8 @@ def dequant32(fmt: str, data, rows: int, cols: int) -> np.ndarray:
     """float32 dequantization: the exact value rounded once to nearest-even.
 
     Q8_0, Q6_K and INT4 products fit in binary32's 24-bit significand, so the
-    float32 value equals the exact one; Q4_K rounds once, at the subtraction.
+    float32 value equals the exact one; Q4_K and Q5_K round once, at the
+    subtraction.
     """
     return dequant64(fmt, data, rows, cols).astype(np.float32)
 

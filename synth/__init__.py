@@ -12,6 +12,7 @@ descriptions of the decode GEMV configurations:
 * Q8_0: fp16 scale d ~ U(0.002, 0.02), int8 codes ~ U{-127..127}.
 * Q4_K: fp16 d and dmin ~ U(0.001, 0.01), 6-bit sub-block scale and min
   ~ U{0..63}, 4-bit codes ~ U{0..15}.
+* Q5_K: as Q4_K, with 5-bit codes ~ U{0..31}.
 * Q6_K: fp16 d ~ U(0.001, 0.01), int8 sub-scales ~ U{-128..127}, 6-bit codes
   ~ U{0..63}.
 * INT4 symmetric group-128: codes ~ U{-8..7}, fp16 group scale
@@ -29,7 +30,7 @@ from __future__ import annotations
 
 import numpy as np
 
-QK = {"q8_0": 32, "q4_k": 256, "q6_k": 256, "int4_g128": 128}
+QK = {"q8_0": 32, "q4_k": 256, "q6_k": 256, "int4_g128": 128, "q5_k": 256}
 
 
 def rng(seed: int) -> np.random.Generator:
@@ -61,6 +62,18 @@ def gen_q4_k(rows: int, cols: int, seed: int, d_range=(0.001, 0.01),
     return {"d_bits": d_bits, "dmin_bits": dmin_bits, "sc": sc, "m": m, "u": u}
 
 
+def gen_q5_k(rows: int, cols: int, seed: int, d_range=(0.001, 0.01),
+             dmin_range=(0.001, 0.01)) -> dict:
+    g = rng(seed)
+    nb = cols // 256
+    d_bits = fp16_uniform_bits(g, (rows, nb), *d_range)
+    dmin_bits = fp16_uniform_bits(g, (rows, nb), *dmin_range)
+    sc = g.integers(0, 64, size=(rows, nb, 8), dtype=np.uint8)
+    m = g.integers(0, 64, size=(rows, nb, 8), dtype=np.uint8)
+    u = g.integers(0, 32, size=(rows, cols), dtype=np.uint8)
+    return {"d_bits": d_bits, "dmin_bits": dmin_bits, "sc": sc, "m": m, "u": u}
+
+
 def gen_q6_k(rows: int, cols: int, seed: int, d_range=(0.001, 0.01)) -> dict:
     g = rng(seed)
     nb = cols // 256
@@ -79,7 +92,7 @@ def gen_int4_g128(rows: int, cols: int, seed: int, s_range=(0.005, 0.05)) -> dic
 
 
 GENERATORS = {"q8_0": gen_q8_0, "q4_k": gen_q4_k, "q6_k": gen_q6_k,
-              "int4_g128": gen_int4_g128}
+              "int4_g128": gen_int4_g128, "q5_k": gen_q5_k}
 
 
 def gen_weights(fmt: str, rows: int, cols: int, seed: int, **kw) -> dict:

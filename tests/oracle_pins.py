@@ -13,7 +13,8 @@ oracle disagrees with:
 * invariants: zero scale -> zero weights, weights affine in the code with slope
   d*sc, the zero point of each format;
 * brute force: the float64 GEMV against an exact rational sum;
-* the byte counts of the decode workloads (34, 144 and 210 bytes per block).
+* the byte counts of the decode workloads (34, 144 and 210 bytes per block)
+  and of GGUF's Q5_K block (176 bytes).
 
 They are plain functions so tests/test_oracle_mutants.py can run them against
 an oracle with a planted mistake and check that some pin catches it.
@@ -26,7 +27,8 @@ import oracle
 from golden_io import all_names, load
 from synth import gen_weights, gen_x, rng
 
-FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128", "q5_k")
+MIN_FMTS = ("q4_k", "q5_k")     # formats with a per-sub-block min term
 
 
 # -- encodings ----------------------------------------------------------------
@@ -94,6 +96,7 @@ def pin_packed_sizes():
     assert oracle.packed_size("q8_0", 1, 32) == 34
     assert oracle.packed_size("q4_k", 1, 256) == 144
     assert oracle.packed_size("q6_k", 1, 256) == 210
+    assert oracle.packed_size("q5_k", 1, 256) == 176   # 2 + 2 + 12 + 32 + 128
     assert oracle.packed_size("int4_g128", 1, 128) == 64 + 2
     assert oracle.packed_size("q8_0", 1536, 1536) == 2_506_752
     assert oracle.packed_size("q4_k", 18944, 3584) == 38_191_104
@@ -108,7 +111,7 @@ def _fields(fmt, rows, cols, seed, scale_bits=None):
     if scale_bits is not None:
         key = "s_bits" if fmt == "int4_g128" else "d_bits"
         f[key] = np.broadcast_to(np.asarray(scale_bits, np.uint16), f[key].shape).copy()
-        if fmt == "q4_k":
+        if fmt in MIN_FMTS:
             f["dmin_bits"] = f[key][:, ::-1].copy()
     return f
 
@@ -132,11 +135,11 @@ def pin_roundtrip(fmt):
     # extreme codes
     f = _fields(fmt, rows, cols, 9)
     lo_hi = {"q8_0": ("q", -128, 127), "q4_k": ("u", 0, 15), "q6_k": ("q", 0, 63),
-             "int4_g128": ("q", -8, 7)}[fmt]
+             "int4_g128": ("q", -8, 7), "q5_k": ("u", 0, 31)}[fmt]
     key, lo, hi = lo_hi
     f[key][:, ::2] = lo
     f[key][:, 1::2] = hi
-    if fmt == "q4_k":
+    if fmt in MIN_FMTS:
         f["sc"][...] = 63
         f["m"][:, :, ::2] = 0
     back = oracle.unpack(fmt, oracle.pack(fmt, f, rows, cols), rows, cols)
@@ -153,10 +156,10 @@ def pin_single_rounding(fmt):
         w64 = oracle.dequant64(fmt, data, rows, cols)
         w32 = oracle.dequant32(fmt, data, rows, cols)
         assert np.array_equal(w32, w64.astype(np.float32))
-        if fmt != "q4_k":
+        if fmt not in MIN_FMTS:
             assert np.array_equal(w32.astype(np.float64), w64), "product must be exact in float32"
             continue
-        # Q4_K: the two products are exact in float32, so any order gives the same result.
+        # Q4_K / Q5_K: the two products are exact in float32, so any order gives the same result.
         nb = cols // 256
         d = oracle.fp16_bits_to_f64(f["d_bits"]).astype(np.float32)[:, :, None, None]
         dm = oracle.fp16_bits_to_f64(f["dmin_bits"]).astype(np.float32)[:, :, None, None]
@@ -172,11 +175,11 @@ def pin_single_rounding(fmt):
 def pin_zero_scale(fmt):
     rows, cols = 2, 2 * oracle.QK[fmt]
     f = _fields(fmt, rows, cols, 200, 0x0000)
-    if fmt == "q4_k":
+    if fmt in MIN_FMTS:
         f["dmin_bits"][...] = 0
     w = oracle.dequant64(fmt, oracle.pack(fmt, f, rows, cols), rows, cols)
     assert np.all(w == 0)
-    if fmt == "q4_k":  # d = 0 leaves only the min term
+    if fmt in MIN_FMTS:  # d = 0 leaves only the min term
         f["dmin_bits"][...] = 0x3C00
         w = oracle.dequant64(fmt, oracle.pack(fmt, f, rows, cols), rows, cols)
         want = -np.repeat(f["m"].astype(np.float64).reshape(rows, -1), 32, axis=1)
@@ -187,13 +190,13 @@ def pin_affine_in_code(fmt):
     """All codes equal to c: w(c+1) - w(c) = d*sc exactly; the format's zero point gives 0."""
     rows, cols = 2, oracle.QK[fmt]
     f = _fields(fmt, rows, cols, 300)
-    key = {"q8_0": "q", "q4_k": "u", "q6_k": "q", "int4_g128": "q"}[fmt]
+    key = {"q8_0": "q", "q4_k": "u", "q6_k": "q", "int4_g128": "q", "q5_k": "u"}[fmt]
     rng_c = {"q8_0": range(-128, 127), "q4_k": range(0, 15), "q6_k": range(0, 63),
-             "int4_g128": range(-8, 7)}[fmt]
+             "int4_g128": range(-8, 7), "q5_k": range(0, 31)}[fmt]
     zero = {"q8_0": 0, "q6_k": 32, "int4_g128": 0}
     prev = None
     d = _scale64(fmt, f)[:, 0]
-    if fmt == "q4_k":
+    if fmt in MIN_FMTS:
         slope = np.repeat(d[:, None] * f["sc"][:, 0, :].astype(np.float64), 32, axis=1)
     elif fmt == "q6_k":
         slope = np.repeat(d[:, None] * f["sc"][:, 0, :].astype(np.float64), 16, axis=1)
@@ -206,7 +209,7 @@ def pin_affine_in_code(fmt):
             assert np.array_equal(w - prev, slope), (fmt, c)
         if fmt in zero and c == zero[fmt]:
             assert np.all(w == 0), (fmt, c)
-        if fmt == "q4_k" and c == 0:
+        if fmt in MIN_FMTS and c == 0:
             dmin = oracle.fp16_bits_to_f64(f["dmin_bits"])[:, 0]
             want = -np.repeat(dmin[:, None] * f["m"][:, 0, :].astype(np.float64), 32, axis=1)
             assert np.array_equal(w, want)

@@ -73,6 +73,25 @@ def _q6k_dequant(offset, group):
     return f
 
 
+def _q5k_codes(bit_of, high_weight):
+    def f(qh, qs):
+        low = F.q4_k_qs_to_codes(qs).reshape(qs.shape[:-1] + (8, 32))
+        qh = np.asarray(qh, np.uint8)
+        high = np.stack([(qh >> bit_of(s)) & 1 for s in range(8)], axis=-2)
+        return (low + high * high_weight).astype(np.uint8).reshape(qs.shape[:-1] + (256,))
+    return f
+
+
+def _q5k_unpack_planes_swapped(data, rows, cols):
+    nb = cols // 256
+    blk = data.reshape(rows, nb, 176)
+    sc, m = F.q4_k_bytes_to_scales(blk[:, :, 4:16])
+    return {"d_bits": blk[:, :, 0].astype(np.uint16) | (blk[:, :, 1].astype(np.uint16) << 8),
+            "dmin_bits": blk[:, :, 2].astype(np.uint16) | (blk[:, :, 3].astype(np.uint16) << 8),
+            "sc": sc, "m": m,
+            "u": F.q5_k_bytes_to_codes(blk[:, :, 144:176], blk[:, :, 16:144]).reshape(rows, cols)}
+
+
 def _q8_unpack_big_endian(data, rows, cols):
     nb = cols // 32
     blk = data.reshape(rows, nb, 34)
@@ -120,6 +139,10 @@ MUTANTS = {
     "q6_k ql halves swapped": [(F, "q6_k_bytes_to_codes", _q6k_codes_halves_swapped)],
     "q6_k offset 31": [(F._DEQUANT, "q6_k", _q6k_dequant(31.0, 16))],
     "q6_k sub-blocks of 32": [(F._DEQUANT, "q6_k", _q6k_dequant(32.0, 32))],
+    "q5_k fifth bit at 4h + c": [(F, "q5_k_bytes_to_codes", _q5k_codes(lambda s: 4 * (s & 1) + (s >> 1), 16))],
+    "q5_k fifth bit worth 32": [(F, "q5_k_bytes_to_codes", _q5k_codes(lambda s: s, 32))],
+    "q5_k qs before qh": [(F._UNPACK, "q5_k", _q5k_unpack_planes_swapped)],
+    "q5_k min term dropped": [(F._DEQUANT, "q5_k", _q4k_dequant(0.0))],
     "q8_0 d big-endian": [(F._UNPACK, "q8_0", _q8_unpack_big_endian)],
     "int4 nibbles swapped": [(F._UNPACK, "int4_g128", _int4_unpack(True, 8))],
     "int4 offset 7": [(F._UNPACK, "int4_g128", _int4_unpack(False, 7))],

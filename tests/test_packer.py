@@ -39,7 +39,7 @@ def test_extreme_fields_pack_identically(fmt):
     assert np.array_equal(qmv.pack_fields(fmt, f, rows, cols), oracle.pack(fmt, f, rows, cols))
 
 
-@pytest.mark.parametrize("name", all_names())
+@pytest.mark.parametrize("name", [n for n in all_names() if load(n)["fmt"] in FMTS])
 def test_golden_blocks_repack(name):
     g = load(name)
     f = oracle.unpack(g["fmt"], g["data"], g["rows"], g["cols"])
