@@ -19,7 +19,7 @@ to that kernel's launches, replayed between HIP events on the replay stream.
 `cpu_baseline` times the CPU oracle (float64 decode + dot) on a bounded sample
 of the same matrices.
 
-    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5}] [--batch M]
+    python bench.py [--steps K] [--warmup W] [--config {1,2,3,4,5,6}] [--batch M]
 """
 from __future__ import annotations
 
@@ -49,11 +49,11 @@ def kernel_source_hash() -> str:
 def kernel_name(fmt: str, cols_list, x_dtype: str) -> str:
     """Instantiation the library launches for matrices of these widths in one
     launch (mirrors the launcher: waves per workgroup = max(4, widest K split))."""
-    per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096}[fmt]
+    per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096, "q5_k": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
     cfg = "2, 2, 256" if waves <= 4 else ("2, 2, 512" if waves <= 8 else "1, 2, 1024")
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
-           "int4_g128": "Int4G128Policy"}[fmt]
+           "int4_g128": "Int4G128Policy", "q5_k": "Q5KPolicy"}[fmt]
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
     return f"qmv::gemv_kernel<qmv::{pol}, {xt}, {cfg}>"
 
@@ -129,7 +129,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--batch", type=int, default=None, help="activation rows (config 5 only)")
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)

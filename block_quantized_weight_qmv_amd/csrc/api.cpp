@@ -45,6 +45,7 @@ static int64_t gemv_max_cols(int32_t fmt) {
     case QMV_Q8_0: return 16 * 64 * 32;
     case QMV_Q4_K: return 16 * 16 * 256;
     case QMV_Q6_K: return 16 * 16 * 256;
+    case QMV_Q5_K: return 16 * 16 * 256;
     case QMV_INT4_G128: return 16 * 64 * 64;
     default: return 0;
   }
@@ -82,6 +83,7 @@ int32_t qmv_block_size(int32_t fmt) {
     case QMV_Q8_0: return 32;
     case QMV_Q4_K: return 256;
     case QMV_Q6_K: return 256;
+    case QMV_Q5_K: return 256;
     case QMV_INT4_G128: return 128;
     default: return 0;
   }
@@ -96,6 +98,7 @@ uint64_t qmv_packed_size(int32_t fmt, int64_t rows, int64_t cols) {
     case QMV_Q8_0: return nblk * 34;
     case QMV_Q4_K: return nblk * 144;
     case QMV_Q6_K: return nblk * 210;
+    case QMV_Q5_K: return nblk * 176;
     default: return static_cast<uint64_t>(rows) * cols / 2 + nblk * 2;
   }
 }
@@ -187,6 +190,7 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   switch (fmt) {
     case QMV_Q8_0: e = qmv::gemv_q8_0(calls, n, x_dtype, batch, s); break;
     case QMV_Q4_K: e = qmv::gemv_q4_k(calls, n, x_dtype, batch, s); break;
+    case QMV_Q5_K: e = qmv::gemv_q5_k(calls, n, x_dtype, batch, s); break;
     case QMV_Q6_K: e = qmv::gemv_q6_k(calls, n, x_dtype, batch, s); break;
     default: e = qmv::gemv_int4_g128(calls, n, x_dtype, batch, s); break;
   }

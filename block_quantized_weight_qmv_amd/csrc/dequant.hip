@@ -5,10 +5,13 @@
 // thread decodes four consecutive weights of one row, reading the bytes named
 // by the layout tables below one at a time, and stores them as one vector.
 //
+// Q5_K (hipEngine 0.3.0, "GGUF Support", read as GGUF's published block) is
+// decoded the same way.
+//
 // Exactness: every product here is exact in fp32 (Q8_0 11+7 bits, Q6_K
-// 11 + 12 bits, INT4 11+3 bits, Q4_K d*sc*u 21 bits and dmin*m 17 bits), so
-// the fp32 result is the exact weight, except Q4_K which rounds once at the
-// subtraction.  fp16 / bf16 outputs are that fp32 value rounded to nearest even.
+// 11 + 12 bits, INT4 11+3 bits, Q4_K d*sc*u 21 bits, Q5_K 22 bits, dmin*m
+// 17 bits), so the fp32 result is the exact weight, except Q4_K and Q5_K,
+// which round once at the subtraction.  fp16 / bf16 outputs are that fp32 value rounded to nearest even.
 #include "device_util.h"
 #include "launch.h"
 
@@ -28,25 +31,50 @@ __device__ __forceinline__ void dq_q8_0(const uint8_t* row, int k, float* w) {
   }
 }
 
+// Six-bit scale and min of sub-block s from the twelve scale bytes of a Q4_K or
+// Q5_K block.
+__device__ __forceinline__ void k_scale_min(const uint8_t* sc, int s, uint32_t& scale,
+                                            uint32_t& mn) {
+  if (s < 4) {
+    scale = ld_u8(sc + s) & 63;
+    mn = ld_u8(sc + s + 4) & 63;
+  } else {
+    scale = (ld_u8(sc + s + 4) & 15) | ((ld_u8(sc + s - 4) >> 6) << 4);
+    mn = (ld_u8(sc + s + 4) >> 4) | ((ld_u8(sc + s) >> 6) << 4);
+  }
+}
+
 // Q4_K: d | dmin | scales[12] | qs[128]; t = 64c + 32h + l, u = nibble h of qs[32c+l].
 __device__ __forceinline__ void dq_q4_k(const uint8_t* row, int k, float* w) {
   const uint8_t* b = row + (k / 256) * 144;
   const float d = f16_to_f32(ld_le16(b));
   const float dmin = f16_to_f32(ld_le16(b + 2));
-  const uint8_t* sc = b + 4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
     const int t = (k + e) % 256;
     const int c = t >> 6, h = (t >> 5) & 1, l = t & 31, s = t >> 5;
     uint32_t scale, mn;
-    if (s < 4) {
-      scale = ld_u8(sc + s) & 63;
-      mn = ld_u8(sc + s + 4) & 63;
-    } else {
-      scale = (ld_u8(sc + s + 4) & 15) | ((ld_u8(sc + s - 4) >> 6) << 4);
-      mn = (ld_u8(sc + s + 4) >> 4) | ((ld_u8(sc + s) >> 6) << 4);
-    }
+    k_scale_min(b + 4, s, scale, mn);
     const uint32_t u = (ld_u8(b + 16 + 32 * c + l) >> (4 * h)) & 15;
+    w[e] = (d * static_cast<float>(scale)) * static_cast<float>(u) - dmin * static_cast<float>(mn);
+  }
+}
+
+// Q5_K: d | dmin | scales[12] | qh[32] | qs[128]; t = 64c + 32h + l,
+// u = (nibble h of qs[32c+l]) | (bit 2c+h of qh[l]) << 4.
+__device__ __forceinline__ void dq_q5_k(const uint8_t* row, int k, float* w) {
+  const uint8_t* b = row + (k / 256) * 176;
+  const float d = f16_to_f32(ld_le16(b));
+  const float dmin = f16_to_f32(ld_le16(b + 2));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = (k + e) % 256;
+    const int c = t >> 6, h = (t >> 5) & 1, l = t & 31, s = t >> 5;
+    uint32_t scale, mn;
+    k_scale_min(b + 4, s, scale, mn);
+    const uint32_t lo = (ld_u8(b + 48 + 32 * c + l) >> (4 * h)) & 15;
+    const uint32_t hi = (ld_u8(b + 16 + l) >> s) & 1;
+    const uint32_t u = lo | (hi << 4);
     w[e] = (d * static_cast<float>(scale)) * static_cast<float>(u) - dmin * static_cast<float>(mn);
   }
 }
@@ -103,6 +131,8 @@ dequant_kernel(const uint8_t* __restrict__ w, uint64_t scales_offset, int rows, 
       dq_q8_0(w + static_cast<size_t>(r) * (cols / 32) * 34, k, v);
     } else if (FMT == QMV_Q4_K) {
       dq_q4_k(w + static_cast<size_t>(r) * (cols / 256) * 144, k, v);
+    } else if (FMT == QMV_Q5_K) {
+      dq_q5_k(w + static_cast<size_t>(r) * (cols / 256) * 176, k, v);
     } else if (FMT == QMV_Q6_K) {
       dq_q6_k(w + static_cast<size_t>(r) * (cols / 256) * 210, k, v);
     } else {
@@ -152,6 +182,7 @@ hipError_t dequant(const qmv_weights& W, void* out, int out_dtype, hipStream_t s
   switch (W.fmt) {
     case QMV_Q8_0: return dequant_fmt<QMV_Q8_0>(W, out, out_dtype, s);
     case QMV_Q4_K: return dequant_fmt<QMV_Q4_K>(W, out, out_dtype, s);
+    case QMV_Q5_K: return dequant_fmt<QMV_Q5_K>(W, out, out_dtype, s);
     case QMV_Q6_K: return dequant_fmt<QMV_Q6_K>(W, out, out_dtype, s);
     case QMV_INT4_G128: return dequant_fmt<QMV_INT4_G128>(W, out, out_dtype, s);
     default: return hipErrorInvalidValue;

@@ -24,6 +24,7 @@ constexpr int64_t kMaxBatch = 65535;
 
 hipError_t gemv_q8_0(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
 hipError_t gemv_q4_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
+hipError_t gemv_q5_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
 hipError_t gemv_q6_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
 hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                           hipStream_t s);

@@ -18,7 +18,7 @@ import numpy as np
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG_DIR, "libqmv.so")
 
-FMT = {"q8_0": 1, "q4_k": 2, "q6_k": 3, "int4_g128": 4}
+FMT = {"q8_0": 1, "q4_k": 2, "q6_k": 3, "int4_g128": 4, "q5_k": 5}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
 
 QMV_OK = 0
@@ -54,6 +54,7 @@ _SIGS = {
     "qmv_packed_size": (_u64, [_i32, _i64, _i64]),
     "qmv_pack_q8_0": (_i32, [_p, _p, _i64, _i64, _p, _u64]),
     "qmv_pack_q4_k": (_i32, [_p, _p, _p, _p, _p, _i64, _i64, _p, _u64]),
+    "qmv_pack_q5_k": (_i32, [_p, _p, _p, _p, _p, _i64, _i64, _p, _u64]),
     "qmv_pack_q6_k": (_i32, [_p, _p, _p, _i64, _i64, _p, _u64]),
     "qmv_pack_int4_g128": (_i32, [_p, _p, _i64, _i64, _p, _u64]),
     "qmv_create_weights": (_i32, [_i32, _i64, _i64, _p, _u64, ctypes.POINTER(QmvWeights)]),
@@ -163,6 +164,15 @@ def qmv_pack_q4_k(d_bits, dmin_bits, sc6, m6, q4, rows: int, cols: int) -> np.nd
     return out
 
 
+def qmv_pack_q5_k(d_bits, dmin_bits, sc6, m6, q5, rows: int, cols: int) -> np.ndarray:
+    d, dm = _c(d_bits, np.uint16), _c(dmin_bits, np.uint16)
+    sc, m, q = _c(sc6, np.uint8), _c(m6, np.uint8), _c(q5, np.uint8)
+    out = _pack_out("q5_k", rows, cols)
+    _check(lib().qmv_pack_q5_k(_ptr(d), _ptr(dm), _ptr(sc), _ptr(m), _ptr(q), rows, cols,
+                               _ptr(out), out.size))
+    return out
+
+
 def qmv_pack_q6_k(d_bits, sc8, q6, rows: int, cols: int) -> np.ndarray:
     d, sc, q = _c(d_bits, np.uint16), _c(sc8, np.int8), _c(q6, np.uint8)
     out = _pack_out("q6_k", rows, cols)
@@ -182,6 +192,9 @@ def pack_fields(fmt: str, fields: dict, rows: int, cols: int) -> np.ndarray:
         return qmv_pack_q8_0(fields["d_bits"], fields["q"], rows, cols)
     if fmt == "q4_k":
         return qmv_pack_q4_k(fields["d_bits"], fields["dmin_bits"], fields["sc"], fields["m"],
+                             fields["u"], rows, cols)
+    if fmt == "q5_k":
+        return qmv_pack_q5_k(fields["d_bits"], fields["dmin_bits"], fields["sc"], fields["m"],
                              fields["u"], rows, cols)
     if fmt == "q6_k":
         return qmv_pack_q6_k(fields["d_bits"], fields["sc"], fields["q"], rows, cols)

@@ -26,6 +26,11 @@
  *         j<4:  sc_j = scales[j]&63, m_j = scales[j+4]&63
  *         j>=4: sc_j = (scales[j+4]&15) | (scales[j-4]>>6)<<4,
  *               m_j  = (scales[j+4]>>4) | (scales[j]>>6)<<4
+ *     Q5_K (QK 256, 176 B): d fp16 | dmin fp16 | scales[12] as Q4_K |
+ *         qh[32] | qs[128] as Q4_K.  hipEngine 0.3.0, "GGUF Support", counts
+ *         the type in a Q4_K_M file's payload; the bytes are GGUF's published
+ *         Q5_K block.  Weight t = 64c+32h+l: u = (nibble h of qs[32c+l]) |
+ *         (bit 2c+h of qh[l]) << 4 in 0..31, w_t = d*sc_s*u - dmin*m_s.
  *     Q6_K (QK 256, 210 B): ql[128] | qh[64] | sc[16] int8 | d fp16.
  *         Weight t = 128h+32g+l: low4 = nibble (g>>1) of ql[64h+32(g&1)+l],
  *         high2 = bits 2g..2g+1 of qh[32h+l], q6 = low4 | high2<<4,
@@ -60,7 +65,8 @@ enum {
   QMV_Q8_0 = 1,
   QMV_Q4_K = 2,
   QMV_Q6_K = 3,
-  QMV_INT4_G128 = 4
+  QMV_INT4_G128 = 4,
+  QMV_Q5_K = 5
 };
 
 enum { QMV_F32 = 0, QMV_F16 = 1, QMV_BF16 = 2 };
@@ -83,7 +89,7 @@ enum {
  * caller-owned; it only points at the packed bytes, which must stay alive
  * (and unmodified) until every enqueued call that reads them has finished. */
 typedef struct qmv_weights {
-  int32_t fmt;            /* QMV_Q8_0 .. QMV_INT4_G128                       */
+  int32_t fmt;            /* QMV_Q8_0 .. QMV_Q5_K                            */
   int32_t reserved;       /* 0                                               */
   int64_t rows, cols;     /* logical shape of W                              */
   const void* data;       /* device pointer to the packed bytes (16 B aligned)*/
@@ -92,7 +98,8 @@ typedef struct qmv_weights {
                           /* for the block formats                           */
 } qmv_weights;
 
-/* Codes per block: 32, 256, 256, 128; 0 for an unknown format. */
+/* Codes per block: 32, 256, 256, 128, 256 (Q8_0, Q4_K, Q6_K, INT4_G128,
+ * Q5_K); 0 for an unknown format. */
 int32_t qmv_block_size(int32_t fmt);
 
 /* Bytes of a packed rows x cols tensor; 0 if fmt is unknown, rows or cols < 1
@@ -113,6 +120,13 @@ int32_t qmv_pack_q8_0(const uint16_t* d_bits, const int8_t* q, int64_t rows,
  * in 0..63; q4 [rows][cols] in 0..15. */
 int32_t qmv_pack_q4_k(const uint16_t* d_bits, const uint16_t* dmin_bits,
                       const uint8_t* sc6, const uint8_t* m6, const uint8_t* q4,
+                      int64_t rows, int64_t cols, uint8_t* out,
+                      uint64_t out_bytes);
+
+/* Q5_K: d_bits, dmin_bits [rows][cols/256]; sc6, m6 [rows][cols/256][8] each
+ * in 0..63; q5 [rows][cols] in 0..31. */
+int32_t qmv_pack_q5_k(const uint16_t* d_bits, const uint16_t* dmin_bits,
+                      const uint8_t* sc6, const uint8_t* m6, const uint8_t* q5,
                       int64_t rows, int64_t cols, uint8_t* out,
                       uint64_t out_bytes);
 

@@ -135,6 +135,10 @@ CONFIGS = {
         "mats": [("lm_head", VOCAB, HIDDEN)]},
     5: {"name": "q4_k_batched_ffn_7b", "fmt": "q4_k", "x_dtype": "bf16",
         "batch": [1, 4, 16, 64, 512], "mats": [("gate", FFN, HIDDEN)]},
+    # Q5_K holds the expert-down projections of a Q4_K_M file (hipEngine 0.3.0,
+    # "GGUF Support", payload table); the 7B down shape stands in for them.
+    6: {"name": "q5_k_ffn_down_7b", "fmt": "q5_k", "x_dtype": "f32", "batch": [1],
+        "mats": [("down", HIDDEN, FFN)]},
 }
 
 

@@ -30,12 +30,13 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_block_and_packed_sizes():
-    assert [qmv.qmv_block_size(f) for f in ("q8_0", "q4_k", "q6_k", "int4_g128")] == [32, 256, 256, 128]
-    assert qmv.qmv_block_size(0) == 0 and qmv.qmv_block_size(5) == 0
+    assert [qmv.qmv_block_size(f) for f in ("q8_0", "q4_k", "q6_k", "int4_g128", "q5_k")] == [32, 256, 256, 128, 256]
+    assert qmv.qmv_block_size(0) == 0 and qmv.qmv_block_size(6) == 0
     assert qmv.qmv_packed_size("q8_0", 1536, 1536) == 2_506_752
     assert qmv.qmv_packed_size("q4_k", 18944, 3584) == 38_191_104
     assert qmv.qmv_packed_size("q6_k", 152064, 3584) == 447_068_160
     assert qmv.qmv_packed_size("int4_g128", 3584, 18944) == 35_008_512
+    assert qmv.qmv_packed_size("q5_k", 3584, 18944) == 46_678_016
     for bad in [(0, 256), (1, 0), (1, 255), (-1, 256)]:
         assert qmv.qmv_packed_size("q4_k", *bad) == 0
 

@@ -9,7 +9,7 @@ from gpu_util import DEV, Weights, say
 
 pytestmark = pytest.mark.gpu
 
-FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128", "q5_k")
 SHAPES = [(1, 1), (3, 2), (37, 14), (130, 17), (5, 74)]
 
 
@@ -53,10 +53,10 @@ def test_dequant_edge_scales(fmt):
     f = gen_weights(fmt, rows, cols, 5)
     sk = "s_bits" if fmt == "int4_g128" else "d_bits"
     f[sk][...] = np.resize(np.array([0x0000, 0x0001, 0x03FF, 0x7BFF, 0xBC00, 0x8001], np.uint16), f[sk].shape)
-    if fmt == "q4_k":
+    if fmt in ("q4_k", "q5_k"):
         f["dmin_bits"][...] = np.resize(np.array([0x7BFF, 0x0000, 0x0001, 0x3C00], np.uint16), f["dmin_bits"].shape)
     key, lo, hi = {"q8_0": ("q", -128, 127), "q4_k": ("u", 0, 15), "q6_k": ("q", 0, 63),
-                   "int4_g128": ("q", -8, 7)}[fmt]
+                   "int4_g128": ("q", -8, 7), "q5_k": ("u", 0, 31)}[fmt]
     f[key][::2] = lo
     f[key][1::2] = hi
     w = Weights(fmt, rows, cols, fields=f)

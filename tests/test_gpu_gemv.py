@@ -18,13 +18,14 @@ from synth import CONFIGS, gen_weights, gen_x, weight_seed, x_seed
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128", "q5_k")
 # (rows, blocks per row): single block, ragged wave tiles, several waves along K
 SHAPES = {
     "q8_0": [(1, 1), (5, 3), (67, 48), (33, 65), (9, 200)],
     "q4_k": [(1, 1), (5, 3), (67, 14), (33, 17), (9, 74)],
     "q6_k": [(1, 1), (5, 3), (67, 14), (33, 17), (9, 74)],
     "int4_g128": [(1, 1), (5, 3), (67, 28), (33, 33), (9, 148)],
+    "q5_k": [(1, 1), (5, 3), (67, 14), (33, 17), (9, 74)],
 }
 CASES = [(f, r, n) for f in FMTS for (r, n) in SHAPES[f]]
 
@@ -66,7 +67,7 @@ def test_unit_vectors_extract_columns_exactly(fmt):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_integer_case_is_exact(fmt):
     """Scales 1 and x in {-1, 0, 1}: every float32 partial sum is an exact integer."""
-    rows, nblk = 40, {"q8_0": 70, "q4_k": 20, "q6_k": 20, "int4_g128": 40}[fmt]
+    rows, nblk = 40, {"q8_0": 70, "q4_k": 20, "q6_k": 20, "int4_g128": 40, "q5_k": 20}[fmt]
     cols = nblk * oracle.QK[fmt]
     f = gen_weights(fmt, rows, cols, 8)
     for k in ("d_bits", "dmin_bits", "s_bits"):
@@ -142,7 +143,7 @@ def _sample_rows(rows, n=48, seed=0):
     return ids
 
 
-@pytest.mark.parametrize("config", [1, 2, 3, 4])
+@pytest.mark.parametrize("config", [1, 2, 3, 4, 6])
 def test_full_size_configs_sampled_rows(config):
     cfg = CONFIGS[config]
     for i, (name, rows, cols) in enumerate(cfg["mats"]):

@@ -7,7 +7,7 @@ from block_quantized_weight_qmv_amd import qmv
 from golden_io import all_names, load
 from synth import gen_weights
 
-FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128", "q5_k")
 
 
 @pytest.mark.parametrize("fmt", FMTS)
@@ -25,12 +25,12 @@ def test_extreme_fields_pack_identically(fmt):
     rows, cols = 4, 2 * oracle.QK[fmt]
     f = gen_weights(fmt, rows, cols, seed=11)
     key, lo, hi = {"q8_0": ("q", -128, 127), "q4_k": ("u", 0, 15), "q6_k": ("q", 0, 63),
-                   "int4_g128": ("q", -8, 7)}[fmt]
+                   "int4_g128": ("q", -8, 7), "q5_k": ("u", 0, 31)}[fmt]
     f[key][0::2] = lo
     f[key][1::2] = hi
     sk = "s_bits" if fmt == "int4_g128" else "d_bits"
     f[sk][...] = np.array([0x0000, 0x0001, 0x7BFF, 0x8000][: f[sk].shape[1]] * 4, np.uint16)[: f[sk].size].reshape(f[sk].shape)
-    if fmt == "q4_k":
+    if fmt in ("q4_k", "q5_k"):
         f["sc"][...] = 63
         f["m"][0] = 0
     if fmt == "q6_k":
@@ -39,7 +39,7 @@ def test_extreme_fields_pack_identically(fmt):
     assert np.array_equal(qmv.pack_fields(fmt, f, rows, cols), oracle.pack(fmt, f, rows, cols))
 
 
-@pytest.mark.parametrize("name", [n for n in all_names() if load(n)["fmt"] in FMTS])
+@pytest.mark.parametrize("name", all_names())
 def test_golden_blocks_repack(name):
     g = load(name)
     f = oracle.unpack(g["fmt"], g["data"], g["rows"], g["cols"])
@@ -48,6 +48,7 @@ def test_golden_blocks_repack(name):
 
 @pytest.mark.parametrize("fmt,field,value", [
     ("q4_k", "u", 16), ("q4_k", "sc", 64), ("q4_k", "m", 64), ("q6_k", "q", 64),
+    ("q5_k", "u", 32), ("q5_k", "sc", 64), ("q5_k", "m", 64),
     ("int4_g128", "q", 8), ("int4_g128", "q", -9)])
 def test_range_errors(fmt, field, value):
     rows, cols = 2, oracle.QK[fmt]
