@@ -38,17 +38,39 @@ COUNTERS_FILE = os.path.join(ROOT, "profiles", "counters.json")
 CSRC = os.path.join(ROOT, "block_quantized_weight_qmv_amd", "csrc")
 
 
-def kernel_source_hash() -> str:
+# Sources each kernel family is built from: a change to any of them voids the
+# committed counter figures for that family (and only for it).
+_KERNEL_SOURCES = {
+    "gemv_kernel": ["gemv_skeleton.h", "device_util.h"],
+    "gemm_q4_k_bf16_kernel": ["gemm_q4_k_mfma.hip", "device_util.h"],
+}
+_POLICY_SOURCE = {"Q80Policy": "gemv_q8_0.hip", "Q4KPolicy": "gemv_q4_k.hip",
+                  "Q5KPolicy": "gemv_q5_k.hip", "Q6KPolicy": "gemv_q6_k.hip",
+                  "Int4G128Policy": "gemv_int4_g128.hip"}
+
+
+def kernel_source_hash(kernel: str) -> str:
+    """Hash of the source files the named kernel instantiation is compiled from."""
+    fam = kernel.split("::")[1].split("<")[0] if "::" in kernel else kernel
+    files = list(_KERNEL_SOURCES.get(fam, sorted(os.listdir(CSRC))))
+    for pol, src in _POLICY_SOURCE.items():
+        if pol in kernel:
+            files.append(src)
     h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
+    for name in sorted(files):
         with open(os.path.join(CSRC, name), "rb") as fh:
             h.update(name.encode() + b"\0" + fh.read())
     return h.hexdigest()[:16]
 
 
-def kernel_name(fmt: str, cols_list, x_dtype: str) -> str:
+def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
     """Instantiation the library launches for matrices of these widths in one
-    launch (mirrors the launcher: waves per workgroup = max(4, widest K split))."""
+    launch (mirrors the dispatch in api.cpp and the GEMV launcher: Q4_K x bf16
+    with batch >= 3 -> matrix-core kernel, M tile by batch; otherwise waves per
+    workgroup = max(4, widest K split))."""
+    if fmt == "q4_k" and x_dtype == "bf16" and batch >= 3:
+        mb = 1 if batch <= 16 else (2 if batch <= 32 else 4)
+        return f"qmv::gemm_q4_k_bf16_kernel<{mb}>"
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096, "q5_k": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
     cfg = "2, 2, 256" if waves <= 4 else ("2, 2, 512" if waves <= 8 else "1, 2, 1024")
@@ -83,7 +105,7 @@ def measured_traffic(kernel: str, workload: str):
     except (OSError, ValueError):
         return None
     rec = data.get(workload, {})
-    if rec.get("kernel") != kernel or rec.get("source_hash") != kernel_source_hash():
+    if rec.get("kernel") != kernel or rec.get("source_hash") != kernel_source_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -124,6 +146,155 @@ def cpu_baseline(mats, fmt, x_dtype, fields_list, xs, seconds):
                        f"matrix-vector product (BLAS, {blas_threads} threads); packing excluded")}
 
 
+PEAK_TFLOPS_BF16 = 2500.0   # MI355X dense bf16 matrix cores, vendor figure
+
+
+def workload_plan(config: int, batch: int | None, separate: bool) -> dict:
+    """Launches of one step and their algorithmic bytes and flops (no GPU needed).
+
+    Bytes per launch = packed weights + each activation once + y; flops =
+    2 * batch * rows * cols over the launch's matrices.  Each launch's bound is
+    the roofline the kernel runs against: matrix cores when its arithmetic
+    intensity exceeds the machine balance (dense bf16 peak / HBM peak), HBM
+    otherwise."""
+    from block_quantized_weight_qmv_amd import qmv
+    from synth import CONFIGS
+    cfg = CONFIGS[config]
+    fmt, x_dtype = cfg["fmt"], cfg["x_dtype"]
+    batch = batch or cfg["batch"][0]
+    mats = cfg["mats"]
+    names = [n for n, _, _ in mats]
+    groups = [[m] for m in range(len(mats))] if separate else decode_groups(names)
+    xb = {"f32": 4, "f16": 2, "bf16": 2}[x_dtype]
+    wbytes = [int(qmv.qmv_packed_size(fmt, r, c)) for _, r, c in mats]
+    gbytes = [sum(wbytes[m] + batch * mats[m][1] * 4 for m in g) + batch * mats[g[0]][2] * xb
+              for g in groups]
+    gflops = [sum(2.0 * batch * mats[m][1] * mats[m][2] for m in g) for g in groups]
+    kname = [kernel_name(fmt, [mats[m][2] for m in g], x_dtype, batch) for g in groups]
+    balance = PEAK_TFLOPS_BF16 * 1e12 / (PEAK_GBPS * 1e9)
+    bound = ["mfma" if kname[i].startswith("qmv::gemm") and gflops[i] / gbytes[i] > balance
+             else "hbm" for i in range(len(groups))]
+    by_kernel = {}
+    for gi in range(len(groups)):
+        by_kernel.setdefault(kname[gi], []).append(gi)
+    dom = max(by_kernel, key=lambda k: sum(gbytes[gi] for gi in by_kernel[k]))
+    workload = cfg["name"] + (f"_m{batch}" if config == 5 else "")
+    return {"cfg": cfg, "fmt": fmt, "x_dtype": x_dtype, "batch": batch, "mats": mats,
+            "names": names, "groups": groups, "wbytes": wbytes, "gbytes": gbytes,
+            "gflops": gflops, "kname": kname, "bound": bound, "by_kernel": by_kernel,
+            "dom": dom, "workload": workload,
+            "launch_names": ["+".join(names[m] for m in g) for g in groups]}
+
+
+def _counter_csv(d: str):
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    return files
+
+
+def _per_dispatch(d: str, counter: str):
+    """[(kernel name without 'void ' and arguments, summed counter value)] in dispatch order."""
+    import csv
+    acc = {}
+    for f in _counter_csv(d):
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                key = (f, int(r["Dispatch_Id"]))
+                name = r["Kernel_Name"].split("(")[0]
+                name = name[5:] if name.startswith("void ") else name
+                prev = acc.get(key, (name, 0.0, int(r.get("Grid_Size", 0) or 0)))
+                acc[key] = (name, prev[1] + float(r["Counter_Value"]), prev[2])
+    return [acc[k] for k in sorted(acc)]
+
+
+def summarize_counters(args) -> int:
+    """Turn four rocprofv3 --pmc runs into HBM bytes per launch (profiles/counters.json).
+
+    Runs: FETCH_SIZE and WRITE_SIZE of `bench.py --eager-pass` for the workload,
+    and of `python -m block_quantized_weight_qmv_amd.probe copy --mib N` for the
+    scale factors (a copy of N MiB reads and writes N MiB)."""
+    fetch_d, write_d, cfetch_d, cwrite_d = args.summarize_counters
+    plan = workload_plan(args.config, args.batch, args.separate)
+    groups, kname, gbytes = plan["groups"], plan["kname"], plan["gbytes"]
+    copy_kib = args.copy_mib * 1024.0
+
+    def copy_mean(d, counter):
+        v = [val for name, val, _ in _per_dispatch(d, counter) if "probe_copy" in name]
+        v = v[1:] or v
+        return sum(v) / len(v)
+    fetch_scale = copy_kib / copy_mean(cfetch_d, "FETCH_SIZE")
+    write_scale = copy_kib / copy_mean(cwrite_d, "WRITE_SIZE")
+
+    # expected dispatch sequence of one step: the GEMV kernel once per launch,
+    # the matrix-core kernel once per matrix
+    seq = []
+    for gi, g in enumerate(groups):
+        seq += [gi] * (len(g) if kname[gi].startswith("qmv::gemm") else 1)
+    per_launch = []
+    for counter, d in (("FETCH_SIZE", fetch_d), ("WRITE_SIZE", write_d)):
+        ds = [x for x in _per_dispatch(d, counter) if x[0].startswith("qmv::")]
+        n_steps = len(ds) // len(seq)
+        if n_steps * len(seq) != len(ds) or n_steps <= args.warmup:
+            raise SystemExit(f"{counter}: {len(ds)} qmv dispatches, not a whole number of "
+                             f"{len(seq)}-dispatch steps after {args.warmup} warmup steps")
+        sums = [[0.0, 0, 0] for _ in groups]
+        for i, (name, val, grid) in enumerate(ds):
+            gi = seq[i % len(seq)]
+            if name != kname[gi]:
+                raise SystemExit(f"dispatch {i}: kernel {name!r}, expected {kname[gi]!r}")
+            if i // len(seq) >= args.warmup:
+                sums[gi][0] += val
+                sums[gi][1] += 1
+                sums[gi][2] = grid
+        steps = n_steps - args.warmup
+        for gi in range(len(groups)):
+            if counter == "FETCH_SIZE":
+                per_launch.append({"kernel": kname[gi], "launch": plan["launch_names"][gi],
+                                   "grid": sums[gi][2]})
+            per_launch[gi][counter.split("_")[0].lower() + "_kib"] = round(sums[gi][0] / steps, 3)
+    for gi, pl in enumerate(per_launch):
+        pl["fetch_bytes"] = round(pl["fetch_kib"] * 1024 * fetch_scale)
+        pl["write_bytes"] = round(pl["write_kib"] * 1024 * write_scale)
+        pl["algorithmic_bytes"] = int(gbytes[gi])
+        pl["ratio"] = round((pl["fetch_bytes"] + pl["write_bytes"]) / gbytes[gi], 4)
+    dom = plan["dom"]
+    gis = plan["by_kernel"][dom]
+
+    def avg(key):
+        return sum(per_launch[gi][key] for gi in gis) / len(gis)
+    rec = {"kernel": dom, "source_hash": kernel_source_hash(dom), "launches_per_step": len(gis),
+           "hbm_bytes_per_launch": round(avg("fetch_bytes") + avg("write_bytes")),
+           "fetch_bytes_per_launch": round(avg("fetch_bytes")),
+           "write_bytes_per_launch": round(avg("write_bytes")),
+           "algorithmic_bytes_per_launch": round(avg("algorithmic_bytes")),
+           "fetch_scale": round(fetch_scale, 5), "write_scale": round(write_scale, 5),
+           "per_launch": per_launch, "summary": args.summary_file}
+    try:
+        with open(COUNTERS_FILE) as fh:
+            data = json.load(fh)
+    except (OSError, ValueError):
+        data = {}
+    data[plan["workload"]] = rec
+    with open(COUNTERS_FILE, "w") as fh:
+        json.dump(data, fh, indent=1)
+        fh.write("\n")
+    print(f"scale: HBM bytes = {fetch_scale:.5f} x FETCH_SIZE x 1024 + {write_scale:.5f} x WRITE_SIZE x 1024")
+    print("| kernel | launch | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes | algorithmic bytes | ratio |")
+    print("|---|---|---:|---:|---:|---:|---:|")
+    for pl in per_launch:
+        print(f"| `{pl['kernel']}` | {pl['launch']} | {pl['fetch_kib']:.1f} | {pl['write_kib']:.1f} | "
+              f"{pl['fetch_bytes'] + pl['write_bytes']} | {pl['algorithmic_bytes']} | {pl['ratio']:.3f} |")
+    print(f"dominant `{dom}`: {rec['hbm_bytes_per_launch']} HBM bytes per launch, "
+          f"{rec['algorithmic_bytes_per_launch']} algorithmic (ratio "
+          f"{rec['hbm_bytes_per_launch'] / rec['algorithmic_bytes_per_launch']:.3f}); "
+          f"source hash {rec['source_hash']}")
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -137,7 +308,14 @@ def main() -> int:
     ap.add_argument("--separate", action="store_true", help="one launch per matrix")
     ap.add_argument("--eager-pass", action="store_true",
                     help="only issue warmup + steps eagerly (no graphs, no timing): for counter runs")
+    ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                    help="rocprofv3 --pmc output dirs of the eager pass (same --config/--batch/"
+                         "--separate/--warmup) and of the probe copy: write profiles/counters.json")
+    ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy")
+    ap.add_argument("--summary-file", default="", help="profiles/ summary recorded with the counters")
     args = ap.parse_args()
+    if args.summarize_counters:
+        return summarize_counters(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -153,19 +331,12 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = CONFIGS[args.config]
-    fmt, x_dtype = cfg["fmt"], cfg["x_dtype"]
-    batch = args.batch or cfg["batch"][0]
-    mats = cfg["mats"]
-    xb = {"f32": 4, "f16": 2, "bf16": 2}[x_dtype]
+    plan = workload_plan(args.config, args.batch, args.separate)
+    cfg, fmt, x_dtype, batch = plan["cfg"], plan["fmt"], plan["x_dtype"], plan["batch"]
+    mats, names, groups = plan["mats"], plan["names"], plan["groups"]
+    gbytes, gflops, kname, by_kernel, dom = (plan["gbytes"], plan["gflops"], plan["kname"],
+                                             plan["by_kernel"], plan["dom"])
     tdt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[x_dtype]
-
-    # -- launch groups: projections that read the same activation share a launch --
-    names = [n for n, _, _ in mats]
-    if args.separate:
-        groups = [[m] for m in range(len(mats))]
-    else:
-        groups = decode_groups(names)
 
     # -- inputs: synthesize, pack on the host with the library packer, upload ---
     fields_list, packed_dev, xs, xs_dev, ys = [], [], [], [], []
@@ -184,9 +355,7 @@ def main() -> int:
             xs_dev.append(xs_dev[leader[i]])
         ys.append(torch.empty(batch, rows, dtype=torch.float32, device=dev))
     step_w_bytes = sum(p.numel() for p in packed_dev)
-    # algorithmic bytes: packed weights, each activation once per launch, y
-    gbytes = [sum(packed_dev[m].numel() + batch * mats[m][1] * 4 for m in g)
-              + batch * mats[g[0]][2] * xb for g in groups]
+    assert step_w_bytes == sum(plan["wbytes"])
     step_bytes = sum(gbytes)
     copies = max(1, int(np.ceil(args.rotate_gib * 2 ** 30 / step_w_bytes)))
     descs = []  # descs[c][m]
@@ -212,12 +381,8 @@ def main() -> int:
             qmv.qmv_gemv_multi(fmt, x_dtype, batch,
                                [(descs[c][m], xs_dev[m], ys[m]) for m in g], sptr)
 
-    # dominant kernel: the instantiation with the most algorithmic bytes per step
-    kname = [kernel_name(fmt, [mats[m][2] for m in g], x_dtype) for g in groups]
-    by_kernel = {}
-    for gi in range(len(groups)):
-        by_kernel.setdefault(kname[gi], []).append(gi)
-    dom = max(by_kernel, key=lambda k: sum(gbytes[gi] for gi in by_kernel[k]))
+    # dominant kernel (plan["dom"]): the instantiation with the most algorithmic
+    # bytes per step
 
     for s in range(args.warmup):
         for g in groups:
@@ -280,7 +445,12 @@ def main() -> int:
         per_launch = None
     dom_avg_us = kern[dom]["avg_launch_us"]
     dom_bytes_per_launch = kern[dom]["bytes_per_launch"]
-    achieved = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9
+    dom_flops_per_launch = sum(gflops[gi] for gi in by_kernel[dom]) / len(by_kernel[dom])
+    dom_bound = plan["bound"][by_kernel[dom][0]]
+    if dom_bound == "mfma":
+        achieved, peak, unit = dom_flops_per_launch / (dom_avg_us * 1e-6) / 1e12, PEAK_TFLOPS_BF16, "TFLOP/s"
+    else:
+        achieved, peak, unit = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9, PEAK_GBPS, "GB/s"
     detail = kern
 
     # -- HBM read ceiling on this GPU (128-bit streaming read of 2 GiB) ----------------
@@ -299,7 +469,7 @@ def main() -> int:
     read_ceiling = nb * 10 / (a.elapsed_time(b) * 1e-3) / 1e9
     del buf, out
 
-    workload = cfg["name"] + (f"_m{batch}" if args.config == 5 else "")
+    workload = plan["workload"]
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     rec = {
         "metric": "achieved HBM GB/s (% of peak) and µs per GEMV, batch-1 7B-shaped Q4_K",
@@ -312,7 +482,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp32",
+        "dtype": "bf16" if dom.startswith("qmv::gemm") else "fp32",
         "data": "synthetic",
         "config": {"workload": workload, "format": fmt, "batch": batch, "x_dtype": x_dtype,
                    "matrices": {n: f"{r}x{c}" for n, r, c in mats},
@@ -323,14 +493,15 @@ def main() -> int:
         "per_kernel": detail,
         "per_launch": per_launch,
         "read_ceiling_GBps": round(read_ceiling, 1),
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBPS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_GBPS, 4),
+        "roofline": {"bound": dom_bound, "achieved": round(achieved, 1), "peak": peak,
+                     "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(dom, workload),
                      "kernel": dom, "avg_launch_us": round(dom_avg_us, 3),
                      "launches_per_step": len(by_kernel[dom]),
                      "timing": "HIP events around a graph replay of the K steps restricted "
                                "to this kernel's launches, on the replay stream",
-                     "bytes_per_launch": round(dom_bytes_per_launch, 1)},
+                     "bytes_per_launch": round(dom_bytes_per_launch, 1),
+                     "flops_per_launch": round(dom_flops_per_launch, 1)},
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(mats, fmt, x_dtype, fields_list, xs, args.cpu_seconds)
