@@ -116,4 +116,27 @@ __device__ __forceinline__ void x_to_f32(const uint4* raw, float* out, const bf1
   }
 }
 
+// Host side: compute units and LDS bytes per workgroup of the current device,
+// queried once per device (gfx950: 256 CUs, 160 KB).
+inline int device_attr_cached(hipDeviceAttribute_t attr, int (&cache)[64], int fallback) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
+  if (cache[dev] == 0) {
+    int v = 0;
+    if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) v = fallback;
+    cache[dev] = v;
+  }
+  return cache[dev];
+}
+
+inline int device_cus() {
+  static int cache[64];
+  return device_attr_cached(hipDeviceAttributeMultiprocessorCount, cache, 256);
+}
+
+inline int device_lds_per_block() {
+  static int cache[64];
+  return device_attr_cached(hipDeviceAttributeMaxSharedMemoryPerBlock, cache, 65536);
+}
+
 }  // namespace qmv

@@ -305,20 +305,6 @@ inline int64_t resident_workgroups(K kernel, int block) {
 constexpr int kMaxWavesPerSimd = QMV_WAVES_PER_SIMD;
 constexpr int kMinRowsPerWave = QMV_MIN_ROWS_PER_WAVE;
 
-inline int device_cus() {
-  static int cache[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
-    int cus = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        cus <= 0)
-      cus = 256;
-    cache[dev] = cus;
-  }
-  return cache[dev];
-}
-
 template <class P, typename XT, int R, int D, int MAXT>
 hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream,
                       int waves_per_simd) {

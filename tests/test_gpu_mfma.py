@@ -4,10 +4,12 @@ Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
 sub-block scales are applied in fp32, so results are not bitwise those of the
 fp32 GEMV; inputs whose products and sums are small integers are exact on both
-paths and are checked exactly.  Shapes cover every batch tiling (batch tiles of
-16, 32 and 64 rows, ragged in rows and in batch, several tiles along the
-batch), the smallest batch routed here (3), and the full-size batched workload
-(18944 x 3584, M = 4, 16, 64 and 512) on sampled rows.
+paths and are checked exactly.  Shapes cover the three kernels behind the call
+(batch <= 16 with X in LDS: one to eight 16-row tiles per workgroup and more
+workgroups than CUs; batch <= 32 or K too long for LDS: K split over waves;
+larger batches: 64 x 64 tiles), ragged rows and batches, the smallest batch
+routed here (3), and the full-size batched workload (18944 x 3584, M = 4, 16,
+64 and 512) on sampled rows.
 """
 import numpy as np
 import pytest
@@ -24,7 +26,9 @@ TOL = 2e-3
 
 @pytest.mark.parametrize("rows,nblk,batch", [(64, 1, 64), (67, 14, 64), (130, 3, 65), (33, 5, 100),
                                              (200, 14, 128), (1, 2, 64), (70, 3, 3), (67, 5, 4),
-                                             (96, 2, 16), (65, 3, 17), (40, 2, 32), (33, 4, 33)])
+                                             (96, 2, 16), (65, 3, 17), (40, 2, 32), (33, 4, 33),
+                                             (17, 74, 8), (300, 9, 24), (1, 1, 3), (16, 1, 31),
+                                             (4100, 2, 5), (40000, 1, 9), (3, 16, 16), (33, 17, 12)])
 def test_mfma_matches_oracle(rows, nblk, batch):
     cols = nblk * 256
     say(f"mfma q4_k {rows}x{cols} batch {batch}")
@@ -55,8 +59,9 @@ def test_mfma_integer_case_is_exact():
     np.testing.assert_array_equal(y, y64.astype(np.float32))
 
 
-def test_mfma_deterministic_and_graph_replay():
-    rows, cols, batch = 256, 14 * 256, 64
+@pytest.mark.parametrize("batch", [16, 64])
+def test_mfma_deterministic_and_graph_replay(batch):
+    rows, cols = 256, 14 * 256
     w = Weights("q4_k", rows, cols, seed=11)
     x = to_dev_x(gen_x(batch, cols, "bf16", seed=12), "bf16")
     y1 = w.gemv(x, "bf16", batch)
