@@ -27,6 +27,10 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
 HIP_SOURCES = ["api.cpp", "gemv_q8_0.hip", "gemv_q4_k.hip", "gemv_q5_k.hip", "gemv_q6_k.hip",
                "gemv_int4_g128.hip", "gemm_q4_k_mfma.hip", "dequant.hip", "probe.hip"]
 CXX_SOURCES = ["packer.cpp"]
+# Per-source device flags.  The matrix-core kernels scale each product in
+# VALU right away; in accumulation registers every result would need a
+# v_accvgpr_read first, so their results are kept in ordinary VGPRs.
+SOURCE_FLAGS = {"gemm_q4_k_mfma.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _run(cmd, verbose):
@@ -48,7 +52,8 @@ def build(verbose: bool = False, jobs: int | None = None) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(OBJDIR, src + ".o")
         lang = ["-x", "hip"] if src.endswith(".cpp") else []
-        cmds.append([HIPCC] + COMMON + DEVICE + lang + ["-c", os.path.join(CSRC, src), "-o", obj])
+        cmds.append([HIPCC] + COMMON + DEVICE + SOURCE_FLAGS.get(src, []) + lang +
+                    ["-c", os.path.join(CSRC, src), "-o", obj])
         objs.append(obj)
     for src in CXX_SOURCES:
         obj = os.path.join(OBJDIR, src + ".o")

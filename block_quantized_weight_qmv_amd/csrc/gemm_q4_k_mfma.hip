@@ -44,167 +44,52 @@ namespace qmv {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-constexpr int kXRow = 256 + 8;  // bf16 per staged X row (528 bytes)
+// Workgroup barrier for LDS hand-offs: waits only for this wave's LDS
+// operations (lgkmcnt(0); vmcnt and expcnt left at their maxima), then
+// s_barrier.  __syncthreads() also fences global memory, which makes every
+// wave wait for all of its outstanding loads -- here the weight prefetch of
+// the next blocks, which would then be drained at every barrier.  The empty
+// asm statements keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
+}
 
-// 6-bit scale and min of sub-block s (0..7) from the header dwords holding
-// scales[0..3] (h1), [4..7] (h2) and [8..11] (h3).
-__device__ __forceinline__ void q4k_scale_min(uint32_t h1, uint32_t h2, uint32_t h3, int s,
-                                              uint32_t& sc, uint32_t& mn) {
-  auto byte = [&](int i) -> uint32_t {
-    const uint32_t word = i < 4 ? h1 : (i < 8 ? h2 : h3);
-    return (word >> (8 * (i & 3))) & 0xFFu;
-  };
-  if (s < 4) {
-    sc = byte(s) & 63u;
-    mn = byte(s + 4) & 63u;
-  } else {
-    sc = (byte(s + 4) & 15u) | ((byte(s - 4) >> 6) << 4);
-    mn = (byte(s + 4) >> 4) | ((byte(s) >> 6) << 4);
-  }
+// v with every bit cleared unless keep: an AND with a mask the compiler cannot
+// see through.  A select of a loaded value is turned into a branch around the
+// load, and a load under a branch makes the wait-count analysis wait for
+// every outstanding load.
+__device__ __forceinline__ uint4 keep_if(uint4 v, bool keep) {
+  uint32_t k = keep ? 0xFFFFFFFFu : 0u;
+  __asm__("" : "+v"(k));
+  return make_uint4(v.x & k, v.y & k, v.z & k, v.w & k);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// Sum of the eight bf16 values of a 16-byte chunk in fp32: four
+// v_dot2c_f32_bf16 against bf16 ones (exact products, fp32 sums).
+__device__ __forceinline__ float bf16x8_sum(uint4 v) {
+  const bf16x2_t one = __builtin_bit_cast(bf16x2_t, 0x3F803F80u);
+  float s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.x), one, 0.f, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.y), one, s, false);
+  s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.z), one, s, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, v.w), one, s, false);
+}
+
+// Sum over the four lanes of a quad (lanes 4i..4i+3) with DPP quad
+// permutes -- register-to-register, unlike __shfl_xor (ds_bpermute).
+__device__ __forceinline__ float quad_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));  // lane ^ 1
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));  // lane ^ 2
+  return v;
 }
 
 // Two columns of a permuted 8-group: (x0, x2) and (x1, x3) from (x0, x1), (x2, x3).
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
-
-struct WRegs {
-  uint4 hd;     // block header of this lane's row
-  uint2 q[4];   // code bytes 32c + 8 (lane / 16) .. +7 of chunks c = 0..3
-};
-
-template <int MB>
-__global__ void __launch_bounds__(256)
-gemm_q4_k_bf16_kernel(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M) {
-  constexpr int MT = 16 * MB;
-  constexpr int kPairs = MT * 8;                 // (batch row, sub-block) sums per block
-  constexpr int kPairsPerThread = (kPairs + 255) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[2][MT][kXRow];
-  __shared__ __attribute__((aligned(16))) float xsum[2][8][MT];
-  __shared__ __attribute__((aligned(16))) float sds[4][8][16];   // ds per (wave, s, row)
-  __shared__ __attribute__((aligned(16))) float sdm[4][8][16];   // 128 ds + dm
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int q = lane >> 4, l16 = lane & 15;
-  const int nb = K / 256;
-  const int n0 = static_cast<int>(blockIdx.x) * 64 + wave * 16;
-  const int m0 = static_cast<int>(blockIdx.y) * MT;
-  const uint8_t* wrow = w + static_cast<size_t>(min(n0 + l16, N - 1)) * (static_cast<size_t>(nb) * 144);
-
-  auto load_w = [&](int b, WRegs& r) {
-    const uint8_t* p = wrow + static_cast<size_t>(min(b, nb - 1)) * 144;
-    r.hd = *reinterpret_cast<const uint4*>(p);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) r.q[c] = *reinterpret_cast<const uint2*>(p + 16 + 32 * c + 8 * q);
-  };
-  // X staging: thread handles pairs (m, s) = (pi / 8, pi % 8): 32 columns.
-  uint4 xr[2][kPairsPerThread][4];  // X of the next two blocks in flight
-  auto load_x = [&](int b, int slot) {
-#pragma unroll
-    for (int t = 0; t < kPairsPerThread; ++t) {
-      const int pi = min(tid + 256 * t, kPairs - 1);
-      const int m = pi >> 3, s = pi & 7;
-      const uint16_t* p = x + static_cast<size_t>(min(m0 + m, M - 1)) * K +
-                          static_cast<size_t>(min(b, nb - 1)) * 256 + 32 * s;
-#pragma unroll
-      for (int g = 0; g < 4; ++g) xr[slot][t][g] = reinterpret_cast<const uint4*>(p)[g];
-    }
-  };
-  auto stage_x = [&](int buf) {
-#pragma unroll
-    for (int t = 0; t < kPairsPerThread; ++t) {
-      const int pi = tid + 256 * t;
-      if (pi < kPairs) {
-        const int m = pi >> 3, s = pi & 7;
-        float sum = 0.f;
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const uint4 v = xr[buf][t][g];
-          const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            sum += __uint_as_float(d[i] << 16);
-            sum += __uint_as_float(d[i] & 0xFFFF0000u);
-          }
-          *reinterpret_cast<uint4*>(&xs[buf][m][32 * s + 8 * g]) =
-              make_uint4(lo_pair(v.x, v.y), hi_pair(v.x, v.y), lo_pair(v.z, v.w), hi_pair(v.z, v.w));
-        }
-        xsum[buf][s][m] = sum;
-      }
-    }
-  };
-
-  f32x4_t acc[MB];
-#pragma unroll
-  for (int i = 0; i < MB; ++i) acc[i] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  auto step = [&](int b, const WRegs& r) {
-    const int buf = b & 1;
-    stage_x(buf);
-    __syncthreads();
-    load_x(b + 2, buf);
-    // Scales of this lane's row for sub-blocks 2q and 2q + 1.
-    {
-      const float d = f16_to_f32(r.hd.x & 0xFFFFu), dmin = f16_to_f32(r.hd.x >> 16);
-#pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int s = 2 * q + i;
-        uint32_t sc, mn;
-        q4k_scale_min(r.hd.y, r.hd.z, r.hd.w, s, sc, mn);
-        const float ds = d * static_cast<float>(sc);
-        sds[wave][s][l16] = ds;
-        sdm[wave][s][l16] = fmaf(128.f, ds, dmin * static_cast<float>(mn));
-      }
-    }
-#pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      const uint2 pc = r.q[s >> 1];
-      const uint32_t v0 = (s & 1) ? pc.x >> 4 : pc.x, v1 = (s & 1) ? pc.y >> 4 : pc.y;
-      const uint32_t a[4] = {(v0 & 0x000F000Fu) | 0x43004300u, ((v0 >> 8) & 0x000F000Fu) | 0x43004300u,
-                             (v1 & 0x000F000Fu) | 0x43004300u, ((v1 >> 8) & 0x000F000Fu) | 0x43004300u};
-      const bf16x8_t A = __builtin_bit_cast(bf16x8_t, a);
-      const f32x4_t ds4 = *reinterpret_cast<const f32x4_t*>(&sds[wave][s][4 * q]);
-      const f32x4_t dm4 = *reinterpret_cast<const f32x4_t*>(&sdm[wave][s][4 * q]);
-#pragma unroll
-      for (int mb = 0; mb < MB; ++mb) {
-        const bf16x8_t B = *reinterpret_cast<const bf16x8_t*>(&xs[buf][16 * mb + l16][32 * s + 8 * q]);
-        const f32x4_t S =
-            __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-        const float xsv = xsum[buf][s][16 * mb + l16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) acc[mb][i] = fmaf(-dm4[i], xsv, fmaf(ds4[i], S[i], acc[mb][i]));
-      }
-    }
-  };
-
-  WRegs ra, rb;
-  load_w(0, ra);
-  load_w(1, rb);
-  load_x(0, 0);
-  load_x(1, 1);
-  int b = 0;
-#pragma unroll 1
-  for (; b + 2 < nb; b += 2) {
-    step(b, ra);
-    load_w(b + 2, ra);
-    step(b + 1, rb);
-    load_w(b + 3, rb);
-  }
-  step(b, ra);
-  if (b + 1 < nb) step(b + 1, rb);
-
-#pragma unroll
-  for (int mb = 0; mb < MB; ++mb) {
-    const int m = m0 + 16 * mb + l16;
-    if (m < M) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int n = n0 + 4 * q + i;
-        if (n < N) y[static_cast<size_t>(m) * N + n] = acc[mb][i];
-      }
-    }
-  }
-}
-
 
 // ---------------------------------------------------------------------------
 // Small batches (M <= 32): K split over the waves of a workgroup.
@@ -468,21 +353,18 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   // bound), so 32 nb <= 512 threads cover a row.
   const bool xl = tid < 32 * nb;
   const int xb_ = tid >> 5, xs_ = (tid >> 2) & 7, xk = tid & 3;
+  // Unconditional loads, clamped into X (a load under a branch makes the
+  // compiler's wait-count analysis wait for every outstanding load); rows past
+  // the batch are zeroed after they arrive.
+  const int xt = min(tid, 32 * nb - 1);
   uint4 xv[16];
 #pragma unroll
-  for (int m = 0; m < 16; ++m) {
-    xv[m] = make_uint4(0u, 0u, 0u, 0u);
-    if (xl && m < M) xv[m] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + 8 * tid);
-  }
+  for (int m = 0; m < 16; ++m)
+    xv[m] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(min(m, M - 1)) * K + 8 * xt);
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
-    const uint4 v = xv[m];
-    const uint32_t d[4] = {v.x, v.y, v.z, v.w};
-    float sum = 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) sum += __uint_as_float(d[e] << 16) + __uint_as_float(d[e] & 0xFFFF0000u);
-    sum += __shfl_xor(sum, 1);  // the four quarters of a sub-block are lanes 4i..4i+3
-    sum += __shfl_xor(sum, 2);
+    const uint4 v = keep_if(xv[m], m < M);
+    const float sum = quad_sum(bf16x8_sum(v));  // the four quarters of a sub-block are lanes 4i..4i+3
     if (xl) {
       *reinterpret_cast<uint4*>(xa + ((static_cast<size_t>(xb_) * 8 + xs_) * 4 + xk) * 256 +
                                 (m ^ ((4 * xs_ + xk) & 15)) * 16) =
@@ -496,7 +378,7 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   for (int j = 0; j < kDepth; ++j) load(u0 + j, f[j]);
   __asm__ __volatile__("" ::: "memory");
   __builtin_amdgcn_sched_barrier(0);
-  __syncthreads();
+  lds_barrier();
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   // First tile of wave k's run: floor(floor(k U / W) / nb) = floor(k nt / W).
@@ -554,7 +436,7 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   for (int j = 0; j < kDepth; ++j)
     if (u + j < u1) unit(u + j, f[j]);
 
-  __syncthreads();
+  lds_barrier();
   // Tile t of the workgroup gets the partials of the waves whose run meets
   // it, in wave order.  Wave k's run is [floor(k U / W), floor((k+1) U / W))
   // (W a power of two: no division); its partial of tile t sits in slot
@@ -573,6 +455,251 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Larger batches: tiles of 64 NB weight rows by 16 MB WM batch rows.
+//
+// A workgroup has 4 x WM waves: wave (wn, wm) owns NB 16-row tiles of W
+// (rows 16 NB wn ..) and MB 16-row tiles of the batch (rows 16 MB wm ..).  X
+// advances one block (256 columns) at a time through two LDS buffers with one
+// barrier per block: the loads of block b + 2 are issued while block b is
+// multiplied and stored after it, so their latency is hidden by a whole block
+// of work.  W comes straight from memory into registers, two blocks ahead.
+// Operand roles as in the kernels above (A = X, B = codes, lane (q, c)
+// accumulates Y[4q + r][c]).
+//
+// Per sub-block s the matrix cores give S = sum_k (128 + u_k) X_k, which the
+// lane scales by its row's ds = d sc_s (one FMA per accumulator).  The rest
+// of each weight, -128 ds - dm per sub-block, is a product over sub-blocks:
+//   sum_s (128 d sc_s + dmin m_s) Xs_s = 128 d T1 + dmin T2,
+//   T1 = sum_s sc_s Xs_s,  T2 = sum_s m_s Xs_s,
+// two more matrix-core products per block with K = the 8 sub-blocks: A holds
+// each sub-block sum split exactly into three bf16 parts (8 + 8 + 8
+// significant bits; K slots 8j + s for part j, the fourth group zero) and B
+// the 6-bit sc_s or m_s, exact in bf16.  The products are exact and the sums
+// fp32, as for S.
+template <int NB>
+struct TileRegs {
+  uint4 hd[NB];
+  uint2 q[NB][4];
+};
+
+// LDS bytes per buffer: X operands of 16 MT rows x 256 columns, then the
+// split sub-block sums (1 KB per 16 rows).
+template <int MT>
+__host__ __device__ constexpr size_t tile_buf_bytes() {
+  return static_cast<size_t>(MT) * 512 + static_cast<size_t>(MT / 16) * 1024;
+}
+
+template <int NB, int MB, int WM>
+__global__ void __launch_bounds__(256 * WM)
+gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
+  constexpr int MT = 16 * MB * WM;             // batch rows of the workgroup
+  constexpr int kThreads = 256 * WM;
+  constexpr size_t kXBytes = static_cast<size_t>(MT) * 512;
+  constexpr size_t kBuf = tile_buf_bytes<MT>();
+  constexpr int kItems = (MT * 8 + kThreads - 1) / kThreads;  // (row, sub-block) items per thread
+  // Buffer layout: X operands [8 s][MT / 16][4 q][16 slots][16 B], batch row
+  // m (within its 16-row tile) of quarter q of sub-block s in slot
+  // m ^ ((s + 4 q) & 15); then the split sums [MT / 16][4 j][16 m][8 s] bf16
+  // (j = 3 stays zero).  The swizzle spreads both the staging stores (lanes
+  // along s, one row, one quarter) and the operand reads (lanes along m) over
+  // all 32 banks.
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wn = wave & 3, wm = wave >> 2;
+  const int q = lane >> 4, c = lane & 15;
+  const int nb = K >> 8;
+  const int n0 = static_cast<int>(blockIdx.x) * 64 * NB + wn * 16 * NB;
+  const int mw0 = static_cast<int>(blockIdx.y) * MT;           // first batch row of the workgroup
+  const size_t row_bytes = static_cast<size_t>(nb) * 144;
+  const uint8_t* wr[NB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+    wr[t] = w + static_cast<size_t>(min(n0 + 16 * t + c, N - 1)) * row_bytes;
+
+  // Zero the fourth part group of both split-sum buffers once.
+  for (int i = tid; i < 2 * (MT / 16) * 16; i += kThreads) {
+    const int buf = i / ((MT / 16) * 16), mb = (i >> 4) % (MT / 16), e = i & 15;
+    *reinterpret_cast<uint4*>(tl_lds + buf * kBuf + kXBytes + (mb * 4 + 3) * 256 + e * 16) =
+        make_uint4(0u, 0u, 0u, 0u);
+  }
+
+  auto load_w = [&](int b, TileRegs<NB>& r) {
+    const int bb = min(b, nb - 1);
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const uint8_t* p = wr[t] + static_cast<size_t>(bb) * 144;
+      r.hd[t] = *reinterpret_cast<const uint4*>(p);
+#pragma unroll
+      for (int cc = 0; cc < 4; ++cc) r.q[t][cc] = *reinterpret_cast<const uint2*>(p + 16 + 32 * cc + 8 * q);
+    }
+  };
+  // Item i = tid + kThreads j: batch row i / 8 of the workgroup, sub-block
+  // i % 8 -- 64 contiguous bytes of X, read as four 16-byte quarters.
+  // Loads are unconditional (clamped): a load under a branch makes the
+  // compiler's wait-count analysis wait for every outstanding load.
+  auto load_x = [&](int b, uint4 (&v)[kItems][4]) {
+    const int bb = min(b, nb - 1);
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int i = min(tid + kThreads * j, MT * 8 - 1);
+      const int m = min(mw0 + (i >> 3), M - 1);
+      const uint4* p = reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + 256 * bb + 32 * (i & 7));
+#pragma unroll
+      for (int k = 0; k < 4; ++k) v[j][k] = p[k];
+    }
+  };
+  const bool ragged = mw0 + MT > M;  // only the last batch tile has rows past M
+  auto stage_x = [&](uint4 (&v)[kItems][4], int buf) {
+    uint8_t* base = tl_lds + buf * kBuf;
+#pragma unroll
+    for (int j = 0; j < kItems; ++j) {
+      const int i = tid + kThreads * j;
+      if (kItems * kThreads > MT * 8 && i >= MT * 8) continue;
+      const int row = i >> 3, s = i & 7, mb = row >> 4, mr = row & 15;
+      if (ragged) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) v[j][k] = keep_if(v[j][k], mw0 + row < M);
+      }
+      float sum = 0.f;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint4 u = v[j][k];
+        sum += bf16x8_sum(u);
+        *reinterpret_cast<uint4*>(base + ((s * (MT / 16) + mb) * 4 + k) * 256 + (mr ^ ((s + 4 * k) & 15)) * 16) =
+            make_uint4(lo_pair(u.x, u.y), hi_pair(u.x, u.y), lo_pair(u.z, u.w), hi_pair(u.z, u.w));
+      }
+      // exact three-way bf16 split: truncations, each residual exact in fp32
+      const uint32_t hb = __float_as_uint(sum) & 0xFFFF0000u;
+      const float r1 = sum - __uint_as_float(hb);
+      const uint32_t mbits = __float_as_uint(r1) & 0xFFFF0000u;
+      const float r2 = r1 - __uint_as_float(mbits);
+      uint16_t* t = reinterpret_cast<uint16_t*>(base + kXBytes + mb * 1024 + mr * 16) + s;
+      t[0] = static_cast<uint16_t>(hb >> 16);
+      t[256 / 2] = static_cast<uint16_t>(mbits >> 16);
+      t[512 / 2] = static_cast<uint16_t>(__float_as_uint(r2) >> 16);
+    }
+  };
+
+  f32x4_t acc[NB][MB];
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) acc[t][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const uint32_t bias = vgpr_const(0x43004300u);
+
+  auto compute = [&](const TileRegs<NB>& r, int buf) {
+    const uint8_t* base = tl_lds + buf * kBuf;
+    float ds[NB][8], d128[NB], dmin[NB];
+    uint32_t bt1[NB][4], bt2[NB][4];
+#pragma unroll
+    for (int t = 0; t < NB; ++t) {
+      const uint4 h = r.hd[t];
+      const float d = f16_to_f32(h.x & 0xFFFFu);
+      d128[t] = 128.f * d;
+      dmin[t] = f16_to_f32(h.x >> 16);
+      const uint32_t sc03 = h.y & 0x3F3F3F3Fu, m03 = h.z & 0x3F3F3F3Fu;
+      const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
+      const uint32_t m47 = ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u);
+      float scf[8], mf[8];
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        scf[s] = ubyte_f32(s < 4 ? sc03 : sc47, s);
+        mf[s] = ubyte_f32(s < 4 ? m03 : m47, s);
+        ds[t][s] = d * scf[s];
+      }
+      // small integers: the top half of the fp32 value is the exact bf16
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        bt1[t][e] = (__float_as_uint(scf[2 * e]) >> 16) | (__float_as_uint(scf[2 * e + 1]) & 0xFFFF0000u);
+        bt2[t][e] = (__float_as_uint(mf[2 * e]) >> 16) | (__float_as_uint(mf[2 * e + 1]) & 0xFFFF0000u);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 8; ++s) {
+      bf16x8_t A[MB];
+#pragma unroll
+      for (int mb = 0; mb < MB; ++mb)
+        A[mb] = *reinterpret_cast<const bf16x8_t*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
+                                                   (c ^ ((s + 4 * q) & 15)) * 16);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const uint2 pc = r.q[t][s >> 1];
+        const int sh = 4 * (s & 1);
+        const uint32_t bw[4] = {((pc.x >> sh) & 0x000F000Fu) | bias, ((pc.x >> (8 + sh)) & 0x000F000Fu) | bias,
+                                ((pc.y >> sh) & 0x000F000Fu) | bias, ((pc.y >> (8 + sh)) & 0x000F000Fu) | bias};
+        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb) {
+          const f32x4_t S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(ds[t][s], S[i], acc[t][mb][i]);
+          // Pin the scaling to its sub-block: left alone, the compiler sinks
+          // every FMA below all the block's products and parks those
+          // products in accumulation registers (hundreds of them).
+          __asm__ __volatile__("" : "+v"(acc[t][mb]));
+        }
+      }
+    }
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb) {
+      const bf16x8_t AT =
+          *reinterpret_cast<const bf16x8_t*>(base + kXBytes + ((MB * wm + mb) * 4 + q) * 256 + c * 16);
+#pragma unroll
+      for (int t = 0; t < NB; ++t) {
+        const f32x4_t T1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            AT, __builtin_bit_cast(bf16x8_t, bt1[t]), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        const f32x4_t T2 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            AT, __builtin_bit_cast(bf16x8_t, bt2[t]), f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(-d128[t], T1[i], fmaf(-dmin[t], T2[i], acc[t][mb][i]));
+      }
+    }
+  };
+
+  TileRegs<NB> ra, rb;
+  uint4 xv[kItems][4];
+  load_x(0, xv);
+  load_w(0, ra);
+  load_w(1, rb);
+  stage_x(xv, 0);
+  load_x(1, xv);
+  lds_barrier();
+  int b = 0;
+#pragma unroll 1
+  for (; b + 2 < nb; b += 2) {
+    compute(ra, 0);
+    load_w(b + 2, ra);
+    stage_x(xv, 1);
+    lds_barrier();
+    load_x(b + 2, xv);
+    compute(rb, 1);
+    load_w(b + 3, rb);
+    stage_x(xv, 0);
+    lds_barrier();
+    load_x(b + 3, xv);
+  }
+  compute(ra, 0);
+  if (b + 1 < nb) {
+    stage_x(xv, 1);
+    lds_barrier();
+    compute(rb, 1);
+  }
+
+#pragma unroll
+  for (int t = 0; t < NB; ++t)
+#pragma unroll
+    for (int mb = 0; mb < MB; ++mb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int m = mw0 + 16 * (MB * wm + mb) + 4 * q + i, n = n0 + 16 * t + c;
+        if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = acc[t][mb][i];
+      }
+}
+
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t stream) {
   const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols), M = static_cast<int>(batch);
@@ -589,7 +716,10 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
                        stream, w, N, K, xb, y, M);
     return hipGetLastError();
   }
-  if (M <= 32) {
+#ifndef QMV_TILE_MIN_BATCH
+#define QMV_TILE_MIN_BATCH 17
+#endif
+  if (M < QMV_TILE_MIN_BATCH) {
     // K split: enough waves for about eight per SIMD, at most 8 per workgroup
     // and never more than one per block.
     const unsigned n_groups = static_cast<unsigned>((N + 15) / 16);
@@ -605,10 +735,20 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
                          w, N, K, xb, y, M, kw);
     return hipGetLastError();
   }
-  const unsigned n_tiles = static_cast<unsigned>((N + 63) / 64);
-  const unsigned m_tiles = static_cast<unsigned>((M + 63) / 64);
-  hipLaunchKernelGGL(gemm_q4_k_bf16_kernel<4>, dim3(n_tiles, m_tiles), dim3(256), 0, stream, w, N,
-                     K, xb, y, M);
+#ifndef QMV_TILE_NB2_MIN_BATCH
+#define QMV_TILE_NB2_MIN_BATCH 100000
+#endif
+  const unsigned n64 = static_cast<unsigned>((N + 63) / 64);
+  if (M <= 32) {
+    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 1, 2>), dim3(n64, (M + 31) / 32), dim3(512),
+                       2 * tile_buf_bytes<32>(), stream, w, N, K, xb, y, M);
+  } else if (M < QMV_TILE_NB2_MIN_BATCH) {
+    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 2, 2>), dim3(n64, (M + 63) / 64), dim3(512),
+                       2 * tile_buf_bytes<64>(), stream, w, N, K, xb, y, M);
+  } else {
+    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<2, 2, 2>), dim3((N + 127) / 128, (M + 63) / 64), dim3(512),
+                       2 * tile_buf_bytes<64>(), stream, w, N, K, xb, y, M);
+  }
   return hipGetLastError();
 }
 
