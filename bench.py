@@ -42,7 +42,9 @@ CSRC = os.path.join(ROOT, "block_quantized_weight_qmv_amd", "csrc")
 # committed counter figures for that family (and only for it).
 _KERNEL_SOURCES = {
     "gemv_kernel": ["gemv_skeleton.h", "device_util.h"],
-    "gemm_q4_k_bf16_kernel": ["gemm_q4_k_mfma.hip", "device_util.h"],
+    "gemm_q4_k_bf16_stream": ["gemm_q4_k_mfma.hip", "device_util.h"],
+    "gemm_q4_k_bf16_ksplit": ["gemm_q4_k_mfma.hip", "device_util.h"],
+    "gemm_q4_k_bf16_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
 }
 _POLICY_SOURCE = {"Q80Policy": "gemv_q8_0.hip", "Q4KPolicy": "gemv_q4_k.hip",
                   "Q5KPolicy": "gemv_q5_k.hip", "Q6KPolicy": "gemv_q6_k.hip",
@@ -66,11 +68,16 @@ def kernel_source_hash(kernel: str) -> str:
 def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
     """Instantiation the library launches for matrices of these widths in one
     launch (mirrors the dispatch in api.cpp and the GEMV launcher: Q4_K x bf16
-    with batch >= 3 -> matrix-core kernel, M tile by batch; otherwise waves per
-    workgroup = max(4, widest K split))."""
+    with batch >= 3 -> one of the matrix-core kernels, chosen by batch and by
+    whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
+    split))."""
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 3:
-        mb = 1 if batch <= 16 else (2 if batch <= 32 else 4)
-        return f"qmv::gemm_q4_k_bf16_kernel<{mb}>"
+        nb = max(cols_list) // 256
+        if batch <= 16 and nb * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024:  # X fits in LDS
+            return "qmv::gemm_q4_k_bf16_stream"
+        if batch <= 16:
+            return "qmv::gemm_q4_k_bf16_ksplit<1, 1>"
+        return "qmv::gemm_q4_k_bf16_tile<1, 1, 2>" if batch <= 32 else "qmv::gemm_q4_k_bf16_tile<1, 2, 2>"
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096, "q5_k": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
     cfg = "2, 2, 256" if waves <= 4 else ("2, 2, 512" if waves <= 8 else "1, 2, 1024")

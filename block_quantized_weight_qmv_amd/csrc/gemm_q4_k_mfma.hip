@@ -16,26 +16,30 @@
 // (bits 0x4300 | u, one AND-OR per two codes), X enters as given, and one
 // instruction covers one sub-block (K = 32).  With S = sum (128 + u) X and
 // Xs = sum X, the row's contribution is ds S - (128 ds + dm) Xs with
-// ds = d sc_s, dm = dmin m_s, applied in fp32 to the 16x16 result.  Nothing
-// is dequantized to memory, W is read once per tile of up to 64 batch rows,
-// and the products are exact (the 2e-3 GEMV bound is spent only on fp32
-// summation).
+// ds = d sc_s, dm = dmin m_s, applied in fp32.  Nothing is dequantized to
+// memory and the products are exact (the 2e-3 GEMV bound is spent only on
+// fp32 summation).
 //
-// Workgroup: 4 waves, 64 rows of W (16 per wave), MT = 16 MB batch rows,
-// stepping one Q4_K block (256 K) at a time:
-//   * X's block for the tile is staged in LDS (double buffered, one barrier
-//     per block, its global loads issued two blocks ahead) with each group of
-//     8 columns permuted to the code order below, together with its 8
-//     sub-block sums;
-//   * each lane streams its row's header and 4 x 8 code bytes straight into
-//     registers (two blocks in flight) and builds the A operands there;
-//   * ds and 128 ds + dm of its 16 rows are exchanged through per-wave LDS.
+// Operand roles: A = 16 batch rows of X, B = the codes of 16 weight rows, so
+// accumulator r of lane (q, c) = (l / 16, l % 16) is Y[4q + r][c]: batch rows
+// 4q..4q+3 of weight row c, the row whose block header that lane loads.
+// Every scale is applied from the lane's own registers.
+//
+// Three kernels, by batch (routing in gemm_q4_k_bf16 below):
+//   * M <= 16 and X fits in LDS: gemm_q4_k_bf16_stream -- one workgroup per
+//     CU streams its share of W past an LDS copy of all of X;
+//   * 17 <= M: gemm_q4_k_bf16_tile -- 64 NB x 16 MB WM tiles, X staged per
+//     block through double-buffered LDS, min and offset terms as two extra
+//     matrix-core products per block;
+//   * M <= 16 with X too large for LDS: gemm_q4_k_bf16_ksplit -- K split over
+//     the waves of a workgroup, X read from memory.
 //
 // v_mfma_f32_16x16x32_bf16 (layout checked on the device): lane l holds
 // A[l % 16][8 (l / 16) + e] and B[8 (l / 16) + e][l % 16], e = 0..7, and
 // accumulator r of lane l is D[4 (l / 16) + r][l % 16].  Code slot 8q + e of a
 // sub-block maps to weight 8q + (0, 2, 1, 3, 4, 6, 5, 7)[e], the order in which
-// masking one dword of code bytes yields bf16 pairs.
+// masking one dword of code bytes yields bf16 pairs; X is permuted to match
+// where it is staged.
 #include "device_util.h"
 #include "launch.h"
 
@@ -92,15 +96,11 @@ __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a 
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
 // ---------------------------------------------------------------------------
-// Small batches (M <= 32): K split over the waves of a workgroup.
+// Small batches with X too large for LDS: K split over the waves of a workgroup.
 //
-// Operands swapped relative to the tile kernel above: A = 16 batch rows of X,
-// B = the codes of 16 weight rows, so accumulator r of lane (q, c) is
-// Y[4q + r][c] -- batch rows 4q..4q+3 of weight row c, the row whose block
-// header that lane loads itself.  Every scale is then applied from the lane's
-// own registers, with no exchange.  The sub-block sums of X come from one
-// more matrix-core product per sub-block, against a B of bf16 ones, which
-// lands them in the same accumulator layout (Xs[4q + r] in every lane).
+// The sub-block sums of X come from one more matrix-core product per
+// sub-block, against a B of bf16 ones, which lands them in the accumulator
+// layout (Xs[4q + r] in every lane).
 //
 // A workgroup owns 16 NB weight rows and 16 MB batch rows; its kw waves take
 // consecutive, near-equal runs of blocks along K.  X is read straight from
@@ -273,8 +273,6 @@ gemm_q4_k_bf16_ksplit(const uint8_t* w, int N, int K, const uint16_t* x, float* 
 // two tiles; its partial tiles are parked in LDS and added in wave order at
 // the end (results do not depend on timing).
 //
-// Operand roles as in the K-split kernel: A = X (rows = batch), B = codes,
-// accumulator r of lane (q, c) is Y[4q + r][c] of weight row c.
 #ifndef QMV_STREAM_WAVES
 #define QMV_STREAM_WAVES 8
 #endif
