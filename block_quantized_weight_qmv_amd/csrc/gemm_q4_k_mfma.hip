@@ -351,17 +351,19 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   // bound), so 32 nb <= 512 threads cover a row.
   const bool xl = tid < 32 * nb;
   const int xb_ = tid >> 5, xs_ = (tid >> 2) & 7, xk = tid & 3;
-  // Unconditional loads, clamped into X (a load under a branch makes the
-  // compiler's wait-count analysis wait for every outstanding load); rows past
-  // the batch are zeroed after they arrive.
+  // Only the M real rows are read and stored: the operand rows past M (left
+  // as whatever LDS holds) feed only accumulator rows past M, which are never
+  // stored.  The loads may sit under the (uniform) row test: nothing else is
+  // in flight yet, so waiting for them waits for nothing more.
   const int xt = min(tid, 32 * nb - 1);
   uint4 xv[16];
 #pragma unroll
   for (int m = 0; m < 16; ++m)
-    xv[m] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(min(m, M - 1)) * K + 8 * xt);
+    if (m < M) xv[m] = *reinterpret_cast<const uint4*>(x + static_cast<size_t>(m) * K + 8 * xt);
 #pragma unroll
   for (int m = 0; m < 16; ++m) {
-    const uint4 v = keep_if(xv[m], m < M);
+    if (m >= M) continue;  // uniform; the loop stays unrolled
+    const uint4 v = xv[m];
     const float sum = quad_sum(bf16x8_sum(v));  // the four quarters of a sub-block are lanes 4i..4i+3
     if (xl) {
       *reinterpret_cast<uint4*>(xa + ((static_cast<size_t>(xb_) * 8 + xs_) * 4 + xk) * 256 +
