@@ -18,13 +18,14 @@ from synth import gen_x
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128")
+FMTS = ("q8_0", "q4_k", "q6_k", "int4_g128", "q5_k")
 # (rows, blocks per row) per item; the last item spans several waves along K
 ITEMS = {
     "q8_0": [(67, 48), (5, 48), (130, 48), (33, 300)],
     "q4_k": [(67, 14), (5, 14), (130, 14), (33, 40)],
     "q6_k": [(67, 14), (5, 14), (130, 14), (33, 40)],
     "int4_g128": [(67, 28), (5, 28), (130, 28), (33, 80)],
+    "q5_k": [(67, 14), (5, 14), (130, 14), (33, 40)],
 }
 
 
@@ -71,7 +72,7 @@ def test_multi_matches_oracle_and_single_calls(fmt, x_dtype):
 @pytest.mark.parametrize("fmt", FMTS)
 def test_multi_sixteen_items(fmt):
     qk = oracle.QK[fmt]
-    nblk = {"q8_0": 40, "q4_k": 5, "q6_k": 5, "int4_g128": 10}[fmt]
+    nblk = {"q8_0": 40, "q4_k": 5, "q6_k": 5, "int4_g128": 10, "q5_k": 5}[fmt]
     cols = nblk * qk
     ws = [Weights(fmt, 3 + 11 * i, cols, seed=500 + i) for i in range(16)]
     x_np = gen_x(1, cols, "f32", seed=5)
@@ -107,3 +108,29 @@ def test_multi_graph_replay_matches_eager():
         torch.cuda.synchronize()
         for y, e in zip(ys, eager):
             assert torch.equal(y, e), f"replay {rep} differs"
+
+
+@pytest.mark.parametrize("batch", [4, 24, 64])
+def test_multi_q4_k_bf16_batches_take_the_matrix_cores(batch):
+    """Q4_K x bf16 with batch >= 3: each item runs the batched kernel for its
+    batch size; results match the oracle and the same item called alone
+    (same kernel, same arithmetic: bitwise)."""
+    items = [(67, 14), (16, 14), (130, 3), (33, 20)]
+    ws, xs_np, xs, ys = [], [], [], []
+    for i, (rows, nblk) in enumerate(items):
+        cols = nblk * 256
+        w = Weights("q4_k", rows, cols, seed=1500 + 11 * i)
+        x = gen_x(batch, cols, "bf16", seed=1600 + i)
+        ws.append(w)
+        xs_np.append(x)
+        xs.append(to_dev_x(x, "bf16"))
+        ys.append(torch.full((batch, rows), -3.0, dtype=torch.float32, device=DEV))
+    say(f"multi q4_k bf16 batch {batch}: " + ", ".join(f"{w.rows}x{w.cols}" for w in ws))
+    qmv.qmv_gemv_multi("q4_k", "bf16", batch, [(w.desc, x, y) for w, x, y in zip(ws, xs, ys)])
+    torch.cuda.synchronize()
+    for w, x_np, x, y in zip(ws, xs_np, xs, ys):
+        got = y.cpu().numpy()
+        err = oracle.normwise_rel_err(got, oracle_y(w, x_np, "bf16"))
+        assert np.all(err <= TOL), (w.rows, w.cols, err.max())
+        alone = w.gemv(x, "bf16", batch).cpu().numpy()
+        assert np.array_equal(got, alone), (w.rows, w.cols)
