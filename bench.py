@@ -77,7 +77,9 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
             return "qmv::gemm_q4_k_bf16_stream"
         if batch <= 16:
             return "qmv::gemm_q4_k_bf16_ksplit<1, 1>"
-        return "qmv::gemm_q4_k_bf16_tile<1, 1, 2>" if batch <= 32 else "qmv::gemm_q4_k_bf16_tile<1, 2, 2>"
+        if batch <= 32:
+            return "qmv::gemm_q4_k_bf16_tile<1, 1, 2, 5>"
+        return "qmv::gemm_q4_k_bf16_tile<1, 2, 2, 5>" if batch <= 64 else "qmv::gemm_q4_k_bf16_tile<1, 4, 2, 5>"
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096, "q5_k": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
     cfg = "2, 2, 256" if waves <= 4 else ("2, 2, 512" if waves <= 8 else "1, 2, 1024")

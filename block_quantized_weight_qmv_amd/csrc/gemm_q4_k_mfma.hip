@@ -40,6 +40,8 @@
 // sub-block maps to weight 8q + (0, 2, 1, 3, 4, 6, 5, 7)[e], the order in which
 // masking one dword of code bytes yields bf16 pairs; X is permuted to match
 // where it is staged.
+#include <type_traits>
+
 #include "device_util.h"
 #include "launch.h"
 
@@ -457,10 +459,14 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
 
 
 // ---------------------------------------------------------------------------
-// Larger batches: tiles of 64 NB weight rows by 16 MB WM batch rows.
+// Larger batches: workgroups of WN x WM waves over a run of 16-row tiles of W
+// and 16 MB WM batch rows.
 //
-// A workgroup has 4 x WM waves: wave (wn, wm) owns NB 16-row tiles of W
-// (rows 16 NB wn ..) and MB 16-row tiles of the batch (rows 16 MB wm ..).  X
+// Workgroup g owns a run of nt <= WN NB consecutive 16-row tiles of W (runs
+// as equal as the tile count allows, so that with one workgroup per CU every
+// CU gets the same work up to one tile); wave (wn, wm) owns NB tiles of that
+// run (wn < nt / NB; a wave whose slot lies past the run only stages X) and
+// MB 16-row tiles of the batch (rows 16 MB wm ..).  X
 // advances one block (256 columns) at a time through two LDS buffers with one
 // barrier per block: the loads of block b + 2 are issued while block b is
 // multiplied and stored after it, so their latency is hidden by a whole block
@@ -491,12 +497,12 @@ __host__ __device__ constexpr size_t tile_buf_bytes() {
   return static_cast<size_t>(MT) * 512 + static_cast<size_t>(MT / 16) * 1024;
 }
 
-template <int NB, int MB, int WM>
-__global__ void __launch_bounds__(256 * WM)
+template <int NB, int MB, int WM, int WN>
+__global__ void __launch_bounds__(64 * WN * WM)
 gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   constexpr int MT = 16 * MB * WM;             // batch rows of the workgroup
-  constexpr int kThreads = 256 * WM;
+  constexpr int kThreads = 64 * WN * WM;
   constexpr size_t kXBytes = static_cast<size_t>(MT) * 512;
   constexpr size_t kBuf = tile_buf_bytes<MT>();
   constexpr int kItems = (MT * 8 + kThreads - 1) / kThreads;  // (row, sub-block) items per thread
@@ -509,10 +515,14 @@ gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y,
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wn = wave & 3, wm = wave >> 2;
+  const int wn = wave % WN, wm = wave / WN;
   const int q = lane >> 4, c = lane & 15;
   const int nb = K >> 8;
-  const int n0 = static_cast<int>(blockIdx.x) * 64 * NB + wn * 16 * NB;
+  const int T = (N + 15) >> 4, G = static_cast<int>(gridDim.x), g = static_cast<int>(blockIdx.x);
+  const int t0 = g * (T / G) + min(g, T % G);
+  const int nt = T / G + (g < T % G ? 1 : 0);
+  const bool active = wn * NB < nt;  // wave-uniform
+  const int n0 = 16 * (t0 + wn * NB);
   const int mw0 = static_cast<int>(blockIdx.y) * MT;           // first batch row of the workgroup
   const size_t row_bytes = static_cast<size_t>(nb) * 144;
   const uint8_t* wr[NB];
@@ -618,29 +628,76 @@ gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y,
         bt2[t][e] = (__float_as_uint(mf[2 * e]) >> 16) | (__float_as_uint(mf[2 * e + 1]) & 0xFFFF0000u);
       }
     }
+    // Two orders of the sub-block loop, both pinning each step's scaling in
+    // place with an empty asm (left alone, the compiler sinks every FMA below
+    // all the block's products and parks those products in registers --
+    // hundreds of them).  With one or two batch tiles per wave the loop is
+    // software-pipelined: iteration s reads the A operands of s + 1, issues
+    // the products of s and then scales those of s - 1, so neither the LDS
+    // nor the matrix-core latency sits in front of a dependent instruction.
+    // With four batch tiles the products of a step already cover that
+    // latency, and the straight order measured faster.
+    if constexpr (MB <= 2) {
+      auto read_a = [&](int s, bf16x8_t (&A)[MB]) {
 #pragma unroll
-    for (int s = 0; s < 8; ++s) {
-      bf16x8_t A[MB];
+        for (int mb = 0; mb < MB; ++mb)
+          A[mb] = *reinterpret_cast<const bf16x8_t*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
+                                                     (c ^ ((s + 4 * q) & 15)) * 16);
+      };
+      auto scale = [&](int s, const f32x4_t (&S)[NB][MB]) {
 #pragma unroll
-      for (int mb = 0; mb < MB; ++mb)
-        A[mb] = *reinterpret_cast<const bf16x8_t*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
-                                                   (c ^ ((s + 4 * q) & 15)) * 16);
+        for (int t = 0; t < NB; ++t)
 #pragma unroll
-      for (int t = 0; t < NB; ++t) {
-        const uint2 pc = r.q[t][s >> 1];
-        const int sh = 4 * (s & 1);
-        const uint32_t bw[4] = {((pc.x >> sh) & 0x000F000Fu) | bias, ((pc.x >> (8 + sh)) & 0x000F000Fu) | bias,
-                                ((pc.y >> sh) & 0x000F000Fu) | bias, ((pc.y >> (8 + sh)) & 0x000F000Fu) | bias};
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bw);
+          for (int mb = 0; mb < MB; ++mb) {
 #pragma unroll
-        for (int mb = 0; mb < MB; ++mb) {
-          const f32x4_t S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(ds[t][s], S[t][mb][i], acc[t][mb][i]);
+            __asm__ __volatile__("" : "+v"(acc[t][mb]));
+          }
+      };
+      bf16x8_t A[2][MB];
+      f32x4_t S[2][NB][MB];
+      read_a(0, A[0]);
 #pragma unroll
-          for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(ds[t][s], S[i], acc[t][mb][i]);
-          // Pin the scaling to its sub-block: left alone, the compiler sinks
-          // every FMA below all the block's products and parks those
-          // products in accumulation registers (hundreds of them).
-          __asm__ __volatile__("" : "+v"(acc[t][mb]));
+      for (int s = 0; s < 8; ++s) {
+        if (s < 7) read_a(s + 1, A[(s + 1) & 1]);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const uint2 pc = r.q[t][s >> 1];
+          const int sh = 4 * (s & 1);
+          const uint32_t bw[4] = {((pc.x >> sh) & 0x000F000Fu) | bias, ((pc.x >> (8 + sh)) & 0x000F000Fu) | bias,
+                                  ((pc.y >> sh) & 0x000F000Fu) | bias, ((pc.y >> (8 + sh)) & 0x000F000Fu) | bias};
+          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb)
+            S[s & 1][t][mb] =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s & 1][mb], B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+        }
+        if (s > 0) scale(s - 1, S[(s - 1) & 1]);
+      }
+      scale(7, S[1]);
+    } else {
+#pragma unroll
+      for (int s = 0; s < 8; ++s) {
+        bf16x8_t A[MB];
+#pragma unroll
+        for (int mb = 0; mb < MB; ++mb)
+          A[mb] = *reinterpret_cast<const bf16x8_t*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
+                                                     (c ^ ((s + 4 * q) & 15)) * 16);
+#pragma unroll
+        for (int t = 0; t < NB; ++t) {
+          const uint2 pc = r.q[t][s >> 1];
+          const int sh = 4 * (s & 1);
+          const uint32_t bw[4] = {((pc.x >> sh) & 0x000F000Fu) | bias, ((pc.x >> (8 + sh)) & 0x000F000Fu) | bias,
+                                  ((pc.y >> sh) & 0x000F000Fu) | bias, ((pc.y >> (8 + sh)) & 0x000F000Fu) | bias};
+          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bw);
+#pragma unroll
+          for (int mb = 0; mb < MB; ++mb) {
+            const f32x4_t S =
+                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(ds[t][s], S[i], acc[t][mb][i]);
+            __asm__ __volatile__("" : "+v"(acc[t][mb]));
+          }
         }
       }
     }
@@ -660,33 +717,52 @@ gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y,
     }
   };
 
-  TileRegs<NB> ra, rb;
-  uint4 xv[kItems][4];
-  load_x(0, xv);
-  load_w(0, ra);
-  load_w(1, rb);
-  stage_x(xv, 0);
-  load_x(1, xv);
-  lds_barrier();
-  int b = 0;
-#pragma unroll 1
-  for (; b + 2 < nb; b += 2) {
-    compute(ra, 0);
-    load_w(b + 2, ra);
-    stage_x(xv, 1);
-    lds_barrier();
-    load_x(b + 2, xv);
-    compute(rb, 1);
-    load_w(b + 3, rb);
+  // The block loop, once with the products and once staging only (a wave
+  // whose tile slot lies past the run): two copies rather than a branch in
+  // the loop, so that the wait counts of the working copy stay exact.  Both
+  // meet the same barriers in the same order.
+  auto run = [&](auto with_products) {
+    constexpr bool kWork = decltype(with_products)::value;
+    TileRegs<NB> ra, rb;
+    uint4 xv[kItems][4];
+    load_x(0, xv);
+    if constexpr (kWork) {
+      load_w(0, ra);
+      load_w(1, rb);
+    }
     stage_x(xv, 0);
+    load_x(1, xv);
     lds_barrier();
-    load_x(b + 3, xv);
-  }
-  compute(ra, 0);
-  if (b + 1 < nb) {
-    stage_x(xv, 1);
-    lds_barrier();
-    compute(rb, 1);
+    int b = 0;
+#pragma unroll 1
+    for (; b + 2 < nb; b += 2) {
+      if constexpr (kWork) {
+        compute(ra, 0);
+        load_w(b + 2, ra);
+      }
+      stage_x(xv, 1);
+      lds_barrier();
+      load_x(b + 2, xv);
+      if constexpr (kWork) {
+        compute(rb, 1);
+        load_w(b + 3, rb);
+      }
+      stage_x(xv, 0);
+      lds_barrier();
+      load_x(b + 3, xv);
+    }
+    if constexpr (kWork) compute(ra, 0);
+    if (b + 1 < nb) {
+      stage_x(xv, 1);
+      lds_barrier();
+      if constexpr (kWork) compute(rb, 1);
+    }
+  };
+  if (active) {
+    run(std::true_type{});
+  } else {
+    run(std::false_type{});
+    return;
   }
 
 #pragma unroll
@@ -716,38 +792,34 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
                        stream, w, N, K, xb, y, M);
     return hipGetLastError();
   }
-#ifndef QMV_TILE_MIN_BATCH
-#define QMV_TILE_MIN_BATCH 17
-#endif
-  if (M < QMV_TILE_MIN_BATCH) {
-    // K split: enough waves for about eight per SIMD, at most 8 per workgroup
-    // and never more than one per block.
+  if (M <= 16) {
+    // X too large for LDS: K split over up to 8 waves per workgroup (about
+    // eight waves per SIMD in all, never more than one per block).
     const unsigned n_groups = static_cast<unsigned>((N + 15) / 16);
     int kw = static_cast<int>((8192 + n_groups - 1) / n_groups);
     kw = kw < 1 ? 1 : (kw > 8 ? 8 : kw);
     kw = kw > nb ? nb : kw;
-    const size_t lds = static_cast<size_t>(kw) * (M <= 16 ? 1 : 2) * 4 * 64 * sizeof(float);
-    if (M <= 16)
-      hipLaunchKernelGGL((gemm_q4_k_bf16_ksplit<1, 1>), dim3(n_groups, 1), dim3(64 * kw), lds, stream,
-                         w, N, K, xb, y, M, kw);
-    else
-      hipLaunchKernelGGL((gemm_q4_k_bf16_ksplit<1, 2>), dim3(n_groups, 1), dim3(64 * kw), lds, stream,
-                         w, N, K, xb, y, M, kw);
+    const size_t lds = static_cast<size_t>(kw) * 4 * 64 * sizeof(float);
+    hipLaunchKernelGGL((gemm_q4_k_bf16_ksplit<1, 1>), dim3(n_groups, 1), dim3(64 * kw), lds, stream,
+                       w, N, K, xb, y, M, kw);
     return hipGetLastError();
   }
-#ifndef QMV_TILE_NB2_MIN_BATCH
-#define QMV_TILE_NB2_MIN_BATCH 100000
-#endif
-  const unsigned n64 = static_cast<unsigned>((N + 63) / 64);
-  if (M <= 32) {
-    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 1, 2>), dim3(n64, (M + 31) / 32), dim3(512),
-                       2 * tile_buf_bytes<32>(), stream, w, N, K, xb, y, M);
-  } else if (M < QMV_TILE_NB2_MIN_BATCH) {
-    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 2, 2>), dim3(n64, (M + 63) / 64), dim3(512),
-                       2 * tile_buf_bytes<64>(), stream, w, N, K, xb, y, M);
+  // 17 <= M: runs of 4-5 weight tiles, one workgroup per CU for each batch
+  // tile of 32, 64 or 128 rows (every CU gets the same work up to one tile).
+  const int T = (N + 15) / 16;
+  int G = device_cus();
+  if (G > T) G = T;
+  if (G < (T + 4) / 5) G = (T + 4) / 5;
+  if (M <= 64) {
+    if (M <= 32)
+      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 1, 2, 5>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<32>(),
+                         stream, w, N, K, xb, y, M);
+    else
+      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 2, 2, 5>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<64>(),
+                         stream, w, N, K, xb, y, M);
   } else {
-    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<2, 2, 2>), dim3((N + 127) / 128, (M + 63) / 64), dim3(512),
-                       2 * tile_buf_bytes<64>(), stream, w, N, K, xb, y, M);
+    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 4, 2, 5>), dim3(G, (M + 127) / 128), dim3(640),
+                       2 * tile_buf_bytes<128>(), stream, w, N, K, xb, y, M);
   }
   return hipGetLastError();
 }
