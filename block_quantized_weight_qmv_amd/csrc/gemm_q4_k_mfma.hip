@@ -445,12 +445,20 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   // t - floor(k nt / W).
   for (int e = tid; e < nt * 256; e += 64 * kStreamWaves) {
     const int tt = e >> 8, r = (e >> 6) & 3, ln = e & 63;
+    // All slots are read first (clamped to a valid one), then the ones that
+    // hold a partial of this tile are added in wave order: reads under the
+    // per-wave test would each wait out the LDS latency in turn.
+    float p[kStreamWaves];
+#pragma unroll
+    for (int k = 0; k < kStreamWaves; ++k) {
+      const int slot = min(max(tt - k * nt / kStreamWaves, 0), 1);
+      p[k] = part[((k * 2 + slot) * 4 + r) * 64 + ln];
+    }
     float v = 0.f;
 #pragma unroll
     for (int k = 0; k < kStreamWaves; ++k) {
       const int ku0 = k * U / kStreamWaves, ku1 = (k + 1) * U / kStreamWaves;
-      if (ku1 > ku0 && ku0 < (tt + 1) * nb && ku1 > tt * nb)
-        v += part[((k * 2 + (tt - k * nt / kStreamWaves)) * 4 + r) * 64 + ln];
+      if (ku1 > ku0 && ku0 < (tt + 1) * nb && ku1 > tt * nb) v += p[k];
     }
     const int m = 4 * (ln >> 4) + r, n = 16 * (t0 + tt) + (ln & 15);
     if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = v;
