@@ -1,0 +1,79 @@
+"""bench.py's host-side bookkeeping (CPU only).
+
+* The kernel instantiation bench.py names for each workload (the key of its
+  per-kernel timings and of the committed counter figures) must exist in the
+  built library -- it mirrors the launcher's routing, and this catches drift.
+* Algorithmic bytes per launch = packed weights + each activation once + y,
+  with packed sizes from the library; flops = 2 batch rows cols.
+* More than one GPU is refused with an explanation.
+"""
+import os
+import re
+import shutil
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+
+import bench  # noqa: E402
+from block_quantized_weight_qmv_amd import qmv  # noqa: E402
+from synth import CONFIGS  # noqa: E402
+
+CASES = [(c, b) for c, cfg in CONFIGS.items() for b in cfg["batch"]] + [(5, 3), (5, 17), (5, 33), (5, 65)]
+
+
+def _library_kernels():
+    if shutil.which("nm") is None or not os.path.exists(qmv.LIB_PATH):
+        pytest.skip("nm or the built library is not available")
+    out = subprocess.run(["nm", "-C", qmv.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    names = set()
+    # this nm leaves the _Float16 instantiations mangled
+    f16 = re.compile(r"_ZN3qmv11gemv_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchE")
+    for line in out.splitlines():
+        m = f16.search(line)
+        if m:
+            names.add(f"qmv::gemv_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, {m.group(4)}>")
+            continue
+        if "qmv::gemv_kernel<" in line or "qmv::gemm_q4_k_bf16_" in line:
+            sym = line.split(" ", 2)[2]
+            sym = sym[5:] if sym.startswith("void ") else sym
+            names.add(sym.split("(")[0])
+    return names
+
+
+@pytest.mark.parametrize("config,batch", CASES)
+def test_named_kernel_exists_in_library(config, batch):
+    names = _library_kernels()
+    plan = bench.workload_plan(config, batch, separate=False)
+    for k in plan["kname"]:
+        assert k in names, (k, sorted(n for n in names if k.split("<")[0] in n))
+
+
+@pytest.mark.parametrize("config,batch", CASES)
+def test_algorithmic_bytes_and_flops(config, batch):
+    plan = bench.workload_plan(config, batch, separate=False)
+    xb = {"f32": 4, "f16": 2, "bf16": 2}[plan["x_dtype"]]
+    mats = plan["mats"]
+    for gi, g in enumerate(plan["groups"]):
+        w = sum(qmv.qmv_packed_size(plan["fmt"], mats[m][1], mats[m][2]) for m in g)
+        y = sum(batch * mats[m][1] * 4 for m in g)
+        x = batch * mats[g[0]][2] * xb           # one activation per launch
+        assert all(mats[m][2] == mats[g[0]][2] for m in g)
+        assert plan["gbytes"][gi] == w + x + y
+        assert plan["gflops"][gi] == sum(2.0 * batch * mats[m][1] * mats[m][2] for m in g)
+    assert plan["dom"] in plan["kname"]
+
+
+def test_decode_groups_share_activations():
+    assert bench.decode_groups(["q", "k", "v", "o", "gate", "up", "down"]) == [[0, 1, 2], [3], [4, 5], [6]]
+    assert bench.decode_groups(["gate", "up", "down"]) == [[0, 1], [2]]
+    assert bench.decode_groups(["w"]) == [[0]]
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "single GPU" in r.stderr
