@@ -68,10 +68,10 @@ def kernel_source_hash(kernel: str) -> str:
 def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
     """Instantiation the library launches for matrices of these widths in one
     launch (mirrors the dispatch in api.cpp and the GEMV launcher: Q4_K x bf16
-    with batch >= 3 -> one of the matrix-core kernels, chosen by batch and by
+    with batch >= 2 -> one of the matrix-core kernels, chosen by batch and by
     whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
     split))."""
-    if fmt == "q4_k" and x_dtype == "bf16" and batch >= 3:
+    if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:
         nb = max(cols_list) // 256
         if batch <= 16 and nb * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024:  # X fits in LDS
             return "qmv::gemm_q4_k_bf16_stream"

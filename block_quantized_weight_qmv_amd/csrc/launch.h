@@ -31,7 +31,10 @@ hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t bat
 
 // Batched Q4_K x bf16 on MFMA (gemm_q4_k_mfma.hip); the GEMV entry points use
 // it for batches of at least kMfmaMinBatch rows.
-constexpr int64_t kMfmaMinBatch = 3;
+#ifndef QMV_MFMA_MIN_BATCH
+#define QMV_MFMA_MIN_BATCH 2
+#endif
+constexpr int64_t kMfmaMinBatch = QMV_MFMA_MIN_BATCH;
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t s);
 

@@ -153,7 +153,7 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * x is [batch][cols] of x_dtype (QMV_F32, QMV_F16 or QMV_BF16), y is
  * [batch][rows] fp32; x and y device pointers, 16-byte aligned.  Enqueues on
  * `stream` and returns; legal inside HIP stream capture.  For Q4_K with bf16
- * activations and batch >= 3 the call runs the matrix-core path (weights read
+ * activations and batch >= 2 the call runs the matrix-core path (weights read
  * once for up to 16 activation rows, once per tile of 32, 64 or 128 rows
  * above; exact products, fp32 sums, results independent of timing);
  * otherwise each activation row is a GEMV over the packed weights. */

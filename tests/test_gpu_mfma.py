@@ -1,4 +1,4 @@
-"""Batched Q4_K x bf16 on the matrix-core path (qmv_gemv with batch >= 3).
+"""Batched Q4_K x bf16 on the matrix-core path (qmv_gemv with batch >= 2).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
@@ -8,7 +8,7 @@ paths and are checked exactly.  Shapes cover the three kernels behind the call
 (batch <= 16 with X in LDS: one to eight 16-row tiles per workgroup and more
 workgroups than CUs; batch <= 32 or K too long for LDS: K split over waves;
 larger batches: 64 x 64 tiles), ragged rows and batches, the smallest batch
-routed here (3), and the full-size batched workload (18944 x 3584, M = 4, 16,
+routed here (2), and the full-size batched workload (18944 x 3584, M = 4, 16,
 64 and 512) on sampled rows.
 """
 import numpy as np
@@ -28,7 +28,8 @@ TOL = 2e-3
                                              (200, 14, 128), (1, 2, 64), (70, 3, 3), (67, 5, 4),
                                              (96, 2, 16), (65, 3, 17), (40, 2, 32), (33, 4, 33),
                                              (17, 74, 8), (300, 9, 24), (1, 1, 3), (16, 1, 31),
-                                             (4100, 2, 5), (40000, 1, 9), (3, 16, 16), (33, 17, 12)])
+                                             (4100, 2, 5), (40000, 1, 9), (3, 16, 16), (33, 17, 12),
+                                             (70, 3, 2), (4100, 2, 2), (1, 1, 2), (17, 74, 2)])
 def test_mfma_matches_oracle(rows, nblk, batch):
     cols = nblk * 256
     say(f"mfma q4_k {rows}x{cols} batch {batch}")
