@@ -70,7 +70,7 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
     launch (mirrors the dispatch in api.cpp and the GEMV launcher: Q4_K x bf16
     with batch >= 2 -> one of the matrix-core kernels, chosen by batch and by
     whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
-    split))."""
+    split), and the shared-activation kernel when no matrix splits K))."""
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:
         nb = max(cols_list) // 256
         if batch <= 16 and nb * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024:  # X fits in LDS
@@ -82,7 +82,11 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
         return "qmv::gemm_q4_k_bf16_tile<1, 2, 2, 5>" if batch <= 64 else "qmv::gemm_q4_k_bf16_tile<1, 4, 2, 5>"
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096, "q5_k": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
-    cfg = "2, 2, 256" if waves <= 4 else ("2, 2, 512" if waves <= 8 else "1, 2, 1024")
+    kw = max(-(-c // per_wave) for c in cols_list)
+    if kw == 1:
+        cfg = "2, 2, 256, true"
+    else:
+        cfg = "2, 2, 256, false" if waves <= 4 else ("2, 2, 512, false" if waves <= 8 else "1, 2, 1024, false")
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
            "int4_g128": "Int4G128Policy", "q5_k": "Q5KPolicy"}[fmt]
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]

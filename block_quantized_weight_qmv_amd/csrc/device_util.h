@@ -71,14 +71,55 @@ __device__ __forceinline__ float cvt_ubyte(uint32_t v) {
   return static_cast<float>((v >> (8 * B)) & 0xFFu);
 }
 
-// Raw activation loads: N elements of XT starting at a 16-byte aligned element,
+// Where activations are read from.  Both sources hand out 16-byte chunks by
+// element index (the index of the chunk's first element, a multiple of
+// 16 / sizeof(XT)).
+//  * XGlobal: the activation row in global memory.
+//  * XShared: a copy of the row in LDS, written by xshared_slot().  Chunk g
+//    of the row sits in slot g ^ ((g >> 4) & 15): the low four bits of the
+//    slot (its group of four banks) are rotated by bits 4-7 of g, so lanes
+//    whose chunks lie 256 bytes apart (the GEMV lane mappings) fall on
+//    different banks.  Slots stay within the row's chunk count rounded up to
+//    a multiple of 16.
+template <typename XT>
+struct XGlobal {
+  typedef XT elem;
+  const XT* p;
+  __device__ uint4 chunk(int e) const { return *reinterpret_cast<const uint4*>(p + e); }
+};
+
+__device__ __forceinline__ int xshared_slot(int g) { return g ^ ((g >> 4) & 15); }
+
+template <typename XT>
+struct XShared {
+  typedef XT elem;
+  const uint4* lds;
+  __device__ uint4 chunk(int e) const {
+    return lds[xshared_slot(e / static_cast<int>(16 / sizeof(XT)))];
+  }
+};
+
+// Raw activation loads: N elements starting at element e (16-byte aligned),
 // as N * sizeof(XT) / 16 uint4 words; converted later by x_to_f32 so that the
 // conversion does not force a wait before the weight loads are issued.
-template <int N, typename XT>
-__device__ __forceinline__ void load_x_raw(const XT* p, uint4* raw) {
+template <int N, class XS>
+__device__ __forceinline__ void load_x_raw(const XS& x, int e, uint4* raw) {
+  constexpr int kPer = 16 / static_cast<int>(sizeof(typename XS::elem));
 #pragma unroll
-  for (int i = 0; i < N * static_cast<int>(sizeof(XT)) / 16; ++i)
-    raw[i] = reinterpret_cast<const uint4*>(p)[i];
+  for (int i = 0; i < N / kPer; ++i) raw[i] = x.chunk(e + i * kPer);
+}
+
+// Workgroup barrier for LDS hand-offs: waits only for this wave's LDS
+// operations (lgkmcnt(0); vmcnt and expcnt left at their maxima), then
+// s_barrier.  __syncthreads() also fences global memory, which makes every
+// wave wait for all of its outstanding loads, the weight prefetch included.
+// The empty asm statements keep the compiler from moving memory accesses
+// across.
+__device__ __forceinline__ void lds_barrier() {
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  __builtin_amdgcn_s_barrier();
+  __asm__ __volatile__("" ::: "memory");
 }
 
 template <int N>

@@ -50,19 +50,6 @@ namespace qmv {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
-// Workgroup barrier for LDS hand-offs: waits only for this wave's LDS
-// operations (lgkmcnt(0); vmcnt and expcnt left at their maxima), then
-// s_barrier.  __syncthreads() also fences global memory, which makes every
-// wave wait for all of its outstanding loads -- here the weight prefetch of
-// the next blocks, which would then be drained at every barrier.  The empty
-// asm statements keep the compiler from moving memory accesses across.
-__device__ __forceinline__ void lds_barrier() {
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);
-  __builtin_amdgcn_s_barrier();
-  __asm__ __volatile__("" ::: "memory");
-}
-
 // v with every bit cleared unless keep: an AND with a mask the compiler cannot
 // see through.  A select of a loaded value is turned into a branch around the
 // load, and a load under a branch makes the wait-count analysis wait for

@@ -50,11 +50,11 @@ struct Int4G128Policy {
     }
   }
 
-  template <typename XT>
-  __device__ void load_x_raw(const XT* x, uint4* raw) const {
-    constexpr int kPer = 32 * static_cast<int>(sizeof(XT)) / 16;
-    qmv::load_x_raw<32>(x + col[0], raw);
-    qmv::load_x_raw<32>(x + col[1], raw + kPer);
+  template <class XS>
+  __device__ void load_x_raw(const XS& x, uint4* raw) const {
+    constexpr int kPer = 32 * static_cast<int>(sizeof(typename XS::elem)) / 16;
+    qmv::load_x_raw<32>(x, col[0], raw);
+    qmv::load_x_raw<32>(x, col[1], raw + kPer);
   }
 
   template <typename XT>

@@ -72,9 +72,9 @@ struct Q5KPolicy {
     rg = c2 + 1u;
   }
 
-  template <typename XT>
-  __device__ void load_x_raw(const XT* x, uint4* raw) const {
-    qmv::load_x_raw<64>(x + col0, raw);
+  template <class XS>
+  __device__ void load_x_raw(const XS& x, uint4* raw) const {
+    qmv::load_x_raw<64>(x, col0, raw);
   }
 
   template <typename XT>

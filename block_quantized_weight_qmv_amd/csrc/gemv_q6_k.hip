@@ -49,11 +49,11 @@ struct Q6KPolicy {
     col0 = jc * 256 + 128 * h + 16 * i;
   }
 
-  template <typename XT>
-  __device__ void load_x_raw(const XT* x, uint4* raw) const {
-    constexpr int kPer = 16 * static_cast<int>(sizeof(XT)) / 16;  // uint4 words per run of 16
+  template <class XS>
+  __device__ void load_x_raw(const XS& x, uint4* raw) const {
+    constexpr int kPer = 16 * static_cast<int>(sizeof(typename XS::elem)) / 16;  // uint4 words per run of 16
 #pragma unroll
-    for (int g = 0; g < 4; ++g) qmv::load_x_raw<16>(x + col0 + 32 * g, raw + g * kPer);
+    for (int g = 0; g < 4; ++g) qmv::load_x_raw<16>(x, col0 + 32 * g, raw + g * kPer);
   }
 
   template <typename XT>

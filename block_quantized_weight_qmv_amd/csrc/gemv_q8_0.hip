@@ -40,9 +40,9 @@ struct Q80Policy {
     col0 = jc * 32;
   }
 
-  template <typename XT>
-  __device__ void load_x_raw(const XT* x, uint4* raw) const {
-    qmv::load_x_raw<32>(x + col0, raw);
+  template <class XS>
+  __device__ void load_x_raw(const XS& x, uint4* raw) const {
+    qmv::load_x_raw<32>(x, col0, raw);
   }
 
   template <typename XT>

@@ -20,6 +20,13 @@
 //    block and carry a zero x slice), so the compiler can track them exactly:
 //    the x slice and two tiles are requested before the first wait, and the
 //    next tile is requested before the current one is consumed.
+//  * When every matrix of the launch fits one wave's K slice (kw == 1, the
+//    SX kernels), all waves of a workgroup need the same activations: the
+//    workgroup reads x from global memory once, a quarter per wave, into LDS,
+//    and each wave takes its slice from there.  Read per wave instead, x
+//    (16 KB per wave for fp32 x and 4096 columns) is a large share of what
+//    the compute unit's vector memory path has to move before the first
+//    weights arrive.
 //  * The R row partials of a tile are reduced together: two DPP exchange
 //    steps leave each lane of a quad with one row's quad sum, then rotations
 //    within rows of 16 lanes and swaps across rows finish the sum.  The order
@@ -125,7 +132,7 @@ struct GemvLaunch {
   GemvItem item[kMaxItems];
 };
 
-template <class P, typename XT, int R, int D, int MAXT>
+template <class P, typename XT, int R, int D, int MAXT, bool SX>
 __global__ void __launch_bounds__(MAXT)
 gemv_kernel(const GemvLaunch args) {
   // This workgroup's matrix (wave-uniform scan over at most kMaxItems).
@@ -137,31 +144,67 @@ gemv_kernel(const GemvLaunch args) {
 
   const int lane = __lane_id();
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kw = m.kw;
-  if (wave >= kw * m.sets_per_wg) return;  // spare waves of a kw > 1 workgroup
+  const int kw = SX ? 1 : m.kw;
+  if (!SX && wave >= kw * m.sets_per_wg) return;  // spare waves of a kw > 1 workgroup
   const int kslot = wave % kw;
   const int set = (blockIdx.x - m.wg_begin) * m.sets_per_wg + wave / kw;
-  if (set >= m.nsets) return;  // only with kw == 1, where no barrier is shared
+  // Only with kw == 1, where no barrier is shared.  The SX kernels keep such
+  // waves to the x copy and give them no rows.
+  if (!SX && set >= m.nsets) return;
   const XT* x = static_cast<const XT*>(m.x) + static_cast<size_t>(blockIdx.y) * m.cols;
   float* y = m.y + static_cast<size_t>(blockIdx.y) * m.rows;
-  const int r_begin = set * m.q + min(set, m.rem);
-  const int r_end = r_begin + m.q + (set < m.rem ? 1 : 0);
+  int r_begin = set * m.q + min(set, m.rem);
+  int r_end = r_begin + m.q + (set < m.rem ? 1 : 0);
+  if (SX && set >= m.nsets) r_begin = r_end = m.rows;  // tile loads clamp to the last row
   const int r_last = r_end - 1;
 
-  // K-split partial sums: one column of part_stride floats per wave.
+  // K-split partial sums: one column of part_stride floats per wave; in the
+  // SX kernels, the workgroup's copy of x.
   extern __shared__ float part_lds[];
   float* part = part_lds + wave * args.part_stride;
   const P pol(m.w, m.scales_offset, m.cols, kslot, lane);
 
-  // Issue order: x slice, tile 0, tile 1; only then wait for x.
   uint4 raw[P::kXElems * sizeof(XT) / 16];
-  pol.load_x_raw(x, raw);
-  __builtin_amdgcn_sched_barrier(0);
   typename P::Frag f[D][R];
+  if constexpr (SX) {
+    // Issue order: this thread's x chunks, tile 0, tile 1; the chunks are
+    // stored to LDS once they arrive (the tiles stay in flight), then every
+    // wave reads its slice.  Chunk indices past the row's end are clamped:
+    // those threads re-read and re-store the last chunk.
+    constexpr int kChunks = P::kColsPerWave * static_cast<int>(sizeof(XT)) / 16;
+    constexpr int kPerThread = (kChunks + MAXT - 1) / MAXT;
+    // (A native vector type: copies of uint4, a struct, become memcpy calls
+    // that keep the array in scratch memory.)
+    typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+    const int nchunks = m.cols * static_cast<int>(sizeof(XT)) / 16;
+    const u32x4* gx = reinterpret_cast<const u32x4*>(x);
+    u32x4 xc[kPerThread];
+    int slot[kPerThread];
 #pragma unroll
-  for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
-  __asm__ __volatile__("" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
+    for (int k = 0; k < kPerThread; ++k) {
+      const int g = min(static_cast<int>(threadIdx.x) + k * MAXT, nchunks - 1);
+      xc[k] = gx[g];
+      slot[k] = xshared_slot(g);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+    u32x4* xl = reinterpret_cast<u32x4*>(part_lds);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) xl[slot[k]] = xc[k];
+    lds_barrier();
+    pol.load_x_raw(XShared<XT>{reinterpret_cast<const uint4*>(part_lds)}, raw);
+  } else {
+    // Issue order: x slice, tile 0, tile 1; only then wait for x.
+    pol.load_x_raw(XGlobal<XT>{x}, raw);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
+    __asm__ __volatile__("" ::: "memory");
+    __builtin_amdgcn_sched_barrier(0);
+  }
   typename P::XSlice xs;
   pol.template finish_x<XT>(raw, xs);
 
@@ -201,7 +244,7 @@ gemv_kernel(const GemvLaunch args) {
   // K split: after one barrier, the kw waves of the set add the columns of
   // their set in slot order, row by row (waves that left early count as
   // arrived at a barrier).
-  if (kw > 1) {
+  if (!SX && kw > 1) {
     __syncthreads();
     const float* cols = part_lds + (wave - kslot) * args.part_stride;
     for (int j = kslot * 64 + lane; j < r_end - r_begin; j += kw * 64) {
@@ -305,11 +348,12 @@ inline int64_t resident_workgroups(K kernel, int block) {
 constexpr int kMaxWavesPerSimd = QMV_WAVES_PER_SIMD;
 constexpr int kMinRowsPerWave = QMV_MIN_ROWS_PER_WAVE;
 
-template <class P, typename XT, int R, int D, int MAXT>
+template <class P, typename XT, int R, int D, int MAXT, bool SX>
 hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream,
                       int waves_per_simd) {
-  auto kernel = gemv_kernel<P, XT, R, D, MAXT>;
+  auto kernel = gemv_kernel<P, XT, R, D, MAXT, SX>;
   const int block = 64 * waves;
+  if (SX && block != MAXT) return hipErrorInvalidValue;  // the x copy assumes MAXT threads
   const int cus = device_cus();
   int64_t wave_rows = 0;
   for (int i = 0; i < n; ++i)
@@ -326,7 +370,13 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   if (target > resident) target = resident;
   GemvLaunch L;
   const int grid = plan_gemv<P>(calls, n, waves, target, &L);
-  const size_t lds = static_cast<size_t>(waves) * L.part_stride * sizeof(float);
+  size_t lds = static_cast<size_t>(waves) * L.part_stride * sizeof(float);
+  if (SX) {  // the x copy: the longest row's chunks, rounded up to 16 (xshared_slot)
+    int64_t cols = 0;
+    for (int i = 0; i < n; ++i) cols = calls[i].W->cols > cols ? calls[i].W->cols : cols;
+    const int64_t chunks = (cols * static_cast<int64_t>(sizeof(XT)) / 16 + 15) / 16 * 16;
+    lds = static_cast<size_t>(chunks) * 16;
+  }
   hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(block), lds, stream,
                      L);
   return hipGetLastError();
@@ -342,9 +392,10 @@ hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStr
   // flight, or two waves with 4, were no faster in total; the younger wave of
   // a SIMD trails the older one under the oldest-first issue order, but a
   // deeper single wave loses more on the small matrices and at steady state.)
-  if (waves <= 4) return launch_cfg<P, XT, 2, 2, 256>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
-  if (waves <= 8) return launch_cfg<P, XT, 2, 2, 512>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
-  return launch_cfg<P, XT, 1, 2, 1024>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+  if (kw == 1) return launch_cfg<P, XT, 2, 2, 256, true>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+  if (waves <= 4) return launch_cfg<P, XT, 2, 2, 256, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+  if (waves <= 8) return launch_cfg<P, XT, 2, 2, 512, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+  return launch_cfg<P, XT, 1, 2, 1024, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
 }
 
 template <class P>

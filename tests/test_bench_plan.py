@@ -31,11 +31,12 @@ def _library_kernels():
     out = subprocess.run(["nm", "-C", qmv.LIB_PATH], capture_output=True, text=True, check=True).stdout
     names = set()
     # this nm leaves the _Float16 instantiations mangled
-    f16 = re.compile(r"_ZN3qmv11gemv_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchE")
+    f16 = re.compile(r"_ZN3qmv11gemv_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELb([01])EEEvNS_10GemvLaunchE")
     for line in out.splitlines():
         m = f16.search(line)
         if m:
-            names.add(f"qmv::gemv_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, {m.group(4)}>")
+            sx = "true" if m.group(5) == "1" else "false"
+            names.add(f"qmv::gemv_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, {m.group(4)}, {sx}>")
             continue
         if "qmv::gemv_kernel<" in line or "qmv::gemm_q4_k_bf16_" in line:
             sym = line.split(" ", 2)[2]
