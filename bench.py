@@ -466,7 +466,7 @@ def main() -> int:
         achieved, peak, unit = dom_bytes_per_launch / (dom_avg_us * 1e-6) / 1e9, PEAK_GBPS, "GB/s"
     detail = kern
 
-    # -- HBM read ceiling on this GPU (128-bit streaming read of 2 GiB) ----------------
+    # -- HBM read ceiling on this GPU (nontemporal 128-bit streaming read of 2 GiB) ------
     nb = 2 * 2 ** 30
     buf = torch.empty(nb, dtype=torch.uint8, device=dev)
     buf.fill_(1)

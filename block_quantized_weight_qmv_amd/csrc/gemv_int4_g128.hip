@@ -9,7 +9,9 @@
 // Lane mapping: a wave covers 4096 columns = 2048 code bytes of a row.  Lane l
 // owns code bytes [16l, 16l+16) and [1024+16l, 1024+16l+16), so each of the two
 // 16-byte load instructions reads 1 KB of consecutive bytes, plus the fp16
-// scale of each half's group.  Per lane, half and row, fp32 (codes enter as
+// scale of each half's group.  The code loads carry the nontemporal hint: no
+// other instruction reads their lines (a row's code bytes are a multiple of
+// 64 B, so only a row boundary can split a line).  Per lane, half and row, fp32 (codes enter as
 // fp16 subnormals, see device_util.h):
 //   Se = sum u_even x_even 2^-24,  So = sum 16 u_odd x_odd 2^-24
 //   partial += s (2^24 (Se + So/16) - 8 X),  X = sum of the half's 32 activations
@@ -74,7 +76,7 @@ struct Int4G128Policy {
   __device__ void load(int row, Frag& f) const {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      f.q[h] = ld16(codes[h] + static_cast<size_t>(row) * code_row);
+      f.q[h] = ld16_stream(codes[h] + static_cast<size_t>(row) * code_row);
       f.sb[h] = ld_u16(scales[h] + static_cast<size_t>(row) * scale_row);
     }
   }

@@ -8,29 +8,43 @@ namespace qmv {
 
 constexpr int kProbeThreads = 256;
 constexpr int kProbeUnroll = 4;
+constexpr int64_t kProbeMaxBlocks = 1024;
 
 int64_t probe_read_blocks(uint64_t nbytes) {
   const int64_t vec = static_cast<int64_t>(nbytes / 16);
   int64_t blocks = (vec + kProbeThreads * kProbeUnroll - 1) / (kProbeThreads * kProbeUnroll);
-  if (blocks > 4096) blocks = 4096;
+  if (blocks > kProbeMaxBlocks) blocks = kProbeMaxBlocks;
   if (blocks < 1) blocks = 1;
   return blocks;
 }
 
+// Each workgroup reads one contiguous chunk (a whole number of
+// threads x unroll vectors) with nontemporal 128-bit loads, so every 128-byte
+// line is requested by exactly one load instruction.  Among the access
+// patterns, grid shapes and cache hints measured on gfx950 (grid-stride,
+// chunk per workgroup, chunk per wave; plain and nontemporal; 256-8192
+// workgroups), this is the fastest family for a 2 GiB stream: about 7.0 TB/s,
+// against 5.5-6.2 TB/s for the same loads without the hint.
 __global__ void __launch_bounds__(kProbeThreads)
 probe_read_kernel(const uint4* __restrict__ src, int64_t nvec, float* __restrict__ out) {
+  typedef uint32_t v4_t __attribute__((ext_vector_type(4)));
+  const v4_t* p = reinterpret_cast<const v4_t*>(src);
+  constexpr int64_t kStep = static_cast<int64_t>(kProbeThreads) * kProbeUnroll;
+  int64_t chunk = (nvec + gridDim.x - 1) / gridDim.x;
+  chunk = (chunk + kStep - 1) / kStep * kStep;
+  const int64_t begin = static_cast<int64_t>(blockIdx.x) * chunk;
+  const int64_t end = begin + chunk < nvec ? begin + chunk : nvec;
   uint32_t acc = 0;
-  const int64_t stride = static_cast<int64_t>(gridDim.x) * kProbeThreads;
-  int64_t i = static_cast<int64_t>(blockIdx.x) * kProbeThreads + threadIdx.x;
-  for (; i + (kProbeUnroll - 1) * stride < nvec; i += kProbeUnroll * stride) {
-    uint4 v[kProbeUnroll];
+  int64_t i = begin + threadIdx.x;
+  for (; i + (kProbeUnroll - 1) * kProbeThreads < end; i += kStep) {
+    v4_t v[kProbeUnroll];
 #pragma unroll
-    for (int u = 0; u < kProbeUnroll; ++u) v[u] = src[i + u * stride];
+    for (int u = 0; u < kProbeUnroll; ++u) v[u] = __builtin_nontemporal_load(p + i + u * kProbeThreads);
 #pragma unroll
     for (int u = 0; u < kProbeUnroll; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
   }
-  for (; i < nvec; i += stride) {
-    const uint4 v = src[i];
+  for (; i < end; i += kProbeThreads) {
+    const v4_t v = __builtin_nontemporal_load(p + i);
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
   }
   __shared__ uint32_t red[kProbeThreads];

@@ -190,8 +190,10 @@ int32_t qmv_dequant(const qmv_weights* W, void* out, int32_t out_dtype,
                     void* stream);
 
 /* Measurement kernels for the HBM roofline (not part of the GEMV path).
- * qmv_probe_read streams nbytes (multiple of 16) from src with 128-bit loads
- * and writes one fp32 per workgroup to out (out must hold
+ * qmv_probe_read streams nbytes (multiple of 16) from src with nontemporal
+ * 128-bit loads, one contiguous chunk per workgroup (the fastest streaming
+ * read measured on the part), and writes one fp32 per workgroup to out (out
+ * must hold
  * qmv_probe_read_outputs(nbytes) floats).  qmv_probe_copy copies nbytes
  * (multiple of 16) from src to dst with 128-bit loads and stores. */
 int64_t qmv_probe_read_outputs(uint64_t nbytes);
