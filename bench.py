@@ -47,6 +47,7 @@ _KERNEL_SOURCES = {
     "gemm_q4_k_bf16_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
 }
 _POLICY_SOURCE = {"Q80Policy": "gemv_q8_0.hip", "Q4KPolicy": "gemv_q4_k.hip",
+                  "Q4KPlanesPolicy": "gemv_q4_k.hip",
                   "Q5KPolicy": "gemv_q5_k.hip", "Q6KPolicy": "gemv_q6_k.hip",
                   "Int4G128Policy": "gemv_int4_g128.hip"}
 
@@ -65,12 +66,13 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
+def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str = "blocks") -> str:
     """Instantiation the library launches for matrices of these widths in one
     launch (mirrors the dispatch in api.cpp and the GEMV launcher: Q4_K x bf16
     with batch >= 2 -> one of the matrix-core kernels, chosen by batch and by
     whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
-    split), and the shared-activation kernel when no matrix splits K))."""
+    split), and the shared-activation kernel when no matrix splits K; Q4_K
+    weights in the plane layout take the plane policy))."""
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:
         nb = max(cols_list) // 256
         if batch <= 16 and nb * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024:  # X fits in LDS
@@ -89,6 +91,8 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1) -> str:
         cfg = "2, 2, 256, false" if waves <= 4 else ("2, 2, 512, false" if waves <= 8 else "1, 2, 1024, false")
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
            "int4_g128": "Int4G128Policy", "q5_k": "Q5KPolicy"}[fmt]
+    if layout == "planes":
+        pol = "Q4KPlanesPolicy"
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
     return f"qmv::gemv_kernel<qmv::{pol}, {xt}, {cfg}>"
 
@@ -162,7 +166,18 @@ def cpu_baseline(mats, fmt, x_dtype, fields_list, xs, seconds):
 PEAK_TFLOPS_BF16 = 2500.0   # MI355X dense bf16 matrix cores, vendor figure
 
 
-def workload_plan(config: int, batch: int | None, separate: bool) -> dict:
+def default_layout(config: int, batch: int | None) -> str:
+    """Q4_K on the GEMV path streams the plane layout (repacked once at load,
+    as a decode layout replacing the blocks); the matrix-core path and the
+    other formats read the canonical blocks."""
+    from synth import CONFIGS
+    cfg = CONFIGS[config]
+    b = batch or cfg["batch"][0]
+    gemv = not (cfg["x_dtype"] == "bf16" and b >= 2)
+    return "planes" if cfg["fmt"] == "q4_k" and gemv else "blocks"
+
+
+def workload_plan(config: int, batch: int | None, separate: bool, layout: str = "blocks") -> dict:
     """Launches of one step and their algorithmic bytes and flops (no GPU needed).
 
     Bytes per launch = packed weights + each activation once + y; flops =
@@ -179,11 +194,12 @@ def workload_plan(config: int, batch: int | None, separate: bool) -> dict:
     names = [n for n, _, _ in mats]
     groups = [[m] for m in range(len(mats))] if separate else decode_groups(names)
     xb = {"f32": 4, "f16": 2, "bf16": 2}[x_dtype]
-    wbytes = [int(qmv.qmv_packed_size(fmt, r, c)) for _, r, c in mats]
+    size = qmv.qmv_planes_size if layout == "planes" else qmv.qmv_packed_size
+    wbytes = [int(size(fmt, r, c)) for _, r, c in mats]
     gbytes = [sum(wbytes[m] + batch * mats[m][1] * 4 for m in g) + batch * mats[g[0]][2] * xb
               for g in groups]
     gflops = [sum(2.0 * batch * mats[m][1] * mats[m][2] for m in g) for g in groups]
-    kname = [kernel_name(fmt, [mats[m][2] for m in g], x_dtype, batch) for g in groups]
+    kname = [kernel_name(fmt, [mats[m][2] for m in g], x_dtype, batch, layout) for g in groups]
     balance = PEAK_TFLOPS_BF16 * 1e12 / (PEAK_GBPS * 1e9)
     bound = ["mfma" if kname[i].startswith("qmv::gemm") and gflops[i] / gbytes[i] > balance
              else "hbm" for i in range(len(groups))]
@@ -195,7 +211,7 @@ def workload_plan(config: int, batch: int | None, separate: bool) -> dict:
     return {"cfg": cfg, "fmt": fmt, "x_dtype": x_dtype, "batch": batch, "mats": mats,
             "names": names, "groups": groups, "wbytes": wbytes, "gbytes": gbytes,
             "gflops": gflops, "kname": kname, "bound": bound, "by_kernel": by_kernel,
-            "dom": dom, "workload": workload,
+            "dom": dom, "workload": workload, "layout": layout,
             "launch_names": ["+".join(names[m] for m in g) for g in groups]}
 
 
@@ -231,7 +247,7 @@ def summarize_counters(args) -> int:
     and of `python -m block_quantized_weight_qmv_amd.probe copy --mib N` for the
     scale factors (a copy of N MiB reads and writes N MiB)."""
     fetch_d, write_d, cfetch_d, cwrite_d = args.summarize_counters
-    plan = workload_plan(args.config, args.batch, args.separate)
+    plan = workload_plan(args.config, args.batch, args.separate, _layout(args))
     groups, kname, gbytes = plan["groups"], plan["kname"], plan["gbytes"]
     copy_kib = args.copy_mib * 1024.0
 
@@ -308,6 +324,10 @@ def summarize_counters(args) -> int:
     return 0
 
 
+def _layout(args) -> str:
+    return default_layout(args.config, args.batch) if args.layout == "auto" else args.layout
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -319,6 +339,8 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true", help="one launch per matrix")
+    ap.add_argument("--layout", choices=["auto", "blocks", "planes"], default="auto",
+                    help="weight layout in HBM (auto: planes for Q4_K on the GEMV path, else blocks)")
     ap.add_argument("--eager-pass", action="store_true",
                     help="only issue warmup + steps eagerly (no graphs, no timing): for counter runs")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
@@ -344,7 +366,8 @@ def main() -> int:
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    plan = workload_plan(args.config, args.batch, args.separate)
+    layout = _layout(args)
+    plan = workload_plan(args.config, args.batch, args.separate, layout)
     cfg, fmt, x_dtype, batch = plan["cfg"], plan["fmt"], plan["x_dtype"], plan["batch"]
     mats, names, groups = plan["mats"], plan["names"], plan["groups"]
     gbytes, gflops, kname, by_kernel, dom = (plan["gbytes"], plan["gflops"], plan["kname"],
@@ -367,8 +390,7 @@ def main() -> int:
             xs.append(xs[leader[i]])
             xs_dev.append(xs_dev[leader[i]])
         ys.append(torch.empty(batch, rows, dtype=torch.float32, device=dev))
-    step_w_bytes = sum(p.numel() for p in packed_dev)
-    assert step_w_bytes == sum(plan["wbytes"])
+    step_w_bytes = sum(plan["wbytes"])
     step_bytes = sum(gbytes)
     copies = max(1, int(np.ceil(args.rotate_gib * 2 ** 30 / step_w_bytes)))
     descs = []  # descs[c][m]
@@ -377,9 +399,17 @@ def main() -> int:
         row = []
         for m, (name, rows, cols) in enumerate(mats):
             t = packed_dev[m] if c == 0 else packed_dev[m].clone()
+            d = qmv.qmv_create_weights(fmt, rows, cols, t)
+            if layout == "planes":  # repacked once, at load; the planes replace the blocks
+                planes = torch.empty(plan["wbytes"][m], dtype=torch.uint8, device=dev)
+                d = qmv.qmv_repack_planes(d, planes)
+                torch.cuda.synchronize()
+                t = planes
             keep.append(t)
-            row.append(qmv.qmv_create_weights(fmt, rows, cols, t))
+            row.append(d)
         descs.append(row)
+    if layout == "planes":
+        del packed_dev
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream(dev)
@@ -497,7 +527,7 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "bf16" if dom.startswith("qmv::gemm") else "fp32",
         "data": "synthetic",
-        "config": {"workload": workload, "format": fmt, "batch": batch, "x_dtype": x_dtype,
+        "config": {"workload": workload, "format": fmt, "layout": layout, "batch": batch, "x_dtype": x_dtype,
                    "matrices": {n: f"{r}x{c}" for n, r, c in mats},
                    "launches": ["+".join(names[m] for m in g) for g in groups],
                    "bytes_per_step": int(step_bytes), "weight_copies": copies},

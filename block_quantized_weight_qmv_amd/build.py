@@ -25,7 +25,7 @@ DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-p
           "-munsafe-fp-atomics"]
 
 HIP_SOURCES = ["api.cpp", "gemv_q8_0.hip", "gemv_q4_k.hip", "gemv_q5_k.hip", "gemv_q6_k.hip",
-               "gemv_int4_g128.hip", "gemm_q4_k_mfma.hip", "dequant.hip", "probe.hip"]
+               "gemv_int4_g128.hip", "gemm_q4_k_mfma.hip", "dequant.hip", "repack.hip", "probe.hip"]
 CXX_SOURCES = ["packer.cpp"]
 # Per-source device flags.  The matrix-core kernels scale each product in
 # VALU right away; in accumulation registers every result would need a

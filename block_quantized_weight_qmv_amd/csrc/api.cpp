@@ -14,6 +14,7 @@
 
 #include "api_internal.h"
 #include "launch.h"
+#include "planes.h"
 
 namespace qmv {
 
@@ -55,14 +56,22 @@ static int32_t check_weights(const qmv_weights* W) {
   if (!W) return fail(QMV_ERR_NULL, "weights descriptor is NULL");
   if (!W->data) return fail(QMV_ERR_NULL, "weights data pointer is NULL");
   if (qmv_block_size(W->fmt) == 0) return fail(QMV_ERR_FORMAT, "unknown format %d", W->fmt);
-  const uint64_t need = qmv_packed_size(W->fmt, W->rows, W->cols);
+  if (W->layout != QMV_LAYOUT_BLOCKS && W->layout != QMV_LAYOUT_PLANES)
+    return fail(QMV_ERR_FORMAT, "unknown layout %d", W->layout);
+  const bool planes = W->layout == QMV_LAYOUT_PLANES;
+  if (planes && W->fmt != QMV_Q4_K)
+    return fail(QMV_ERR_UNSUPPORTED, "format %d has no plane layout", W->fmt);
+  const uint64_t need = planes ? qmv_planes_size(W->fmt, W->rows, W->cols)
+                               : qmv_packed_size(W->fmt, W->rows, W->cols);
   if (need == 0)
     return fail(QMV_ERR_SHAPE, "bad weight shape %lld x %lld for format %d", (long long)W->rows,
                 (long long)W->cols, W->fmt);
   if (W->nbytes != need)
     return fail(QMV_ERR_SIZE, "weights hold %llu bytes, format needs %llu",
                 (unsigned long long)W->nbytes, (unsigned long long)need);
-  const uint64_t soff = W->fmt == QMV_INT4_G128 ? static_cast<uint64_t>(W->rows * W->cols / 2) : 0;
+  const uint64_t soff = W->fmt == QMV_INT4_G128 ? static_cast<uint64_t>(W->rows * W->cols / 2)
+                        : planes                ? q4k_planes(W->rows, W->cols).a
+                                                : 0;
   if (W->scales_offset != soff)
     return fail(QMV_ERR_FORMAT, "scales_offset %llu, expected %llu",
                 (unsigned long long)W->scales_offset, (unsigned long long)soff);
@@ -103,6 +112,39 @@ uint64_t qmv_packed_size(int32_t fmt, int64_t rows, int64_t cols) {
   }
 }
 
+uint64_t qmv_planes_size(int32_t fmt, int64_t rows, int64_t cols) {
+  if (fmt != QMV_Q4_K || qmv_packed_size(fmt, rows, cols) == 0) return 0;
+  return qmv::q4k_planes(rows, cols).total;
+}
+
+int32_t qmv_repack_planes(const qmv_weights* src, void* dst, uint64_t dst_bytes, qmv_weights* out,
+                          void* stream) {
+  if (!out) return fail(QMV_ERR_NULL, "output descriptor is NULL");
+  if (!dst) return fail(QMV_ERR_NULL, "destination is NULL");
+  int32_t st = qmv::check_weights(src);
+  if (st != QMV_OK) return st;
+  if (src->layout != QMV_LAYOUT_BLOCKS)
+    return fail(QMV_ERR_UNSUPPORTED, "source is not in the canonical block layout");
+  if (src->fmt != QMV_Q4_K) return fail(QMV_ERR_UNSUPPORTED, "format %d has no plane layout", src->fmt);
+  const uint64_t need = qmv_planes_size(src->fmt, src->rows, src->cols);
+  if (dst_bytes < need)
+    return fail(QMV_ERR_SIZE, "destination holds %llu bytes, planes need %llu",
+                (unsigned long long)dst_bytes, (unsigned long long)need);
+  if (!qmv::aligned16(dst)) return fail(QMV_ERR_ALIGN, "destination not 16-byte aligned");
+  const uintptr_t s0 = reinterpret_cast<uintptr_t>(src->data), s1 = s0 + src->nbytes;
+  const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), d1 = d0 + need;
+  if (s0 < d1 && d0 < s1) return fail(QMV_ERR_SHAPE, "destination overlaps the source");
+  const hipError_t e = qmv::repack_q4_k_planes(*src, dst, static_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return qmv::from_hip(e, "qmv_repack_planes launch");
+  qmv_weights w = *src;
+  w.layout = QMV_LAYOUT_PLANES;
+  w.data = dst;
+  w.nbytes = need;
+  w.scales_offset = qmv::q4k_planes(src->rows, src->cols).a;
+  *out = w;
+  return qmv::ok();
+}
+
 int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols, const void* dev_packed,
                            uint64_t nbytes, qmv_weights* out) {
   if (!out) return fail(QMV_ERR_NULL, "output descriptor is NULL");
@@ -119,7 +161,7 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols, const void* 
     return fail(QMV_ERR_ALIGN, "packed data not 16-byte aligned");
   qmv_weights w;
   w.fmt = fmt;
-  w.reserved = 0;
+  w.layout = QMV_LAYOUT_BLOCKS;
   w.rows = rows;
   w.cols = cols;
   w.data = dev_packed;
@@ -160,6 +202,9 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     if (st != QMV_OK) return st;
     if (it.W->fmt != fmt)
       return fail(QMV_ERR_FORMAT, "item %d has format %d, launch format %d", i, it.W->fmt, fmt);
+    if (it.W->layout != items[0].W->layout)
+      return fail(QMV_ERR_UNSUPPORTED, "item %d has layout %d, item 0 layout %d", i, it.W->layout,
+                  items[0].W->layout);
     if (!it.x || !it.y) return fail(QMV_ERR_NULL, "item %d: x or y is NULL", i);
     if (!qmv::aligned16(it.x) || !qmv::aligned16(it.y))
       return fail(QMV_ERR_ALIGN, "item %d: x or y not 16-byte aligned", i);
@@ -182,14 +227,22 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   // Q4_K with bf16 activations and a batch of at least kMfmaMinBatch rows: the
   // matrix-core kernel, one launch per matrix (the GEMV path would read the
   // weights once per activation row).
+  const bool planes = items[0].W->layout == QMV_LAYOUT_PLANES;
   if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
+    if (planes)
+      return fail(QMV_ERR_UNSUPPORTED,
+                  "the matrix-core path (bf16, batch >= %lld) takes the canonical block layout",
+                  (long long)qmv::kMfmaMinBatch);
     for (int i = 0; i < n && e == hipSuccess; ++i)
       e = qmv::gemm_q4_k_bf16(*calls[i].W, calls[i].x, calls[i].y, batch, s);
     return qmv::from_hip(e, "qmv_gemv (MFMA tiles) launch");
   }
   switch (fmt) {
     case QMV_Q8_0: e = qmv::gemv_q8_0(calls, n, x_dtype, batch, s); break;
-    case QMV_Q4_K: e = qmv::gemv_q4_k(calls, n, x_dtype, batch, s); break;
+    case QMV_Q4_K:
+      e = planes ? qmv::gemv_q4_k_planes(calls, n, x_dtype, batch, s)
+                 : qmv::gemv_q4_k(calls, n, x_dtype, batch, s);
+      break;
     case QMV_Q5_K: e = qmv::gemv_q5_k(calls, n, x_dtype, batch, s); break;
     case QMV_Q6_K: e = qmv::gemv_q6_k(calls, n, x_dtype, batch, s); break;
     default: e = qmv::gemv_int4_g128(calls, n, x_dtype, batch, s); break;

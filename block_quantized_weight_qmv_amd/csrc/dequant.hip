@@ -14,6 +14,7 @@
 // which round once at the subtraction.  fp16 / bf16 outputs are that fp32 value rounded to nearest even.
 #include "device_util.h"
 #include "launch.h"
+#include "planes.h"
 
 namespace qmv {
 
@@ -57,6 +58,28 @@ __device__ __forceinline__ void dq_q4_k(const uint8_t* row, int k, float* w) {
     k_scale_min(b + 4, s, scale, mn);
     const uint32_t u = (ld_u8(b + 16 + 32 * c + l) >> (4 * h)) & 15;
     w[e] = (d * static_cast<float>(scale)) * static_cast<float>(u) - dmin * static_cast<float>(mn);
+  }
+}
+
+// Q4_K in the plane layout (planes.h): the header of block b at 16 b,
+// qs[32c + l] at a + 64 b + 16 c + l (l < 16) or 5 a + 64 b + 16 c + l - 16.
+// Same decode as dq_q4_k, byte addresses aside.
+constexpr int kQ4KPlanes = 0x102;  // kernel template tag, not a public format
+
+__device__ __forceinline__ void dq_q4_k_planes(const uint8_t* w, uint64_t a, int64_t b, int k,
+                                               float* out) {
+  const uint8_t* h = w + 16 * b;
+  const float d = f16_to_f32(ld_le16(h));
+  const float dmin = f16_to_f32(ld_le16(h + 2));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = (k + e) % 256;
+    const int c = t >> 6, hh = (t >> 5) & 1, l = t & 31, s = t >> 5;
+    uint32_t scale, mn;
+    k_scale_min(h + 4, s, scale, mn);
+    const uint8_t* q = l < 16 ? w + a + 64 * b + 16 * c + l : w + 5 * a + 64 * b + 16 * c + (l - 16);
+    const uint32_t u = (ld_u8(q) >> (4 * hh)) & 15;
+    out[e] = (d * static_cast<float>(scale)) * static_cast<float>(u) - dmin * static_cast<float>(mn);
   }
 }
 
@@ -131,6 +154,8 @@ dequant_kernel(const uint8_t* __restrict__ w, uint64_t scales_offset, int rows, 
       dq_q8_0(w + static_cast<size_t>(r) * (cols / 32) * 34, k, v);
     } else if (FMT == QMV_Q4_K) {
       dq_q4_k(w + static_cast<size_t>(r) * (cols / 256) * 144, k, v);
+    } else if (FMT == kQ4KPlanes) {
+      dq_q4_k_planes(w, scales_offset, static_cast<int64_t>(r) * (cols / 256) + k / 256, k, v);
     } else if (FMT == QMV_Q5_K) {
       dq_q5_k(w + static_cast<size_t>(r) * (cols / 256) * 176, k, v);
     } else if (FMT == QMV_Q6_K) {
@@ -179,6 +204,8 @@ static hipError_t dequant_fmt(const qmv_weights& W, void* out, int out_dtype, hi
 }
 
 hipError_t dequant(const qmv_weights& W, void* out, int out_dtype, hipStream_t s) {
+  if (W.layout == QMV_LAYOUT_PLANES)
+    return W.fmt == QMV_Q4_K ? dequant_fmt<kQ4KPlanes>(W, out, out_dtype, s) : hipErrorInvalidValue;
   switch (W.fmt) {
     case QMV_Q8_0: return dequant_fmt<QMV_Q8_0>(W, out, out_dtype, s);
     case QMV_Q4_K: return dequant_fmt<QMV_Q4_K>(W, out, out_dtype, s);

@@ -117,8 +117,45 @@ struct Q4KPolicy {
   }
 };
 
+// The same GEMV over the plane layout of planes.h: the lane mapping, the
+// arithmetic and its order are Q4KPolicy's, only the addresses differ.  Lane
+// (j, c) reads block j's header from the header plane (16 headers = 256
+// consecutive bytes per instruction; the four lanes of a block share one
+// address) and its two code quarters from planes A and B, where one
+// instruction of the wave reads 16 blocks x 64 bytes = 1 KB of consecutive
+// bytes that no other instruction reads.  Those code loads carry the
+// nontemporal hint; the header loads, whose lines are shared with the next
+// row's headers, do not.
+struct Q4KPlanesPolicy : Q4KPolicy {
+  const uint8_t* hdr;
+  const uint8_t* qa;
+  const uint8_t* qb;
+  uint32_t nb;
+
+  __device__ Q4KPlanesPolicy(const uint8_t* w, uint64_t a, int cols, int kslot, int lane)
+      : Q4KPolicy(w, 0, cols, kslot, lane) {
+    nb = static_cast<uint32_t>(cols / 256);
+    const int jc = col0 / 256;  // this lane's block in the row (clamped as in Q4KPolicy)
+    hdr = w + static_cast<size_t>(jc) * 16;
+    qa = w + a + static_cast<size_t>(jc) * 64 + 16 * c;
+    qb = w + 5 * a + static_cast<size_t>(jc) * 64 + 16 * c;
+  }
+
+  __device__ void load(int row, Frag& f) const {
+    const size_t b = static_cast<size_t>(row) * nb;
+    f.hd = ld16(hdr + 16 * b);
+    f.qa = ld16_stream(qa + 64 * b);
+    f.qb = ld16_stream(qb + 64 * b);
+  }
+};
+
 hipError_t gemv_q4_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
   return launch_gemv<Q4KPolicy>(calls, n, x_dtype, batch, s);
+}
+
+hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
+                            hipStream_t s) {
+  return launch_gemv<Q4KPlanesPolicy>(calls, n, x_dtype, batch, s);
 }
 
 }  // namespace qmv

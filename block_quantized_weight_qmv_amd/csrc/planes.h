@@ -1,0 +1,38 @@
+// Plane layout of Q4_K weights ("decode-repacked" layout, after hipEngine
+// 0.3.0, "GGUF Support": GGUF blocks are repacked into decode layouts on load
+// and the repacked copy replaces the source).
+//
+// The canonical layout keeps each 144-byte block whole, so the GEMV's three
+// load instructions per lane (block header, code quarter A, code quarter B)
+// all touch the same 128-byte lines.  The plane layout moves the same bytes
+// into three planes, so that each code load instruction of a wave reads 1 KB
+// of consecutive bytes that no other instruction reads:
+//
+//   N = rows * (cols / 256) blocks, block b = r * (cols / 256) + j,
+//   a = 16 N rounded up to a multiple of 256,
+//   H  plane at 0:     header of block b (its first 16 bytes: d, dmin,
+//                      scales[12]) at 16 b;
+//   QA plane at a:     qs[32c .. 32c+16) of block b at a + 64 b + 16 c;
+//   QB plane at 5 a:   qs[32c+16 .. 32c+32) of block b at 5 a + 64 b + 16 c;
+//   total 5 a + 64 N bytes (the 144 N bytes of the blocks plus under
+//   1280 bytes of padding between the planes).
+//
+// a is recorded in the descriptor's scales_offset field.
+#pragma once
+
+#include <stdint.h>
+
+namespace qmv {
+
+struct Q4KPlanes {
+  uint64_t a;      // byte offset of the QA plane; the QB plane is at 5 a
+  uint64_t total;  // bytes of the whole layout
+};
+
+__host__ __device__ inline Q4KPlanes q4k_planes(int64_t rows, int64_t cols) {
+  const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 256);
+  const uint64_t a = (16 * n + 255) / 256 * 256;
+  return Q4KPlanes{a, 5 * a + 64 * n};
+}
+
+}  // namespace qmv

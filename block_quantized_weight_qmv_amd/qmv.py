@@ -20,6 +20,7 @@ LIB_PATH = os.path.join(PKG_DIR, "libqmv.so")
 
 FMT = {"q8_0": 1, "q4_k": 2, "q6_k": 3, "int4_g128": 4, "q5_k": 5}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
+LAYOUT = {"blocks": 0, "planes": 1}
 
 QMV_OK = 0
 STATUS = {0: "QMV_OK", -1: "QMV_ERR_NULL", -2: "QMV_ERR_FORMAT", -3: "QMV_ERR_SHAPE",
@@ -35,7 +36,7 @@ class QmvError(RuntimeError):
 
 class QmvWeights(ctypes.Structure):
     """Mirror of struct qmv_weights."""
-    _fields_ = [("fmt", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    _fields_ = [("fmt", ctypes.c_int32), ("layout", ctypes.c_int32),
                 ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
                 ("data", ctypes.c_void_p), ("nbytes", ctypes.c_uint64),
                 ("scales_offset", ctypes.c_uint64)]
@@ -58,6 +59,8 @@ _SIGS = {
     "qmv_pack_q6_k": (_i32, [_p, _p, _p, _i64, _i64, _p, _u64]),
     "qmv_pack_int4_g128": (_i32, [_p, _p, _i64, _i64, _p, _u64]),
     "qmv_create_weights": (_i32, [_i32, _i64, _i64, _p, _u64, ctypes.POINTER(QmvWeights)]),
+    "qmv_planes_size": (_u64, [_i32, _i64, _i64]),
+    "qmv_repack_planes": (_i32, [ctypes.POINTER(QmvWeights), _p, _u64, ctypes.POINTER(QmvWeights), _p]),
     "qmv_gemv": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
     "qmv_gemv_multi": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32, _p]),
     "qmv_dequant": (_i32, [ctypes.POINTER(QmvWeights), _p, _i32, _p]),
@@ -213,6 +216,22 @@ def qmv_create_weights(fmt, rows: int, cols: int, dev_packed, nbytes: int | None
     # caching allocator may hand its memory back to the driver (empty_cache(),
     # which graph capture calls) while launches still read it.
     w.owner = None if isinstance(dev_packed, int) else dev_packed
+    return w
+
+
+def qmv_planes_size(fmt, rows: int, cols: int) -> int:
+    return lib().qmv_planes_size(_fmt(fmt), rows, cols)
+
+
+def qmv_repack_planes(src: QmvWeights, dst, dst_bytes: int | None = None, stream=None) -> QmvWeights:
+    """Enqueue the repack of canonical Q4_K blocks into the plane layout at dst
+    (a uint8 device tensor or a pointer); returns the planes descriptor."""
+    if dst_bytes is None:
+        dst_bytes = dst.numel() * dst.element_size()
+    w = QmvWeights()
+    _check(lib().qmv_repack_planes(ctypes.byref(src), _ptr(dst), dst_bytes, ctypes.byref(w),
+                                   _stream(stream, dst)))
+    w.owner = None if isinstance(dst, int) else dst
     return w
 
 

@@ -71,6 +71,24 @@ enum {
 
 enum { QMV_F32 = 0, QMV_F16 = 1, QMV_BF16 = 2 };
 
+/* Byte layouts of a weight tensor in device memory.
+ *   QMV_LAYOUT_BLOCKS: the canonical blocks above, row-major.
+ *   QMV_LAYOUT_PLANES (Q4_K only): the same bytes rearranged for streaming,
+ *     a decode-repacked layout in the sense of hipEngine 0.3.0, "GGUF
+ *     Support" (GGUF blocks repacked at load time into decode layouts that
+ *     replace the source).  With N = rows*(cols/256) blocks, block
+ *     b = r*(cols/256) + j, and a = 16*N rounded up to a multiple of 256:
+ *       header plane at 0:   bytes 0..15 of block b (d, dmin, scales) at 16*b;
+ *       code plane A at a:   qs[32c .. 32c+16) of block b at a + 64*b + 16*c;
+ *       code plane B at 5*a: qs[32c+16 .. 32c+32) of block b at
+ *                            5*a + 64*b + 16*c   (c = 0..3);
+ *     qmv_planes_size bytes in all; the descriptor's scales_offset holds a.
+ *     Made on the device by qmv_repack_planes.  The GEMV streams each code
+ *     plane with load instructions that read whole 128-byte lines no other
+ *     instruction reads (which lets it use nontemporal loads), so the plane
+ *     base should be 256-byte aligned for full speed (16 is required). */
+enum { QMV_LAYOUT_BLOCKS = 0, QMV_LAYOUT_PLANES = 1 };
+
 enum {
   QMV_OK = 0,
   QMV_ERR_NULL = -1,        /* a required pointer is NULL                    */
@@ -90,12 +108,14 @@ enum {
  * (and unmodified) until every enqueued call that reads them has finished. */
 typedef struct qmv_weights {
   int32_t fmt;            /* QMV_Q8_0 .. QMV_Q5_K                            */
-  int32_t reserved;       /* 0                                               */
+  int32_t layout;         /* QMV_LAYOUT_BLOCKS (0) or QMV_LAYOUT_PLANES      */
   int64_t rows, cols;     /* logical shape of W                              */
   const void* data;       /* device pointer to the packed bytes (16 B aligned)*/
-  uint64_t nbytes;        /* == qmv_packed_size(fmt, rows, cols)             */
-  uint64_t scales_offset; /* INT4_G128: byte offset of the scales plane; 0   */
-                          /* for the block formats                           */
+  uint64_t nbytes;        /* == qmv_packed_size(fmt, rows, cols), or         */
+                          /* qmv_planes_size for QMV_LAYOUT_PLANES           */
+  uint64_t scales_offset; /* INT4_G128: byte offset of the scales plane;     */
+                          /* QMV_LAYOUT_PLANES: offset a of code plane A;    */
+                          /* 0 for the block formats                         */
 } qmv_weights;
 
 /* Codes per block: 32, 256, 256, 128, 256 (Q8_0, Q4_K, Q6_K, INT4_G128,
@@ -141,6 +161,24 @@ int32_t qmv_pack_int4_g128(const uint16_t* s_bits, const int8_t* q,
                            int64_t rows, int64_t cols, uint8_t* out,
                            uint64_t out_bytes);
 
+/* Bytes of the QMV_LAYOUT_PLANES layout of a rows x cols tensor; 0 if the
+ * format has no plane layout (every format but Q4_K) or the shape is
+ * invalid. */
+uint64_t qmv_planes_size(int32_t fmt, int64_t rows, int64_t cols);
+
+/* Enqueue the repack of canonical Q4_K blocks (src, QMV_LAYOUT_BLOCKS) into
+ * the plane layout at dst (device memory of dst_bytes >= qmv_planes_size
+ * bytes, 16-byte aligned, 256 recommended, not overlapping src) and fill
+ * *out with a QMV_LAYOUT_PLANES descriptor of dst.  Bytes are moved, not
+ * changed: qmv_dequant of the result equals qmv_dequant of src bit for bit.
+ * src must stay alive until the repack has run (stream order); after that
+ * the caller may free it.  Errors: QMV_ERR_NULL, QMV_ERR_UNSUPPORTED (a
+ * format other than Q4_K, or src already in planes), QMV_ERR_SIZE
+ * (dst_bytes too small), QMV_ERR_ALIGN, QMV_ERR_SHAPE (dst overlaps src),
+ * or any error of the src descriptor's validation. */
+int32_t qmv_repack_planes(const qmv_weights* src, void* dst,
+                          uint64_t dst_bytes, qmv_weights* out, void* stream);
+
 /* Validate shape and size and fill *out.  No HIP call, no allocation.
  * dev_packed must be 16-byte aligned (QMV_ERR_ALIGN) and nbytes must equal
  * qmv_packed_size (QMV_ERR_SIZE). */
@@ -156,7 +194,11 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * activations and batch >= 2 the call runs the matrix-core path (weights read
  * once for up to 16 activation rows, once per tile of 32, 64 or 128 rows
  * above; exact products, fp32 sums, results independent of timing);
- * otherwise each activation row is a GEMV over the packed weights. */
+ * otherwise each activation row is a GEMV over the packed weights.
+ * Q4_K weights in QMV_LAYOUT_PLANES run the same GEMV arithmetic, in the same
+ * order, as the canonical layout (results equal bit for bit); the
+ * matrix-core path takes the canonical layout only (QMV_ERR_UNSUPPORTED for
+ * planes there). */
 int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,
                  int32_t x_dtype, float* y, int64_t rows, int64_t cols,
                  int64_t batch, void* stream);
@@ -177,7 +219,8 @@ typedef struct qmv_gemv_item {
  * one dtype for every weight of a dispatch, K a whole number of blocks, and
  * output tiles that never overlap).  Each item is validated as in qmv_gemv;
  * the y ranges must be disjoint (QMV_ERR_SHAPE otherwise); every x and y is a
- * 16-byte aligned device pointer.  Results equal n separate qmv_gemv calls
+ * 16-byte aligned device pointer; all items share one layout
+ * (QMV_ERR_UNSUPPORTED otherwise).  Results equal n separate qmv_gemv calls
  * up to float32 summation order. */
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch,
                        const qmv_gemv_item* items, int32_t n, void* stream);

@@ -141,3 +141,46 @@ def test_single_hip_runtime_mapped():
     qmv.lib()
     maps = {line.split()[-1] for line in open("/proc/self/maps") if "libamdhip64" in line}
     assert len(maps) == 1, maps
+
+
+def test_planes_sizes_and_repack_validation_errors():
+    """Plane layout: sizes, and every refusal of qmv_repack_planes, of a plane
+    descriptor that does not match its shape, and of mixed or matrix-core
+    launches -- all before any HIP call."""
+    n_blocks = 8 * 2
+    a = (16 * n_blocks + 255) // 256 * 256
+    assert qmv.qmv_planes_size("q4_k", 8, 512) == 5 * a + 64 * n_blocks
+    assert qmv.qmv_planes_size("q4_k", 18944, 3584) == 38_191_104  # 16 N is a multiple of 256 there
+    for f in ("q8_0", "q6_k", "int4_g128", "q5_k"):
+        assert qmv.qmv_planes_size(f, 8, 512) == 0
+    assert qmv.qmv_planes_size("q4_k", 8, 500) == 0
+    src = _desc()
+    need = qmv.qmv_planes_size("q4_k", 8, 512)
+    dst = FAKE + (1 << 20)
+    r = qmv.qmv_repack_planes
+    _expect(-1, r, src, None, need)
+    _expect(-5, r, src, dst, need - 1)
+    _expect(-4, r, src, dst + 8, need)
+    _expect(-3, r, src, FAKE + 64, need)                    # overlaps the source
+    _expect(-6, r, _desc("q6_k", 8, 512), dst, need)        # no plane layout for Q6_K
+    bad = _desc()
+    bad.nbytes += 1
+    _expect(-5, r, bad, dst, need)
+    # a plane descriptor, filled by hand as a caller restoring saved planes would
+    p = _desc()
+    p.layout, p.nbytes, p.scales_offset = 1, need, a
+    _expect(-6, r, p, dst, need)                            # already planes
+    g = qmv.qmv_gemv
+    tampered = _desc()
+    tampered.layout, tampered.nbytes, tampered.scales_offset = 1, need, 0
+    _expect(-2, g, "q4_k", tampered, FAKE, "f32", FAKE, 8, 512, 1)  # wrong plane offset
+    tampered.scales_offset, tampered.nbytes = a, need + 16
+    _expect(-5, g, "q4_k", tampered, FAKE, "f32", FAKE, 8, 512, 1)
+    tampered.nbytes, tampered.layout = need, 7
+    _expect(-2, g, "q4_k", tampered, FAKE, "f32", FAKE, 8, 512, 1)  # unknown layout
+    q6 = _desc("q6_k", 8, 512)
+    q6.layout = 1
+    _expect(-6, g, "q6_k", q6, FAKE, "f32", FAKE, 8, 512, 1)
+    _expect(-6, qmv.qmv_gemv_multi, "q4_k", "f32", 1, [(src, FAKE, FAKE), (p, FAKE, FAKE + 4096)])
+    _expect(-6, g, "q4_k", p, FAKE, "bf16", FAKE, 8, 512, 4)  # matrix-core path: blocks only
+    assert _desc().layout == 0

@@ -45,21 +45,41 @@ def _library_kernels():
     return names
 
 
+def _layouts(config, batch):
+    """The layout bench.py uses by default, and the canonical blocks."""
+    return sorted({bench.default_layout(config, batch), "blocks"})
+
+
 @pytest.mark.parametrize("config,batch", CASES)
 def test_named_kernel_exists_in_library(config, batch):
     names = _library_kernels()
-    plan = bench.workload_plan(config, batch, separate=False)
-    for k in plan["kname"]:
-        assert k in names, (k, sorted(n for n in names if k.split("<")[0] in n))
+    for layout in _layouts(config, batch):
+        plan = bench.workload_plan(config, batch, separate=False, layout=layout)
+        for k in plan["kname"]:
+            assert k in names, (k, sorted(n for n in names if k.split("<")[0] in n))
+
+
+def test_default_layout():
+    assert bench.default_layout(3, None) == "planes"
+    assert bench.default_layout(5, 1) == "planes"
+    assert bench.default_layout(5, 4) == "blocks"       # matrix-core path
+    for c in (1, 2, 4, 6):
+        assert bench.default_layout(c, None) == "blocks"
 
 
 @pytest.mark.parametrize("config,batch", CASES)
 def test_algorithmic_bytes_and_flops(config, batch):
-    plan = bench.workload_plan(config, batch, separate=False)
+    for layout in _layouts(config, batch):
+        _check_bytes_and_flops(config, batch, layout)
+
+
+def _check_bytes_and_flops(config, batch, layout):
+    plan = bench.workload_plan(config, batch, separate=False, layout=layout)
+    size = qmv.qmv_planes_size if layout == "planes" else qmv.qmv_packed_size
     xb = {"f32": 4, "f16": 2, "bf16": 2}[plan["x_dtype"]]
     mats = plan["mats"]
     for gi, g in enumerate(plan["groups"]):
-        w = sum(qmv.qmv_packed_size(plan["fmt"], mats[m][1], mats[m][2]) for m in g)
+        w = sum(size(plan["fmt"], mats[m][1], mats[m][2]) for m in g)
         y = sum(batch * mats[m][1] * 4 for m in g)
         x = batch * mats[g[0]][2] * xb           # one activation per launch
         assert all(mats[m][2] == mats[g[0]][2] for m in g)
