@@ -7,8 +7,11 @@
 //    [k*P::kColsPerWave, ...) and keeps that slice of x_i in VGPRs (fp32) for
 //    its whole life, so activations are read once per wave, not once per row.
 //  * The rows of matrix i are cut into nsets_i contiguous row sets of q_i or
-//    q_i+1 rows; a set is processed by kw_i waves of one workgroup, R rows per
-//    tile.  All workgroups have the same size (the largest kw among the
+//    q_i+R rows (q_i a multiple of R; only the matrix's last set can end in
+//    a partial tile); a set is processed by kw_i waves of one workgroup, R
+//    rows per tile.  Whole tiles matter for streams read with the
+//    nontemporal hint: a partial tile re-reads its last row, and such a line
+//    is no longer in L2.  All workgroups have the same size (the largest kw among the
 //    matrices, at least 4 waves); with kw_i == 1 a workgroup serves one set
 //    per wave, with kw_i > 1 one set (spare waves leave at once).  Set sizes
 //    are chosen so that every wave streams about the same number of bytes and
@@ -122,7 +125,7 @@ struct GemvItem {
   int rows, cols;
   int kw;             // waves along K
   int sets_per_wg;    // row sets per workgroup (kw waves each)
-  int nsets, q, rem;  // rows = q * nsets + rem; set s has q + (s < rem) rows
+  int nsets, q, rem;  // set s has q + R (s < rem) or q rows, the last one clamped to rows
   int wg_begin;       // first workgroup of this matrix
 };
 
@@ -153,8 +156,8 @@ gemv_kernel(const GemvLaunch args) {
   if (!SX && set >= m.nsets) return;
   const XT* x = static_cast<const XT*>(m.x) + static_cast<size_t>(blockIdx.y) * m.cols;
   float* y = m.y + static_cast<size_t>(blockIdx.y) * m.rows;
-  int r_begin = set * m.q + min(set, m.rem);
-  int r_end = r_begin + m.q + (set < m.rem ? 1 : 0);
+  int r_begin = set * m.q + R * min(set, m.rem);
+  int r_end = min(r_begin + m.q + (set < m.rem ? R : 0), m.rows);
   if (SX && set >= m.nsets) r_begin = r_end = m.rows;  // tile loads clamp to the last row
   const int r_last = r_end - 1;
 
@@ -272,8 +275,9 @@ inline int max_kw(const GemvCall* calls, int n) {
 
 // Lay out a launch over `n` matrices with `waves` waves per workgroup: K split
 // and row sets per matrix, workgroup ranges.  Rows per set are the same for
-// every matrix, chosen so that the launch holds about `target_waves` waves.
-template <class P>
+// every matrix, a whole number of R-row tiles, chosen so that the launch
+// holds about `target_waves` waves.
+template <class P, int R>
 inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_waves,
                      GemvLaunch* L) {
   int64_t wave_rows = 0;  // sum over matrices of rows * kw
@@ -281,7 +285,8 @@ inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_wav
     wave_rows += calls[i].W->rows *
                  ((calls[i].W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
   int64_t rps = (wave_rows + target_waves - 1) / target_waves;
-  if (rps < 1) rps = 1;
+  rps = (rps + R - 1) / R * R;  // a wave's tile count is ceil(rows / R) either way
+  if (rps < R) rps = R;
   int wg = 0;
   L->n = n;
   L->part_stride = 0;
@@ -298,11 +303,12 @@ inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_wav
     m.sets_per_wg = waves / m.kw;
     int64_t set_rows = rps;
     if (m.kw > 1 && set_rows > kMaxPartStride) set_rows = kMaxPartStride;  // LDS of the partials
-    m.nsets = static_cast<int>((m.rows + set_rows - 1) / set_rows);
-    m.q = m.rows / m.nsets;
-    m.rem = m.rows % m.nsets;
+    const int units = (m.rows + R - 1) / R;  // tiles of R rows
+    m.nsets = static_cast<int>((units + set_rows / R - 1) / (set_rows / R));
+    m.q = (units / m.nsets) * R;
+    m.rem = units % m.nsets;
     if (m.kw > 1) {
-      const int need = m.q + (m.rem ? 1 : 0);
+      const int need = m.q + (m.rem ? R : 0);
       L->part_stride = need > L->part_stride ? need : L->part_stride;
     }
     m.wg_begin = wg;
@@ -369,7 +375,7 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   target = per_cu * cus * waves;
   if (target > resident) target = resident;
   GemvLaunch L;
-  const int grid = plan_gemv<P>(calls, n, waves, target, &L);
+  const int grid = plan_gemv<P, R>(calls, n, waves, target, &L);
   size_t lds = static_cast<size_t>(waves) * L.part_stride * sizeof(float);
   if (SX) {  // the x copy: the longest row's chunks, rounded up to 16 (xshared_slot)
     int64_t cols = 0;
