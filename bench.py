@@ -265,7 +265,9 @@ def summarize_counters(args) -> int:
         seq += [gi] * (len(g) if kname[gi].startswith("qmv::gemm") else 1)
     per_launch = []
     for counter, d in (("FETCH_SIZE", fetch_d), ("WRITE_SIZE", write_d)):
-        ds = [x for x in _per_dispatch(d, counter) if x[0].startswith("qmv::")]
+        # GEMV / matrix-core dispatches only (the plane repack runs at load)
+        ds = [x for x in _per_dispatch(d, counter)
+              if x[0].startswith("qmv::") and "repack" not in x[0]]
         n_steps = len(ds) // len(seq)
         if n_steps * len(seq) != len(ds) or n_steps <= args.warmup:
             raise SystemExit(f"{counter}: {len(ds)} qmv dispatches, not a whole number of "
