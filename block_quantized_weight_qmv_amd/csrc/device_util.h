@@ -77,6 +77,13 @@ __device__ __forceinline__ float fma_hi(uint32_t bits, float x, float acc) {
   return fmaf(static_cast<float>(__builtin_bit_cast(h2_t, bits).y), x, acc);
 }
 
+// Two codes held as fp16 subnormals in the halves of `bits`, times two fp16
+// activations, both products added to acc in fp32 (v_dot2_f32_f16).  The
+// products are exact (4 + 11 significant bits).
+__device__ __forceinline__ float dot2_lo_hi(uint32_t bits, h2_t x, float acc) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, bits), x, acc, false);
+}
+
 // Byte B of v as fp32 via v_cvt_f32_ubyte{B}.  The empty asm hides how v was
 // computed, which keeps the compiler from rewriting mask-then-convert into a
 // bitfield extract per byte.
