@@ -179,6 +179,53 @@ __device__ __forceinline__ void x_to_f32(const uint4* raw, float* out, const bf1
   }
 }
 
+// A lane's 64 activations as the Q4_K and Q5_K GEMVs multiply them: scaled by
+// 2^-e, a power of two chosen per lane so that the largest |x| lands in
+// [2^14, 2^15) (exact), and rounded once to fp16 (relative error <= 2^-11),
+// paired in the order the code halves come (dword i of the lane's codes:
+// (byte 0, byte 2) and (byte 1, byte 3), low nibbles against activations
+// 4i.., high nibbles against 32 + 4i..).  xs = 2^(24+e) undoes both the
+// scaling and the 2^-24 of the subnormal codes; s0 and s1 are fp32 sums of
+// the unrounded activations of the two sub-blocks, which the min terms take.
+// e is kept where 2^(24+e) is a normal float (|x| below 2^117).
+struct HalfXSlice {
+  h2_t h[32];
+  float s0, s1;
+  float xs;
+};
+
+__device__ __forceinline__ _Float16 scaled_f16(float v, int e) {
+  return static_cast<_Float16>(__builtin_amdgcn_ldexpf(v, -e));
+}
+
+template <typename XT>
+__device__ __forceinline__ void finish_half_xslice(const uint4* raw, bool ok, HalfXSlice& s) {
+  float v[64];
+  x_to_f32<64>(raw, v, static_cast<const XT*>(nullptr));
+#pragma unroll
+  for (int i = 0; i < 64; ++i) v[i] = ok ? v[i] : 0.f;
+  s.s0 = 0.f;
+  s.s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) s.s0 += v[i];
+#pragma unroll
+  for (int i = 32; i < 64; ++i) s.s1 += v[i];
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < 64; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  // mx = m 2^E with m in [0.5, 1): scaled by 2^-(E-15) it lies in [2^14, 2^15)
+  int e = __builtin_amdgcn_frexp_expf(mx) - 15;
+  e = e < -150 ? -150 : (e > 103 ? 103 : e);
+  s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    s.h[4 * i + 0] = h2_t{scaled_f16(v[4 * i], e), scaled_f16(v[4 * i + 2], e)};
+    s.h[4 * i + 1] = h2_t{scaled_f16(v[4 * i + 1], e), scaled_f16(v[4 * i + 3], e)};
+    s.h[4 * i + 2] = h2_t{scaled_f16(v[32 + 4 * i], e), scaled_f16(v[32 + 4 * i + 2], e)};
+    s.h[4 * i + 3] = h2_t{scaled_f16(v[32 + 4 * i + 1], e), scaled_f16(v[32 + 4 * i + 3], e)};
+  }
+}
+
 // Host side: compute units and LDS bytes per workgroup of the current device,
 // queried once per device (gfx950: 256 CUs, 160 KB).
 inline int device_attr_cached(hipDeviceAttribute_t attr, int (&cache)[64], int fallback) {

@@ -35,11 +35,7 @@ namespace qmv {
 struct Q4KPolicy {
   static constexpr int kColsPerWave = 16 * 256;
   static constexpr int kXElems = 64;
-  struct XSlice {
-    h2_t h[32];    // scaled fp16 activations, paired in the order the code halves come
-    float s0, s1;  // sums of the unrounded activations of sub-blocks 2c and 2c+1
-    float xs;      // 2^(24 + e)
-  };
+  typedef HalfXSlice XSlice;
   struct Frag {
     uint4 hd, qa, qb;
   };
@@ -81,37 +77,7 @@ struct Q4KPolicy {
 
   template <typename XT>
   __device__ void finish_x(const uint4* raw, XSlice& s) const {
-    float v[64];
-    x_to_f32<64>(raw, v, static_cast<const XT*>(nullptr));
-#pragma unroll
-    for (int i = 0; i < 64; ++i) v[i] = ok ? v[i] : 0.f;
-    s.s0 = 0.f;
-    s.s1 = 0.f;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) s.s0 += v[i];
-#pragma unroll
-    for (int i = 32; i < 64; ++i) s.s1 += v[i];
-    float mx = 0.f;
-#pragma unroll
-    for (int i = 0; i < 64; ++i) mx = fmaxf(mx, fabsf(v[i]));
-    // mx = m 2^E with m in [0.5, 1): scaled by 2^-(E-15) it lies in [2^14, 2^15).
-    // e is kept where 2^(24+e) is a normal float (|x| below 2^117).
-    int e = __builtin_amdgcn_frexp_expf(mx) - 15;
-    e = e < -150 ? -150 : (e > 103 ? 103 : e);
-    s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
-    // Code pairs of dword i: (byte 0, byte 2) and (byte 1, byte 3), low nibbles
-    // for sub-block 2c (activations v[4i + ...]), high for 2c+1 (v[32 + 4i + ...]).
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      s.h[4 * i + 0] = h2_t{to_f16(v[4 * i], e), to_f16(v[4 * i + 2], e)};
-      s.h[4 * i + 1] = h2_t{to_f16(v[4 * i + 1], e), to_f16(v[4 * i + 3], e)};
-      s.h[4 * i + 2] = h2_t{to_f16(v[32 + 4 * i], e), to_f16(v[32 + 4 * i + 2], e)};
-      s.h[4 * i + 3] = h2_t{to_f16(v[32 + 4 * i + 1], e), to_f16(v[32 + 4 * i + 3], e)};
-    }
-  }
-
-  static __device__ _Float16 to_f16(float v, int e) {
-    return static_cast<_Float16>(__builtin_amdgcn_ldexpf(v, -e));
+    finish_half_xslice<XT>(raw, ok, s);
   }
 
   __device__ void load(int row, Frag& f) const {

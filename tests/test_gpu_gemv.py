@@ -162,14 +162,14 @@ def test_full_size_configs_sampled_rows(config):
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("layout", ["blocks", "planes"])
+@pytest.mark.parametrize("fmt,layout", [("q4_k", "blocks"), ("q4_k", "planes"), ("q5_k", "blocks")])
 @pytest.mark.parametrize("spread", ["wide", "large", "tiny"])
-def test_q4_k_activation_range(layout, spread):
-    """Q4_K rounds each lane's activations to fp16 after scaling them by a
-    power of two of their own: magnitudes far outside fp16's range (and a
+def test_half_activation_range(fmt, layout, spread):
+    """Q4_K and Q5_K round each lane's activations to fp16 after scaling them
+    by a power of two of their own: magnitudes far outside fp16's range (and a
     spread of twelve decades within one row) must still meet the gate."""
     rows, cols = 96, 17 * 256
-    w = Weights("q4_k", rows, cols, seed=808)
+    w = Weights(fmt, rows, cols, seed=808)
     g = np.random.Generator(np.random.PCG64({"wide": 1, "large": 2, "tiny": 3}[spread]))
     x = g.standard_normal((2, cols))
     if spread == "wide":
@@ -183,9 +183,9 @@ def test_q4_k_activation_range(layout, spread):
     if layout == "planes":
         dst = torch.empty(qmv.qmv_planes_size("q4_k", rows, cols), dtype=torch.uint8, device=DEV)
         desc = qmv.qmv_repack_planes(w.desc, dst)
-    say(f"q4_k activation range {spread} ({layout})")
+    say(f"{fmt} activation range {spread} ({layout})")
     y = torch.empty(2, rows, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv("q4_k", desc, to_dev_x(x, "f32"), "f32", y, rows, cols, 2)
+    qmv.qmv_gemv(fmt, desc, to_dev_x(x, "f32"), "f32", y, rows, cols, 2)
     got = y.cpu().numpy()
     assert np.all(np.isfinite(got))
     err = _err(got, oracle_y(w, x, "f32"))
