@@ -118,6 +118,28 @@ __device__ __forceinline__ void dq_q6_k(const uint8_t* row, int k, float* w) {
   }
 }
 
+// Q6_K in the plane layout (planes.h): ql[64h + 32m + 16i + t] of block b at
+// 4 m a + 64 b + 16 (2h + i) + t, qh[32h + 16i + t] at 8 a + 64 b +
+// 16 (2h + i) + t, sc[k] at 12 a + 16 b + k, d at 13 a + 2 b.  Same decode as
+// dq_q6_k, byte addresses aside.
+constexpr int kQ6KPlanes = 0x103;  // kernel template tag, not a public format
+
+__device__ __forceinline__ void dq_q6_k_planes(const uint8_t* w, uint64_t a, int64_t b, int k,
+                                               float* out) {
+  const float d = f16_to_f32(ld_le16(w + 13 * a + 2 * b));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = (k + e) % 256;
+    const int h = t >> 7, g = (t >> 5) & 3, l = t & 31;
+    const int m = g & 1, i = l >> 4, tt = l & 15, p = 2 * h + i;
+    const uint32_t lo = (ld_u8(w + 4 * m * a + 64 * b + 16 * p + tt) >> (4 * (g >> 1))) & 15;
+    const uint32_t hi = (ld_u8(w + 8 * a + 64 * b + 16 * p + tt) >> (2 * g)) & 3;
+    const int q6 = static_cast<int>(lo | (hi << 4)) - 32;
+    const int sc = static_cast<int8_t>(ld_u8(w + 12 * a + 16 * b + t / 16));
+    out[e] = (d * static_cast<float>(sc)) * static_cast<float>(q6);
+  }
+}
+
 // INT4_G128: codes plane (u_{2j} low nibble, u_{2j+1} high) then fp16 scales.
 __device__ __forceinline__ void dq_int4(const uint8_t* codes_row, const uint8_t* scales_row,
                                         int k, float* w) {
@@ -156,6 +178,8 @@ dequant_kernel(const uint8_t* __restrict__ w, uint64_t scales_offset, int rows, 
       dq_q4_k(w + static_cast<size_t>(r) * (cols / 256) * 144, k, v);
     } else if (FMT == kQ4KPlanes) {
       dq_q4_k_planes(w, scales_offset, static_cast<int64_t>(r) * (cols / 256) + k / 256, k, v);
+    } else if (FMT == kQ6KPlanes) {
+      dq_q6_k_planes(w, scales_offset, static_cast<int64_t>(r) * (cols / 256) + k / 256, k, v);
     } else if (FMT == QMV_Q5_K) {
       dq_q5_k(w + static_cast<size_t>(r) * (cols / 256) * 176, k, v);
     } else if (FMT == QMV_Q6_K) {
@@ -204,8 +228,11 @@ static hipError_t dequant_fmt(const qmv_weights& W, void* out, int out_dtype, hi
 }
 
 hipError_t dequant(const qmv_weights& W, void* out, int out_dtype, hipStream_t s) {
-  if (W.layout == QMV_LAYOUT_PLANES)
-    return W.fmt == QMV_Q4_K ? dequant_fmt<kQ4KPlanes>(W, out, out_dtype, s) : hipErrorInvalidValue;
+  if (W.layout == QMV_LAYOUT_PLANES) {
+    if (W.fmt == QMV_Q4_K) return dequant_fmt<kQ4KPlanes>(W, out, out_dtype, s);
+    if (W.fmt == QMV_Q6_K) return dequant_fmt<kQ6KPlanes>(W, out, out_dtype, s);
+    return hipErrorInvalidValue;
+  }
   switch (W.fmt) {
     case QMV_Q8_0: return dequant_fmt<QMV_Q8_0>(W, out, out_dtype, s);
     case QMV_Q4_K: return dequant_fmt<QMV_Q4_K>(W, out, out_dtype, s);

@@ -113,8 +113,50 @@ struct Q6KPolicy {
   }
 };
 
+// The same GEMV over the Q6_K plane layout of planes.h: lane mapping,
+// arithmetic and its order are Q6KPolicy's.  Lane p = 2h + i of block j reads
+// its two ql chunks and its qh chunk from the L0, L1 and QH planes, where one
+// instruction of the wave reads 16 blocks x 64 bytes = 1 KB of consecutive
+// bytes that no other instruction reads (nontemporal loads), and its eight
+// sub-scales and d from the SC and D planes (plain loads: those lines are
+// shared with the neighbouring rows' instructions).
+struct Q6KPlanesPolicy : Q6KPolicy {
+  const uint8_t* l0;
+  const uint8_t* l1;
+  const uint8_t* qh;
+  const uint8_t* scp;
+  const uint8_t* dp;
+  uint32_t nb;
+
+  __device__ Q6KPlanesPolicy(const uint8_t* w, uint64_t a, int cols, int kslot, int lane)
+      : Q6KPolicy(w, 0, cols, kslot, lane) {
+    nb = static_cast<uint32_t>(cols / 256);
+    const int jc = (col0 - 128 * h - 16 * i) / 256;  // this lane's block (clamped as in Q6KPolicy)
+    const int p = 2 * h + i;
+    l0 = w + static_cast<size_t>(jc) * 64 + 16 * p;
+    l1 = w + 4 * a + static_cast<size_t>(jc) * 64 + 16 * p;
+    qh = w + 8 * a + static_cast<size_t>(jc) * 64 + 16 * p;
+    scp = w + 12 * a + static_cast<size_t>(jc) * 16 + 8 * h;
+    dp = w + 13 * a + static_cast<size_t>(jc) * 2;
+  }
+
+  __device__ void load(int row, Frag& f) const {
+    const size_t b = static_cast<size_t>(row) * nb;
+    f.la = ld16_stream(l0 + 64 * b);
+    f.lb = ld16_stream(l1 + 64 * b);
+    f.qh = ld16_stream(qh + 64 * b);
+    f.sc = ld8_any(scp + 16 * b);
+    f.d = ld_u16(dp + 2 * b);
+  }
+};
+
 hipError_t gemv_q6_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
   return launch_gemv<Q6KPolicy>(calls, n, x_dtype, batch, s);
+}
+
+hipError_t gemv_q6_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
+                            hipStream_t s) {
+  return launch_gemv<Q6KPlanesPolicy>(calls, n, x_dtype, batch, s);
 }
 
 }  // namespace qmv

@@ -1,4 +1,4 @@
-// Plane layout of Q4_K weights ("decode-repacked" layout, after hipEngine
+// Plane layouts of Q4_K and Q6_K weights ("decode-repacked" layouts, after hipEngine
 // 0.3.0, "GGUF Support": GGUF blocks are repacked into decode layouts on load
 // and the repacked copy replaces the source).
 //
@@ -18,6 +18,18 @@
 //   1280 bytes of padding between the planes).
 //
 // a is recorded in the descriptor's scales_offset field.
+//
+// Q6_K (210-byte blocks: ql[128] | qh[64] | sc[16] | d), same N, b and a,
+// with p = 2h + i for the GEMV lane (h, i) of a block (h, i in {0, 1}):
+//   L0 plane at 0:     ql[64h + 16i .. +16)        of block b at 64 b + 16 p;
+//   L1 plane at 4 a:   ql[64h + 32 + 16i .. +16)   of block b at 4 a + 64 b + 16 p;
+//   QH plane at 8 a:   qh[32h + 16i .. +16)        of block b at 8 a + 64 b + 16 p;
+//   SC plane at 12 a:  sc[0 .. 16)                 of block b at 12 a + 16 b;
+//   D  plane at 13 a:  d                           of block b at 13 a + 2 b;
+//   total 13 a + 2 N bytes (210 N plus under 3328 bytes of padding).
+// The three 64-byte planes are read with nontemporal loads, 1 KB of
+// consecutive bytes per wave instruction; the sub-scales and d, whose lines
+// the next row's instructions share, with plain loads.
 #pragma once
 
 #include <stdint.h>
@@ -25,7 +37,7 @@
 namespace qmv {
 
 struct Q4KPlanes {
-  uint64_t a;      // byte offset of the QA plane; the QB plane is at 5 a
+  uint64_t a;      // the plane unit a (16 N rounded up to 256); plane offsets are multiples of it
   uint64_t total;  // bytes of the whole layout
 };
 
@@ -33,6 +45,12 @@ __host__ __device__ inline Q4KPlanes q4k_planes(int64_t rows, int64_t cols) {
   const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 256);
   const uint64_t a = (16 * n + 255) / 256 * 256;
   return Q4KPlanes{a, 5 * a + 64 * n};
+}
+
+__host__ __device__ inline Q4KPlanes q6k_planes(int64_t rows, int64_t cols) {
+  const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 256);
+  const uint64_t a = (16 * n + 255) / 256 * 256;
+  return Q4KPlanes{a, 13 * a + 2 * n};
 }
 
 }  // namespace qmv

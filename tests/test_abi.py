@@ -151,7 +151,9 @@ def test_planes_sizes_and_repack_validation_errors():
     a = (16 * n_blocks + 255) // 256 * 256
     assert qmv.qmv_planes_size("q4_k", 8, 512) == 5 * a + 64 * n_blocks
     assert qmv.qmv_planes_size("q4_k", 18944, 3584) == 38_191_104  # 16 N is a multiple of 256 there
-    for f in ("q8_0", "q6_k", "int4_g128", "q5_k"):
+    assert qmv.qmv_planes_size("q6_k", 8, 512) == 13 * a + 2 * n_blocks
+    assert qmv.qmv_planes_size("q6_k", 152064, 3584) == 447_068_160  # no padding at the lm-head shape
+    for f in ("q8_0", "int4_g128", "q5_k"):
         assert qmv.qmv_planes_size(f, 8, 512) == 0
     assert qmv.qmv_planes_size("q4_k", 8, 500) == 0
     src = _desc()
@@ -162,7 +164,7 @@ def test_planes_sizes_and_repack_validation_errors():
     _expect(-5, r, src, dst, need - 1)
     _expect(-4, r, src, dst + 8, need)
     _expect(-3, r, src, FAKE + 64, need)                    # overlaps the source
-    _expect(-6, r, _desc("q6_k", 8, 512), dst, need)        # no plane layout for Q6_K
+    _expect(-6, r, _desc("q5_k", 8, 512), dst, need)        # no plane layout for Q5_K
     bad = _desc()
     bad.nbytes += 1
     _expect(-5, r, bad, dst, need)
@@ -178,9 +180,9 @@ def test_planes_sizes_and_repack_validation_errors():
     _expect(-5, g, "q4_k", tampered, FAKE, "f32", FAKE, 8, 512, 1)
     tampered.nbytes, tampered.layout = need, 7
     _expect(-2, g, "q4_k", tampered, FAKE, "f32", FAKE, 8, 512, 1)  # unknown layout
-    q6 = _desc("q6_k", 8, 512)
-    q6.layout = 1
-    _expect(-6, g, "q6_k", q6, FAKE, "f32", FAKE, 8, 512, 1)
+    q8 = _desc("q8_0", 8, 512)
+    q8.layout = 1
+    _expect(-6, g, "q8_0", q8, FAKE, "f32", FAKE, 8, 512, 1)
     _expect(-6, qmv.qmv_gemv_multi, "q4_k", "f32", 1, [(src, FAKE, FAKE), (p, FAKE, FAKE + 4096)])
     _expect(-6, g, "q4_k", p, FAKE, "bf16", FAKE, 8, 512, 4)  # matrix-core path: blocks only
     assert _desc().layout == 0

@@ -1,11 +1,12 @@
-"""Q4_K in the plane layout (qmv_repack_planes) on the GPU.
+"""Q4_K and Q6_K in the plane layout (qmv_repack_planes) on the GPU.
 
 The repack only moves bytes, so dequantization from planes must equal the
 canonical layout's bit for bit (and the oracle's).  The plane GEMV runs the
 canonical GEMV's arithmetic in the same order with the same launch shape, so
 its outputs must equal the canonical layout's bitwise, and the oracle's
 within the 2e-3 normwise gate.  The full 7B decoder-layer shapes are checked
-in the launch grouping the benchmark times (q+k+v, o, gate+up, down).
+in the launch grouping the benchmark times (q+k+v, o, gate+up, down), and
+the Q6_K lm-head at full size.
 """
 import numpy as np
 import pytest
@@ -24,8 +25,11 @@ TOL = 2e-3
 SHAPES = [(1, 1), (3, 1), (5, 3), (67, 14), (33, 17), (9, 74), (40, 5)]
 
 
+FMTS = ["q4_k", "q6_k"]
+
+
 def _planes(w: Weights, align_pad=0):
-    n = qmv.qmv_planes_size("q4_k", w.rows, w.cols)
+    n = qmv.qmv_planes_size(w.fmt, w.rows, w.cols)
     buf = torch.full((n + align_pad,), 0xA5, dtype=torch.uint8, device=DEV)
     dst = buf[align_pad:] if align_pad else buf
     desc = qmv.qmv_repack_planes(w.desc, dst)
@@ -33,20 +37,21 @@ def _planes(w: Weights, align_pad=0):
     return desc
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rows,nblk", SHAPES)
-def test_repack_dequant_bit_exact(rows, nblk):
+def test_repack_dequant_bit_exact(fmt, rows, nblk):
     cols = nblk * 256
-    say(f"planes dequant {rows}x{cols}")
-    w = Weights("q4_k", rows, cols, seed=900 + rows + nblk)
+    say(f"planes dequant {fmt} {rows}x{cols}")
+    w = Weights(fmt, rows, cols, seed=900 + rows + nblk)
     p = _planes(w, align_pad=16 if rows == 5 else 0)  # one case off 256-byte alignment
-    assert p.layout == 1 and p.nbytes == qmv.qmv_planes_size("q4_k", rows, cols)
+    assert p.layout == 1 and p.nbytes == qmv.qmv_planes_size(fmt, rows, cols)
     a = torch.empty(rows, cols, dtype=torch.float32, device=DEV)
     b = torch.empty_like(a)
     qmv.qmv_dequant(w.desc, a, "f32")
     qmv.qmv_dequant(p, b, "f32")
     got = b.cpu().numpy()
     assert np.array_equal(got, a.cpu().numpy())
-    assert np.array_equal(got, oracle.dequant32("q4_k", w.oracle_bytes(), rows, cols))
+    assert np.array_equal(got, oracle.dequant32(fmt, w.oracle_bytes(), rows, cols))
     for dt, tdt in (("f16", torch.float16), ("bf16", torch.bfloat16)):
         c = torch.empty(rows, cols, dtype=tdt, device=DEV)
         d = torch.empty_like(c)
@@ -55,19 +60,21 @@ def test_repack_dequant_bit_exact(rows, nblk):
         assert torch.equal(c.view(torch.int16), d.view(torch.int16)), dt
 
 
+@pytest.mark.parametrize("fmt", FMTS)
 @pytest.mark.parametrize("rows,nblk", SHAPES)
 @pytest.mark.parametrize("x_dtype", ["f32", "f16", "bf16"])
-def test_planes_gemv_equals_blocks_and_oracle(rows, nblk, x_dtype):
+def test_planes_gemv_equals_blocks_and_oracle(fmt, rows, nblk, x_dtype):
     cols = nblk * 256
-    batch = 1 if x_dtype == "bf16" else (3 if rows < 40 else 1)  # bf16 batch >= 2 is the MFMA path
-    say(f"planes gemv {rows}x{cols} batch {batch} x {x_dtype}")
-    w = Weights("q4_k", rows, cols, seed=700 + rows + nblk)
+    # Q4_K x bf16 with batch >= 2 is the matrix-core path (canonical blocks only)
+    batch = 1 if (x_dtype == "bf16" and fmt == "q4_k") else (3 if rows < 40 else 1)
+    say(f"planes gemv {fmt} {rows}x{cols} batch {batch} x {x_dtype}")
+    w = Weights(fmt, rows, cols, seed=700 + rows + nblk)
     p = _planes(w)
     x = gen_x(batch, cols, x_dtype, seed=77 + nblk)
     xd = to_dev_x(x, x_dtype)
     y_blocks = w.gemv(xd, x_dtype, batch)
     y_planes = torch.full((batch, rows), 123.0, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv("q4_k", p, xd, x_dtype, y_planes, rows, cols, batch)
+    qmv.qmv_gemv(fmt, p, xd, x_dtype, y_planes, rows, cols, batch)
     got = y_planes.cpu().numpy()
     assert np.array_equal(got, y_blocks.cpu().numpy())
     err = oracle.normwise_rel_err(got, oracle_y(w, x, x_dtype))
@@ -75,22 +82,23 @@ def test_planes_gemv_equals_blocks_and_oracle(rows, nblk, x_dtype):
     assert np.all(err <= TOL), err
 
 
-def test_planes_multi_matches_separate_calls():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_planes_multi_matches_separate_calls(fmt):
     items = [(67, 14), (16, 14), (130, 14), (33, 14)]
     ws, ps, ys = [], [], []
     x = gen_x(1, 14 * 256, "f32", seed=5)
     xd = to_dev_x(x, "f32")
     for i, (rows, nblk) in enumerate(items):
-        w = Weights("q4_k", rows, nblk * 256, seed=1100 + i)
+        w = Weights(fmt, rows, nblk * 256, seed=1100 + i)
         ws.append(w)
         ps.append(_planes(w))
         ys.append(torch.full((1, rows), -2.0, dtype=torch.float32, device=DEV))
-    say("planes multi: " + ", ".join(f"{w.rows}x{w.cols}" for w in ws))
-    qmv.qmv_gemv_multi("q4_k", "f32", 1, [(p, xd, y) for p, y in zip(ps, ys)])
+    say(f"planes multi {fmt}: " + ", ".join(f"{w.rows}x{w.cols}" for w in ws))
+    qmv.qmv_gemv_multi(fmt, "f32", 1, [(p, xd, y) for p, y in zip(ps, ys)])
     ref = []
     for w in ws:
         ref.append(torch.empty(1, w.rows, dtype=torch.float32, device=DEV))
-    qmv.qmv_gemv_multi("q4_k", "f32", 1, [(w.desc, xd, y) for w, y in zip(ws, ref)])
+    qmv.qmv_gemv_multi(fmt, "f32", 1, [(w.desc, xd, y) for w, y in zip(ws, ref)])
     torch.cuda.synchronize()
     for w, y, r in zip(ws, ys, ref):
         assert torch.equal(y, r), (w.rows, w.cols)
@@ -165,4 +173,27 @@ def test_full_size_layer_in_planes_sampled_rows():
             say(f"  {n}: sampled normwise err {err.max():.3e}")
             assert np.all(err <= TOL)
     del ws, ps
+    torch.cuda.empty_cache()
+
+
+def test_full_size_q6_k_lm_head_in_planes_sampled_rows():
+    """The Q6_K lm-head (152064 x 3584), repacked: every output equals the
+    canonical layout's, and sampled rows meet the gate."""
+    cfg = CONFIGS[4]
+    name, rows, cols = cfg["mats"][0]
+    say(f"planes full-size q6_k {name} {rows}x{cols}")
+    w = Weights("q6_k", rows, cols, seed=weight_seed(4, 0))
+    p = _planes(w)
+    x = gen_x(1, cols, "f32", x_seed(4, 0))
+    xd = to_dev_x(x, "f32")
+    yp = torch.empty(1, rows, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv("q6_k", p, xd, "f32", yp, rows, cols, 1)
+    yb = w.gemv(xd, "f32", 1)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, yb)
+    ids = _sample_rows(rows, seed=4)
+    err = oracle.normwise_rel_err(yp.cpu().numpy()[:, ids], oracle_y(w, x, "f32", ids))
+    say(f"  sampled normwise err {err.max():.3e}")
+    assert np.all(err <= TOL)
+    del w, p
     torch.cuda.empty_cache()
