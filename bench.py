@@ -338,6 +338,8 @@ def main() -> int:
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
     ap.add_argument("--batch", type=int, default=None, help="activation rows (config 5 only)")
     ap.add_argument("--rotate-gib", type=float, default=1.25)
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed graph replays before each timed one (steady-state clocks)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true", help="one launch per matrix")
@@ -462,6 +464,13 @@ def main() -> int:
                     launch(c, groups[gi], cap.cuda_stream)
         g.replay()                    # untimed: first-touch costs
         torch.cuda.synchronize()
+        # untimed replays for --settle-ms: the first timed region otherwise runs
+        # before the clocks settle under load (a single-launch step measured
+        # 92 us in the first graph and 80 us in the next, same kernel)
+        t_end = time.perf_counter() + args.settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            g.replay()
+            torch.cuda.synchronize()
         t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         t0.record(stream)
         g.replay()                    # replays on the current stream
@@ -544,7 +553,8 @@ def main() -> int:
                      "kernel": dom, "avg_launch_us": round(dom_avg_us, 3),
                      "launches_per_step": len(by_kernel[dom]),
                      "timing": "HIP events around a graph replay of the K steps restricted "
-                               "to this kernel's launches, on the replay stream",
+                               "to this kernel's launches, on the replay stream, after "
+                               f"{args.settle_ms:g} ms of untimed replays",
                      "bytes_per_launch": round(dom_bytes_per_launch, 1),
                      "flops_per_launch": round(dom_flops_per_launch, 1)},
     }
