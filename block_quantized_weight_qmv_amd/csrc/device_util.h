@@ -179,9 +179,13 @@ __device__ __forceinline__ void x_to_f32(const uint4* raw, float* out, const bf1
   }
 }
 
-// A lane's 64 activations as the Q4_K and Q5_K GEMVs multiply them: scaled by
-// 2^-e, a power of two chosen per lane so that the largest |x| lands in
-// [2^14, 2^15) (exact), and rounded once to fp16 (relative error <= 2^-11),
+// A lane's 64 fp16 or bf16 activations as the Q4_K and Q5_K GEMVs multiply
+// them: fp16 activations as they are (e = 0); bf16 ones scaled by 2^-e, a
+// power of two chosen per lane so that the largest |x| lands in
+// [2^14, 2^15), and converted to fp16 -- exact, bf16's 8 significant bits
+// fitting fp16's 11, for every element above 2^-31 of the lane's largest
+// (smaller ones fall into fp16's subnormal range: absolute error at most
+// 2^-40 of the largest),
 // paired in the order the code halves come (dword i of the lane's codes:
 // (byte 0, byte 2) and (byte 1, byte 3), low nibbles against activations
 // 4i.., high nibbles against 32 + 4i..).  xs = 2^(24+e) undoes both the
@@ -194,8 +198,41 @@ struct HalfXSlice {
   float xs;
 };
 
+// Activation slice type of a policy by activation type: fp32 activations keep
+// the exact fp32 slice F32 (one FMA per weight); fp16 and bf16 activations use
+// Half (two products per instruction).  Rounding fp32 activations to fp16
+// instead would cost up to 2^-11 of each product, which a row whose terms
+// cancel turns into a relative error above 2e-3 (measured: one 128-wide INT4
+// row at 2.3e-3).
+template <typename XT, class F32, class Half>
+struct XSliceFor {
+  typedef Half type;
+};
+template <class F32, class Half>
+struct XSliceFor<float, F32, Half> {
+  typedef F32 type;
+};
+
 __device__ __forceinline__ _Float16 scaled_f16(float v, int e) {
   return static_cast<_Float16>(__builtin_amdgcn_ldexpf(v, -e));
+}
+
+// The power of two e of a lane's n activations: 0 for fp16 activations (they
+// are used as given, exactly), else the one that puts the largest |x| into
+// [2^14, 2^15), kept where 2^(24+e) is a normal float (bf16 reaches 2^127:
+// e <= 103 covers |x| below 2^117).
+template <typename XT, int N>
+__device__ __forceinline__ int half_scale_exp(const float* v) {
+  if constexpr (__is_same(XT, _Float16)) {
+    return 0;
+  } else {
+    float mx = 0.f;
+#pragma unroll
+    for (int i = 0; i < N; ++i) mx = fmaxf(mx, fabsf(v[i]));
+    // mx = m 2^E with m in [0.5, 1): scaled by 2^-(E-15) it lies in [2^14, 2^15)
+    const int e = __builtin_amdgcn_frexp_expf(mx) - 15;
+    return e < -150 ? -150 : (e > 103 ? 103 : e);
+  }
 }
 
 template <typename XT>
@@ -210,12 +247,7 @@ __device__ __forceinline__ void finish_half_xslice(const uint4* raw, bool ok, Ha
   for (int i = 0; i < 32; ++i) s.s0 += v[i];
 #pragma unroll
   for (int i = 32; i < 64; ++i) s.s1 += v[i];
-  float mx = 0.f;
-#pragma unroll
-  for (int i = 0; i < 64; ++i) mx = fmaxf(mx, fabsf(v[i]));
-  // mx = m 2^E with m in [0.5, 1): scaled by 2^-(E-15) it lies in [2^14, 2^15)
-  int e = __builtin_amdgcn_frexp_expf(mx) - 15;
-  e = e < -150 ? -150 : (e > 103 ? 103 : e);
+  const int e = half_scale_exp<XT, 64>(v);
   s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
 #pragma unroll
   for (int i = 0; i < 8; ++i) {

@@ -11,10 +11,15 @@
 // 16-byte load instructions reads 1 KB of consecutive bytes, plus the fp16
 // scale of each half's group.  The code loads carry the nontemporal hint: no
 // other instruction reads their lines (a row's code bytes are a multiple of
-// 64 B, so only a row boundary can split a line).  Per lane, half and row, fp32 (codes enter as
-// fp16 subnormals, see device_util.h):
+// 64 B, so only a row boundary can split a line).  Per lane, half and row,
+// codes enter as fp16 subnormals (see device_util.h), sums in fp32:
 //   Se = sum u_even x_even 2^-24,  So = sum 16 u_odd x_odd 2^-24
-//   partial += s (2^24 (Se + So/16) - 8 X),  X = sum of the half's 32 activations
+//   partial += s (2^24 (Se + So/16) - 8 X),  X = fp32 sum of the half's 32 activations
+// fp32 activations: one v_fma_mix_f32 per weight.  fp16 activations (the
+// datastack runtime's FP16 activations) and bf16: two products per
+// v_dot2_f32_f16 against the activations as fp16 -- fp16 as given, bf16
+// scaled per lane by a power of two (half_scale_exp; exact) -- with 2^(24+e)
+// in place of 2^24.
 #include "gemv_skeleton.h"
 
 namespace qmv {
@@ -22,10 +27,17 @@ namespace qmv {
 struct Int4G128Policy {
   static constexpr int kColsPerWave = 64 * 64;
   static constexpr int kXElems = 64;
-  struct XSlice {
+  struct XSliceF32 {
     float v[64];  // v[32h + k]: activation of column col[h] + k
     float s[2];
   };
+  struct XSliceHalf {
+    h2_t h[32];  // h[16 hf + 4 i + p]: fp16 activation pairs of half hf, dword i, pair p
+    float s[2];  // fp32 sums of each half's 32 activations
+    float xs;    // 2^(24 + e)
+  };
+  template <typename XT>
+  using XSliceT = typename XSliceFor<XT, XSliceF32, XSliceHalf>::type;
   struct Frag {
     uint4 q[2];
     uint32_t sb[2];
@@ -60,16 +72,37 @@ struct Int4G128Policy {
   }
 
   template <typename XT>
-  __device__ void finish_x(const uint4* raw, XSlice& s) const {
-    x_to_f32<64>(raw, s.v, static_cast<const XT*>(nullptr));
+  __device__ void finish_x(const uint4* raw, XSliceT<XT>& s) const {
+    float v[64];  // v[32 hf + k]: activation of column col[hf] + k
+    float* dst = v;
+    if constexpr (__is_same(XT, float)) dst = s.v;
+    x_to_f32<64>(raw, dst, static_cast<const XT*>(nullptr));
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      s.s[h] = 0.f;
+    for (int hf = 0; hf < 2; ++hf) {
+      s.s[hf] = 0.f;
 #pragma unroll
       for (int k = 0; k < 32; ++k) {
-        s.v[32 * h + k] = okh[h] ? s.v[32 * h + k] : 0.f;
-        s.s[h] += s.v[32 * h + k];
+        dst[32 * hf + k] = okh[hf] ? dst[32 * hf + k] : 0.f;
+        s.s[hf] += dst[32 * hf + k];
       }
+    }
+    if constexpr (!__is_same(XT, float)) {
+      const int e = half_scale_exp<XT, 64>(v);
+      s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
+      // dword i of a half holds weights 8i..8i+7, two per byte; the code pairs
+      // are (8i, 8i+4), (8i+2, 8i+6) from the low nibbles and (8i+1, 8i+5),
+      // (8i+3, 8i+7) from the high nibbles
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* x = v + 32 * hf + 8 * i;
+          h2_t* o = s.h + 16 * hf + 4 * i;
+          o[0] = h2_t{scaled_f16(x[0], e), scaled_f16(x[4], e)};
+          o[1] = h2_t{scaled_f16(x[2], e), scaled_f16(x[6], e)};
+          o[2] = h2_t{scaled_f16(x[1], e), scaled_f16(x[5], e)};
+          o[3] = h2_t{scaled_f16(x[3], e), scaled_f16(x[7], e)};
+        }
     }
   }
 
@@ -81,12 +114,12 @@ struct Int4G128Policy {
     }
   }
 
-  __device__ float dot(const Frag& f, const XSlice& s) const {
+  template <typename XT>
+  __device__ float dot(const Frag& f, const XSliceT<XT>& s) const {
     float out = 0.f;
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t q[4] = {f.q[h].x, f.q[h].y, f.q[h].z, f.q[h].w};
-      const float* v = s.v + 32 * h;
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t q[4] = {f.q[hf].x, f.q[hf].y, f.q[hf].z, f.q[hf].w};
       float se = 0.f, so = 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -94,18 +127,31 @@ struct Int4G128Policy {
         const uint32_t w0 = q[i], w8 = q[i] >> 8;
         const uint32_t a = w0 & 0x000F000Fu, b = w8 & 0x000F000Fu;  // u_{8i}, u_{8i+4} | u_{8i+2}, u_{8i+6}
         const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;  // 16 u_{8i+1}, ... (odd weights)
-        const float* x = v + 8 * i;
-        se = fma_lo(a, x[0], se);
-        se = fma_lo(b, x[2], se);
-        se = fma_hi(a, x[4], se);
-        se = fma_hi(b, x[6], se);
-        so = fma_lo(e, x[1], so);
-        so = fma_lo(g, x[3], so);
-        so = fma_hi(e, x[5], so);
-        so = fma_hi(g, x[7], so);
+        if constexpr (__is_same(XT, float)) {
+          const float* x = s.v + 32 * hf + 8 * i;
+          se = fma_lo(a, x[0], se);
+          se = fma_lo(b, x[2], se);
+          se = fma_hi(a, x[4], se);
+          se = fma_hi(b, x[6], se);
+          so = fma_lo(e, x[1], so);
+          so = fma_lo(g, x[3], so);
+          so = fma_hi(e, x[5], so);
+          so = fma_hi(g, x[7], so);
+        } else {
+          const h2_t* x = s.h + 16 * hf + 4 * i;
+          se = dot2_lo_hi(a, x[0], se);
+          se = dot2_lo_hi(b, x[1], se);
+          so = dot2_lo_hi(e, x[2], so);
+          so = dot2_lo_hi(g, x[3], so);
+        }
       }
-      const float t = fmaf(kTwo24, fmaf(so, 0.0625f, se), -8.f * s.s[h]);
-      out = fmaf(f16_to_f32(f.sb[h]), t, out);
+      float xs;
+      if constexpr (__is_same(XT, float))
+        xs = kTwo24;
+      else
+        xs = s.xs;
+      const float t = fmaf(xs, fmaf(so, 0.0625f, se), -8.f * s.s[hf]);
+      out = fmaf(f16_to_f32(f.sb[hf]), t, out);
     }
     return out;
   }

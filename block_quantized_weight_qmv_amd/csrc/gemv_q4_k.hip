@@ -10,24 +10,15 @@
 // blocks (4096 columns) with three 16-byte loads per lane and row: the block
 // header (shared by the four lanes) and the lane's two qs quarters.
 //
-// Arithmetic per lane and row, two products per instruction:
-//   S0 = sum_l u_lo[l] xh[l] 2^-24,  S1 = sum_l 16 u_hi[l] xh[32+l] 2^-24
-//   partial = d 2^(24+e) (sc0 S0 + sc1/16 S1) - dmin (m0 X0 + m1 X1)
-// Each dword of qs (8 codes) costs one shift and four ANDs (masks 0x000F000F
-// / 0x00F000F0 leave two codes per dword as fp16 subnormals) and four
-// v_dot2_f32_f16, which multiply two code halves by two fp16 activations and
-// add both products to an fp32 sum.  xh is the lane's 64 activations scaled
-// by 2^-e (a power of two chosen per lane so that its largest |x| lands in
-// [2^14, 2^15)) and rounded once to fp16; the 2^e is folded into d's 2^24.
-// The codes and the scaling are exact, so the only change from fp32
-// activations is that rounding: a relative error of at most 2^-11 per
-// activation, about 2.5e-4 normwise on y for N(0,1) activations, against
-// the 2e-3 bound.  Integer activations, unit vectors and power-of-two
-// multiples of x stay exact.  X0, X1, the sub-block sums of the unrounded
-// activations that the min term takes, are computed in fp32 once per wave.
-// With one v_fma_mix_f32 per weight instead, the VALU work was the part of
-// the 7B layer's time that the memory stream did not hide (gate+up 17.8-18.3
-// us against 15.2-15.9 us with two products per instruction, same box).
+// Arithmetic per lane and row.  fp32 activations (exact, one rounding per FMA):
+//   S0 = sum_l u_lo[l] x[l] 2^-24,  S1 = sum_l 16 u_hi[l] x[32+l] 2^-24
+//   partial = d 2^24 (sc0 S0 + sc1/16 S1) - dmin (m0 X0 + m1 X1)
+// X0, X1 are the sub-block sums of x, computed once per wave.  Each dword of
+// qs (8 codes) costs one shift and four ANDs (masks 0x000F000F / 0x00F000F0
+// leave two codes per dword as fp16 subnormals) and eight v_fma_mix_f32.
+// fp16 and bf16 activations (HalfXSlice, exact): the same sums with two
+// products per v_dot2_f32_f16, four per dword instead of eight FMAs, and
+// 2^(24+e) in place of 2^24 for the lane's power-of-two activation scale.
 #include "gemv_skeleton.h"
 
 namespace qmv {
@@ -35,7 +26,12 @@ namespace qmv {
 struct Q4KPolicy {
   static constexpr int kColsPerWave = 16 * 256;
   static constexpr int kXElems = 64;
-  typedef HalfXSlice XSlice;
+  struct XSliceF32 {
+    float v[64];
+    float s0, s1;
+  };
+  template <typename XT>
+  using XSliceT = typename XSliceFor<XT, XSliceF32, HalfXSlice>::type;
   struct Frag {
     uint4 hd, qa, qb;
   };
@@ -76,8 +72,20 @@ struct Q4KPolicy {
   }
 
   template <typename XT>
-  __device__ void finish_x(const uint4* raw, XSlice& s) const {
-    finish_half_xslice<XT>(raw, ok, s);
+  __device__ void finish_x(const uint4* raw, XSliceT<XT>& s) const {
+    if constexpr (__is_same(XT, float)) {
+      x_to_f32<64>(raw, s.v, static_cast<const XT*>(nullptr));
+#pragma unroll
+      for (int i = 0; i < 64; ++i) s.v[i] = ok ? s.v[i] : 0.f;
+      s.s0 = 0.f;
+      s.s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s.s0 += s.v[i];
+#pragma unroll
+      for (int i = 32; i < 64; ++i) s.s1 += s.v[i];
+    } else {
+      finish_half_xslice<XT>(raw, ok, s);
+    }
   }
 
   __device__ void load(int row, Frag& f) const {
@@ -87,24 +95,46 @@ struct Q4KPolicy {
     f.qb = ld16(p + 32 + 32 * c);
   }
 
-  __device__ float dot(const Frag& f, const XSlice& s) const {
+  template <typename XT>
+  __device__ float dot(const Frag& f, const XSliceT<XT>& s) const {
     const uint32_t t1 = f.hd.y >> sh, t2 = f.hd.z >> sh, t3 = f.hd.w >> sh;
     const uint32_t sc = ((hi ? t3 : t1) & mask_a) | ((t1 >> 2) & mask_b);
     const uint32_t mn = ((hi ? (t3 >> 4) : t2) & mask_a) | ((t2 >> 2) & mask_b);
-    const float d = f16_to_f32(f.hd.x & 0xFFFFu) * s.xs;
     const float dmin = f16_to_f32(f.hd.x >> 16);
 
     const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
     float s0 = 0.f, s1 = 0.f;
+    float d;
+    if constexpr (__is_same(XT, float)) {
+      d = f16_to_f32(f.hd.x & 0xFFFFu) * kTwo24;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t w0 = q[i], w8 = q[i] >> 8;
-      const uint32_t a = w0 & 0x000F000Fu, b = w8 & 0x000F000Fu;  // low nibbles, bytes 0/2 and 1/3
-      const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;  // high nibbles (x16)
-      s0 = dot2_lo_hi(a, s.h[4 * i + 0], s0);
-      s0 = dot2_lo_hi(b, s.h[4 * i + 1], s0);
-      s1 = dot2_lo_hi(e, s.h[4 * i + 2], s1);
-      s1 = dot2_lo_hi(g, s.h[4 * i + 3], s1);
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w0 = q[i], w8 = q[i] >> 8;
+        const uint32_t a = w0 & 0x000F000Fu, b = w8 & 0x000F000Fu;  // low nibbles, bytes 0/2 and 1/3
+        const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;  // high nibbles (x16)
+        const float* x0 = s.v + 4 * i;
+        const float* x1 = s.v + 32 + 4 * i;
+        s0 = fma_lo(a, x0[0], s0);
+        s0 = fma_lo(b, x0[1], s0);
+        s0 = fma_hi(a, x0[2], s0);
+        s0 = fma_hi(b, x0[3], s0);
+        s1 = fma_lo(e, x1[0], s1);
+        s1 = fma_lo(g, x1[1], s1);
+        s1 = fma_hi(e, x1[2], s1);
+        s1 = fma_hi(g, x1[3], s1);
+      }
+    } else {
+      d = f16_to_f32(f.hd.x & 0xFFFFu) * s.xs;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t w0 = q[i], w8 = q[i] >> 8;
+        const uint32_t a = w0 & 0x000F000Fu, b = w8 & 0x000F000Fu;
+        const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;
+        s0 = dot2_lo_hi(a, s.h[4 * i + 0], s0);
+        s0 = dot2_lo_hi(b, s.h[4 * i + 1], s0);
+        s1 = dot2_lo_hi(e, s.h[4 * i + 2], s1);
+        s1 = dot2_lo_hi(g, s.h[4 * i + 3], s1);
+      }
     }
     const float t = fmaf(cvt_ubyte<1>(sc) * 0.0625f, s1, cvt_ubyte<0>(sc) * s0);
     const float mm = fmaf(cvt_ubyte<1>(mn), s.s1, cvt_ubyte<0>(mn) * s.s0);

@@ -22,11 +22,12 @@
 //   e = bytes 0, 2 high nibbles at bits 4-7 / 20-23, fifth bit to 8 / 24
 //   g = bytes 1, 3 high nibbles (after >> 8),        fifth bit to 8 / 24
 // so a and b carry u (0..31) and e and g carry 16u (0..496) as fp16
-// subnormals, and the sums are as in Q4_K, two products per v_dot2_f32_f16
-// against the lane's activations scaled by 2^-e and rounded to fp16
-// (HalfXSlice; products exact, 9 + 11 significant bits):
-//   S0 = sum u xh 2^-24, S1 = sum 16 u xh 2^-24,
-//   partial = d 2^(24+e) (sc0 S0 + sc1/16 S1) - dmin (m0 X0 + m1 X1).
+// subnormals, and the sums are as in Q4_K:
+//   S0 = sum u x 2^-24, S1 = sum 16 u x 2^-24,
+//   partial = d 2^24 (sc0 S0 + sc1/16 S1) - dmin (m0 X0 + m1 X1),
+// one v_fma_mix_f32 per weight for fp32 activations; for fp16 and bf16
+// activations two products per v_dot2_f32_f16 (HalfXSlice; exact, 9 + 11
+// significant bits), with 2^(24+e) for the lane's activation scale.
 #include "gemv_skeleton.h"
 
 namespace qmv {
@@ -34,7 +35,12 @@ namespace qmv {
 struct Q5KPolicy {
   static constexpr int kColsPerWave = 16 * 256;
   static constexpr int kXElems = 64;
-  typedef HalfXSlice XSlice;
+  struct XSliceF32 {
+    float v[64];
+    float s0, s1;
+  };
+  template <typename XT>
+  using XSliceT = typename XSliceFor<XT, XSliceF32, HalfXSlice>::type;
   struct Frag {
     uint4 hd, h0, h1, qa, qb;
   };
@@ -77,8 +83,20 @@ struct Q5KPolicy {
   }
 
   template <typename XT>
-  __device__ void finish_x(const uint4* raw, XSlice& s) const {
-    finish_half_xslice<XT>(raw, ok, s);
+  __device__ void finish_x(const uint4* raw, XSliceT<XT>& s) const {
+    if constexpr (__is_same(XT, float)) {
+      x_to_f32<64>(raw, s.v, static_cast<const XT*>(nullptr));
+#pragma unroll
+      for (int i = 0; i < 64; ++i) s.v[i] = ok ? s.v[i] : 0.f;
+      s.s0 = 0.f;
+      s.s1 = 0.f;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) s.s0 += s.v[i];
+#pragma unroll
+      for (int i = 32; i < 64; ++i) s.s1 += s.v[i];
+    } else {
+      finish_half_xslice<XT>(raw, ok, s);
+    }
   }
 
   __device__ void load(int row, Frag& f) const {
@@ -90,11 +108,16 @@ struct Q5KPolicy {
     f.qb = ld16(p + 64 + 32 * c);
   }
 
-  __device__ float dot(const Frag& f, const XSlice& s) const {
+  template <typename XT>
+  __device__ float dot(const Frag& f, const XSliceT<XT>& s) const {
     const uint32_t t1 = f.hd.y >> sh, t2 = f.hd.z >> sh, t3 = f.hd.w >> sh;
     const uint32_t sc = ((hi ? t3 : t1) & mask_a) | ((t1 >> 2) & mask_b);
     const uint32_t mn = ((hi ? (t3 >> 4) : t2) & mask_a) | ((t2 >> 2) & mask_b);
-    const float d = f16_to_f32(f.hd.x & 0xFFFFu) * s.xs;
+    float d;
+    if constexpr (__is_same(XT, float))
+      d = f16_to_f32(f.hd.x & 0xFFFFu) * kTwo24;
+    else
+      d = f16_to_f32(f.hd.x & 0xFFFFu) * s.xs;
     const float dmin = f16_to_f32(f.hd.x >> 16);
 
     const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
@@ -107,10 +130,23 @@ struct Q5KPolicy {
       const uint32_t b = (w8 & 0x000F000Fu) | (__builtin_rotateright32(h[i], rb) & 0x00100010u);
       const uint32_t e = (w0 & 0x00F000F0u) | (__builtin_rotateright32(h[i], re) & 0x01000100u);
       const uint32_t g = (w8 & 0x00F000F0u) | (__builtin_rotateright32(h[i], rg) & 0x01000100u);
-      s0 = dot2_lo_hi(a, s.h[4 * i + 0], s0);
-      s0 = dot2_lo_hi(b, s.h[4 * i + 1], s0);
-      s1 = dot2_lo_hi(e, s.h[4 * i + 2], s1);
-      s1 = dot2_lo_hi(g, s.h[4 * i + 3], s1);
+      if constexpr (__is_same(XT, float)) {
+        const float* x0 = s.v + 4 * i;
+        const float* x1 = s.v + 32 + 4 * i;
+        s0 = fma_lo(a, x0[0], s0);
+        s0 = fma_lo(b, x0[1], s0);
+        s0 = fma_hi(a, x0[2], s0);
+        s0 = fma_hi(b, x0[3], s0);
+        s1 = fma_lo(e, x1[0], s1);
+        s1 = fma_lo(g, x1[1], s1);
+        s1 = fma_hi(e, x1[2], s1);
+        s1 = fma_hi(g, x1[3], s1);
+      } else {
+        s0 = dot2_lo_hi(a, s.h[4 * i + 0], s0);
+        s0 = dot2_lo_hi(b, s.h[4 * i + 1], s0);
+        s1 = dot2_lo_hi(e, s.h[4 * i + 2], s1);
+        s1 = dot2_lo_hi(g, s.h[4 * i + 3], s1);
+      }
     }
     const float t = fmaf(cvt_ubyte<1>(sc) * 0.0625f, s1, cvt_ubyte<0>(sc) * s0);
     const float mm = fmaf(cvt_ubyte<1>(mn), s.s1, cvt_ubyte<0>(mn) * s.s0);

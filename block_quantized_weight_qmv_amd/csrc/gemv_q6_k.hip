@@ -25,6 +25,8 @@ struct Q6KPolicy {
     float v[64];  // v[16g + t] = x[col0 + 32g + t]
     float s[4];
   };
+  template <typename XT>
+  using XSliceT = XSlice;  // fp32 activations for every activation type
   struct Frag {
     uint4 la, lb, qh;
     uint2 sc;
@@ -79,6 +81,7 @@ struct Q6KPolicy {
     f.d = ld_u16(p + 208);
   }
 
+  template <typename XT>
   __device__ float dot(const Frag& f, const XSlice& s) const {
     const uint32_t la[4] = {f.la.x, f.la.y, f.la.z, f.la.w};
     const uint32_t lb[4] = {f.lb.x, f.lb.y, f.lb.z, f.lb.w};

@@ -20,6 +20,8 @@ struct Q80Policy {
     float v[32];
     float s;
   };
+  template <typename XT>
+  using XSliceT = XSlice;  // fp32 activations for every activation type
   struct Frag {
     uint4 qa, qb;
     uint32_t d;
@@ -63,6 +65,7 @@ struct Q80Policy {
     f.qb = ld16_any(p + 18);
   }
 
+  template <typename XT>
   __device__ float dot(const Frag& f, const XSlice& s) const {
     const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
     float acc = 0.f;

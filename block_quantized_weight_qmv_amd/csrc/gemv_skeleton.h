@@ -36,10 +36,11 @@
 //    is fixed, so results are deterministic; with kw > 1 the wave totals are
 //    added in wave order through LDS.  y is overwritten.
 //
-// A format policy P provides kColsPerWave, kXElems, XSlice, Frag, a
+// A format policy P provides kColsPerWave, kXElems, XSliceT<XT> (the lane's
+// activations as the policy multiplies activations of type XT), Frag, a
 // constructor (w, scales_offset, cols, kslot, lane), load_x_raw(x, uint4*),
-// finish_x<XT>(raw, XSlice&), load(row, Frag&) and dot(Frag, XSlice) -> this
-// lane's partial of W[row] . x.
+// finish_x<XT>(raw, XSliceT<XT>&), load(row, Frag&) and
+// dot<XT>(Frag, XSliceT<XT>) -> this lane's partial of W[row] . x.
 #pragma once
 
 #include "device_util.h"
@@ -95,13 +96,13 @@ __device__ __forceinline__ void load_tile(const P& pol, typename P::Frag* f, int
 
 // Reduce a tile and store its rows: to y when this wave covers all of K, else
 // this wave's K-slice sums to its LDS column `part` (indexed by row - r_begin).
-template <class P, int R>
+template <class P, typename XT, int R>
 __device__ __forceinline__ void finish_tile(const P& pol, const typename P::Frag* f,
-                                            const typename P::XSlice& xs, float* y, int row0,
+                                            const typename P::template XSliceT<XT>& xs, float* y, int row0,
                                             int r_begin, int r_end, int kw, int lane, float* part) {
   float acc[R];
 #pragma unroll
-  for (int r = 0; r < R; ++r) acc[r] = pol.dot(f[r], xs);
+  for (int r = 0; r < R; ++r) acc[r] = pol.template dot<XT>(f[r], xs);
   const float t = reduce_rows<R>(acc, lane);
   if (lane < R && row0 + lane < r_end) {
     // The LDS write is a relaxed atomic store (a plain ds_write) so that the
@@ -208,7 +209,7 @@ gemv_kernel(const GemvLaunch args) {
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   }
-  typename P::XSlice xs;
+  typename P::template XSliceT<XT> xs;
   pol.template finish_x<XT>(raw, xs);
 
   // Each prefetch is pinned right after the tile whose registers it reuses:
@@ -233,7 +234,7 @@ gemv_kernel(const GemvLaunch args) {
   for (int t = D; t < ntiles; t += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-      finish_tile<P, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
+      finish_tile<P, XT, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
       load_tile<P, R>(pol, f[j], r0 + (j + D) * R, r_last);
       __asm__ __volatile__("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
@@ -242,7 +243,7 @@ gemv_kernel(const GemvLaunch args) {
   }
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (r0 + j * R < r_end) finish_tile<P, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
+    if (r0 + j * R < r_end) finish_tile<P, XT, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
 
   // K split: after one barrier, the kw waves of the set add the columns of
   // their set in slot order, row by row (waves that left early count as

@@ -162,32 +162,34 @@ def test_full_size_configs_sampled_rows(config):
         torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("fmt,layout", [("q4_k", "blocks"), ("q4_k", "planes"), ("q5_k", "blocks")])
+@pytest.mark.parametrize("fmt,layout", [("q4_k", "blocks"), ("q4_k", "planes"), ("q5_k", "blocks"),
+                                        ("int4_g128", "blocks")])
 @pytest.mark.parametrize("spread", ["wide", "large", "tiny"])
-def test_half_activation_range(fmt, layout, spread):
-    """Q4_K and Q5_K round each lane's activations to fp16 after scaling them
-    by a power of two of their own: magnitudes far outside fp16's range (and a
-    spread of twelve decades within one row) must still meet the gate."""
+def test_bf16_activation_range(fmt, layout, spread):
+    """Q4_K, Q5_K and INT4 take bf16 activations as fp16 after scaling each
+    lane's activations by a power of two of their own: magnitudes far outside
+    fp16's range (and a spread of twelve decades within one row) must still
+    meet the gate."""
     rows, cols = 96, 17 * 256
     w = Weights(fmt, rows, cols, seed=808)
     g = np.random.Generator(np.random.PCG64({"wide": 1, "large": 2, "tiny": 3}[spread]))
-    x = g.standard_normal((2, cols))
+    x = g.standard_normal((1, cols))
     if spread == "wide":
         x *= 10.0 ** g.uniform(-6, 6, size=x.shape)
     elif spread == "large":
         x *= 1e20
     else:
         x *= 1e-30
-    x = x.astype(np.float32)
+    x = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # bf16 bit patterns
     desc = w.desc
     if layout == "planes":
-        dst = torch.empty(qmv.qmv_planes_size("q4_k", rows, cols), dtype=torch.uint8, device=DEV)
+        dst = torch.empty(qmv.qmv_planes_size(fmt, rows, cols), dtype=torch.uint8, device=DEV)
         desc = qmv.qmv_repack_planes(w.desc, dst)
-    say(f"{fmt} activation range {spread} ({layout})")
-    y = torch.empty(2, rows, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv(fmt, desc, to_dev_x(x, "f32"), "f32", y, rows, cols, 2)
+    say(f"{fmt} bf16 activation range {spread} ({layout})")
+    y = torch.empty(1, rows, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv(fmt, desc, to_dev_x(x, "bf16"), "bf16", y, rows, cols, 1)
     got = y.cpu().numpy()
     assert np.all(np.isfinite(got))
-    err = _err(got, oracle_y(w, x, "f32"))
+    err = _err(got, oracle_y(w, x, "bf16"))
     say(f"  normwise err {err.max():.3e}")
     assert np.all(err <= TOL), err
