@@ -47,7 +47,8 @@ _KERNEL_SOURCES = {
     "gemm_q4_k_bf16_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
 }
 _POLICY_SOURCE = {"Q80Policy": "gemv_q8_0.hip", "Q4KPolicy": "gemv_q4_k.hip",
-                  "Q4KPlanesPolicy": "gemv_q4_k.hip", "Q6KPlanesPolicy": "gemv_q6_k.hip",
+                  "Q4KPlanesPolicy": "gemv_q4_k.hip", "Q5KPlanesPolicy": "gemv_q5_k.hip",
+                  "Q6KPlanesPolicy": "gemv_q6_k.hip",
                   "Q5KPolicy": "gemv_q5_k.hip", "Q6KPolicy": "gemv_q6_k.hip",
                   "Int4G128Policy": "gemv_int4_g128.hip"}
 
@@ -92,7 +93,7 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
            "int4_g128": "Int4G128Policy", "q5_k": "Q5KPolicy"}[fmt]
     if layout == "planes":
-        pol = {"q4_k": "Q4KPlanesPolicy", "q6_k": "Q6KPlanesPolicy"}[fmt]
+        pol = {"q4_k": "Q4KPlanesPolicy", "q5_k": "Q5KPlanesPolicy", "q6_k": "Q6KPlanesPolicy"}[fmt]
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
     return f"qmv::gemv_kernel<qmv::{pol}, {xt}, {cfg}>"
 
@@ -167,14 +168,14 @@ PEAK_TFLOPS_BF16 = 2500.0   # MI355X dense bf16 matrix cores, vendor figure
 
 
 def default_layout(config: int, batch: int | None) -> str:
-    """Q4_K and Q6_K on the GEMV path stream the plane layout (repacked once at
+    """Q4_K, Q5_K and Q6_K on the GEMV path stream the plane layout (repacked once at
     load, as a decode layout replacing the blocks); the matrix-core path and
     the other formats read the canonical blocks."""
     from synth import CONFIGS
     cfg = CONFIGS[config]
     b = batch or cfg["batch"][0]
     gemv = not (cfg["x_dtype"] == "bf16" and b >= 2)
-    return "planes" if cfg["fmt"] in ("q4_k", "q6_k") and gemv else "blocks"
+    return "planes" if cfg["fmt"] in ("q4_k", "q5_k", "q6_k") and gemv else "blocks"
 
 
 def workload_plan(config: int, batch: int | None, separate: bool, layout: str = "blocks") -> dict:
@@ -344,7 +345,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true", help="one launch per matrix")
     ap.add_argument("--layout", choices=["auto", "blocks", "planes"], default="auto",
-                    help="weight layout in HBM (auto: planes for Q4_K and Q6_K on the GEMV path, else blocks)")
+                    help="weight layout in HBM (auto: planes for Q4_K, Q5_K and Q6_K on the GEMV path, else blocks)")
     ap.add_argument("--eager-pass", action="store_true",
                     help="only issue warmup + steps eagerly (no graphs, no timing): for counter runs")
     ap.add_argument("--summarize-counters", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),

@@ -59,7 +59,7 @@ static int32_t check_weights(const qmv_weights* W) {
   if (W->layout != QMV_LAYOUT_BLOCKS && W->layout != QMV_LAYOUT_PLANES)
     return fail(QMV_ERR_FORMAT, "unknown layout %d", W->layout);
   const bool planes = W->layout == QMV_LAYOUT_PLANES;
-  if (planes && W->fmt != QMV_Q4_K && W->fmt != QMV_Q6_K)
+  if (planes && W->fmt != QMV_Q4_K && W->fmt != QMV_Q5_K && W->fmt != QMV_Q6_K)
     return fail(QMV_ERR_UNSUPPORTED, "format %d has no plane layout", W->fmt);
   const uint64_t need = planes ? qmv_planes_size(W->fmt, W->rows, W->cols)
                                : qmv_packed_size(W->fmt, W->rows, W->cols);
@@ -70,7 +70,7 @@ static int32_t check_weights(const qmv_weights* W) {
     return fail(QMV_ERR_SIZE, "weights hold %llu bytes, format needs %llu",
                 (unsigned long long)W->nbytes, (unsigned long long)need);
   const uint64_t soff = W->fmt == QMV_INT4_G128 ? static_cast<uint64_t>(W->rows * W->cols / 2)
-                        : planes                ? q4k_planes(W->rows, W->cols).a  // same unit for Q6_K
+                        : planes                ? q4k_planes(W->rows, W->cols).a  // same unit for Q5_K, Q6_K
                                                 : 0;
   if (W->scales_offset != soff)
     return fail(QMV_ERR_FORMAT, "scales_offset %llu, expected %llu",
@@ -113,8 +113,11 @@ uint64_t qmv_packed_size(int32_t fmt, int64_t rows, int64_t cols) {
 }
 
 uint64_t qmv_planes_size(int32_t fmt, int64_t rows, int64_t cols) {
-  if ((fmt != QMV_Q4_K && fmt != QMV_Q6_K) || qmv_packed_size(fmt, rows, cols) == 0) return 0;
-  return fmt == QMV_Q4_K ? qmv::q4k_planes(rows, cols).total : qmv::q6k_planes(rows, cols).total;
+  if ((fmt != QMV_Q4_K && fmt != QMV_Q5_K && fmt != QMV_Q6_K) || qmv_packed_size(fmt, rows, cols) == 0)
+    return 0;
+  return fmt == QMV_Q4_K   ? qmv::q4k_planes(rows, cols).total
+         : fmt == QMV_Q5_K ? qmv::q5k_planes(rows, cols).total
+                           : qmv::q6k_planes(rows, cols).total;
 }
 
 int32_t qmv_repack_planes(const qmv_weights* src, void* dst, uint64_t dst_bytes, qmv_weights* out,
@@ -125,7 +128,7 @@ int32_t qmv_repack_planes(const qmv_weights* src, void* dst, uint64_t dst_bytes,
   if (st != QMV_OK) return st;
   if (src->layout != QMV_LAYOUT_BLOCKS)
     return fail(QMV_ERR_UNSUPPORTED, "source is not in the canonical block layout");
-  if (src->fmt != QMV_Q4_K && src->fmt != QMV_Q6_K)
+  if (src->fmt != QMV_Q4_K && src->fmt != QMV_Q5_K && src->fmt != QMV_Q6_K)
     return fail(QMV_ERR_UNSUPPORTED, "format %d has no plane layout", src->fmt);
   const uint64_t need = qmv_planes_size(src->fmt, src->rows, src->cols);
   if (dst_bytes < need)
@@ -135,9 +138,10 @@ int32_t qmv_repack_planes(const qmv_weights* src, void* dst, uint64_t dst_bytes,
   const uintptr_t s0 = reinterpret_cast<uintptr_t>(src->data), s1 = s0 + src->nbytes;
   const uintptr_t d0 = reinterpret_cast<uintptr_t>(dst), d1 = d0 + need;
   if (s0 < d1 && d0 < s1) return fail(QMV_ERR_SHAPE, "destination overlaps the source");
-  const hipError_t e = src->fmt == QMV_Q4_K
-                           ? qmv::repack_q4_k_planes(*src, dst, static_cast<hipStream_t>(stream))
-                           : qmv::repack_q6_k_planes(*src, dst, static_cast<hipStream_t>(stream));
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const hipError_t e = src->fmt == QMV_Q4_K   ? qmv::repack_q4_k_planes(*src, dst, s)
+                       : src->fmt == QMV_Q5_K ? qmv::repack_q5_k_planes(*src, dst, s)
+                                              : qmv::repack_q6_k_planes(*src, dst, s);
   if (e != hipSuccess) return qmv::from_hip(e, "qmv_repack_planes launch");
   qmv_weights w = *src;
   w.layout = QMV_LAYOUT_PLANES;
@@ -246,7 +250,10 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
       e = planes ? qmv::gemv_q4_k_planes(calls, n, x_dtype, batch, s)
                  : qmv::gemv_q4_k(calls, n, x_dtype, batch, s);
       break;
-    case QMV_Q5_K: e = qmv::gemv_q5_k(calls, n, x_dtype, batch, s); break;
+    case QMV_Q5_K:
+      e = planes ? qmv::gemv_q5_k_planes(calls, n, x_dtype, batch, s)
+                 : qmv::gemv_q5_k(calls, n, x_dtype, batch, s);
+      break;
     case QMV_Q6_K:
       e = planes ? qmv::gemv_q6_k_planes(calls, n, x_dtype, batch, s)
                  : qmv::gemv_q6_k(calls, n, x_dtype, batch, s);

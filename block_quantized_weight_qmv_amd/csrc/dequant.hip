@@ -123,6 +123,31 @@ __device__ __forceinline__ void dq_q6_k(const uint8_t* row, int k, float* w) {
 // 16 (2h + i) + t, sc[k] at 12 a + 16 b + k, d at 13 a + 2 b.  Same decode as
 // dq_q6_k, byte addresses aside.
 constexpr int kQ6KPlanes = 0x103;  // kernel template tag, not a public format
+constexpr int kQ5KPlanes = 0x105;  // kernel template tag, not a public format
+
+// Q5_K in the plane layout (planes.h): header of block b at 16 b, qh[l] at
+// a + 16 b + l (l < 16) or 2 a + 16 b + l - 16, qs[32c + l] at
+// 3 a + 64 b + 16 c + l (l < 16) or 7 a + 64 b + 16 c + l - 16.  Same decode
+// as dq_q5_k, byte addresses aside.
+__device__ __forceinline__ void dq_q5_k_planes(const uint8_t* w, uint64_t a, int64_t b, int k,
+                                               float* out) {
+  const uint8_t* h = w + 16 * b;
+  const float d = f16_to_f32(ld_le16(h));
+  const float dmin = f16_to_f32(ld_le16(h + 2));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const int t = (k + e) % 256;
+    const int c = t >> 6, hh = (t >> 5) & 1, l = t & 31, s = t >> 5;
+    uint32_t scale, mn;
+    k_scale_min(h + 4, s, scale, mn);
+    const uint8_t* q = l < 16 ? w + 3 * a + 64 * b + 16 * c + l : w + 7 * a + 64 * b + 16 * c + (l - 16);
+    const uint8_t* qh = l < 16 ? w + a + 16 * b + l : w + 2 * a + 16 * b + (l - 16);
+    const uint32_t lo = (ld_u8(q) >> (4 * hh)) & 15;
+    const uint32_t hi = (ld_u8(qh) >> s) & 1;
+    const uint32_t u = lo | (hi << 4);
+    out[e] = (d * static_cast<float>(scale)) * static_cast<float>(u) - dmin * static_cast<float>(mn);
+  }
+}
 
 __device__ __forceinline__ void dq_q6_k_planes(const uint8_t* w, uint64_t a, int64_t b, int k,
                                                float* out) {
@@ -178,6 +203,8 @@ dequant_kernel(const uint8_t* __restrict__ w, uint64_t scales_offset, int rows, 
       dq_q4_k(w + static_cast<size_t>(r) * (cols / 256) * 144, k, v);
     } else if (FMT == kQ4KPlanes) {
       dq_q4_k_planes(w, scales_offset, static_cast<int64_t>(r) * (cols / 256) + k / 256, k, v);
+    } else if (FMT == kQ5KPlanes) {
+      dq_q5_k_planes(w, scales_offset, static_cast<int64_t>(r) * (cols / 256) + k / 256, k, v);
     } else if (FMT == kQ6KPlanes) {
       dq_q6_k_planes(w, scales_offset, static_cast<int64_t>(r) * (cols / 256) + k / 256, k, v);
     } else if (FMT == QMV_Q5_K) {
@@ -230,6 +257,7 @@ static hipError_t dequant_fmt(const qmv_weights& W, void* out, int out_dtype, hi
 hipError_t dequant(const qmv_weights& W, void* out, int out_dtype, hipStream_t s) {
   if (W.layout == QMV_LAYOUT_PLANES) {
     if (W.fmt == QMV_Q4_K) return dequant_fmt<kQ4KPlanes>(W, out, out_dtype, s);
+    if (W.fmt == QMV_Q5_K) return dequant_fmt<kQ5KPlanes>(W, out, out_dtype, s);
     if (W.fmt == QMV_Q6_K) return dequant_fmt<kQ6KPlanes>(W, out, out_dtype, s);
     return hipErrorInvalidValue;
   }

@@ -154,8 +154,49 @@ struct Q5KPolicy {
   }
 };
 
+// The same GEMV over the Q5_K plane layout of planes.h: lane mapping,
+// arithmetic and its order are Q5KPolicy's.  Lane (j, c) reads block j's
+// header and both qh halves from the H, QH0 and QH1 planes (plain loads: the
+// four lanes of a block share them) and its two code quarters from the QA
+// and QB planes, where one instruction of the wave reads 16 blocks x 64 bytes
+// = 1 KB of consecutive bytes that no other instruction reads (nontemporal
+// loads).
+struct Q5KPlanesPolicy : Q5KPolicy {
+  const uint8_t* hdr;
+  const uint8_t* qh0;
+  const uint8_t* qh1;
+  const uint8_t* qa;
+  const uint8_t* qb;
+  uint32_t nb;
+
+  __device__ Q5KPlanesPolicy(const uint8_t* w, uint64_t a, int cols, int kslot, int lane)
+      : Q5KPolicy(w, 0, cols, kslot, lane) {
+    nb = static_cast<uint32_t>(cols / 256);
+    const size_t jc = static_cast<size_t>(col0 / 256);  // this lane's block (clamped as in Q5KPolicy)
+    hdr = w + jc * 16;
+    qh0 = w + a + jc * 16;
+    qh1 = w + 2 * a + jc * 16;
+    qa = w + 3 * a + jc * 64 + 16 * c;
+    qb = w + 7 * a + jc * 64 + 16 * c;
+  }
+
+  __device__ void load(int row, Frag& f) const {
+    const size_t b = static_cast<size_t>(row) * nb;
+    f.hd = ld16(hdr + 16 * b);
+    f.h0 = ld16(qh0 + 16 * b);
+    f.h1 = ld16(qh1 + 16 * b);
+    f.qa = ld16_stream(qa + 64 * b);
+    f.qb = ld16_stream(qb + 64 * b);
+  }
+};
+
 hipError_t gemv_q5_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
   return launch_gemv<Q5KPolicy>(calls, n, x_dtype, batch, s);
+}
+
+hipError_t gemv_q5_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
+                            hipStream_t s) {
+  return launch_gemv<Q5KPlanesPolicy>(calls, n, x_dtype, batch, s);
 }
 
 }  // namespace qmv

@@ -24,10 +24,12 @@ constexpr int64_t kMaxBatch = 65535;
 
 hipError_t gemv_q8_0(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
 hipError_t gemv_q4_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
-// Q4_K / Q6_K weights in the plane layout (planes.h); every item in that layout.
+// Q4_K / Q5_K / Q6_K weights in the plane layout (planes.h); every item in that layout.
 hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t s);
 hipError_t gemv_q5_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
+hipError_t gemv_q5_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
+                            hipStream_t s);
 hipError_t gemv_q6_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
 hipError_t gemv_q6_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t s);
@@ -45,8 +47,9 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
 
 hipError_t dequant(const qmv_weights& W, void* out, int out_dtype, hipStream_t s);
 
-// Canonical Q4_K / Q6_K blocks -> plane layout (planes.h) at dst.
+// Canonical Q4_K / Q5_K / Q6_K blocks -> plane layout (planes.h) at dst.
 hipError_t repack_q4_k_planes(const qmv_weights& src, void* dst, hipStream_t s);
+hipError_t repack_q5_k_planes(const qmv_weights& src, void* dst, hipStream_t s);
 hipError_t repack_q6_k_planes(const qmv_weights& src, void* dst, hipStream_t s);
 
 int64_t probe_read_blocks(uint64_t nbytes);

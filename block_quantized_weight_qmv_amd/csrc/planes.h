@@ -1,4 +1,4 @@
-// Plane layouts of Q4_K and Q6_K weights ("decode-repacked" layouts, after hipEngine
+// Plane layouts of Q4_K, Q5_K and Q6_K weights ("decode-repacked" layouts, after hipEngine
 // 0.3.0, "GGUF Support": GGUF blocks are repacked into decode layouts on load
 // and the repacked copy replaces the source).
 //
@@ -30,6 +30,17 @@
 // The three 64-byte planes are read with nontemporal loads, 1 KB of
 // consecutive bytes per wave instruction; the sub-scales and d, whose lines
 // the next row's instructions share, with plain loads.
+//
+// Q5_K (176-byte blocks: d | dmin | scales[12] | qh[32] | qs[128]), same N,
+// b and a:
+//   H   plane at 0:     bytes 0..15 of block b (d, dmin, scales) at 16 b;
+//   QH0 plane at a:     qh[0 .. 16) of block b at a + 16 b;
+//   QH1 plane at 2 a:   qh[16 .. 32) of block b at 2 a + 16 b;
+//   QA  plane at 3 a:   qs[32c .. 32c+16) of block b at 3 a + 64 b + 16 c;
+//   QB  plane at 7 a:   qs[32c+16 .. 32c+32) of block b at 7 a + 64 b + 16 c;
+//   total 7 a + 64 N bytes (176 N plus under 1792 bytes of padding).
+// QA and QB are read with nontemporal loads; the header and qh planes, which
+// the four lanes of a block share, with plain loads.
 #pragma once
 
 #include <stdint.h>
@@ -45,6 +56,12 @@ __host__ __device__ inline Q4KPlanes q4k_planes(int64_t rows, int64_t cols) {
   const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 256);
   const uint64_t a = (16 * n + 255) / 256 * 256;
   return Q4KPlanes{a, 5 * a + 64 * n};
+}
+
+__host__ __device__ inline Q4KPlanes q5k_planes(int64_t rows, int64_t cols) {
+  const uint64_t n = static_cast<uint64_t>(rows) * static_cast<uint64_t>(cols / 256);
+  const uint64_t a = (16 * n + 255) / 256 * 256;
+  return Q4KPlanes{a, 7 * a + 64 * n};
 }
 
 __host__ __device__ inline Q4KPlanes q6k_planes(int64_t rows, int64_t cols) {

@@ -1,4 +1,4 @@
-// Repack of canonical Q4_K and Q6_K blocks into the plane layouts of
+// Repack of canonical Q4_K, Q5_K and Q6_K blocks into the plane layouts of
 // planes.h, on the device, once per weight tensor (hipEngine 0.3.0, "GGUF Support": the
 // decode repack happens at load time).  Q4_K: one thread per block, nine
 // 16-byte loads of the block, one 16-byte store to each plane slot.  Bytes are moved,
@@ -27,6 +27,40 @@ repack_q4_k_planes_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__
     qa[c] = v[1 + 2 * c];
     qb[c] = v[2 + 2 * c];
   }
+}
+
+// Q5_K: one thread per block, eleven 16-byte loads, one store per plane slot.
+__global__ void __launch_bounds__(256)
+repack_q5_k_planes_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst, int64_t nblocks,
+                          uint64_t a) {
+  const int64_t b = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  if (b >= nblocks) return;
+  const uint4* s = reinterpret_cast<const uint4*>(src + b * 176);
+  uint4 v[11];
+#pragma unroll
+  for (int i = 0; i < 11; ++i) v[i] = s[i];
+  reinterpret_cast<uint4*>(dst)[b] = v[0];                // header
+  reinterpret_cast<uint4*>(dst + a)[b] = v[1];            // qh[0 .. 16)
+  reinterpret_cast<uint4*>(dst + 2 * a)[b] = v[2];        // qh[16 .. 32)
+  uint4* qa = reinterpret_cast<uint4*>(dst + 3 * a + 64 * b);
+  uint4* qb = reinterpret_cast<uint4*>(dst + 7 * a + 64 * b);
+  // qs[32c .. 32c+16) is block chunk 3 + 2c, qs[32c+16 .. 32c+32) chunk 4 + 2c
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    qa[c] = v[3 + 2 * c];
+    qb[c] = v[4 + 2 * c];
+  }
+}
+
+hipError_t repack_q5_k_planes(const qmv_weights& src, void* dst, hipStream_t s) {
+  const int64_t nblocks = src.rows * (src.cols / 256);
+  const Q4KPlanes pl = q5k_planes(src.rows, src.cols);
+  const int64_t grid = (nblocks + 255) / 256;
+  if (grid > INT32_MAX) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(repack_q5_k_planes_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
+                     static_cast<const uint8_t*>(src.data), static_cast<uint8_t*>(dst), nblocks,
+                     pl.a);
+  return hipGetLastError();
 }
 
 // Q6_K: one thread per (2-byte aligned) block, read with unaligned 16-byte

@@ -73,7 +73,7 @@ enum { QMV_F32 = 0, QMV_F16 = 1, QMV_BF16 = 2 };
 
 /* Byte layouts of a weight tensor in device memory.
  *   QMV_LAYOUT_BLOCKS: the canonical blocks above, row-major.
- *   QMV_LAYOUT_PLANES (Q4_K and Q6_K): the same bytes rearranged for streaming,
+ *   QMV_LAYOUT_PLANES (Q4_K, Q5_K, Q6_K): the same bytes rearranged for streaming,
  *     a decode-repacked layout in the sense of hipEngine 0.3.0, "GGUF
  *     Support" (GGUF blocks repacked at load time into decode layouts that
  *     replace the source).  With N = rows*(cols/256) blocks, block
@@ -82,6 +82,9 @@ enum { QMV_F32 = 0, QMV_F16 = 1, QMV_BF16 = 2 };
  *       code plane A at a:   qs[32c .. 32c+16) of block b at a + 64*b + 16*c;
  *       code plane B at 5*a: qs[32c+16 .. 32c+32) of block b at
  *                            5*a + 64*b + 16*c   (c = 0..3);
+ *     Q5_K, same N, b and a: bytes 0..15 of block b at 16*b; qh[0 .. 16)
+ *       at a + 16*b; qh[16 .. 32) at 2*a + 16*b; qs[32c .. 32c+16) at
+ *       3*a + 64*b + 16*c; qs[32c+16 .. 32c+32) at 7*a + 64*b + 16*c.
  *     Q6_K, same N, b and a, with p = 2h + i (h, i in {0, 1}):
  *       ql[64h + 16i .. +16) of block b at 64*b + 16*p;
  *       ql[64h + 32 + 16i .. +16) at 4*a + 64*b + 16*p;
@@ -167,11 +170,11 @@ int32_t qmv_pack_int4_g128(const uint16_t* s_bits, const int8_t* q,
                            uint64_t out_bytes);
 
 /* Bytes of the QMV_LAYOUT_PLANES layout of a rows x cols tensor; 0 if the
- * format has no plane layout (Q8_0, Q5_K, INT4_G128) or the shape is
+ * format has no plane layout (Q8_0, INT4_G128) or the shape is
  * invalid. */
 uint64_t qmv_planes_size(int32_t fmt, int64_t rows, int64_t cols);
 
-/* Enqueue the repack of canonical Q4_K or Q6_K blocks (src, QMV_LAYOUT_BLOCKS) into
+/* Enqueue the repack of canonical Q4_K, Q5_K or Q6_K blocks (src, QMV_LAYOUT_BLOCKS) into
  * the plane layout at dst (device memory of dst_bytes >= qmv_planes_size
  * bytes, 16-byte aligned, 256 recommended, not overlapping src) and fill
  * *out with a QMV_LAYOUT_PLANES descriptor of dst.  Bytes are moved, not
@@ -200,8 +203,9 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * once for up to 16 activation rows, once per tile of 32, 64 or 128 rows
  * above; exact products, fp32 sums, results independent of timing);
  * otherwise each activation row is a GEMV over the packed weights.
- * Q4_K and Q6_K weights in QMV_LAYOUT_PLANES run the same GEMV arithmetic, in
- * the same order, as the canonical layout (results equal bit for bit); the
+ * Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the same GEMV
+ * arithmetic, in the same order, as the canonical layout (results equal bit
+ * for bit); the
  * matrix-core path takes the canonical layout only (QMV_ERR_UNSUPPORTED for
  * planes there). */
 int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,

@@ -153,7 +153,9 @@ def test_planes_sizes_and_repack_validation_errors():
     assert qmv.qmv_planes_size("q4_k", 18944, 3584) == 38_191_104  # 16 N is a multiple of 256 there
     assert qmv.qmv_planes_size("q6_k", 8, 512) == 13 * a + 2 * n_blocks
     assert qmv.qmv_planes_size("q6_k", 152064, 3584) == 447_068_160  # no padding at the lm-head shape
-    for f in ("q8_0", "int4_g128", "q5_k"):
+    assert qmv.qmv_planes_size("q5_k", 8, 512) == 7 * a + 64 * n_blocks
+    assert qmv.qmv_planes_size("q5_k", 3584, 18944) == 46_678_016  # no padding at the down shape
+    for f in ("q8_0", "int4_g128"):
         assert qmv.qmv_planes_size(f, 8, 512) == 0
     assert qmv.qmv_planes_size("q4_k", 8, 500) == 0
     src = _desc()
@@ -164,7 +166,7 @@ def test_planes_sizes_and_repack_validation_errors():
     _expect(-5, r, src, dst, need - 1)
     _expect(-4, r, src, dst + 8, need)
     _expect(-3, r, src, FAKE + 64, need)                    # overlaps the source
-    _expect(-6, r, _desc("q5_k", 8, 512), dst, need)        # no plane layout for Q5_K
+    _expect(-6, r, _desc("q8_0", 8, 512), dst, need)        # no plane layout for Q8_0
     bad = _desc()
     bad.nbytes += 1
     _expect(-5, r, bad, dst, need)

@@ -64,7 +64,8 @@ def test_default_layout():
     assert bench.default_layout(5, 1) == "planes"
     assert bench.default_layout(5, 4) == "blocks"       # matrix-core path
     assert bench.default_layout(4, None) == "planes"
-    for c in (1, 2, 6):
+    assert bench.default_layout(6, None) == "planes"
+    for c in (1, 2):
         assert bench.default_layout(c, None) == "blocks"
 
 

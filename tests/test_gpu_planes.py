@@ -1,12 +1,12 @@
-"""Q4_K and Q6_K in the plane layout (qmv_repack_planes) on the GPU.
+"""Q4_K, Q5_K and Q6_K in the plane layout (qmv_repack_planes) on the GPU.
 
 The repack only moves bytes, so dequantization from planes must equal the
 canonical layout's bit for bit (and the oracle's).  The plane GEMV runs the
 canonical GEMV's arithmetic in the same order with the same launch shape, so
 its outputs must equal the canonical layout's bitwise, and the oracle's
 within the 2e-3 normwise gate.  The full 7B decoder-layer shapes are checked
-in the launch grouping the benchmark times (q+k+v, o, gate+up, down), and
-the Q6_K lm-head at full size.
+in the launch grouping the benchmark times (q+k+v, o, gate+up, down), the
+Q6_K lm-head and the Q5_K down projection at full size.
 """
 import numpy as np
 import pytest
@@ -25,7 +25,7 @@ TOL = 2e-3
 SHAPES = [(1, 1), (3, 1), (5, 3), (67, 14), (33, 17), (9, 74), (40, 5)]
 
 
-FMTS = ["q4_k", "q6_k"]
+FMTS = ["q4_k", "q5_k", "q6_k"]
 
 
 def _planes(w: Weights, align_pad=0):
@@ -197,3 +197,24 @@ def test_full_size_q6_k_lm_head_in_planes_sampled_rows():
     assert np.all(err <= TOL)
     del w, p
     torch.cuda.empty_cache()
+
+
+def test_full_size_q5_k_down_in_planes_sampled_rows():
+    """The Q5_K down projection (3584 x 18944), repacked: every output equals
+    the canonical layout's, and sampled rows meet the gate."""
+    cfg = CONFIGS[6]
+    name, rows, cols = cfg["mats"][0]
+    say(f"planes full-size q5_k {name} {rows}x{cols}")
+    w = Weights("q5_k", rows, cols, seed=weight_seed(6, 0))
+    p = _planes(w)
+    x = gen_x(1, cols, "f32", x_seed(6, 0))
+    xd = to_dev_x(x, "f32")
+    yp = torch.empty(1, rows, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv("q5_k", p, xd, "f32", yp, rows, cols, 1)
+    yb = w.gemv(xd, "f32", 1)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, yb)
+    ids = _sample_rows(rows, seed=6)
+    err = oracle.normwise_rel_err(yp.cpu().numpy()[:, ids], oracle_y(w, x, "f32", ids))
+    say(f"  sampled normwise err {err.max():.3e}")
+    assert np.all(err <= TOL)
