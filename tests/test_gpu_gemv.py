@@ -193,3 +193,32 @@ def test_bf16_activation_range(fmt, layout, spread):
     err = _err(got, oracle_y(w, x, "bf16"))
     say(f"  normwise err {err.max():.3e}")
     assert np.all(err <= TOL), err
+
+
+# longest rows a GEMV launch accepts (16 waves along K): the 1024-thread
+# kernel, and a 10-wave split in between
+LONG = [("q8_0", 16 * 64 * 32), ("q4_k", 16 * 16 * 256), ("q5_k", 10 * 16 * 256),
+        ("q6_k", 16 * 16 * 256), ("int4_g128", 16 * 64 * 64)]
+
+
+@pytest.mark.parametrize("fmt,cols", LONG)
+@pytest.mark.parametrize("x_dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("layout", ["blocks", "planes"])
+def test_longest_rows(fmt, cols, x_dtype, layout):
+    if layout == "planes" and fmt not in ("q4_k", "q5_k", "q6_k"):
+        pytest.skip("no plane layout for this format")
+    rows = 37
+    say(f"longest rows {fmt} {rows}x{cols} x {x_dtype} {layout}")
+    w = Weights(fmt, rows, cols, seed=515)
+    desc = w.desc
+    if layout == "planes":
+        buf = torch.empty(qmv.qmv_planes_size(fmt, rows, cols), dtype=torch.uint8, device=DEV)
+        desc = qmv.qmv_repack_planes(w.desc, buf)
+    x = gen_x(1, cols, x_dtype, seed=516)
+    y = torch.full((1, rows), 5.0, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv(fmt, desc, to_dev_x(x, x_dtype), x_dtype, y, rows, cols, 1)
+    err = _err(y.cpu().numpy(), oracle_y(w, x, x_dtype))
+    say(f"  normwise err {err.max():.3e}")
+    assert np.all(err <= TOL), err
+    if layout == "planes":
+        assert torch.equal(y, w.gemv(to_dev_x(x, x_dtype), x_dtype, 1))
