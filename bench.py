@@ -359,8 +359,9 @@ def main() -> int:
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures a single GPU: this library has no multi-GPU path "
-              "(sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures a single GPU: this library has no multi-GPU path (over P GPUs "
+              "each would hold rows/P of every matrix, take the whole activation and all-gather "
+              "y). Run with --gpus 1.", file=sys.stderr)
         return 2
 
     import numpy as np
