@@ -120,6 +120,33 @@ uint64_t qmv_planes_size(int32_t fmt, int64_t rows, int64_t cols) {
                            : qmv::q6k_planes(rows, cols).total;
 }
 
+int32_t qmv_create_weights_planes(int32_t fmt, int64_t rows, int64_t cols, const void* dev_planes,
+                                  uint64_t nbytes, qmv_weights* out) {
+  if (!out) return fail(QMV_ERR_NULL, "output descriptor is NULL");
+  if (!dev_planes) return fail(QMV_ERR_NULL, "planes data pointer is NULL");
+  if (qmv_block_size(fmt) == 0) return fail(QMV_ERR_FORMAT, "unknown format %d", fmt);
+  if (fmt != QMV_Q4_K && fmt != QMV_Q5_K && fmt != QMV_Q6_K)
+    return fail(QMV_ERR_UNSUPPORTED, "format %d has no plane layout", fmt);
+  const uint64_t need = qmv_planes_size(fmt, rows, cols);
+  if (need == 0)
+    return fail(QMV_ERR_SHAPE, "bad shape %lld x %lld (cols must be a positive multiple of 256)",
+                (long long)rows, (long long)cols);
+  if (nbytes != need)
+    return fail(QMV_ERR_SIZE, "got %llu bytes, planes need %llu", (unsigned long long)nbytes,
+                (unsigned long long)need);
+  if (!qmv::aligned16(dev_planes)) return fail(QMV_ERR_ALIGN, "planes data not 16-byte aligned");
+  qmv_weights w;
+  w.fmt = fmt;
+  w.layout = QMV_LAYOUT_PLANES;
+  w.rows = rows;
+  w.cols = cols;
+  w.data = dev_planes;
+  w.nbytes = nbytes;
+  w.scales_offset = qmv::q4k_planes(rows, cols).a;  // the plane unit, the same for every format
+  *out = w;
+  return qmv::ok();
+}
+
 int32_t qmv_repack_planes(const qmv_weights* src, void* dst, uint64_t dst_bytes, qmv_weights* out,
                           void* stream) {
   if (!out) return fail(QMV_ERR_NULL, "output descriptor is NULL");

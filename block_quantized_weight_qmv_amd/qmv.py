@@ -60,6 +60,7 @@ _SIGS = {
     "qmv_pack_int4_g128": (_i32, [_p, _p, _i64, _i64, _p, _u64]),
     "qmv_create_weights": (_i32, [_i32, _i64, _i64, _p, _u64, ctypes.POINTER(QmvWeights)]),
     "qmv_planes_size": (_u64, [_i32, _i64, _i64]),
+    "qmv_create_weights_planes": (_i32, [_i32, _i64, _i64, _p, _u64, ctypes.POINTER(QmvWeights)]),
     "qmv_repack_planes": (_i32, [ctypes.POINTER(QmvWeights), _p, _u64, ctypes.POINTER(QmvWeights), _p]),
     "qmv_gemv": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
     "qmv_gemv_multi": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32, _p]),
@@ -221,6 +222,16 @@ def qmv_create_weights(fmt, rows: int, cols: int, dev_packed, nbytes: int | None
 
 def qmv_planes_size(fmt, rows: int, cols: int) -> int:
     return lib().qmv_planes_size(_fmt(fmt), rows, cols)
+
+
+def qmv_create_weights_planes(fmt, rows: int, cols: int, dev_planes, nbytes: int | None = None) -> QmvWeights:
+    """Descriptor for plane-layout bytes already in device memory (a uint8 tensor or a pointer)."""
+    if nbytes is None:
+        nbytes = dev_planes.numel() * dev_planes.element_size()
+    w = QmvWeights()
+    _check(lib().qmv_create_weights_planes(_fmt(fmt), rows, cols, _ptr(dev_planes), nbytes, ctypes.byref(w)))
+    w.owner = None if isinstance(dev_planes, int) else dev_planes
+    return w
 
 
 def qmv_repack_planes(src: QmvWeights, dst, dst_bytes: int | None = None, stream=None) -> QmvWeights:

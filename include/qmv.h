@@ -187,6 +187,15 @@ uint64_t qmv_planes_size(int32_t fmt, int64_t rows, int64_t cols);
 int32_t qmv_repack_planes(const qmv_weights* src, void* dst,
                           uint64_t dst_bytes, qmv_weights* out, void* stream);
 
+/* Descriptor for plane-layout bytes already in device memory (for example
+ * planes made by qmv_repack_planes earlier and kept): validates format,
+ * shape, size (nbytes == qmv_planes_size; QMV_ERR_SIZE) and alignment and
+ * fills *out with layout QMV_LAYOUT_PLANES.  No HIP call, no allocation; the
+ * bytes are not inspected. */
+int32_t qmv_create_weights_planes(int32_t fmt, int64_t rows, int64_t cols,
+                                  const void* dev_planes, uint64_t nbytes,
+                                  qmv_weights* out);
+
 /* Validate shape and size and fill *out.  No HIP call, no allocation.
  * dev_packed must be 16-byte aligned (QMV_ERR_ALIGN) and nbytes must equal
  * qmv_packed_size (QMV_ERR_SIZE). */

@@ -188,3 +188,21 @@ def test_planes_sizes_and_repack_validation_errors():
     _expect(-6, qmv.qmv_gemv_multi, "q4_k", "f32", 1, [(src, FAKE, FAKE), (p, FAKE, FAKE + 4096)])
     _expect(-6, g, "q4_k", p, FAKE, "bf16", FAKE, 8, 512, 4)  # matrix-core path: blocks only
     assert _desc().layout == 0
+
+
+def test_create_weights_planes():
+    """Wrapping kept plane bytes: the descriptor equals what qmv_repack_planes
+    would return, and every refusal comes before any HIP call."""
+    c = qmv.qmv_create_weights_planes
+    for fmt in ("q4_k", "q5_k", "q6_k"):
+        n = qmv.qmv_planes_size(fmt, 8, 512)
+        w = c(fmt, 8, 512, FAKE, n)
+        a = (16 * 16 + 255) // 256 * 256
+        assert (w.fmt, w.layout, w.rows, w.cols, w.nbytes, w.scales_offset) == (qmv.FMT[fmt], 1, 8, 512, n, a)
+    n = qmv.qmv_planes_size("q4_k", 8, 512)
+    _expect(-1, c, "q4_k", 8, 512, None, n)
+    _expect(-2, c, 9, 8, 512, FAKE, n)
+    _expect(-6, c, "q8_0", 8, 512, FAKE, n)
+    _expect(-3, c, "q4_k", 8, 500, FAKE, n)
+    _expect(-5, c, "q4_k", 8, 512, FAKE, n - 16)
+    _expect(-4, c, "q4_k", 8, 512, FAKE + 8, n)

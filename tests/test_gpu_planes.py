@@ -106,6 +106,22 @@ def test_planes_multi_matches_separate_calls(fmt):
         assert np.all(err <= TOL)
 
 
+@pytest.mark.parametrize("fmt", FMTS)
+def test_kept_planes_rewrapped(fmt):
+    """Planes copied to a new buffer and wrapped with qmv_create_weights_planes
+    compute what the repack's own descriptor computes, bitwise."""
+    w = Weights(fmt, 50, 20 * 256, seed=21)
+    p = _planes(w)
+    copy = p.keep[:p.nbytes].clone()
+    q = qmv.qmv_create_weights_planes(fmt, w.rows, w.cols, copy)
+    x = to_dev_x(gen_x(1, w.cols, "f32", seed=22), "f32")
+    ya = torch.empty(1, w.rows, dtype=torch.float32, device=DEV)
+    yb = torch.empty_like(ya)
+    qmv.qmv_gemv(fmt, p, x, "f32", ya, w.rows, w.cols, 1)
+    qmv.qmv_gemv(fmt, q, x, "f32", yb, w.rows, w.cols, 1)
+    assert torch.equal(ya, yb)
+
+
 def test_planes_graph_replay_equals_eager():
     w = Weights("q4_k", 300, 14 * 256, seed=12)
     p = _planes(w)
