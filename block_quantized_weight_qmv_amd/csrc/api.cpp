@@ -263,10 +263,6 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   // weights once per activation row).
   const bool planes = items[0].W->layout == QMV_LAYOUT_PLANES;
   if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
-    if (planes)
-      return fail(QMV_ERR_UNSUPPORTED,
-                  "the matrix-core path (bf16, batch >= %lld) takes the canonical block layout",
-                  (long long)qmv::kMfmaMinBatch);
     for (int i = 0; i < n && e == hipSuccess; ++i)
       e = qmv::gemm_q4_k_bf16(*calls[i].W, calls[i].x, calls[i].y, batch, s);
     return qmv::from_hip(e, "qmv_gemv (MFMA tiles) launch");

@@ -97,6 +97,29 @@ __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a 
 // partial tiles are added in wave order through LDS at the end (results do
 // not depend on timing).  W and X of the next block are in flight while the
 // current one is multiplied.
+// Where a lane finds Q4_K block `blk` (= row * blocks per row + block): its
+// 16-byte header, and its 8-byte piece qs[32 cc + 8 q .. +8) of code chunk
+// cc, in the canonical layout (PL = false: 144-byte blocks) or the plane
+// layout of planes.h (PL = true: header plane; qs[32cc .. 32cc+16) in code
+// plane A at a, qs[32cc+16 .. 32cc+32) in plane B at 5a, 64 bytes per block).
+template <bool PL>
+struct Q4KBlockAddr {
+  static constexpr size_t kH = PL ? 16 : 144;  // header stride per block
+  static constexpr size_t kQ = PL ? 64 : 144;  // code stride per block
+  static constexpr int kC = PL ? 16 : 32;      // code chunk stride
+  const uint8_t* hbase;
+  const uint8_t* qbase;
+  __device__ Q4KBlockAddr(const uint8_t* w, uint64_t a, int q) {
+    hbase = w;
+    if constexpr (PL)
+      qbase = w + (q < 2 ? a : 5 * a) + 8 * (q & 1);
+    else
+      qbase = w + 16 + 8 * q;
+  }
+  __device__ const uint8_t* hd(size_t blk) const { return hbase + blk * kH; }
+  __device__ const uint8_t* qs(size_t blk, int cc) const { return qbase + blk * kQ + cc * kC; }
+};
+
 template <int NB, int MB>
 struct KsRegs {
   uint4 hd[NB];       // block header of this lane's row, per row tile
@@ -104,9 +127,10 @@ struct KsRegs {
   uint4 x[MB][8];     // X[16 mb + lane % 16][32 s + 8 (lane / 16) .. +7], s = 0..7
 };
 
-template <int NB, int MB>
+template <int NB, int MB, bool PL>
 __global__ void __launch_bounds__(512)
-gemm_q4_k_bf16_ksplit(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M, int kw) {
+gemm_q4_k_bf16_ksplit(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M,
+                      int kw) {
   extern __shared__ float ks_part[];  // [kw][NB * MB * 4][64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -115,11 +139,10 @@ gemm_q4_k_bf16_ksplit(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   const int b0 = wave * nb / kw, b1 = (wave + 1) * nb / kw;  // kw <= nb: never empty
   const int n0 = static_cast<int>(blockIdx.x) * 16 * NB;
   const int m0 = static_cast<int>(blockIdx.y) * 16 * MB;
-  const size_t row_bytes = static_cast<size_t>(nb) * 144;
-  const uint8_t* wr[NB];
+  const Q4KBlockAddr<PL> wa(w, pa, q);
+  size_t wr[NB];  // first block of this lane's row, per row tile
 #pragma unroll
-  for (int t = 0; t < NB; ++t)
-    wr[t] = w + static_cast<size_t>(min(n0 + 16 * t + c, N - 1)) * row_bytes + 16 + 8 * q;
+  for (int t = 0; t < NB; ++t) wr[t] = static_cast<size_t>(min(n0 + 16 * t + c, N - 1)) * nb;
   const uint16_t* xr[MB];
 #pragma unroll
   for (int mb = 0; mb < MB; ++mb)
@@ -130,10 +153,10 @@ gemm_q4_k_bf16_ksplit(const uint8_t* w, int N, int K, const uint16_t* x, float* 
     const int bb = min(b, nb - 1);
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
-      const uint8_t* p = wr[t] + static_cast<size_t>(bb) * 144;
-      r.hd[t] = *reinterpret_cast<const uint4*>(p - 16 - 8 * q);
+      const size_t blk = wr[t] + bb;
+      r.hd[t] = *reinterpret_cast<const uint4*>(wa.hd(blk));
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) r.q[t][cc] = *reinterpret_cast<const uint2*>(p + 32 * cc);
+      for (int cc = 0; cc < 4; ++cc) r.q[t][cc] = *reinterpret_cast<const uint2*>(wa.qs(blk, cc));
     }
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb)
@@ -301,8 +324,9 @@ __host__ __device__ constexpr size_t stream_lds_bytes(int nb) {
          static_cast<size_t>(kStreamWaves) * 2 * 4 * 64 * 4;      // two partial tiles per wave
 }
 
+template <bool PL>
 __global__ void __launch_bounds__(64 * kStreamWaves)
-gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M) {
+gemm_q4_k_bf16_stream(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M) {
   extern __shared__ __attribute__((aligned(16))) uint8_t st_lds[];
   const int nb = K >> 8;
   // X operands: [nb][8 s][4 q][16 slots][16 B], batch row m of quarter q of
@@ -322,16 +346,15 @@ gemm_q4_k_bf16_stream(const uint8_t* w, int N, int K, const uint16_t* x, float* 
   const int nt = T / G + (g < T % G ? 1 : 0);
   const int U = nt * nb;
   const int u0 = wave * U / kStreamWaves, u1 = (wave + 1) * U / kStreamWaves;
-  const size_t row_bytes = static_cast<size_t>(nb) * 144;
+  const Q4KBlockAddr<PL> wa(w, pa, q);
 
   auto load = [&](int u, UnitRegs& r) {
     const int uu = min(u, max(u1 - 1, 0));   // clamped: in bounds, results unused
     const int tr = t0 + uu / nb, b = uu - (uu / nb) * nb;
-    const uint8_t* p = w + static_cast<size_t>(min(16 * tr + c, N - 1)) * row_bytes +
-                       static_cast<size_t>(b) * 144;
-    r.hd = *reinterpret_cast<const uint4*>(p);
+    const size_t blk = static_cast<size_t>(min(16 * tr + c, N - 1)) * nb + b;
+    r.hd = *reinterpret_cast<const uint4*>(wa.hd(blk));
 #pragma unroll
-    for (int cc = 0; cc < 4; ++cc) r.q[cc] = *reinterpret_cast<const uint2*>(p + 16 + 32 * cc + 8 * q);
+    for (int cc = 0; cc < 4; ++cc) r.q[cc] = *reinterpret_cast<const uint2*>(wa.qs(blk, cc));
   };
 
   // Row m of X is 32 nb chunks of 16 bytes; thread j reads chunk j of every
@@ -492,9 +515,9 @@ __host__ __device__ constexpr size_t tile_buf_bytes() {
   return static_cast<size_t>(MT) * 512 + static_cast<size_t>(MT / 16) * 1024;
 }
 
-template <int NB, int MB, int WM, int WN>
+template <int NB, int MB, int WM, int WN, bool PL>
 __global__ void __launch_bounds__(64 * WN * WM)
-gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y, int M) {
+gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M) {
   extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   constexpr int MT = 16 * MB * WM;             // batch rows of the workgroup
   constexpr int kThreads = 64 * WN * WM;
@@ -519,11 +542,10 @@ gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y,
   const bool active = wn * NB < nt;  // wave-uniform
   const int n0 = 16 * (t0 + wn * NB);
   const int mw0 = static_cast<int>(blockIdx.y) * MT;           // first batch row of the workgroup
-  const size_t row_bytes = static_cast<size_t>(nb) * 144;
-  const uint8_t* wr[NB];
+  const Q4KBlockAddr<PL> wa(w, pa, q);
+  size_t wr[NB];  // first block of this lane's row, per row tile
 #pragma unroll
-  for (int t = 0; t < NB; ++t)
-    wr[t] = w + static_cast<size_t>(min(n0 + 16 * t + c, N - 1)) * row_bytes;
+  for (int t = 0; t < NB; ++t) wr[t] = static_cast<size_t>(min(n0 + 16 * t + c, N - 1)) * nb;
 
   // Zero the fourth part group of both split-sum buffers once.
   for (int i = tid; i < 2 * (MT / 16) * 16; i += kThreads) {
@@ -536,10 +558,10 @@ gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y,
     const int bb = min(b, nb - 1);
 #pragma unroll
     for (int t = 0; t < NB; ++t) {
-      const uint8_t* p = wr[t] + static_cast<size_t>(bb) * 144;
-      r.hd[t] = *reinterpret_cast<const uint4*>(p);
+      const size_t blk = wr[t] + bb;
+      r.hd[t] = *reinterpret_cast<const uint4*>(wa.hd(blk));
 #pragma unroll
-      for (int cc = 0; cc < 4; ++cc) r.q[t][cc] = *reinterpret_cast<const uint2*>(p + 16 + 32 * cc + 8 * q);
+      for (int cc = 0; cc < 4; ++cc) r.q[t][cc] = *reinterpret_cast<const uint2*>(wa.qs(blk, cc));
     }
   };
   // Item i = tid + kThreads j: batch row i / 8 of the workgroup, sub-block
@@ -771,8 +793,10 @@ gemm_q4_k_bf16_tile(const uint8_t* w, int N, int K, const uint16_t* x, float* y,
       }
 }
 
-hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
-                          hipStream_t stream) {
+template <bool PL>
+static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, float* y, int64_t batch,
+                                        hipStream_t stream) {
+  const uint64_t pa = W.scales_offset;  // plane unit a (planes); 0 (canonical)
   const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols), M = static_cast<int>(batch);
   const uint8_t* w = static_cast<const uint8_t*>(W.data);
   const uint16_t* xb = static_cast<const uint16_t*>(x);
@@ -783,8 +807,8 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
     int G = device_cus();
     if (G > T) G = T;
     if (G < (T + 7) / 8) G = (T + 7) / 8;
-    hipLaunchKernelGGL(gemm_q4_k_bf16_stream, dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(nb),
-                       stream, w, N, K, xb, y, M);
+    hipLaunchKernelGGL(gemm_q4_k_bf16_stream<PL>, dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(nb),
+                       stream, w, pa, N, K, xb, y, M);
     return hipGetLastError();
   }
   if (M <= 16) {
@@ -795,8 +819,8 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
     kw = kw < 1 ? 1 : (kw > 8 ? 8 : kw);
     kw = kw > nb ? nb : kw;
     const size_t lds = static_cast<size_t>(kw) * 4 * 64 * sizeof(float);
-    hipLaunchKernelGGL((gemm_q4_k_bf16_ksplit<1, 1>), dim3(n_groups, 1), dim3(64 * kw), lds, stream,
-                       w, N, K, xb, y, M, kw);
+    hipLaunchKernelGGL((gemm_q4_k_bf16_ksplit<1, 1, PL>), dim3(n_groups, 1), dim3(64 * kw), lds, stream,
+                       w, pa, N, K, xb, y, M, kw);
     return hipGetLastError();
   }
   // 17 <= M: runs of 4-5 weight tiles, one workgroup per CU for each batch
@@ -807,16 +831,22 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
   if (G < (T + 4) / 5) G = (T + 4) / 5;
   if (M <= 64) {
     if (M <= 32)
-      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 1, 2, 5>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<32>(),
-                         stream, w, N, K, xb, y, M);
+      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 1, 2, 5, PL>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<32>(),
+                         stream, w, pa, N, K, xb, y, M);
     else
-      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 2, 2, 5>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<64>(),
-                         stream, w, N, K, xb, y, M);
+      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 2, 2, 5, PL>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<64>(),
+                         stream, w, pa, N, K, xb, y, M);
   } else {
-    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 4, 2, 5>), dim3(G, (M + 127) / 128), dim3(640),
-                       2 * tile_buf_bytes<128>(), stream, w, N, K, xb, y, M);
+    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 4, 2, 5, PL>), dim3(G, (M + 127) / 128), dim3(640),
+                       2 * tile_buf_bytes<128>(), stream, w, pa, N, K, xb, y, M);
   }
   return hipGetLastError();
+}
+
+hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
+                          hipStream_t stream) {
+  return W.layout == QMV_LAYOUT_PLANES ? gemm_q4_k_bf16_layout<true>(W, x, y, batch, stream)
+                                       : gemm_q4_k_bf16_layout<false>(W, x, y, batch, stream);
 }
 
 }  // namespace qmv

@@ -212,11 +212,9 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * once for up to 16 activation rows, once per tile of 32, 64 or 128 rows
  * above; exact products, fp32 sums, results independent of timing);
  * otherwise each activation row is a GEMV over the packed weights.
- * Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the same GEMV
- * arithmetic, in the same order, as the canonical layout (results equal bit
- * for bit); the
- * matrix-core path takes the canonical layout only (QMV_ERR_UNSUPPORTED for
- * planes there). */
+ * Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the same arithmetic,
+ * in the same order, as the canonical layout -- the GEMV and, for Q4_K x
+ * bf16 batches, the matrix-core path -- so results equal bit for bit. */
 int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,
                  int32_t x_dtype, float* y, int64_t rows, int64_t cols,
                  int64_t batch, void* stream);

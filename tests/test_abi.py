@@ -186,7 +186,6 @@ def test_planes_sizes_and_repack_validation_errors():
     q8.layout = 1
     _expect(-6, g, "q8_0", q8, FAKE, "f32", FAKE, 8, 512, 1)
     _expect(-6, qmv.qmv_gemv_multi, "q4_k", "f32", 1, [(src, FAKE, FAKE), (p, FAKE, FAKE + 4096)])
-    _expect(-6, g, "q4_k", p, FAKE, "bf16", FAKE, 8, 512, 4)  # matrix-core path: blocks only
     assert _desc().layout == 0
 
 

@@ -62,7 +62,7 @@ def test_named_kernel_exists_in_library(config, batch):
 def test_default_layout():
     assert bench.default_layout(3, None) == "planes"
     assert bench.default_layout(5, 1) == "planes"
-    assert bench.default_layout(5, 4) == "blocks"       # matrix-core path
+    assert bench.default_layout(5, 4) == "blocks"       # matrix cores: blocks stream faster
     assert bench.default_layout(4, None) == "planes"
     assert bench.default_layout(6, None) == "planes"
     for c in (1, 2):

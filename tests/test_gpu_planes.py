@@ -65,8 +65,7 @@ def test_repack_dequant_bit_exact(fmt, rows, nblk):
 @pytest.mark.parametrize("x_dtype", ["f32", "f16", "bf16"])
 def test_planes_gemv_equals_blocks_and_oracle(fmt, rows, nblk, x_dtype):
     cols = nblk * 256
-    # Q4_K x bf16 with batch >= 2 is the matrix-core path (canonical blocks only)
-    batch = 1 if (x_dtype == "bf16" and fmt == "q4_k") else (3 if rows < 40 else 1)
+    batch = 3 if rows < 40 else 1  # Q4_K x bf16 with batch >= 2: the matrix-core path
     say(f"planes gemv {fmt} {rows}x{cols} batch {batch} x {x_dtype}")
     w = Weights(fmt, rows, cols, seed=700 + rows + nblk)
     p = _planes(w)
@@ -143,14 +142,24 @@ def test_planes_graph_replay_equals_eager():
         assert torch.equal(y, eager), f"replay {rep} differs"
 
 
-def test_planes_refused_on_the_matrix_core_path():
-    w = Weights("q4_k", 16, 512, seed=1)
+@pytest.mark.parametrize("rows,nblk,batch", [(16, 2, 4), (70, 14, 16), (33, 20, 5),
+                                             (130, 3, 17), (67, 14, 64), (40, 5, 130)])
+def test_planes_on_the_matrix_core_path(rows, nblk, batch):
+    """Q4_K x bf16 batches (every batched kernel: stream, K split, tile) read
+    the plane layout with the canonical arithmetic: results equal bitwise."""
+    cols = nblk * 256
+    say(f"planes matrix cores {rows}x{cols} batch {batch}")
+    w = Weights("q4_k", rows, cols, seed=60 + rows)
     p = _planes(w)
-    x = to_dev_x(gen_x(4, 512, "bf16", seed=1), "bf16")
-    y = torch.empty(4, 16, dtype=torch.float32, device=DEV)
-    with pytest.raises(qmv.QmvError) as e:
-        qmv.qmv_gemv("q4_k", p, x, "bf16", y, 16, 512, 4)
-    assert e.value.status == -6
+    x = gen_x(batch, cols, "bf16", seed=61 + batch)
+    xd = to_dev_x(x, "bf16")
+    yp = torch.full((batch, rows), 3.0, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv("q4_k", p, xd, "bf16", yp, rows, cols, batch)
+    yb = w.gemv(xd, "bf16", batch)
+    torch.cuda.synchronize()
+    assert torch.equal(yp, yb)
+    err = oracle.normwise_rel_err(yp.cpu().numpy(), oracle_y(w, x, "bf16"))
+    assert np.all(err <= TOL), err
 
 
 def _sample_rows(rows, n=48, seed=0):
