@@ -354,6 +354,12 @@ inline int64_t resident_workgroups(K kernel, int block) {
 #endif
 constexpr int kMaxWavesPerSimd = QMV_WAVES_PER_SIMD;
 constexpr int kMinRowsPerWave = QMV_MIN_ROWS_PER_WAVE;
+// Launches long enough to give every wave at least this many rows at two
+// waves per SIMD run three: the ramp-up that more bytes in flight costs is
+// then small against the whole (measured on the 152064-row lm-head: 72.1-72.4
+// us against 73.2-73.3 us; on the 7B layer's launches, all far below, three
+// waves per SIMD was slower).
+constexpr int kLongRowsPerWave = 48;
 
 template <class P, typename XT, int R, int D, int MAXT, bool SX>
 hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream,
@@ -366,6 +372,8 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   for (int i = 0; i < n; ++i)
     wave_rows += calls[i].W->rows * ((calls[i].W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
   const int64_t resident = resident_workgroups(kernel, block) * waves;
+  if (waves_per_simd == 2 && wave_rows >= static_cast<int64_t>(cus) * 4 * 2 * kLongRowsPerWave)
+    waves_per_simd = 3;
   int64_t target = wave_rows / kMinRowsPerWave;
   if (target > static_cast<int64_t>(cus) * 4 * waves_per_simd)
     target = static_cast<int64_t>(cus) * 4 * waves_per_simd;
