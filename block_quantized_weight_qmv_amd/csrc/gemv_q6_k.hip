@@ -14,6 +14,10 @@
 //   q6 = (ql >> 4(g>>1)) & 0x0F0F0F0F  |  (qh shifted so bits 2g land on 4..5) & 0x30303030
 // and enter the FMAs two per dword as fp16 subnormals (device_util.h):
 //   partial = d sum_g sc_g (2^24 S_g - 32 X_g)
+// one v_fma_mix_f32 per weight for fp32 activations; fp16 and bf16 ones enter
+// as fp16 (bf16 scaled per lane by a power of two, exact; half_scale_exp),
+// two products per v_dot2_f32_f16 (exact: 6 + 11 significant bits), with
+// 2^(24+e) in place of 2^24.
 #include "gemv_skeleton.h"
 
 namespace qmv {
@@ -25,8 +29,13 @@ struct Q6KPolicy {
     float v[64];  // v[16g + t] = x[col0 + 32g + t]
     float s[4];
   };
+  struct XSliceHalf {
+    h2_t h[32];  // h[8g + 2k + p]: pair p of dword k of group g: (4k, 4k+2), (4k+1, 4k+3)
+    float s[4];  // fp32 sums of each group's 16 activations
+    float xs;    // 2^(24 + e)
+  };
   template <typename XT>
-  using XSliceT = XSlice;  // fp32 activations for every activation type
+  using XSliceT = typename XSliceFor<XT, XSlice, XSliceHalf>::type;
   struct Frag {
     uint4 la, lb, qh;
     uint2 sc;
@@ -59,16 +68,31 @@ struct Q6KPolicy {
   }
 
   template <typename XT>
-  __device__ void finish_x(const uint4* raw, XSlice& s) const {
-    x_to_f32<64>(raw, s.v, static_cast<const XT*>(nullptr));
+  __device__ void finish_x(const uint4* raw, XSliceT<XT>& s) const {
+    float v[64];  // v[16g + t] = x[col0 + 32g + t]
+    float* dst = v;
+    if constexpr (__is_same(XT, float)) dst = s.v;
+    x_to_f32<64>(raw, dst, static_cast<const XT*>(nullptr));
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
       s.s[g] = 0.f;
 #pragma unroll
       for (int t = 0; t < 16; ++t) {
-        s.v[16 * g + t] = ok ? s.v[16 * g + t] : 0.f;
-        s.s[g] += s.v[16 * g + t];
+        dst[16 * g + t] = ok ? dst[16 * g + t] : 0.f;
+        s.s[g] += dst[16 * g + t];
       }
+    }
+    if constexpr (!__is_same(XT, float)) {
+      const int e = half_scale_exp<XT, 64>(v);
+      s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float* x = v + 16 * g + 4 * k;
+          s.h[8 * g + 2 * k] = h2_t{scaled_f16(x[0], e), scaled_f16(x[2], e)};
+          s.h[8 * g + 2 * k + 1] = h2_t{scaled_f16(x[1], e), scaled_f16(x[3], e)};
+        }
     }
   }
 
@@ -82,7 +106,7 @@ struct Q6KPolicy {
   }
 
   template <typename XT>
-  __device__ float dot(const Frag& f, const XSlice& s) const {
+  __device__ float dot(const Frag& f, const XSliceT<XT>& s) const {
     const uint32_t la[4] = {f.la.x, f.la.y, f.la.z, f.la.w};
     const uint32_t lb[4] = {f.lb.x, f.lb.y, f.lb.z, f.lb.w};
     const uint32_t qh[4] = {f.qh.x, f.qh.y, f.qh.z, f.qh.w};
@@ -97,11 +121,16 @@ struct Q6KPolicy {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const uint32_t a = q6[g] & 0x003F003Fu, b = (q6[g] >> 8) & 0x003F003Fu;  // l 0,2 | 1,3
-        const float* x = s.v + 16 * g + 4 * k;
-        acc[g] = fma_lo(a, x[0], acc[g]);
-        acc[g] = fma_lo(b, x[1], acc[g]);
-        acc[g] = fma_hi(a, x[2], acc[g]);
-        acc[g] = fma_hi(b, x[3], acc[g]);
+        if constexpr (__is_same(XT, float)) {
+          const float* x = s.v + 16 * g + 4 * k;
+          acc[g] = fma_lo(a, x[0], acc[g]);
+          acc[g] = fma_lo(b, x[1], acc[g]);
+          acc[g] = fma_hi(a, x[2], acc[g]);
+          acc[g] = fma_hi(b, x[3], acc[g]);
+        } else {
+          acc[g] = dot2_lo_hi(a, s.h[8 * g + 2 * k], acc[g]);
+          acc[g] = dot2_lo_hi(b, s.h[8 * g + 2 * k + 1], acc[g]);
+        }
       }
     }
     // sub-scale of g is sc[8h + 2g + i] = byte (2g + i) of the 8 loaded scales
@@ -110,7 +139,12 @@ struct Q6KPolicy {
     for (int g = 0; g < 4; ++g) {
       const uint32_t word = g < 2 ? f.sc.x : f.sc.y;
       const int sc = static_cast<int8_t>((word >> (8 * (2 * (g & 1) + i))) & 0xFFu);
-      t = fmaf(static_cast<float>(sc), fmaf(kTwo24, acc[g], -32.f * s.s[g]), t);
+      float xs;
+      if constexpr (__is_same(XT, float))
+        xs = kTwo24;
+      else
+        xs = s.xs;
+      t = fmaf(static_cast<float>(sc), fmaf(xs, acc[g], -32.f * s.s[g]), t);
     }
     return f16_to_f32(f.d) * t;
   }

@@ -9,6 +9,10 @@
 // (2048 columns).  Codes are made unsigned by flipping bit 7 of every byte
 // (u = q + 128 < 1024) and enter the FMAs as fp16 subnormals (device_util.h):
 //   partial = d (2^24 sum u x 2^-24 - 128 X),  X = sum of the lane's activations
+// one v_fma_mix_f32 per weight for fp32 activations; fp16 and bf16 ones enter
+// as fp16 (bf16 scaled per lane by a power of two, exact; half_scale_exp),
+// two products per v_dot2_f32_f16 (exact: 8 + 11 significant bits), with
+// 2^(24+e) in place of 2^24.
 #include "gemv_skeleton.h"
 
 namespace qmv {
@@ -20,8 +24,13 @@ struct Q80Policy {
     float v[32];
     float s;
   };
+  struct XSliceHalf {
+    h2_t h[16];  // h[2i + p]: pair p of dword i: (4i, 4i+2), (4i+1, 4i+3)
+    float s;     // fp32 sum of the lane's 32 activations
+    float xs;    // 2^(24 + e)
+  };
   template <typename XT>
-  using XSliceT = XSlice;  // fp32 activations for every activation type
+  using XSliceT = typename XSliceFor<XT, XSlice, XSliceHalf>::type;
   struct Frag {
     uint4 qa, qb;
     uint32_t d;
@@ -48,13 +57,25 @@ struct Q80Policy {
   }
 
   template <typename XT>
-  __device__ void finish_x(const uint4* raw, XSlice& s) const {
-    x_to_f32<32>(raw, s.v, static_cast<const XT*>(nullptr));
+  __device__ void finish_x(const uint4* raw, XSliceT<XT>& s) const {
+    float v[32];
+    float* dst = v;
+    if constexpr (__is_same(XT, float)) dst = s.v;
+    x_to_f32<32>(raw, dst, static_cast<const XT*>(nullptr));
     s.s = 0.f;
 #pragma unroll
     for (int i = 0; i < 32; ++i) {
-      s.v[i] = ok ? s.v[i] : 0.f;
-      s.s += s.v[i];
+      dst[i] = ok ? dst[i] : 0.f;
+      s.s += dst[i];
+    }
+    if constexpr (!__is_same(XT, float)) {
+      const int e = half_scale_exp<XT, 32>(v);
+      s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        s.h[2 * i] = h2_t{scaled_f16(v[4 * i], e), scaled_f16(v[4 * i + 2], e)};
+        s.h[2 * i + 1] = h2_t{scaled_f16(v[4 * i + 1], e), scaled_f16(v[4 * i + 3], e)};
+      }
     }
   }
 
@@ -66,19 +87,29 @@ struct Q80Policy {
   }
 
   template <typename XT>
-  __device__ float dot(const Frag& f, const XSlice& s) const {
+  __device__ float dot(const Frag& f, const XSliceT<XT>& s) const {
     const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
     float acc = 0.f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const uint32_t u = q[i] ^ 0x80808080u;
       const uint32_t a = u & 0x00FF00FFu, b = (u >> 8) & 0x00FF00FFu;  // codes 0,2 | 1,3
-      acc = fma_lo(a, s.v[4 * i + 0], acc);
-      acc = fma_lo(b, s.v[4 * i + 1], acc);
-      acc = fma_hi(a, s.v[4 * i + 2], acc);
-      acc = fma_hi(b, s.v[4 * i + 3], acc);
+      if constexpr (__is_same(XT, float)) {
+        acc = fma_lo(a, s.v[4 * i + 0], acc);
+        acc = fma_lo(b, s.v[4 * i + 1], acc);
+        acc = fma_hi(a, s.v[4 * i + 2], acc);
+        acc = fma_hi(b, s.v[4 * i + 3], acc);
+      } else {
+        acc = dot2_lo_hi(a, s.h[2 * i], acc);
+        acc = dot2_lo_hi(b, s.h[2 * i + 1], acc);
+      }
     }
-    return f16_to_f32(f.d) * fmaf(kTwo24, acc, -128.f * s.s);
+    float xs;
+    if constexpr (__is_same(XT, float))
+      xs = kTwo24;
+    else
+      xs = s.xs;
+    return f16_to_f32(f.d) * fmaf(xs, acc, -128.f * s.s);
   }
 };
 

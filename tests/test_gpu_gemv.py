@@ -163,13 +163,14 @@ def test_full_size_configs_sampled_rows(config):
 
 
 @pytest.mark.parametrize("fmt,layout", [("q4_k", "blocks"), ("q4_k", "planes"), ("q5_k", "blocks"),
-                                        ("int4_g128", "blocks")])
+                                        ("int4_g128", "blocks"), ("q8_0", "blocks"),
+                                        ("q6_k", "blocks"), ("q6_k", "planes")])
 @pytest.mark.parametrize("spread", ["wide", "large", "tiny"])
 def test_bf16_activation_range(fmt, layout, spread):
-    """Q4_K, Q5_K and INT4 take bf16 activations as fp16 after scaling each
-    lane's activations by a power of two of their own: magnitudes far outside
-    fp16's range (and a spread of twelve decades within one row) must still
-    meet the gate."""
+    """Every format takes bf16 activations as fp16 after scaling each lane's
+    activations by a power of two of their own: magnitudes far outside fp16's
+    range (and a spread of twelve decades within one row) must still meet the
+    gate."""
     rows, cols = 96, 17 * 256
     w = Weights(fmt, rows, cols, seed=808)
     g = np.random.Generator(np.random.PCG64({"wide": 1, "large": 2, "tiny": 3}[spread]))
