@@ -106,6 +106,32 @@ def test_planes_multi_matches_separate_calls(fmt):
 
 
 @pytest.mark.parametrize("fmt", FMTS)
+def test_planes_multi_mixed_widths(fmt):
+    """One launch over plane-layout matrices of different widths (one wave's
+    K slice, two and five waves along K), each with its own activation:
+    bitwise equal to the canonical layout's launch, within the gate."""
+    items = [(67, 14), (16, 17), (33, 74), (5, 3)]
+    ws, ps, xs_np, xs, yp, yb = [], [], [], [], [], []
+    for i, (rows, nblk) in enumerate(items):
+        w = Weights(fmt, rows, nblk * 256, seed=1300 + i)
+        ws.append(w)
+        ps.append(_planes(w))
+        x = gen_x(1, nblk * 256, "f32", seed=1400 + i)
+        xs_np.append(x)
+        xs.append(to_dev_x(x, "f32"))
+        yp.append(torch.full((1, rows), -4.0, dtype=torch.float32, device=DEV))
+        yb.append(torch.full((1, rows), -4.0, dtype=torch.float32, device=DEV))
+    say(f"planes multi mixed widths {fmt}: " + ", ".join(f"{w.rows}x{w.cols}" for w in ws))
+    qmv.qmv_gemv_multi(fmt, "f32", 1, [(p, x, y) for p, x, y in zip(ps, xs, yp)])
+    qmv.qmv_gemv_multi(fmt, "f32", 1, [(w.desc, x, y) for w, x, y in zip(ws, xs, yb)])
+    torch.cuda.synchronize()
+    for w, x, a, b in zip(ws, xs_np, yp, yb):
+        assert torch.equal(a, b), (w.rows, w.cols)
+        err = oracle.normwise_rel_err(a.cpu().numpy(), oracle_y(w, x, "f32"))
+        assert np.all(err <= TOL), (w.rows, w.cols, err.max())
+
+
+@pytest.mark.parametrize("fmt", FMTS)
 def test_kept_planes_rewrapped(fmt):
     """Planes copied to a new buffer and wrapped with qmv_create_weights_planes
     compute what the repack's own descriptor computes, bitwise."""
