@@ -159,8 +159,14 @@ def cpu_baseline(mats, fmt, x_dtype, fields_list, xs, seconds):
         done_bytes += data.size + cols * xb + len(ids) * 4
         rows_done += len(ids)
         it += 1
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
     return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": cpu_model, "affinity_cores": len(os.sched_getaffinity(0)),
             "sample": (f"{rows_done} rows in {chunk}-row chunks cycling over the workload's "
                        f"matrices, {spent:.1f} s; numpy float64 decode (1 thread) + float64 "
                        f"matrix-vector product (BLAS, {blas_threads} threads); packing excluded")}
@@ -553,6 +559,7 @@ def main() -> int:
         "per_kernel": detail,
         "per_launch": per_launch,
         "read_ceiling_GBps": round(read_ceiling, 1),
+        "pct_of_read_ceiling": round(100 * value / read_ceiling, 1),
         "roofline": {"bound": dom_bound, "achieved": round(achieved, 1), "peak": peak,
                      "unit": unit, "frac": round(achieved / peak, 4),
                      "traffic": measured_traffic(dom, workload),
