@@ -42,6 +42,7 @@ CSRC = os.path.join(ROOT, "block_quantized_weight_qmv_amd", "csrc")
 # committed counter figures for that family (and only for it).
 _KERNEL_SOURCES = {
     "gemv_kernel": ["gemv_skeleton.h", "device_util.h"],
+    "gemv_rows_kernel": ["gemv_skeleton.h", "device_util.h"],
     "gemm_q4_k_bf16_stream": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_bf16_ksplit": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_bf16_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
@@ -70,10 +71,18 @@ def kernel_source_hash(kernel: str) -> str:
 def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str = "blocks") -> str:
     """Instantiation the library launches for matrices of these widths in one
     launch (mirrors the dispatch in api.cpp and the GEMV launcher: Q4_K x bf16
-    with batch >= 2 -> one of the matrix-core kernels, chosen by batch and by
+    with batch >= 2 not taken by the multi-row GEMV (below) -> one of the
+    matrix-core kernels, chosen by batch and by
     whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
     split), and the shared-activation kernel when no matrix splits K; Q4_K
-    weights in the plane layout take the plane policy))."""
+    weights in the plane layout take the plane policy; Q4_K x fp16 with two or
+    more rows, or x bf16 with 2-4 rows, against matrices of at most 4096
+    columns -> the multi-row GEMV)."""
+    if (fmt == "q4_k" and max(cols_list) <= 4096 and batch >= 2
+            and (x_dtype == "f16" or (x_dtype == "bf16" and batch <= 4))):
+        pol = "Q4KPlanesPolicy" if layout == "planes" else "Q4KPolicy"
+        xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
+        return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, {'2, 2, 256, 2' if batch == 2 else '1, 3, 256, 4'}>"
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:
         nb = max(cols_list) // 256
         pl = "true" if layout == "planes" else "false"
@@ -184,7 +193,7 @@ def default_layout(config: int, batch: int | None = None) -> str:
     from synth import CONFIGS
     cfg = CONFIGS[config]
     b = batch or cfg["batch"][0]
-    gemv = not (cfg["x_dtype"] == "bf16" and b >= 2)
+    gemv = not (cfg["x_dtype"] == "bf16" and b >= 5)  # batches of 2-4: the multi-row GEMV
     return "planes" if cfg["fmt"] in ("q4_k", "q5_k", "q6_k") and gemv else "blocks"
 
 

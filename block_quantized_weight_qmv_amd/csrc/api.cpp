@@ -262,6 +262,33 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   // matrix-core kernel, one launch per matrix (the GEMV path would read the
   // weights once per activation row).
   const bool planes = items[0].W->layout == QMV_LAYOUT_PLANES;
+  // Q4_K with two or more fp16 rows, or 2..kRowsMaxBf16Batch bf16 rows: the
+  // matrices of at most 4096 columns take the multi-row GEMV (one launch, one
+  // pass over the weights per two or four activation rows), the wider ones
+  // the kernel their own call would take, so that every item's result is the
+  // same as that of the item called alone.
+  if (fmt == QMV_Q4_K && batch >= 2 &&
+      (x_dtype == QMV_F16 || (x_dtype == QMV_BF16 && batch <= qmv::kRowsMaxBf16Batch))) {
+    qmv::GemvCall narrow[qmv::kMaxItems], wide[qmv::kMaxItems];
+    int nn = 0, nw = 0;
+    for (int i = 0; i < n; ++i) {
+      if (calls[i].W->cols <= 4096)
+        narrow[nn++] = calls[i];
+      else
+        wide[nw++] = calls[i];
+    }
+    if (nn) e = qmv::gemv_q4_k_rows(narrow, nn, x_dtype, batch, planes, s);
+    if (e == hipSuccess && nw) {
+      if (x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
+        for (int i = 0; i < nw && e == hipSuccess; ++i)
+          e = qmv::gemm_q4_k_bf16(*wide[i].W, wide[i].x, wide[i].y, batch, s);
+      } else {
+        e = planes ? qmv::gemv_q4_k_planes(wide, nw, x_dtype, batch, s)
+                   : qmv::gemv_q4_k(wide, nw, x_dtype, batch, s);
+      }
+    }
+    return qmv::from_hip(e, "qmv_gemv (multi-row) launch");
+  }
   if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
     for (int i = 0; i < n && e == hipSuccess; ++i)
       e = qmv::gemm_q4_k_bf16(*calls[i].W, calls[i].x, calls[i].y, batch, s);

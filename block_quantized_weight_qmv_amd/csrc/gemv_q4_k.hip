@@ -140,6 +140,44 @@ struct Q4KPolicy {
     const float mm = fmaf(cvt_ubyte<1>(mn), s.s1, cvt_ubyte<0>(mn) * s.s0);
     return fmaf(d, t, -dmin * mm);
   }
+
+  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the header decode
+  // and the code masks are computed once, then each row's sums follow dot's
+  // operations in dot's order, so out[m] equals dot(f, s[m]) bit for bit.
+  template <typename XT, int NBR>
+  __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
+    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
+    const uint32_t t1 = f.hd.y >> sh, t2 = f.hd.z >> sh, t3 = f.hd.w >> sh;
+    const uint32_t sc = ((hi ? t3 : t1) & mask_a) | ((t1 >> 2) & mask_b);
+    const uint32_t mn = ((hi ? (t3 >> 4) : t2) & mask_a) | ((t2 >> 2) & mask_b);
+    const float dmin = f16_to_f32(f.hd.x >> 16);
+    const float d16 = f16_to_f32(f.hd.x & 0xFFFFu);
+
+    const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
+    float s0[NBR], s1[NBR];
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) s0[m] = s1[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w0 = q[i], w8 = q[i] >> 8;
+      const uint32_t a = w0 & 0x000F000Fu, b = w8 & 0x000F000Fu;
+      const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;
+#pragma unroll
+      for (int m = 0; m < NBR; ++m) {
+        s0[m] = dot2_lo_hi(a, s[m].h[4 * i + 0], s0[m]);
+        s0[m] = dot2_lo_hi(b, s[m].h[4 * i + 1], s0[m]);
+        s1[m] = dot2_lo_hi(e, s[m].h[4 * i + 2], s1[m]);
+        s1[m] = dot2_lo_hi(g, s[m].h[4 * i + 3], s1[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) {
+      const float d = d16 * s[m].xs;
+      const float t = fmaf(cvt_ubyte<1>(sc) * 0.0625f, s1[m], cvt_ubyte<0>(sc) * s0[m]);
+      const float mm = fmaf(cvt_ubyte<1>(mn), s[m].s1, cvt_ubyte<0>(mn) * s[m].s0);
+      out[m] = fmaf(d, t, -dmin * mm);
+    }
+  }
 };
 
 // The same GEMV over the plane layout of planes.h: the lane mapping, the
@@ -181,6 +219,12 @@ hipError_t gemv_q4_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, h
 hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t s) {
   return launch_gemv<Q4KPlanesPolicy>(calls, n, x_dtype, batch, s);
+}
+
+hipError_t gemv_q4_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,
+                          hipStream_t s) {
+  return planes ? launch_gemv_rows<Q4KPlanesPolicy>(calls, n, x_dtype, batch, s)
+                : launch_gemv_rows<Q4KPolicy>(calls, n, x_dtype, batch, s);
 }
 
 }  // namespace qmv

@@ -259,6 +259,103 @@ gemv_kernel(const GemvLaunch args) {
   }
 }
 
+// Small activation batches (2-4 rows) against one wave's K slice: the work
+// split and tile pipeline of the shared-activation gemv_kernel, but each wave
+// carries NBR activation rows, so W is read once for all of them instead of
+// once per row.  All waves of a workgroup need the same NBR activation slices
+// (every matrix fits one wave's K slice): wave m < NBR reads row m from global
+// memory, converts it and leaves each lane's slice in LDS (word k of lane l at
+// [m][k][l]); after a barrier every wave reads all NBR slices.
+// P::dot_rows<XT, NBR> gives a row tile's NBR partials, sharing the block
+// decode, and the R x NBR partials (at most 4) are reduced together.  Grid y
+// covers the batch in steps of NBR (rows past the batch re-read the last row
+// and are not stored).
+template <class P, typename XT, int R, int D, int MAXT, int NBR>
+__global__ void __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(2)))
+gemv_rows_kernel(const GemvLaunch args, int batch) {
+  static_assert(R * NBR <= 4, "reduce_rows handles at most four partials");
+  static_assert(NBR <= MAXT / 64, "one converting wave per activation row");
+  typedef typename P::template XSliceT<XT> XS;
+  static_assert(sizeof(XS) % 4 == 0, "slices move through LDS as 32-bit words");
+  constexpr int kWords = static_cast<int>(sizeof(XS) / 4);
+  int it = 0;
+#pragma unroll 1
+  for (int k = 1; k < args.n; ++k)
+    if (static_cast<int>(blockIdx.x) >= args.item[k].wg_begin) it = k;
+  const GemvItem& m = args.item[it];
+
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int set = (blockIdx.x - m.wg_begin) * m.sets_per_wg + wave;
+  const int mb0 = static_cast<int>(blockIdx.y) * NBR;  // first activation row
+  int r_begin = set * m.q + R * min(set, m.rem);
+  int r_end = min(r_begin + m.q + (set < m.rem ? R : 0), m.rows);
+  if (set >= m.nsets) r_begin = r_end = m.rows;  // slices only; tile loads clamp to the last row
+  const int r_last = r_end - 1;
+
+  extern __shared__ float part_lds[];
+  uint32_t* slices = reinterpret_cast<uint32_t*>(part_lds);
+  const P pol(m.w, m.scales_offset, m.cols, 0, lane);
+  typename P::Frag f[D][R];
+
+  // Issue order: the converting wave's x slice, tile 0, tile 1.
+  const bool conv = wave < NBR;
+  uint4 raw[P::kXElems * sizeof(XT) / 16];
+  if (conv) {
+    const XT* xr = static_cast<const XT*>(m.x) + static_cast<size_t>(min(mb0 + wave, batch - 1)) * m.cols;
+    pol.load_x_raw(XGlobal<XT>{xr}, raw);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  if (conv) {
+    XS own;
+    pol.template finish_x<XT>(raw, own);
+    uint32_t w[kWords];
+    __builtin_memcpy(w, &own, sizeof(XS));
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) slices[(wave * kWords + k) * 64 + lane] = w[k];
+  }
+  lds_barrier();
+  XS xs[NBR];
+#pragma unroll
+  for (int mi = 0; mi < NBR; ++mi) {
+    uint32_t w[kWords];
+#pragma unroll
+    for (int k = 0; k < kWords; ++k) w[k] = slices[(mi * kWords + k) * 64 + lane];
+    __builtin_memcpy(&xs[mi], w, sizeof(XS));
+  }
+
+  auto finish = [&](const typename P::Frag* fr, int row0) {
+    float acc[R * NBR];
+#pragma unroll
+    for (int r = 0; r < R; ++r) pol.template dot_rows<XT, NBR>(fr[r], xs, acc + r * NBR);
+    const float t = reduce_rows<R * NBR>(acc, lane);
+    const int r = lane / NBR, mi = lane - (lane / NBR) * NBR;
+    if (lane < R * NBR && row0 + r < r_end && mb0 + mi < batch)
+      m.y[static_cast<size_t>(mb0 + mi) * m.rows + row0 + r] = t;
+  };
+  // Single-exit tile loop with pinned prefetches, as in gemv_kernel.
+  const int ntiles = (r_end - r_begin + R - 1) / R;
+  int r0 = r_begin;
+#pragma unroll 1
+  for (int t = D; t < ntiles; t += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      finish(f[j], r0 + j * R);
+      load_tile<P, R>(pol, f[j], r0 + (j + D) * R, r_last);
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    r0 += D * R;
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (r0 + j * R < r_end) finish(f[j], r0 + j * R);
+}
+
 // Rows of a K-split set are capped so that the partial sums of a workgroup
 // (waves x rows floats) stay within 16 waves x kMaxPartStride x 4 bytes.
 constexpr int kMaxPartStride = 256;
@@ -395,6 +492,61 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(block), lds, stream,
                      L);
   return hipGetLastError();
+}
+
+// Tiles in flight per wave of gemv_rows_kernel: two with two activation rows
+// (R = 2), three with four (R = 1).  (Measured on the 18944 x 3584 FFN shape:
+// deeper pipelines were slower at both sizes, two tiles of four rows 0.3 us
+// slower.)
+template <int NBR>
+constexpr int rows_tiles_in_flight() { return NBR == 4 ? 3 : 2; }
+
+// Launch of gemv_rows_kernel: every matrix within one wave's K slice, NBR
+// activation rows per wave (R rows per tile, R x NBR <= 4), four-wave
+// workgroups, the launch shape of the shared-activation GEMV.
+template <class P, typename XT, int R, int NBR>
+hipError_t launch_rows(const GemvCall* calls, int n, int64_t batch, hipStream_t stream) {
+  constexpr int kWaves = 4;
+  auto kernel = gemv_rows_kernel<P, XT, R, rows_tiles_in_flight<NBR>(), 64 * kWaves, NBR>;
+  const int cus = device_cus();
+  int64_t wave_rows = 0;
+  for (int i = 0; i < n; ++i) {
+    if (calls[i].W->cols > P::kColsPerWave) return hipErrorInvalidValue;
+    wave_rows += calls[i].W->rows;
+  }
+  const int64_t resident = resident_workgroups(kernel, 64 * kWaves) * kWaves;
+  int64_t target = wave_rows / kMinRowsPerWave;
+  if (target > static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd) target = static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd;
+  if (target < static_cast<int64_t>(cus) * 4) target = static_cast<int64_t>(cus) * 4;
+  int64_t per_cu = target / (static_cast<int64_t>(cus) * kWaves);
+  if (per_cu < 1) per_cu = 1;
+  target = per_cu * cus * kWaves;
+  if (target > resident) target = resident;
+  GemvLaunch L;
+  const int grid = plan_gemv<P, R>(calls, n, kWaves, target, &L);
+  const size_t lds = static_cast<size_t>(NBR) * sizeof(typename P::template XSliceT<XT>) * 64;
+  hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>((batch + NBR - 1) / NBR)),
+                     dim3(64 * kWaves), lds, stream, L, static_cast<int>(batch));
+  return hipGetLastError();
+}
+
+// Batches of two or more fp16 or bf16 activation rows against matrices no
+// wider than one wave's K slice: two rows in one pass over W, otherwise
+// groups of four rows, one pass over W per group.
+template <class P>
+hipError_t launch_gemv_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch,
+                            hipStream_t stream) {
+  if (batch < 2) return hipErrorInvalidValue;
+  const bool two = batch == 2;
+  switch (x_dtype) {
+    case QMV_F16:
+      return two ? launch_rows<P, _Float16, 2, 2>(calls, n, batch, stream)
+                 : launch_rows<P, _Float16, 1, 4>(calls, n, batch, stream);
+    case QMV_BF16:
+      return two ? launch_rows<P, bf16_t, 2, 2>(calls, n, batch, stream)
+                 : launch_rows<P, bf16_t, 1, 4>(calls, n, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <class P, typename XT>

@@ -38,7 +38,7 @@ def _library_kernels():
             sx = "true" if m.group(5) == "1" else "false"
             names.add(f"qmv::gemv_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, {m.group(4)}, {sx}>")
             continue
-        if "qmv::gemv_kernel<" in line or "qmv::gemm_q4_k_bf16_" in line:
+        if "qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemm_q4_k_bf16_" in line:
             sym = line.split(" ", 2)[2]
             sym = sym[5:] if sym.startswith("void ") else sym
             names.add(sym.split("(")[0])
@@ -62,7 +62,8 @@ def test_named_kernel_exists_in_library(config, batch):
 def test_default_layout():
     assert bench.default_layout(3, None) == "planes"
     assert bench.default_layout(5, 1) == "planes"
-    assert bench.default_layout(5, 4) == "blocks"       # matrix cores: blocks stream faster
+    assert bench.default_layout(5, 4) == "planes"       # multi-row GEMV
+    assert bench.default_layout(5, 16) == "blocks"      # matrix cores: blocks stream faster
     assert bench.default_layout(4, None) == "planes"
     assert bench.default_layout(6, None) == "planes"
     for c in (1, 2):

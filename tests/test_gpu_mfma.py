@@ -8,7 +8,8 @@ paths and are checked exactly.  Shapes cover the three kernels behind the call
 (batch <= 16 with X in LDS: one to eight 16-row tiles per workgroup and more
 workgroups than CUs; batch <= 32 or K too long for LDS: K split over waves;
 larger batches: 64 x 64 tiles), ragged rows and batches, the smallest batch
-routed here (2), and the full-size batched workload (18944 x 3584, M = 4, 16,
+routed here (2: matrices wider than 4096 columns; narrower ones at batch 2-4
+take the multi-row GEMV), and the full-size batched workload (18944 x 3584, M = 4, 16,
 64 and 512) on sampled rows.
 """
 import numpy as np

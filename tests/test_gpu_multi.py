@@ -111,10 +111,12 @@ def test_multi_graph_replay_matches_eager():
 
 
 @pytest.mark.parametrize("batch", [2, 4, 24, 64])
-def test_multi_q4_k_bf16_batches_take_the_matrix_cores(batch):
-    """Q4_K x bf16 with batch >= 2: each item runs the batched kernel for its
-    batch size; results match the oracle and the same item called alone
-    (same kernel, same arithmetic: bitwise)."""
+def test_multi_q4_k_bf16_batches_per_item_routing(batch):
+    """Q4_K x bf16 with batch >= 2: each item runs the kernel its own call
+    takes (the multi-row GEMV for matrices of at most 4096 columns at batch
+    2-4, the matrix cores otherwise), whatever the other items of the launch;
+    results match the oracle and the same item called alone (same kernel,
+    same arithmetic: bitwise)."""
     items = [(67, 14), (16, 14), (130, 3), (33, 20)]
     ws, xs_np, xs, ys = [], [], [], []
     for i, (rows, nblk) in enumerate(items):
