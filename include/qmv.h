@@ -207,14 +207,17 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * fmt, rows and cols must repeat the descriptor's (QMV_ERR_FORMAT otherwise),
  * x is [batch][cols] of x_dtype (QMV_F32, QMV_F16 or QMV_BF16), y is
  * [batch][rows] fp32; x and y device pointers, 16-byte aligned.  Enqueues on
- * `stream` and returns; legal inside HIP stream capture.  For Q4_K with bf16
- * activations and batch >= 2 the call runs the matrix-core path (weights read
- * once for up to 16 activation rows, once per tile of 32, 64 or 128 rows
- * above; exact products, fp32 sums, results independent of timing);
- * otherwise each activation row is a GEMV over the packed weights.
- * Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the same arithmetic,
- * in the same order, as the canonical layout -- the GEMV and, for Q4_K x
- * bf16 batches, the matrix-core path -- so results equal bit for bit. */
+ * `stream` and returns; legal inside HIP stream capture.  Q4_K with cols <=
+ * 4096 and either 2..4 bf16 activation rows or any batch >= 2 of fp16 rows
+ * runs the multi-row GEMV: weights read once per two or four activation
+ * rows, and each output row equal bit for bit to the batch-1 call on that
+ * activation row.  Other Q4_K x bf16 calls with batch >= 2 run the
+ * matrix-core path (weights read once for up to 16 activation rows, once per
+ * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
+ * independent of timing).  Otherwise each activation row is a GEMV over the
+ * packed weights.  Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the
+ * same arithmetic, in the same order, as the canonical layout on every one
+ * of these paths, so results equal bit for bit. */
 int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,
                  int32_t x_dtype, float* y, int64_t rows, int64_t cols,
                  int64_t batch, void* stream);
@@ -237,7 +240,9 @@ typedef struct qmv_gemv_item {
  * the y ranges must be disjoint (QMV_ERR_SHAPE otherwise); every x and y is a
  * 16-byte aligned device pointer; all items share one layout
  * (QMV_ERR_UNSUPPORTED otherwise).  Results equal n separate qmv_gemv calls
- * up to float32 summation order. */
+ * up to float32 summation order; where the calls would take the multi-row
+ * GEMV or the matrix-core path, the launch routes each item as its own call
+ * would, and results equal bit for bit. */
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch,
                        const qmv_gemv_item* items, int32_t n, void* stream);
 
