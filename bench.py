@@ -75,12 +75,14 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     matrix-core kernels, chosen by batch and by
     whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
     split), and the shared-activation kernel when no matrix splits K; Q4_K
-    weights in the plane layout take the plane policy; Q4_K x fp16 with two or
-    more rows, or x bf16 with 2-4 rows, against matrices of at most 4096
-    columns -> the multi-row GEMV)."""
-    if (fmt == "q4_k" and max(cols_list) <= 4096 and batch >= 2
-            and (x_dtype == "f16" or (x_dtype == "bf16" and batch <= 4))):
-        pol = "Q4KPlanesPolicy" if layout == "planes" else "Q4KPolicy"
+    weights in the plane layout take the plane policy; Q4_K, Q6_K and INT4
+    with two or more fp16 or bf16 rows (Q4_K x bf16: 2-4 rows) against
+    matrices of at most 4096 columns -> the multi-row GEMV)."""
+    if (fmt in ("q4_k", "q6_k", "int4_g128") and max(cols_list) <= 4096 and batch >= 2
+            and x_dtype in ("f16", "bf16") and not (fmt == "q4_k" and x_dtype == "bf16" and batch > 4)):
+        pol = {"q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy", "int4_g128": "Int4G128Policy"}[fmt]
+        if layout == "planes":
+            pol = {"q4_k": "Q4KPlanesPolicy", "q6_k": "Q6KPlanesPolicy"}[fmt]
         xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
         return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, {'2, 2, 256, 2' if batch == 2 else '1, 3, 256, 4'}>"
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:
@@ -184,7 +186,7 @@ def cpu_baseline(mats, fmt, x_dtype, fields_list, xs, seconds):
 PEAK_TFLOPS_BF16 = 2500.0   # MI355X dense bf16 matrix cores, vendor figure
 
 
-def default_layout(config: int, batch: int | None = None) -> str:
+def default_layout(config: int, batch: int | None = None, x_dtype: str | None = None) -> str:
     """Q4_K, Q5_K and Q6_K on the GEMV path stream the plane layout (repacked
     once at load, as a decode layout replacing the blocks); Q4_K x bf16
     batches on the matrix cores read the canonical blocks, which they stream
@@ -193,11 +195,14 @@ def default_layout(config: int, batch: int | None = None) -> str:
     from synth import CONFIGS
     cfg = CONFIGS[config]
     b = batch or cfg["batch"][0]
-    gemv = not (cfg["x_dtype"] == "bf16" and b >= 5)  # batches of 2-4: the multi-row GEMV
+    xd = x_dtype or cfg["x_dtype"]
+    # Q4_K x bf16 batches of 5 or more run on the matrix cores; 2-4 rows take the multi-row GEMV
+    gemv = not (cfg["fmt"] == "q4_k" and xd == "bf16" and b >= 5)
     return "planes" if cfg["fmt"] in ("q4_k", "q5_k", "q6_k") and gemv else "blocks"
 
 
-def workload_plan(config: int, batch: int | None, separate: bool, layout: str = "blocks") -> dict:
+def workload_plan(config: int, batch: int | None, separate: bool, layout: str = "blocks",
+                  x_dtype: str | None = None) -> dict:
     """Launches of one step and their algorithmic bytes and flops (no GPU needed).
 
     Bytes per launch = packed weights + each activation once + y; flops =
@@ -208,7 +213,9 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
     from block_quantized_weight_qmv_amd import qmv
     from synth import CONFIGS
     cfg = CONFIGS[config]
-    fmt, x_dtype = cfg["fmt"], cfg["x_dtype"]
+    fmt = cfg["fmt"]
+    x_dtype = x_dtype or cfg["x_dtype"]
+    batch_given = batch is not None and batch != cfg["batch"][0]
     batch = batch or cfg["batch"][0]
     mats = cfg["mats"]
     names = [n for n, _, _ in mats]
@@ -227,7 +234,8 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
     for gi in range(len(groups)):
         by_kernel.setdefault(kname[gi], []).append(gi)
     dom = max(by_kernel, key=lambda k: sum(gbytes[gi] for gi in by_kernel[k]))
-    workload = cfg["name"] + (f"_m{batch}" if config == 5 else "")
+    workload = (cfg["name"] + (f"_m{batch}" if config == 5 or batch_given else "")
+                + (f"_x{x_dtype}" if x_dtype != cfg["x_dtype"] else ""))
     return {"cfg": cfg, "fmt": fmt, "x_dtype": x_dtype, "batch": batch, "mats": mats,
             "names": names, "groups": groups, "wbytes": wbytes, "gbytes": gbytes,
             "gflops": gflops, "kname": kname, "bound": bound, "by_kernel": by_kernel,
@@ -267,7 +275,7 @@ def summarize_counters(args) -> int:
     and of `python -m block_quantized_weight_qmv_amd.probe copy --mib N` for the
     scale factors (a copy of N MiB reads and writes N MiB)."""
     fetch_d, write_d, cfetch_d, cwrite_d = args.summarize_counters
-    plan = workload_plan(args.config, args.batch, args.separate, _layout(args))
+    plan = workload_plan(args.config, args.batch, args.separate, _layout(args), args.x_dtype)
     groups, kname, gbytes = plan["groups"], plan["kname"], plan["gbytes"]
     copy_kib = args.copy_mib * 1024.0
 
@@ -347,7 +355,8 @@ def summarize_counters(args) -> int:
 
 
 def _layout(args) -> str:
-    return default_layout(args.config, args.batch) if args.layout == "auto" else args.layout
+    return (default_layout(args.config, args.batch, args.x_dtype) if args.layout == "auto"
+            else args.layout)
 
 
 def main() -> int:
@@ -356,7 +365,10 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--config", type=int, default=3, choices=[1, 2, 3, 4, 5, 6])
-    ap.add_argument("--batch", type=int, default=None, help="activation rows (config 5 only)")
+    ap.add_argument("--batch", type=int, default=None,
+                    help="activation rows (default: the configuration's; config 5 is quoted at 1, 4, 16, 64, 512)")
+    ap.add_argument("--x-dtype", choices=["f32", "f16", "bf16"], default=None,
+                    help="activation dtype in place of the configuration's (same seeded values)")
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed graph replays before each timed one (steady-state clocks)")
@@ -392,7 +404,7 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     layout = _layout(args)
-    plan = workload_plan(args.config, args.batch, args.separate, layout)
+    plan = workload_plan(args.config, args.batch, args.separate, layout, args.x_dtype)
     cfg, fmt, x_dtype, batch = plan["cfg"], plan["fmt"], plan["x_dtype"], plan["batch"]
     mats, names, groups = plan["mats"], plan["names"], plan["groups"]
     gbytes, gflops, kname, by_kernel, dom = (plan["gbytes"], plan["gflops"], plan["kname"],

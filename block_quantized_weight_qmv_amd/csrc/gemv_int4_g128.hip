@@ -155,7 +155,49 @@ struct Int4G128Policy {
     }
     return out;
   }
+
+  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the code masks
+  // are computed once, then each row's sums follow dot's operations in dot's
+  // order, so out[m] equals dot(f, s[m]) bit for bit.
+  template <typename XT, int NBR>
+  __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
+    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) out[m] = 0.f;
+#pragma unroll
+    for (int hf = 0; hf < 2; ++hf) {
+      const uint32_t q[4] = {f.q[hf].x, f.q[hf].y, f.q[hf].z, f.q[hf].w};
+      float se[NBR], so[NBR];
+#pragma unroll
+      for (int m = 0; m < NBR; ++m) se[m] = so[m] = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w0 = q[i], w8 = q[i] >> 8;
+        const uint32_t a = w0 & 0x000F000Fu, b = w8 & 0x000F000Fu;
+        const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;
+#pragma unroll
+        for (int m = 0; m < NBR; ++m) {
+          const h2_t* x = s[m].h + 16 * hf + 4 * i;
+          se[m] = dot2_lo_hi(a, x[0], se[m]);
+          se[m] = dot2_lo_hi(b, x[1], se[m]);
+          so[m] = dot2_lo_hi(e, x[2], so[m]);
+          so[m] = dot2_lo_hi(g, x[3], so[m]);
+        }
+      }
+      const float sc = f16_to_f32(f.sb[hf]);
+#pragma unroll
+      for (int m = 0; m < NBR; ++m) {
+        const float t = fmaf(s[m].xs, fmaf(so[m], 0.0625f, se[m]), -8.f * s[m].s[hf]);
+        out[m] = fmaf(sc, t, out[m]);
+      }
+    }
+  }
 };
+
+hipError_t gemv_int4_g128_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch,
+                               hipStream_t s) {
+  return launch_gemv_rows<Int4G128Policy>(calls, n, x_dtype, batch, s);
+}
 
 hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
   return launch_gemv<Int4G128Policy>(calls, n, x_dtype, batch, s);

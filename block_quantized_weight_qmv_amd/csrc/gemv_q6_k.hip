@@ -148,6 +148,53 @@ struct Q6KPolicy {
     }
     return f16_to_f32(f.d) * t;
   }
+
+  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the 6-bit codes
+  // and the sub-scales are assembled once, then each row's sums follow dot's
+  // operations in dot's order, so out[m] equals dot(f, s[m]) bit for bit.
+  template <typename XT, int NBR>
+  __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
+    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
+    const uint32_t la[4] = {f.la.x, f.la.y, f.la.z, f.la.w};
+    const uint32_t lb[4] = {f.lb.x, f.lb.y, f.lb.z, f.lb.w};
+    const uint32_t qh[4] = {f.qh.x, f.qh.y, f.qh.z, f.qh.w};
+    float acc[NBR][4];
+#pragma unroll
+    for (int m = 0; m < NBR; ++m)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) acc[m][g] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t q6[4] = {
+          (la[k] & 0x0F0F0F0Fu) | ((qh[k] << 4) & 0x30303030u),
+          (lb[k] & 0x0F0F0F0Fu) | ((qh[k] << 2) & 0x30303030u),
+          ((la[k] >> 4) & 0x0F0F0F0Fu) | (qh[k] & 0x30303030u),
+          ((lb[k] >> 4) & 0x0F0F0F0Fu) | ((qh[k] >> 2) & 0x30303030u)};
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const uint32_t a = q6[g] & 0x003F003Fu, b = (q6[g] >> 8) & 0x003F003Fu;
+#pragma unroll
+        for (int m = 0; m < NBR; ++m) {
+          acc[m][g] = dot2_lo_hi(a, s[m].h[8 * g + 2 * k], acc[m][g]);
+          acc[m][g] = dot2_lo_hi(b, s[m].h[8 * g + 2 * k + 1], acc[m][g]);
+        }
+      }
+    }
+    float scf[4];
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      const uint32_t word = g < 2 ? f.sc.x : f.sc.y;
+      scf[g] = static_cast<float>(static_cast<int8_t>((word >> (8 * (2 * (g & 1) + i))) & 0xFFu));
+    }
+    const float d = f16_to_f32(f.d);
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) {
+      float t = 0.f;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) t = fmaf(scf[g], fmaf(s[m].xs, acc[m][g], -32.f * s[m].s[g]), t);
+      out[m] = d * t;
+    }
+  }
 };
 
 // The same GEMV over the Q6_K plane layout of planes.h: lane mapping,
@@ -186,6 +233,12 @@ struct Q6KPlanesPolicy : Q6KPolicy {
     f.d = ld_u16(dp + 2 * b);
   }
 };
+
+hipError_t gemv_q6_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,
+                          hipStream_t s) {
+  return planes ? launch_gemv_rows<Q6KPlanesPolicy>(calls, n, x_dtype, batch, s)
+                : launch_gemv_rows<Q6KPolicy>(calls, n, x_dtype, batch, s);
+}
 
 hipError_t gemv_q6_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
   return launch_gemv<Q6KPolicy>(calls, n, x_dtype, batch, s);

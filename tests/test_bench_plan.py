@@ -32,11 +32,17 @@ def _library_kernels():
     names = set()
     # this nm leaves the _Float16 instantiations mangled
     f16 = re.compile(r"_ZN3qmv11gemv_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELb([01])EEEvNS_10GemvLaunchE")
+    f16_rows = re.compile(r"_ZN3qmv16gemv_rows_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi")
     for line in out.splitlines():
         m = f16.search(line)
         if m:
             sx = "true" if m.group(5) == "1" else "false"
             names.add(f"qmv::gemv_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, {m.group(4)}, {sx}>")
+            continue
+        m = f16_rows.search(line)
+        if m:
+            names.add(f"qmv::gemv_rows_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, "
+                      f"{m.group(4)}, {m.group(5)}>")
             continue
         if "qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemm_q4_k_bf16_" in line:
             sym = line.split(" ", 2)[2]
@@ -101,3 +107,18 @@ def test_more_than_one_gpu_is_refused():
     r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and "single GPU" in r.stderr
+
+
+@pytest.mark.parametrize("config,batch,x_dtype", [(2, 4, None), (2, 3, "bf16"), (4, 4, "bf16"), (4, 2, "f16"),
+                                                  (3, 2, "f16"), (5, 4, "f16"), (5, 8, "f16")])
+def test_small_batch_overrides_name_library_kernels(config, batch, x_dtype):
+    # --batch on any configuration and --x-dtype: the multi-row GEMV for the
+    # formats that have one, named as the library exports it
+    names = _library_kernels()
+    layout = bench.default_layout(config, batch, x_dtype)
+    plan = bench.workload_plan(config, batch, separate=False, layout=layout, x_dtype=x_dtype)
+    assert plan["x_dtype"] == (x_dtype or CONFIGS[config]["x_dtype"])
+    for k, g in zip(plan["kname"], plan["groups"]):
+        assert k in names, k
+    narrow = [k for k in plan["kname"] if "gemv_rows_kernel" in k]
+    assert narrow, plan["kname"]

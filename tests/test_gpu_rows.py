@@ -1,16 +1,19 @@
-"""Q4_K with several fp16 or bf16 activation rows: the multi-row GEMV.
+"""Q4_K, Q6_K and INT4-g128 with several fp16 or bf16 activation rows: the
+multi-row GEMV.
 
-qmv_gemv routes Q4_K with two or more fp16 activation rows, or 2-4 bf16 rows,
-against matrices of at most 4096 columns to a GEMV that reads W once per two
-or four rows.  Each row's products and sums are the batch-1 GEMV's operations
-in the same order and the wave reduction adds in the same order, so every
-output row must equal the batch-1 GEMV of that activation row bit for bit,
-and the float64 oracle within the 2e-3 normwise gate.  Shapes: one block,
-ragged tiles, a full wave K slice, odd block counts; batches 2, 3 (a partial
-group of four) and 4, fp16 batches of several groups; both layouts; several
-matrices in one launch; graph replay; the full 18944 x 3584 batched workload
-at M = 2, 3, 4 (all rows compared with the batch-1 GEMV, sampled rows with
-the oracle).
+qmv_gemv routes these formats with two or more fp16 or bf16 activation rows
+(Q4_K x bf16: 2-4 rows; larger bf16 batches take the matrix cores) against
+matrices of at most 4096 columns to a GEMV that reads W once per two or four
+rows.  Each row's products and sums are the batch-1 GEMV's operations in the
+same order and the wave reduction adds in the same order, so every output row
+must equal the batch-1 GEMV of that activation row bit for bit, and the
+float64 oracle within the 2e-3 normwise gate.  Shapes: one block, ragged
+tiles, a full wave K slice, odd block counts; batches 2, 3 (a partial group of
+four) and 4, and batches of several groups; every layout of the format;
+several matrices in one launch, one of them wider than a wave's K slice
+(routed as its own call); graph replay; the full 18944 x 3584 gate shape at
+M = 2, 3, 4 (all rows against the batch-1 GEMV, sampled rows against the
+oracle).
 """
 import numpy as np
 import pytest
@@ -24,6 +27,9 @@ from synth import CONFIGS, gen_x, weight_seed, x_seed
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
+FMTS = ["q4_k", "q6_k", "int4_g128"]
+LAYOUTS = {"q4_k": ["blocks", "planes"], "q6_k": ["blocks", "planes"], "int4_g128": ["blocks"]}
+FMT_LAYOUTS = [(f, lay) for f in FMTS for lay in LAYOUTS[f]]
 SHAPES = [(1, 1), (3, 1), (5, 3), (67, 14), (9, 16), (40, 5), (130, 2)]
 
 
@@ -34,86 +40,96 @@ def _planes(w: Weights):
     return desc
 
 
-def _per_row(desc, rows, cols, xd, x_dtype, batch):
+def _desc(w: Weights, layout):
+    return w.desc if layout == "blocks" else _planes(w)
+
+
+def _per_row(fmt, desc, rows, cols, xd, x_dtype, batch):
     """The batch-1 GEMV of each activation row."""
     out = []
     for i in range(batch):
         y = torch.empty(1, rows, dtype=torch.float32, device=DEV)  # own buffer: 16-byte aligned
-        qmv.qmv_gemv("q4_k", desc, xd[i:i + 1].clone(), x_dtype, y, rows, cols, 1)
+        qmv.qmv_gemv(fmt, desc, xd[i:i + 1].clone(), x_dtype, y, rows, cols, 1)
         out.append(y)
     return torch.cat(out)
 
 
-@pytest.mark.parametrize("layout", ["blocks", "planes"])
-@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
-@pytest.mark.parametrize("batch", [2, 3, 4])
-@pytest.mark.parametrize("rows,nblk", SHAPES)
-def test_rows_equal_batch1_and_oracle(layout, x_dtype, batch, rows, nblk):
-    cols = nblk * 256
-    say(f"multi-row q4_k {layout} {rows}x{cols} batch {batch} x {x_dtype}")
-    w = Weights("q4_k", rows, cols, seed=1300 + rows + nblk)
-    desc = w.desc if layout == "blocks" else _planes(w)
-    x = gen_x(batch, cols, x_dtype, seed=130 + batch + nblk)
+def _check(fmt, layout, rows, cols, batch, x_dtype, seed):
+    w = Weights(fmt, rows, cols, seed=seed)
+    desc = _desc(w, layout)
+    x = gen_x(batch, cols, x_dtype, seed=seed + 7)
     xd = to_dev_x(x, x_dtype)
     # one row past the batch: must stay untouched
     y = torch.full((batch + 1, rows), 7.25, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv("q4_k", desc, xd, x_dtype, y, rows, cols, batch)
+    qmv.qmv_gemv(fmt, desc, xd, x_dtype, y, rows, cols, batch)
     got = y.cpu().numpy()
     assert np.all(got[batch] == 7.25)
-    np.testing.assert_array_equal(got[:batch], _per_row(desc, rows, cols, xd, x_dtype, batch).cpu().numpy())
+    np.testing.assert_array_equal(got[:batch], _per_row(fmt, desc, rows, cols, xd, x_dtype, batch).cpu().numpy())
     err = oracle.normwise_rel_err(got[:batch], oracle_y(w, x, x_dtype))
     say(f"  normwise err max {err.max():.3e}")
     assert np.all(err <= TOL), err
 
 
-@pytest.mark.parametrize("layout", ["blocks", "planes"])
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("batch", [2, 3, 4])
+@pytest.mark.parametrize("rows,nblk", SHAPES)
+def test_rows_equal_batch1_and_oracle(fmt, layout, x_dtype, batch, rows, nblk):
+    cols = nblk * 256
+    say(f"multi-row {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
+    _check(fmt, layout, rows, cols, batch, x_dtype, seed=1300 + rows + nblk)
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
 @pytest.mark.parametrize("batch", [5, 8, 9, 30])
 @pytest.mark.parametrize("rows,nblk", [(3, 1), (67, 14), (130, 2)])
-def test_rows_f16_groups_of_four(layout, batch, rows, nblk):
-    # fp16 batches above four: one pass over W per group of four rows, the
-    # last group partial unless four divides the batch
+def test_rows_groups_of_four(fmt, layout, x_dtype, batch, rows, nblk):
+    # batches above four: one pass over W per group of four rows, the last
+    # group partial unless four divides the batch (Q4_K x bf16 batches above
+    # four take the matrix cores and are not this kernel's)
+    if fmt == "q4_k" and x_dtype == "bf16":
+        pytest.skip("Q4_K x bf16 batches above four run on the matrix cores (test_gpu_mfma.py)")
     cols = nblk * 256
-    say(f"multi-row q4_k {layout} {rows}x{cols} batch {batch} x f16")
-    w = Weights("q4_k", rows, cols, seed=1600 + rows + nblk)
-    desc = w.desc if layout == "blocks" else _planes(w)
-    x = gen_x(batch, cols, "f16", seed=160 + batch + nblk)
-    xd = to_dev_x(x, "f16")
-    y = torch.full((batch + 1, rows), 7.25, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv("q4_k", desc, xd, "f16", y, rows, cols, batch)
-    got = y.cpu().numpy()
-    assert np.all(got[batch] == 7.25)
-    np.testing.assert_array_equal(got[:batch], _per_row(desc, rows, cols, xd, "f16", batch).cpu().numpy())
-    assert np.all(oracle.normwise_rel_err(got[:batch], oracle_y(w, x, "f16")) <= TOL)
+    say(f"multi-row {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
+    _check(fmt, layout, rows, cols, batch, x_dtype, seed=1600 + rows + nblk)
 
 
-@pytest.mark.parametrize("layout", ["blocks", "planes"])
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
 @pytest.mark.parametrize("batch", [2, 4])
-def test_rows_multi_matrix_launch(layout, batch):
-    # q, k, v-shaped matrices (scaled down) in one launch, each with its own x
-    shapes = [(96, 14), (16, 14), (16, 14), (33, 3)]
-    say(f"multi-row multi-matrix {layout} batch {batch}")
+def test_rows_multi_matrix_launch(fmt, layout, batch):
+    # q, k, v-shaped matrices (scaled down) and one wider than a wave's K
+    # slice in one launch, each with its own x; every item must equal its own
+    # call's result bitwise
+    shapes = [(96, 14), (16, 14), (16, 14), (33, 3), (9, 20)]
+    say(f"multi-row multi-matrix {fmt} {layout} batch {batch}")
     ws, descs, xs, ys, items = [], [], [], [], []
     for i, (rows, nblk) in enumerate(shapes):
-        w = Weights("q4_k", rows, nblk * 256, seed=1400 + i)
-        d = w.desc if layout == "blocks" else _planes(w)
+        w = Weights(fmt, rows, nblk * 256, seed=1400 + i)
+        d = _desc(w, layout)
         x = gen_x(batch, nblk * 256, "bf16", seed=140 + i)
         ws.append(w)
         descs.append(d)
         xs.append((x, to_dev_x(x, "bf16")))
         ys.append(torch.full((batch, rows), -1.0, dtype=torch.float32, device=DEV))
         items.append((d, xs[-1][1], ys[-1]))
-    qmv.qmv_gemv_multi("q4_k", "bf16", batch, items)
+    qmv.qmv_gemv_multi(fmt, "bf16", batch, items)
     for w, d, (x, xd), y in zip(ws, descs, xs, ys):
         got = y.cpu().numpy()
-        ref = _per_row(d, w.rows, w.cols, xd, "bf16", batch).cpu().numpy()
-        np.testing.assert_array_equal(got, ref)
+        alone = torch.empty(batch, w.rows, dtype=torch.float32, device=DEV)
+        qmv.qmv_gemv(fmt, d, xd, "bf16", alone, w.rows, w.cols, batch)
+        np.testing.assert_array_equal(got, alone.cpu().numpy())
+        if w.cols <= 4096:
+            ref = _per_row(fmt, d, w.rows, w.cols, xd, "bf16", batch).cpu().numpy()
+            np.testing.assert_array_equal(got, ref)
         assert np.all(oracle.normwise_rel_err(got, oracle_y(w, x, "bf16")) <= TOL)
 
 
-def test_rows_graph_replay():
+@pytest.mark.parametrize("fmt", FMTS)
+def test_rows_graph_replay(fmt):
     rows, cols, batch = 300, 14 * 256, 4
-    say("multi-row graph replay")
-    w = Weights("q4_k", rows, cols, seed=1500)
+    say(f"multi-row graph replay {fmt}")
+    w = Weights(fmt, rows, cols, seed=1500)
     xd = to_dev_x(gen_x(batch, cols, "bf16", seed=150), "bf16")
     y0 = w.gemv(xd, "bf16", batch)
     s = torch.cuda.Stream()
@@ -132,24 +148,32 @@ def test_rows_graph_replay():
         assert torch.equal(yg, y0)
 
 
-@pytest.mark.parametrize("layout", ["blocks", "planes"])
+# full-size shapes: the Q4_K FFN gate (bf16 x), the INT4 FFN gate (fp16 x), the
+# Q6_K lm-head (bf16 x)
+FULL = [("q4_k", 5, "bf16", "blocks"), ("q4_k", 5, "bf16", "planes"), ("int4_g128", 2, "f16", "blocks"),
+        ("q6_k", 4, "bf16", "planes")]
+
+
+@pytest.mark.parametrize("fmt,config,x_dtype,layout", FULL)
 @pytest.mark.parametrize("batch", [2, 3, 4])
-def test_rows_full_size_batched_ffn(layout, batch):
-    cfg = CONFIGS[5]
+def test_rows_full_size(fmt, config, x_dtype, layout, batch):
+    cfg = CONFIGS[config]
     rows, cols = cfg["mats"][0][1], cfg["mats"][0][2]
-    say(f"full-size multi-row {layout} {rows}x{cols} batch {batch}")
-    w = Weights("q4_k", rows, cols, seed=weight_seed(5, 0))
-    desc = w.desc if layout == "blocks" else _planes(w)
-    x = gen_x(batch, cols, "bf16", x_seed(5, 0))
-    xd = to_dev_x(x, "bf16")
+    say(f"full-size multi-row {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
+    w = Weights(fmt, rows, cols, seed=weight_seed(config, 0))
+    desc = _desc(w, layout)
+    x = gen_x(batch, cols, x_dtype, x_seed(config, 0))
+    xd = to_dev_x(x, x_dtype)
     y = torch.empty(batch, rows, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv("q4_k", desc, xd, "bf16", y, rows, cols, batch)
+    qmv.qmv_gemv(fmt, desc, xd, x_dtype, y, rows, cols, batch)
     got = y.cpu().numpy()
-    np.testing.assert_array_equal(got, _per_row(desc, rows, cols, xd, "bf16", batch).cpu().numpy())
+    np.testing.assert_array_equal(got, _per_row(fmt, desc, rows, cols, xd, x_dtype, batch).cpu().numpy())
     g = np.random.Generator(np.random.PCG64(40 + batch))
     ids = np.sort(g.choice(rows, size=48, replace=False))
     ids = np.unique(np.concatenate([ids, [0, rows - 1]]))
-    ref = oracle_y(w, x, "bf16", row_ids=ids)
+    ref = oracle_y(w, x, x_dtype, row_ids=ids)
     err = oracle.normwise_rel_err(got[:, ids], ref)
     say(f"  sampled normwise err max {err.max():.3e}")
     assert np.all(err <= TOL), err
+    del w, desc
+    torch.cuda.empty_cache()
