@@ -75,14 +75,16 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     matrix-core kernels, chosen by batch and by
     whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
     split), and the shared-activation kernel when no matrix splits K; Q4_K
-    weights in the plane layout take the plane policy; Q4_K, Q6_K and INT4
-    with two or more fp16 or bf16 rows (Q4_K x bf16: 2-4 rows) against
-    matrices of at most 4096 columns -> the multi-row GEMV)."""
-    if (fmt in ("q4_k", "q6_k", "int4_g128") and max(cols_list) <= 4096 and batch >= 2
-            and x_dtype in ("f16", "bf16") and not (fmt == "q4_k" and x_dtype == "bf16" and batch > 4)):
-        pol = {"q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy", "int4_g128": "Int4G128Policy"}[fmt]
+    weights in the plane layout take the plane policy; two or more fp16 or
+    bf16 rows (Q4_K x bf16: 2-4 rows) against matrices within one wave's K
+    slice (4096 columns, Q8_0 2048) -> the multi-row GEMV)."""
+    wave_cols = 2048 if fmt == "q8_0" else 4096
+    if (max(cols_list) <= wave_cols and batch >= 2 and x_dtype in ("f16", "bf16")
+            and not (fmt == "q4_k" and x_dtype == "bf16" and batch > 4)):
+        pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q5_k": "Q5KPolicy", "q6_k": "Q6KPolicy",
+               "int4_g128": "Int4G128Policy"}[fmt]
         if layout == "planes":
-            pol = {"q4_k": "Q4KPlanesPolicy", "q6_k": "Q6KPlanesPolicy"}[fmt]
+            pol = {"q4_k": "Q4KPlanesPolicy", "q5_k": "Q5KPlanesPolicy", "q6_k": "Q6KPlanesPolicy"}[fmt]
         xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
         return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, {'2, 2, 256, 2' if batch == 2 else '1, 3, 256, 4'}>"
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:

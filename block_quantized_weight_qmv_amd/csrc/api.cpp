@@ -262,19 +262,19 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   // matrix-core kernel, one launch per matrix (the GEMV path would read the
   // weights once per activation row).
   const bool planes = items[0].W->layout == QMV_LAYOUT_PLANES;
-  // Q4_K, Q6_K and INT4 with two or more fp16 or bf16 rows (Q4_K bf16: up to
-  // kRowsMaxBf16Batch): the matrices of at most 4096 columns take the
-  // multi-row GEMV (one launch, one pass over the weights per two or four
-  // activation rows), the wider ones the kernel their own call would take, so
-  // that every item's result is the same as that of the item called alone.
-  const bool rows_fmt = fmt == QMV_Q4_K || fmt == QMV_Q6_K || fmt == QMV_INT4_G128;
+  // Two or more fp16 or bf16 rows (Q4_K bf16: up to kRowsMaxBf16Batch): the
+  // matrices within one wave's K slice take the multi-row GEMV (one launch,
+  // one pass over the weights per two or four activation rows), the wider
+  // ones the kernel their own call would take, so that every item's result
+  // is the same as that of the item called alone.
   const bool half_x = x_dtype == QMV_F16 || x_dtype == QMV_BF16;
-  if (rows_fmt && half_x && batch >= 2 &&
+  const int64_t wave_cols = fmt == QMV_Q8_0 ? 2048 : 4096;
+  if (half_x && batch >= 2 &&
       !(fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch > qmv::kRowsMaxBf16Batch)) {
     qmv::GemvCall narrow[qmv::kMaxItems], wide[qmv::kMaxItems];
     int nn = 0, nw = 0;
     for (int i = 0; i < n; ++i) {
-      if (calls[i].W->cols <= 4096)
+      if (calls[i].W->cols <= wave_cols)
         narrow[nn++] = calls[i];
       else
         wide[nw++] = calls[i];
@@ -283,6 +283,8 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
       switch (fmt) {
         case QMV_Q4_K: e = qmv::gemv_q4_k_rows(narrow, nn, x_dtype, batch, planes, s); break;
         case QMV_Q6_K: e = qmv::gemv_q6_k_rows(narrow, nn, x_dtype, batch, planes, s); break;
+        case QMV_Q5_K: e = qmv::gemv_q5_k_rows(narrow, nn, x_dtype, batch, planes, s); break;
+        case QMV_Q8_0: e = qmv::gemv_q8_0_rows(narrow, nn, x_dtype, batch, s); break;
         default: e = qmv::gemv_int4_g128_rows(narrow, nn, x_dtype, batch, s); break;
       }
     }
@@ -300,6 +302,11 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
             e = planes ? qmv::gemv_q6_k_planes(wide, nw, x_dtype, batch, s)
                        : qmv::gemv_q6_k(wide, nw, x_dtype, batch, s);
             break;
+          case QMV_Q5_K:
+            e = planes ? qmv::gemv_q5_k_planes(wide, nw, x_dtype, batch, s)
+                       : qmv::gemv_q5_k(wide, nw, x_dtype, batch, s);
+            break;
+          case QMV_Q8_0: e = qmv::gemv_q8_0(wide, nw, x_dtype, batch, s); break;
           default: e = qmv::gemv_int4_g128(wide, nw, x_dtype, batch, s); break;
         }
       }

@@ -152,6 +152,47 @@ struct Q5KPolicy {
     const float mm = fmaf(cvt_ubyte<1>(mn), s.s1, cvt_ubyte<0>(mn) * s.s0);
     return fmaf(d, t, -dmin * mm);
   }
+
+  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the header decode
+  // and the five-bit codes are formed once, then each row's sums follow dot's
+  // operations in dot's order, so out[m] equals dot(f, s[m]) bit for bit.
+  template <typename XT, int NBR>
+  __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
+    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
+    const uint32_t t1 = f.hd.y >> sh, t2 = f.hd.z >> sh, t3 = f.hd.w >> sh;
+    const uint32_t sc = ((hi ? t3 : t1) & mask_a) | ((t1 >> 2) & mask_b);
+    const uint32_t mn = ((hi ? (t3 >> 4) : t2) & mask_a) | ((t2 >> 2) & mask_b);
+    const float d16 = f16_to_f32(f.hd.x & 0xFFFFu);
+    const float dmin = f16_to_f32(f.hd.x >> 16);
+
+    const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
+    const uint32_t h[8] = {f.h0.x, f.h0.y, f.h0.z, f.h0.w, f.h1.x, f.h1.y, f.h1.z, f.h1.w};
+    float s0[NBR], s1[NBR];
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) s0[m] = s1[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t w0 = q[i], w8 = q[i] >> 8;
+      const uint32_t a = (w0 & 0x000F000Fu) | (__builtin_rotateright32(h[i], ra) & 0x00100010u);
+      const uint32_t b = (w8 & 0x000F000Fu) | (__builtin_rotateright32(h[i], rb) & 0x00100010u);
+      const uint32_t e = (w0 & 0x00F000F0u) | (__builtin_rotateright32(h[i], re) & 0x01000100u);
+      const uint32_t g = (w8 & 0x00F000F0u) | (__builtin_rotateright32(h[i], rg) & 0x01000100u);
+#pragma unroll
+      for (int m = 0; m < NBR; ++m) {
+        s0[m] = dot2_lo_hi(a, s[m].h[4 * i + 0], s0[m]);
+        s0[m] = dot2_lo_hi(b, s[m].h[4 * i + 1], s0[m]);
+        s1[m] = dot2_lo_hi(e, s[m].h[4 * i + 2], s1[m]);
+        s1[m] = dot2_lo_hi(g, s[m].h[4 * i + 3], s1[m]);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) {
+      const float d = d16 * s[m].xs;
+      const float t = fmaf(cvt_ubyte<1>(sc) * 0.0625f, s1[m], cvt_ubyte<0>(sc) * s0[m]);
+      const float mm = fmaf(cvt_ubyte<1>(mn), s[m].s1, cvt_ubyte<0>(mn) * s[m].s0);
+      out[m] = fmaf(d, t, -dmin * mm);
+    }
+  }
 };
 
 // The same GEMV over the Q5_K plane layout of planes.h: lane mapping,
@@ -189,6 +230,12 @@ struct Q5KPlanesPolicy : Q5KPolicy {
     f.qb = ld16_stream(qb + 64 * b);
   }
 };
+
+hipError_t gemv_q5_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,
+                          hipStream_t s) {
+  return planes ? launch_gemv_rows<Q5KPlanesPolicy>(calls, n, x_dtype, batch, s)
+                : launch_gemv_rows<Q5KPolicy>(calls, n, x_dtype, batch, s);
+}
 
 hipError_t gemv_q5_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
   return launch_gemv<Q5KPolicy>(calls, n, x_dtype, batch, s);

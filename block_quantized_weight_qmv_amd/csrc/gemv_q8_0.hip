@@ -111,7 +111,36 @@ struct Q80Policy {
       xs = s.xs;
     return f16_to_f32(f.d) * fmaf(xs, acc, -128.f * s.s);
   }
+
+  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the offset codes
+  // are formed once, then each row's sum follows dot's operations in dot's
+  // order, so out[m] equals dot(f, s[m]) bit for bit.
+  template <typename XT, int NBR>
+  __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
+    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
+    const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
+    float acc[NBR];
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) acc[m] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = q[i] ^ 0x80808080u;
+      const uint32_t a = u & 0x00FF00FFu, b = (u >> 8) & 0x00FF00FFu;
+#pragma unroll
+      for (int m = 0; m < NBR; ++m) {
+        acc[m] = dot2_lo_hi(a, s[m].h[2 * i], acc[m]);
+        acc[m] = dot2_lo_hi(b, s[m].h[2 * i + 1], acc[m]);
+      }
+    }
+    const float d = f16_to_f32(f.d);
+#pragma unroll
+    for (int m = 0; m < NBR; ++m) out[m] = d * fmaf(s[m].xs, acc[m], -128.f * s[m].s);
+  }
 };
+
+hipError_t gemv_q8_0_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
+  return launch_gemv_rows<Q80Policy>(calls, n, x_dtype, batch, s);
+}
 
 hipError_t gemv_q8_0(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s) {
   return launch_gemv<Q80Policy>(calls, n, x_dtype, batch, s);

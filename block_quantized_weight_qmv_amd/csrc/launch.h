@@ -27,10 +27,10 @@ hipError_t gemv_q4_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, h
 // Q4_K / Q5_K / Q6_K weights in the plane layout (planes.h); every item in that layout.
 hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t s);
-// Q4_K, Q6_K and INT4-g128 with two or more fp16 or bf16 activation rows,
-// every matrix at most 4096 columns: one pass over the weights per two or four
-// rows (gemv_rows_kernel).  Q4_K bf16 batches above kRowsMaxBf16Batch go to
-// the matrix cores; every other batch of these formats takes this path.
+// Every format with two or more fp16 or bf16 activation rows, every matrix
+// within one wave's K slice (4096 columns; Q8_0 2048): one pass over the
+// weights per two or four rows (gemv_rows_kernel).  Q4_K bf16 batches above
+// kRowsMaxBf16Batch go to the matrix cores.
 #ifndef QMV_ROWS_MAX_BF16_BATCH
 #define QMV_ROWS_MAX_BF16_BATCH 4
 #endif
@@ -41,6 +41,9 @@ hipError_t gemv_q6_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t bat
                           hipStream_t s);
 hipError_t gemv_int4_g128_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                                hipStream_t s);
+hipError_t gemv_q5_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,
+                          hipStream_t s);
+hipError_t gemv_q8_0_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
 hipError_t gemv_q5_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, hipStream_t s);
 hipError_t gemv_q5_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t s);

@@ -1,19 +1,19 @@
-"""Q4_K, Q6_K and INT4-g128 with several fp16 or bf16 activation rows: the
-multi-row GEMV.
+"""Every format with several fp16 or bf16 activation rows: the multi-row GEMV.
 
-qmv_gemv routes these formats with two or more fp16 or bf16 activation rows
-(Q4_K x bf16: 2-4 rows; larger bf16 batches take the matrix cores) against
-matrices of at most 4096 columns to a GEMV that reads W once per two or four
-rows.  Each row's products and sums are the batch-1 GEMV's operations in the
-same order and the wave reduction adds in the same order, so every output row
-must equal the batch-1 GEMV of that activation row bit for bit, and the
-float64 oracle within the 2e-3 normwise gate.  Shapes: one block, ragged
-tiles, a full wave K slice, odd block counts; batches 2, 3 (a partial group of
-four) and 4, and batches of several groups; every layout of the format;
-several matrices in one launch, one of them wider than a wave's K slice
-(routed as its own call); graph replay; the full 18944 x 3584 gate shape at
-M = 2, 3, 4 (all rows against the batch-1 GEMV, sampled rows against the
-oracle).
+qmv_gemv routes two or more fp16 or bf16 activation rows (Q4_K x bf16: 2-4
+rows; larger bf16 batches take the matrix cores) against matrices within one
+wave's K slice (4096 columns; Q8_0 2048) to a GEMV that reads W once per two
+or four rows.  Each row's products and sums are the batch-1 GEMV's operations
+in the same order and the wave reduction adds in the same order, so every
+output row must equal the batch-1 GEMV of that activation row bit for bit,
+and the float64 oracle within the 2e-3 normwise gate.  Shapes: one block,
+ragged tiles, a full wave K slice, odd block counts (the widest of them take
+the once-per-row route for Q8_0, which must agree as well); batches 2, 3 (a
+partial group of four) and 4, and batches of several groups; every layout of
+the format; several matrices in one launch, one of them wider than a wave's K
+slice (routed as its own call); graph replay; full-size shapes (Q4_K and INT4
+18944 x 3584, Q6_K 152064 x 3584, Q8_0 1536 x 1536) at M = 2, 3, 4 (all rows
+against the batch-1 GEMV, sampled rows against the oracle).
 """
 import numpy as np
 import pytest
@@ -27,8 +27,9 @@ from synth import CONFIGS, gen_x, weight_seed, x_seed
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-3
-FMTS = ["q4_k", "q6_k", "int4_g128"]
-LAYOUTS = {"q4_k": ["blocks", "planes"], "q6_k": ["blocks", "planes"], "int4_g128": ["blocks"]}
+FMTS = ["q4_k", "q6_k", "int4_g128", "q5_k", "q8_0"]
+LAYOUTS = {"q4_k": ["blocks", "planes"], "q6_k": ["blocks", "planes"], "int4_g128": ["blocks"],
+           "q5_k": ["blocks", "planes"], "q8_0": ["blocks"]}
 FMT_LAYOUTS = [(f, lay) for f in FMTS for lay in LAYOUTS[f]]
 SHAPES = [(1, 1), (3, 1), (5, 3), (67, 14), (9, 16), (40, 5), (130, 2)]
 
@@ -149,9 +150,9 @@ def test_rows_graph_replay(fmt):
 
 
 # full-size shapes: the Q4_K FFN gate (bf16 x), the INT4 FFN gate (fp16 x), the
-# Q6_K lm-head (bf16 x)
+# Q6_K lm-head (bf16 x), the Q8_0 1536 x 1536 matrix (fp16 x)
 FULL = [("q4_k", 5, "bf16", "blocks"), ("q4_k", 5, "bf16", "planes"), ("int4_g128", 2, "f16", "blocks"),
-        ("q6_k", 4, "bf16", "planes")]
+        ("q6_k", 4, "bf16", "planes"), ("q8_0", 1, "f16", "blocks")]
 
 
 @pytest.mark.parametrize("fmt,config,x_dtype,layout", FULL)
