@@ -264,32 +264,39 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   const bool planes = items[0].W->layout == QMV_LAYOUT_PLANES;
   // Two or more fp16 or bf16 rows (Q4_K bf16: up to kRowsMaxBf16Batch): the
   // matrices within one wave's K slice take the multi-row GEMV (one launch,
-  // one pass over the weights per two or four activation rows), the wider
-  // ones the kernel their own call would take, so that every item's result
-  // is the same as that of the item called alone.
+  // one pass over the weights per two or four activation rows), those of two
+  // to eight waves along K its K-split form (one launch, one pass per two
+  // rows; Q4_K x bf16 keeps the matrix cores), the wider ones the GEMV once
+  // per row.  Every item's result is the same as that of the item called
+  // alone.
   const bool half_x = x_dtype == QMV_F16 || x_dtype == QMV_BF16;
   const int64_t wave_cols = fmt == QMV_Q8_0 ? 2048 : 4096;
   if (half_x && batch >= 2 &&
       !(fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch > qmv::kRowsMaxBf16Batch)) {
-    qmv::GemvCall narrow[qmv::kMaxItems], wide[qmv::kMaxItems];
-    int nn = 0, nw = 0;
+    qmv::GemvCall narrow[qmv::kMaxItems], split[qmv::kMaxItems], wide[qmv::kMaxItems];
+    int nn = 0, ns = 0, nw = 0;
+    const bool mfma_wide = fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch;
     for (int i = 0; i < n; ++i) {
       if (calls[i].W->cols <= wave_cols)
         narrow[nn++] = calls[i];
+      else if (calls[i].W->cols <= qmv::kRowsSplitMaxWaves * wave_cols && !mfma_wide)
+        split[ns++] = calls[i];
       else
         wide[nw++] = calls[i];
     }
-    if (nn) {
+    auto rows = [&](const qmv::GemvCall* c, int k) -> hipError_t {
       switch (fmt) {
-        case QMV_Q4_K: e = qmv::gemv_q4_k_rows(narrow, nn, x_dtype, batch, planes, s); break;
-        case QMV_Q6_K: e = qmv::gemv_q6_k_rows(narrow, nn, x_dtype, batch, planes, s); break;
-        case QMV_Q5_K: e = qmv::gemv_q5_k_rows(narrow, nn, x_dtype, batch, planes, s); break;
-        case QMV_Q8_0: e = qmv::gemv_q8_0_rows(narrow, nn, x_dtype, batch, s); break;
-        default: e = qmv::gemv_int4_g128_rows(narrow, nn, x_dtype, batch, s); break;
+        case QMV_Q4_K: return qmv::gemv_q4_k_rows(c, k, x_dtype, batch, planes, s);
+        case QMV_Q6_K: return qmv::gemv_q6_k_rows(c, k, x_dtype, batch, planes, s);
+        case QMV_Q5_K: return qmv::gemv_q5_k_rows(c, k, x_dtype, batch, planes, s);
+        case QMV_Q8_0: return qmv::gemv_q8_0_rows(c, k, x_dtype, batch, s);
+        default: return qmv::gemv_int4_g128_rows(c, k, x_dtype, batch, s);
       }
-    }
+    };
+    if (nn) e = rows(narrow, nn);
+    if (e == hipSuccess && ns) e = rows(split, ns);
     if (e == hipSuccess && nw) {
-      if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
+      if (mfma_wide) {
         for (int i = 0; i < nw && e == hipSuccess; ++i)
           e = qmv::gemm_q4_k_bf16(*wide[i].W, wide[i].x, wide[i].y, batch, s);
       } else {

@@ -356,6 +356,102 @@ gemv_rows_kernel(const GemvLaunch args, int batch) {
     if (r0 + j * R < r_end) finish(f[j], r0 + j * R);
 }
 
+// Two activation rows against matrices split along K (kw > 1 waves per row
+// set): gemv_kernel's K-split structure with gemv_rows_kernel's shared block
+// decode.  Each wave needs both rows' slices of its own K slot, so it reads
+// and converts them itself, one row at a time.  A tile's R x 2 wave totals go
+// to the wave's LDS column ([row - r_begin][activation row]); after one
+// barrier the kw waves of the set add their columns in slot order, the batch-1
+// K split's order, so every output equals the batch-1 GEMV's bit for bit.
+// Grid y covers the batch in steps of two (a last odd row re-reads its
+// predecessor's neighbour, clamped, and is not stored).
+template <class P, typename XT, int R, int D, int MAXT>
+__global__ void __launch_bounds__(MAXT) __attribute__((amdgpu_waves_per_eu(2)))
+gemv_rows_split_kernel(const GemvLaunch args, int batch) {
+  constexpr int NBR = 2;
+  static_assert(R * NBR <= 4, "reduce_rows handles at most four partials");
+  int it = 0;
+#pragma unroll 1
+  for (int k = 1; k < args.n; ++k)
+    if (static_cast<int>(blockIdx.x) >= args.item[k].wg_begin) it = k;
+  const GemvItem& m = args.item[it];
+
+  const int lane = __lane_id();
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kw = m.kw;
+  if (wave >= kw * m.sets_per_wg) return;  // spare waves (they count as arrived at the barrier)
+  const int kslot = wave % kw;
+  const int set = (blockIdx.x - m.wg_begin) * m.sets_per_wg + wave / kw;
+  if (set >= m.nsets) return;  // a whole set absent: all its waves leave together
+  const int mb0 = static_cast<int>(blockIdx.y) * NBR;
+  const int r_begin = set * m.q + R * min(set, m.rem);
+  const int r_end = min(r_begin + m.q + (set < m.rem ? R : 0), m.rows);
+  const int r_last = r_end - 1;
+
+  extern __shared__ float part_lds[];
+  float* part = part_lds + wave * args.part_stride * NBR;
+  const P pol(m.w, m.scales_offset, m.cols, kslot, lane);
+  typename P::Frag f[D][R];
+
+  // Issue order: both rows' x slices, tile 0, tile 1; then convert row by row.
+  uint4 raw[NBR][P::kXElems * sizeof(XT) / 16];
+#pragma unroll
+  for (int mi = 0; mi < NBR; ++mi) {
+    const XT* xr = static_cast<const XT*>(m.x) + static_cast<size_t>(min(mb0 + mi, batch - 1)) * m.cols;
+    pol.load_x_raw(XGlobal<XT>{xr}, raw[mi]);
+  }
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  typename P::template XSliceT<XT> xs[NBR];
+#pragma unroll
+  for (int mi = 0; mi < NBR; ++mi) {
+    pol.template finish_x<XT>(raw[mi], xs[mi]);
+    __builtin_amdgcn_sched_barrier(0);  // one row's conversion temporaries at a time
+  }
+
+  auto finish = [&](const typename P::Frag* fr, int row0) {
+    float acc[R * NBR];
+#pragma unroll
+    for (int r = 0; r < R; ++r) pol.template dot_rows<XT, NBR>(fr[r], xs, acc + r * NBR);
+    const float t = reduce_rows<R * NBR>(acc, lane);
+    // lane q < R x NBR holds partial q = r x NBR + mi of rows row0 + r
+    if (lane < R * NBR && row0 + lane / NBR < r_end)
+      __hip_atomic_store(part + (row0 - r_begin) * NBR + lane, t, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_WORKGROUP);
+  };
+  // Single-exit tile loop with pinned prefetches, as in gemv_kernel.
+  const int ntiles = (r_end - r_begin + R - 1) / R;
+  int r0 = r_begin;
+#pragma unroll 1
+  for (int t = D; t < ntiles; t += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      finish(f[j], r0 + j * R);
+      load_tile<P, R>(pol, f[j], r0 + (j + D) * R, r_last);
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    r0 += D * R;
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (r0 + j * R < r_end) finish(f[j], r0 + j * R);
+
+  // K split: the kw waves of the set add their columns in slot order.
+  __syncthreads();
+  const float* cols = part_lds + (wave - kslot) * args.part_stride * NBR;
+  const int n_out = (r_end - r_begin) * NBR;
+  for (int j = kslot * 64 + lane; j < n_out; j += kw * 64) {
+    float v = cols[j];
+    for (int k = 1; k < kw; ++k) v += cols[k * args.part_stride * NBR + j];
+    const int mi = j % NBR;
+    if (mb0 + mi < batch) m.y[static_cast<size_t>(mb0 + mi) * m.rows + r_begin + j / NBR] = v;
+  }
+}
+
 // Rows of a K-split set are capped so that the partial sums of a workgroup
 // (waves x rows floats) stay within 16 waves x kMaxPartStride x 4 bytes.
 constexpr int kMaxPartStride = 256;
@@ -530,13 +626,66 @@ hipError_t launch_rows(const GemvCall* calls, int n, int64_t batch, hipStream_t 
   return hipGetLastError();
 }
 
-// Batches of two or more fp16 or bf16 activation rows against matrices no
-// wider than one wave's K slice: two rows in one pass over W, otherwise
-// groups of four rows, one pass over W per group.
+// Launch of gemv_rows_split_kernel: matrices of two to eight waves along K,
+// max(4, widest K split) waves per workgroup, the launch shape of the K-split
+// GEMV.
+template <class P, typename XT, int MAXT>
+hipError_t launch_rows_split(const GemvCall* calls, int n, int64_t batch, hipStream_t stream) {
+  // Two weight rows per tile; one where a row's fragment is above 64 bytes
+  // (Q5_K), which would not fit two waves per SIMD without spilling.
+  constexpr int R = sizeof(typename P::Frag) > 64 ? 1 : 2;
+  auto kernel = gemv_rows_split_kernel<P, XT, R, 2, MAXT>;
+  const int kw = max_kw<P>(calls, n);
+  const int waves = kw < 4 ? 4 : kw;
+  if (64 * waves > MAXT) return hipErrorInvalidValue;
+  const int cus = device_cus();
+  int64_t wave_rows = 0;
+  for (int i = 0; i < n; ++i)
+    wave_rows += calls[i].W->rows * ((calls[i].W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
+  const int64_t resident = resident_workgroups(kernel, 64 * waves) * waves;
+  int64_t target = wave_rows / kMinRowsPerWave;
+  if (target > static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd) target = static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd;
+  if (target < static_cast<int64_t>(cus) * 4) target = static_cast<int64_t>(cus) * 4;
+  int64_t per_cu = target / (static_cast<int64_t>(cus) * waves);
+  if (per_cu < 1) per_cu = 1;
+  target = per_cu * cus * waves;
+  if (target > resident) target = resident;
+  GemvLaunch L;
+  const int grid = plan_gemv<P, R>(calls, n, waves, target, &L);
+  const size_t lds = static_cast<size_t>(waves) * L.part_stride * 2 * sizeof(float);
+  hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>((batch + 1) / 2)), dim3(64 * waves), lds,
+                     stream, L, static_cast<int>(batch));
+  return hipGetLastError();
+}
+
+// Two or more fp16 or bf16 activation rows against matrices split along K
+// (two to eight waves): one pass over W per two rows.
+template <class P>
+hipError_t launch_gemv_rows_split(const GemvCall* calls, int n, int x_dtype, int64_t batch,
+                                  hipStream_t stream) {
+  if (batch < 2) return hipErrorInvalidValue;
+  const int kw = max_kw<P>(calls, n);
+  if (kw < 2 || kw > 8) return hipErrorInvalidValue;
+  switch (x_dtype) {
+    case QMV_F16:
+      return kw <= 4 ? launch_rows_split<P, _Float16, 256>(calls, n, batch, stream)
+                     : launch_rows_split<P, _Float16, 512>(calls, n, batch, stream);
+    case QMV_BF16:
+      return kw <= 4 ? launch_rows_split<P, bf16_t, 256>(calls, n, batch, stream)
+                     : launch_rows_split<P, bf16_t, 512>(calls, n, batch, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Batches of two or more fp16 or bf16 activation rows: against matrices no
+// wider than one wave's K slice, two rows in one pass over W, otherwise
+// groups of four rows, one pass over W per group; against matrices split along
+// K (two to eight waves, every matrix of the launch), one pass per two rows.
 template <class P>
 hipError_t launch_gemv_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t stream) {
   if (batch < 2) return hipErrorInvalidValue;
+  if (max_kw<P>(calls, n) > 1) return launch_gemv_rows_split<P>(calls, n, x_dtype, batch, stream);
   const bool two = batch == 2;
   switch (x_dtype) {
     case QMV_F16:

@@ -27,14 +27,23 @@ hipError_t gemv_q4_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, h
 // Q4_K / Q5_K / Q6_K weights in the plane layout (planes.h); every item in that layout.
 hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t s);
-// Every format with two or more fp16 or bf16 activation rows, every matrix
-// within one wave's K slice (4096 columns; Q8_0 2048): one pass over the
-// weights per two or four rows (gemv_rows_kernel).  Q4_K bf16 batches above
-// kRowsMaxBf16Batch go to the matrix cores.
+// Every format with two or more fp16 or bf16 activation rows: matrices within
+// one wave's K slice (4096 columns; Q8_0 2048) take one pass over the weights
+// per two or four rows (gemv_rows_kernel), matrices of 2..kRowsSplitMaxWaves
+// waves along K one pass per two rows (gemv_rows_split_kernel; every item of
+// one call of the same kind).  Q4_K bf16 batches above kRowsMaxBf16Batch go
+// to the matrix cores.
 #ifndef QMV_ROWS_MAX_BF16_BATCH
 #define QMV_ROWS_MAX_BF16_BATCH 4
 #endif
 constexpr int64_t kRowsMaxBf16Batch = QMV_ROWS_MAX_BF16_BATCH;
+// Matrices of two to kRowsSplitMaxWaves waves along K take the K-split form
+// of the multi-row GEMV (two activation rows per pass); wider ones run the
+// GEMV once per activation row.
+#ifndef QMV_ROWS_SPLIT_MAX_WAVES
+#define QMV_ROWS_SPLIT_MAX_WAVES 8
+#endif
+constexpr int64_t kRowsSplitMaxWaves = QMV_ROWS_SPLIT_MAX_WAVES;
 hipError_t gemv_q4_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,
                           hipStream_t s);
 hipError_t gemv_q6_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,

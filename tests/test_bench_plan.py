@@ -33,18 +33,25 @@ def _library_kernels():
     # this nm leaves the _Float16 instantiations mangled
     f16 = re.compile(r"_ZN3qmv11gemv_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELb([01])EEEvNS_10GemvLaunchE")
     f16_rows = re.compile(r"_ZN3qmv16gemv_rows_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi")
+    f16_split = re.compile(r"_ZN3qmv22gemv_rows_split_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi")
     for line in out.splitlines():
         m = f16.search(line)
         if m:
             sx = "true" if m.group(5) == "1" else "false"
             names.add(f"qmv::gemv_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, {m.group(4)}, {sx}>")
             continue
+        m = f16_split.search(line)
+        if m:
+            names.add(f"qmv::gemv_rows_split_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, "
+                      f"{m.group(4)}>")
+            continue
         m = f16_rows.search(line)
         if m:
             names.add(f"qmv::gemv_rows_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, "
                       f"{m.group(4)}, {m.group(5)}>")
             continue
-        if "qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemm_q4_k_bf16_" in line:
+        if ("qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemv_rows_split_kernel<" in line
+                or "qmv::gemm_q4_k_bf16_" in line):
             sym = line.split(" ", 2)[2]
             sym = sym[5:] if sym.startswith("void ") else sym
             names.add(sym.split("(")[0])
@@ -121,5 +128,15 @@ def test_small_batch_overrides_name_library_kernels(config, batch, x_dtype):
     assert plan["x_dtype"] == (x_dtype or CONFIGS[config]["x_dtype"])
     for k, g in zip(plan["kname"], plan["groups"]):
         assert k in names, k
-    narrow = [k for k in plan["kname"] if "gemv_rows_kernel" in k]
-    assert narrow, plan["kname"]
+    multi = [k for k in plan["kname"] if "gemv_rows_kernel" in k or "gemv_rows_split_kernel" in k]
+    assert multi, plan["kname"]
+
+
+@pytest.mark.parametrize("config,batch,x_dtype", [(2, 2, None), (6, 2, "bf16"), (6, 4, "f16"), (3, 2, "f16")])
+def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
+    # the down projections (several waves along K) take the K-split form
+    names = _library_kernels()
+    layout = bench.default_layout(config, batch, x_dtype)
+    plan = bench.workload_plan(config, batch, separate=False, layout=layout, x_dtype=x_dtype)
+    split = [k for k in plan["kname"] if "gemv_rows_split_kernel" in k]
+    assert split and all(k in names for k in split), plan["kname"]

@@ -3,7 +3,8 @@
 qmv_gemv routes two or more fp16 or bf16 activation rows (Q4_K x bf16: 2-4
 rows; larger bf16 batches take the matrix cores) against matrices within one
 wave's K slice (4096 columns; Q8_0 2048) to a GEMV that reads W once per two
-or four rows.  Each row's products and sums are the batch-1 GEMV's operations
+or four rows, and against matrices of two to eight waves along K (except
+Q4_K x bf16) to its K-split form, W once per two rows.  Each row's products and sums are the batch-1 GEMV's operations
 in the same order and the wave reduction adds in the same order, so every
 output row must equal the batch-1 GEMV of that activation row bit for bit,
 and the float64 oracle within the 2e-3 normwise gate.  Shapes: one block,
@@ -11,9 +12,11 @@ ragged tiles, a full wave K slice, odd block counts (the widest of them take
 the once-per-row route for Q8_0, which must agree as well); batches 2, 3 (a
 partial group of four) and 4, and batches of several groups; every layout of
 the format; several matrices in one launch, one of them wider than a wave's K
-slice (routed as its own call); graph replay; full-size shapes (Q4_K and INT4
-18944 x 3584, Q6_K 152064 x 3584, Q8_0 1536 x 1536) at M = 2, 3, 4 (all rows
-against the batch-1 GEMV, sampled rows against the oracle).
+slice (routed as its own call); matrices of two to nine waves along K (the
+K-split form, two rows per pass); graph replay; full-size shapes (Q4_K and
+INT4 18944 x 3584, Q6_K 152064 x 3584, Q8_0 1536 x 1536 at M = 2, 3, 4; the
+INT4, Q5_K and Q4_K down projections 3584 x 18944 at M = 2, 3), all rows
+against the batch-1 GEMV, sampled rows against the oracle.
 """
 import numpy as np
 import pytest
@@ -96,6 +99,29 @@ def test_rows_groups_of_four(fmt, layout, x_dtype, batch, rows, nblk):
     _check(fmt, layout, rows, cols, batch, x_dtype, seed=1600 + rows + nblk)
 
 
+# (rows, 256-column blocks): two, three, five and nine waves along K for the
+# 4096-column formats (Q8_0, 2048 columns per wave: three, five and ten; its
+# widest shape is above its limit); more than eight waves take the
+# once-per-row route, which must agree as well
+SPLIT_SHAPES = [(67, 20), (9, 40), (33, 74), (5, 130)]
+
+
+@pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("batch", [2, 3, 5])
+@pytest.mark.parametrize("rows,nblk", SPLIT_SHAPES)
+def test_rows_split_k_equal_batch1_and_oracle(fmt, layout, x_dtype, batch, rows, nblk):
+    # matrices wider than a wave's K slice: the K-split form, two activation
+    # rows per pass (odd batches end in a half-used pass)
+    if fmt == "q4_k" and x_dtype == "bf16":
+        pytest.skip("Q4_K x bf16 batches of wide matrices run on the matrix cores (test_gpu_mfma.py)")
+    cols = nblk * 256
+    if fmt == "q8_0" and cols > 16 * 2048:
+        pytest.skip("above the Q8_0 GEMV's 32768-column limit")
+    say(f"multi-row split-K {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
+    _check(fmt, layout, rows, cols, batch, x_dtype, seed=1700 + rows + nblk)
+
+
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
 @pytest.mark.parametrize("batch", [2, 4])
 def test_rows_multi_matrix_launch(fmt, layout, batch):
@@ -120,7 +146,7 @@ def test_rows_multi_matrix_launch(fmt, layout, batch):
         alone = torch.empty(batch, w.rows, dtype=torch.float32, device=DEV)
         qmv.qmv_gemv(fmt, d, xd, "bf16", alone, w.rows, w.cols, batch)
         np.testing.assert_array_equal(got, alone.cpu().numpy())
-        if w.cols <= 4096:
+        if not (fmt == "q4_k" and w.cols > 4096):  # Q4_K x bf16 wide: the matrix cores
             ref = _per_row(fmt, d, w.rows, w.cols, xd, "bf16", batch).cpu().numpy()
             np.testing.assert_array_equal(got, ref)
         assert np.all(oracle.normwise_rel_err(got, oracle_y(w, x, "bf16")) <= TOL)
@@ -155,15 +181,31 @@ FULL = [("q4_k", 5, "bf16", "blocks"), ("q4_k", 5, "bf16", "planes"), ("int4_g12
         ("q6_k", 4, "bf16", "planes"), ("q8_0", 1, "f16", "blocks")]
 
 
+# the down projections (3584 x 18944, five waves along K): INT4 (fp16 x), Q5_K
+# (bf16 x), Q4_K (fp16 x); matrix index into the configuration's list
+FULL_SPLIT = [("int4_g128", 2, "f16", "blocks", 2), ("q5_k", 6, "bf16", "planes", 0),
+              ("q4_k", 3, "f16", "planes", 6)]
+
+
 @pytest.mark.parametrize("fmt,config,x_dtype,layout", FULL)
 @pytest.mark.parametrize("batch", [2, 3, 4])
 def test_rows_full_size(fmt, config, x_dtype, layout, batch):
+    _full_size(fmt, config, x_dtype, layout, batch, 0)
+
+
+@pytest.mark.parametrize("fmt,config,x_dtype,layout,mat", FULL_SPLIT)
+@pytest.mark.parametrize("batch", [2, 3])
+def test_rows_split_k_full_size(fmt, config, x_dtype, layout, mat, batch):
+    _full_size(fmt, config, x_dtype, layout, batch, mat)
+
+
+def _full_size(fmt, config, x_dtype, layout, batch, mat):
     cfg = CONFIGS[config]
-    rows, cols = cfg["mats"][0][1], cfg["mats"][0][2]
+    rows, cols = cfg["mats"][mat][1], cfg["mats"][mat][2]
     say(f"full-size multi-row {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
-    w = Weights(fmt, rows, cols, seed=weight_seed(config, 0))
+    w = Weights(fmt, rows, cols, seed=weight_seed(config, mat))
     desc = _desc(w, layout)
-    x = gen_x(batch, cols, x_dtype, x_seed(config, 0))
+    x = gen_x(batch, cols, x_dtype, x_seed(config, mat))
     xd = to_dev_x(x, x_dtype)
     y = torch.empty(batch, rows, dtype=torch.float32, device=DEV)
     qmv.qmv_gemv(fmt, desc, xd, x_dtype, y, rows, cols, batch)
