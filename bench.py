@@ -78,12 +78,13 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     weights in the plane layout take the plane policy; two or more fp16 or
     bf16 rows (Q4_K x bf16: 2-4 rows) against matrices within one wave's K
     slice (4096 columns, Q8_0 2048) -> the multi-row GEMV, against two to
-    eight waves along K -> its K-split form, except Q4_K x bf16)."""
+    eight waves along K -> its K-split form, except Q4_K x bf16 above two
+    rows)."""
     wave_cols = 2048 if fmt == "q8_0" else 4096
     kw_max = -(-max(cols_list) // wave_cols)
     q4k_bf16 = fmt == "q4_k" and x_dtype == "bf16"
     if (batch >= 2 and x_dtype in ("f16", "bf16") and not (q4k_bf16 and batch > 4)
-            and (kw_max == 1 or (2 <= kw_max <= 8 and not q4k_bf16))):
+            and (kw_max == 1 or (2 <= kw_max <= 8 and not (q4k_bf16 and batch > 2)))):
         pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q5_k": "Q5KPolicy", "q6_k": "Q6KPolicy",
                "int4_g128": "Int4G128Policy"}[fmt]
         if layout == "planes":

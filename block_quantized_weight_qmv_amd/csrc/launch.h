@@ -31,8 +31,9 @@ hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t b
 // one wave's K slice (4096 columns; Q8_0 2048) take one pass over the weights
 // per two or four rows (gemv_rows_kernel), matrices of 2..kRowsSplitMaxWaves
 // waves along K one pass per two rows (gemv_rows_split_kernel; every item of
-// one call of the same kind).  Q4_K bf16 batches above kRowsMaxBf16Batch go
-// to the matrix cores.
+// one call of the same kind).  Q4_K bf16 batches above kRowsMaxBf16Batch, and
+// Q4_K bf16 batches above two against matrices split along K, go to the
+// matrix cores.
 #ifndef QMV_ROWS_MAX_BF16_BATCH
 #define QMV_ROWS_MAX_BF16_BATCH 4
 #endif

@@ -8,8 +8,9 @@ paths and are checked exactly.  Shapes cover the three kernels behind the call
 (batch <= 16 with X in LDS: one to eight 16-row tiles per workgroup and more
 workgroups than CUs; batch <= 32 or K too long for LDS: K split over waves;
 larger batches: 64 x 64 tiles), ragged rows and batches, the smallest batch
-routed here (2: matrices wider than 4096 columns; narrower ones at batch 2-4
-take the multi-row GEMV), and the full-size batched workload (18944 x 3584, M = 4, 16,
+routed here (2: matrices wider than eight waves along K; narrower ones take
+the multi-row GEMV at batch 2, and at 3-4 those within one wave's K slice),
+and the full-size batched workload (18944 x 3584, M = 4, 16,
 64 and 512) on sampled rows.
 """
 import numpy as np
@@ -30,7 +31,7 @@ TOL = 2e-3
                                              (96, 2, 16), (65, 3, 17), (40, 2, 32), (33, 4, 33),
                                              (17, 74, 8), (300, 9, 24), (1, 1, 3), (16, 1, 31),
                                              (4100, 2, 5), (40000, 1, 9), (3, 16, 16), (33, 17, 12),
-                                             (70, 3, 2), (4100, 2, 2), (1, 1, 2), (17, 74, 2)])
+                                             (70, 3, 2), (4100, 2, 2), (1, 1, 2), (17, 74, 2), (5, 130, 2)])
 def test_mfma_matches_oracle(rows, nblk, batch):
     cols = nblk * 256
     say(f"mfma q4_k {rows}x{cols} batch {batch}")

@@ -3,8 +3,8 @@
 qmv_gemv routes two or more fp16 or bf16 activation rows (Q4_K x bf16: 2-4
 rows; larger bf16 batches take the matrix cores) against matrices within one
 wave's K slice (4096 columns; Q8_0 2048) to a GEMV that reads W once per two
-or four rows, and against matrices of two to eight waves along K (except
-Q4_K x bf16) to its K-split form, W once per two rows.  Each row's products and sums are the batch-1 GEMV's operations
+or four rows, and against matrices of two to eight waves along K (Q4_K x
+bf16: two rows only) to its K-split form, W once per two rows.  Each row's products and sums are the batch-1 GEMV's operations
 in the same order and the wave reduction adds in the same order, so every
 output row must equal the batch-1 GEMV of that activation row bit for bit,
 and the float64 oracle within the 2e-3 normwise gate.  Shapes: one block,
@@ -113,9 +113,10 @@ SPLIT_SHAPES = [(67, 20), (9, 40), (33, 74), (5, 130)]
 def test_rows_split_k_equal_batch1_and_oracle(fmt, layout, x_dtype, batch, rows, nblk):
     # matrices wider than a wave's K slice: the K-split form, two activation
     # rows per pass (odd batches end in a half-used pass)
-    if fmt == "q4_k" and x_dtype == "bf16":
-        pytest.skip("Q4_K x bf16 batches of wide matrices run on the matrix cores (test_gpu_mfma.py)")
     cols = nblk * 256
+    if fmt == "q4_k" and x_dtype == "bf16" and (batch > 2 or cols > 8 * 4096):
+        pytest.skip("Q4_K x bf16 of wide matrices above two rows, or above eight waves along K, "
+                    "runs on the matrix cores (test_gpu_mfma.py)")
     if fmt == "q8_0" and cols > 16 * 2048:
         pytest.skip("above the Q8_0 GEMV's 32768-column limit")
     say(f"multi-row split-K {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
@@ -146,7 +147,7 @@ def test_rows_multi_matrix_launch(fmt, layout, batch):
         alone = torch.empty(batch, w.rows, dtype=torch.float32, device=DEV)
         qmv.qmv_gemv(fmt, d, xd, "bf16", alone, w.rows, w.cols, batch)
         np.testing.assert_array_equal(got, alone.cpu().numpy())
-        if not (fmt == "q4_k" and w.cols > 4096):  # Q4_K x bf16 wide: the matrix cores
+        if not (fmt == "q4_k" and w.cols > 4096 and batch > 2):  # Q4_K x bf16 wide, M > 2: matrix cores
             ref = _per_row(fmt, d, w.rows, w.cols, xd, "bf16", batch).cpu().numpy()
             np.testing.assert_array_equal(got, ref)
         assert np.all(oracle.normwise_rel_err(got, oracle_y(w, x, "bf16")) <= TOL)
@@ -184,7 +185,7 @@ FULL = [("q4_k", 5, "bf16", "blocks"), ("q4_k", 5, "bf16", "planes"), ("int4_g12
 # the down projections (3584 x 18944, five waves along K): INT4 (fp16 x), Q5_K
 # (bf16 x), Q4_K (fp16 x); matrix index into the configuration's list
 FULL_SPLIT = [("int4_g128", 2, "f16", "blocks", 2), ("q5_k", 6, "bf16", "planes", 0),
-              ("q4_k", 3, "f16", "planes", 6)]
+              ("q4_k", 3, "f16", "planes", 6), ("q4_k", 3, "bf16", "planes", 6)]
 
 
 @pytest.mark.parametrize("fmt,config,x_dtype,layout", FULL)
@@ -196,6 +197,8 @@ def test_rows_full_size(fmt, config, x_dtype, layout, batch):
 @pytest.mark.parametrize("fmt,config,x_dtype,layout,mat", FULL_SPLIT)
 @pytest.mark.parametrize("batch", [2, 3])
 def test_rows_split_k_full_size(fmt, config, x_dtype, layout, mat, batch):
+    if fmt == "q4_k" and x_dtype == "bf16" and batch > 2:
+        pytest.skip("Q4_K x bf16 above two rows: the matrix cores (test_gpu_mfma.py)")
     _full_size(fmt, config, x_dtype, layout, batch, mat)
 
 
