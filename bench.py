@@ -75,25 +75,26 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     matrix-core kernels, chosen by batch and by
     whether X fits in LDS; otherwise waves per workgroup = max(4, widest K
     split), and the shared-activation kernel when no matrix splits K; Q4_K
-    weights in the plane layout take the plane policy; two or more fp16 or
-    bf16 rows (Q4_K x bf16: 2-4 rows) against matrices within one wave's K
-    slice (4096 columns, Q8_0 2048) -> the multi-row GEMV, against two to
-    eight waves along K -> its K-split form, except Q4_K x bf16 above two
-    rows)."""
+    weights in the plane layout take the plane policy; two or more rows
+    (Q4_K x bf16: 2-4 rows) against matrices within one wave's K slice (4096
+    columns, Q8_0 2048) -> the multi-row GEMV (fp32: two rows per pass);
+    fp16/bf16 against two to eight waves along K -> its K-split form, except
+    Q4_K x bf16 above two rows)."""
     wave_cols = 2048 if fmt == "q8_0" else 4096
     kw_max = -(-max(cols_list) // wave_cols)
     q4k_bf16 = fmt == "q4_k" and x_dtype == "bf16"
-    if (batch >= 2 and x_dtype in ("f16", "bf16") and not (q4k_bf16 and batch > 4)
-            and (kw_max == 1 or (2 <= kw_max <= 8 and not (q4k_bf16 and batch > 2)))):
+    half = x_dtype in ("f16", "bf16")
+    if (batch >= 2 and not (q4k_bf16 and batch > 4)
+            and (kw_max == 1 or (2 <= kw_max <= 8 and half and not (q4k_bf16 and batch > 2)))):
         pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q5_k": "Q5KPolicy", "q6_k": "Q6KPolicy",
                "int4_g128": "Int4G128Policy"}[fmt]
         if layout == "planes":
             pol = {"q4_k": "Q4KPlanesPolicy", "q5_k": "Q5KPlanesPolicy", "q6_k": "Q6KPlanesPolicy"}[fmt]
-        xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
+        xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
         if kw_max > 1:  # K-split form, two rows per pass
             r = 1 if fmt == "q5_k" else 2
             return f"qmv::gemv_rows_split_kernel<qmv::{pol}, {xt}, {r}, 2, {256 if max(kw_max, 4) <= 4 else 512}>"
-        return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, {'2, 2, 256, 2' if batch == 2 else '1, 3, 256, 4'}>"
+        return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, {'2, 2, 256, 2' if batch == 2 or not half else '1, 3, 256, 4'}>"
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:
         nb = max(cols_list) // 256
         pl = "true" if layout == "planes" else "false"

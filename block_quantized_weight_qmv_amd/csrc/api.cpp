@@ -262,16 +262,16 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   // matrix-core kernel, one launch per matrix (the GEMV path would read the
   // weights once per activation row).
   const bool planes = items[0].W->layout == QMV_LAYOUT_PLANES;
-  // Two or more fp16 or bf16 rows (Q4_K bf16: up to kRowsMaxBf16Batch): the
-  // matrices within one wave's K slice take the multi-row GEMV (one launch,
-  // one pass over the weights per two or four activation rows), those of two
-  // to eight waves along K its K-split form (one launch, one pass per two
-  // rows; Q4_K x bf16 above two rows keeps the matrix cores), the wider ones
-  // the GEMV once per row.  Every item's result is the same as that of the item called
-  // alone.
+  // Two or more rows (Q4_K bf16: up to kRowsMaxBf16Batch): the matrices
+  // within one wave's K slice take the multi-row GEMV (one launch, one pass
+  // over the weights per two or four activation rows, two for fp32), those of
+  // two to eight waves along K its K-split form (fp16/bf16; one launch, one
+  // pass per two rows; Q4_K x bf16 above two rows keeps the matrix cores),
+  // the wider ones the GEMV once per row.  Every item's result is the same as
+  // that of the item called alone.
   const bool half_x = x_dtype == QMV_F16 || x_dtype == QMV_BF16;
   const int64_t wave_cols = fmt == QMV_Q8_0 ? 2048 : 4096;
-  if (half_x && batch >= 2 &&
+  if (batch >= 2 &&
       !(fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch > qmv::kRowsMaxBf16Batch)) {
     qmv::GemvCall narrow[qmv::kMaxItems], split[qmv::kMaxItems], wide[qmv::kMaxItems];
     int nn = 0, ns = 0, nw = 0;
@@ -283,7 +283,7 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     for (int i = 0; i < n; ++i) {
       if (calls[i].W->cols <= wave_cols)
         narrow[nn++] = calls[i];
-      else if (calls[i].W->cols <= qmv::kRowsSplitMaxWaves * wave_cols && !mfma_split)
+      else if (calls[i].W->cols <= qmv::kRowsSplitMaxWaves * wave_cols && half_x && !mfma_split)
         split[ns++] = calls[i];
       else
         wide[nw++] = calls[i];

@@ -156,12 +156,11 @@ struct Int4G128Policy {
     return out;
   }
 
-  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the code masks
-  // are computed once, then each row's sums follow dot's operations in dot's
-  // order, so out[m] equals dot(f, s[m]) bit for bit.
+  // dot<XT> for NBR activation rows at once: the code masks are computed
+  // once, then each row's sums follow dot's operations in dot's order, so
+  // out[m] equals dot(f, s[m]) bit for bit.
   template <typename XT, int NBR>
   __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
-    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
 #pragma unroll
     for (int m = 0; m < NBR; ++m) out[m] = 0.f;
 #pragma unroll
@@ -177,17 +176,34 @@ struct Int4G128Policy {
         const uint32_t e = w0 & 0x00F000F0u, g = w8 & 0x00F000F0u;
 #pragma unroll
         for (int m = 0; m < NBR; ++m) {
-          const h2_t* x = s[m].h + 16 * hf + 4 * i;
-          se[m] = dot2_lo_hi(a, x[0], se[m]);
-          se[m] = dot2_lo_hi(b, x[1], se[m]);
-          so[m] = dot2_lo_hi(e, x[2], so[m]);
-          so[m] = dot2_lo_hi(g, x[3], so[m]);
+          if constexpr (__is_same(XT, float)) {
+            const float* x = s[m].v + 32 * hf + 8 * i;
+            se[m] = fma_lo(a, x[0], se[m]);
+            se[m] = fma_lo(b, x[2], se[m]);
+            se[m] = fma_hi(a, x[4], se[m]);
+            se[m] = fma_hi(b, x[6], se[m]);
+            so[m] = fma_lo(e, x[1], so[m]);
+            so[m] = fma_lo(g, x[3], so[m]);
+            so[m] = fma_hi(e, x[5], so[m]);
+            so[m] = fma_hi(g, x[7], so[m]);
+          } else {
+            const h2_t* x = s[m].h + 16 * hf + 4 * i;
+            se[m] = dot2_lo_hi(a, x[0], se[m]);
+            se[m] = dot2_lo_hi(b, x[1], se[m]);
+            so[m] = dot2_lo_hi(e, x[2], so[m]);
+            so[m] = dot2_lo_hi(g, x[3], so[m]);
+          }
         }
       }
       const float sc = f16_to_f32(f.sb[hf]);
 #pragma unroll
       for (int m = 0; m < NBR; ++m) {
-        const float t = fmaf(s[m].xs, fmaf(so[m], 0.0625f, se[m]), -8.f * s[m].s[hf]);
+        float xs;
+        if constexpr (__is_same(XT, float))
+          xs = kTwo24;
+        else
+          xs = s[m].xs;
+        const float t = fmaf(xs, fmaf(so[m], 0.0625f, se[m]), -8.f * s[m].s[hf]);
         out[m] = fmaf(sc, t, out[m]);
       }
     }

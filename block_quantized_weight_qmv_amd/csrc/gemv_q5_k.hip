@@ -153,12 +153,11 @@ struct Q5KPolicy {
     return fmaf(d, t, -dmin * mm);
   }
 
-  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the header decode
-  // and the five-bit codes are formed once, then each row's sums follow dot's
+  // dot<XT> for NBR activation rows at once: the header decode and the
+  // five-bit codes are formed once, then each row's sums follow dot's
   // operations in dot's order, so out[m] equals dot(f, s[m]) bit for bit.
   template <typename XT, int NBR>
   __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
-    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
     const uint32_t t1 = f.hd.y >> sh, t2 = f.hd.z >> sh, t3 = f.hd.w >> sh;
     const uint32_t sc = ((hi ? t3 : t1) & mask_a) | ((t1 >> 2) & mask_b);
     const uint32_t mn = ((hi ? (t3 >> 4) : t2) & mask_a) | ((t2 >> 2) & mask_b);
@@ -179,15 +178,32 @@ struct Q5KPolicy {
       const uint32_t g = (w8 & 0x00F000F0u) | (__builtin_rotateright32(h[i], rg) & 0x01000100u);
 #pragma unroll
       for (int m = 0; m < NBR; ++m) {
-        s0[m] = dot2_lo_hi(a, s[m].h[4 * i + 0], s0[m]);
-        s0[m] = dot2_lo_hi(b, s[m].h[4 * i + 1], s0[m]);
-        s1[m] = dot2_lo_hi(e, s[m].h[4 * i + 2], s1[m]);
-        s1[m] = dot2_lo_hi(g, s[m].h[4 * i + 3], s1[m]);
+        if constexpr (__is_same(XT, float)) {
+          const float* x0 = s[m].v + 4 * i;
+          const float* x1 = s[m].v + 32 + 4 * i;
+          s0[m] = fma_lo(a, x0[0], s0[m]);
+          s0[m] = fma_lo(b, x0[1], s0[m]);
+          s0[m] = fma_hi(a, x0[2], s0[m]);
+          s0[m] = fma_hi(b, x0[3], s0[m]);
+          s1[m] = fma_lo(e, x1[0], s1[m]);
+          s1[m] = fma_lo(g, x1[1], s1[m]);
+          s1[m] = fma_hi(e, x1[2], s1[m]);
+          s1[m] = fma_hi(g, x1[3], s1[m]);
+        } else {
+          s0[m] = dot2_lo_hi(a, s[m].h[4 * i + 0], s0[m]);
+          s0[m] = dot2_lo_hi(b, s[m].h[4 * i + 1], s0[m]);
+          s1[m] = dot2_lo_hi(e, s[m].h[4 * i + 2], s1[m]);
+          s1[m] = dot2_lo_hi(g, s[m].h[4 * i + 3], s1[m]);
+        }
       }
     }
 #pragma unroll
     for (int m = 0; m < NBR; ++m) {
-      const float d = d16 * s[m].xs;
+      float d;
+      if constexpr (__is_same(XT, float))
+        d = d16 * kTwo24;
+      else
+        d = d16 * s[m].xs;
       const float t = fmaf(cvt_ubyte<1>(sc) * 0.0625f, s1[m], cvt_ubyte<0>(sc) * s0[m]);
       const float mm = fmaf(cvt_ubyte<1>(mn), s[m].s1, cvt_ubyte<0>(mn) * s[m].s0);
       out[m] = fmaf(d, t, -dmin * mm);

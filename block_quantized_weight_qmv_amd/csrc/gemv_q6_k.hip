@@ -149,12 +149,11 @@ struct Q6KPolicy {
     return f16_to_f32(f.d) * t;
   }
 
-  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the 6-bit codes
-  // and the sub-scales are assembled once, then each row's sums follow dot's
+  // dot<XT> for NBR activation rows at once: the 6-bit codes and the
+  // sub-scales are assembled once, then each row's sums follow dot's
   // operations in dot's order, so out[m] equals dot(f, s[m]) bit for bit.
   template <typename XT, int NBR>
   __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
-    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
     const uint32_t la[4] = {f.la.x, f.la.y, f.la.z, f.la.w};
     const uint32_t lb[4] = {f.lb.x, f.lb.y, f.lb.z, f.lb.w};
     const uint32_t qh[4] = {f.qh.x, f.qh.y, f.qh.z, f.qh.w};
@@ -175,8 +174,16 @@ struct Q6KPolicy {
         const uint32_t a = q6[g] & 0x003F003Fu, b = (q6[g] >> 8) & 0x003F003Fu;
 #pragma unroll
         for (int m = 0; m < NBR; ++m) {
-          acc[m][g] = dot2_lo_hi(a, s[m].h[8 * g + 2 * k], acc[m][g]);
-          acc[m][g] = dot2_lo_hi(b, s[m].h[8 * g + 2 * k + 1], acc[m][g]);
+          if constexpr (__is_same(XT, float)) {
+            const float* x = s[m].v + 16 * g + 4 * k;
+            acc[m][g] = fma_lo(a, x[0], acc[m][g]);
+            acc[m][g] = fma_lo(b, x[1], acc[m][g]);
+            acc[m][g] = fma_hi(a, x[2], acc[m][g]);
+            acc[m][g] = fma_hi(b, x[3], acc[m][g]);
+          } else {
+            acc[m][g] = dot2_lo_hi(a, s[m].h[8 * g + 2 * k], acc[m][g]);
+            acc[m][g] = dot2_lo_hi(b, s[m].h[8 * g + 2 * k + 1], acc[m][g]);
+          }
         }
       }
     }
@@ -189,9 +196,14 @@ struct Q6KPolicy {
     const float d = f16_to_f32(f.d);
 #pragma unroll
     for (int m = 0; m < NBR; ++m) {
+      float xs;
+      if constexpr (__is_same(XT, float))
+        xs = kTwo24;
+      else
+        xs = s[m].xs;
       float t = 0.f;
 #pragma unroll
-      for (int g = 0; g < 4; ++g) t = fmaf(scf[g], fmaf(s[m].xs, acc[m][g], -32.f * s[m].s[g]), t);
+      for (int g = 0; g < 4; ++g) t = fmaf(scf[g], fmaf(xs, acc[m][g], -32.f * s[m].s[g]), t);
       out[m] = d * t;
     }
   }

@@ -112,12 +112,11 @@ struct Q80Policy {
     return f16_to_f32(f.d) * fmaf(xs, acc, -128.f * s.s);
   }
 
-  // dot<XT> for NBR activation rows (fp16 or bf16) at once: the offset codes
-  // are formed once, then each row's sum follows dot's operations in dot's
-  // order, so out[m] equals dot(f, s[m]) bit for bit.
+  // dot<XT> for NBR activation rows at once: the offset codes are formed
+  // once, then each row's sum follows dot's operations in dot's order, so
+  // out[m] equals dot(f, s[m]) bit for bit.
   template <typename XT, int NBR>
   __device__ void dot_rows(const Frag& f, const XSliceT<XT>* s, float* out) const {
-    static_assert(!__is_same(XT, float), "multi-row products take fp16 or bf16 activations");
     const uint32_t q[8] = {f.qa.x, f.qa.y, f.qa.z, f.qa.w, f.qb.x, f.qb.y, f.qb.z, f.qb.w};
     float acc[NBR];
 #pragma unroll
@@ -128,13 +127,27 @@ struct Q80Policy {
       const uint32_t a = u & 0x00FF00FFu, b = (u >> 8) & 0x00FF00FFu;
 #pragma unroll
       for (int m = 0; m < NBR; ++m) {
-        acc[m] = dot2_lo_hi(a, s[m].h[2 * i], acc[m]);
-        acc[m] = dot2_lo_hi(b, s[m].h[2 * i + 1], acc[m]);
+        if constexpr (__is_same(XT, float)) {
+          acc[m] = fma_lo(a, s[m].v[4 * i + 0], acc[m]);
+          acc[m] = fma_lo(b, s[m].v[4 * i + 1], acc[m]);
+          acc[m] = fma_hi(a, s[m].v[4 * i + 2], acc[m]);
+          acc[m] = fma_hi(b, s[m].v[4 * i + 3], acc[m]);
+        } else {
+          acc[m] = dot2_lo_hi(a, s[m].h[2 * i], acc[m]);
+          acc[m] = dot2_lo_hi(b, s[m].h[2 * i + 1], acc[m]);
+        }
       }
     }
     const float d = f16_to_f32(f.d);
 #pragma unroll
-    for (int m = 0; m < NBR; ++m) out[m] = d * fmaf(s[m].xs, acc[m], -128.f * s[m].s);
+    for (int m = 0; m < NBR; ++m) {
+      float xs;
+      if constexpr (__is_same(XT, float))
+        xs = kTwo24;
+      else
+        xs = s[m].xs;
+      out[m] = d * fmaf(xs, acc[m], -128.f * s[m].s);
+    }
   }
 };
 

@@ -663,7 +663,8 @@ hipError_t launch_rows_split(const GemvCall* calls, int n, int64_t batch, hipStr
 template <class P>
 hipError_t launch_gemv_rows_split(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                                   hipStream_t stream) {
-  if (batch < 2) return hipErrorInvalidValue;
+  // (fp32: two rows' raw activations and slices do not fit beside the tiles)
+  if (batch < 2 || x_dtype == QMV_F32) return hipErrorInvalidValue;
   const int kw = max_kw<P>(calls, n);
   if (kw < 2 || kw > 8) return hipErrorInvalidValue;
   switch (x_dtype) {
@@ -677,10 +678,11 @@ hipError_t launch_gemv_rows_split(const GemvCall* calls, int n, int x_dtype, int
   }
 }
 
-// Batches of two or more fp16 or bf16 activation rows: against matrices no
-// wider than one wave's K slice, two rows in one pass over W, otherwise
-// groups of four rows, one pass over W per group; against matrices split along
-// K (two to eight waves, every matrix of the launch), one pass per two rows.
+// Batches of two or more activation rows.  Against matrices no wider than one
+// wave's K slice: fp16 and bf16 two rows in one pass over W, otherwise groups
+// of four rows, one pass per group; fp32 (66-word slices) groups of two rows.
+// Against matrices split along K (two to eight waves, every matrix of the
+// launch), fp16 and bf16 only: one pass per two rows.
 template <class P>
 hipError_t launch_gemv_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t stream) {
@@ -688,6 +690,8 @@ hipError_t launch_gemv_rows(const GemvCall* calls, int n, int x_dtype, int64_t b
   if (max_kw<P>(calls, n) > 1) return launch_gemv_rows_split<P>(calls, n, x_dtype, batch, stream);
   const bool two = batch == 2;
   switch (x_dtype) {
+    case QMV_F32:  // 66-word slices: two rows per pass
+      return launch_rows<P, float, 2, 2>(calls, n, batch, stream);
     case QMV_F16:
       return two ? launch_rows<P, _Float16, 2, 2>(calls, n, batch, stream)
                  : launch_rows<P, _Float16, 1, 4>(calls, n, batch, stream);

@@ -207,12 +207,12 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * fmt, rows and cols must repeat the descriptor's (QMV_ERR_FORMAT otherwise),
  * x is [batch][cols] of x_dtype (QMV_F32, QMV_F16 or QMV_BF16), y is
  * [batch][rows] fp32; x and y device pointers, 16-byte aligned.  Enqueues on
- * `stream` and returns; legal inside HIP stream capture.  batch >= 2 fp16 or
- * bf16 rows (Q4_K x bf16: 2..4 rows) run the multi-row GEMV in every format:
- * weights read once per two or four activation rows (cols <= 4096; Q8_0:
- * 2048), or once per two rows for up to eight times that width (not Q4_K x
- * bf16), and each output row equal bit for bit to the batch-1 call on that
- * activation row.  Other Q4_K x bf16 calls with batch >= 2 run the
+ * `stream` and returns; legal inside HIP stream capture.  batch >= 2 rows
+ * (Q4_K x bf16: 2..4 rows) run the multi-row GEMV in every format: weights
+ * read once per two or four activation rows (fp32: two) for cols <= 4096
+ * (Q8_0: 2048), and, for fp16/bf16 rows, once per two rows up to eight times
+ * that width (Q4_K x bf16: at two rows); each output row equals bit for bit
+ * the batch-1 call on that activation row.  Other Q4_K x bf16 calls with batch >= 2 run the
  * matrix-core path (weights read once for up to 16 activation rows, once per
  * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
  * independent of timing).  Otherwise each activation row is a GEMV over the

@@ -118,7 +118,7 @@ def test_more_than_one_gpu_is_refused():
 
 @pytest.mark.parametrize("config,batch,x_dtype", [(2, 4, None), (2, 3, "bf16"), (4, 4, "bf16"), (4, 2, "f16"),
                                                   (3, 2, "f16"), (5, 4, "f16"), (5, 8, "f16"), (1, 4, "f16"),
-                                                  (1, 2, "bf16")])
+                                                  (1, 2, "bf16"), (3, 2, None), (4, 4, None), (5, 3, "f32")])
 def test_small_batch_overrides_name_library_kernels(config, batch, x_dtype):
     # --batch on any configuration and --x-dtype: the multi-row GEMV for the
     # formats that have one, named as the library exports it

@@ -1,10 +1,11 @@
-"""Every format with several fp16 or bf16 activation rows: the multi-row GEMV.
+"""Every format with several activation rows: the multi-row GEMV.
 
-qmv_gemv routes two or more fp16 or bf16 activation rows (Q4_K x bf16: 2-4
-rows; larger bf16 batches take the matrix cores) against matrices within one
-wave's K slice (4096 columns; Q8_0 2048) to a GEMV that reads W once per two
-or four rows, and against matrices of two to eight waves along K (Q4_K x
-bf16: two rows only) to its K-split form, W once per two rows.  Each row's products and sums are the batch-1 GEMV's operations
+qmv_gemv routes two or more activation rows (Q4_K x bf16: 2-4 rows; larger
+bf16 batches take the matrix cores) against matrices within one wave's K
+slice (4096 columns; Q8_0 2048) to a GEMV that reads W once per two or four
+rows (fp32: two), and fp16/bf16 rows against matrices of two to eight waves
+along K (Q4_K x bf16: two rows only) to its K-split form, W once per two
+rows; fp32 rows against those run the GEMV once per row.  Each row's products and sums are the batch-1 GEMV's operations
 in the same order and the wave reduction adds in the same order, so every
 output row must equal the batch-1 GEMV of that activation row bit for bit,
 and the float64 oracle within the 2e-3 normwise gate.  Shapes: one block,
@@ -75,7 +76,7 @@ def _check(fmt, layout, rows, cols, batch, x_dtype, seed):
 
 
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
-@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("batch", [2, 3, 4])
 @pytest.mark.parametrize("rows,nblk", SHAPES)
 def test_rows_equal_batch1_and_oracle(fmt, layout, x_dtype, batch, rows, nblk):
@@ -85,13 +86,13 @@ def test_rows_equal_batch1_and_oracle(fmt, layout, x_dtype, batch, rows, nblk):
 
 
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
-@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("batch", [5, 8, 9, 30])
 @pytest.mark.parametrize("rows,nblk", [(3, 1), (67, 14), (130, 2)])
 def test_rows_groups_of_four(fmt, layout, x_dtype, batch, rows, nblk):
-    # batches above four: one pass over W per group of four rows, the last
-    # group partial unless four divides the batch (Q4_K x bf16 batches above
-    # four take the matrix cores and are not this kernel's)
+    # batches above four: one pass over W per group of four rows (fp32: two),
+    # the last group partial unless the group size divides the batch (Q4_K x
+    # bf16 batches above four take the matrix cores and are not this kernel's)
     if fmt == "q4_k" and x_dtype == "bf16":
         pytest.skip("Q4_K x bf16 batches above four run on the matrix cores (test_gpu_mfma.py)")
     cols = nblk * 256
@@ -107,7 +108,7 @@ SPLIT_SHAPES = [(67, 20), (9, 40), (33, 74), (5, 130)]
 
 
 @pytest.mark.parametrize("fmt,layout", FMT_LAYOUTS)
-@pytest.mark.parametrize("x_dtype", ["f16", "bf16"])
+@pytest.mark.parametrize("x_dtype", ["f16", "bf16", "f32"])
 @pytest.mark.parametrize("batch", [2, 3, 5])
 @pytest.mark.parametrize("rows,nblk", SPLIT_SHAPES)
 def test_rows_split_k_equal_batch1_and_oracle(fmt, layout, x_dtype, batch, rows, nblk):
@@ -176,10 +177,11 @@ def test_rows_graph_replay(fmt):
         assert torch.equal(yg, y0)
 
 
-# full-size shapes: the Q4_K FFN gate (bf16 x), the INT4 FFN gate (fp16 x), the
-# Q6_K lm-head (bf16 x), the Q8_0 1536 x 1536 matrix (fp16 x)
+# full-size shapes: the Q4_K FFN gate (bf16 and fp32 x), the INT4 FFN gate (fp16
+# x), the Q6_K lm-head (bf16 and fp32 x), the Q8_0 1536 x 1536 matrix (fp16 x)
 FULL = [("q4_k", 5, "bf16", "blocks"), ("q4_k", 5, "bf16", "planes"), ("int4_g128", 2, "f16", "blocks"),
-        ("q6_k", 4, "bf16", "planes"), ("q8_0", 1, "f16", "blocks")]
+        ("q6_k", 4, "bf16", "planes"), ("q8_0", 1, "f16", "blocks"), ("q4_k", 5, "f32", "planes"),
+        ("q6_k", 4, "f32", "planes")]
 
 
 # the down projections (3584 x 18944, five waves along K): INT4 (fp16 x), Q5_K
