@@ -225,3 +225,24 @@ def _full_size(fmt, config, x_dtype, layout, batch, mat):
     assert np.all(err <= TOL), err
     del w, desc
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("fmt", ["q4_k", "int4_g128"])
+@pytest.mark.parametrize("x_dtype,batch", [("f16", 3), ("bf16", 2), ("f32", 2)])
+def test_rows_sixteen_items(fmt, x_dtype, batch):
+    # the largest launch: 16 matrices, narrow ones and ones split along K
+    # (fp32: those run once per row), each equal to its own call bitwise
+    say(f"multi-row 16 items {fmt} batch {batch} x {x_dtype}")
+    ws, items, ys = [], [], []
+    for i in range(16):
+        rows, nblk = 3 + 13 * i, (5 if i % 3 else 20)
+        w = Weights(fmt, rows, nblk * 256, seed=1800 + i)
+        x = to_dev_x(gen_x(batch, nblk * 256, x_dtype, seed=180 + i), x_dtype)
+        y = torch.full((batch, rows), -2.0, dtype=torch.float32, device=DEV)
+        ws.append((w, x))
+        ys.append(y)
+        items.append((w.desc, x, y))
+    qmv.qmv_gemv_multi(fmt, x_dtype, batch, items)
+    for (w, x), y in zip(ws, ys):
+        alone = w.gemv(x, x_dtype, batch)
+        assert torch.equal(y, alone), (w.rows, w.cols)
