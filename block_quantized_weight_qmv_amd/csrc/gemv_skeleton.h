@@ -39,8 +39,10 @@
 // A format policy P provides kColsPerWave, kXElems, XSliceT<XT> (the lane's
 // activations as the policy multiplies activations of type XT), Frag, a
 // constructor (w, scales_offset, cols, kslot, lane), load_x_raw(x, uint4*),
-// finish_x<XT>(raw, XSliceT<XT>&), load(row, Frag&) and
-// dot<XT>(Frag, XSliceT<XT>) -> this lane's partial of W[row] . x.
+// finish_x<XT>(raw, XSliceT<XT>&), load(row, Frag&),
+// dot<XT>(Frag, XSliceT<XT>) -> this lane's partial of W[row] . x, and, for
+// the multi-row kernels below, dot_rows<XT, NBR>(Frag, const XSliceT<XT>*,
+// float* out) -> out[m] = dot<XT>(Frag, slice m), bit for bit.
 #pragma once
 
 #include "device_util.h"
@@ -259,10 +261,10 @@ gemv_kernel(const GemvLaunch args) {
   }
 }
 
-// Small activation batches (2-4 rows) against one wave's K slice: the work
-// split and tile pipeline of the shared-activation gemv_kernel, but each wave
-// carries NBR activation rows, so W is read once for all of them instead of
-// once per row.  All waves of a workgroup need the same NBR activation slices
+// Batches of activation rows against matrices within one wave's K slice: the
+// work split and tile pipeline of the shared-activation gemv_kernel, but each
+// wave carries NBR (2 or 4) activation rows, so W is read once per NBR rows
+// instead of once per row.  All waves of a workgroup need the same NBR activation slices
 // (every matrix fits one wave's K slice): wave m < NBR reads row m from global
 // memory, converts it and leaves each lane's slice in LDS (word k of lane l at
 // [m][k][l]); after a barrier every wave reads all NBR slices.

@@ -27,11 +27,11 @@ hipError_t gemv_q4_k(const GemvCall* calls, int n, int x_dtype, int64_t batch, h
 // Q4_K / Q5_K / Q6_K weights in the plane layout (planes.h); every item in that layout.
 hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                             hipStream_t s);
-// Every format with two or more fp16 or bf16 activation rows: matrices within
-// one wave's K slice (4096 columns; Q8_0 2048) take one pass over the weights
-// per two or four rows (gemv_rows_kernel), matrices of 2..kRowsSplitMaxWaves
-// waves along K one pass per two rows (gemv_rows_split_kernel; every item of
-// one call of the same kind).  Q4_K bf16 batches above kRowsMaxBf16Batch, and
+// Every format with two or more activation rows: matrices within one wave's K
+// slice (4096 columns; Q8_0 2048) take one pass over the weights per two or
+// four rows (gemv_rows_kernel; fp32: two), and, for fp16/bf16 rows, matrices
+// of 2..kRowsSplitMaxWaves waves along K one pass per two rows
+// (gemv_rows_split_kernel; every item of one call of the same kind).  Q4_K bf16 batches above kRowsMaxBf16Batch, and
 // Q4_K bf16 batches above two against matrices split along K, go to the
 // matrix cores.
 #ifndef QMV_ROWS_MAX_BF16_BATCH
