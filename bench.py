@@ -94,7 +94,8 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         if kw_max > 1:  # K-split form, two rows per pass
             r = 1 if fmt == "q5_k" else 2
             return f"qmv::gemv_rows_split_kernel<qmv::{pol}, {xt}, {r}, 2, {256 if max(kw_max, 4) <= 4 else 512}>"
-        return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, {'2, 2, 256, 2' if batch == 2 or not half else '1, 3, 256, 4'}>"
+        shape = "2, 2, 256, 2" if batch == 2 or not half else ("1, 3, 256, 3" if batch == 3 else "1, 3, 256, 4")
+        return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, {shape}>"
     if fmt == "q4_k" and x_dtype == "bf16" and batch >= 2:
         nb = max(cols_list) // 256
         pl = "true" if layout == "planes" else "false"

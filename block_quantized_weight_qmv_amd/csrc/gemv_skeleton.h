@@ -331,10 +331,14 @@ gemv_rows_kernel(const GemvLaunch args, int batch) {
   }
 
   auto finish = [&](const typename P::Frag* fr, int row0) {
-    float acc[R * NBR];
+    // three partials (one weight row, three activation rows) are reduced as
+    // four, the fourth zero and not stored
+    constexpr int kParts = R * NBR == 3 ? 4 : R * NBR;
+    float acc[kParts];
+    if constexpr (kParts > R * NBR) acc[kParts - 1] = 0.f;
 #pragma unroll
     for (int r = 0; r < R; ++r) pol.template dot_rows<XT, NBR>(fr[r], xs, acc + r * NBR);
-    const float t = reduce_rows<R * NBR>(acc, lane);
+    const float t = reduce_rows<kParts>(acc, lane);
     const int r = lane / NBR, mi = lane - (lane / NBR) * NBR;
     if (lane < R * NBR && row0 + r < r_end && mb0 + mi < batch)
       m.y[static_cast<size_t>(mb0 + mi) * m.rows + row0 + r] = t;
@@ -593,11 +597,11 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
 }
 
 // Tiles in flight per wave of gemv_rows_kernel: two with two activation rows
-// (R = 2), three with four (R = 1).  (Measured on the 18944 x 3584 FFN shape:
-// deeper pipelines were slower at both sizes, two tiles of four rows 0.3 us
-// slower.)
+// (R = 2), three with three or four (R = 1).  (Measured on the 18944 x 3584
+// FFN shape: deeper pipelines were slower at both sizes, two tiles of four
+// rows 0.3 us slower.)
 template <int NBR>
-constexpr int rows_tiles_in_flight() { return NBR == 4 ? 3 : 2; }
+constexpr int rows_tiles_in_flight() { return NBR >= 3 ? 3 : 2; }
 
 // Launch of gemv_rows_kernel: every matrix within one wave's K slice, NBR
 // activation rows per wave (R rows per tile, R x NBR <= 4), four-wave
@@ -681,8 +685,9 @@ hipError_t launch_gemv_rows_split(const GemvCall* calls, int n, int x_dtype, int
 }
 
 // Batches of two or more activation rows.  Against matrices no wider than one
-// wave's K slice: fp16 and bf16 two rows in one pass over W, otherwise groups
-// of four rows, one pass per group; fp32 (66-word slices) groups of two rows.
+// wave's K slice: fp16 and bf16 two or three rows in one pass over W,
+// otherwise groups of four rows, one pass per group; fp32 (66-word slices)
+// groups of two rows.
 // Against matrices split along K (two to eight waves, every matrix of the
 // launch), fp16 and bf16 only: one pass per two rows.
 template <class P>
@@ -690,16 +695,17 @@ hipError_t launch_gemv_rows(const GemvCall* calls, int n, int x_dtype, int64_t b
                             hipStream_t stream) {
   if (batch < 2) return hipErrorInvalidValue;
   if (max_kw<P>(calls, n) > 1) return launch_gemv_rows_split<P>(calls, n, x_dtype, batch, stream);
-  const bool two = batch == 2;
   switch (x_dtype) {
     case QMV_F32:  // 66-word slices: two rows per pass
       return launch_rows<P, float, 2, 2>(calls, n, batch, stream);
     case QMV_F16:
-      return two ? launch_rows<P, _Float16, 2, 2>(calls, n, batch, stream)
-                 : launch_rows<P, _Float16, 1, 4>(calls, n, batch, stream);
+      return batch == 2   ? launch_rows<P, _Float16, 2, 2>(calls, n, batch, stream)
+             : batch == 3 ? launch_rows<P, _Float16, 1, 3>(calls, n, batch, stream)
+                          : launch_rows<P, _Float16, 1, 4>(calls, n, batch, stream);
     case QMV_BF16:
-      return two ? launch_rows<P, bf16_t, 2, 2>(calls, n, batch, stream)
-                 : launch_rows<P, bf16_t, 1, 4>(calls, n, batch, stream);
+      return batch == 2   ? launch_rows<P, bf16_t, 2, 2>(calls, n, batch, stream)
+             : batch == 3 ? launch_rows<P, bf16_t, 1, 3>(calls, n, batch, stream)
+                          : launch_rows<P, bf16_t, 1, 4>(calls, n, batch, stream);
     default: return hipErrorInvalidValue;
   }
 }
