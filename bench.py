@@ -43,7 +43,7 @@ CSRC = os.path.join(ROOT, "block_quantized_weight_qmv_amd", "csrc")
 _KERNEL_SOURCES = {
     "gemv_kernel": ["gemv_skeleton.h", "device_util.h"],
     "gemv_rows_kernel": ["gemv_skeleton.h", "device_util.h"],
-    "gemm_q4_k_bf16_stream": ["gemm_q4_k_mfma.hip", "device_util.h"],
+    "gemm_q4_k_stream": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_bf16_ksplit": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_bf16_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
 }
@@ -79,7 +79,12 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     (Q4_K x bf16: 2-4 rows) against matrices within one wave's K slice (4096
     columns, Q8_0 2048) -> the multi-row GEMV (fp32: two rows per pass);
     fp16/bf16 against two to eight waves along K -> its K-split form, except
-    Q4_K x bf16 above two rows)."""
+    Q4_K x bf16 above two rows; Q4_K x fp16 at 5-16 rows with X in LDS -> the
+    fp16 matrix-core stream kernel)."""
+    nb_max = max(cols_list) // 256
+    if (fmt == "q4_k" and x_dtype == "f16" and 5 <= batch <= 16
+            and nb_max * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024):  # fp16 X fits the stream kernel's LDS
+        return f"qmv::gemm_q4_k_stream<{'true' if layout == 'planes' else 'false'}, true>"
     wave_cols = 2048 if fmt == "q8_0" else 4096
     kw_max = -(-max(cols_list) // wave_cols)
     q4k_bf16 = fmt == "q4_k" and x_dtype == "bf16"
@@ -100,7 +105,7 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         nb = max(cols_list) // 256
         pl = "true" if layout == "planes" else "false"
         if batch <= 16 and nb * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024:  # X fits in LDS
-            return f"qmv::gemm_q4_k_bf16_stream<{pl}>"
+            return f"qmv::gemm_q4_k_stream<{pl}, false>"
         if batch <= 16:
             return f"qmv::gemm_q4_k_bf16_ksplit<1, 1, {pl}>"
         if batch <= 32:
@@ -208,7 +213,7 @@ def default_layout(config: int, batch: int | None = None, x_dtype: str | None = 
     b = batch or cfg["batch"][0]
     xd = x_dtype or cfg["x_dtype"]
     # Q4_K x bf16 batches of 5 or more run on the matrix cores; 2-4 rows take the multi-row GEMV
-    gemv = not (cfg["fmt"] == "q4_k" and xd == "bf16" and b >= 5)
+    gemv = not (cfg["fmt"] == "q4_k" and ((xd == "bf16" and b >= 5) or (xd == "f16" and 5 <= b <= 16)))
     return "planes" if cfg["fmt"] in ("q4_k", "q5_k", "q6_k") and gemv else "blocks"
 
 

@@ -274,14 +274,20 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   if (batch >= 2 &&
       !(fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch > qmv::kRowsMaxBf16Batch)) {
     qmv::GemvCall narrow[qmv::kMaxItems], split[qmv::kMaxItems], wide[qmv::kMaxItems];
-    int nn = 0, ns = 0, nw = 0;
+    qmv::GemvCall mfma16[qmv::kMaxItems];
+    int nn = 0, ns = 0, nw = 0, nm = 0;
+    // Q4_K x fp16, 5..16 rows, X within the streaming kernel's LDS copy: the
+    // matrix cores with fp16 operands
+    const bool f16_mfma = fmt == QMV_Q4_K && x_dtype == QMV_F16 && batch >= qmv::kMfmaMinF16Batch;
     // Q4_K x bf16 against wide matrices: the K-split form for two rows, the
     // matrix cores above (3584 x 18944: 14.7 against 24.8 us at two rows,
     // 27.0 against 25.1 us at three)
     const bool q4k_mfma = fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch;
     const bool mfma_split = q4k_mfma && batch > 2;
     for (int i = 0; i < n; ++i) {
-      if (calls[i].W->cols <= wave_cols)
+      if (f16_mfma && qmv::gemm_q4_k_f16_fits(calls[i].W->cols, batch))
+        mfma16[nm++] = calls[i];
+      else if (calls[i].W->cols <= wave_cols)
         narrow[nn++] = calls[i];
       else if (calls[i].W->cols <= qmv::kRowsSplitMaxWaves * wave_cols && half_x && !mfma_split)
         split[ns++] = calls[i];
@@ -299,6 +305,8 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     };
     if (nn) e = rows(narrow, nn);
     if (e == hipSuccess && ns) e = rows(split, ns);
+    for (int i = 0; i < nm && e == hipSuccess; ++i)
+      e = qmv::gemm_q4_k_f16(*mfma16[i].W, mfma16[i].x, mfma16[i].y, batch, s);
     if (e == hipSuccess && nw) {
       if (q4k_mfma) {
         for (int i = 0; i < nw && e == hipSuccess; ++i)

@@ -26,7 +26,7 @@
 // Every scale is applied from the lane's own registers.
 //
 // Three kernels, by batch (routing in gemm_q4_k_bf16 below):
-//   * M <= 16 and X fits in LDS: gemm_q4_k_bf16_stream -- one workgroup per
+//   * M <= 16 and X fits in LDS: gemm_q4_k_stream (also for fp16 X) -- one workgroup per
 //     CU streams its share of W past an LDS copy of all of X;
 //   * 17 <= M: gemm_q4_k_bf16_tile -- 64 NB x 16 MB WM tiles, X staged per
 //     block through double-buffered LDS, min and offset terms as two extra
@@ -324,9 +324,45 @@ __host__ __device__ constexpr size_t stream_lds_bytes(int nb) {
          static_cast<size_t>(kStreamWaves) * 2 * 4 * 64 * 4;      // two partial tiles per wave
 }
 
-template <bool PL>
+// The activation type of the streaming kernel.  bf16: the codes enter the
+// matrix cores as bf16(128 + u) (0x4300 | u).  fp16: as fp16(1024 + u)
+// (0x6400 | u, exact, the same one AND-OR per two codes); products are exact
+// in fp32 either way, and the 1024 X offset removed afterwards costs at most
+// about 2^-24 * 1024 / 8 relative to a sub-block's sum.
+template <bool F16>
+struct StreamX {
+  typedef bf16x8_t vec8;
+  static constexpr uint32_t kBias2 = 0x43004300u;  // two bf16 128.0
+  static constexpr float kBias = 128.f;
+  __device__ static float sum8(uint4 v) { return bf16x8_sum(v); }
+  __device__ static f32x4_t mfma(vec8 a, vec8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+};
+template <>
+struct StreamX<true> {
+  typedef _Float16 vec8 __attribute__((ext_vector_type(8)));
+  static constexpr uint32_t kBias2 = 0x64006400u;  // two fp16 1024.0
+  static constexpr float kBias = 1024.f;
+  // Sum of the eight fp16 values of a chunk in fp32: four v_dot2_f32_f16
+  // against fp16 ones (exact products, fp32 sums).
+  __device__ static float sum8(uint4 v) {
+    const h2_t one = __builtin_bit_cast(h2_t, 0x3C003C00u);
+    float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.x), one, 0.f, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.y), one, s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.z), one, s, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.w), one, s, false);
+  }
+  __device__ static f32x4_t mfma(vec8 a, vec8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+};
+
+template <bool PL, bool F16>
 __global__ void __launch_bounds__(64 * kStreamWaves)
-gemm_q4_k_bf16_stream(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M) {
+gemm_q4_k_stream(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M) {
+  typedef StreamX<F16> XT;
+  typedef typename XT::vec8 vec8;
   extern __shared__ __attribute__((aligned(16))) uint8_t st_lds[];
   const int nb = K >> 8;
   // X operands: [nb][8 s][4 q][16 slots][16 B], batch row m of quarter q of
@@ -376,7 +412,7 @@ gemm_q4_k_bf16_stream(const uint8_t* w, uint64_t pa, int N, int K, const uint16_
   for (int m = 0; m < 16; ++m) {
     if (m >= M) continue;  // uniform; the loop stays unrolled
     const uint4 v = xv[m];
-    const float sum = quad_sum(bf16x8_sum(v));  // the four quarters of a sub-block are lanes 4i..4i+3
+    const float sum = quad_sum(XT::sum8(v));  // the four quarters of a sub-block are lanes 4i..4i+3
     if (xl) {
       *reinterpret_cast<uint4*>(xa + ((static_cast<size_t>(xb_) * 8 + xs_) * 4 + xk) * 256 +
                                 (m ^ ((4 * xs_ + xk) & 15)) * 16) =
@@ -396,7 +432,7 @@ gemm_q4_k_bf16_stream(const uint8_t* w, uint64_t pa, int N, int K, const uint16_
   // First tile of wave k's run: floor(floor(k U / W) / nb) = floor(k nt / W).
   const int tf = wave * nt / kStreamWaves;
 
-  const uint32_t bias = vgpr_const(0x43004300u);  // two bf16 128.0
+  const uint32_t bias = vgpr_const(XT::kBias2);
 
   auto unit = [&](int u, const UnitRegs& r) {
     const int b = u - (u / nb) * nb;
@@ -409,16 +445,15 @@ gemm_q4_k_bf16_stream(const uint8_t* w, uint64_t pa, int N, int K, const uint16_
     const float* xsb = xsum + b * 8 * 16 + 4 * q;
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      const bf16x8_t A = *reinterpret_cast<const bf16x8_t*>(xb + s * 1024 + ((c ^ ((4 * s + q) & 15)) * 16));
+      const vec8 A = *reinterpret_cast<const vec8*>(xb + s * 1024 + ((c ^ ((4 * s + q) & 15)) * 16));
       const f32x4_t xs = *reinterpret_cast<const f32x4_t*>(xsb + s * 16);
       const float ds = d * ubyte_f32(s < 4 ? sc03 : sc47, s);
-      const float dmp = fmaf(128.f, ds, dmin * ubyte_f32(s < 4 ? m03 : m47, s));
+      const float dmp = fmaf(XT::kBias, ds, dmin * ubyte_f32(s < 4 ? m03 : m47, s));
       const uint2 pc = r.q[s >> 1];
       const int sh = 4 * (s & 1);
       const uint32_t bw[4] = {((pc.x >> sh) & 0x000F000Fu) | bias, ((pc.x >> (8 + sh)) & 0x000F000Fu) | bias,
                               ((pc.y >> sh) & 0x000F000Fu) | bias, ((pc.y >> (8 + sh)) & 0x000F000Fu) | bias};
-      const f32x4_t S = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A, __builtin_bit_cast(bf16x8_t, bw),
-                                                                f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+      const f32x4_t S = XT::mfma(A, __builtin_bit_cast(vec8, bw));
 #pragma unroll
       for (int i = 0; i < 4; ++i) acc[i] = fmaf(-dmp, xs[i], fmaf(ds, S[i], acc[i]));
     }
@@ -474,6 +509,7 @@ gemm_q4_k_bf16_stream(const uint8_t* w, uint64_t pa, int N, int K, const uint16_
     if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = v;
   }
 }
+
 
 
 // ---------------------------------------------------------------------------
@@ -807,7 +843,7 @@ static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, flo
     int G = device_cus();
     if (G > T) G = T;
     if (G < (T + 7) / 8) G = (T + 7) / 8;
-    hipLaunchKernelGGL(gemm_q4_k_bf16_stream<PL>, dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(nb),
+    hipLaunchKernelGGL((gemm_q4_k_stream<PL, false>), dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(nb),
                        stream, w, pa, N, K, xb, y, M);
     return hipGetLastError();
   }
@@ -840,6 +876,32 @@ static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, flo
     hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 4, 2, 5, PL>), dim3(G, (M + 127) / 128), dim3(640),
                        2 * tile_buf_bytes<128>(), stream, w, pa, N, K, xb, y, M);
   }
+  return hipGetLastError();
+}
+
+// fp16 activations, 2..16 rows, X within the LDS bound of the streaming
+// kernel (gemm_q4_k_f16_fits): the fp16 streaming kernel.
+bool gemm_q4_k_f16_fits(int64_t cols, int64_t batch) {
+  return batch >= 2 && batch <= 16 &&
+         stream_lds_bytes(static_cast<int>(cols / 256)) <= static_cast<size_t>(device_lds_per_block());
+}
+
+hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t batch,
+                         hipStream_t stream) {
+  if (!gemm_q4_k_f16_fits(W.cols, batch)) return hipErrorInvalidValue;
+  const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols), M = static_cast<int>(batch);
+  const uint8_t* w = static_cast<const uint8_t*>(W.data);
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  const int T = (N + 15) / 16;
+  int G = device_cus();
+  if (G > T) G = T;
+  if (G < (T + 7) / 8) G = (T + 7) / 8;
+  if (W.layout == QMV_LAYOUT_PLANES)
+    hipLaunchKernelGGL((gemm_q4_k_stream<true, true>), dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(K / 256),
+                       stream, w, W.scales_offset, N, K, xh, y, M);
+  else
+    hipLaunchKernelGGL((gemm_q4_k_stream<false, true>), dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(K / 256),
+                       stream, w, W.scales_offset, N, K, xh, y, M);
   return hipGetLastError();
 }
 

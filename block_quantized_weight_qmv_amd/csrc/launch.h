@@ -71,6 +71,16 @@ hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t bat
 constexpr int64_t kMfmaMinBatch = QMV_MFMA_MIN_BATCH;
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t s);
+// Q4_K x fp16 on the matrix cores: the streaming kernel with fp16 operands,
+// for 2..16 rows when X fits its LDS copy (gemm_q4_k_f16_fits).  qmv_gemv
+// takes it from kMfmaMinF16Batch rows; below, the multi-row GEMV is faster.
+#ifndef QMV_MFMA_MIN_F16_BATCH
+#define QMV_MFMA_MIN_F16_BATCH 5
+#endif
+constexpr int64_t kMfmaMinF16Batch = QMV_MFMA_MIN_F16_BATCH;
+bool gemm_q4_k_f16_fits(int64_t cols, int64_t batch);
+hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t batch,
+                         hipStream_t s);
 
 hipError_t dequant(const qmv_weights& W, void* out, int out_dtype, hipStream_t s);
 

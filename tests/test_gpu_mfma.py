@@ -1,4 +1,5 @@
-"""Batched Q4_K x bf16 on the matrix-core path (qmv_gemv with batch >= 2).
+"""Batched Q4_K x bf16 on the matrix-core path, and Q4_K x fp16 on its
+streaming kernel (5-16 rows with X in LDS).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
@@ -18,6 +19,7 @@ import pytest
 import torch
 
 import oracle
+from block_quantized_weight_qmv_amd import qmv
 from gpu_util import DEV, Weights, oracle_y, say, to_dev_x
 from synth import CONFIGS, gen_weights, gen_x, weight_seed, x_seed
 
@@ -101,5 +103,62 @@ def test_full_size_batched_ffn_sampled_rows(batch):
     say(f"  sampled normwise err max {err.max():.3e}")
     assert np.all(err <= TOL)
     assert np.all(np.isfinite(y))
+    del w
+    torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("layout", ["blocks", "planes"])
+@pytest.mark.parametrize("rows,nblk,batch", [(67, 14, 5), (130, 3, 16), (1, 1, 8), (33, 16, 9), (200, 14, 12),
+                                             (16, 2, 7)])
+def test_mfma_f16_matches_oracle(layout, rows, nblk, batch):
+    # Q4_K x fp16 at 5-16 rows with X in LDS: the streaming kernel with fp16
+    # operands (codes as fp16(1024 + u), exact; fp32 sums)
+    cols = nblk * 256
+    say(f"mfma fp16 q4_k {layout} {rows}x{cols} batch {batch}")
+    w = Weights("q4_k", rows, cols, seed=900 + rows + nblk)
+    desc = w.desc
+    if layout == "planes":
+        buf = torch.empty(qmv.qmv_planes_size("q4_k", rows, cols), dtype=torch.uint8, device=DEV)
+        desc = qmv.qmv_repack_planes(w.desc, buf)
+        desc.keep = buf
+    x = gen_x(batch, cols, "f16", seed=91 + batch)
+    y = torch.full((batch, rows), 3.5, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv("q4_k", desc, to_dev_x(x, "f16"), "f16", y, rows, cols, batch)
+    y = y.cpu().numpy()
+    err = oracle.normwise_rel_err(y, oracle_y(w, x, "f16"))
+    say(f"  normwise err max {err.max():.3e}")
+    assert np.all(err <= TOL), err
+
+
+def test_mfma_f16_integer_case_is_exact():
+    # d = dmin = 1 and x in {-1, 0, 1}: every product and partial sum is an
+    # integer below 2^24, so the fp32 result is exact on any summation order
+    rows, cols, batch = 96, 4 * 256, 12
+    f = gen_weights("q4_k", rows, cols, 6)
+    f["d_bits"][:] = 0x3C00
+    f["dmin_bits"][:] = 0x3C00
+    w = Weights("q4_k", rows, cols, fields=f)
+    g = np.random.Generator(np.random.PCG64(10))
+    x = g.integers(-1, 2, size=(batch, cols)).astype(np.float16)
+    y = w.gemv(to_dev_x(x, "f16"), "f16", batch).cpu().numpy()
+    y64 = oracle_y(w, x, "f16")
+    assert np.abs(y64).max() < 2 ** 24
+    np.testing.assert_array_equal(y, y64.astype(np.float32))
+
+
+@pytest.mark.parametrize("batch", [5, 16])
+def test_full_size_f16_batched_ffn_sampled_rows(batch):
+    cfg = CONFIGS[5]
+    _, rows, cols = cfg["mats"][0]
+    say(f"full-size mfma fp16 {rows}x{cols} batch {batch}")
+    w = Weights("q4_k", rows, cols, seed=weight_seed(5, 0))
+    x = gen_x(batch, cols, "f16", x_seed(5, 0))
+    y = w.gemv(to_dev_x(x, "f16"), "f16", batch).cpu().numpy()
+    g = np.random.Generator(np.random.PCG64(100 + batch))
+    ids = np.sort(g.choice(rows, size=48, replace=False))
+    ids[0], ids[-1] = 0, rows - 1
+    err = oracle.normwise_rel_err(y[:, ids], oracle_y(w, x, "f16", ids))
+    say(f"  sampled normwise err max {err.max():.3e}")
+    assert np.all(err <= TOL)
     del w
     torch.cuda.empty_cache()
