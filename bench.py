@@ -79,11 +79,12 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     (Q4_K x bf16: 2-4 rows) against matrices within one wave's K slice (4096
     columns, Q8_0 2048) -> the multi-row GEMV (fp32: two rows per pass);
     fp16/bf16 against two to eight waves along K -> its K-split form, except
-    Q4_K x bf16 above two rows; Q4_K x fp16 at 5-16 rows with X in LDS -> the
-    fp16 matrix-core stream kernel)."""
+    Q4_K x bf16 above two rows; Q4_K x fp16 from 5 rows with X in LDS -> the
+    fp16 matrix-core stream kernel, one dispatch per 16 rows)."""
     nb_max = max(cols_list) // 256
-    if (fmt == "q4_k" and x_dtype == "f16" and 5 <= batch <= 16
+    if (fmt == "q4_k" and x_dtype == "f16" and batch >= 5
             and nb_max * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024):  # fp16 X fits the stream kernel's LDS
+        # (one dispatch per 16 activation rows: a "launch" here is ceil(batch / 16) dispatches)
         return f"qmv::gemm_q4_k_stream<{'true' if layout == 'planes' else 'false'}, true>"
     wave_cols = 2048 if fmt == "q8_0" else 4096
     kw_max = -(-max(cols_list) // wave_cols)
@@ -213,7 +214,7 @@ def default_layout(config: int, batch: int | None = None, x_dtype: str | None = 
     b = batch or cfg["batch"][0]
     xd = x_dtype or cfg["x_dtype"]
     # Q4_K x bf16 batches of 5 or more run on the matrix cores; 2-4 rows take the multi-row GEMV
-    gemv = not (cfg["fmt"] == "q4_k" and ((xd == "bf16" and b >= 5) or (xd == "f16" and 5 <= b <= 16)))
+    gemv = not (cfg["fmt"] == "q4_k" and xd in ("bf16", "f16") and b >= 5)
     return "planes" if cfg["fmt"] in ("q4_k", "q5_k", "q6_k") and gemv else "blocks"
 
 

@@ -276,8 +276,8 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     qmv::GemvCall narrow[qmv::kMaxItems], split[qmv::kMaxItems], wide[qmv::kMaxItems];
     qmv::GemvCall mfma16[qmv::kMaxItems];
     int nn = 0, ns = 0, nw = 0, nm = 0;
-    // Q4_K x fp16, 5..16 rows, X within the streaming kernel's LDS copy: the
-    // matrix cores with fp16 operands
+    // Q4_K x fp16 from 5 rows, X rows within the streaming kernel's LDS copy:
+    // the matrix cores with fp16 operands, 16 rows per launch
     const bool f16_mfma = fmt == QMV_Q4_K && x_dtype == QMV_F16 && batch >= qmv::kMfmaMinF16Batch;
     // Q4_K x bf16 against wide matrices: the K-split form for two rows, the
     // matrix cores above (3584 x 18944: 14.7 against 24.8 us at two rows,

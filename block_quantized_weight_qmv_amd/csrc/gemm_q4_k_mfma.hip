@@ -879,30 +879,37 @@ static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, flo
   return hipGetLastError();
 }
 
-// fp16 activations, 2..16 rows, X within the LDS bound of the streaming
-// kernel (gemm_q4_k_f16_fits): the fp16 streaming kernel.
+// fp16 activations with X rows within the LDS bound of the streaming kernel
+// (gemm_q4_k_f16_fits): the fp16 streaming kernel, one launch per 16
+// activation rows (the tile kernels take bf16 only).
 bool gemm_q4_k_f16_fits(int64_t cols, int64_t batch) {
-  return batch >= 2 && batch <= 16 &&
+  return batch >= 1 &&
          stream_lds_bytes(static_cast<int>(cols / 256)) <= static_cast<size_t>(device_lds_per_block());
 }
 
 hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                          hipStream_t stream) {
   if (!gemm_q4_k_f16_fits(W.cols, batch)) return hipErrorInvalidValue;
-  const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols), M = static_cast<int>(batch);
+  const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols);
   const uint8_t* w = static_cast<const uint8_t*>(W.data);
-  const uint16_t* xh = static_cast<const uint16_t*>(x);
   const int T = (N + 15) / 16;
   int G = device_cus();
   if (G > T) G = T;
   if (G < (T + 7) / 8) G = (T + 7) / 8;
-  if (W.layout == QMV_LAYOUT_PLANES)
-    hipLaunchKernelGGL((gemm_q4_k_stream<true, true>), dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(K / 256),
-                       stream, w, W.scales_offset, N, K, xh, y, M);
-  else
-    hipLaunchKernelGGL((gemm_q4_k_stream<false, true>), dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(K / 256),
-                       stream, w, W.scales_offset, N, K, xh, y, M);
-  return hipGetLastError();
+  for (int64_t m0 = 0; m0 < batch; m0 += 16) {
+    const int M = static_cast<int>(batch - m0 < 16 ? batch - m0 : 16);
+    const uint16_t* xh = static_cast<const uint16_t*>(x) + m0 * K;
+    float* yc = y + m0 * N;
+    if (W.layout == QMV_LAYOUT_PLANES)
+      hipLaunchKernelGGL((gemm_q4_k_stream<true, true>), dim3(G), dim3(64 * kStreamWaves),
+                         stream_lds_bytes(K / 256), stream, w, W.scales_offset, N, K, xh, yc, M);
+    else
+      hipLaunchKernelGGL((gemm_q4_k_stream<false, true>), dim3(G), dim3(64 * kStreamWaves),
+                         stream_lds_bytes(K / 256), stream, w, W.scales_offset, N, K, xh, yc, M);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,

@@ -72,8 +72,9 @@ constexpr int64_t kMfmaMinBatch = QMV_MFMA_MIN_BATCH;
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t s);
 // Q4_K x fp16 on the matrix cores: the streaming kernel with fp16 operands,
-// for 2..16 rows when X fits its LDS copy (gemm_q4_k_f16_fits).  qmv_gemv
-// takes it from kMfmaMinF16Batch rows; below, the multi-row GEMV is faster.
+// one launch per 16 activation rows, when X rows fit its LDS copy
+// (gemm_q4_k_f16_fits).  qmv_gemv takes it from kMfmaMinF16Batch rows;
+// below, the multi-row GEMV is faster.
 #ifndef QMV_MFMA_MIN_F16_BATCH
 #define QMV_MFMA_MIN_F16_BATCH 5
 #endif

@@ -117,7 +117,7 @@ def test_more_than_one_gpu_is_refused():
 
 
 @pytest.mark.parametrize("config,batch,x_dtype", [(2, 4, None), (2, 3, "bf16"), (4, 4, "bf16"), (4, 2, "f16"),
-                                                  (3, 2, "f16"), (5, 4, "f16"), (5, 30, "f16"), (1, 4, "f16"),
+                                                  (3, 2, "f16"), (5, 4, "f16"), (1, 4, "f16"),
                                                   (1, 2, "bf16"), (3, 2, None), (4, 4, None), (5, 3, "f32")])
 def test_small_batch_overrides_name_library_kernels(config, batch, x_dtype):
     # --batch on any configuration and --x-dtype: the multi-row GEMV for the
@@ -142,9 +142,9 @@ def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
     assert split and all(k in names for k in split), plan["kname"]
 
 
-@pytest.mark.parametrize("batch", [5, 8, 16])
+@pytest.mark.parametrize("batch", [5, 8, 16, 64, 512])
 def test_q4_k_f16_batches_name_the_f16_stream_kernel(batch):
-    # Q4_K x fp16 at 5-16 rows with X in LDS: the matrix cores with fp16 operands
+    # Q4_K x fp16 from 5 rows with X in LDS: the matrix cores with fp16 operands
     names = _library_kernels()
     layout = bench.default_layout(5, batch, "f16")
     assert layout == "blocks"

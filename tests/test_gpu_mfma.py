@@ -1,5 +1,5 @@
 """Batched Q4_K x bf16 on the matrix-core path, and Q4_K x fp16 on its
-streaming kernel (5-16 rows with X in LDS).
+streaming kernel (from 5 rows with X in LDS, 16 rows per launch).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
@@ -109,10 +109,11 @@ def test_full_size_batched_ffn_sampled_rows(batch):
 
 @pytest.mark.parametrize("layout", ["blocks", "planes"])
 @pytest.mark.parametrize("rows,nblk,batch", [(67, 14, 5), (130, 3, 16), (1, 1, 8), (33, 16, 9), (200, 14, 12),
-                                             (16, 2, 7)])
+                                             (16, 2, 7), (40, 5, 17), (70, 3, 33), (33, 14, 64), (9, 2, 100)])
 def test_mfma_f16_matches_oracle(layout, rows, nblk, batch):
-    # Q4_K x fp16 at 5-16 rows with X in LDS: the streaming kernel with fp16
-    # operands (codes as fp16(1024 + u), exact; fp32 sums)
+    # Q4_K x fp16 from 5 rows with X in LDS: the streaming kernel with fp16
+    # operands (codes as fp16(1024 + u), exact; fp32 sums), one launch per 16
+    # activation rows (17, 33, 100: a last partial chunk)
     cols = nblk * 256
     say(f"mfma fp16 q4_k {layout} {rows}x{cols} batch {batch}")
     w = Weights("q4_k", rows, cols, seed=900 + rows + nblk)
@@ -146,7 +147,7 @@ def test_mfma_f16_integer_case_is_exact():
     np.testing.assert_array_equal(y, y64.astype(np.float32))
 
 
-@pytest.mark.parametrize("batch", [5, 16])
+@pytest.mark.parametrize("batch", [5, 16, 64])
 def test_full_size_f16_batched_ffn_sampled_rows(batch):
     cfg = CONFIGS[5]
     _, rows, cols = cfg["mats"][0]

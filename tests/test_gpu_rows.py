@@ -95,8 +95,8 @@ def test_rows_groups_of_four(fmt, layout, x_dtype, batch, rows, nblk):
     # bf16 batches above four take the matrix cores and are not this kernel's)
     if fmt == "q4_k" and x_dtype == "bf16":
         pytest.skip("Q4_K x bf16 batches above four run on the matrix cores (test_gpu_mfma.py)")
-    if fmt == "q4_k" and x_dtype == "f16" and batch <= 16:
-        pytest.skip("Q4_K x fp16 batches of 5-16 run on the matrix cores (test_gpu_mfma.py)")
+    if fmt == "q4_k" and x_dtype == "f16":
+        pytest.skip("Q4_K x fp16 batches from 5 rows run on the matrix cores (test_gpu_mfma.py)")
     cols = nblk * 256
     say(f"multi-row {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
     _check(fmt, layout, rows, cols, batch, x_dtype, seed=1600 + rows + nblk)
