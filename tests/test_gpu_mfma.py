@@ -163,3 +163,28 @@ def test_full_size_f16_batched_ffn_sampled_rows(batch):
     assert np.all(err <= TOL)
     del w
     torch.cuda.empty_cache()
+
+
+def test_mfma_f16_chunked_graph_replay():
+    # 40 fp16 rows: three dispatches of the streaming kernel per call (16, 16,
+    # 8); a captured graph of the call must equal the eager result on every
+    # replay
+    rows, cols, batch = 300, 14 * 256, 40
+    say("mfma fp16 chunked graph replay")
+    w = Weights("q4_k", rows, cols, seed=1900)
+    x = to_dev_x(gen_x(batch, cols, "f16", seed=190), "f16")
+    y0 = w.gemv(x, "f16", batch)
+    s = torch.cuda.Stream()
+    yg = torch.zeros(batch, rows, dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        w.gemv(x, "f16", batch, y=yg, stream=s)  # warm-up outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            w.gemv(x, "f16", batch, y=yg, stream=s)
+    for _ in range(3):
+        yg.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y0)
