@@ -267,8 +267,9 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   // over the weights per two or four activation rows, two for fp32), those of
   // two to eight waves along K its K-split form (fp16/bf16; one launch, one
   // pass per two rows; Q4_K x bf16 above two rows keeps the matrix cores),
-  // the wider ones the GEMV once per row.  Every item's result is the same as
-  // that of the item called alone.
+  // the wider ones the GEMV once per row; Q4_K x fp16 from five rows takes
+  // the fp16 matrix-core streaming kernel where X fits its LDS copy.  Every
+  // item's result is the same as that of the item called alone.
   const bool half_x = x_dtype == QMV_F16 || x_dtype == QMV_BF16;
   const int64_t wave_cols = fmt == QMV_Q8_0 ? 2048 : 4096;
   if (batch >= 2 &&
