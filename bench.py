@@ -45,7 +45,7 @@ _KERNEL_SOURCES = {
     "gemv_rows_kernel": ["gemv_skeleton.h", "device_util.h"],
     "gemm_q4_k_stream": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_bf16_ksplit": ["gemm_q4_k_mfma.hip", "device_util.h"],
-    "gemm_q4_k_bf16_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
+    "gemm_q4_k_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
 }
 _POLICY_SOURCE = {"Q80Policy": "gemv_q8_0.hip", "Q4KPolicy": "gemv_q4_k.hip",
                   "Q4KPlanesPolicy": "gemv_q4_k.hip", "Q5KPlanesPolicy": "gemv_q5_k.hip",
@@ -79,12 +79,15 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     (Q4_K x bf16: 2-4 rows) against matrices within one wave's K slice (4096
     columns, Q8_0 2048) -> the multi-row GEMV (fp32: two rows per pass);
     fp16/bf16 against two to eight waves along K -> its K-split form, except
-    Q4_K x bf16 above two rows; Q4_K x fp16 from 5 rows with X in LDS -> the
-    fp16 matrix-core stream kernel, one dispatch per 16 rows)."""
+    Q4_K x bf16 above two rows; Q4_K x fp16 at 5-16 rows with X in LDS -> the
+    fp16 matrix-core stream kernel, from 17 rows -> the fp16 tile kernels)."""
     nb_max = max(cols_list) // 256
+    if fmt == "q4_k" and x_dtype == "f16" and batch >= 17:  # fp16 on the tile kernels
+        pl = "true" if layout == "planes" else "false"
+        mb = 1 if batch <= 32 else (2 if batch <= 64 else 4)
+        return f"qmv::gemm_q4_k_tile<1, {mb}, 2, 5, {pl}, true>"
     if (fmt == "q4_k" and x_dtype == "f16" and batch >= 5
             and nb_max * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024):  # fp16 X fits the stream kernel's LDS
-        # (one dispatch per 16 activation rows: a "launch" here is ceil(batch / 16) dispatches)
         return f"qmv::gemm_q4_k_stream<{'true' if layout == 'planes' else 'false'}, true>"
     wave_cols = 2048 if fmt == "q8_0" else 4096
     kw_max = -(-max(cols_list) // wave_cols)
@@ -110,9 +113,9 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         if batch <= 16:
             return f"qmv::gemm_q4_k_bf16_ksplit<1, 1, {pl}>"
         if batch <= 32:
-            return f"qmv::gemm_q4_k_bf16_tile<1, 1, 2, 5, {pl}>"
-        return (f"qmv::gemm_q4_k_bf16_tile<1, 2, 2, 5, {pl}>" if batch <= 64
-                else f"qmv::gemm_q4_k_bf16_tile<1, 4, 2, 5, {pl}>")
+            return f"qmv::gemm_q4_k_tile<1, 1, 2, 5, {pl}, false>"
+        return (f"qmv::gemm_q4_k_tile<1, 2, 2, 5, {pl}, false>" if batch <= 64
+                else f"qmv::gemm_q4_k_tile<1, 4, 2, 5, {pl}, false>")
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096, "q5_k": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
     kw = max(-(-c // per_wave) for c in cols_list)

@@ -268,8 +268,8 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
   // two to eight waves along K its K-split form (fp16/bf16; one launch, one
   // pass per two rows; Q4_K x bf16 above two rows keeps the matrix cores),
   // the wider ones the GEMV once per row; Q4_K x fp16 from five rows takes
-  // the fp16 matrix-core streaming kernel where X fits its LDS copy.  Every
-  // item's result is the same as that of the item called alone.
+  // the matrix cores with fp16 operands (gemm_q4_k_f16_fits).  Every item's
+  // result is the same as that of the item called alone.
   const bool half_x = x_dtype == QMV_F16 || x_dtype == QMV_BF16;
   const int64_t wave_cols = fmt == QMV_Q8_0 ? 2048 : 4096;
   if (batch >= 2 &&
@@ -277,8 +277,9 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     qmv::GemvCall narrow[qmv::kMaxItems], split[qmv::kMaxItems], wide[qmv::kMaxItems];
     qmv::GemvCall mfma16[qmv::kMaxItems];
     int nn = 0, ns = 0, nw = 0, nm = 0;
-    // Q4_K x fp16 from 5 rows, X rows within the streaming kernel's LDS copy:
-    // the matrix cores with fp16 operands, 16 rows per launch
+    // Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (the
+    // streaming kernel up to 16 rows where X fits its LDS copy, the tile
+    // kernels from 17 rows)
     const bool f16_mfma = fmt == QMV_Q4_K && x_dtype == QMV_F16 && batch >= qmv::kMfmaMinF16Batch;
     // Q4_K x bf16 against wide matrices: the K-split form for two rows, the
     // matrix cores above (3584 x 18944: 14.7 against 24.8 us at two rows,

@@ -28,7 +28,7 @@
 // Three kernels, by batch (routing in gemm_q4_k_bf16 below):
 //   * M <= 16 and X fits in LDS: gemm_q4_k_stream (also for fp16 X) -- one workgroup per
 //     CU streams its share of W past an LDS copy of all of X;
-//   * 17 <= M: gemm_q4_k_bf16_tile -- 64 NB x 16 MB WM tiles, X staged per
+//   * 17 <= M: gemm_q4_k_tile (also for fp16 X) -- 64 NB x 16 MB WM tiles, X staged per
 //     block through double-buffered LDS, min and offset terms as two extra
 //     matrix-core products per block;
 //   * M <= 16 with X too large for LDS: gemm_q4_k_bf16_ksplit -- K split over
@@ -551,9 +551,14 @@ __host__ __device__ constexpr size_t tile_buf_bytes() {
   return static_cast<size_t>(MT) * 512 + static_cast<size_t>(MT / 16) * 1024;
 }
 
-template <int NB, int MB, int WM, int WN, bool PL>
+// F16: fp16 X.  Only the main products change (codes as fp16(1024 + u), X
+// as given, fp16 sums of eight); the split sub-block sums are fp32 values
+// either way and keep their bf16 products.
+template <int NB, int MB, int WM, int WN, bool PL, bool F16>
 __global__ void __launch_bounds__(64 * WN * WM)
-gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M) {
+gemm_q4_k_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M) {
+  typedef StreamX<F16> XT;
+  typedef typename XT::vec8 vec8;
   extern __shared__ __attribute__((aligned(16))) uint8_t tl_lds[];
   constexpr int MT = 16 * MB * WM;             // batch rows of the workgroup
   constexpr int kThreads = 64 * WN * WM;
@@ -631,7 +636,7 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         const uint4 u = v[j][k];
-        sum += bf16x8_sum(u);
+        sum += XT::sum8(u);
         *reinterpret_cast<uint4*>(base + ((s * (MT / 16) + mb) * 4 + k) * 256 + (mr ^ ((s + 4 * k) & 15)) * 16) =
             make_uint4(lo_pair(u.x, u.y), hi_pair(u.x, u.y), lo_pair(u.z, u.w), hi_pair(u.z, u.w));
       }
@@ -652,7 +657,7 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
   for (int t = 0; t < NB; ++t)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[t][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint32_t bias = vgpr_const(0x43004300u);
+  const uint32_t bias = vgpr_const(XT::kBias2);
 
   auto compute = [&](const TileRegs<NB>& r, int buf) {
     const uint8_t* base = tl_lds + buf * kBuf;
@@ -662,7 +667,7 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
     for (int t = 0; t < NB; ++t) {
       const uint4 h = r.hd[t];
       const float d = f16_to_f32(h.x & 0xFFFFu);
-      d128[t] = 128.f * d;
+      d128[t] = XT::kBias * d;
       dmin[t] = f16_to_f32(h.x >> 16);
       const uint32_t sc03 = h.y & 0x3F3F3F3Fu, m03 = h.z & 0x3F3F3F3Fu;
       const uint32_t sc47 = (h.w & 0x0F0F0F0Fu) | ((h.y >> 2) & 0x30303030u);
@@ -691,11 +696,11 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
     // With four batch tiles the products of a step already cover that
     // latency, and the straight order measured faster.
     if constexpr (MB <= 2) {
-      auto read_a = [&](int s, bf16x8_t (&A)[MB]) {
+      auto read_a = [&](int s, vec8 (&A)[MB]) {
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          A[mb] = *reinterpret_cast<const bf16x8_t*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
-                                                     (c ^ ((s + 4 * q) & 15)) * 16);
+          A[mb] = *reinterpret_cast<const vec8*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
+                                                 (c ^ ((s + 4 * q) & 15)) * 16);
       };
       auto scale = [&](int s, const f32x4_t (&S)[NB][MB]) {
 #pragma unroll
@@ -707,7 +712,7 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
             __asm__ __volatile__("" : "+v"(acc[t][mb]));
           }
       };
-      bf16x8_t A[2][MB];
+      vec8 A[2][MB];
       f32x4_t S[2][NB][MB];
       read_a(0, A[0]);
 #pragma unroll
@@ -719,11 +724,9 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
           const int sh = 4 * (s & 1);
           const uint32_t bw[4] = {((pc.x >> sh) & 0x000F000Fu) | bias, ((pc.x >> (8 + sh)) & 0x000F000Fu) | bias,
                                   ((pc.y >> sh) & 0x000F000Fu) | bias, ((pc.y >> (8 + sh)) & 0x000F000Fu) | bias};
-          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bw);
+          const vec8 B = __builtin_bit_cast(vec8, bw);
 #pragma unroll
-          for (int mb = 0; mb < MB; ++mb)
-            S[s & 1][t][mb] =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[s & 1][mb], B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          for (int mb = 0; mb < MB; ++mb) S[s & 1][t][mb] = XT::mfma(A[s & 1][mb], B);
         }
         if (s > 0) scale(s - 1, S[(s - 1) & 1]);
       }
@@ -731,22 +734,21 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
     } else {
 #pragma unroll
       for (int s = 0; s < 8; ++s) {
-        bf16x8_t A[MB];
+        vec8 A[MB];
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb)
-          A[mb] = *reinterpret_cast<const bf16x8_t*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
-                                                     (c ^ ((s + 4 * q) & 15)) * 16);
+          A[mb] = *reinterpret_cast<const vec8*>(base + ((s * (MT / 16) + MB * wm + mb) * 4 + q) * 256 +
+                                                 (c ^ ((s + 4 * q) & 15)) * 16);
 #pragma unroll
         for (int t = 0; t < NB; ++t) {
           const uint2 pc = r.q[t][s >> 1];
           const int sh = 4 * (s & 1);
           const uint32_t bw[4] = {((pc.x >> sh) & 0x000F000Fu) | bias, ((pc.x >> (8 + sh)) & 0x000F000Fu) | bias,
                                   ((pc.y >> sh) & 0x000F000Fu) | bias, ((pc.y >> (8 + sh)) & 0x000F000Fu) | bias};
-          const bf16x8_t B = __builtin_bit_cast(bf16x8_t, bw);
+          const vec8 B = __builtin_bit_cast(vec8, bw);
 #pragma unroll
           for (int mb = 0; mb < MB; ++mb) {
-            const f32x4_t S =
-                __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+            const f32x4_t S = XT::mfma(A[mb], B);
 #pragma unroll
             for (int i = 0; i < 4; ++i) acc[t][mb][i] = fmaf(ds[t][s], S[i], acc[t][mb][i]);
             __asm__ __volatile__("" : "+v"(acc[t][mb]));
@@ -829,6 +831,29 @@ gemm_q4_k_bf16_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t*
       }
 }
 
+// 17 <= M: runs of 4-5 weight tiles, one workgroup per CU for each batch
+// tile of 32, 64 or 128 rows (every CU gets the same work up to one tile).
+template <bool PL, bool F16>
+static hipError_t launch_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* xb, float* y,
+                              int M, hipStream_t stream) {
+  const int T = (N + 15) / 16;
+  int G = device_cus();
+  if (G > T) G = T;
+  if (G < (T + 4) / 5) G = (T + 4) / 5;
+  if (M <= 64) {
+    if (M <= 32)
+      hipLaunchKernelGGL((gemm_q4_k_tile<1, 1, 2, 5, PL, F16>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<32>(),
+                         stream, w, pa, N, K, xb, y, M);
+    else
+      hipLaunchKernelGGL((gemm_q4_k_tile<1, 2, 2, 5, PL, F16>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<64>(),
+                         stream, w, pa, N, K, xb, y, M);
+  } else {
+    hipLaunchKernelGGL((gemm_q4_k_tile<1, 4, 2, 5, PL, F16>), dim3(G, (M + 127) / 128), dim3(640),
+                       2 * tile_buf_bytes<128>(), stream, w, pa, N, K, xb, y, M);
+  }
+  return hipGetLastError();
+}
+
 template <bool PL>
 static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, float* y, int64_t batch,
                                         hipStream_t stream) {
@@ -859,32 +884,15 @@ static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, flo
                        w, pa, N, K, xb, y, M, kw);
     return hipGetLastError();
   }
-  // 17 <= M: runs of 4-5 weight tiles, one workgroup per CU for each batch
-  // tile of 32, 64 or 128 rows (every CU gets the same work up to one tile).
-  const int T = (N + 15) / 16;
-  int G = device_cus();
-  if (G > T) G = T;
-  if (G < (T + 4) / 5) G = (T + 4) / 5;
-  if (M <= 64) {
-    if (M <= 32)
-      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 1, 2, 5, PL>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<32>(),
-                         stream, w, pa, N, K, xb, y, M);
-    else
-      hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 2, 2, 5, PL>), dim3(G, 1), dim3(640), 2 * tile_buf_bytes<64>(),
-                         stream, w, pa, N, K, xb, y, M);
-  } else {
-    hipLaunchKernelGGL((gemm_q4_k_bf16_tile<1, 4, 2, 5, PL>), dim3(G, (M + 127) / 128), dim3(640),
-                       2 * tile_buf_bytes<128>(), stream, w, pa, N, K, xb, y, M);
-  }
-  return hipGetLastError();
+  return launch_tile<PL, false>(w, pa, N, K, xb, y, M, stream);
 }
 
-// fp16 activations with X rows within the LDS bound of the streaming kernel
-// (gemm_q4_k_f16_fits): the fp16 streaming kernel, one launch per 16
-// activation rows (the tile kernels take bf16 only).
+// fp16 activations: up to 16 rows, the fp16 streaming kernel where X fits
+// its LDS copy; from 17 rows, the fp16 tile kernels (any K).
 bool gemm_q4_k_f16_fits(int64_t cols, int64_t batch) {
-  return batch >= 1 &&
-         stream_lds_bytes(static_cast<int>(cols / 256)) <= static_cast<size_t>(device_lds_per_block());
+  return batch >= 17 ||
+         (batch >= 1 &&
+          stream_lds_bytes(static_cast<int>(cols / 256)) <= static_cast<size_t>(device_lds_per_block()));
 }
 
 hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t batch,
@@ -892,6 +900,12 @@ hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t 
   if (!gemm_q4_k_f16_fits(W.cols, batch)) return hipErrorInvalidValue;
   const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols);
   const uint8_t* w = static_cast<const uint8_t*>(W.data);
+  if (batch >= 17) {
+    const uint16_t* xh = static_cast<const uint16_t*>(x);
+    return W.layout == QMV_LAYOUT_PLANES
+               ? launch_tile<true, true>(w, W.scales_offset, N, K, xh, y, static_cast<int>(batch), stream)
+               : launch_tile<false, true>(w, W.scales_offset, N, K, xh, y, static_cast<int>(batch), stream);
+  }
   const int T = (N + 15) / 16;
   int G = device_cus();
   if (G > T) G = T;

@@ -51,7 +51,8 @@ def _library_kernels():
                       f"{m.group(4)}, {m.group(5)}>")
             continue
         if ("qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemv_rows_split_kernel<" in line
-                or "qmv::gemm_q4_k_bf16_" in line or "qmv::gemm_q4_k_stream<" in line):
+                or "qmv::gemm_q4_k_bf16_" in line or "qmv::gemm_q4_k_stream<" in line
+                or "qmv::gemm_q4_k_tile<" in line):
             sym = line.split(" ", 2)[2]
             sym = sym[5:] if sym.startswith("void ") else sym
             names.add(sym.split("(")[0])
@@ -142,12 +143,16 @@ def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
     assert split and all(k in names for k in split), plan["kname"]
 
 
-@pytest.mark.parametrize("batch", [5, 8, 16, 64, 512])
-def test_q4_k_f16_batches_name_the_f16_stream_kernel(batch):
-    # Q4_K x fp16 from 5 rows with X in LDS: the matrix cores with fp16 operands
+@pytest.mark.parametrize("batch,kernel", [(5, "qmv::gemm_q4_k_stream<false, true>"),
+                                          (16, "qmv::gemm_q4_k_stream<false, true>"),
+                                          (17, "qmv::gemm_q4_k_tile<1, 1, 2, 5, false, true>"),
+                                          (64, "qmv::gemm_q4_k_tile<1, 2, 2, 5, false, true>"),
+                                          (512, "qmv::gemm_q4_k_tile<1, 4, 2, 5, false, true>")])
+def test_q4_k_f16_batches_name_the_f16_matrix_core_kernels(batch, kernel):
+    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands
     names = _library_kernels()
     layout = bench.default_layout(5, batch, "f16")
     assert layout == "blocks"
     plan = bench.workload_plan(5, batch, separate=False, layout=layout, x_dtype="f16")
-    assert plan["kname"] == ["qmv::gemm_q4_k_stream<false, true>"]
-    assert plan["kname"][0] in names
+    assert plan["kname"] == [kernel]
+    assert kernel in names

@@ -1,5 +1,5 @@
 """Batched Q4_K x bf16 on the matrix-core path, and Q4_K x fp16 on its
-streaming kernel (from 5 rows with X in LDS, 16 rows per launch).
+streaming kernel (5-16 rows with X in LDS) and tile kernels (17 rows up).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
@@ -109,11 +109,12 @@ def test_full_size_batched_ffn_sampled_rows(batch):
 
 @pytest.mark.parametrize("layout", ["blocks", "planes"])
 @pytest.mark.parametrize("rows,nblk,batch", [(67, 14, 5), (130, 3, 16), (1, 1, 8), (33, 16, 9), (200, 14, 12),
-                                             (16, 2, 7), (40, 5, 17), (70, 3, 33), (33, 14, 64), (9, 2, 100)])
+                                             (16, 2, 7), (40, 5, 17), (70, 3, 33), (33, 14, 64), (9, 2, 100),
+                                             (17, 74, 20), (130, 3, 129)])
 def test_mfma_f16_matches_oracle(layout, rows, nblk, batch):
-    # Q4_K x fp16 from 5 rows with X in LDS: the streaming kernel with fp16
-    # operands (codes as fp16(1024 + u), exact; fp32 sums), one launch per 16
-    # activation rows (17, 33, 100: a last partial chunk)
+    # Q4_K x fp16 from 5 rows: the streaming kernel (5-16 rows, X in LDS) or
+    # the tile kernels (17 rows up, any K; ragged batch tiles) with fp16
+    # operands (codes as fp16(1024 + u), exact; fp32 sums)
     cols = nblk * 256
     say(f"mfma fp16 q4_k {layout} {rows}x{cols} batch {batch}")
     w = Weights("q4_k", rows, cols, seed=900 + rows + nblk)
@@ -147,7 +148,7 @@ def test_mfma_f16_integer_case_is_exact():
     np.testing.assert_array_equal(y, y64.astype(np.float32))
 
 
-@pytest.mark.parametrize("batch", [5, 16, 64])
+@pytest.mark.parametrize("batch", [5, 16, 64, 512])
 def test_full_size_f16_batched_ffn_sampled_rows(batch):
     cfg = CONFIGS[5]
     _, rows, cols = cfg["mats"][0]
@@ -165,12 +166,11 @@ def test_full_size_f16_batched_ffn_sampled_rows(batch):
     torch.cuda.empty_cache()
 
 
-def test_mfma_f16_chunked_graph_replay():
-    # 40 fp16 rows: three dispatches of the streaming kernel per call (16, 16,
-    # 8); a captured graph of the call must equal the eager result on every
-    # replay
+def test_mfma_f16_tile_graph_replay():
+    # 40 fp16 rows on the tile kernel; a captured graph of the call must equal
+    # the eager result on every replay
     rows, cols, batch = 300, 14 * 256, 40
-    say("mfma fp16 chunked graph replay")
+    say("mfma fp16 tile graph replay")
     w = Weights("q4_k", rows, cols, seed=1900)
     x = to_dev_x(gen_x(batch, cols, "f16", seed=190), "f16")
     y0 = w.gemv(x, "f16", batch)
