@@ -44,7 +44,7 @@ _KERNEL_SOURCES = {
     "gemv_kernel": ["gemv_skeleton.h", "device_util.h"],
     "gemv_rows_kernel": ["gemv_skeleton.h", "device_util.h"],
     "gemm_q4_k_stream": ["gemm_q4_k_mfma.hip", "device_util.h"],
-    "gemm_q4_k_bf16_ksplit": ["gemm_q4_k_mfma.hip", "device_util.h"],
+    "gemm_q4_k_ksplit": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
 }
 _POLICY_SOURCE = {"Q80Policy": "gemv_q8_0.hip", "Q4KPolicy": "gemv_q4_k.hip",
@@ -79,16 +79,18 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     (Q4_K x bf16: 2-4 rows) against matrices within one wave's K slice (4096
     columns, Q8_0 2048) -> the multi-row GEMV (fp32: two rows per pass);
     fp16/bf16 against two to eight waves along K -> its K-split form, except
-    Q4_K x bf16 above two rows; Q4_K x fp16 at 5-16 rows with X in LDS -> the
-    fp16 matrix-core stream kernel, from 17 rows -> the fp16 tile kernels)."""
+    Q4_K x bf16 above two rows; Q4_K x fp16 from 5 rows -> the matrix-core
+    kernels of bf16 with fp16 operands)."""
     nb_max = max(cols_list) // 256
     if fmt == "q4_k" and x_dtype == "f16" and batch >= 17:  # fp16 on the tile kernels
         pl = "true" if layout == "planes" else "false"
         mb = 1 if batch <= 32 else (2 if batch <= 64 else 4)
         return f"qmv::gemm_q4_k_tile<1, {mb}, 2, 5, {pl}, true>"
-    if (fmt == "q4_k" and x_dtype == "f16" and batch >= 5
-            and nb_max * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024):  # fp16 X fits the stream kernel's LDS
-        return f"qmv::gemm_q4_k_stream<{'true' if layout == 'planes' else 'false'}, true>"
+    if fmt == "q4_k" and x_dtype == "f16" and batch >= 5:  # fp16 on the matrix cores, up to 16 rows
+        pl = "true" if layout == "planes" else "false"
+        if nb_max * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024:  # X fits the stream kernel's LDS
+            return f"qmv::gemm_q4_k_stream<{pl}, true>"
+        return f"qmv::gemm_q4_k_ksplit<1, 1, {pl}, true>"
     wave_cols = 2048 if fmt == "q8_0" else 4096
     kw_max = -(-max(cols_list) // wave_cols)
     q4k_bf16 = fmt == "q4_k" and x_dtype == "bf16"
@@ -111,7 +113,7 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         if batch <= 16 and nb * 8 * 1088 + 8 * 2 * 4 * 64 * 4 <= 160 * 1024:  # X fits in LDS
             return f"qmv::gemm_q4_k_stream<{pl}, false>"
         if batch <= 16:
-            return f"qmv::gemm_q4_k_bf16_ksplit<1, 1, {pl}>"
+            return f"qmv::gemm_q4_k_ksplit<1, 1, {pl}, false>"
         if batch <= 32:
             return f"qmv::gemm_q4_k_tile<1, 1, 2, 5, {pl}, false>"
         return (f"qmv::gemm_q4_k_tile<1, 2, 2, 5, {pl}, false>" if batch <= 64

@@ -277,9 +277,7 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     qmv::GemvCall narrow[qmv::kMaxItems], split[qmv::kMaxItems], wide[qmv::kMaxItems];
     qmv::GemvCall mfma16[qmv::kMaxItems];
     int nn = 0, ns = 0, nw = 0, nm = 0;
-    // Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (the
-    // streaming kernel up to 16 rows where X fits its LDS copy, the tile
-    // kernels from 17 rows)
+    // Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands
     const bool f16_mfma = fmt == QMV_Q4_K && x_dtype == QMV_F16 && batch >= qmv::kMfmaMinF16Batch;
     // Q4_K x bf16 against wide matrices: the K-split form for two rows, the
     // matrix cores above (3584 x 18944: 14.7 against 24.8 us at two rows,

@@ -31,7 +31,7 @@
 //   * 17 <= M: gemm_q4_k_tile (also for fp16 X) -- 64 NB x 16 MB WM tiles, X staged per
 //     block through double-buffered LDS, min and offset terms as two extra
 //     matrix-core products per block;
-//   * M <= 16 with X too large for LDS: gemm_q4_k_bf16_ksplit -- K split over
+//   * M <= 16 with X too large for LDS: gemm_q4_k_ksplit (also fp16 X) -- K split over
 //     the waves of a workgroup, X read from memory.
 //
 // v_mfma_f32_16x16x32_bf16 (layout checked on the device): lane l holds
@@ -84,6 +84,42 @@ __device__ __forceinline__ float quad_sum(float v) {
 __device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); }
 __device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); }
 
+// The activation type of the matrix-core kernels.  bf16: the codes enter the
+// matrix cores as bf16(128 + u) (0x4300 | u).  fp16: as fp16(1024 + u)
+// (0x6400 | u, exact, the same one AND-OR per two codes); products are exact
+// in fp32 either way, and the 1024 X offset removed afterwards costs at most
+// about 2^-24 * 1024 / 8 relative to a sub-block's sum.
+template <bool F16>
+struct StreamX {
+  typedef bf16x8_t vec8;
+  static constexpr uint32_t kBias2 = 0x43004300u;  // two bf16 128.0
+  static constexpr float kBias = 128.f;
+  static constexpr uint32_t kOne2 = 0x3F803F80u;   // two bf16 ones
+  __device__ static float sum8(uint4 v) { return bf16x8_sum(v); }
+  __device__ static f32x4_t mfma(vec8 a, vec8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+};
+template <>
+struct StreamX<true> {
+  typedef _Float16 vec8 __attribute__((ext_vector_type(8)));
+  static constexpr uint32_t kBias2 = 0x64006400u;  // two fp16 1024.0
+  static constexpr float kBias = 1024.f;
+  static constexpr uint32_t kOne2 = 0x3C003C00u;   // two fp16 ones
+  // Sum of the eight fp16 values of a chunk in fp32: four v_dot2_f32_f16
+  // against fp16 ones (exact products, fp32 sums).
+  __device__ static float sum8(uint4 v) {
+    const h2_t one = __builtin_bit_cast(h2_t, 0x3C003C00u);
+    float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.x), one, 0.f, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.y), one, s, false);
+    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.z), one, s, false);
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.w), one, s, false);
+  }
+  __device__ static f32x4_t mfma(vec8 a, vec8 b) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+  }
+};
+
 // ---------------------------------------------------------------------------
 // Small batches with X too large for LDS: K split over the waves of a workgroup.
 //
@@ -127,10 +163,11 @@ struct KsRegs {
   uint4 x[MB][8];     // X[16 mb + lane % 16][32 s + 8 (lane / 16) .. +7], s = 0..7
 };
 
-template <int NB, int MB, bool PL>
+template <int NB, int MB, bool PL, bool F16>
 __global__ void __launch_bounds__(512)
-gemm_q4_k_bf16_ksplit(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M,
-                      int kw) {
+gemm_q4_k_ksplit(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, float* y, int M, int kw) {
+  typedef StreamX<F16> XT;
+  typedef typename XT::vec8 vec8;
   extern __shared__ float ks_part[];  // [kw][NB * MB * 4][64]
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
@@ -170,8 +207,8 @@ gemm_q4_k_bf16_ksplit(const uint8_t* w, uint64_t pa, int N, int K, const uint16_
   for (int t = 0; t < NB; ++t)
 #pragma unroll
     for (int mb = 0; mb < MB; ++mb) acc[t][mb] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-  const uint32_t one2 = 0x3F803F80u;  // two bf16 ones
-  const bf16x8_t ones = __builtin_bit_cast(bf16x8_t, make_uint4(one2, one2, one2, one2));
+  const uint32_t one2 = XT::kOne2;
+  const vec8 ones = __builtin_bit_cast(vec8, make_uint4(one2, one2, one2, one2));
 
   auto step = [&](const KsRegs<NB, MB>& r) {
     float d[NB], dmin[NB];
@@ -189,30 +226,28 @@ gemm_q4_k_bf16_ksplit(const uint8_t* w, uint64_t pa, int N, int K, const uint16_
     }
 #pragma unroll
     for (int s = 0; s < 8; ++s) {
-      bf16x8_t A[MB];
+      vec8 A[MB];
       f32x4_t xs[MB];
 #pragma unroll
       for (int mb = 0; mb < MB; ++mb) {
         const uint4 v = r.x[mb][s];
-        A[mb] = __builtin_bit_cast(bf16x8_t, make_uint4(lo_pair(v.x, v.y), hi_pair(v.x, v.y),
-                                                        lo_pair(v.z, v.w), hi_pair(v.z, v.w)));
-        xs[mb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], ones, f32x4_t{0.f, 0.f, 0.f, 0.f},
-                                                         0, 0, 0);
+        A[mb] = __builtin_bit_cast(vec8, make_uint4(lo_pair(v.x, v.y), hi_pair(v.x, v.y),
+                                                    lo_pair(v.z, v.w), hi_pair(v.z, v.w)));
+        xs[mb] = XT::mfma(A[mb], ones);
       }
 #pragma unroll
       for (int t = 0; t < NB; ++t) {
         const uint32_t scw = s < 4 ? sc03[t] : sc47[t], mw = s < 4 ? m03[t] : m47[t];
         const float ds = d[t] * static_cast<float>((scw >> (8 * (s & 3))) & 0xFFu);
-        const float dmp = fmaf(128.f, ds, dmin[t] * static_cast<float>((mw >> (8 * (s & 3))) & 0xFFu));
+        const float dmp = fmaf(XT::kBias, ds, dmin[t] * static_cast<float>((mw >> (8 * (s & 3))) & 0xFFu));
         const uint2 pc = r.q[t][s >> 1];
         const uint32_t v0 = (s & 1) ? pc.x >> 4 : pc.x, v1 = (s & 1) ? pc.y >> 4 : pc.y;
-        const uint32_t b[4] = {(v0 & 0x000F000Fu) | 0x43004300u, ((v0 >> 8) & 0x000F000Fu) | 0x43004300u,
-                               (v1 & 0x000F000Fu) | 0x43004300u, ((v1 >> 8) & 0x000F000Fu) | 0x43004300u};
-        const bf16x8_t B = __builtin_bit_cast(bf16x8_t, b);
+        const uint32_t b[4] = {(v0 & 0x000F000Fu) | XT::kBias2, ((v0 >> 8) & 0x000F000Fu) | XT::kBias2,
+                               (v1 & 0x000F000Fu) | XT::kBias2, ((v1 >> 8) & 0x000F000Fu) | XT::kBias2};
+        const vec8 B = __builtin_bit_cast(vec8, b);
 #pragma unroll
         for (int mb = 0; mb < MB; ++mb) {
-          const f32x4_t S =
-              __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[mb], B, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
+          const f32x4_t S = XT::mfma(A[mb], B);
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             acc[t][mb][i] = fmaf(-dmp, xs[mb][i], fmaf(ds, S[i], acc[t][mb][i]));
@@ -323,40 +358,6 @@ __host__ __device__ constexpr size_t stream_lds_bytes(int nb) {
   return static_cast<size_t>(nb) * 8 * (16 * 32 * 2 + 16 * 4) +  // X operands + sub-block sums
          static_cast<size_t>(kStreamWaves) * 2 * 4 * 64 * 4;      // two partial tiles per wave
 }
-
-// The activation type of the streaming kernel.  bf16: the codes enter the
-// matrix cores as bf16(128 + u) (0x4300 | u).  fp16: as fp16(1024 + u)
-// (0x6400 | u, exact, the same one AND-OR per two codes); products are exact
-// in fp32 either way, and the 1024 X offset removed afterwards costs at most
-// about 2^-24 * 1024 / 8 relative to a sub-block's sum.
-template <bool F16>
-struct StreamX {
-  typedef bf16x8_t vec8;
-  static constexpr uint32_t kBias2 = 0x43004300u;  // two bf16 128.0
-  static constexpr float kBias = 128.f;
-  __device__ static float sum8(uint4 v) { return bf16x8_sum(v); }
-  __device__ static f32x4_t mfma(vec8 a, vec8 b) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-  }
-};
-template <>
-struct StreamX<true> {
-  typedef _Float16 vec8 __attribute__((ext_vector_type(8)));
-  static constexpr uint32_t kBias2 = 0x64006400u;  // two fp16 1024.0
-  static constexpr float kBias = 1024.f;
-  // Sum of the eight fp16 values of a chunk in fp32: four v_dot2_f32_f16
-  // against fp16 ones (exact products, fp32 sums).
-  __device__ static float sum8(uint4 v) {
-    const h2_t one = __builtin_bit_cast(h2_t, 0x3C003C00u);
-    float s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.x), one, 0.f, false);
-    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.y), one, s, false);
-    s = __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.z), one, s, false);
-    return __builtin_amdgcn_fdot2(__builtin_bit_cast(h2_t, v.w), one, s, false);
-  }
-  __device__ static f32x4_t mfma(vec8 a, vec8 b) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, f32x4_t{0.f, 0.f, 0.f, 0.f}, 0, 0, 0);
-  }
-};
 
 template <bool PL, bool F16>
 __global__ void __launch_bounds__(64 * kStreamWaves)
@@ -831,6 +832,22 @@ gemm_q4_k_tile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x, f
       }
 }
 
+// M <= 16 with X too large for LDS: K split over up to 8 waves per workgroup
+// (about eight waves per SIMD in all, never more than one per block).
+template <bool PL, bool F16>
+static hipError_t launch_ksplit(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* xb, float* y,
+                                int M, hipStream_t stream) {
+  const int nb = K / 256;
+  const unsigned n_groups = static_cast<unsigned>((N + 15) / 16);
+  int kw = static_cast<int>((8192 + n_groups - 1) / n_groups);
+  kw = kw < 1 ? 1 : (kw > 8 ? 8 : kw);
+  kw = kw > nb ? nb : kw;
+  const size_t lds = static_cast<size_t>(kw) * 4 * 64 * sizeof(float);
+  hipLaunchKernelGGL((gemm_q4_k_ksplit<1, 1, PL, F16>), dim3(n_groups, 1), dim3(64 * kw), lds, stream, w, pa, N,
+                     K, xb, y, M, kw);
+  return hipGetLastError();
+}
+
 // 17 <= M: runs of 4-5 weight tiles, one workgroup per CU for each batch
 // tile of 32, 64 or 128 rows (every CU gets the same work up to one tile).
 template <bool PL, bool F16>
@@ -872,28 +889,14 @@ static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, flo
                        stream, w, pa, N, K, xb, y, M);
     return hipGetLastError();
   }
-  if (M <= 16) {
-    // X too large for LDS: K split over up to 8 waves per workgroup (about
-    // eight waves per SIMD in all, never more than one per block).
-    const unsigned n_groups = static_cast<unsigned>((N + 15) / 16);
-    int kw = static_cast<int>((8192 + n_groups - 1) / n_groups);
-    kw = kw < 1 ? 1 : (kw > 8 ? 8 : kw);
-    kw = kw > nb ? nb : kw;
-    const size_t lds = static_cast<size_t>(kw) * 4 * 64 * sizeof(float);
-    hipLaunchKernelGGL((gemm_q4_k_bf16_ksplit<1, 1, PL>), dim3(n_groups, 1), dim3(64 * kw), lds, stream,
-                       w, pa, N, K, xb, y, M, kw);
-    return hipGetLastError();
-  }
+  if (M <= 16) return launch_ksplit<PL, false>(w, pa, N, K, xb, y, M, stream);
   return launch_tile<PL, false>(w, pa, N, K, xb, y, M, stream);
 }
 
-// fp16 activations: up to 16 rows, the fp16 streaming kernel where X fits
-// its LDS copy; from 17 rows, the fp16 tile kernels (any K).
-bool gemm_q4_k_f16_fits(int64_t cols, int64_t batch) {
-  return batch >= 17 ||
-         (batch >= 1 &&
-          stream_lds_bytes(static_cast<int>(cols / 256)) <= static_cast<size_t>(device_lds_per_block()));
-}
+// fp16 activations: the kernels of the bf16 path with fp16 operands (up to
+// 16 rows the streaming kernel where X fits its LDS copy, else the K-split
+// kernel; from 17 rows the tile kernels).
+bool gemm_q4_k_f16_fits(int64_t cols, int64_t batch) { return cols >= 256 && batch >= 1; }
 
 hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                          hipStream_t stream) {
@@ -910,20 +913,18 @@ hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t 
   int G = device_cus();
   if (G > T) G = T;
   if (G < (T + 7) / 8) G = (T + 7) / 8;
-  for (int64_t m0 = 0; m0 < batch; m0 += 16) {
-    const int M = static_cast<int>(batch - m0 < 16 ? batch - m0 : 16);
-    const uint16_t* xh = static_cast<const uint16_t*>(x) + m0 * K;
-    float* yc = y + m0 * N;
-    if (W.layout == QMV_LAYOUT_PLANES)
-      hipLaunchKernelGGL((gemm_q4_k_stream<true, true>), dim3(G), dim3(64 * kStreamWaves),
-                         stream_lds_bytes(K / 256), stream, w, W.scales_offset, N, K, xh, yc, M);
-    else
-      hipLaunchKernelGGL((gemm_q4_k_stream<false, true>), dim3(G), dim3(64 * kStreamWaves),
-                         stream_lds_bytes(K / 256), stream, w, W.scales_offset, N, K, xh, yc, M);
-    const hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  const int M = static_cast<int>(batch);
+  const uint16_t* xh = static_cast<const uint16_t*>(x);
+  if (stream_lds_bytes(K / 256) > static_cast<size_t>(device_lds_per_block()))
+    return W.layout == QMV_LAYOUT_PLANES ? launch_ksplit<true, true>(w, W.scales_offset, N, K, xh, y, M, stream)
+                                         : launch_ksplit<false, true>(w, W.scales_offset, N, K, xh, y, M, stream);
+  if (W.layout == QMV_LAYOUT_PLANES)
+    hipLaunchKernelGGL((gemm_q4_k_stream<true, true>), dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(K / 256),
+                       stream, w, W.scales_offset, N, K, xh, y, M);
+  else
+    hipLaunchKernelGGL((gemm_q4_k_stream<false, true>), dim3(G), dim3(64 * kStreamWaves), stream_lds_bytes(K / 256),
+                       stream, w, W.scales_offset, N, K, xh, y, M);
+  return hipGetLastError();
 }
 
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,

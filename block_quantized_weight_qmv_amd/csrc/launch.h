@@ -71,10 +71,9 @@ hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t bat
 constexpr int64_t kMfmaMinBatch = QMV_MFMA_MIN_BATCH;
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t s);
-// Q4_K x fp16 on the matrix cores with fp16 operands: the streaming kernel
-// up to 16 rows when X fits its LDS copy, the tile kernels from 17 rows
-// (gemm_q4_k_f16_fits).  qmv_gemv takes it from kMfmaMinF16Batch rows;
-// below, the multi-row GEMV is faster.
+// Q4_K x fp16 on the matrix cores with fp16 operands: the kernels of the
+// bf16 path (streaming or K-split up to 16 rows, tiles from 17).  qmv_gemv
+// takes it from kMfmaMinF16Batch rows; below, the multi-row GEMV is faster.
 #ifndef QMV_MFMA_MIN_F16_BATCH
 #define QMV_MFMA_MIN_F16_BATCH 5
 #endif

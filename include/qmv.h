@@ -212,9 +212,8 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * read once per two or four activation rows (fp32: two) for cols <= 4096
  * (Q8_0: 2048), and, for fp16/bf16 rows, once per two rows up to eight times
  * that width (Q4_K x bf16: at two rows); each output row equals bit for bit
- * the batch-1 call on that activation row.  Q4_K x fp16 runs on the matrix
- * cores with fp16 operands (exact products, fp32 sums) at 5..16 rows with
- * cols <= 4096 and from 17 rows at any width.  Other Q4_K x bf16 calls with batch >= 2 run the
+ * the batch-1 call on that activation row.  Q4_K x fp16 with 5 or more rows
+ * runs on the matrix cores with fp16 operands (exact products, fp32 sums).  Other Q4_K x bf16 calls with batch >= 2 run the
  * matrix-core path (weights read once for up to 16 activation rows, once per
  * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
  * independent of timing).  Otherwise each activation row is a GEMV over the

@@ -52,7 +52,7 @@ def _library_kernels():
             continue
         if ("qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemv_rows_split_kernel<" in line
                 or "qmv::gemm_q4_k_bf16_" in line or "qmv::gemm_q4_k_stream<" in line
-                or "qmv::gemm_q4_k_tile<" in line):
+                or "qmv::gemm_q4_k_tile<" in line or "qmv::gemm_q4_k_ksplit<" in line):
             sym = line.split(" ", 2)[2]
             sym = sym[5:] if sym.startswith("void ") else sym
             names.add(sym.split("(")[0])
@@ -133,7 +133,8 @@ def test_small_batch_overrides_name_library_kernels(config, batch, x_dtype):
     assert multi, plan["kname"]
 
 
-@pytest.mark.parametrize("config,batch,x_dtype", [(2, 2, None), (6, 2, "bf16"), (6, 4, "f16"), (3, 2, "f16")])
+@pytest.mark.parametrize("config,batch,x_dtype", [(2, 2, None), (6, 2, "bf16"), (6, 4, "f16"), (3, 2, "f16"),
+                                                  (2, 8, "bf16")])
 def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
     # the down projections (several waves along K) take the K-split form
     names = _library_kernels()
@@ -156,3 +157,13 @@ def test_q4_k_f16_batches_name_the_f16_matrix_core_kernels(batch, kernel):
     plan = bench.workload_plan(5, batch, separate=False, layout=layout, x_dtype="f16")
     assert plan["kname"] == [kernel]
     assert kernel in names
+
+
+@pytest.mark.parametrize("config,batch,kernel", [(3, 8, "qmv::gemm_q4_k_ksplit<1, 1, false, true>"),
+                                                 (3, 16, "qmv::gemm_q4_k_ksplit<1, 1, false, true>")])
+def test_q4_k_f16_wide_batches_name_the_f16_ksplit_kernel(config, batch, kernel):
+    # the 7B layer's down projection (K = 18944) at 5-16 fp16 rows: the K-split
+    # matrix-core kernel with fp16 operands
+    names = _library_kernels()
+    plan = bench.workload_plan(config, batch, separate=False, layout="blocks", x_dtype="f16")
+    assert plan["kname"][-1] == kernel and kernel in names

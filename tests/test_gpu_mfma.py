@@ -110,11 +110,12 @@ def test_full_size_batched_ffn_sampled_rows(batch):
 @pytest.mark.parametrize("layout", ["blocks", "planes"])
 @pytest.mark.parametrize("rows,nblk,batch", [(67, 14, 5), (130, 3, 16), (1, 1, 8), (33, 16, 9), (200, 14, 12),
                                              (16, 2, 7), (40, 5, 17), (70, 3, 33), (33, 14, 64), (9, 2, 100),
-                                             (17, 74, 20), (130, 3, 129)])
+                                             (17, 74, 20), (130, 3, 129), (33, 74, 5), (70, 20, 16), (5, 130, 9)])
 def test_mfma_f16_matches_oracle(layout, rows, nblk, batch):
-    # Q4_K x fp16 from 5 rows: the streaming kernel (5-16 rows, X in LDS) or
-    # the tile kernels (17 rows up, any K; ragged batch tiles) with fp16
-    # operands (codes as fp16(1024 + u), exact; fp32 sums)
+    # Q4_K x fp16 from 5 rows: the streaming kernel (5-16 rows, X in LDS),
+    # the K-split kernel (5-16 rows, K > 4096) or the tile kernels (17 rows
+    # up, any K; ragged batch tiles) with fp16 operands (codes as
+    # fp16(1024 + u), exact; fp32 sums)
     cols = nblk * 256
     say(f"mfma fp16 q4_k {layout} {rows}x{cols} batch {batch}")
     w = Weights("q4_k", rows, cols, seed=900 + rows + nblk)

@@ -117,6 +117,8 @@ def test_rows_split_k_equal_batch1_and_oracle(fmt, layout, x_dtype, batch, rows,
     # matrices wider than a wave's K slice: the K-split form, two activation
     # rows per pass (odd batches end in a half-used pass)
     cols = nblk * 256
+    if fmt == "q4_k" and x_dtype == "f16" and batch >= 5:
+        pytest.skip("Q4_K x fp16 from 5 rows runs on the matrix cores (test_gpu_mfma.py)")
     if fmt == "q4_k" and x_dtype == "bf16" and (batch > 2 or cols > 8 * 4096):
         pytest.skip("Q4_K x bf16 of wide matrices above two rows, or above eight waves along K, "
                     "runs on the matrix cores (test_gpu_mfma.py)")
