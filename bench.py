@@ -68,7 +68,8 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str = "blocks") -> str:
+def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str = "blocks",
+                rows_list=None) -> str:
     """Instantiation the library launches for matrices of these widths in one
     launch (mirrors the dispatch in api.cpp and the GEMV launcher: Q4_K x bf16
     with batch >= 2 not taken by the multi-row GEMV (below) -> one of the
@@ -80,8 +81,16 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     columns, Q8_0 2048) -> the multi-row GEMV (fp32: two rows per pass);
     fp16/bf16 against two to eight waves along K -> its K-split form, except
     Q4_K x bf16 above two rows; Q4_K x fp16 from 5 rows -> the matrix-core
-    kernels of bf16 with fp16 operands)."""
+    kernels of bf16 with fp16 operands; two or more small Q4_K matrices at
+    5-16 fp16/bf16 rows (rows_list summing to at most 8192) -> one multi-row
+    launch)."""
     nb_max = max(cols_list) // 256
+    if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and 5 <= batch <= 16 and len(cols_list) >= 2
+            and max(cols_list) <= 4096 and rows_list is not None and sum(rows_list) <= 8192):
+        # several small matrices (q, k, v): one multi-row launch, groups of four rows
+        pol = "Q4KPlanesPolicy" if layout == "planes" else "Q4KPolicy"
+        xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
+        return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, 1, 3, 256, 4>"
     if fmt == "q4_k" and x_dtype == "f16" and batch >= 17:  # fp16 on the tile kernels
         pl = "true" if layout == "planes" else "false"
         mb = 1 if batch <= 32 else (2 if batch <= 64 else 4)
@@ -248,7 +257,8 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
     gbytes = [sum(wbytes[m] + batch * mats[m][1] * 4 for m in g) + batch * mats[g[0]][2] * xb
               for g in groups]
     gflops = [sum(2.0 * batch * mats[m][1] * mats[m][2] for m in g) for g in groups]
-    kname = [kernel_name(fmt, [mats[m][2] for m in g], x_dtype, batch, layout) for g in groups]
+    kname = [kernel_name(fmt, [mats[m][2] for m in g], x_dtype, batch, layout, [mats[m][1] for m in g])
+             for g in groups]
     balance = PEAK_TFLOPS_BF16 * 1e12 / (PEAK_GBPS * 1e9)
     bound = ["mfma" if kname[i].startswith("qmv::gemm") and gflops[i] / gbytes[i] > balance
              else "hbm" for i in range(len(groups))]

@@ -45,6 +45,11 @@ constexpr int64_t kRowsMaxBf16Batch = QMV_ROWS_MAX_BF16_BATCH;
 #define QMV_ROWS_SPLIT_MAX_WAVES 8
 #endif
 constexpr int64_t kRowsSplitMaxWaves = QMV_ROWS_SPLIT_MAX_WAVES;
+// Q4_K calls of two or more matrices within one wave's K slice, at most
+// kRowsSmallMultiMaxRows rows in all, at 5..kRowsSmallMultiMaxBatch fp16/bf16
+// rows: one multi-row launch instead of a matrix-core launch per matrix.
+constexpr int64_t kRowsSmallMultiMaxBatch = 16;
+constexpr int64_t kRowsSmallMultiMaxRows = 8192;
 hipError_t gemv_q4_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,
                           hipStream_t s);
 hipError_t gemv_q6_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,

@@ -244,7 +244,11 @@ typedef struct qmv_gemv_item {
  * (QMV_ERR_UNSUPPORTED otherwise).  Results equal n separate qmv_gemv calls
  * up to float32 summation order; where the calls would take the multi-row
  * GEMV or the matrix-core path, the launch routes each item as its own call
- * would, and results equal bit for bit. */
+ * would, and results equal bit for bit -- except for two or more Q4_K
+ * matrices of at most 4096 columns and 8192 rows in all at 5..16 fp16/bf16
+ * rows, which share one multi-row launch (each output row then equals the
+ * batch-1 result bit for bit) where a call of one of them alone would take
+ * the matrix cores. */
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch,
                        const qmv_gemv_item* items, int32_t n, void* stream);
 

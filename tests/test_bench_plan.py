@@ -167,3 +167,14 @@ def test_q4_k_f16_wide_batches_name_the_f16_ksplit_kernel(config, batch, kernel)
     names = _library_kernels()
     plan = bench.workload_plan(config, batch, separate=False, layout="blocks", x_dtype="f16")
     assert plan["kname"][-1] == kernel and kernel in names
+
+
+@pytest.mark.parametrize("x_dtype,batch", [("bf16", 8), ("f16", 16)])
+def test_small_multi_matrix_batches_name_the_rows_kernel(x_dtype, batch):
+    # the 7B layer's q+k+v (4608 rows in three matrices) at 5-16 rows: one
+    # multi-row launch; o (one matrix) stays on the matrix cores
+    names = _library_kernels()
+    plan = bench.workload_plan(3, batch, separate=False, layout="planes", x_dtype=x_dtype)
+    qkv, o = plan["kname"][0], plan["kname"][1]
+    assert qkv.startswith("qmv::gemv_rows_kernel<") and qkv in names, qkv
+    assert o.startswith("qmv::gemm_q4_k_"), o

@@ -136,3 +136,25 @@ def test_multi_q4_k_bf16_batches_per_item_routing(batch):
         assert np.all(err <= TOL), (w.rows, w.cols, err.max())
         alone = w.gemv(x, "bf16", batch).cpu().numpy()
         assert np.array_equal(got, alone), (w.rows, w.cols)
+
+
+@pytest.mark.parametrize("x_dtype,batch", [("bf16", 5), ("bf16", 8), ("f16", 16)])
+def test_multi_small_q4_k_matrices_share_one_multi_row_launch(x_dtype, batch):
+    """Several small Q4_K matrices (q, k, v shaped, scaled down) at 5-16 rows:
+    one multi-row launch, so every output row equals the batch-1 GEMV of that
+    activation row bitwise, and the oracle within the gate."""
+    items = [(192, 14), (32, 14), (32, 14)]
+    x_np = gen_x(batch, 14 * 256, x_dtype, seed=2100 + batch)
+    xd = to_dev_x(x_np, x_dtype)
+    ws = [Weights("q4_k", r, nb * 256, seed=2000 + i) for i, (r, nb) in enumerate(items)]
+    ys = [torch.full((batch, w.rows), -3.0, dtype=torch.float32, device=DEV) for w in ws]
+    say(f"multi small q4_k x {x_dtype} batch {batch}")
+    qmv.qmv_gemv_multi("q4_k", x_dtype, batch, [(w.desc, xd, y) for w, y in zip(ws, ys)])
+    torch.cuda.synchronize()
+    for w, y in zip(ws, ys):
+        got = y.cpu().numpy()
+        for i in range(batch):
+            one = torch.empty(1, w.rows, dtype=torch.float32, device=DEV)
+            w.gemv(xd[i:i + 1].clone(), x_dtype, 1, y=one)
+            np.testing.assert_array_equal(got[i], one.cpu().numpy()[0])
+        assert np.all(oracle.normwise_rel_err(got, oracle_y(w, x_np, x_dtype)) <= TOL)
