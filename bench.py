@@ -172,46 +172,100 @@ def measured_traffic(kernel: str, workload: str):
     return rec.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(mats, fmt, x_dtype, fields_list, xs, seconds):
-    """Time the CPU oracle (decode to float64 + float64 dot) on row chunks of the workload."""
+def _cpu_model() -> dict:
+    """The host CPU as /proc/cpuinfo names it (model name, family, model, stepping)."""
+    info = {}
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if not ln.strip():
+                    break   # first processor only
+                k, _, v = ln.partition(":")
+                info[k.strip()] = v.strip()
+    except OSError:
+        pass
+    return {"model_name": info.get("model name", ""), "family": info.get("cpu family", ""),
+            "model": info.get("model", ""), "stepping": info.get("stepping", ""),
+            "vendor": info.get("vendor_id", "")}
+
+
+def _median_of_3(fn):
+    """Median of three timed calls after one untimed warm-up call (seconds)."""
+    fn()
+    ts = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        fn()
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[1]
+
+
+def cpu_baseline(mats, fmt, x_dtype, fields_list, xs, sample_rows):
+    """Time the CPU oracle on a bounded sample of every matrix of the workload.
+
+    For each matrix, a block of `sample_rows` rows (all rows if fewer) is packed
+    by the oracle and timed in two parts, each the median of three runs after
+    one warm-up: the float64 decode (oracle.dequant64, numpy, one thread) and
+    the float64 matrix-vector product of the decoded rows (BLAS).  Per-row times
+    are scaled to the whole matrix, so the figures describe one full pass over
+    the workload (one step).  The product is timed again with BLAS limited to
+    one thread."""
     import numpy as np
 
     import oracle
     try:
-        from threadpoolctl import threadpool_info
+        from threadpoolctl import threadpool_info, threadpool_limits
         blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()
                             if i.get("user_api") == "blas"] or [1])
     except Exception:  # noqa: BLE001
-        blas_threads = 1
-    chunk = 512
-    done_bytes, spent, rows_done = 0, 0.0, 0
-    it = 0
-    while spent < seconds and it < 10000:
-        m = it % len(mats)
-        name, rows, cols = mats[m]
-        r0 = (it // len(mats)) * chunk % rows
-        r1 = min(rows, r0 + chunk)
-        ids = np.arange(r0, r1)
+        threadpool_limits, blas_threads = None, 1
+    xb = {"f32": 4, "f16": 2, "bf16": 2}[x_dtype]
+    dq_s = gemv_s = gemv1_s = 0.0
+    step_bytes = 0
+    rows_timed = 0
+    t_all = time.perf_counter()
+    for m, (name, rows, cols) in enumerate(mats):
+        n = min(rows, sample_rows)
+        ids = np.arange(n)
         sub = {k: v[ids] for k, v in fields_list[m].items()}
-        data = oracle.pack(fmt, sub, len(ids), cols)
-        t0 = time.perf_counter()
-        oracle.gemv64(fmt, data, len(ids), cols, xs[m], x_dtype)
-        spent += time.perf_counter() - t0
-        xb = {"f32": 4, "f16": 2, "bf16": 2}[x_dtype]
-        done_bytes += data.size + cols * xb + len(ids) * 4
-        rows_done += len(ids)
-        it += 1
-    cpu_model = ""
-    try:
-        with open("/proc/cpuinfo") as fh:
-            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
-    except OSError:
-        pass
-    return {"value": done_bytes / spent / 1e9, "unit": "GB/s", "cores": int(blas_threads),
-            "kind": "oracle", "cpu_model": cpu_model, "affinity_cores": len(os.sched_getaffinity(0)),
-            "sample": (f"{rows_done} rows in {chunk}-row chunks cycling over the workload's "
-                       f"matrices, {spent:.1f} s; numpy float64 decode (1 thread) + float64 "
-                       f"matrix-vector product (BLAS, {blas_threads} threads); packing excluded")}
+        data = oracle.pack(fmt, sub, n, cols)
+        x64 = oracle.x_to_f64(xs[m], x_dtype).reshape(-1, cols)
+        w = {}
+
+        def dq():
+            w["w"] = oracle.dequant64(fmt, data, n, cols)
+
+        t_dq = _median_of_3(dq)
+        t_mv = _median_of_3(lambda: x64 @ w["w"].T)
+        if threadpool_limits is not None:
+            with threadpool_limits(limits=1, user_api="blas"):
+                t_mv1 = _median_of_3(lambda: x64 @ w["w"].T)
+        else:
+            t_mv1 = t_mv
+        scale = rows / n
+        dq_s += t_dq * scale
+        gemv_s += t_mv * scale
+        gemv1_s += t_mv1 * scale
+        rows_timed += n
+        step_bytes += data.size * scale + x64.size * xb + x64.shape[0] * rows * 4
+    wall = time.perf_counter() - t_all
+    step = dq_s + gemv_s
+    step1 = dq_s + gemv1_s
+    return {"value": step_bytes / step / 1e9, "unit": "GB/s", "cores": int(blas_threads),
+            "kind": "oracle",
+            "dequant_ms_per_step": round(dq_s * 1e3, 3),
+            "gemv64_ms_per_step": round(gemv_s * 1e3, 3),
+            "gemv_per_s": round(len(mats) / step, 3),
+            "single_thread": {"value": step_bytes / step1 / 1e9, "unit": "GB/s",
+                              "gemv64_ms_per_step": round(gemv1_s * 1e3, 3),
+                              "gemv_per_s": round(len(mats) / step1, 3)},
+            "blas_threads": int(blas_threads), "affinity_cores": len(os.sched_getaffinity(0)),
+            "cpu": _cpu_model(),
+            "sample": (f"the first {sample_rows} rows of each of the workload's {len(mats)} matrices "
+                       f"({rows_timed} rows, {wall:.1f} s of wall time); per matrix the oracle's "
+                       "float64 decode (numpy, 1 thread) and its float64 matrix-vector product "
+                       f"(BLAS, {blas_threads} threads; again with 1) each timed as the median of 3 "
+                       "after 1 warm-up, per-row times scaled to the full matrices; packing excluded")}
 
 
 PEAK_TFLOPS_BF16 = 2500.0   # MI355X dense bf16 matrix cores, vendor figure
@@ -404,7 +458,10 @@ def main() -> int:
     ap.add_argument("--rotate-gib", type=float, default=1.25)
     ap.add_argument("--settle-ms", type=float, default=300.0,
                     help="untimed graph replays before each timed one (steady-state clocks)")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-sample-rows", type=int, default=2048,
+                    help="rows of each matrix the CPU oracle baseline times")
+    ap.add_argument("--replays", type=int, default=11,
+                    help="timed graph replays per region; the median is reported")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--separate", action="store_true", help="one launch per matrix")
     ap.add_argument("--layout", choices=["auto", "blocks", "planes"], default="auto",
@@ -518,6 +575,7 @@ def main() -> int:
     # rotation over weight copies and the launch order are unchanged -> its average
     # launch duration (the duration plus the small gap between graph nodes).
     cap = torch.cuda.Stream(dev)
+    spread = []   # (min, median, max) ms of each timed region's replays
 
     def timed_graph(gis):
         g = torch.cuda.CUDAGraph()
@@ -536,21 +594,32 @@ def main() -> int:
         while time.perf_counter() < t_end:
             g.replay()
             torch.cuda.synchronize()
-        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t0.record(stream)
-        g.replay()                    # replays on the current stream
-        t1.record(stream)
-        torch.cuda.synchronize()
-        return t0.elapsed_time(t1)
+        # median of --replays timed replays, each bracketed by events on the
+        # replay stream (the current stream) and a synchronize on both sides
+        times = []
+        for _ in range(args.replays):
+            t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            t0.record(stream)
+            g.replay()
+            t1.record(stream)
+            torch.cuda.synchronize()
+            times.append(t0.elapsed_time(t1))
+        times.sort()
+        spread.append((times[0], times[len(times) // 2], times[-1]))
+        return times[len(times) // 2]
 
     total_ms = timed_graph(list(range(len(groups))))
     ms_per_step = total_ms / args.steps
+    step_spread = [round(v / args.steps, 5) for v in spread[-1]]
     kern = {}
     for k, gis in by_kernel.items():
         el = timed_graph(gis)
         kern[k] = {"launches": ["+".join(names[m] for m in groups[gi]) for gi in gis],
                    "launches_per_step": len(gis),
                    "avg_launch_us": round(el * 1e3 / (args.steps * len(gis)), 3),
+                   "avg_launch_us_min_max": [round(spread[-1][0] * 1e3 / (args.steps * len(gis)), 3),
+                                             round(spread[-1][2] * 1e3 / (args.steps * len(gis)), 3)],
                    "bytes_per_launch": sum(gbytes[gi] for gi in gis) / len(gis)}
         kern[k]["GBps"] = round(kern[k]["bytes_per_launch"] / (kern[k]["avg_launch_us"] * 1e-6) / 1e9, 1)
     if not args.separate or len(groups) > 1:
@@ -559,7 +628,9 @@ def main() -> int:
             el = timed_graph([gi])
             us = el * 1e3 / args.steps
             per_launch["+".join(names[m] for m in g)] = {
-                "us": round(us, 3), "GBps": round(gbytes[gi] / (us * 1e-6) / 1e9, 1)}
+                "us": round(us, 3), "GBps": round(gbytes[gi] / (us * 1e-6) / 1e9, 1),
+                "us_min_max": [round(spread[-1][0] * 1e3 / args.steps, 3),
+                               round(spread[-1][2] * 1e3 / args.steps, 3)]}
     else:
         per_launch = None
     dom_avg_us = kern[dom]["avg_launch_us"]
@@ -598,10 +669,12 @@ def main() -> int:
         "steps": args.steps,
         "warmup": args.warmup,
         "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step_min_median_max": step_spread,
+        "timed_replays": args.replays,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16" if dom.startswith("qmv::gemm") else "fp32",
+        "dtype": {"f32": "fp32", "f16": "fp16", "bf16": "bf16"}[x_dtype],
         "data": "synthetic",
         "config": {"workload": workload, "format": fmt, "layout": layout, "batch": batch, "x_dtype": x_dtype,
                    "matrices": {n: f"{r}x{c}" for n, r, c in mats},
@@ -618,14 +691,15 @@ def main() -> int:
                      "traffic": measured_traffic(dom, workload),
                      "kernel": dom, "avg_launch_us": round(dom_avg_us, 3),
                      "launches_per_step": len(by_kernel[dom]),
-                     "timing": "HIP events around a graph replay of the K steps restricted "
-                               "to this kernel's launches, on the replay stream, after "
+                     "timing": "median of the HIP-event times of "
+                               f"{args.replays} graph replays of the K steps restricted to "
+                               "this kernel's launches, on the replay stream, after "
                                f"{args.settle_ms:g} ms of untimed replays",
                      "bytes_per_launch": round(dom_bytes_per_launch, 1),
                      "flops_per_launch": round(dom_flops_per_launch, 1)},
     }
     if not args.no_cpu_baseline:
-        rec["cpu_baseline"] = cpu_baseline(mats, fmt, x_dtype, fields_list, xs, args.cpu_seconds)
+        rec["cpu_baseline"] = cpu_baseline(mats, fmt, x_dtype, fields_list, xs, args.cpu_sample_rows)
     print(json.dumps(rec), flush=True)
     return 0
 

@@ -21,8 +21,7 @@ ARCH = "gfx950"
 COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", f"-I{INCLUDE}", f"-I{CSRC}"]
 # Device code: gfx950 only; packed-fp32 VALU forms are disabled (the host pass
 # warns that it does not know the feature, which is harmless).
-DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-          "-munsafe-fp-atomics"]
+DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 HIP_SOURCES = ["api.cpp", "gemv_q8_0.hip", "gemv_q4_k.hip", "gemv_q5_k.hip", "gemv_q6_k.hip",
                "gemv_int4_g128.hip", "gemm_q4_k_mfma.hip", "dequant.hip", "repack.hip", "probe.hip"]

@@ -5,6 +5,11 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+#include <map>
+#include <mutex>
+#include <tuple>
+
 namespace qmv {
 
 // Activation element types as seen by the kernels.
@@ -259,26 +264,56 @@ __device__ __forceinline__ void finish_half_xslice(const uint4* raw, bool ok, Ha
 }
 
 // Host side: compute units and LDS bytes per workgroup of the current device,
-// queried once per device (gfx950: 256 CUs, 160 KB).
-inline int device_attr_cached(hipDeviceAttribute_t attr, int (&cache)[64], int fallback) {
+// queried once per device (gfx950: 256 CUs, 160 KB).  The entries are atomics:
+// host threads may race to fill one, and each stores the same value.
+inline int device_attr_cached(hipDeviceAttribute_t attr, std::atomic<int> (&cache)[64], int fallback) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
-    int v = 0;
+  int v = cache[dev].load(std::memory_order_relaxed);
+  if (v == 0) {
     if (hipDeviceGetAttribute(&v, attr, dev) != hipSuccess || v <= 0) v = fallback;
-    cache[dev] = v;
+    cache[dev].store(v, std::memory_order_relaxed);
   }
-  return cache[dev];
+  return v;
 }
 
 inline int device_cus() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   return device_attr_cached(hipDeviceAttributeMultiprocessorCount, cache, 256);
 }
 
 inline int device_lds_per_block() {
-  static int cache[64];
+  static std::atomic<int> cache[64];
   return device_attr_cached(hipDeviceAttributeMaxSharedMemoryPerBlock, cache, 65536);
+}
+
+// Workgroups of kernel `fn` the current device holds at once, for a launch of
+// `block` threads and `lds` bytes of dynamic LDS: compute units x the
+// occupancy query.  One entry per (device, kernel, block, lds), filled on
+// first use under a lock.
+inline int64_t resident_workgroups_of(const void* fn, int block, size_t lds) {
+  static std::mutex mu;
+  static std::map<std::tuple<int, const void*, int, size_t>, int64_t> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) dev = 0;
+  const auto key = std::make_tuple(dev, fn, block, lds);
+  {
+    std::lock_guard<std::mutex> g(mu);
+    const auto it = cache.find(key);
+    if (it != cache.end()) return it->second;
+  }
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, block, lds) != hipSuccess || per_cu <= 0)
+    per_cu = 1;
+  const int64_t v = static_cast<int64_t>(device_cus()) * per_cu;
+  std::lock_guard<std::mutex> g(mu);
+  cache[key] = v;
+  return v;
+}
+
+template <typename K>
+inline int64_t resident_workgroups(K kernel, int block, size_t lds) {
+  return resident_workgroups_of(reinterpret_cast<const void*>(kernel), block, lds);
 }
 
 }  // namespace qmv

@@ -517,26 +517,6 @@ inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_wav
   return wg;
 }
 
-// Workgroups of `kernel` (block threads) the current device holds at once;
-// queried once per kernel and device.
-template <typename K>
-inline int64_t resident_workgroups(K kernel, int block) {
-  static int cache[64];  // per device; 0 = not yet queried
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) dev = 0;
-  if (cache[dev] == 0) {
-    int cus = 0, per_cu = 0;
-    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
-        cus <= 0 || per_cu <= 0) {
-      cus = 256;
-      per_cu = 1;
-    }
-    cache[dev] = cus * per_cu;
-  }
-  return cache[dev];
-}
-
 // Launch shape.  Waves stream their rows with two tiles in flight; the HBM
 // queue holds all of them, so a request waits about (bytes in flight) /
 // bandwidth.  Enough waves keep the memory busy and the SIMDs fed, but every
@@ -560,6 +540,16 @@ constexpr int kMinRowsPerWave = QMV_MIN_ROWS_PER_WAVE;
 // waves per SIMD was slower).
 constexpr int kLongRowsPerWave = 48;
 
+// LDS of the shared-activation kernels: the x copy of the launch's longest
+// row, in 16-byte chunks rounded up to a multiple of 16 (xshared_slot).
+template <typename XT>
+inline size_t sx_lds_bytes(const GemvCall* calls, int n) {
+  int64_t cols = 0;
+  for (int i = 0; i < n; ++i) cols = calls[i].W->cols > cols ? calls[i].W->cols : cols;
+  const int64_t chunks = (cols * static_cast<int64_t>(sizeof(XT)) / 16 + 15) / 16 * 16;
+  return static_cast<size_t>(chunks) * 16;
+}
+
 template <class P, typename XT, int R, int D, int MAXT, bool SX>
 hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream,
                       int waves_per_simd) {
@@ -570,7 +560,10 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   int64_t wave_rows = 0;
   for (int i = 0; i < n; ++i)
     wave_rows += calls[i].W->rows * ((calls[i].W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
-  const int64_t resident = resident_workgroups(kernel, block) * waves;
+  // dynamic LDS: the x copy (SX), else at most kMaxPartStride partial sums per wave
+  size_t lds_max = static_cast<size_t>(waves) * kMaxPartStride * sizeof(float);
+  if (SX) lds_max = sx_lds_bytes<XT>(calls, n);
+  const int64_t resident = resident_workgroups(kernel, block, lds_max) * waves;
   if (waves_per_simd == 2 && wave_rows >= static_cast<int64_t>(cus) * 4 * 2 * kLongRowsPerWave)
     waves_per_simd = 3;
   int64_t target = wave_rows / kMinRowsPerWave;
@@ -585,12 +578,7 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   GemvLaunch L;
   const int grid = plan_gemv<P, R>(calls, n, waves, target, &L);
   size_t lds = static_cast<size_t>(waves) * L.part_stride * sizeof(float);
-  if (SX) {  // the x copy: the longest row's chunks, rounded up to 16 (xshared_slot)
-    int64_t cols = 0;
-    for (int i = 0; i < n; ++i) cols = calls[i].W->cols > cols ? calls[i].W->cols : cols;
-    const int64_t chunks = (cols * static_cast<int64_t>(sizeof(XT)) / 16 + 15) / 16 * 16;
-    lds = static_cast<size_t>(chunks) * 16;
-  }
+  if (SX) lds = sx_lds_bytes<XT>(calls, n);
   hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(block), lds, stream,
                      L);
   return hipGetLastError();
@@ -616,7 +604,8 @@ hipError_t launch_rows(const GemvCall* calls, int n, int64_t batch, hipStream_t 
     if (calls[i].W->cols > P::kColsPerWave) return hipErrorInvalidValue;
     wave_rows += calls[i].W->rows;
   }
-  const int64_t resident = resident_workgroups(kernel, 64 * kWaves) * kWaves;
+  const size_t lds = static_cast<size_t>(NBR) * sizeof(typename P::template XSliceT<XT>) * 64;
+  const int64_t resident = resident_workgroups(kernel, 64 * kWaves, lds) * kWaves;
   int64_t target = wave_rows / kMinRowsPerWave;
   if (target > static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd) target = static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd;
   if (target < static_cast<int64_t>(cus) * 4) target = static_cast<int64_t>(cus) * 4;
@@ -626,7 +615,6 @@ hipError_t launch_rows(const GemvCall* calls, int n, int64_t batch, hipStream_t 
   if (target > resident) target = resident;
   GemvLaunch L;
   const int grid = plan_gemv<P, R>(calls, n, kWaves, target, &L);
-  const size_t lds = static_cast<size_t>(NBR) * sizeof(typename P::template XSliceT<XT>) * 64;
   hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>((batch + NBR - 1) / NBR)),
                      dim3(64 * kWaves), lds, stream, L, static_cast<int>(batch));
   return hipGetLastError();
@@ -648,7 +636,8 @@ hipError_t launch_rows_split(const GemvCall* calls, int n, int64_t batch, hipStr
   int64_t wave_rows = 0;
   for (int i = 0; i < n; ++i)
     wave_rows += calls[i].W->rows * ((calls[i].W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
-  const int64_t resident = resident_workgroups(kernel, 64 * waves) * waves;
+  const int64_t resident =
+      resident_workgroups(kernel, 64 * waves, static_cast<size_t>(waves) * kMaxPartStride * 2 * sizeof(float)) * waves;
   int64_t target = wave_rows / kMinRowsPerWave;
   if (target > static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd) target = static_cast<int64_t>(cus) * 4 * kMaxWavesPerSimd;
   if (target < static_cast<int64_t>(cus) * 4) target = static_cast<int64_t>(cus) * 4;

@@ -16,7 +16,9 @@ import os
 import numpy as np
 
 PKG_DIR = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(PKG_DIR, "libqmv.so")
+# QMV_LIBRARY names another build of the same library (the sanitizer build of
+# the CPU test suite); by default the in-tree libqmv.so.
+LIB_PATH = os.environ.get("QMV_LIBRARY") or os.path.join(PKG_DIR, "libqmv.so")
 
 FMT = {"q8_0": 1, "q4_k": 2, "q6_k": 3, "int4_g128": 4, "q5_k": 5}
 DTYPE = {"f32": 0, "f16": 1, "bf16": 2}
@@ -120,6 +122,39 @@ def _stream(stream, *tensors):
     return None
 
 
+# Tensor dtypes accepted for each activation / output dtype code (bf16 may
+# also arrive as its 16-bit patterns).
+_TORCH_OK = {0: ("float32",), 1: ("float16",), 2: ("bfloat16", "int16", "uint16")}
+_ELEM = {0: 4, 1: 2, 2: 2}
+
+
+def _check_dev(t, what: str, dtype_code: int | None, min_elems: int) -> None:
+    """Refuse a device buffer the kernels could not use safely.
+
+    The C ABI sees raw pointers only, so this is the one layer that can check
+    a torch tensor before the kernels read or write through it: it must live
+    on the GPU, be contiguous, have the element type of ``dtype_code`` (None:
+    any) and hold at least ``min_elems`` elements of that type.  Integer
+    addresses are passed through unchecked (the caller vouches for them)."""
+    if t is None or isinstance(t, int):
+        return
+    if isinstance(t, np.ndarray):
+        raise QmvError(-6, f"{what}: a host numpy array; device memory (a GPU tensor) is required")
+    if not getattr(t, "is_cuda", False):
+        raise QmvError(-6, f"{what}: tensor is not on a GPU")
+    if not t.is_contiguous():
+        raise QmvError(-6, f"{what}: tensor is not contiguous")
+    if dtype_code is not None:
+        name = str(t.dtype).replace("torch.", "")
+        if name not in _TORCH_OK[dtype_code]:
+            raise QmvError(-2, f"{what}: tensor dtype {name}, expected one of {_TORCH_OK[dtype_code]}")
+        have = t.numel() * t.element_size() // _ELEM[dtype_code]
+    else:
+        have = t.numel() * t.element_size()
+    if have < min_elems:
+        raise QmvError(-5, f"{what}: holds {have} elements, needs {min_elems}")
+
+
 def _fmt(fmt) -> int:
     return FMT[fmt] if isinstance(fmt, str) else int(fmt)
 
@@ -211,6 +246,7 @@ def qmv_create_weights(fmt, rows: int, cols: int, dev_packed, nbytes: int | None
     """Descriptor for packed bytes already in device memory (a uint8 tensor or a pointer)."""
     if nbytes is None:
         nbytes = dev_packed.numel() * dev_packed.element_size()
+    _check_dev(dev_packed, "packed weights", None, nbytes)
     w = QmvWeights()
     _check(lib().qmv_create_weights(_fmt(fmt), rows, cols, _ptr(dev_packed), nbytes, ctypes.byref(w)))
     # The descriptor holds a raw pointer: keep the tensor alive with it, or the
@@ -228,6 +264,7 @@ def qmv_create_weights_planes(fmt, rows: int, cols: int, dev_planes, nbytes: int
     """Descriptor for plane-layout bytes already in device memory (a uint8 tensor or a pointer)."""
     if nbytes is None:
         nbytes = dev_planes.numel() * dev_planes.element_size()
+    _check_dev(dev_planes, "plane weights", None, nbytes)
     w = QmvWeights()
     _check(lib().qmv_create_weights_planes(_fmt(fmt), rows, cols, _ptr(dev_planes), nbytes, ctypes.byref(w)))
     w.owner = None if isinstance(dev_planes, int) else dev_planes
@@ -239,6 +276,7 @@ def qmv_repack_planes(src: QmvWeights, dst, dst_bytes: int | None = None, stream
     (a uint8 device tensor or a pointer); returns the planes descriptor."""
     if dst_bytes is None:
         dst_bytes = dst.numel() * dst.element_size()
+    _check_dev(dst, "dst", None, dst_bytes)
     w = QmvWeights()
     _check(lib().qmv_repack_planes(ctypes.byref(src), _ptr(dst), dst_bytes, ctypes.byref(w),
                                    _stream(stream, dst)))
@@ -248,6 +286,9 @@ def qmv_repack_planes(src: QmvWeights, dst, dst_bytes: int | None = None, stream
 
 def qmv_gemv(fmt, W: QmvWeights, x, x_dtype, y, rows: int, cols: int, batch: int,
              stream=None) -> None:
+    xd = _dtype(x_dtype)
+    _check_dev(x, "x", xd, batch * cols)
+    _check_dev(y, "y", 0, batch * rows)
     _check(lib().qmv_gemv(_fmt(fmt), ctypes.byref(W), _ptr(x), _dtype(x_dtype), _ptr(y),
                           rows, cols, batch, _stream(stream, x, y)))
 
@@ -255,7 +296,10 @@ def qmv_gemv(fmt, W: QmvWeights, x, x_dtype, y, rows: int, cols: int, batch: int
 def qmv_gemv_multi(fmt, x_dtype, batch: int, items, stream=None) -> None:
     """items: sequence of (QmvWeights, x, y) triples; one launch for all of them."""
     arr = (QmvGemvItem * max(1, len(items)))()
+    xd = _dtype(x_dtype)
     for i, (W, x, y) in enumerate(items):
+        _check_dev(x, f"item {i} x", xd, batch * W.cols)
+        _check_dev(y, f"item {i} y", 0, batch * W.rows)
         arr[i].W = ctypes.pointer(W)
         arr[i].x = _ptr(x)
         arr[i].y = _ptr(y)
@@ -265,6 +309,8 @@ def qmv_gemv_multi(fmt, x_dtype, batch: int, items, stream=None) -> None:
 
 
 def qmv_dequant(W: QmvWeights, out, out_dtype, stream=None) -> None:
+    od = _dtype(out_dtype)
+    _check_dev(out, "out", od, W.rows * W.cols)
     _check(lib().qmv_dequant(ctypes.byref(W), _ptr(out), _dtype(out_dtype), _stream(stream, out)))
 
 
@@ -273,10 +319,14 @@ def qmv_probe_read_outputs(nbytes: int) -> int:
 
 
 def qmv_probe_read(src, nbytes: int, out, stream=None) -> None:
+    _check_dev(src, "src", None, nbytes)
+    _check_dev(out, "out", 0, qmv_probe_read_outputs(nbytes))
     _check(lib().qmv_probe_read(_ptr(src), nbytes, _ptr(out), _stream(stream, src, out)))
 
 
 def qmv_probe_copy(src, dst, nbytes: int, stream=None) -> None:
+    _check_dev(src, "src", None, nbytes)
+    _check_dev(dst, "dst", None, nbytes)
     _check(lib().qmv_probe_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream, src, dst)))
 
 

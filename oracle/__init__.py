@@ -34,11 +34,15 @@ GGUF file, llama.cpp build or gguf package is available to compare against.
 from .formats import (BLOCK_BYTES, FORMATS, QK, dequant32, dequant64, pack,
                       packed_size, row_slice, unpack)
 from .fp import bf16_bits_to_f64, f32_to_bf16_bits_rne, fp16_bits_to_f64
-from .gemv import elementwise_bound, gemv64, gemv64_rows, normwise_rel_err, x_to_f64
+from .gemv import (elementwise_bound, elementwise_bound_rows, gamma, gemv64, gemv64_and_bound,
+                   gemv64_rows,
+                   normwise_rel_err, x_to_f64)
 
 __all__ = [
     "BLOCK_BYTES", "FORMATS", "QK", "dequant32", "dequant64", "pack", "packed_size",
     "row_slice", "unpack", "bf16_bits_to_f64", "f32_to_bf16_bits_rne",
-    "fp16_bits_to_f64", "elementwise_bound", "gemv64", "gemv64_rows",
+    "fp16_bits_to_f64", "elementwise_bound", "elementwise_bound_rows", "gamma", "gemv64",
+    "gemv64_and_bound",
+    "gemv64_rows",
     "normwise_rel_err", "x_to_f64",
 ]

@@ -70,19 +70,71 @@ def gemv64_rows(fmt: str, data, rows: int, cols: int, x, x_dtype: str,
 
 
 def normwise_rel_err(y, y64) -> np.ndarray:
-    """Per batch row: max_r |y - y64| / max_r |y64| (float64)."""
+    """Per batch row b: max_r |y[b, r] - y64[b, r]| / max_r |y64[b, r]| (float64).
+
+    The reduction runs over the output rows r (the last axis), one value per
+    activation row b.  Two cases the ratio leaves open are fixed here:
+
+    * an all-zero reference row (max_r |y64| = 0, e.g. every weight of the
+      matrix zero): every exact product is then zero and any float32 sum of
+      them is exactly zero, so the only acceptable result is exact zero --
+      the error is 0 if y is zero there and +inf otherwise;
+    * a NaN or infinity in y gives +inf, so no NaN can slip through a
+      ``<=`` comparison.
+    """
     y = np.asarray(y, np.float64).reshape(np.shape(y64))
     y64 = np.asarray(y64, np.float64)
-    num = np.max(np.abs(y - y64), axis=-1)
+    diff = np.abs(y - y64)
+    diff = np.where(np.isfinite(diff), diff, np.inf)
+    num = np.max(diff, axis=-1)
     den = np.max(np.abs(y64), axis=-1)
-    return num / np.where(den == 0, 1.0, den)
+    zero_ref = den == 0
+    safe = np.where(zero_ref, 1.0, den)
+    return np.where(zero_ref, np.where(num == 0, 0.0, np.inf), num / safe)
 
 
-def elementwise_bound(fmt: str, data, rows: int, cols: int, x, x_dtype: str) -> np.ndarray:
-    """gamma_{K+1} * |W| |x|, float64 [batch, rows]."""
+def gamma(n: int) -> float:
+    """gamma_n = n u / (1 - n u) with u = 2^-24, the float32 unit roundoff."""
     u = 2.0 ** -24
-    n = cols + 1
-    gamma = n * u / (1 - n * u)
+    return n * u / (1 - n * u)
+
+
+def elementwise_bound(fmt: str, data, rows: int, cols: int, x, x_dtype: str,
+                      row_chunk: int = 4096) -> np.ndarray:
+    """gamma_{K+1} * sum_k |W[r, k] x[b, k]|, float64 [batch, rows].
+
+    A diagnostic, not a gate: it bounds a float32 dot product of exact
+    operands in any summation order.  Kernels that apply scales after partial
+    sums (the factored sub-block form) round differently and may exceed it."""
     x64 = np.abs(x_to_f64(x, x_dtype).reshape(-1, cols))
-    w = np.abs(dequant64(fmt, data, rows, cols))
-    return gamma * (x64 @ w.T)
+    out = np.empty((x64.shape[0], rows), np.float64)
+    for r0 in range(0, rows, row_chunk):
+        r1 = min(rows, r0 + row_chunk)
+        w = np.abs(dequant64(fmt, row_slice(fmt, data, rows, cols, r0, r1), r1 - r0, cols))
+        out[:, r0:r1] = x64 @ w.T
+    return gamma(cols + 1) * out
+
+
+def gemv64_and_bound(fmt: str, data, rows: int, cols: int, x, x_dtype: str,
+                     row_chunk: int = 4096):
+    """(gemv64, elementwise_bound) of the same operands, each row chunk decoded once."""
+    x64 = x_to_f64(x, x_dtype).reshape(-1, cols)
+    ax = np.abs(x64)
+    y = np.empty((x64.shape[0], rows), np.float64)
+    b = np.empty_like(y)
+    for r0 in range(0, rows, row_chunk):
+        r1 = min(rows, r0 + row_chunk)
+        w = dequant64(fmt, row_slice(fmt, data, rows, cols, r0, r1), r1 - r0, cols)
+        y[:, r0:r1] = x64 @ w.T
+        b[:, r0:r1] = ax @ np.abs(w).T
+    return y, gamma(cols + 1) * b
+
+
+def elementwise_bound_rows(fmt: str, data, rows: int, cols: int, x, x_dtype: str,
+                           row_ids) -> np.ndarray:
+    """elementwise_bound restricted to the given rows: float64 [batch, len(row_ids)]."""
+    x64 = np.abs(x_to_f64(x, x_dtype).reshape(-1, cols))
+    ids = np.asarray(row_ids, np.int64)
+    w = np.stack([dequant64(fmt, row_slice(fmt, data, rows, cols, int(r), int(r) + 1), 1, cols)[0]
+                  for r in ids])
+    return gamma(cols + 1) * (x64 @ np.abs(w).T)

@@ -227,7 +227,7 @@ def pin_gemv_bruteforce(fmt):
             y = oracle.gemv64(fmt, data, rows, cols, x, xd)
             assert y.shape == (batch, rows)
             w = oracle.dequant64(fmt, data, rows, cols)
-            x64 = oracle.x_to_f64(x, xd)
+            x64 = x64_numpy(x, xd)  # not the oracle's own decoder
             for b in range(batch):
                 for r in range(rows):
                     exact = sum(Fraction(float(w[r, k])) * Fraction(float(x64[b, k]))
@@ -247,9 +247,113 @@ def pin_gemv_bruteforce(fmt):
                            rtol=1e-13, atol=0)
 
 
+# -- the parity gate, its diagnostic and the activation reading -----------------
+def x64_numpy(x, x_dtype):
+    """Exact float64 activations built from numpy's own conversions: float32 and
+    float16 values widened by numpy, bf16 bits as the upper half of a binary32."""
+    x = np.asarray(x)
+    if x_dtype == "bf16":
+        return (x.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return x.astype(np.float64)
+
+
+def pin_x_to_f64():
+    """Activation decoding per dtype against numpy's conversions, and the dtype
+    deciding how the same 16 bits are read."""
+    g = rng(11)
+    v = (g.standard_normal(509) * 3.0).astype(np.float32)
+    v[:6] = [0.0, -0.0, 6.0e-8, -65504.0, 1.0e-30, 3.0e38]
+    assert np.array_equal(oracle.x_to_f64(v, "f32"), v.astype(np.float64))
+    h = v[:4].copy()
+    h = np.concatenate([h, v[6:]]).astype(np.float16)
+    assert np.array_equal(oracle.x_to_f64(h, "f16"), h.astype(np.float64))
+    bits = (v.view(np.uint32) >> 16).astype(np.uint16)
+    assert np.array_equal(oracle.x_to_f64(bits, "bf16"),
+                          (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64))
+    # 0x3C00 is 1.0 in binary16 and 2^-7 in bfloat16; 0xC0A0 is -2.3125 and -5.0
+    b = np.array([0x3C00, 0x4000, 0xC0A0], np.uint16)
+    assert np.array_equal(oracle.x_to_f64(b.view(np.float16), "f16"), [1.0, 2.0, -2.3125])
+    assert np.array_equal(oracle.x_to_f64(b, "bf16"), [2.0 ** -7, 2.0, -5.0])
+    for xd, arr in (("f32", h), ("f16", v), ("bf16", h), ("f16", bits)):
+        try:
+            oracle.x_to_f64(arr, xd)
+        except TypeError:
+            continue
+        raise AssertionError(f"{xd} accepted a {arr.dtype} array")
+
+
+def pin_normwise_gate():
+    """The 2e-3 gate's error measure on hand-computed cases: one value per
+    activation row, the largest deviation over that row's outputs divided by
+    that row's largest |y64|; an all-zero reference row admits only exact
+    zero; NaN and infinities fail."""
+    y64 = np.array([[1.0, -4.0, 2.0], [0.5, 0.25, -1.0]])
+    y = np.array([[1.5, -4.0, 2.0], [0.5, 0.5, -1.0]])
+    err = oracle.normwise_rel_err(y, y64)
+    assert err.shape == (2,) and err[0] == 0.125 and err[1] == 0.25   # 0.5/4, 0.25/1
+    # the largest deviation, not an average: one bad output of eight
+    y64 = np.ones((1, 8))
+    y = y64.copy()
+    y[0, 5] += 2.0 ** -4
+    assert oracle.normwise_rel_err(y, y64)[0] == 2.0 ** -4
+    # each activation row is scaled by its own largest |y64|
+    y64 = np.array([[1000.0, 0.0], [1.0, -2.0]])
+    y = np.array([[1000.0, 0.0], [1.0, -2.5]])
+    assert np.array_equal(oracle.normwise_rel_err(y, y64), [0.0, 0.25])
+    # all-zero reference rows
+    y64 = np.zeros((2, 3))
+    y = np.zeros((2, 3))
+    y[1, 2] = 1e-300
+    assert np.array_equal(oracle.normwise_rel_err(y, y64), [0.0, np.inf])
+    assert oracle.normwise_rel_err(np.array([[-0.0, 0.0]]), np.zeros((1, 2)))[0] == 0.0
+    for bad in (np.nan, np.inf, -np.inf):
+        e = oracle.normwise_rel_err(np.array([[1.0, bad]]), np.array([[1.0, 2.0]]))
+        assert e[0] == np.inf, bad
+    # a single activation row as a 1-D vector
+    assert oracle.normwise_rel_err(np.array([3.0, 4.0]), np.array([2.0, 4.0])) == 0.25
+
+
+def pin_elementwise_bound():
+    """gamma_{K+1} * sum_k |w x| on a hand-made row, and as an upper bound of
+    float32 dot products of exact operands summed in three orders."""
+    u = 2.0 ** -24
+    assert oracle.gamma(33) == 33 * u / (1 - 33 * u)
+    f = {"d_bits": np.array([[0x3C00]], np.uint16), "q": np.zeros((1, 32), np.int8)}
+    f["q"][0, :2] = [1, -2]
+    data = oracle.pack("q8_0", f, 1, 32)
+    x = np.zeros((1, 32), np.float32)
+    x[0, :2] = [3.0, 4.0]
+    b = oracle.elementwise_bound("q8_0", data, 1, 32, x, "f32")
+    assert b.shape == (1, 1) and b[0, 0] == 11.0 * oracle.gamma(33)   # |1*3| + |-2*4|
+    assert np.array_equal(oracle.elementwise_bound_rows("q8_0", data, 1, 32, x, "f32", [0]), b)
+    # formats whose weights are exact in float32 (one rounding per product)
+    for fmt in ("q8_0", "q6_k", "int4_g128"):
+        rows, cols = 6, 2 * oracle.QK[fmt]
+        d = _fields(fmt, rows, cols, 610)
+        data = oracle.pack(fmt, d, rows, cols)
+        x = gen_x(2, cols, "f32", 611)
+        w32 = oracle.dequant32(fmt, data, rows, cols)
+        y64 = oracle.gemv64(fmt, data, rows, cols, x, "f32")
+        bound = oracle.elementwise_bound(fmt, data, rows, cols, x, "f32")
+        assert np.allclose(bound[:, [4, 1]],    # float64 summation order differs
+                           oracle.elementwise_bound_rows(fmt, data, rows, cols, x, "f32", [4, 1]),
+                           rtol=1e-13, atol=0)
+        yb, bb = oracle.gemv64_and_bound(fmt, data, rows, cols, x, "f32", row_chunk=4)
+        assert np.allclose(yb, y64, rtol=1e-13, atol=0) and np.allclose(bb, bound, rtol=1e-13, atol=0)
+        for bi in range(2):
+            prods = w32 * x[bi][None, :]                     # float32 products, rounded once
+            seq = np.add.accumulate(prods, axis=1, dtype=np.float32)[:, -1]
+            rev = np.add.accumulate(prods[:, ::-1], axis=1, dtype=np.float32)[:, -1]
+            pair = prods.sum(axis=1, dtype=np.float32)
+            for y32 in (seq, rev, pair):
+                assert np.all(np.abs(y32.astype(np.float64) - y64[bi]) <= bound[bi]), fmt
+
+
 ALL_PINS = (
     [("fp16_decode", pin_fp16_decode, ()), ("bf16_decode", pin_bf16_decode, ()),
-     ("bf16_rne", pin_bf16_rne, ()), ("packed_sizes", pin_packed_sizes, ())]
+     ("bf16_rne", pin_bf16_rne, ()), ("packed_sizes", pin_packed_sizes, ()),
+     ("x_to_f64", pin_x_to_f64, ()), ("normwise_gate", pin_normwise_gate, ()),
+     ("elementwise_bound", pin_elementwise_bound, ())]
     + [(f"golden[{n}]", pin_golden, (n,)) for n in all_names()]
     + [(f"{p.__name__[4:]}[{fmt}]", p, (fmt,)) for fmt in FMTS
        for p in (pin_roundtrip, pin_single_rounding, pin_zero_scale, pin_affine_in_code,

@@ -196,6 +196,47 @@ def test_bf16_activation_range(fmt, layout, spread):
     assert np.all(err <= TOL), err
 
 
+@pytest.mark.parametrize("fmt,layout", [("q4_k", "blocks"), ("q4_k", "planes"), ("q5_k", "blocks"),
+                                        ("int4_g128", "blocks"), ("q8_0", "blocks"),
+                                        ("q6_k", "blocks"), ("q6_k", "planes")])
+@pytest.mark.parametrize("spread", ["wide", "large", "tiny", "tinier", "mixed"])
+@pytest.mark.parametrize("batch", [1, 2])
+def test_f32_activation_range(fmt, layout, spread, batch):
+    """fp32 activations far from N(0, 1): twelve decades within one row, all
+    near 1e20, 1e-30 or 1e-36 (products of codes and activations below
+    float32's normal range unless the kernel rescales), and a row mixing
+    1e-36 and 1e+20 in different lanes.  Every case must meet the gate, in the
+    single-row GEMV and in the two-row pass."""
+    rows, cols = 96, 17 * 256
+    w = Weights(fmt, rows, cols, seed=809)
+    g = np.random.Generator(np.random.PCG64({"wide": 11, "large": 12, "tiny": 13, "tinier": 14,
+                                             "mixed": 15}[spread]))
+    x = g.standard_normal((batch, cols))
+    if spread == "wide":
+        x *= 10.0 ** g.uniform(-6, 6, size=x.shape)
+    elif spread == "large":
+        x *= 1e20
+    elif spread == "tiny":
+        x *= 1e-30
+    elif spread == "tinier":
+        x *= 1e-36
+    else:
+        x *= np.where((np.arange(cols) // 512) % 2 == 0, 1e-36, 1e20)[None, :]
+    x = x.astype(np.float32)
+    desc = w.desc
+    if layout == "planes":
+        dst = torch.empty(qmv.qmv_planes_size(fmt, rows, cols), dtype=torch.uint8, device=DEV)
+        desc = qmv.qmv_repack_planes(w.desc, dst)
+    say(f"{fmt} f32 activation range {spread} ({layout}) batch {batch}")
+    y = torch.empty(batch, rows, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv(fmt, desc, to_dev_x(x, "f32"), "f32", y, rows, cols, batch)
+    got = y.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = _err(got, oracle_y(w, x, "f32"))
+    say(f"  normwise err {err.max():.3e}")
+    assert np.all(err <= TOL), err
+
+
 # longest rows a GEMV launch accepts (16 waves along K): the 1024-thread
 # kernel, and a 10-wave split in between
 LONG = [("q8_0", 16 * 64 * 32), ("q4_k", 16 * 16 * 256), ("q5_k", 10 * 16 * 256),

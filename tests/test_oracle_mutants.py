@@ -127,6 +127,38 @@ def _gemv_drop_last_col(fmt, data, rows, cols, x, x_dtype, row_chunk=4096):
     return x64[:, :-1] @ w[:, :-1].T
 
 
+def _normwise(axis, reduce, zero_guard_one):
+    def f(y, y64):
+        y = np.asarray(y, np.float64).reshape(np.shape(y64))
+        y64 = np.asarray(y64, np.float64)
+        num = reduce(np.abs(y - y64), axis=axis)
+        den = np.max(np.abs(y64), axis=axis)
+        if zero_guard_one:       # the earlier guard: an all-zero row divided by 1
+            return num / np.where(den == 0, 1.0, den)
+        return np.where(den == 0, np.where(num == 0, 0.0, np.inf), num / np.where(den == 0, 1.0, den))
+    return f
+
+
+def _x_to_f64_swapped(x, x_dtype):
+    x = np.asarray(x)
+    if x_dtype == "f16":
+        return FP.bf16_bits_to_f64(x.view(np.uint16))
+    if x_dtype == "bf16":
+        return FP.fp16_bits_to_f64(x)
+    return X_ORIG(x, x_dtype)
+
+
+def _bound_signed(fmt, data, rows, cols, x, x_dtype, row_chunk=4096):
+    x64 = np.abs(G.x_to_f64(x, x_dtype).reshape(-1, cols))
+    return G.gamma(cols + 1) * (x64 @ F.dequant64(fmt, data, rows, cols).T)
+
+
+def _bound_gamma_k(fmt, data, rows, cols, x, x_dtype, row_chunk=4096):
+    return BOUND_ORIG(fmt, data, rows, cols, x, x_dtype) * (G.gamma(cols) / G.gamma(cols + 1))
+
+
+X_ORIG = G.x_to_f64
+BOUND_ORIG = G.elementwise_bound
 FP_ORIG = FP.fp16_bits_to_f64
 Q4K_SCALES_ORIG = F.q4_k_bytes_to_scales
 
@@ -149,6 +181,12 @@ MUTANTS = {
     "fp16 exponent bias 16": [(F, "fp16_bits_to_f64", _fp16_bias16)],
     "gemv transposed operand": [(G, "gemv64", _gemv_transposed), (oracle, "gemv64", _gemv_transposed)],
     "gemv drops last column": [(G, "gemv64", _gemv_drop_last_col), (oracle, "gemv64", _gemv_drop_last_col)],
+    "gate over the batch axis": [(oracle, "normwise_rel_err", _normwise(0, np.max, False))],
+    "gate mean in place of max": [(oracle, "normwise_rel_err", _normwise(-1, np.mean, False))],
+    "gate divides an all-zero row by one": [(oracle, "normwise_rel_err", _normwise(-1, np.max, True))],
+    "activations f16 and bf16 swapped": [(G, "x_to_f64", _x_to_f64_swapped), (oracle, "x_to_f64", _x_to_f64_swapped)],
+    "bound without |W|": [(oracle, "elementwise_bound", _bound_signed)],
+    "bound gamma_K": [(oracle, "elementwise_bound", _bound_gamma_k)],
 }
 
 
