@@ -130,6 +130,13 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     per_wave = {"q8_0": 2048, "q4_k": 4096, "q6_k": 4096, "int4_g128": 4096, "q5_k": 4096}[fmt]
     waves = max([4] + [-(-c // per_wave) for c in cols_list])
     kw = max(-(-c // per_wave) for c in cols_list)
+    pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",
+           "int4_g128": "Int4G128Policy", "q5_k": "Q5KPolicy"}[fmt]
+    if layout == "planes":
+        pol = {"q4_k": "Q4KPlanesPolicy", "q5_k": "Q5KPlanesPolicy", "q6_k": "Q6KPlanesPolicy"}[fmt]
+    xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
+    if len(cols_list) == 1 and 2 <= kw <= 8:   # one matrix split along K: slices in LDS
+        return f"qmv::gemv_lx_kernel<qmv::{pol}, {xt}, 2, 2, 512>"
     if kw == 1:
         cfg = "2, 2, 256, true"
     else:

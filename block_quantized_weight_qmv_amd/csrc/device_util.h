@@ -73,7 +73,6 @@ __device__ __forceinline__ uint32_t ld_u16(const uint8_t* p) {  // 2-byte aligne
 // operand into v_fma_mix_f32 with op_sel, so two codes masked out of one
 // dword (bits 0-15 and 16-31) feed two FMAs with no conversion instruction.
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-constexpr float kTwo24 = 16777216.0f;
 
 __device__ __forceinline__ float fma_lo(uint32_t bits, float x, float acc) {
   return fmaf(static_cast<float>(__builtin_bit_cast(h2_t, bits).x), x, acc);
@@ -217,6 +216,35 @@ template <class F32, class Half>
 struct XSliceFor<float, F32, Half> {
   typedef F32 type;
 };
+
+// fp32 activations enter v_fma_mix_f32 against codes held as u * 2^-24, so a
+// product falls below float32's normal range (2^-126) once |x| is below about
+// 2^-102 and then loses bits.  A lane whose largest |x| lies outside
+// [2^-60, 2^60] therefore scales its slice by 2^-e, e the binary exponent of
+// that largest |x| (clamped to [-100, 64], so xs times an fp16 scale stays
+// finite), and undoes it with xs = 2^(24 + e); inside that range (the usual
+// case) e = 0.  Either way every product of a nonzero code and an element
+// within 2^-40 of the lane's largest stays normal.  Scaling by a power of two
+// is exact and no product is subnormal, so 2x still gives 2y bit for bit.
+//
+// f32_slice_factor returns the factor every activation of the lane is
+// multiplied by -- 2^-e, or 0 for a lane past the row's end, whose
+// activations must not count -- and sets xs and un = 2^e, which turns sums of
+// the scaled activations back into sums of the given ones (exactly).  The
+// multiply replaces the select that zeroes such lanes, so the scaling costs
+// only the maximum.
+template <int N>
+__device__ __forceinline__ float f32_slice_factor(const float* v, bool ok, float& xs, float& un) {
+  float mx = 0.f;
+#pragma unroll
+  for (int i = 0; i < N; ++i) mx = fmaxf(mx, fabsf(v[i]));
+  const bool mid = mx <= 0x1p60f && (mx >= 0x1p-60f || mx == 0.f);
+  int e = __builtin_amdgcn_frexp_expf(mx);
+  e = mid ? 0 : (e < -100 ? -100 : (e > 64 ? 64 : e));
+  xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
+  un = __builtin_amdgcn_ldexpf(1.0f, e);
+  return ok ? __builtin_amdgcn_ldexpf(1.0f, -e) : 0.f;
+}
 
 __device__ __forceinline__ _Float16 scaled_f16(float v, int e) {
   return static_cast<_Float16>(__builtin_amdgcn_ldexpf(v, -e));

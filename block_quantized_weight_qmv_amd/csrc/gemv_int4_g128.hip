@@ -28,8 +28,9 @@ struct Int4G128Policy {
   static constexpr int kColsPerWave = 64 * 64;
   static constexpr int kXElems = 64;
   struct XSliceF32 {
-    float v[64];  // v[32h + k]: activation of column col[h] + k
-    float s[2];
+    float v[64];  // v[32h + k]: activation of column col[h] + k, scaled by 2^-e (f32_slice_factor)
+    float s[2];   // sums of each half's 32 unscaled activations
+    float xs;     // 2^(24 + e)
   };
   struct XSliceHalf {
     h2_t h[32];  // h[16 hf + 4 i + p]: fp16 activation pairs of half hf, dword i, pair p
@@ -77,16 +78,30 @@ struct Int4G128Policy {
     float* dst = v;
     if constexpr (__is_same(XT, float)) dst = s.v;
     x_to_f32<64>(raw, dst, static_cast<const XT*>(nullptr));
+    if constexpr (__is_same(XT, float)) {
+      float un;
+      const float f = f32_slice_factor<64>(s.v, true, s.xs, un);
 #pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      s.s[hf] = 0.f;
+      for (int hf = 0; hf < 2; ++hf) {
+        const float fh = okh[hf] ? f : 0.f;
+        s.s[hf] = 0.f;
 #pragma unroll
-      for (int k = 0; k < 32; ++k) {
-        dst[32 * hf + k] = okh[hf] ? dst[32 * hf + k] : 0.f;
-        s.s[hf] += dst[32 * hf + k];
+        for (int k = 0; k < 32; ++k) {
+          s.v[32 * hf + k] *= fh;
+          s.s[hf] += s.v[32 * hf + k];
+        }
+        s.s[hf] *= un;
       }
-    }
-    if constexpr (!__is_same(XT, float)) {
+    } else {
+#pragma unroll
+      for (int hf = 0; hf < 2; ++hf) {
+        s.s[hf] = 0.f;
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+          dst[32 * hf + k] = okh[hf] ? dst[32 * hf + k] : 0.f;
+          s.s[hf] += dst[32 * hf + k];
+        }
+      }
       const int e = half_scale_exp<XT, 64>(v);
       s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
       // dword i of a half holds weights 8i..8i+7, two per byte; the code pairs
@@ -147,7 +162,7 @@ struct Int4G128Policy {
       }
       float xs;
       if constexpr (__is_same(XT, float))
-        xs = kTwo24;
+        xs = s.xs;
       else
         xs = s.xs;
       const float t = fmaf(xs, fmaf(so, 0.0625f, se), -8.f * s.s[hf]);
@@ -200,7 +215,7 @@ struct Int4G128Policy {
       for (int m = 0; m < NBR; ++m) {
         float xs;
         if constexpr (__is_same(XT, float))
-          xs = kTwo24;
+          xs = s[m].xs;
         else
           xs = s[m].xs;
         const float t = fmaf(xs, fmaf(so[m], 0.0625f, se[m]), -8.f * s[m].s[hf]);

@@ -27,8 +27,9 @@ struct Q4KPolicy {
   static constexpr int kColsPerWave = 16 * 256;
   static constexpr int kXElems = 64;
   struct XSliceF32 {
-    float v[64];
-    float s0, s1;
+    float v[64];   // scaled by 2^-e (f32_slice_factor)
+    float s0, s1;  // sums of the unscaled activations of the two sub-blocks
+    float xs;      // 2^(24 + e)
   };
   template <typename XT>
   using XSliceT = typename XSliceFor<XT, XSliceF32, HalfXSlice>::type;
@@ -75,14 +76,18 @@ struct Q4KPolicy {
   __device__ void finish_x(const uint4* raw, XSliceT<XT>& s) const {
     if constexpr (__is_same(XT, float)) {
       x_to_f32<64>(raw, s.v, static_cast<const XT*>(nullptr));
+      float un;
+      const float f = f32_slice_factor<64>(s.v, ok, s.xs, un);
 #pragma unroll
-      for (int i = 0; i < 64; ++i) s.v[i] = ok ? s.v[i] : 0.f;
+      for (int i = 0; i < 64; ++i) s.v[i] *= f;
       s.s0 = 0.f;
       s.s1 = 0.f;
 #pragma unroll
       for (int i = 0; i < 32; ++i) s.s0 += s.v[i];
 #pragma unroll
       for (int i = 32; i < 64; ++i) s.s1 += s.v[i];
+      s.s0 *= un;
+      s.s1 *= un;
     } else {
       finish_half_xslice<XT>(raw, ok, s);
     }
@@ -106,7 +111,7 @@ struct Q4KPolicy {
     float s0 = 0.f, s1 = 0.f;
     float d;
     if constexpr (__is_same(XT, float)) {
-      d = f16_to_f32(f.hd.x & 0xFFFFu) * kTwo24;
+      d = f16_to_f32(f.hd.x & 0xFFFFu) * s.xs;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
         const uint32_t w0 = q[i], w8 = q[i] >> 8;
@@ -186,7 +191,7 @@ struct Q4KPolicy {
     for (int m = 0; m < NBR; ++m) {
       float d;
       if constexpr (__is_same(XT, float))
-        d = d16 * kTwo24;
+        d = d16 * s[m].xs;
       else
         d = d16 * s[m].xs;
       const float t = fmaf(cvt_ubyte<1>(sc) * 0.0625f, s1[m], cvt_ubyte<0>(sc) * s0[m]);

@@ -26,8 +26,9 @@ struct Q6KPolicy {
   static constexpr int kColsPerWave = 16 * 256;
   static constexpr int kXElems = 64;
   struct XSlice {
-    float v[64];  // v[16g + t] = x[col0 + 32g + t]
-    float s[4];
+    float v[64];  // v[16g + t] = x[col0 + 32g + t], scaled by 2^-e (f32_slice_factor)
+    float s[4];   // sums of each group's 16 unscaled activations
+    float xs;     // 2^(24 + e)
   };
   struct XSliceHalf {
     h2_t h[32];  // h[8g + 2k + p]: pair p of dword k of group g: (4k, 4k+2), (4k+1, 4k+3)
@@ -73,16 +74,29 @@ struct Q6KPolicy {
     float* dst = v;
     if constexpr (__is_same(XT, float)) dst = s.v;
     x_to_f32<64>(raw, dst, static_cast<const XT*>(nullptr));
+    if constexpr (__is_same(XT, float)) {
+      float un;
+      const float f = f32_slice_factor<64>(s.v, ok, s.xs, un);
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      s.s[g] = 0.f;
+      for (int g = 0; g < 4; ++g) {
+        s.s[g] = 0.f;
 #pragma unroll
-      for (int t = 0; t < 16; ++t) {
-        dst[16 * g + t] = ok ? dst[16 * g + t] : 0.f;
-        s.s[g] += dst[16 * g + t];
+        for (int t = 0; t < 16; ++t) {
+          s.v[16 * g + t] *= f;
+          s.s[g] += s.v[16 * g + t];
+        }
+        s.s[g] *= un;
       }
-    }
-    if constexpr (!__is_same(XT, float)) {
+    } else {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        s.s[g] = 0.f;
+#pragma unroll
+        for (int t = 0; t < 16; ++t) {
+          dst[16 * g + t] = ok ? dst[16 * g + t] : 0.f;
+          s.s[g] += dst[16 * g + t];
+        }
+      }
       const int e = half_scale_exp<XT, 64>(v);
       s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
 #pragma unroll
@@ -141,7 +155,7 @@ struct Q6KPolicy {
       const int sc = static_cast<int8_t>((word >> (8 * (2 * (g & 1) + i))) & 0xFFu);
       float xs;
       if constexpr (__is_same(XT, float))
-        xs = kTwo24;
+        xs = s.xs;
       else
         xs = s.xs;
       t = fmaf(static_cast<float>(sc), fmaf(xs, acc[g], -32.f * s.s[g]), t);
@@ -198,7 +212,7 @@ struct Q6KPolicy {
     for (int m = 0; m < NBR; ++m) {
       float xs;
       if constexpr (__is_same(XT, float))
-        xs = kTwo24;
+        xs = s[m].xs;
       else
         xs = s[m].xs;
       float t = 0.f;

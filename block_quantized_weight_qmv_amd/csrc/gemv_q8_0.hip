@@ -21,8 +21,9 @@ struct Q80Policy {
   static constexpr int kColsPerWave = 64 * 32;
   static constexpr int kXElems = 32;
   struct XSlice {
-    float v[32];
-    float s;
+    float v[32];  // scaled by 2^-e (f32_slice_factor)
+    float s;      // sum of the lane's 32 unscaled activations
+    float xs;     // 2^(24 + e)
   };
   struct XSliceHalf {
     h2_t h[16];  // h[2i + p]: pair p of dword i: (4i, 4i+2), (4i+1, 4i+3)
@@ -63,12 +64,21 @@ struct Q80Policy {
     if constexpr (__is_same(XT, float)) dst = s.v;
     x_to_f32<32>(raw, dst, static_cast<const XT*>(nullptr));
     s.s = 0.f;
+    if constexpr (__is_same(XT, float)) {
+      float un;
+      const float f = f32_slice_factor<32>(s.v, ok, s.xs, un);
 #pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      dst[i] = ok ? dst[i] : 0.f;
-      s.s += dst[i];
-    }
-    if constexpr (!__is_same(XT, float)) {
+      for (int i = 0; i < 32; ++i) {
+        s.v[i] *= f;
+        s.s += s.v[i];
+      }
+      s.s *= un;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        dst[i] = ok ? dst[i] : 0.f;
+        s.s += dst[i];
+      }
       const int e = half_scale_exp<XT, 32>(v);
       s.xs = __builtin_amdgcn_ldexpf(1.0f, 24 + e);
 #pragma unroll
@@ -106,7 +116,7 @@ struct Q80Policy {
     }
     float xs;
     if constexpr (__is_same(XT, float))
-      xs = kTwo24;
+      xs = s.xs;
     else
       xs = s.xs;
     return f16_to_f32(f.d) * fmaf(xs, acc, -128.f * s.s);
@@ -143,7 +153,7 @@ struct Q80Policy {
     for (int m = 0; m < NBR; ++m) {
       float xs;
       if constexpr (__is_same(XT, float))
-        xs = kTwo24;
+        xs = s[m].xs;
       else
         xs = s[m].xs;
       out[m] = d * fmaf(xs, acc[m], -128.f * s[m].s);

@@ -458,6 +458,136 @@ gemv_rows_split_kernel(const GemvLaunch args, int batch) {
   }
 }
 
+// Matrices split along K (kw > 1 K slots), any batch row by grid y: the
+// activation slices in LDS.
+//
+// In gemv_kernel's K split every wave of a row set holds a private slice of
+// x in VGPRs (16 KB of fp32 for Q4_K, read from L2 before its first tile)
+// and the set's waves add their partial sums through LDS at the end; with
+// one set per compute unit that leaves 1.25 waves per SIMD to hide the
+// arithmetic behind the loads.  Here the workgroup first stages every lane
+// slice of the row once -- slice (k, l) is exactly what lane l of a wave at
+// K slot k multiplies, converted (fp32: scaled, with its sub-block sums) by
+// the policy's finish_x, and stored as 16-byte words at [k][word][lane] so
+// that a wave's reads are consecutive -- and then each wave streams whole
+// rows, R at a time, K slot after K slot, reading each slot's slice from LDS
+// into VGPRs for the tile.  The R partials of a tile are reduced across the
+// wave as in gemv_kernel, and the slot totals are added in slot order (lane
+// r < R keeps row r's running total), which are the K-split gemv_kernel's
+// operations in its order: outputs are equal bit for bit.  Rows are dealt to
+// the launch's waves in contiguous groups of R.
+struct GemvLxArgs {
+  const uint8_t* w;
+  uint64_t scales_offset;
+  const void* x;      // [batch][cols]
+  float* y;           // [batch][rows]
+  int rows, cols;
+  int nslots;         // K slots (waves' worth of columns) per row
+  int groups;         // row groups of R rows
+};
+
+template <class P, typename XT>
+constexpr int lx_slice_words() {  // 16-byte words of one lane slice
+  return static_cast<int>((sizeof(typename P::template XSliceT<XT>) + 15) / 16);
+}
+
+template <class P, typename XT, int R, int D, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+gemv_lx_kernel(const GemvLxArgs a) {
+  typedef typename P::template XSliceT<XT> XS;
+  constexpr int kW4 = lx_slice_words<P, XT>();
+  const int lane = __lane_id();
+  const int waves = static_cast<int>(blockDim.x) >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = static_cast<int>(gridDim.x) * waves;
+  const int gw = static_cast<int>(blockIdx.x) * waves + wave;
+  // this wave's row groups [g0, g1)
+  const int g0 = static_cast<int>(static_cast<int64_t>(gw) * a.groups / nw);
+  const int g1 = static_cast<int>(static_cast<int64_t>(gw + 1) * a.groups / nw);
+  const int ntiles = (g1 - g0) * a.nslots;
+  const int r_last = a.rows - 1;
+  const XT* x = static_cast<const XT*>(a.x) + static_cast<size_t>(blockIdx.y) * a.cols;
+  float* y = a.y + static_cast<size_t>(blockIdx.y) * a.rows;
+  extern __shared__ uint4 lx_slices[];
+
+  // Tile t of this wave: row group g0 + t / nslots, K slot t % nslots;
+  // tracked incrementally for the tile being loaded and the one finished.
+  int ld_g = g0, ld_k = 0;
+  auto load_next = [&](typename P::Frag* f) {
+    const P pol(a.w, a.scales_offset, a.cols, ld_k, lane);
+#pragma unroll
+    for (int r = 0; r < R; ++r) pol.load(min(ld_g * R + r, r_last), f[r]);
+    if (++ld_k == a.nslots) {
+      ld_k = 0;
+      ++ld_g;
+    }
+  };
+
+  // Issue order: the activations of the slice this thread stages (threads
+  // nslots x 64 and above re-read the last slice and store nothing; the
+  // launch gives a workgroup at least nslots waves), then the first D tiles;
+  // the slice is converted and stored once its loads arrive.
+  const int sidx = min(static_cast<int>(threadIdx.x), a.nslots * 64 - 1);
+  const P pk(a.w, a.scales_offset, a.cols, sidx >> 6, sidx & 63);
+  uint4 raw[P::kXElems * sizeof(XT) / 16];
+  pk.load_x_raw(XGlobal<XT>{x}, raw);
+  __builtin_amdgcn_sched_barrier(0);
+  typename P::Frag f[D][R];
+#pragma unroll
+  for (int j = 0; j < D; ++j) load_next(f[j]);
+  __asm__ __volatile__("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  {
+    XS sl;
+    pk.template finish_x<XT>(raw, sl);
+    uint4 wds[kW4];
+    wds[kW4 - 1] = make_uint4(0, 0, 0, 0);
+    __builtin_memcpy(wds, &sl, sizeof(XS));
+    if (static_cast<int>(threadIdx.x) < a.nslots * 64) {
+#pragma unroll
+      for (int i = 0; i < kW4; ++i) lx_slices[((sidx >> 6) * kW4 + i) * 64 + (sidx & 63)] = wds[i];
+    }
+  }
+  lds_barrier();
+
+  const P pol(a.w, a.scales_offset, a.cols, 0, lane);  // dot() uses lane constants only
+  int fin_g = g0, fin_k = 0;
+  float tot = 0.f;  // lane r < R: running total of row fin_g * R + r over the slots so far
+  auto finish = [&](const typename P::Frag* fr) {
+    uint4 wds[kW4];
+#pragma unroll
+    for (int i = 0; i < kW4; ++i) wds[i] = lx_slices[(fin_k * kW4 + i) * 64 + lane];
+    XS xs;
+    __builtin_memcpy(&xs, wds, sizeof(XS));
+    float acc[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[r] = pol.template dot<XT>(fr[r], xs);
+    const float t = reduce_rows<R>(acc, lane);
+    tot = fin_k == 0 ? t : tot + t;
+    if (++fin_k == a.nslots) {
+      const int row = fin_g * R + lane;
+      if (lane < R && row < a.rows) y[row] = tot;
+      fin_k = 0;
+      ++fin_g;
+    }
+  };
+  // Single-exit tile loop with pinned prefetches, as in gemv_kernel.
+  int t = D;
+#pragma unroll 1
+  for (; t < ntiles; t += D) {
+#pragma unroll
+    for (int j = 0; j < D; ++j) {
+      finish(f[j]);
+      load_next(f[j]);
+      __asm__ __volatile__("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < D; ++j)
+    if (t - D + j < ntiles) finish(f[j]);
+}
+
 // Rows of a K-split set are capped so that the partial sums of a workgroup
 // (waves x rows floats) stay within 16 waves x kMaxPartStride x 4 bytes.
 constexpr int kMaxPartStride = 256;
@@ -699,10 +829,64 @@ hipError_t launch_gemv_rows(const GemvCall* calls, int n, int x_dtype, int64_t b
   }
 }
 
+// K slots whose slices gemv_lx_kernel stages (LDS bytes per workgroup:
+// slots x slice words x 1 KB; fp32 Q4_K slices are 17 words).
+constexpr int kLxMaxSlots = 8;
+// Rows per group of gemv_lx_kernel.
+#ifndef QMV_LX_ROWS
+#define QMV_LX_ROWS 2
+#endif
+// Waves per workgroup (one workgroup per compute unit) at most.
+#ifndef QMV_LX_MAX_WAVES
+#define QMV_LX_MAX_WAVES 8
+#endif
+
+template <class P, typename XT>
+inline size_t lx_lds_bytes(int nslots) {
+  return static_cast<size_t>(nslots) * lx_slice_words<P, XT>() * 64 * 16;
+}
+
+// One matrix split along K (2..kLxMaxSlots slots): gemv_lx_kernel with one
+// workgroup per compute unit and enough waves that each takes about one row
+// group (at least 4, at most QMV_LX_MAX_WAVES waves per workgroup).
+#ifndef QMV_LX_TILES
+#define QMV_LX_TILES 2
+#endif
+
+template <class P, typename XT>
+hipError_t launch_lx(const GemvCall& c, int64_t batch, hipStream_t stream) {
+  constexpr int R = QMV_LX_ROWS;
+  constexpr int D = QMV_LX_TILES;
+  constexpr int kMaxT = 64 * QMV_LX_MAX_WAVES;
+  auto kernel = gemv_lx_kernel<P, XT, R, D, kMaxT>;
+  const qmv_weights* W = c.W;
+  GemvLxArgs a;
+  a.w = static_cast<const uint8_t*>(W->data);
+  a.scales_offset = W->scales_offset;
+  a.x = c.x;
+  a.y = c.y;
+  a.rows = static_cast<int>(W->rows);
+  a.cols = static_cast<int>(W->cols);
+  a.nslots = static_cast<int>((W->cols + P::kColsPerWave - 1) / P::kColsPerWave);
+  a.groups = static_cast<int>((W->rows + R - 1) / R);
+  if (a.nslots > kLxMaxSlots) return hipErrorInvalidValue;
+  const int cus = device_cus();
+  int waves = (a.groups + cus - 1) / cus;
+  waves = waves < 4 ? 4 : (waves > QMV_LX_MAX_WAVES ? QMV_LX_MAX_WAVES : waves);
+  if (waves < a.nslots) waves = a.nslots;  // one staging thread per lane slice
+  int grid = (a.groups + waves - 1) / waves;
+  grid = grid > cus ? cus : grid;
+  const size_t lds = lx_lds_bytes<P, XT>(a.nslots);
+  hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(64 * waves), lds, stream, a);
+  return hipGetLastError();
+}
+
 template <class P, typename XT>
 hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStream_t stream) {
   const int kw = max_kw<P>(calls, n);
   if (kw > 16) return hipErrorInvalidValue;
+  // A single matrix split along K: the activation slices in LDS.
+  if (n == 1 && kw > 1 && kw <= kLxMaxSlots) return launch_lx<P, XT>(calls[0], batch, stream);
   const int waves = kw < 4 ? 4 : kw;
   // Two tiles in flight per wave, two waves per SIMD.  (Measured alternatives
   // on the 7B layer shapes: one wave per SIMD with 3, 4, 6 or 8 tiles in

@@ -42,7 +42,12 @@
  *   GEMV: y[b][r] = sum_k W[r][k] * x[b][k], x [batch][cols] row-major,
  *   y [batch][rows] fp32 row-major, overwritten.  Products and sums are
  *   carried in fp32; activations are converted exactly to fp32 (f16 and
- *   bf16 are subsets of fp32).
+ *   bf16 are subsets of fp32).  Any finite activations are accepted: the
+ *   kernels scale each lane's activations by a power of two where their
+ *   magnitudes would push products out of fp32's normal range, so results
+ *   meet the same bound from |x| near 1e-38 to 1e38 (elements more than
+ *   2^40 below the largest of their 64-element slice contribute with a
+ *   relative error of at most 2^-24 of that largest).
  *
  * Errors: every entry point returns a qmv_status.  Argument validation runs
  * before any HIP call, so it needs no GPU.  After a launch, a failed
