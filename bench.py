@@ -137,8 +137,8 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
     if len(cols_list) == 1 and 2 <= kw <= 8:   # one matrix split along K: slices in LDS
         return f"qmv::gemv_lx_kernel<qmv::{pol}, {xt}, 2, 2, 512>"
-    if kw == 1:
-        cfg = "2, 2, 256, true"
+    if kw == 1:   # the shared-activation kernel; INT4 with one-row tiles, three in flight
+        cfg = "1, 3, 256, true" if fmt == "int4_g128" else "2, 2, 256, true"
     else:
         cfg = "2, 2, 256, false" if waves <= 4 else ("2, 2, 512, false" if waves <= 8 else "1, 2, 1024, false")
     pol = {"q8_0": "Q80Policy", "q4_k": "Q4KPolicy", "q6_k": "Q6KPolicy",

@@ -27,6 +27,8 @@ namespace qmv {
 struct Int4G128Policy {
   static constexpr int kColsPerWave = 64 * 64;
   static constexpr int kXElems = 64;
+  // shared-activation GEMV: one-row tiles, three in flight (SxShape)
+  static constexpr int kSxRows = 1, kSxTiles = 3;
   struct XSliceF32 {
     float v[64];  // v[32h + k]: activation of column col[h] + k, scaled by 2^-e (f32_slice_factor)
     float s[2];   // sums of each half's 32 unscaled activations

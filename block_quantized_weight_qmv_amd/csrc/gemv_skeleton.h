@@ -881,6 +881,21 @@ hipError_t launch_lx(const GemvCall& c, int64_t batch, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Rows per tile and tiles in flight of the shared-activation GEMV: two of
+// two rows, unless the format's policy names its own (P::kSxRows,
+// P::kSxTiles).  Measured on the 7B shapes: two-row tiles are best for the
+// K-quants (one-row tiles with three in flight: Q4_K gate+up 15.6 against
+// 15.2 us), one-row tiles with three in flight for INT4 (gate+up 14.0
+// against 14.4 us).
+template <class P, class = void>
+struct SxShape {
+  static constexpr int kRows = 2, kTiles = 2;
+};
+template <class P>
+struct SxShape<P, decltype(void(P::kSxRows))> {
+  static constexpr int kRows = P::kSxRows, kTiles = P::kSxTiles;
+};
+
 template <class P, typename XT>
 hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStream_t stream) {
   const int kw = max_kw<P>(calls, n);
@@ -893,7 +908,9 @@ hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStr
   // flight, or two waves with 4, were no faster in total; the younger wave of
   // a SIMD trails the older one under the oldest-first issue order, but a
   // deeper single wave loses more on the small matrices and at steady state.)
-  if (kw == 1) return launch_cfg<P, XT, 2, 2, 256, true>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+  if (kw == 1)
+    return launch_cfg<P, XT, SxShape<P>::kRows, SxShape<P>::kTiles, 256, true>(calls, n, waves, batch, stream,
+                                                                              kMaxWavesPerSimd);
   if (waves <= 4) return launch_cfg<P, XT, 2, 2, 256, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
   if (waves <= 8) return launch_cfg<P, XT, 2, 2, 512, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
   return launch_cfg<P, XT, 1, 2, 1024, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
