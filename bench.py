@@ -336,6 +336,32 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
             "launch_names": ["+".join(names[m] for m in g) for g in groups]}
 
 
+_F16_FORMS = [
+    (r"_ZN3qmv11gemv_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELb([01])EEEvNS_10GemvLaunchE",
+     lambda m: f"qmv::gemv_kernel<qmv::{m[1]}, _Float16, {m[2]}, {m[3]}, {m[4]}, {'true' if m[5] == '1' else 'false'}>"),
+    (r"_ZN3qmv14gemv_lx_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLxArgsE",
+     lambda m: f"qmv::gemv_lx_kernel<qmv::{m[1]}, _Float16, {m[2]}, {m[3]}, {m[4]}>"),
+    (r"_ZN3qmv16gemv_rows_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi",
+     lambda m: f"qmv::gemv_rows_kernel<qmv::{m[1]}, _Float16, {m[2]}, {m[3]}, {m[4]}, {m[5]}>"),
+    (r"_ZN3qmv22gemv_rows_split_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi",
+     lambda m: f"qmv::gemv_rows_split_kernel<qmv::{m[1]}, _Float16, {m[2]}, {m[3]}, {m[4]}>"),
+]
+
+
+def kernel_display_name(name: str) -> str:
+    """A kernel name as the traces print it, in bench.py's form: without
+    'void ' and the argument list; the _Float16 instantiations, which the
+    demangler leaves mangled, spelled out."""
+    import re
+    name = name.split("(")[0]
+    name = name[5:] if name.startswith("void ") else name
+    for pat, fmt in _F16_FORMS:
+        m = re.fullmatch(pat, name)
+        if m:
+            return fmt(m)
+    return name
+
+
 def _counter_csv(d: str):
     import glob
     files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
@@ -354,8 +380,7 @@ def _per_dispatch(d: str, counter: str):
                 if r["Counter_Name"] != counter:
                     continue
                 key = (f, int(r["Dispatch_Id"]))
-                name = r["Kernel_Name"].split("(")[0]
-                name = name[5:] if name.startswith("void ") else name
+                name = kernel_display_name(r["Kernel_Name"])
                 prev = acc.get(key, (name, 0.0, int(r.get("Grid_Size", 0) or 0)))
                 acc[key] = (name, prev[1] + float(r["Counter_Value"]), prev[2])
     return [acc[k] for k in sorted(acc)]
@@ -447,6 +472,119 @@ def summarize_counters(args) -> int:
     return 0
 
 
+def summarize_trace(args) -> int:
+    """Kernel durations of a rocprofv3 --kernel-trace run of bench.py, per launch.
+
+    Dispatches are grouped by kernel name and grid size (the launches of a
+    step differ in grid size), and each group is summarized by count and
+    median / mean / min duration.  For the dominant kernel the median
+    durations of its launch groups are averaged with equal weight, as
+    bench.py's per-kernel figure weighs every launch of a step once, and
+    turned into the roofline fraction of the same algorithmic bytes."""
+    import csv
+    import glob
+    import statistics
+    files = sorted(glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_trace.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *kernel_trace.csv under {args.summarize_trace}")
+    groups = {}
+    for f in files:
+        with open(f, newline="") as fh:
+            for r in csv.DictReader(fh):
+                name = kernel_display_name(r["Kernel_Name"])
+                grid = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3  # ns -> us
+                groups.setdefault((name, grid), []).append(dur)
+    plan = workload_plan(args.config, args.batch, args.separate, _layout(args), args.x_dtype)
+    dom = plan["dom"]
+    print("| kernel | grid (work-items) | dispatches | median us | mean us | min us |")
+    print("|---|---|---:|---:|---:|---:|")
+    for (name, grid), d in sorted(groups.items(), key=lambda kv: (-len(kv[1]), kv[0])):
+        if not name.startswith("qmv::"):
+            continue
+        print(f"| `{name}` | {grid[0]}x{grid[1]} | {len(d)} | {statistics.median(d):.3f} | "
+              f"{statistics.mean(d):.3f} | {min(d):.3f} |")
+    dom_groups = sorted(((g, d) for (n, g), d in groups.items() if n == dom), key=lambda x: -len(x[1]))
+    nl = len(plan["by_kernel"][dom])
+    dom_groups = dom_groups[:nl]
+    if len(dom_groups) != nl:
+        raise SystemExit(f"{dom}: {len(dom_groups)} launch groups in the trace, {nl} launches per step")
+    avg = sum(statistics.median(d) for _, d in dom_groups) / nl
+    gis = plan["by_kernel"][dom]
+    bpl = sum(plan["gbytes"][gi] for gi in gis) / nl
+    fpl = sum(plan["gflops"][gi] for gi in gis) / nl
+    if plan["bound"][gis[0]] == "mfma":
+        ach, peak, unit = fpl / (avg * 1e-6) / 1e12, PEAK_TFLOPS_BF16, "TFLOP/s"
+    else:
+        ach, peak, unit = bpl / (avg * 1e-6) / 1e9, PEAK_GBPS, "GB/s"
+    print(f"\ndominant `{dom}`: {nl} launches per step, equal-weight mean of their median durations "
+          f"{avg:.3f} us; {bpl:.0f} algorithmic bytes and {fpl:.3e} flops per launch -> {ach:.1f} {unit} "
+          f"= {ach / peak:.4f} of {peak:g}")
+    return 0
+
+
+SQ_DERIVED = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
+              "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
+              "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD")
+
+
+def summarize_sq(args) -> int:
+    """Per-launch SQ counters of rocprofv3 --pmc runs of `bench.py --eager-pass`.
+
+    Every directory given may hold one pass (a handful of SQ counters each).
+    Values are summed over counter instances per dispatch and averaged over
+    the timed steps (after --warmup).  Derived: VALU instructions per weight
+    and lane (SQ_INSTS_VALU x 64 / weights: every wave instruction covers 64
+    lanes), matrix-core operations against the launch's flops, and the
+    fractions of wave cycles spent waiting (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)
+    and issuing VALU (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES)."""
+    plan = workload_plan(args.config, args.batch, args.separate, _layout(args), args.x_dtype)
+    groups, kname = plan["groups"], plan["kname"]
+    seq = []
+    for gi, g in enumerate(groups):
+        seq += [gi] * (len(g) if kname[gi].startswith("qmv::gemm") else 1)
+    vals = [{} for _ in groups]
+    for d in args.summarize_sq:
+        for counter in SQ_DERIVED:
+            ds = [x for x in _per_dispatch_any(d, counter) if x[0].startswith("qmv::") and "repack" not in x[0]]
+            if not ds:
+                continue
+            n_steps = len(ds) // len(seq)
+            if n_steps * len(seq) != len(ds) or n_steps <= args.warmup:
+                raise SystemExit(f"{d} {counter}: {len(ds)} qmv dispatches, not whole {len(seq)}-dispatch steps")
+            acc = [0.0] * len(groups)
+            for i, (name, val, _grid) in enumerate(ds):
+                gi = seq[i % len(seq)]
+                if name != kname[gi]:
+                    raise SystemExit(f"dispatch {i}: kernel {name!r}, expected {kname[gi]!r}")
+                if i // len(seq) >= args.warmup:
+                    acc[gi] += val
+            steps = n_steps - args.warmup
+            for gi in range(len(groups)):
+                vals[gi][counter] = acc[gi] / steps
+    print("| launch | kernel | " + " | ".join(c for c in SQ_DERIVED if any(c in v for v in vals))
+          + " | VALU / weight / lane | wait / wave cycles | VALU issue / wave cycles |")
+    cols = [c for c in SQ_DERIVED if any(c in v for v in vals)]
+    print("|---|---|" + "---:|" * (len(cols) + 3))
+    for gi, g in enumerate(groups):
+        v = vals[gi]
+        weights = sum(plan["mats"][m][1] * plan["mats"][m][2] for m in g)
+        per_w = v["SQ_INSTS_VALU"] * 64 / weights if "SQ_INSTS_VALU" in v else float("nan")
+        wait = v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"] if v.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in v else float("nan")
+        act = v["SQ_ACTIVE_INST_VALU"] / v["SQ_WAVE_CYCLES"] if v.get("SQ_WAVE_CYCLES") and "SQ_ACTIVE_INST_VALU" in v else float("nan")
+        print(f"| {plan['launch_names'][gi]} | `{kname[gi]}` | " + " | ".join(f"{v.get(c, float('nan')):.4g}" for c in cols)
+              + f" | {per_w:.3f} | {wait:.3f} | {act:.3f} |")
+    return 0
+
+
+def _per_dispatch_any(d, counter):
+    """_per_dispatch, or [] when the directory's runs hold no such counter."""
+    try:
+        return _per_dispatch(d, counter)
+    except SystemExit:
+        return []
+
+
 def _layout(args) -> str:
     return (default_layout(args.config, args.batch, args.x_dtype) if args.layout == "auto"
             else args.layout)
@@ -480,9 +618,18 @@ def main() -> int:
                          "--separate/--warmup) and of the probe copy: write profiles/counters.json")
     ap.add_argument("--copy-mib", type=int, default=256, help="size of the calibration copy")
     ap.add_argument("--summary-file", default="", help="profiles/ summary recorded with the counters")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="rocprofv3 --kernel-trace output dir of a bench.py run: per-launch durations "
+                         "(grouped by kernel and grid) and the dominant kernel's roofline fraction")
+    ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
+                    help="rocprofv3 --pmc output dirs (SQ counters) of the eager pass: per-launch table")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(args)
+    if args.summarize_trace:
+        return summarize_trace(args)
+    if args.summarize_sq:
+        return summarize_sq(args)
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
