@@ -512,11 +512,14 @@ gemv_lx_kernel(const GemvLxArgs a) {
 
   // Tile t of this wave: row group g0 + t / nslots, K slot t % nslots;
   // tracked incrementally for the tile being loaded and the one finished.
+  // Prefetches past the wave's own tiles re-read the matrix's last row,
+  // which every wave shares (L2 hits), rather than rows of the next wave.
   int ld_g = g0, ld_k = 0;
   auto load_next = [&](typename P::Frag* f) {
     const P pol(a.w, a.scales_offset, a.cols, ld_k, lane);
+    const int rb = ld_g < g1 ? ld_g * R : r_last;
 #pragma unroll
-    for (int r = 0; r < R; ++r) pol.load(min(ld_g * R + r, r_last), f[r]);
+    for (int r = 0; r < R; ++r) pol.load(min(rb + r, r_last), f[r]);
     if (++ld_k == a.nslots) {
       ld_k = 0;
       ++ld_g;
