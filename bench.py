@@ -83,7 +83,8 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     Q4_K x bf16 above two rows; Q4_K x fp16 from 5 rows -> the matrix-core
     kernels of bf16 with fp16 operands; two or more small Q4_K matrices at
     5-16 fp16/bf16 rows (rows_list summing to at most 8192) -> one multi-row
-    launch)."""
+    launch; Q4_K x fp16/bf16 from 384 rows against matrices of at least 256
+    rows -> the dequantized-tile kernel)."""
     nb_max = max(cols_list) // 256
     if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and 5 <= batch <= 16 and len(cols_list) >= 2
             and max(cols_list) <= 4096 and rows_list is not None and sum(rows_list) <= 8192):
@@ -91,6 +92,10 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         pol = "Q4KPlanesPolicy" if layout == "planes" else "Q4KPolicy"
         xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
         return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, 1, 3, 256, 4>"
+    if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and batch >= 384 and rows_list is not None
+            and min(rows_list) >= 256):  # the dequantized-tile kernel
+        pl = "true" if layout == "planes" else "false"
+        return f"qmv::gemm_q4_k_dqtile<{pl}, {'true' if x_dtype == 'f16' else 'false'}>"
     if fmt == "q4_k" and x_dtype == "f16" and batch >= 17:  # fp16 on the tile kernels
         pl = "true" if layout == "planes" else "false"
         mb = 1 if batch <= 32 else (2 if batch <= 64 else 4)

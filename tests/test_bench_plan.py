@@ -58,7 +58,8 @@ def _library_kernels():
         if ("qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemv_rows_split_kernel<" in line
                 or "qmv::gemv_lx_kernel<" in line
                 or "qmv::gemm_q4_k_bf16_" in line or "qmv::gemm_q4_k_stream<" in line
-                or "qmv::gemm_q4_k_tile<" in line or "qmv::gemm_q4_k_ksplit<" in line):
+                or "qmv::gemm_q4_k_tile<" in line or "qmv::gemm_q4_k_ksplit<" in line
+                or "qmv::gemm_q4_k_dqtile<" in line):
             sym = line.split(" ", 2)[2]
             sym = sym[5:] if sym.startswith("void ") else sym
             names.add(sym.split("(")[0])
@@ -154,9 +155,11 @@ def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
                                           (16, "qmv::gemm_q4_k_stream<false, true>"),
                                           (17, "qmv::gemm_q4_k_tile<1, 1, 2, 5, false, true>"),
                                           (64, "qmv::gemm_q4_k_tile<1, 2, 2, 5, false, true>"),
-                                          (512, "qmv::gemm_q4_k_tile<1, 4, 2, 5, false, true>")])
+                                          (128, "qmv::gemm_q4_k_tile<1, 4, 2, 5, false, true>"),
+                                          (512, "qmv::gemm_q4_k_dqtile<false, true>")])
 def test_q4_k_f16_batches_name_the_f16_matrix_core_kernels(batch, kernel):
-    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands
+    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (from 384
+    # rows, the dequantized-tile kernel)
     names = _library_kernels()
     layout = bench.default_layout(5, batch, "f16")
     assert layout == "blocks"

@@ -33,7 +33,10 @@ TOL = 2e-3
                                              (96, 2, 16), (65, 3, 17), (40, 2, 32), (33, 4, 33),
                                              (17, 74, 8), (300, 9, 24), (1, 1, 3), (16, 1, 31),
                                              (4100, 2, 5), (40000, 1, 9), (3, 16, 16), (33, 17, 12),
-                                             (70, 3, 2), (4100, 2, 2), (1, 1, 2), (17, 74, 2), (5, 130, 2)])
+                                             (70, 3, 2), (4100, 2, 2), (1, 1, 2), (17, 74, 2), (5, 130, 2),
+                                             (300, 3, 130), (257, 2, 256), (1, 1, 128), (520, 5, 300),
+                                             (256, 14, 129), (33, 74, 200), (300, 3, 384), (257, 2, 400),
+                                             (520, 5, 390), (256, 14, 385), (1, 3, 400)])
 def test_mfma_matches_oracle(rows, nblk, batch):
     cols = nblk * 256
     say(f"mfma q4_k {rows}x{cols} batch {batch}")
@@ -47,10 +50,13 @@ def test_mfma_matches_oracle(rows, nblk, batch):
     assert np.all(err <= TOL), err
 
 
-def test_mfma_integer_case_is_exact():
+@pytest.mark.parametrize("rows,batch", [(96, 64), (96, 128), (300, 384), (300, 400)])
+def test_mfma_integer_case_is_exact(rows, batch):
     # d = dmin = 1 and x in {-1, 0, 1}: every product and partial sum is an
-    # integer below 2^24, so the fp32 result is exact on any summation order.
-    rows, cols, batch = 96, 4 * 256, 64
+    # integer below 2^24, so the fp32 result is exact on any summation order
+    # (on the dequantized-tile kernel, from 384 batch rows against 256 weight
+    # rows, the fp16 weights sc u - m are exact integers too).
+    cols = 4 * 256
     f = gen_weights("q4_k", rows, cols, 5)
     f["d_bits"][:] = 0x3C00
     f["dmin_bits"][:] = 0x3C00
@@ -110,7 +116,8 @@ def test_full_size_batched_ffn_sampled_rows(batch):
 @pytest.mark.parametrize("layout", ["blocks", "planes"])
 @pytest.mark.parametrize("rows,nblk,batch", [(67, 14, 5), (130, 3, 16), (1, 1, 8), (33, 16, 9), (200, 14, 12),
                                              (16, 2, 7), (40, 5, 17), (70, 3, 33), (33, 14, 64), (9, 2, 100),
-                                             (17, 74, 20), (130, 3, 129), (33, 74, 5), (70, 20, 16), (5, 130, 9)])
+                                             (17, 74, 20), (130, 3, 129), (33, 74, 5), (70, 20, 16), (5, 130, 9),
+                                             (300, 3, 400), (257, 5, 390)])
 def test_mfma_f16_matches_oracle(layout, rows, nblk, batch):
     # Q4_K x fp16 from 5 rows: the streaming kernel (5-16 rows, X in LDS),
     # the K-split kernel (5-16 rows, K > 4096) or the tile kernels (17 rows
@@ -183,6 +190,76 @@ def test_mfma_f16_tile_graph_replay():
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=s):
             w.gemv(x, "f16", batch, y=yg, stream=s)
+    for _ in range(3):
+        yg.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(yg, y0)
+
+
+@pytest.mark.parametrize("layout", ["blocks", "planes"])
+@pytest.mark.parametrize("spread", ["wide", "large", "tiny", "rising", "falling", "zero_blocks"])
+def test_dq_bf16_activation_range(layout, spread):
+    """From 384 rows the activations enter the matrix cores as fp16, scaled
+    per row by a power of two that follows the largest |x| seen along K and
+    rescales the accumulators when a later block raises it.  Rows far outside
+    fp16's range, twelve decades within a row, magnitudes rising or falling
+    by 2^20 per block along K, and all-zero blocks must all meet the gate."""
+    rows, nblk, batch = 300, 9, 400
+    cols = nblk * 256
+    w = Weights("q4_k", rows, cols, seed=1300)
+    g = np.random.Generator(np.random.PCG64({"wide": 1, "large": 2, "tiny": 3, "rising": 4, "falling": 5,
+                                             "zero_blocks": 6}[spread]))
+    x = g.standard_normal((batch, cols))
+    blk = np.arange(cols) // 256
+    if spread == "wide":
+        x *= 10.0 ** g.uniform(-6, 6, size=x.shape)
+    elif spread == "large":
+        x *= 1e30
+    elif spread == "tiny":
+        x *= 1e-33
+    elif spread == "rising":
+        x *= 2.0 ** (20.0 * blk - 80.0)
+    elif spread == "falling":
+        x *= 2.0 ** (80.0 - 20.0 * blk)
+    else:
+        x[:, (blk % 3) == 1] = 0.0
+        x[::7] = 0.0  # some rows all zero
+    x = (x.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)  # bf16 bit patterns
+    desc = w.desc
+    keep = None
+    if layout == "planes":
+        keep = torch.empty(qmv.qmv_planes_size("q4_k", rows, cols), dtype=torch.uint8, device=DEV)
+        desc = qmv.qmv_repack_planes(w.desc, keep)
+    say(f"dq bf16 activation range {spread} ({layout}) {rows}x{cols} batch {batch}")
+    y = torch.full((batch, rows), 3.5, dtype=torch.float32, device=DEV)
+    qmv.qmv_gemv("q4_k", desc, to_dev_x(x, "bf16"), "bf16", y, rows, cols, batch)
+    got = y.cpu().numpy()
+    assert np.all(np.isfinite(got))
+    err = oracle.normwise_rel_err(got, oracle_y(w, x, "bf16"))
+    say(f"  normwise err max {err.max():.3e}")
+    assert np.all(err <= TOL), err
+
+
+@pytest.mark.parametrize("x_dtype", ["bf16", "f16"])
+def test_dq_deterministic_and_graph_replay(x_dtype):
+    # 400 rows on the dequantized-tile kernel: bitwise equal on a second call
+    # and on every replay of a captured graph
+    rows, cols, batch = 520, 6 * 256, 400
+    say(f"dq {x_dtype} determinism and graph replay")
+    w = Weights("q4_k", rows, cols, seed=1400)
+    x = to_dev_x(gen_x(batch, cols, x_dtype, seed=140), x_dtype)
+    y0 = w.gemv(x, x_dtype, batch)
+    assert torch.equal(w.gemv(x, x_dtype, batch), y0)
+    s = torch.cuda.Stream()
+    yg = torch.zeros(batch, rows, dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        w.gemv(x, x_dtype, batch, y=yg, stream=s)  # warm-up outside the capture
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            w.gemv(x, x_dtype, batch, y=yg, stream=s)
     for _ in range(3):
         yg.fill_(0.0)
         torch.cuda.synchronize()
