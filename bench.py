@@ -530,7 +530,7 @@ def summarize_trace(args) -> int:
 
 SQ_DERIVED = ("SQ_INSTS_VALU", "SQ_INSTS_MFMA", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F16",
               "SQ_BUSY_CYCLES", "SQ_WAVE_CYCLES", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_VALU",
-              "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_LDS", "SQ_INSTS_VMEM_RD")
+              "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_WAVES", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_INSTS_VMEM_RD")
 
 
 def summarize_sq(args) -> int:
@@ -542,7 +542,9 @@ def summarize_sq(args) -> int:
     and lane (SQ_INSTS_VALU x 64 / weights: every wave instruction covers 64
     lanes), matrix-core operations against the launch's flops, and the
     fractions of wave cycles spent waiting (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES)
-    and issuing VALU (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES)."""
+    and issuing VALU (SQ_ACTIVE_INST_VALU / SQ_WAVE_CYCLES), VALU instructions
+    per matrix-core instruction, and LDS bank-conflict cycles per LDS
+    instruction."""
     plan = workload_plan(args.config, args.batch, args.separate, _layout(args), args.x_dtype)
     groups, kname = plan["groups"], plan["kname"]
     seq = []
@@ -568,17 +570,21 @@ def summarize_sq(args) -> int:
             for gi in range(len(groups)):
                 vals[gi][counter] = acc[gi] / steps
     print("| launch | kernel | " + " | ".join(c for c in SQ_DERIVED if any(c in v for v in vals))
-          + " | VALU / weight / lane | wait / wave cycles | VALU issue / wave cycles |")
+          + " | VALU / weight / lane | wait / wave cycles | VALU issue / wave cycles | VALU / MFMA |"
+          " LDS conflict cycles / LDS instruction |")
     cols = [c for c in SQ_DERIVED if any(c in v for v in vals)]
-    print("|---|---|" + "---:|" * (len(cols) + 3))
+    print("|---|---|" + "---:|" * (len(cols) + 5))
     for gi, g in enumerate(groups):
         v = vals[gi]
         weights = sum(plan["mats"][m][1] * plan["mats"][m][2] for m in g)
         per_w = v["SQ_INSTS_VALU"] * 64 / weights if "SQ_INSTS_VALU" in v else float("nan")
         wait = v["SQ_WAIT_INST_ANY"] / v["SQ_WAVE_CYCLES"] if v.get("SQ_WAVE_CYCLES") and "SQ_WAIT_INST_ANY" in v else float("nan")
         act = v["SQ_ACTIVE_INST_VALU"] / v["SQ_WAVE_CYCLES"] if v.get("SQ_WAVE_CYCLES") and "SQ_ACTIVE_INST_VALU" in v else float("nan")
+        per_mfma = v["SQ_INSTS_VALU"] / v["SQ_INSTS_MFMA"] if v.get("SQ_INSTS_MFMA") and "SQ_INSTS_VALU" in v else float("nan")
+        conf = (v["SQ_LDS_BANK_CONFLICT"] / v["SQ_INSTS_LDS"]
+                if v.get("SQ_INSTS_LDS") and "SQ_LDS_BANK_CONFLICT" in v else float("nan"))
         print(f"| {plan['launch_names'][gi]} | `{kname[gi]}` | " + " | ".join(f"{v.get(c, float('nan')):.4g}" for c in cols)
-              + f" | {per_w:.3f} | {wait:.3f} | {act:.3f} |")
+              + f" | {per_w:.3f} | {wait:.3f} | {act:.3f} | {per_mfma:.2f} | {conf:.2f} |")
     return 0
 
 
