@@ -68,6 +68,49 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
+# Compute units of the MI355X; the dequantized-tile dispatch depends on it.
+DEVICE_CUS = 256
+# Q4_K x fp16/bf16 batches from this many rows take the dequantized-tile kernels.
+DQ_MIN_BATCH = 192
+
+
+def dqreg_form(rows: int, batch: int, cus: int = DEVICE_CUS) -> int:
+    """Tiles per wave of gemm_q4_k_dqreg (eight B tiles of 16 activation
+    rows): the launcher's model, rounds of workgroups over the compute units
+    times each workgroup's issue time (18 cycles per product within two VALU
+    instructions per product, 4.5 cycles per further instruction; forming A
+    costs 16 / (2 NB), staging the activations 6 / T per product).  Ties keep
+    the smaller T."""
+    best = None
+    for t in (1, 2, 3, 4, 5):
+        nb = 8
+        wgs = -(-rows // (64 * t)) * -(-batch // (16 * nb))
+        valu = 16.0 / (2 * nb) + 6.0 / t + 0.4
+        per = 18.0 if valu <= 2 else 18.0 + 4.5 * (valu - 2)
+        cost = -(-wgs // cus) * t * nb * per
+        if best is None or cost < best[0]:
+            best = (cost, t)
+    return best[1]
+
+
+def dq_kernel_name(rows: int, batch: int, layout: str, x_dtype: str, cus: int = DEVICE_CUS, cols: int = 0) -> str:
+    """The dequantized-fp16 kernel for one matrix of `rows` x `cols`: the
+    register kernel needs its byte offsets (weights in either layout, the
+    activations) within 32 bits."""
+    pl = "true" if layout == "planes" else "false"
+    f16 = "true" if x_dtype == "f16" else "false"
+    wgs = -(-rows // 256) * -(-batch // 128)
+    nb = cols // 256
+    a = -(-16 * rows * nb // 256) * 256  # the plane unit
+    wbytes = (5 * a + 64 * rows * nb) if layout == "planes" else 144 * rows * nb
+    fits = wbytes < 2 ** 32 and 2 * batch * cols < 2 ** 32
+    if (wgs <= cus and 2 * wgs >= cus) or not fits:
+        return f"qmv::gemm_q4_k_dqtile<{pl}, {f16}>"
+    t = dqreg_form(rows, batch, cus)
+    d = 1 if t >= 3 else 2
+    return f"qmv::gemm_q4_k_dqreg<{t}, 8, {d}, {d}, {pl}, {f16}>"
+
+
 def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str = "blocks",
                 rows_list=None) -> str:
     """Instantiation the library launches for matrices of these widths in one
@@ -83,8 +126,11 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     Q4_K x bf16 above two rows; Q4_K x fp16 from 5 rows -> the matrix-core
     kernels of bf16 with fp16 operands; two or more small Q4_K matrices at
     5-16 fp16/bf16 rows (rows_list summing to at most 8192) -> one multi-row
-    launch; Q4_K x fp16/bf16 from 384 rows against matrices of at least 256
-    rows -> the dequantized-tile kernel)."""
+    launch; Q4_K x fp16/bf16 from 192 rows against matrices of at least 256
+    rows -> a dequantized-tile kernel: gemm_q4_k_dqtile while its grid of
+    256 x 128 tiles fills between half and all of the compute units in one
+    round, else gemm_q4_k_dqreg with its tile height from dqreg_form; the
+    first matrix of a group names the group)."""
     nb_max = max(cols_list) // 256
     if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and 5 <= batch <= 16 and len(cols_list) >= 2
             and max(cols_list) <= 4096 and rows_list is not None and sum(rows_list) <= 8192):
@@ -92,10 +138,9 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         pol = "Q4KPlanesPolicy" if layout == "planes" else "Q4KPolicy"
         xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
         return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, 1, 3, 256, 4>"
-    if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and batch >= 384 and rows_list is not None
-            and min(rows_list) >= 256):  # the dequantized-tile kernel
-        pl = "true" if layout == "planes" else "false"
-        return f"qmv::gemm_q4_k_dqtile<{pl}, {'true' if x_dtype == 'f16' else 'false'}>"
+    if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and batch >= DQ_MIN_BATCH and rows_list is not None
+            and min(rows_list) >= 256):  # the dequantized-tile kernels
+        return dq_kernel_name(rows_list[0], batch, layout, x_dtype, cols=cols_list[0])
     if fmt == "q4_k" and x_dtype == "f16" and batch >= 17:  # fp16 on the tile kernels
         pl = "true" if layout == "planes" else "false"
         mb = 1 if batch <= 32 else (2 if batch <= 64 else 4)

@@ -56,8 +56,8 @@ typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kDqThreads = 512;
-constexpr int kDqRows = 256;   // weight rows per workgroup
-constexpr int kDqBatch = 128;  // batch rows per workgroup
+constexpr int kDqRows = static_cast<int>(kDqTileRows);    // weight rows per workgroup
+constexpr int kDqBatch = static_cast<int>(kDqTileBatch);  // batch rows per workgroup
 constexpr int kDqBufUnits = 2 * kDqRows * 4 + 2 * kDqBatch * 4;
 constexpr size_t kDqLdsBytes = 2 * static_cast<size_t>(kDqBufUnits) * 16 + 3 * kDqBatch * sizeof(float);
 
@@ -327,6 +327,17 @@ gemm_q4_k_dqtile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x,
 
 hipError_t gemm_q4_k_dq(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
                         hipStream_t stream) {
+  // This kernel while its grid fills between half and all of the compute
+  // units in one round; otherwise (a second round of workgroups, or too few
+  // weight rows to fill the device) the register-dequantized kernel, whose
+  // tile height follows the shape (measured on the 7B FFN shapes, bf16: 18944
+  // rows at 256-384 batch rows 86-87 us here against 87-106 us there; at 512
+  // rows 165 against 111 us; 3584 rows at 192-512 batch rows 333-350 against
+  // 208 us).
+  const int64_t wgs = (W.rows + kDqTileRows - 1) / kDqTileRows * ((batch + kDqTileBatch - 1) / kDqTileBatch);
+  const int64_t cus = device_cus();
+  if ((wgs > cus || 2 * wgs < cus) && gemm_q4_k_dqreg_fits(W, batch))
+    return gemm_q4_k_dqreg(W, x, f16x, y, batch, stream);
   const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols), M = static_cast<int>(batch);
   const uint8_t* w = static_cast<const uint8_t*>(W.data);
   const uint16_t* xh = static_cast<const uint16_t*>(x);

@@ -77,23 +77,32 @@ constexpr int64_t kMfmaMinBatch = QMV_MFMA_MIN_BATCH;
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t s);
 // Batches of at least kDqMinBatch rows (bf16 or fp16 activations) against
-// matrices of at least kDqMinRows rows: the dequantized-tile kernel
-// (gemm_q4_k_dq.hip), entered from the launchers of gemm_q4_k_mfma.hip.  It
-// rounds each weight to fp16 (relative error near 2^-11), which the
-// normwise bound absorbs over a matrix of a few hundred rows (about 4e-4 on
-// the 7B FFN shapes) but not over a handful of rows, where one output's
-// cancellation sets the error; smaller matrices keep the exact-product
-// kernels.  Measured against the 64-row tile kernel on the 7B FFN shapes:
-// 512 rows, 18944 x 3584 166 against 171 us and 3584 x 18944 349 against
-// 668 us; 256 rows 86 against 90 and 351 against 335 us; 128 rows 86
-// against 47 us.
+// matrices of at least kDqMinRows rows: the dequantized-tile kernels
+// (gemm_q4_k_dq.hip, which hands shapes whose grid would not fill one round
+// well to gemm_q4_k_dqreg.hip), entered from the launchers of
+// gemm_q4_k_mfma.hip.  They round each weight to fp16 (relative error near
+// 2^-11), which the normwise bound absorbs over a matrix of a few hundred
+// rows (about 4e-4 on the 7B FFN shapes) but not over a handful of rows,
+// where one output's cancellation sets the error; smaller matrices keep the
+// exact-product kernels.  Measured against the 64-row tile kernel on the 7B
+// FFN shapes (bf16): 18944 x 3584 at 128 rows 65 against 47 us, at 192-256
+// rows 86-87 against 90 us, at 512 rows 111 against 171 us; 3584 x 18944 at
+// 128 rows 209 against 169 us, at 192 rows 207 against 333 us.
 #ifndef QMV_DQ_MIN_BATCH
-#define QMV_DQ_MIN_BATCH 384
+#define QMV_DQ_MIN_BATCH 192
 #endif
 constexpr int64_t kDqMinBatch = QMV_DQ_MIN_BATCH;
 constexpr int64_t kDqMinRows = 256;
+// Tile of gemm_q4_k_dq: weight rows x activation rows per workgroup.
+constexpr int64_t kDqTileRows = 256, kDqTileBatch = 128;
 hipError_t gemm_q4_k_dq(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
                         hipStream_t s);
+// The register-dequantized kernel (gemm_q4_k_dqreg.hip): tile shape chosen
+// by dqreg_form; byte offsets must fit in 32 bits.
+bool gemm_q4_k_dqreg_fits(const qmv_weights& W, int64_t batch);
+int dqreg_form(int64_t rows, int64_t batch);
+hipError_t gemm_q4_k_dqreg(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
+                           hipStream_t s);
 // Q4_K x fp16 on the matrix cores with fp16 operands: the kernels of the
 // bf16 path (streaming or K-split up to 16 rows, tiles from 17).  qmv_gemv
 // takes it from kMfmaMinF16Batch rows; below, the multi-row GEMV is faster.

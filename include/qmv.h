@@ -221,12 +221,14 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * runs on the matrix cores with fp16 operands (exact products, fp32 sums).  Other Q4_K x bf16 calls with batch >= 2 run the
  * matrix-core path (weights read once for up to 16 activation rows, once per
  * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
- * independent of timing).  From 384 activation rows against at least 256
- * weight rows, Q4_K x bf16/fp16 runs the dequantized-tile kernel instead:
- * each weight is rounded to fp16 once per tile (relative error near 2^-11)
- * and each activation row is scaled by a power of two into fp16, so the
- * products are no longer exact; the normwise bound still holds over such
- * matrices (about 4e-4 on the 7B FFN shapes).  Otherwise each activation row is a GEMV over the
+ * independent of timing).  From 192 activation rows against at least 256
+ * weight rows, Q4_K x bf16/fp16 runs one of two dequantized-fp16 kernels
+ * instead (weight tiles shared in LDS when that grid fills half to all of
+ * the compute units in one round, else per-wave fragments in registers):
+ * each weight is rounded to fp16 (relative error near 2^-11) and each bf16
+ * activation row is scaled by a power of two into fp16, so the products are
+ * no longer exact; the normwise bound still holds over such matrices (about
+ * 4e-4 on the 7B FFN shapes).  Results stay independent of timing.  Otherwise each activation row is a GEMV over the
  * packed weights.  Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the
  * same arithmetic, in the same order, as the canonical layout on every one
  * of these paths, so results equal bit for bit. */

@@ -59,7 +59,7 @@ def _library_kernels():
                 or "qmv::gemv_lx_kernel<" in line
                 or "qmv::gemm_q4_k_bf16_" in line or "qmv::gemm_q4_k_stream<" in line
                 or "qmv::gemm_q4_k_tile<" in line or "qmv::gemm_q4_k_ksplit<" in line
-                or "qmv::gemm_q4_k_dqtile<" in line):
+                or "qmv::gemm_q4_k_dqtile<" in line or "qmv::gemm_q4_k_dqreg<" in line):
             sym = line.split(" ", 2)[2]
             sym = sym[5:] if sym.startswith("void ") else sym
             names.add(sym.split("(")[0])
@@ -156,10 +156,12 @@ def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
                                           (17, "qmv::gemm_q4_k_tile<1, 1, 2, 5, false, true>"),
                                           (64, "qmv::gemm_q4_k_tile<1, 2, 2, 5, false, true>"),
                                           (128, "qmv::gemm_q4_k_tile<1, 4, 2, 5, false, true>"),
-                                          (512, "qmv::gemm_q4_k_dqtile<false, true>")])
+                                          (256, "qmv::gemm_q4_k_dqtile<false, true>"),
+                                          (512, "qmv::gemm_q4_k_dqreg<5, 8, 1, 1, false, true>")])
 def test_q4_k_f16_batches_name_the_f16_matrix_core_kernels(batch, kernel):
-    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (from 384
-    # rows, the dequantized-tile kernel)
+    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (from 192
+    # rows, a dequantized-tile kernel: 18944 rows in 256 x 128 tiles fill one
+    # round at 256 rows, not at 512)
     names = _library_kernels()
     layout = bench.default_layout(5, batch, "f16")
     assert layout == "blocks"
@@ -187,3 +189,17 @@ def test_small_multi_matrix_batches_name_the_rows_kernel(x_dtype, batch):
     qkv, o = plan["kname"][0], plan["kname"][1]
     assert qkv.startswith("qmv::gemv_rows_kernel<") and qkv in names, qkv
     assert o.startswith("qmv::gemm_q4_k_"), o
+
+
+@pytest.mark.parametrize("rows,batch,form", [(18944, 512, 5), (3584, 512, 1), (3584, 192, 1), (18944, 640, 3),
+                                             (300, 400, 1), (4096, 1024, 2)])
+def test_dqreg_form(rows, batch, form):
+    # the tile height the launcher's model picks (mirrored here for naming)
+    assert bench.dqreg_form(rows, batch) == form
+
+
+@pytest.mark.parametrize("rows,batch,kind", [(18944, 192, "dqtile"), (18944, 384, "dqtile"), (18944, 512, "dqreg"),
+                                             (3584, 512, "dqreg"), (300, 400, "dqreg"), (32768, 256, "dqtile")])
+def test_dq_kernel_choice(rows, batch, kind):
+    # the 256 x 128 tile kernel while its grid fills half to all of 256 CUs in one round
+    assert bench.dq_kernel_name(rows, batch, "blocks", "bf16").startswith(f"qmv::gemm_q4_k_{kind}<")

@@ -1,5 +1,8 @@
 """Batched Q4_K x bf16 on the matrix-core path, and Q4_K x fp16 on its
-streaming kernel (5-16 rows with X in LDS) and tile kernels (17 rows up).
+streaming kernel (5-16 rows with X in LDS) and tile kernels (17 rows up);
+from 192 rows against 256 weight rows and more, the two kernels on fp16
+weights dequantized on the chip (tiles shared in LDS, or per-wave fragments
+in registers, each in every tile form the launcher picks).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
@@ -8,11 +11,12 @@ fp32 GEMV; inputs whose products and sums are small integers are exact on both
 paths and are checked exactly.  Shapes cover the three kernels behind the call
 (batch <= 16 with X in LDS: one to eight 16-row tiles per workgroup and more
 workgroups than CUs; batch <= 32 or K too long for LDS: K split over waves;
-larger batches: 64 x 64 tiles), ragged rows and batches, the smallest batch
-routed here (2: matrices wider than eight waves along K; narrower ones take
-the multi-row GEMV at batch 2, and at 3-4 those within one wave's K slice),
-and the full-size batched workload (18944 x 3584, M = 4, 16,
-64 and 512) on sampled rows.
+larger batches: 64 x 64 tiles; from 192 rows the dequantized-fp16 kernels),
+ragged rows and batches, the smallest batch routed here (2: matrices wider
+than eight waves along K; narrower ones take the multi-row GEMV at batch 2,
+and at 3-4 those within one wave's K slice), and the full-size batched
+workload (18944 x 3584 at M = 4, 16, 64, 256 and 512, and 3584 x 18944 at
+M = 512) on sampled rows.
 """
 import numpy as np
 import pytest
@@ -36,7 +40,12 @@ TOL = 2e-3
                                              (70, 3, 2), (4100, 2, 2), (1, 1, 2), (17, 74, 2), (5, 130, 2),
                                              (300, 3, 130), (257, 2, 256), (1, 1, 128), (520, 5, 300),
                                              (256, 14, 129), (33, 74, 200), (300, 3, 384), (257, 2, 400),
-                                             (520, 5, 390), (256, 14, 385), (1, 3, 400)])
+                                             (520, 5, 390), (256, 14, 385), (1, 3, 400),
+                                             # per-wave register fragments, 2..5 tiles per wave
+                                             (10000, 1, 300), (10001, 3, 300), (18944, 1, 640), (18950, 2, 630),
+                                             (30000, 1, 512), (30001, 1, 500), (18944, 2, 512), (18900, 3, 509),
+                                             # LDS-shared tiles (grids of half to all compute units)
+                                             (4100, 1, 1000), (8200, 2, 520), (6000, 3, 700)])
 def test_mfma_matches_oracle(rows, nblk, batch):
     cols = nblk * 256
     say(f"mfma q4_k {rows}x{cols} batch {batch}")
@@ -50,12 +59,12 @@ def test_mfma_matches_oracle(rows, nblk, batch):
     assert np.all(err <= TOL), err
 
 
-@pytest.mark.parametrize("rows,batch", [(96, 64), (96, 128), (300, 384), (300, 400)])
+@pytest.mark.parametrize("rows,batch", [(96, 64), (96, 128), (300, 384), (300, 400), (4100, 1000)])
 def test_mfma_integer_case_is_exact(rows, batch):
     # d = dmin = 1 and x in {-1, 0, 1}: every product and partial sum is an
     # integer below 2^24, so the fp32 result is exact on any summation order
-    # (on the dequantized-tile kernel, from 384 batch rows against 256 weight
-    # rows, the fp16 weights sc u - m are exact integers too).
+    # (on the dequantized-fp16 kernels, from 192 batch rows against 256
+    # weight rows, the fp16 weights sc u - m are exact integers too).
     cols = 4 * 256
     f = gen_weights("q4_k", rows, cols, 5)
     f["d_bits"][:] = 0x3C00
@@ -93,13 +102,14 @@ def test_mfma_deterministic_and_graph_replay(batch):
         assert torch.equal(yg, y1)
 
 
-@pytest.mark.parametrize("batch", [4, 16, 64, 512])
-def test_full_size_batched_ffn_sampled_rows(batch):
-    cfg = CONFIGS[5]
-    _, rows, cols = cfg["mats"][0]
+@pytest.mark.parametrize("config,mat,batch", [(5, 0, 4), (5, 0, 16), (5, 0, 64), (5, 0, 256), (5, 0, 512),
+                                              (3, 6, 512)])
+def test_full_size_batched_ffn_sampled_rows(config, mat, batch):
+    # the 7B FFN's gate (18944 x 3584) and down (3584 x 18944) matrices
+    _, rows, cols = CONFIGS[config]["mats"][mat]
     say(f"full-size mfma {rows}x{cols} batch {batch}")
-    w = Weights("q4_k", rows, cols, seed=weight_seed(5, 0))
-    x = gen_x(batch, cols, "bf16", x_seed(5, 0))
+    w = Weights("q4_k", rows, cols, seed=weight_seed(config, mat))
+    x = gen_x(batch, cols, "bf16", x_seed(config, 0))
     y = w.gemv(to_dev_x(x, "bf16"), "bf16", batch).cpu().numpy()
     g = np.random.Generator(np.random.PCG64(batch))
     ids = np.sort(g.choice(rows, size=48, replace=False))
@@ -156,7 +166,7 @@ def test_mfma_f16_integer_case_is_exact():
     np.testing.assert_array_equal(y, y64.astype(np.float32))
 
 
-@pytest.mark.parametrize("batch", [5, 16, 64, 512])
+@pytest.mark.parametrize("batch", [5, 16, 64, 256, 512])
 def test_full_size_f16_batched_ffn_sampled_rows(batch):
     cfg = CONFIGS[5]
     _, rows, cols = cfg["mats"][0]
@@ -200,13 +210,16 @@ def test_mfma_f16_tile_graph_replay():
 
 @pytest.mark.parametrize("layout", ["blocks", "planes"])
 @pytest.mark.parametrize("spread", ["wide", "large", "tiny", "rising", "falling", "zero_blocks"])
-def test_dq_bf16_activation_range(layout, spread):
-    """From 384 rows the activations enter the matrix cores as fp16, scaled
-    per row by a power of two that follows the largest |x| seen along K and
-    rescales the accumulators when a later block raises it.  Rows far outside
-    fp16's range, twelve decades within a row, magnitudes rising or falling
-    by 2^20 per block along K, and all-zero blocks must all meet the gate."""
-    rows, nblk, batch = 300, 9, 400
+@pytest.mark.parametrize("rows,nblk,batch", [(300, 9, 400), (18944, 3, 512), (4100, 3, 1000)])
+def test_dq_bf16_activation_range(layout, spread, rows, nblk, batch):
+    """From 192 rows the activations enter the matrix cores as fp16, scaled
+    per row by a power of two: on the LDS-tile kernel one that follows the
+    largest |x| seen along K and rescales the accumulators when a later block
+    raises it; on the register-fragment kernel one fixed per row from its
+    first block, the row's pass taken again from its maximum when a later
+    block would overflow fp16.  Rows far outside fp16's range, twelve decades
+    within a row, magnitudes rising or falling by 2^20 per block along K, and
+    all-zero blocks must all meet the gate, on one to five tiles per wave."""
     cols = nblk * 256
     w = Weights("q4_k", rows, cols, seed=1300)
     g = np.random.Generator(np.random.PCG64({"wide": 1, "large": 2, "tiny": 3, "rising": 4, "falling": 5,
@@ -243,11 +256,12 @@ def test_dq_bf16_activation_range(layout, spread):
 
 
 @pytest.mark.parametrize("x_dtype", ["bf16", "f16"])
-def test_dq_deterministic_and_graph_replay(x_dtype):
-    # 400 rows on the dequantized-tile kernel: bitwise equal on a second call
-    # and on every replay of a captured graph
-    rows, cols, batch = 520, 6 * 256, 400
-    say(f"dq {x_dtype} determinism and graph replay")
+@pytest.mark.parametrize("rows,cols,batch", [(520, 6 * 256, 400), (4100, 2 * 256, 1000), (18944, 2 * 256, 512)])
+def test_dq_deterministic_and_graph_replay(x_dtype, rows, cols, batch):
+    # the dequantized-fp16 kernels (register fragments, LDS tiles, five tiles
+    # per wave): bitwise equal on a second call and on every replay of a
+    # captured graph
+    say(f"dq {x_dtype} determinism and graph replay {rows}x{cols} batch {batch}")
     w = Weights("q4_k", rows, cols, seed=1400)
     x = to_dev_x(gen_x(batch, cols, x_dtype, seed=140), x_dtype)
     y0 = w.gemv(x, x_dtype, batch)

@@ -7,7 +7,7 @@ one eager step of bench.py is traced with rocprofv3 (kernel trace only) in a
 child process, and the GEMV dispatches of that step, in order, must carry the
 names the plan gives (the load-time repacks and the probes are left out).  A
 launch group served by the matrix-core kernels dispatches one kernel per
-matrix; every other group is one dispatch.
+matrix, named for that matrix's shape; every other group is one dispatch.
 """
 import csv
 import glob
@@ -27,8 +27,8 @@ import bench  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 PLANS = [(1, None, None), (2, None, None), (3, None, None), (4, None, None), (6, None, None),
-         (5, 1, None), (5, 4, None), (5, 16, None), (5, 64, None), (5, 512, None),
-         (3, 8, "bf16"), (3, 8, "f16"), (5, 512, "f16"), (5, 100, "f16"), (2, 4, None)]
+         (5, 1, None), (5, 4, None), (5, 16, None), (5, 64, None), (5, 256, None), (5, 512, None),
+         (3, 8, "bf16"), (3, 8, "f16"), (5, 512, "f16"), (5, 100, "f16"), (2, 4, None), (3, 256, "bf16")]
 
 
 def _dispatched(trace_dir):
@@ -64,6 +64,10 @@ def test_bench_kernel_names_are_dispatched(config, batch, x_dtype):
         got = _dispatched(td)
     want = []
     for g, k in zip(plan["groups"], plan["kname"]):
-        want += [k] * (len(g) if k.startswith("qmv::gemm_q4_k_") else 1)
+        if k.startswith("qmv::gemm_q4_k_"):  # one matrix-core dispatch per matrix, each named for its shape
+            want += [bench.kernel_name(plan["fmt"], [plan["mats"][m][2]], plan["x_dtype"], plan["batch"], layout,
+                                       [plan["mats"][m][1]]) for m in g]
+        else:
+            want.append(k)
     say(f"  dispatched {got}")
     assert got == want, (got, want)
