@@ -377,12 +377,20 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
     for gi in range(len(groups)):
         by_kernel.setdefault(kname[gi], []).append(gi)
     dom = max(by_kernel, key=lambda k: sum(gbytes[gi] for gi in by_kernel[k]))
+    # the dispatches of one step in order: one per matrix where a group runs
+    # on the matrix-core kernels (each named for its matrix), else one per group
+    dispatches = []
+    for gi, g in enumerate(groups):
+        if kname[gi].startswith("qmv::gemm"):
+            dispatches += [(gi, m, kernel_name(fmt, [mats[m][2]], x_dtype, batch, layout, [mats[m][1]])) for m in g]
+        else:
+            dispatches.append((gi, None, kname[gi]))
     workload = (cfg["name"] + (f"_m{batch}" if config == 5 or batch_given else "")
                 + (f"_x{x_dtype}" if x_dtype != cfg["x_dtype"] else ""))
     return {"cfg": cfg, "fmt": fmt, "x_dtype": x_dtype, "batch": batch, "mats": mats,
             "names": names, "groups": groups, "wbytes": wbytes, "gbytes": gbytes,
             "gflops": gflops, "kname": kname, "bound": bound, "by_kernel": by_kernel,
-            "dom": dom, "workload": workload, "layout": layout,
+            "dom": dom, "workload": workload, "layout": layout, "dispatches": dispatches,
             "launch_names": ["+".join(names[m] for m in g) for g in groups]}
 
 
@@ -525,51 +533,125 @@ def summarize_counters(args) -> int:
 def summarize_trace(args) -> int:
     """Kernel durations of a rocprofv3 --kernel-trace run of bench.py, per launch.
 
-    Dispatches are grouped by kernel name and grid size (the launches of a
-    step differ in grid size), and each group is summarized by count and
-    median / mean / min duration.  For the dominant kernel the median
-    durations of its launch groups are averaged with equal weight, as
-    bench.py's per-kernel figure weighs every launch of a step once, and
-    turned into the roofline fraction of the same algorithmic bytes."""
+    The trace holds full steps, the timing replays restricted to one kernel's
+    launches or to one launch, and load-time work.  The first full step in it
+    fixes each dispatch's grid; the dispatches are then read in time order as
+    a chain of those replays (at each point the replay just matched if it
+    matches again, as a graph repeats one pattern, else the longest that
+    matches by kernel name and grid), which assigns every dispatch to its
+    matrix even where several matrices share a kernel and a grid (a run of
+    replays that could be any of several goes to the one whose durations in
+    the full steps are nearest).  Every dispatch of a
+    step is summarized by count and median / mean / min duration; a launch
+    takes the sum of its dispatches' medians.  For the dominant kernel these
+    launch times are averaged with equal weight, as bench.py's per-kernel
+    figure weighs every launch of a step once, and turned into the roofline
+    fraction of the same algorithmic bytes or flops."""
     import csv
     import glob
     import statistics
     files = sorted(glob.glob(os.path.join(args.summarize_trace, "**", "*kernel_trace.csv"), recursive=True))
     if not files:
         raise SystemExit(f"no *kernel_trace.csv under {args.summarize_trace}")
-    groups = {}
+    rows = []
     for f in files:
         with open(f, newline="") as fh:
             for r in csv.DictReader(fh):
                 name = kernel_display_name(r["Kernel_Name"])
                 grid = (int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
-                dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-3  # ns -> us
-                groups.setdefault((name, grid), []).append(dur)
+                start = int(r["Start_Timestamp"])
+                rows.append((start, name, grid, (int(r["End_Timestamp"]) - start) * 1e-3))  # ns -> us
+    rows.sort()
     plan = workload_plan(args.config, args.batch, args.separate, _layout(args), args.x_dtype)
-    dom = plan["dom"]
-    print("| kernel | grid (work-items) | dispatches | median us | mean us | min us |")
-    print("|---|---|---:|---:|---:|---:|")
-    for (name, grid), d in sorted(groups.items(), key=lambda kv: (-len(kv[1]), kv[0])):
-        if not name.startswith("qmv::"):
-            continue
-        print(f"| `{name}` | {grid[0]}x{grid[1]} | {len(d)} | {statistics.median(d):.3f} | "
+    disp = plan["dispatches"]
+    step_names = [n for _, _, n in disp]
+    toks = [(n, g, d) for _, n, g, d in rows if n in step_names]
+    others = {}
+    for _, n, g, d in rows:
+        if n not in step_names and n.startswith("qmv::"):
+            others.setdefault((n, g), []).append(d)
+    first = next((i for i in range(len(toks) - len(disp) + 1)
+                  if [t[0] for t in toks[i:i + len(disp)]] == step_names), None)
+    if first is None:
+        raise SystemExit("no full step in the trace")
+    slot_tok = [(n, toks[first + si][1]) for si, n in enumerate(step_names)]
+    pats = {tuple(range(len(disp)))}
+    for gis in plan["by_kernel"].values():
+        pats.add(tuple(si for si, d in enumerate(disp) if d[0] in gis))
+    for gi in range(len(plan["groups"])):
+        pats.add(tuple(si for si, d in enumerate(disp) if d[0] == gi))
+    # replays whose dispatches look alike (say two matrices of one kernel and
+    # grid, each timed alone) form one class; a run of such replays goes to
+    # the member whose durations in the full steps are nearest
+    classes = {}
+    for pat in pats:
+        classes.setdefault(tuple(slot_tok[si] for si in pat), []).append(pat)
+    order = sorted(classes, key=len, reverse=True)
+    durs = [[] for _ in disp]
+    runs = []  # (class key, [dispatch durations per replay]) for ambiguous classes
+    p = unmatched = 0
+    prev = None
+    while p < len(toks):
+        # a graph replays one pattern many times over: the pattern just seen
+        # first, then the longest
+        for key in ([prev] if prev else []) + order:
+            if p + len(key) <= len(toks) and all(toks[p + k][:2] == key[k] for k in range(len(key))):
+                prev = key
+                ds = [toks[p + k][2] for k in range(len(key))]
+                if len(classes[key]) == 1:
+                    for k, si in enumerate(classes[key][0]):
+                        durs[si].append(ds[k])
+                elif runs and runs[-1][0] == key and runs[-1][2] == p:
+                    runs[-1][1].append(ds)
+                    runs[-1][2] = p + len(key)
+                else:
+                    runs.append([key, [ds], p + len(key)])
+                p += len(key)
+                break
+        else:
+            unmatched += 1
+            p += 1
+            prev = None
+    ref = [statistics.median(d) if d else None for d in durs]
+    for key, reps, _ in runs:
+        run_med = [statistics.median(r[k] for r in reps) for k in range(len(key))]
+
+        def miss(pat):
+            return sum(abs(run_med[k] / ref[si] - 1.0) if ref[si] else 1e9 for k, si in enumerate(pat))
+        best = min(classes[key], key=miss)
+        for r in reps:
+            for k, si in enumerate(best):
+                durs[si].append(r[k])
+    names, mats = plan["names"], plan["mats"]
+    print("| launch | matrix | kernel | grid (work-items) | dispatches | median us | mean us | min us |")
+    print("|---|---|---|---|---:|---:|---:|---:|")
+    launch_us = [0.0] * len(plan["groups"])
+    for si, (gi, m, name) in enumerate(disp):
+        d = durs[si]
+        grid = slot_tok[si][1]
+        med = statistics.median(d)
+        launch_us[gi] += med
+        mat = f"{names[m]} {mats[m][1]}x{mats[m][2]}" if m is not None else "all"
+        print(f"| {plan['launch_names'][gi]} | {mat} | `{name}` | {grid[0]}x{grid[1]} | {len(d)} | {med:.3f} | "
               f"{statistics.mean(d):.3f} | {min(d):.3f} |")
-    dom_groups = sorted(((g, d) for (n, g), d in groups.items() if n == dom), key=lambda x: -len(x[1]))
-    nl = len(plan["by_kernel"][dom])
-    dom_groups = dom_groups[:nl]
-    if len(dom_groups) != nl:
-        raise SystemExit(f"{dom}: {len(dom_groups)} launch groups in the trace, {nl} launches per step")
-    avg = sum(statistics.median(d) for _, d in dom_groups) / nl
+    for (name, grid), d in sorted(others.items()):
+        print(f"| (other) | | `{name}` | {grid[0]}x{grid[1]} | {len(d)} | {statistics.median(d):.3f} | "
+              f"{statistics.mean(d):.3f} | {min(d):.3f} |")
+    if unmatched:
+        print(f"\n{unmatched} dispatches of these kernels matched no replay of the step and are left out.")
+    dom = plan["dom"]
     gis = plan["by_kernel"][dom]
+    nl = len(gis)
+    avg = sum(launch_us[gi] for gi in gis) / nl
     bpl = sum(plan["gbytes"][gi] for gi in gis) / nl
     fpl = sum(plan["gflops"][gi] for gi in gis) / nl
     if plan["bound"][gis[0]] == "mfma":
         ach, peak, unit = fpl / (avg * 1e-6) / 1e12, PEAK_TFLOPS_BF16, "TFLOP/s"
     else:
         ach, peak, unit = bpl / (avg * 1e-6) / 1e9, PEAK_GBPS, "GB/s"
-    print(f"\ndominant `{dom}`: {nl} launches per step, equal-weight mean of their median durations "
-          f"{avg:.3f} us; {bpl:.0f} algorithmic bytes and {fpl:.3e} flops per launch -> {ach:.1f} {unit} "
-          f"= {ach / peak:.4f} of {peak:g}")
+    print(f"\ndominant `{dom}`: {nl} launches per step, equal-weight mean of their durations (sums of their "
+          f"dispatch medians) {avg:.3f} us; {bpl:.0f} algorithmic bytes and {fpl:.3e} flops per launch -> "
+          f"{ach:.1f} {unit} = {ach / peak:.4f} of {peak:g}")
     return 0
 
 
