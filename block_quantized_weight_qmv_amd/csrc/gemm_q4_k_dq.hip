@@ -308,19 +308,30 @@ gemm_q4_k_dqtile(const uint8_t* w, uint64_t pa, int N, int K, const uint16_t* x,
     if (qx == 0) fin_lds[rx] = __builtin_amdgcn_ldexpf(1.f, e_run);
     lds_barrier();
   }
+  // Lane (q4, r16) holds outputs n .. n + 3 of activation row mrow: one
+  // 16-byte store when the row length keeps it aligned.
   const int r16 = lane & 15, q4 = lane >> 4;
+  const bool row4 = (N & 3) == 0;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int mrow = 64 * wm + 16 * j + r16;
     const int m = m0 + mrow;
     const float fs = F16X ? 1.f : fin_lds[mrow];
+    if (m < M) {
+      float* yr = y + static_cast<size_t>(m) * N;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < 4; ++i) {
+        const int n = n0 + 64 * wn + 16 * i + 4 * q4;
+        const f32x4_t v = acc[i][j] * fs;
+        if (row4 && n + 4 <= N) {
+          *reinterpret_cast<f32x4_t*>(yr + n) = v;
+        } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = n0 + 64 * wn + 16 * i + 4 * q4 + r;
-        if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = acc[i][j][r] * fs;
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) yr[n + r] = v[r];
+        }
       }
+    }
   }
 }
 

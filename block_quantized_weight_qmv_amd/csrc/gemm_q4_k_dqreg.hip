@@ -503,18 +503,30 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
     }
     lds_barrier();
   }
+  // Lane (g, r16) holds outputs n .. n + 3 (n = 16 i + 4 g) of activation
+  // row 16 j + r16: one 16-byte store when the row length keeps it aligned
+  // (scattered 4-byte stores cost about a fifth of the kernel at five tiles).
+  const bool row4 = (N & 3) == 0;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
     const int mr = 16 * j + r16;
     const int m = m0 + mr;
     const float fs = F16X ? 1.f : fin_lds[mr];
+    if (m < M) {
+      float* yr = y + static_cast<size_t>(m) * N;
 #pragma unroll
-    for (int i = 0; i < T; ++i)
+      for (int i = 0; i < T; ++i) {
+        const int n = nw0 + 16 * i + 4 * g;
+        const f32x4_t v = acc[i][j] * fs;
+        if (row4 && n + 4 <= N) {
+          *reinterpret_cast<f32x4_t*>(yr + n) = v;
+        } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int n = nw0 + 16 * i + 4 * g + r;
-        if (m < M && n < N) y[static_cast<size_t>(m) * N + n] = acc[i][j][r] * fs;
+          for (int r = 0; r < 4; ++r)
+            if (n + r < N) yr[n + r] = v[r];
+        }
       }
+    }
   }
 }
 

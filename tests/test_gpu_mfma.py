@@ -45,7 +45,7 @@ TOL = 2e-3
                                              (10000, 1, 300), (10001, 3, 300), (18944, 1, 640), (18950, 2, 630),
                                              (30000, 1, 512), (30001, 1, 500), (18944, 2, 512), (18900, 3, 509),
                                              # LDS-shared tiles (grids of half to all compute units)
-                                             (4100, 1, 1000), (8200, 2, 520), (6000, 3, 700)])
+                                             (4100, 1, 1000), (8200, 2, 520), (6000, 3, 700), (4099, 2, 1000)])
 def test_mfma_matches_oracle(rows, nblk, batch):
     cols = nblk * 256
     say(f"mfma q4_k {rows}x{cols} batch {batch}")
