@@ -68,47 +68,81 @@ def kernel_source_hash(kernel: str) -> str:
     return h.hexdigest()[:16]
 
 
-# Compute units of the MI355X; the dequantized-tile dispatch depends on it.
+# Compute units of the MI355X; the register-dequantized plans depend on it.
 DEVICE_CUS = 256
-# Q4_K x fp16/bf16 batches from this many rows take the dequantized-tile kernels.
-DQ_MIN_BATCH = 192
+# Q4_K x fp16/bf16 batches take the register-dequantized kernels from
+# DQ_MIN_BATCH rows, or from DQ_MIN_BATCH_LONGK rows against matrices of at
+# least DQ_LONGK columns, against matrices of at least DQ_MIN_ROWS rows.
+DQ_MIN_BATCH, DQ_MIN_BATCH_LONGK, DQ_LONGK, DQ_MIN_ROWS = 128, 64, 8192, 256
 
 
-def dqreg_form(rows: int, batch: int, cus: int = DEVICE_CUS) -> int:
-    """Tiles per wave of gemm_q4_k_dqreg (eight B tiles of 16 activation
-    rows): the launcher's model, rounds of workgroups over the compute units
-    times each workgroup's issue time (18 cycles per product within two VALU
-    instructions per product, 4.5 cycles per further instruction; forming A
-    costs 16 / (2 NB), staging the activations 6 / T per product).  Ties keep
-    the smaller T."""
-    best = None
-    for t in (1, 2, 3, 4, 5):
-        nb = 8
-        wgs = -(-rows // (64 * t)) * -(-batch // (16 * nb))
-        valu = 16.0 / (2 * nb) + 6.0 / t + 0.4
-        per = 18.0 if valu <= 2 else 18.0 + 4.5 * (valu - 2)
-        cost = -(-wgs // cus) * t * nb * per
-        if best is None or cost < best[0]:
-            best = (cost, t)
-    return best[1]
-
-
-def dq_kernel_name(rows: int, batch: int, layout: str, x_dtype: str, cus: int = DEVICE_CUS, cols: int = 0) -> str:
-    """The dequantized-fp16 kernel for one matrix of `rows` x `cols`: the
-    register kernel needs its byte offsets (weights in either layout, the
-    activations) within 32 bits."""
-    pl = "true" if layout == "planes" else "false"
-    f16 = "true" if x_dtype == "f16" else "false"
-    wgs = -(-rows // 256) * -(-batch // 128)
+def dq_route(rows: int, cols: int, batch: int, layout: str) -> bool:
+    """The launcher's dqreg_route for a Q4_K matrix and fp16/bf16 rows (byte
+    offsets of weights and activations within 32 bits)."""
+    if rows < DQ_MIN_ROWS or not (batch >= DQ_MIN_BATCH or (batch >= DQ_MIN_BATCH_LONGK and cols >= DQ_LONGK)):
+        return False
     nb = cols // 256
     a = -(-16 * rows * nb // 256) * 256  # the plane unit
     wbytes = (5 * a + 64 * rows * nb) if layout == "planes" else 144 * rows * nb
-    fits = wbytes < 2 ** 32 and 2 * batch * cols < 2 ** 32
-    if (wgs <= cus and 2 * wgs >= cus) or not fits:
-        return f"qmv::gemm_q4_k_dqtile<{pl}, {f16}>"
-    t = dqreg_form(rows, batch, cus)
+    return wbytes < 2 ** 32 and 2 * batch * cols < 2 ** 32
+
+
+def dqreg_plan(rows: int, cols: int, batch: int, cus: int = DEVICE_CUS):
+    """(T, NB, slices, blocks per slice) of gemm_q4_k_dqreg: the launcher's
+    model, rounds of workgroups over the compute units times a workgroup's
+    time ((14 + 17 / T) ns per product of a wave at NB = 8, (20 + 16 / T) at
+    NB = 4, 5.5 us fixed), plus the sum of the partial outputs when K is
+    sliced (3 us and its bytes at 8 TB/s).  Ties keep the first in the order
+    NB = 8 then 4, smaller T, fewer slices."""
+    nb = cols // 256
+    best = None
+    for nbt in (8, 4):
+        for t in (1, 2, 3, 4, 5):
+            for s in range(1, min(8, nb) + 1):
+                bps = -(-nb // s)
+                splits = -(-nb // bps)
+                if splits != s:
+                    continue
+                wgs = -(-rows // (64 * t)) * -(-batch // (16 * nbt)) * splits
+                products = float(bps * 8 * nbt * t)
+                per = 20.0 + 16.0 / t if nbt == 4 else 14.0 + 17.0 / t
+                us = float(-(-wgs // cus)) * (products * per * 1e-3 + 5.5)
+                if splits > 1:
+                    us += 3.0 + float(splits + 1) * rows * batch * 4 / 8e6
+                if best is None or us < best[0]:
+                    best = (us, t, nbt, splits, bps)
+    return best[1:]
+
+
+def dq_kernel_name(rows: int, cols: int, batch: int, layout: str) -> str:
+    """The register-dequantized kernel for one matrix of `rows` x `cols`."""
+    pl = "true" if layout == "planes" else "false"
+    t, nbt = dqreg_plan(rows, cols, batch)[:2]
     d = 1 if t >= 3 else 2
-    return f"qmv::gemm_q4_k_dqreg<{t}, 8, {d}, {d}, {pl}, {f16}>"
+    return f"qmv::gemm_q4_k_dqreg<{t}, {nbt}, {d}, {d}, {pl}>"
+
+
+def group_dispatches(fmt: str, mats, x_dtype: str, batch: int, layout: str):
+    """Kernels the matrices (rows, cols) of one launch on the matrix-core path
+    dispatch, in order: each register-dequantized matrix after the
+    activation conversion (skipped when the previous matrix was converted
+    from the same activations: a launch's matrices share them) and, with K
+    in slices, before the sum of its partial outputs."""
+    out = []
+    prev = None
+    for rows, cols in mats:
+        k = kernel_name(fmt, [cols], x_dtype, batch, layout, [rows])
+        if k.startswith("qmv::gemm_q4_k_dqreg<"):
+            if prev != cols:
+                out.append(f"qmv::act_rows_f16<{'false' if x_dtype == 'f16' else 'true'}>")
+            out.append(k)
+            if dqreg_plan(rows, cols, batch)[2] > 1:
+                out.append("qmv::dqreg_sum")
+            prev = cols
+        else:
+            out.append(k)
+            prev = None
+    return out
 
 
 def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str = "blocks",
@@ -126,11 +160,9 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     Q4_K x bf16 above two rows; Q4_K x fp16 from 5 rows -> the matrix-core
     kernels of bf16 with fp16 operands; two or more small Q4_K matrices at
     5-16 fp16/bf16 rows (rows_list summing to at most 8192) -> one multi-row
-    launch; Q4_K x fp16/bf16 from 192 rows against matrices of at least 256
-    rows -> a dequantized-tile kernel: gemm_q4_k_dqtile while its grid of
-    256 x 128 tiles fills between half and all of the compute units in one
-    round, else gemm_q4_k_dqreg with its tile height from dqreg_form; the
-    first matrix of a group names the group)."""
+    launch; Q4_K x fp16/bf16 from 128 rows (from 64 against 8192 columns and
+    more) against matrices of at least 256 rows -> gemm_q4_k_dqreg in the
+    form dqreg_plan picks; the first matrix of a group names the group)."""
     nb_max = max(cols_list) // 256
     if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and 5 <= batch <= 16 and len(cols_list) >= 2
             and max(cols_list) <= 4096 and rows_list is not None and sum(rows_list) <= 8192):
@@ -138,9 +170,9 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         pol = "Q4KPlanesPolicy" if layout == "planes" else "Q4KPolicy"
         xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
         return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, 1, 3, 256, 4>"
-    if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and batch >= DQ_MIN_BATCH and rows_list is not None
-            and min(rows_list) >= 256):  # the dequantized-tile kernels
-        return dq_kernel_name(rows_list[0], batch, layout, x_dtype, cols=cols_list[0])
+    if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and rows_list is not None
+            and dq_route(rows_list[0], cols_list[0], batch, layout)):  # the register-dequantized kernels
+        return dq_kernel_name(rows_list[0], cols_list[0], batch, layout)
     if fmt == "q4_k" and x_dtype == "f16" and batch >= 17:  # fp16 on the tile kernels
         pl = "true" if layout == "planes" else "false"
         mb = 1 if batch <= 32 else (2 if batch <= 64 else 4)
@@ -377,12 +409,19 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
     for gi in range(len(groups)):
         by_kernel.setdefault(kname[gi], []).append(gi)
     dom = max(by_kernel, key=lambda k: sum(gbytes[gi] for gi in by_kernel[k]))
-    # the dispatches of one step in order: one per matrix where a group runs
-    # on the matrix-core kernels (each named for its matrix), else one per group
+    # the dispatches of one step in order: per matrix where a group runs on
+    # the matrix-core kernels (each named for its matrix, with the register
+    # kernel's conversion and sum kernels), else one per group
     dispatches = []
     for gi, g in enumerate(groups):
         if kname[gi].startswith("qmv::gemm"):
-            dispatches += [(gi, m, kernel_name(fmt, [mats[m][2]], x_dtype, batch, layout, [mats[m][1]])) for m in g]
+            ks = group_dispatches(fmt, [(mats[m][1], mats[m][2]) for m in g], x_dtype, batch, layout)
+            # each dispatch is credited to the matrix of the product kernel it serves
+            mi = 0
+            for k in ks:
+                dispatches.append((gi, g[min(mi, len(g) - 1)], k))
+                if k.startswith("qmv::gemm"):
+                    mi += 1
         else:
             dispatches.append((gi, None, kname[gi]))
     workload = (cfg["name"] + (f"_m{batch}" if config == 5 or batch_given else "")
@@ -462,11 +501,9 @@ def summarize_counters(args) -> int:
     fetch_scale = copy_kib / copy_mean(cfetch_d, "FETCH_SIZE")
     write_scale = copy_kib / copy_mean(cwrite_d, "WRITE_SIZE")
 
-    # expected dispatch sequence of one step: the GEMV kernel once per launch,
-    # the matrix-core kernel once per matrix
-    seq = []
-    for gi, g in enumerate(groups):
-        seq += [gi] * (len(g) if kname[gi].startswith("qmv::gemm") else 1)
+    # expected dispatch sequence of one step (launch of each dispatch): the
+    # GEMV kernel once per launch, the matrix-core kernels per matrix
+    seq = [d[0] for d in plan["dispatches"]]
     per_launch = []
     for counter, d in (("FETCH_SIZE", fetch_d), ("WRITE_SIZE", write_d)):
         # GEMV / matrix-core dispatches only (the plane repack runs at load)
@@ -674,9 +711,10 @@ def summarize_sq(args) -> int:
     instruction."""
     plan = workload_plan(args.config, args.batch, args.separate, _layout(args), args.x_dtype)
     groups, kname = plan["groups"], plan["kname"]
-    seq = []
-    for gi, g in enumerate(groups):
-        seq += [gi] * (len(g) if kname[gi].startswith("qmv::gemm") else 1)
+    # launch of each dispatch of a step; only the kernel that names the
+    # launch is counted (not the activation conversion or the partial sums)
+    seq = [d[0] for d in plan["dispatches"]]
+    counted = [d[2] == kname[d[0]] for d in plan["dispatches"]]
     vals = [{} for _ in groups]
     for d in args.summarize_sq:
         for counter in SQ_DERIVED:
@@ -689,9 +727,10 @@ def summarize_sq(args) -> int:
             acc = [0.0] * len(groups)
             for i, (name, val, _grid) in enumerate(ds):
                 gi = seq[i % len(seq)]
-                if name != kname[gi]:
-                    raise SystemExit(f"dispatch {i}: kernel {name!r}, expected {kname[gi]!r}")
-                if i // len(seq) >= args.warmup:
+                want = plan["dispatches"][i % len(seq)][2]
+                if name != want:
+                    raise SystemExit(f"dispatch {i}: kernel {name!r}, expected {want!r}")
+                if i // len(seq) >= args.warmup and counted[i % len(seq)]:
                     acc[gi] += val
             steps = n_steps - args.warmup
             for gi in range(len(groups)):
@@ -867,6 +906,11 @@ def main() -> int:
     # rotation over weight copies and the launch order are unchanged -> its average
     # launch duration (the duration plus the small gap between graph nodes).
     cap = torch.cuda.Stream(dev)
+    # one eager step on the capture stream first: the batched kernels keep a
+    # workspace per stream, which is allocated outside graph capture
+    for g in groups:
+        launch(0, g, cap.cuda_stream)
+    torch.cuda.synchronize()
     spread = []   # (min, median, max) ms of each timed region's replays
 
     def timed_graph(gis):

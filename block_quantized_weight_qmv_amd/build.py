@@ -24,7 +24,7 @@ COMMON = ["-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno-unused-function", f"-I{IN
 DEVICE = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 HIP_SOURCES = ["api.cpp", "gemv_q8_0.hip", "gemv_q4_k.hip", "gemv_q5_k.hip", "gemv_q6_k.hip",
-               "gemv_int4_g128.hip", "gemm_q4_k_mfma.hip", "gemm_q4_k_dq.hip", "gemm_q4_k_dqreg.hip", "dequant.hip", "repack.hip", "probe.hip"]
+               "gemv_int4_g128.hip", "gemm_q4_k_mfma.hip", "gemm_q4_k_dqreg.hip", "dequant.hip", "repack.hip", "probe.hip"]
 CXX_SOURCES = ["packer.cpp"]
 # Per-source device flags.  The matrix-core kernels scale each product in
 # VALU right away; in accumulation registers every result would need a

@@ -10,6 +10,9 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+#include <vector>
+
 #include <hip/hip_runtime.h>
 
 #include "api_internal.h"
@@ -34,6 +37,52 @@ int32_t ok() {
 }
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Workspaces of the batched kernels, one per (device, stream).  Calls on one
+// stream run in order, so its workspace is never used by two calls at once;
+// calls on different streams never share one.  A workspace that grows is
+// replaced, not freed: graphs captured earlier keep valid addresses.
+namespace {
+struct Workspace {
+  int dev;
+  hipStream_t stream;
+  void* ptr;
+  size_t bytes;
+};
+std::mutex g_ws_mu;
+std::vector<Workspace> g_ws;
+}  // namespace
+
+hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lock(g_ws_mu);
+  Workspace* ws = nullptr;
+  for (Workspace& w : g_ws)
+    if (w.dev == dev && w.stream == s) ws = &w;
+  if (ws && ws->bytes >= bytes) {
+    *out = ws->ptr;
+    return hipSuccess;
+  }
+  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+  e = hipStreamIsCapturing(s, &cap);
+  if (e != hipSuccess) return e;
+  if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
+  const size_t grow = ws ? 2 * bytes : bytes;
+  const size_t want = (grow + (2u << 20) - 1) / (2u << 20) * (2u << 20);
+  void* p = nullptr;
+  e = hipMalloc(&p, want);
+  if (e != hipSuccess) return e;
+  if (ws) {
+    ws->ptr = p;
+    ws->bytes = want;
+  } else {
+    g_ws.push_back(Workspace{dev, s, p, want});
+  }
+  *out = p;
+  return hipSuccess;
+}
 
 static int32_t from_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -321,12 +370,10 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     };
     if (nn) e = rows(narrow, nn);
     if (e == hipSuccess && ns) e = rows(split, ns);
-    for (int i = 0; i < nm && e == hipSuccess; ++i)
-      e = qmv::gemm_q4_k_f16(*mfma16[i].W, mfma16[i].x, mfma16[i].y, batch, s);
+    if (e == hipSuccess && nm) e = qmv::gemm_q4_k_mfma_items(mfma16, nm, true, batch, s);
     if (e == hipSuccess && nw) {
       if (q4k_mfma) {
-        for (int i = 0; i < nw && e == hipSuccess; ++i)
-          e = qmv::gemm_q4_k_bf16(*wide[i].W, wide[i].x, wide[i].y, batch, s);
+        e = qmv::gemm_q4_k_mfma_items(wide, nw, false, batch, s);
       } else {
         switch (fmt) {
           case QMV_Q4_K:
@@ -346,11 +393,16 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
         }
       }
     }
+    if (e == hipErrorStreamCaptureUnsupported)
+      return qmv::fail(QMV_ERR_HIP, "qmv_gemv: the workspace of this stream must grow, which cannot happen "
+                                    "under stream capture: make the same call once before capturing");
     return qmv::from_hip(e, "qmv_gemv (multi-row) launch");
   }
   if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
-    for (int i = 0; i < n && e == hipSuccess; ++i)
-      e = qmv::gemm_q4_k_bf16(*calls[i].W, calls[i].x, calls[i].y, batch, s);
+    e = qmv::gemm_q4_k_mfma_items(calls, n, false, batch, s);
+    if (e == hipErrorStreamCaptureUnsupported)
+      return qmv::fail(QMV_ERR_HIP, "qmv_gemv: the workspace of this stream must grow, which cannot happen "
+                                    "under stream capture: make the same call once before capturing");
     return qmv::from_hip(e, "qmv_gemv (MFMA tiles) launch");
   }
   switch (fmt) {

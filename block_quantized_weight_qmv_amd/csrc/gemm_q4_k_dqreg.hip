@@ -1,29 +1,39 @@
 // Batched Q4_K on the gfx950 matrix cores, weights dequantized into operand
-// registers: Y[m][n] = sum_k X[m][k] W[n][k] for a hundred or more activation
-// rows X (bf16 or fp16) and Q4_K weights W (canonical or plane layout),
-// y layout [batch][rows].
+// registers: Y[m][n] = sum_k X[m][k] W[n][k] for tens to hundreds of
+// activation rows X (bf16 or fp16) and Q4_K weights W (canonical or plane
+// layout), y layout [batch][rows].
 //
 // The batched-prefill reading of the pages' kernel families (hipEngine
 // "Quickstart": matrix-core prefill beside GEMV decode): once a weight meets
-// a hundred or more activation rows, it is cheaper to convert it to the
-// matrix-core type once than to apply its scales to every product.
+// tens of activation rows, it is cheaper to convert it to the matrix-core
+// type once than to apply its scales to every product.
+//
+// Three kernels per call, in stream order:
+// 1. act_rows_f16: the activations to fp16 once, into the workspace: bf16
+//    rows scaled by a power of two 2^-e per row (e from the row's largest
+//    |x|, which lands in [2^14, 2^15)), fp16 rows as given; each group of
+//    eight columns in the operand order (0, 2, 1, 3, 4, 6, 5, 7) below.
+// 2. gemm_q4_k_dqreg: the products over one of S slices of K (whole
+//    256-column blocks); with S = 1 straight into y, else into S partial
+//    outputs in the workspace.  Results are multiplied by 2^e at the end.
+// 3. (S > 1) dqreg_sum: y = the sum of the partial outputs in slice order,
+//    so results are independent of timing.
 //
 // Workgroup: four waves, one per SIMD.  Wave w owns 16 T consecutive weight
 // rows (T tiles of 16) and all 16 NB activation rows of the workgroup's batch
-// tile (NB = 8 or 16 B tiles).  Each wave dequantizes its own weight tiles
-// straight into A operand registers: weights never pass through LDS and are
-// converted once.  The activation tile is converted to fp16 once per
-// workgroup into LDS, where all four waves read it as B operands.  Per
-// 32-column step a wave issues NB T v_mfma_f32_16x16x32_f16 against NB LDS
-// reads.
+// tile.  Each wave dequantizes its own weight tiles straight into A operand
+// registers: weights never pass through LDS and are converted once.  The
+// fp16 activation tile is copied into LDS per half block (no arithmetic),
+// where all four waves read it as B operands.  Per 32-column step a wave
+// issues NB T v_mfma_f32_16x16x32_f16 against NB LDS reads.
 //
-// What sets the time (measured on gfx950 with an issue probe): one wave
-// issues about two independent VALU instructions under each 16-cycle
-// product for free; beyond that the VALU issue sets the pace.  Forming an A
-// operand costs about 16 VALU instructions (two per product at NB = 8, one
-// at NB = 16); converting the activation tile costs about 3 per value, i.e.
-// about 6 / T per product.  The host picks (T, NB) per shape from that and
-// from how many workgroups fill the compute units.
+// What sets the time (gfx950, measured): one wave issues about two
+// independent VALU instructions under each 16-cycle product for free; beyond
+// that the VALU issue sets the pace.  Forming an A operand costs about 16
+// VALU instructions (two per product at NB = 8).  Each B operand read (1 KB
+// per wave) serves T products, so T = 1 leaves the four waves bound by LDS
+// bandwidth.  The host picks T and S per shape from a model fitted to such
+// measurements and from how many workgroups fill the compute units.
 //
 // K order.  A block is walked in two halves of four steps, half h covering
 // columns 128 h .. 128 h + 128 (code chunks c = 2h and 2h + 1: sub-blocks
@@ -41,27 +51,13 @@
 // packed add.  Each weight carries about one and a half fp16 roundings
 // (relative error near 2^-11) against its fp32 value.
 //
-// Activations are staged per half block (16 NB rows x 128 columns of fp16)
-// into one of two LDS buffers, one barrier per half block; their loads run
-// one or two half blocks ahead.  bf16 rows are scaled by a power of two 2^-e
-// fixed per row for the whole of K: e is set from the row's largest |x| in
-// the first half block with 8 bits of headroom (and at least -112), so that
-// the fp16 copy is exact from 256 times that maximum down to 2^-20 of it;
-// the conversion is integer arithmetic on the bit patterns (exponent minus
-// 112 + e, saturating at zero, mantissa moved up three bits), and bf16
-// subnormals become zero.  Every later half block checks its own maximum
-// against the headroom; if any row of the workgroup would overflow, the
-// workgroup computes its tile once more with each row's e taken from its
-// largest |x| over all of K (found on the first pass).  A rising magnitude
-// along K costs a second pass; no accumulator is ever rescaled.  Results are
-// multiplied by 2^e at the end.  fp16 activations enter as given.
-//
 // LDS unit (16 bytes) of activation row n, step t of the half, k-group g:
 // 16 n + 8 (t & 1) + (f(t, g) ^ s(n)) with f(t, g) = (t >> 1) + 2 (g & 1) +
 // 4 ((t & 1) ^ (g >> 1)) and s(n) = 4 (n & 1) + ((n >> 1) & 3).  The operand
 // reads (eight rows at one (t, g)) and the staging stores (two rows, four
 // consecutive 16-byte pieces each) both land any eight lanes of a row of the
 // wave on eight different 16-byte bank groups of a 128-byte line.
+#include <algorithm>
 #include <type_traits>
 #include <utility>
 
@@ -78,36 +74,15 @@ typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kRgThreads = 256;  // four waves
 constexpr int kRgRowUnits = 16;  // 16-byte units per activation row and half block
-constexpr int kRgHeadroom = 8;   // bits of bf16 row-scale headroom over the first half block
+constexpr int kRgNB = 8;         // B tiles per workgroup: 128 activation rows
 
 __host__ __device__ constexpr int rg_batch(int nb) { return 16 * nb; }
 __host__ __device__ constexpr int rg_buf_units(int nb) { return rg_batch(nb) * kRgRowUnits; }
-__host__ __device__ constexpr size_t rg_lds_bytes(int nb) {
-  return 2 * static_cast<size_t>(rg_buf_units(nb)) * 16 + rg_batch(nb) * sizeof(float) + 16;
-}
+__host__ __device__ constexpr size_t rg_lds_bytes(int nb) { return 2 * static_cast<size_t>(rg_buf_units(nb)) * 16; }
 
 __device__ __forceinline__ int rg_swz(int n) { return ((n & 1) << 2) | ((n >> 1) & 3); }
 __device__ __forceinline__ int rg_unit(int n, int t, int g) {
   return 16 * n + 8 * (t & 1) + (((t >> 1) | ((g & 1) << 1) | (((t & 1) ^ (g >> 1)) << 2)) ^ rg_swz(n));
-}
-
-// Exponent index of a row's largest |x| (from its sign-cleared bf16 bit
-// patterns, the four lanes of the row combined): eb such that the maximum
-// scaled by 2^-eb lies in [2^14, 2^15).
-__device__ __forceinline__ int rg_eb(u16x2_t m2) {
-  int mx = max(static_cast<int>(m2.x), static_cast<int>(m2.y));
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0xB1, 0xF, 0xF, false));  // lane ^ 1
-  mx = max(mx, __builtin_amdgcn_update_dpp(0, mx, 0x4E, 0xF, 0xF, false));  // lane ^ 2
-  const int eb = (mx >> 7) - 127 - 14;  // the maximum lies in [2^E, 2^(E+1)), E = (bits >> 7) - 127
-  return eb < -126 ? -126 : (eb > 113 ? 113 : eb);
-}
-
-// bf16 pair (sign-cleared m, original v) scaled by 2^-e to an fp16 pair:
-// exponent field minus 112 + e (sub = that << 7 in both halves), saturating
-// at zero, mantissa up three bits, sign back.
-__device__ __forceinline__ uint32_t rg_bf16x2_to_f16x2(uint32_t m, uint32_t v, u16x2_t sub) {
-  const u16x2_t t = __builtin_elementwise_sub_sat(__builtin_bit_cast(u16x2_t, m), sub) << 3;
-  return __builtin_bit_cast(uint32_t, t) | (v & 0x80008000u);
 }
 
 template <int V>
@@ -123,32 +98,116 @@ __device__ __forceinline__ void rg_static_for(F&& f) {
   rg_static_for(f, std::make_integer_sequence<int, N>{});
 }
 
-// Nothing may be scheduled across this point: the instruction order of a
-// step is the order written.
+// Nothing may be scheduled across this point.
 __device__ __forceinline__ void rg_fence() { __builtin_amdgcn_sched_barrier(0); }
+
+// Two fp16 bit patterns a (low), b (high) as one dword.
+__device__ __forceinline__ uint32_t rg_pack(_Float16 a, _Float16 b) {
+  return static_cast<uint32_t>(__builtin_bit_cast(unsigned short, a)) |
+         (static_cast<uint32_t>(__builtin_bit_cast(unsigned short, b)) << 16);
+}
 
 }  // namespace
 
+// Activations [M][K] (bf16 when BF16, else fp16) to the operand form of
+// gemm_q4_k_dqreg: out [M][K] fp16, each group of eight columns in the order
+// (0, 2, 1, 3, 4, 6, 5, 7); scale[m] = 2^e, the factor the products of row m
+// carry back.  bf16 row m is multiplied by 2^-e with e set from its largest
+// |x| (bit patterns with the sign cleared order as the magnitudes do): the
+// largest lands in [2^14, 2^15), so no value overflows fp16 and values down
+// to 2^-24 of the largest keep full fp16 precision; each value is rounded to
+// nearest once.  e = 0 for an all-zero row; e stays within [-126, 127].  One
+// workgroup per row: a pass for the maximum (four loads in flight per
+// thread), a pass for the conversion (the row is in L2 by then).  K a
+// multiple of 8, x and out 16-byte aligned.
+template <bool BF16>
+__global__ void __launch_bounds__(256) act_rows_f16(const uint16_t* x, int K, uint16_t* out, float* scale) {
+  __shared__ int wmax[4];
+  const int tid = static_cast<int>(threadIdx.x), lane = tid & 63;
+  const int row = static_cast<int>(blockIdx.x);
+  const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<size_t>(row) * K);
+  uint4* orow = reinterpret_cast<uint4*>(out + static_cast<size_t>(row) * K);
+  const int n8 = K >> 3;
+  int e = 0;
+  if constexpr (BF16) {
+    u16x2_t m2 = {0, 0};
+    int i = tid;
+    for (; i + 3 * 256 < n8; i += 4 * 256) {
+      uint4 v[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) v[u] = xr[i + 256 * u];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].x & 0x7FFF7FFFu));
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].y & 0x7FFF7FFFu));
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].z & 0x7FFF7FFFu));
+        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].w & 0x7FFF7FFFu));
+      }
+    }
+    for (; i < n8; i += 256) {
+      const uint4 v = xr[i];
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu));
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu));
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
+    }
+    int mx = max(static_cast<int>(m2.x), static_cast<int>(m2.y));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = max(mx, __shfl_xor(mx, o));
+    if (lane == 0) wmax[tid >> 6] = mx;
+    __syncthreads();
+    mx = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    // the largest lies in [2^E, 2^(E+1)) with E = (bits >> 7) - 127
+    e = mx == 0 ? 0 : (mx >> 7) - 127 - 14;
+    e = e < -126 ? -126 : (e > 127 ? 127 : e);
+  }
+  const float s = __builtin_amdgcn_ldexpf(1.f, -e);
+  for (int i = tid; i < n8; i += 256) {
+    const uint4 v = xr[i];  // (x0 x1) (x2 x3) (x4 x5) (x6 x7)
+    uint4 o;
+    if constexpr (BF16) {
+      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      _Float16 h[8];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        h[2 * k] = static_cast<_Float16>(__builtin_bit_cast(float, w[k] << 16) * s);
+        h[2 * k + 1] = static_cast<_Float16>(__builtin_bit_cast(float, w[k] & 0xFFFF0000u) * s);
+      }
+      o = make_uint4(rg_pack(h[0], h[2]), rg_pack(h[1], h[3]), rg_pack(h[4], h[6]), rg_pack(h[5], h[7]));
+    } else {
+      o = make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
+                     __builtin_amdgcn_perm(v.w, v.z, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+    }
+    orow[i] = o;
+  }
+  if (tid == 0) scale[row] = __builtin_amdgcn_ldexpf(1.f, e);
+}
+
 // T: 16-row weight tiles per wave.  NB: 16-row activation (B) tiles per
-// workgroup, 8 or 16.  XD: activation loads run XD half blocks ahead (1 or
-// 2).  CD: code loads run CD half blocks ahead (1 or 2).  PL: plane layout.
-// F16X: fp16 activations (else bf16).  All byte offsets fit in 32 bits
-// (checked by the launcher).
-template <int T, int NB, int XD, int CD, bool PL, bool F16X>
+// workgroup.  XD: activation loads run XD half blocks ahead (1 or 2).  CD:
+// code loads run CD half blocks ahead (1 or 2).  PL: plane layout.  x: the
+// activations in act_rows_f16's form; xs[m]: the factor of row m.  Blocks
+// kb0 = z bps .. min(kb0 + bps, K / 256) of the slice z = blockIdx.z; out:
+// y when there is one slice, else the partial outputs of slice z at
+// out + z zs ([M][N] each).  All byte offsets fit in 32 bits (checked by the
+// launcher).
+template <int T, int NB, int XD, int CD, bool PL>
 __global__ void __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, float* y, int M) {
+gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, const float* xs, float* out,
+                size_t zs, int M, int bps) {
   constexpr int kBatch = rg_batch(NB), kBufUnits = rg_buf_units(NB);
   constexpr int RS = NB / 4;  // activation rows staged per lane
   extern __shared__ __attribute__((aligned(16))) uint4 rg_lds[];
-  float* fin_lds = reinterpret_cast<float*>(rg_lds + 2 * kBufUnits);  // [activation row]: 2^e
-  int* ovf_lds = reinterpret_cast<int*>(fin_lds + kBatch);             // [wave]: a row would overflow
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nb = K >> 8;
+  const int kb0 = static_cast<int>(blockIdx.z) * bps;
+  const int kb1 = min(kb0 + bps, nb);
   const int m0 = static_cast<int>(blockIdx.y) * kBatch;
   const int g = lane >> 4, r16 = lane & 15;
   const uint8_t* xbytes = reinterpret_cast<const uint8_t*>(x);
+  float* y = out + blockIdx.z * zs;
 
   // Weight role: tile i of this wave is weight rows nw0 + 16 i .. + 16; lane
   // (g, r16) loads row nw0 + 16 i + r16 (rows past N re-read the last row,
@@ -162,7 +221,8 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
   uint4 hdr[T];            // header of the next block to decode
   uint4 qc[CD][2][T];      // code pieces [block parity (CD = 2)][half][tile]
   uint32_t scl[T][2][2];   // [tile][half h][nibble]: (fp16(d sc), -fp16(dmin m)) of sub-block 2c + nibble
-  // The code pieces of half h of block b into ring slot (sp, h).
+  // The code pieces of half h of block b into ring slot (sp, h) (loads past
+  // the slice read the next blocks, up to the last, unused).
   auto load_codes = [&](int b, auto sp_c, auto h_c) {
     constexpr int sp = decltype(sp_c)::value, h = decltype(h_c)::value;
     const uint32_t bc = static_cast<uint32_t>(min(b, nb - 1));
@@ -201,7 +261,7 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
     }
   };
 
-  // Staging role: lane 4 q + gs of the wave stages the 8-column pieces
+  // Staging role: lane 4 q + gs of the wave copies the 8-column pieces
   // 4 k + gs (k = 0..3) of the half of activation rows n = 16 wave + q + 64 s
   // (s < RS; rows past M re-read the last row): the four lanes of a row read
   // 64 consecutive bytes per load instruction.
@@ -210,7 +270,7 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
 #pragma unroll
   for (int s = 0; s < RS; ++s)
     xoff[s] = 2u * (static_cast<uint32_t>(min(m0 + ns + 64 * s, M - 1)) * static_cast<uint32_t>(K) + 8u * gs);
-  uint4 xr[XD][RS][4];  // raw pieces [ring slot][row][k]
+  uint4 xr[XD][RS][4];  // pieces in flight [ring slot][row][k]
   // Loads of half block H (clamped to the last): columns 128 H + 32 k + 8 gs.
   auto load_x = [&](int H, auto slot_c) {
     constexpr int slot = decltype(slot_c)::value;
@@ -220,80 +280,14 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
 #pragma unroll
       for (int k = 0; k < 4; ++k) xr[slot][s][k] = ld16(xbytes + (xoff[s] + kb + 64u * k));
   };
-
-  // bf16 row scales of this lane's staged rows: the exponent in use, the
-  // largest seen over K, the packed exponent subtrahend, and whether a row
-  // would overflow.
-  int e_fix[RS], e_max[RS];
-  u16x2_t esub[RS];
-  u16x2_t mrow[RS];  // running |x| maxima over a half
-#pragma unroll
-  for (int s = 0; s < RS; ++s) {
-    e_fix[s] = 0;
-    e_max[s] = -126;
-    esub[s] = u16x2_t{0, 0};
-    mrow[s] = u16x2_t{0, 0};
-  }
-  uint32_t ovf = 0;
-  int pass = 0;
-  uint32_t ostage[2] = {0, 0};  // the first two dwords of a piece being converted
-  auto set_scale = [&](int s, int e) {
-    e_fix[s] = e < -112 ? -112 : (e > 126 ? 126 : e);
-    const unsigned short v = static_cast<unsigned short>((112 + e_fix[s]) << 7);
-    esub[s] = u16x2_t{v, v};
-  };
-
-  // Staging pieces.  store (r, k, h) converts dwords 2 h, 2 h + 1 of piece k
-  // of row r (h = 1 stores the piece: columns 32 k + 8 gs of the half, step
-  // t = 2 (gs & 1) + (k & 1), k-group g = 2 (k >> 1) + (gs >> 1)), folding
-  // the values into the row's running maximum when tracked; check (r) checks
-  // the row's maximum against its scale.
-  auto store = [&](auto xs_c, auto nx_c, auto r_c, auto k_c, auto h_c, bool track) {
-    constexpr int xs = decltype(xs_c)::value, nx = decltype(nx_c)::value, r = decltype(r_c)::value;
-    constexpr int k = decltype(k_c)::value, h = decltype(h_c)::value;
-    const uint4 v = xr[xs][r][k];  // columns c .. c + 8: (x0 x1) (x2 x3) (x4 x5) (x6 x7)
-    const uint32_t lo = h ? v.z : v.x, hi = h ? v.w : v.y;
-    uint32_t cl, ch;
-    if constexpr (F16X) {
-      cl = lo;
-      ch = hi;
-    } else {
-      const uint32_t ml = lo & 0x7FFF7FFFu, mh = hi & 0x7FFF7FFFu;
-      if (track) {
-        const u16x2_t m = (k == 0 && h == 0) ? u16x2_t{0, 0} : mrow[r];
-        mrow[r] = __builtin_elementwise_max(__builtin_elementwise_max(m, __builtin_bit_cast(u16x2_t, ml)),
-                                            __builtin_bit_cast(u16x2_t, mh));
-      }
-      cl = rg_bf16x2_to_f16x2(ml, lo, esub[r]);
-      ch = rg_bf16x2_to_f16x2(mh, hi, esub[r]);
-    }
-    const uint32_t o0 = __builtin_amdgcn_perm(ch, cl, 0x05040100u);  // (x0, x2) / (x4, x6)
-    const uint32_t o1 = __builtin_amdgcn_perm(ch, cl, 0x07060302u);  // (x1, x3) / (x5, x7)
-    if constexpr (h == 0) {
-      ostage[0] = o0;
-      ostage[1] = o1;
-    } else {
-      const int n = ns + 64 * r;
-      rg_lds[nx * kBufUnits + rg_unit(n, 2 * (gs & 1) + (k & 1), 2 * (k >> 1) + (gs >> 1))] =
-          make_uint4(ostage[0], ostage[1], o0, o1);
-    }
-  };
-  auto check = [&](auto r_c) {
-    constexpr int r = decltype(r_c)::value;
-    const int eb = rg_eb(mrow[r]);
-    // values below 2^(eb + 15) stay below 65504 after scaling by 2^-e iff eb <= e + 1
-    ovf |= eb > e_fix[r] + 1 ? 1u : 0u;
-    e_max[r] = max(e_max[r], eb);
-  };
-  // The staging chunks of a half: 8 RS stores (tracking the maxima), then RS
-  // checks.
-  constexpr int kChunks = 8 * RS + (F16X ? 0 : RS);
+  // Staging chunk c of a half: piece k of row r (columns 32 k + 8 gs of the
+  // half: step t = 2 (gs & 1) + (k & 1), k-group g = 2 (k >> 1) + (gs >> 1)).
+  constexpr int kChunks = 4 * RS;
   auto chunk = [&](auto c_c, auto xs_c, auto nx_c) {
-    constexpr int c = decltype(c_c)::value;
-    if constexpr (c < 8 * RS)
-      store(xs_c, nx_c, IC<c / 8>{}, IC<(c % 8) / 2>{}, IC<c % 2>{}, true);
-    else
-      check(IC<c - 8 * RS>{});
+    constexpr int c = decltype(c_c)::value, xsl = decltype(xs_c)::value, nx = decltype(nx_c)::value;
+    constexpr int r = c / 4, k = c % 4;
+    const int n = ns + 64 * r;
+    rg_lds[nx * kBufUnits + rg_unit(n, 2 * (gs & 1) + (k & 1), 2 * (k >> 1) + (gs >> 1))] = xr[xsl][r][k];
   };
 
   f32x4_t acc[T][NB];
@@ -338,13 +332,15 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
   // the last step the last tile forms no next A operand and every slot
   // stages.  Staging slots per step: T (NB - 4), plus 4 in the last step.
   constexpr int QG = NB / 4;
-  // The products of step t of a half, in a fixed order: each product is
-  // followed by a little VALU work, so that the matrix core runs while the
-  // VALU works, with no scheduling heuristics involved.  a_cur holds tile
-  // 0's A operand and leaves with the next step's; bb holds the B operands,
-  // and behind the last tile's product j the next step's operand j is read
-  // into the register that product has finished with.  stage(c) runs staging
-  // slot c of the step.
+  // The products of step t of a half, in a fixed order of groups of four:
+  // each product is written with a little VALU work behind it, and the
+  // compiler interleaves the instructions within a group of four products
+  // (fences between groups; one fence per product kept every dependent
+  // VALU chain in line with its product and was 7 % slower).  a_cur holds
+  // tile 0's A operand and leaves with the next step's; bb holds the B
+  // operands, and behind the last tile's product j the next step's operand
+  // j is read into the register that product has finished with.  stage(c)
+  // runs staging slot c of the step.
   auto mstep = [&](auto cpar_c, auto par_c, auto t_c, h8_t(&bb)[NB], h8_t& a_cur, auto&& stage) {
     constexpr int t = decltype(t_c)::value;
     constexpr int tn = t < 3 ? t + 1 : 3;
@@ -356,7 +352,6 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
         constexpr int j = decltype(j_c)::value;
         acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a_cur, bb[j], acc[i][j], 0, 0, 0);
         if constexpr (i + 1 == T && t < 3) bb[j] = read_b(par_c, IC<tn>{}, j);
-        rg_fence();
         if constexpr (j % QG == 0 && next_a) {
           if constexpr (i + 1 < T)
             wq[j / QG] = dq_pair(cpar_c, par_c, t_c, IC<i + 1>{}, IC<j / QG>{});
@@ -365,9 +360,10 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
         } else {
           stage(IC<i*(NB - 4) + (next_a ? (j / QG) * (QG - 1) + (j % QG) - 1 : j)>{});
         }
-        rg_fence();
+        if constexpr (j % 4 == 3) rg_fence();
       });
       if constexpr (next_a) a_cur = pack_a(wq);
+      rg_fence();
     });
   };
 
@@ -389,10 +385,10 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
       rg_static_for<4>([&](auto q_c) { wq[decltype(q_c)::value] = dq_pair(cpar_c, par_c, IC<0>{}, IC<0>{}, q_c); });
       a_cur = pack_a(wq);
     }
-    // The next half's staging (ring slot xs, LDS buffer par ^ 1) in the
+    // The next half's staging (ring slot xsl, LDS buffer par ^ 1) in the
     // slots of steps t0..3: every step when its activations were loaded two
     // halves ahead, the last two when one half ahead.
-    constexpr int nx = par ^ 1, xs = XD == 2 ? nx : 0, t0 = XD == 2 ? 0 : 2;
+    constexpr int nx = par ^ 1, xsl = XD == 2 ? nx : 0, t0 = XD == 2 ? 0 : 2;
     constexpr int per_step = T * (NB - 4);
     constexpr int slots = (3 - t0) * per_step + per_step + 4;
     constexpr int cps = (kChunks + slots - 1) / slots;  // chunks per slot
@@ -404,7 +400,7 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
           constexpr int slot = (t - t0) * per_step + c;
           rg_static_for<cps>([&](auto k_c) {
             constexpr int ch = slot * cps + decltype(k_c)::value;
-            if constexpr (ch < kChunks) chunk(IC<ch>{}, IC<xs>{}, IC<nx>{});
+            if constexpr (ch < kChunks) chunk(IC<ch>{}, IC<xsl>{}, IC<nx>{});
           });
         }
       };
@@ -427,92 +423,38 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
     half(2 * b + 1, cpar_c, IC<1>{});
   };
 
-  for (;; ++pass) {
-    // (the address bases pass through an empty asm: otherwise their derived
-    // addresses are computed once before this loop and all held live through
-    // the block loop)
 #pragma unroll
-    for (int i = 0; i < T; ++i) __asm__ volatile("" : "+v"(bidx[i]));
+  for (int i = 0; i < T; ++i)
 #pragma unroll
-    for (int s = 0; s < RS; ++s) __asm__ volatile("" : "+v"(xoff[s]));
-#pragma unroll
-    for (int t = 0; t < 4; ++t) __asm__ volatile("" : "+v"(bofs[t]));
-#pragma unroll
-    for (int i = 0; i < T; ++i)
-#pragma unroll
-      for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    // Prologue: block 0's codes and header, the first halves of X in flight,
-    // half 0 staged (on the first pass its maxima set the row scales first).
-    load_header(0);
-    load_codes(0, IC<0>{}, IC<0>{});
-    if constexpr (CD == 2) load_codes(0, IC<0>{}, IC<1>{});
-    load_x(0, IC<0>{});
-    if constexpr (XD == 2) load_x(1, IC<1>{});
-    if constexpr (!F16X) {
-      if (pass == 0) {
-        rg_static_for<RS>([&](auto r_c) {
-          constexpr int r = decltype(r_c)::value;
-          u16x2_t m2 = {0, 0};
-#pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const uint4 v = xr[0][r][k];
-            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu));
-            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
-            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu));
-            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
-          }
-          const int eb = rg_eb(m2);
-          e_max[r] = eb;
-          set_scale(r, eb + kRgHeadroom);
-        });
-      }
-    }
-    rg_static_for<8 * RS>([&](auto c_c) {
-      constexpr int c = decltype(c_c)::value;
-      store(IC<0>{}, IC<0>{}, IC<c / 8>{}, IC<(c % 8) / 2>{}, IC<c % 2>{}, false);
-    });
-    lds_barrier();
-    // The last half stages a half past the end (clamped loads of the last
-    // half, never multiplied; its maximum is the last half's again).
-    int b = 0;
+    for (int j = 0; j < NB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // Prologue: the first block's codes and header, the first halves of X in
+  // flight, the first half staged.
+  load_header(kb0);
+  load_codes(kb0, IC<0>{}, IC<0>{});
+  if constexpr (CD == 2) load_codes(kb0, IC<0>{}, IC<1>{});
+  load_x(2 * kb0, IC<0>{});
+  if constexpr (XD == 2) load_x(2 * kb0 + 1, IC<1>{});
+  rg_static_for<kChunks>([&](auto c_c) { chunk(c_c, IC<0>{}, IC<0>{}); });
+  lds_barrier();
+  // The last half stages a half past the slice (loads clamped to the last
+  // half of K, never multiplied).
+  int b = kb0;
 #pragma unroll 1
-    for (; b + 2 <= nb; b += 2) {
-      block(b, IC<0>{});
-      block(b + 1, IC<1>{});
-    }
-    if (b < nb) block(b, IC<0>{});
-    if constexpr (F16X) {
-      break;
-    } else {
-      // a second pass only if some row of the workgroup would have overflowed
-      if (lane == 0) ovf_lds[wave] = __builtin_amdgcn_ballot_w64(ovf != 0) != 0 ? 1 : 0;
-      lds_barrier();
-      const bool again = pass == 0 && (ovf_lds[0] | ovf_lds[1] | ovf_lds[2] | ovf_lds[3]) != 0;
-      lds_barrier();
-      if (!again) break;
-#pragma unroll
-      for (int s = 0; s < RS; ++s) set_scale(s, e_max[s]);
-      ovf = 0;
-    }
+  for (; b + 2 <= kb1; b += 2) {
+    block(b, IC<0>{});
+    block(b + 1, IC<1>{});
   }
+  if (b < kb1) block(b, IC<0>{});
 
-  if constexpr (!F16X) {
-    if (gs == 0) {
-#pragma unroll
-      for (int s = 0; s < RS; ++s) fin_lds[ns + 64 * s] = __builtin_amdgcn_ldexpf(1.f, e_fix[s]);
-    }
-    lds_barrier();
-  }
   // Lane (g, r16) holds outputs n .. n + 3 (n = 16 i + 4 g) of activation
   // row 16 j + r16: one 16-byte store when the row length keeps it aligned
   // (scattered 4-byte stores cost about a fifth of the kernel at five tiles).
   const bool row4 = (N & 3) == 0;
 #pragma unroll
   for (int j = 0; j < NB; ++j) {
-    const int mr = 16 * j + r16;
-    const int m = m0 + mr;
-    const float fs = F16X ? 1.f : fin_lds[mr];
+    const int m = m0 + 16 * j + r16;
     if (m < M) {
+      const float fs = xs[m];
       float* yr = y + static_cast<size_t>(m) * N;
 #pragma unroll
       for (int i = 0; i < T; ++i) {
@@ -530,6 +472,26 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
   }
 }
 
+// y[e] = the sum over s < S of part[s zs + e] in order of s, for e < n
+// (zs a multiple of 4; part and y 16-byte aligned).
+__global__ void __launch_bounds__(256) dqreg_sum(const float* part, int S, size_t zs, size_t n, float* y) {
+  const size_t n4 = n / 4, z4 = zs / 4;
+  const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part);
+  f32x4_t* o = reinterpret_cast<f32x4_t*>(y);
+  const size_t i0 = blockIdx.x * static_cast<size_t>(blockDim.x) + threadIdx.x;
+  const size_t step = static_cast<size_t>(gridDim.x) * blockDim.x;
+  for (size_t i = i0; i < n4; i += step) {
+    f32x4_t v = p[i];
+    for (int s = 1; s < S; ++s) v += p[s * z4 + i];
+    o[i] = v;
+  }
+  for (size_t e = 4 * n4 + i0; e < n; e += step) {
+    float v = part[e];
+    for (int s = 1; s < S; ++s) v += part[s * zs + e];
+    y[e] = v;
+  }
+}
+
 namespace {
 
 // Prefetch distances: activations and codes two half blocks ahead up to
@@ -537,87 +499,151 @@ namespace {
 // cover the loads, and the registers of a second half in flight cost more
 // than they save (measured at four tiles: 202 against 184 us on the 7B FFN
 // gate at 512 rows).
-#ifndef QMV_DQREG_XD
-#define QMV_DQREG_XD(T, NB) ((T) >= 3 || (NB) > 8 ? 1 : 2)
-#endif
-#ifndef QMV_DQREG_CD
-#define QMV_DQREG_CD(T, NB) ((T) >= 3 || (NB) > 8 ? 1 : 2)
-#endif
+constexpr int rg_xd(int t) { return t >= 3 ? 1 : 2; }
+
+size_t rg_align(size_t v) { return (v + 255) / 256 * 256; }
+// Floats from one slice's partial outputs to the next: 256-byte aligned.
+size_t rg_slice_floats(int64_t rows, int64_t batch) { return rg_align(static_cast<size_t>(rows) * batch * 4) / 4; }
 
 template <int T, int NB>
-hipError_t launch_dqreg(const qmv_weights& W, const uint16_t* x, bool f16x, float* y, int M, hipStream_t stream) {
-  constexpr int XD = QMV_DQREG_XD(T, NB), CD = QMV_DQREG_CD(T, NB);
+hipError_t launch_dqreg(const qmv_weights& W, const uint16_t* x16, const float* xs, float* out, size_t zs, int M,
+                        int splits, int bps, hipStream_t stream) {
+  constexpr int D = rg_xd(T);
   const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols);
   const uint8_t* w = static_cast<const uint8_t*>(W.data);
   const uint32_t pa = static_cast<uint32_t>(W.scales_offset);
-  const dim3 grid((N + 64 * T - 1) / (64 * T), (M + rg_batch(NB) - 1) / rg_batch(NB));
+  const dim3 grid((N + 64 * T - 1) / (64 * T), (M + rg_batch(NB) - 1) / rg_batch(NB), splits);
   const size_t lds = rg_lds_bytes(NB);
-  const bool pl = W.layout == QMV_LAYOUT_PLANES;
-  if (pl && f16x)
-    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, XD, CD, true, true>), grid, dim3(kRgThreads), lds, stream, w, pa, N, K,
-                       x, y, M);
-  else if (pl)
-    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, XD, CD, true, false>), grid, dim3(kRgThreads), lds, stream, w, pa, N,
-                       K, x, y, M);
-  else if (f16x)
-    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, XD, CD, false, true>), grid, dim3(kRgThreads), lds, stream, w, pa, N,
-                       K, x, y, M);
+  if (W.layout == QMV_LAYOUT_PLANES)
+    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, D, D, true>), grid, dim3(kRgThreads), lds, stream, w, pa, N, K, x16,
+                       xs, out, zs, M, bps);
   else
-    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, XD, CD, false, false>), grid, dim3(kRgThreads), lds, stream, w, pa, N,
-                       K, x, y, M);
+    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, D, D, false>), grid, dim3(kRgThreads), lds, stream, w, pa, N, K, x16,
+                       xs, out, zs, M, bps);
   return hipGetLastError();
 }
 
-// The (tiles per wave, B tiles) forms built, and the modelled time of one:
-// workgroup rounds over the compute units times the issue time of a
-// workgroup, from the probe: about 18 cycles per product while the VALU work
-// per product stays within two instructions, about 4.5 cycles per further
-// instruction.
-struct DqregForm {
-  int t, nb;
-};
-constexpr DqregForm kDqregForms[] = {{1, 8}, {2, 8}, {3, 8}, {4, 8}, {5, 8}};
-constexpr int kDqregFormCount = static_cast<int>(sizeof(kDqregForms) / sizeof(kDqregForms[0]));
+template <int NB>
+hipError_t launch_dqreg_t(int t, const qmv_weights& W, const uint16_t* x16, const float* xs, float* out, size_t zs,
+                          int M, int splits, int bps, hipStream_t stream) {
+  switch (t) {
+    case 1: return launch_dqreg<1, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
+    case 2: return launch_dqreg<2, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
+    case 3: return launch_dqreg<3, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
+    case 4: return launch_dqreg<4, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
+    default: return launch_dqreg<5, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
+  }
+}
 
-double dqreg_cost(int64_t rows, int64_t batch, int64_t cus, DqregForm f) {
-  const int64_t wgs = (rows + 64 * f.t - 1) / (64 * f.t) * ((batch + rg_batch(f.nb) - 1) / rg_batch(f.nb));
-  const double valu_per_product = 16.0 / (2 * f.nb) + 6.0 / f.t + 0.4;
-  const double per_product = valu_per_product <= 2 ? 18.0 : 18.0 + 4.5 * (valu_per_product - 2);
-  return static_cast<double>((wgs + cus - 1) / cus) * f.t * f.nb * per_product;
+// Modelled time (us) of one launch: workgroup rounds over the compute units
+// times a workgroup's time, (14 + 17 / T) ns per product of a wave at
+// NB = 8 and (20 + 16 / T) ns at NB = 4 (where each A operand serves four
+// products), plus 5.5 us of prologue and epilogue; with several slices, the
+// sum kernel, 3 us plus the partial outputs read and y written once at
+// 8 TB/s.  Fitted to kernel traces of the 7B layer's matrices at 128 to 512
+// rows (T = 1..5, 2 to 74 blocks per slice: within 10 %).
+double dqreg_cost(int64_t rows, int64_t batch, int64_t cus, int t, int nbt, int splits, int bps) {
+  const int64_t wgs = (rows + 64 * t - 1) / (64 * t) * ((batch + rg_batch(nbt) - 1) / rg_batch(nbt)) * splits;
+  const double products = static_cast<double>(bps) * 8 * nbt * t;
+  const double per = nbt == 4 ? 20.0 + 16.0 / t : 14.0 + 17.0 / t;
+  double us = static_cast<double>((wgs + cus - 1) / cus) * (products * per * 1e-3 + 5.5);
+  if (splits > 1) us += 3.0 + static_cast<double>(splits + 1) * rows * batch * 4 / 8e6;
+  return us;
 }
 
 }  // namespace
 
-int dqreg_form(int64_t rows, int64_t batch) {
-  const int64_t cus = device_cus();
-  int best = 0;
-  for (int k = 1; k < kDqregFormCount; ++k)
-    if (dqreg_cost(rows, batch, cus, kDqregForms[k]) < dqreg_cost(rows, batch, cus, kDqregForms[best])) best = k;
-  return best;
-}
-
-bool gemm_q4_k_dqreg_fits(const qmv_weights& W, int64_t batch) {
+bool dqreg_route(const qmv_weights& W, int64_t batch) {
+  if (W.fmt != QMV_Q4_K || W.rows < kDqMinRows) return false;
+  if (batch < kDqMinBatch && !(batch >= kDqMinBatchLongK && W.cols >= kDqLongK)) return false;
   const uint64_t wbytes = W.layout == QMV_LAYOUT_PLANES ? 5 * W.scales_offset + 64 * (W.rows * (W.cols / 256))
                                                         : 144 * static_cast<uint64_t>(W.rows) * (W.cols / 256);
   return wbytes < (1ull << 32) && 2 * static_cast<uint64_t>(batch) * W.cols < (1ull << 32);
 }
 
-hipError_t gemm_q4_k_dqreg(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
-                           hipStream_t stream) {
-  const uint16_t* xh = static_cast<const uint16_t*>(x);
-  const int M = static_cast<int>(batch);
-#ifdef QMV_DQREG_FORM
-  const int form = QMV_DQREG_FORM;
-#else
-  const int form = dqreg_form(W.rows, batch);
-#endif
-  switch (form) {
-    case 0: return launch_dqreg<1, 8>(W, xh, f16x, y, M, stream);
-    case 1: return launch_dqreg<2, 8>(W, xh, f16x, y, M, stream);
-    case 2: return launch_dqreg<3, 8>(W, xh, f16x, y, M, stream);
-    case 3: return launch_dqreg<4, 8>(W, xh, f16x, y, M, stream);
-    default: return launch_dqreg<5, 8>(W, xh, f16x, y, M, stream);
+DqregPlan dqreg_plan(int64_t rows, int64_t cols, int64_t batch) {
+  const int64_t cus = device_cus();
+  const int nb = static_cast<int>(cols / 256);
+  DqregPlan best{1, 8, 1, nb};
+  double best_us = -1;
+  for (int nbt : {8, 4})
+    for (int t = 1; t <= 5; ++t)
+      for (int s = 1; s <= kDqregMaxSplits && s <= nb; ++s) {
+        const int bps = (nb + s - 1) / s;
+        const int splits = (nb + bps - 1) / bps;  // every slice holds at least one block
+        if (splits != s) continue;
+        const double us = dqreg_cost(rows, batch, cus, t, nbt, splits, bps);
+        if (best_us < 0 || us < best_us) {
+          best = DqregPlan{t, nbt, splits, bps};
+          best_us = us;
+        }
+      }
+  return best;
+}
+
+size_t dqreg_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, const DqregPlan& p) {
+  size_t b = rg_align(static_cast<size_t>(batch) * cols * 2) + rg_align(static_cast<size_t>(batch) * 4);
+  if (p.splits > 1) b += static_cast<size_t>(p.splits) * rg_slice_floats(rows, batch) * 4;
+  return b;
+}
+
+hipError_t gemm_q4_k_dqreg_ws(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
+                              const DqregPlan& p, void* ws, bool convert, hipStream_t stream) {
+  const int M = static_cast<int>(batch), N = static_cast<int>(W.rows), K = static_cast<int>(W.cols);
+  uint8_t* base = static_cast<uint8_t*>(ws);
+  uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
+  float* xs = reinterpret_cast<float*>(base + rg_align(static_cast<size_t>(M) * K * 2));
+  float* part = reinterpret_cast<float*>(base + rg_align(static_cast<size_t>(M) * K * 2) +
+                                         rg_align(static_cast<size_t>(M) * 4));
+  hipError_t e = hipSuccess;
+  if (convert) {
+    if (f16x)
+      hipLaunchKernelGGL((act_rows_f16<false>), dim3(M), dim3(256), 0, stream, static_cast<const uint16_t*>(x), K,
+                         x16, xs);
+    else
+      hipLaunchKernelGGL((act_rows_f16<true>), dim3(M), dim3(256), 0, stream, static_cast<const uint16_t*>(x), K, x16,
+                         xs);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
+  float* out = p.splits > 1 ? part : y;
+  const size_t zs = rg_slice_floats(N, M);
+  e = p.nb == 4 ? launch_dqreg_t<4>(p.t, W, x16, xs, out, zs, M, p.splits, p.bps, stream)
+                : launch_dqreg_t<8>(p.t, W, x16, xs, out, zs, M, p.splits, p.bps, stream);
+  if (e != hipSuccess || p.splits == 1) return e;
+  const size_t n = static_cast<size_t>(M) * N;
+  const int blocks = static_cast<int>(std::min<size_t>((n / 4 + 255) / 256 + 1, 4096));
+  hipLaunchKernelGGL(dqreg_sum, dim3(blocks), dim3(256), 0, stream, part, p.splits, zs, n, y);
+  return hipGetLastError();
+}
+
+hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t stream) {
+  DqregPlan plans[kMaxItems];
+  bool reg[kMaxItems];
+  size_t bytes = 0;
+  for (int i = 0; i < n; ++i) {
+    reg[i] = dqreg_route(*calls[i].W, batch);
+    if (!reg[i]) continue;
+    plans[i] = dqreg_plan(calls[i].W->rows, calls[i].W->cols, batch);
+    bytes = std::max(bytes, dqreg_workspace_bytes(calls[i].W->rows, calls[i].W->cols, batch, plans[i]));
+  }
+  void* ws = nullptr;
+  if (bytes) {
+    const hipError_t e = workspace(stream, bytes, &ws);
+    if (e != hipSuccess) return e;
+  }
+  hipError_t e = hipSuccess;
+  for (int i = 0; i < n && e == hipSuccess; ++i) {
+    const GemvCall& c = calls[i];
+    if (reg[i]) {
+      // the previous call left these activations converted in the workspace
+      const bool same = i > 0 && reg[i - 1] && calls[i - 1].x == c.x && calls[i - 1].W->cols == c.W->cols;
+      e = gemm_q4_k_dqreg_ws(*c.W, c.x, f16x, c.y, batch, plans[i], ws, !same, stream);
+    } else {
+      e = f16x ? gemm_q4_k_f16(*c.W, c.x, c.y, batch, stream) : gemm_q4_k_bf16(*c.W, c.x, c.y, batch, stream);
+    }
+  }
+  return e;
 }
 
 }  // namespace qmv

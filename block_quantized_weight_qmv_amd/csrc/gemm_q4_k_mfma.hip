@@ -890,7 +890,6 @@ static hipError_t gemm_q4_k_bf16_layout(const qmv_weights& W, const void* x, flo
     return hipGetLastError();
   }
   if (M <= 16) return launch_ksplit<PL, false>(w, pa, N, K, xb, y, M, stream);
-  if (M >= kDqMinBatch && N >= kDqMinRows) return gemm_q4_k_dq(W, x, false, y, batch, stream);
   return launch_tile<PL, false>(w, pa, N, K, xb, y, M, stream);
 }
 
@@ -904,7 +903,6 @@ hipError_t gemm_q4_k_f16(const qmv_weights& W, const void* x, float* y, int64_t 
   if (!gemm_q4_k_f16_fits(W.cols, batch)) return hipErrorInvalidValue;
   const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols);
   const uint8_t* w = static_cast<const uint8_t*>(W.data);
-  if (batch >= kDqMinBatch && W.rows >= kDqMinRows) return gemm_q4_k_dq(W, x, true, y, batch, stream);
   if (batch >= 17) {
     const uint16_t* xh = static_cast<const uint16_t*>(x);
     return W.layout == QMV_LAYOUT_PLANES

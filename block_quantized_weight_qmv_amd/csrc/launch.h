@@ -76,33 +76,46 @@ hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t bat
 constexpr int64_t kMfmaMinBatch = QMV_MFMA_MIN_BATCH;
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t s);
-// Batches of at least kDqMinBatch rows (bf16 or fp16 activations) against
-// matrices of at least kDqMinRows rows: the dequantized-tile kernels
-// (gemm_q4_k_dq.hip, which hands shapes whose grid would not fill one round
-// well to gemm_q4_k_dqreg.hip), entered from the launchers of
-// gemm_q4_k_mfma.hip.  They round each weight to fp16 (relative error near
-// 2^-11), which the normwise bound absorbs over a matrix of a few hundred
-// rows (about 4e-4 on the 7B FFN shapes) but not over a handful of rows,
-// where one output's cancellation sets the error; smaller matrices keep the
-// exact-product kernels.  Measured against the 64-row tile kernel on the 7B
-// FFN shapes (bf16): 18944 x 3584 at 128 rows 65 against 47 us, at 192-256
-// rows 86-87 against 90 us, at 512 rows 111 against 171 us; 3584 x 18944 at
-// 128 rows 209 against 169 us, at 192 rows 207 against 333 us.
-#ifndef QMV_DQ_MIN_BATCH
-#define QMV_DQ_MIN_BATCH 192
-#endif
-constexpr int64_t kDqMinBatch = QMV_DQ_MIN_BATCH;
-constexpr int64_t kDqMinRows = 256;
-// Tile of gemm_q4_k_dq: weight rows x activation rows per workgroup.
-constexpr int64_t kDqTileRows = 256, kDqTileBatch = 128;
-hipError_t gemm_q4_k_dq(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
-                        hipStream_t s);
-// The register-dequantized kernel (gemm_q4_k_dqreg.hip): tile shape chosen
-// by dqreg_form; byte offsets must fit in 32 bits.
-bool gemm_q4_k_dqreg_fits(const qmv_weights& W, int64_t batch);
-int dqreg_form(int64_t rows, int64_t batch);
-hipError_t gemm_q4_k_dqreg(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
-                           hipStream_t s);
+// Q4_K x bf16/fp16 batches from kDqMinBatch rows, or from kDqMinBatchLongK
+// rows against matrices of at least kDqLongK columns, against matrices of at
+// least kDqMinRows rows whose byte offsets fit in 32 bits: the
+// register-dequantized kernels (gemm_q4_k_dqreg.hip; dqreg_route).  They
+// round each weight to fp16 (relative error near 2^-11), which the normwise
+// bound absorbs over a matrix of a few hundred rows (about 4e-4 on the 7B
+// FFN shapes) but not over a handful of rows, where one output's
+// cancellation sets the error; smaller matrices keep the exact-product
+// kernels.  Measured against the tile kernels on the 7B FFN shapes (bf16,
+// graph replays): 18944 x 3584 at 64 rows 26 (tile) against 39 us, at 128
+// rows 47 against 45 us; 3584 x 18944 at 64 rows 75 against 63 us, at 128
+// rows 169 against 66 us.
+constexpr int64_t kDqMinBatch = 128, kDqMinBatchLongK = 64, kDqLongK = 8192, kDqMinRows = 256;
+// The activations converted once into a workspace, T 16-row tiles per wave
+// against NB 16-row activation tiles per workgroup, K in `splits` slices of
+// `bps` blocks (partial outputs summed in slice order).
+struct DqregPlan {
+  int t, nb, splits, bps;
+};
+constexpr int kDqregMaxSplits = 8;
+bool dqreg_route(const qmv_weights& W, int64_t batch);
+DqregPlan dqreg_plan(int64_t rows, int64_t cols, int64_t batch);
+size_t dqreg_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, const DqregPlan& p);
+// With the caller's workspace ws (dqreg_workspace_bytes, 256-byte aligned);
+// convert = false reuses the converted activations a previous call on the
+// same stream left in ws (same x, batch and cols).
+hipError_t gemm_q4_k_dqreg_ws(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
+                              const DqregPlan& p, void* ws, bool convert, hipStream_t s);
+// The matrix-core calls of one launch (Q4_K, bf16 or fp16 rows, batch >= 2)
+// in order: each on the register-dequantized kernels when dqreg_route says
+// so (with the workspace of stream s, sized for the largest; consecutive
+// calls on the same activations convert them once), else on the kernels of
+// gemm_q4_k_bf16 / gemm_q4_k_f16.
+hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t s);
+// Device workspace for stream s on the current device: at least `bytes`,
+// 256-byte aligned, one per (device, stream), kept until the process ends.
+// Growing it (hipMalloc of a new one; the old one stays allocated, so
+// graphs captured with it stay valid) is refused while s is capturing
+// (hipErrorStreamCaptureUnsupported).
+hipError_t workspace(hipStream_t s, size_t bytes, void** out);
 // Q4_K x fp16 on the matrix cores with fp16 operands: the kernels of the
 // bf16 path (streaming or K-split up to 16 rows, tiles from 17).  qmv_gemv
 // takes it from kMfmaMinF16Batch rows; below, the multi-row GEMV is faster.

@@ -212,7 +212,8 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * fmt, rows and cols must repeat the descriptor's (QMV_ERR_FORMAT otherwise),
  * x is [batch][cols] of x_dtype (QMV_F32, QMV_F16 or QMV_BF16), y is
  * [batch][rows] fp32; x and y device pointers, 16-byte aligned.  Enqueues on
- * `stream` and returns; legal inside HIP stream capture.  batch >= 2 rows
+ * `stream` and returns; legal inside HIP stream capture (see the workspace
+ * of the register-dequantized kernels below).  batch >= 2 rows
  * (Q4_K x bf16: 2..4 rows) run the multi-row GEMV in every format: weights
  * read once per two or four activation rows (fp32: two) for cols <= 4096
  * (Q8_0: 2048), and, for fp16/bf16 rows, once per two rows up to eight times
@@ -221,14 +222,23 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * runs on the matrix cores with fp16 operands (exact products, fp32 sums).  Other Q4_K x bf16 calls with batch >= 2 run the
  * matrix-core path (weights read once for up to 16 activation rows, once per
  * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
- * independent of timing).  From 192 activation rows against at least 256
- * weight rows, Q4_K x bf16/fp16 runs one of two dequantized-fp16 kernels
- * instead (weight tiles shared in LDS when that grid fills half to all of
- * the compute units in one round, else per-wave fragments in registers):
- * each weight is rounded to fp16 (relative error near 2^-11) and each bf16
- * activation row is scaled by a power of two into fp16, so the products are
- * no longer exact; the normwise bound still holds over such matrices (about
- * 4e-4 on the 7B FFN shapes).  Results stay independent of timing.  Otherwise each activation row is a GEMV over the
+ * independent of timing).  From 128 activation rows (from 64 against
+ * matrices of 8192 columns and more) against at least 256 weight rows,
+ * Q4_K x bf16/fp16 runs the register-dequantized kernels instead: the
+ * activations are converted once to fp16 (a bf16 row scaled by the power of
+ * two that brings its largest |x| into [2^14, 2^15)), each weight is rounded
+ * to fp16 (relative error near 2^-11), so the products are no longer exact;
+ * the normwise bound still holds over such matrices (about 4e-4 on the 7B
+ * FFN shapes).  K may be cut into slices whose partial outputs are summed in
+ * a fixed order, so results stay independent of timing.  These kernels use
+ * a device workspace per (device, stream) that the library allocates
+ * (hipMalloc) on the first call that needs it, or a larger one, and keeps
+ * until the process ends (a grown-out one included, so graphs captured with
+ * it stay valid); the converted activations and partial outputs go there.
+ * Under stream capture it cannot be allocated: such a call fails with
+ * QMV_ERR_HIP unless the same or a larger call ran on that stream before
+ * the capture.  Graphs captured on one stream share its workspace: replay
+ * them in order on one stream.  Otherwise each activation row is a GEMV over the
  * packed weights.  Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the
  * same arithmetic, in the same order, as the canonical layout on every one
  * of these paths, so results equal bit for bit. */

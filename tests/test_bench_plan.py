@@ -59,7 +59,7 @@ def _library_kernels():
                 or "qmv::gemv_lx_kernel<" in line
                 or "qmv::gemm_q4_k_bf16_" in line or "qmv::gemm_q4_k_stream<" in line
                 or "qmv::gemm_q4_k_tile<" in line or "qmv::gemm_q4_k_ksplit<" in line
-                or "qmv::gemm_q4_k_dqtile<" in line or "qmv::gemm_q4_k_dqreg<" in line):
+                or "qmv::act_rows_f16<" in line or "qmv::gemm_q4_k_dqreg<" in line or "qmv::dqreg_sum" in line):
             sym = line.split(" ", 2)[2]
             sym = sym[5:] if sym.startswith("void ") else sym
             names.add(sym.split("(")[0])
@@ -155,19 +155,18 @@ def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
                                           (16, "qmv::gemm_q4_k_stream<false, true>"),
                                           (17, "qmv::gemm_q4_k_tile<1, 1, 2, 5, false, true>"),
                                           (64, "qmv::gemm_q4_k_tile<1, 2, 2, 5, false, true>"),
-                                          (128, "qmv::gemm_q4_k_tile<1, 4, 2, 5, false, true>"),
-                                          (256, "qmv::gemm_q4_k_dqtile<false, true>"),
-                                          (512, "qmv::gemm_q4_k_dqreg<5, 8, 1, 1, false, true>")])
+                                          (100, "qmv::gemm_q4_k_tile<1, 4, 2, 5, false, true>"),
+                                          (128, "qmv::gemm_q4_k_dqreg<"),
+                                          (512, "qmv::gemm_q4_k_dqreg<")])
 def test_q4_k_f16_batches_name_the_f16_matrix_core_kernels(batch, kernel):
-    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (from 192
-    # rows, a dequantized-tile kernel: 18944 rows in 256 x 128 tiles fill one
-    # round at 256 rows, not at 512)
+    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (from 128
+    # rows the register-dequantized kernels, in the form the plan picks)
     names = _library_kernels()
     layout = bench.default_layout(5, batch, "f16")
     assert layout == "blocks"
     plan = bench.workload_plan(5, batch, separate=False, layout=layout, x_dtype="f16")
-    assert plan["kname"] == [kernel]
-    assert kernel in names
+    assert len(plan["kname"]) == 1 and plan["kname"][0].startswith(kernel)
+    assert all(d[2] in names for d in plan["dispatches"]), plan["dispatches"]
 
 
 @pytest.mark.parametrize("config,batch,kernel", [(3, 8, "qmv::gemm_q4_k_ksplit<1, 1, false, true>"),
@@ -191,15 +190,24 @@ def test_small_multi_matrix_batches_name_the_rows_kernel(x_dtype, batch):
     assert o.startswith("qmv::gemm_q4_k_"), o
 
 
-@pytest.mark.parametrize("rows,batch,form", [(18944, 512, 5), (3584, 512, 1), (3584, 192, 1), (18944, 640, 3),
-                                             (300, 400, 1), (4096, 1024, 2)])
-def test_dqreg_form(rows, batch, form):
-    # the tile height the launcher's model picks (mirrored here for naming)
-    assert bench.dqreg_form(rows, batch) == form
+@pytest.mark.parametrize("rows,cols,batch", [(18944, 3584, 512), (3584, 18944, 512), (3584, 3584, 512),
+                                             (512, 3584, 512), (18944, 3584, 128), (3584, 18944, 64),
+                                             (300, 768, 400), (4100, 512, 1000), (30001, 256, 500)])
+def test_dqreg_plan_is_well_formed(rows, cols, batch):
+    # the launcher's model (mirrored here for naming): a built form, slices
+    # that cover K with at least one block each
+    t, nbt, splits, bps = bench.dqreg_plan(rows, cols, batch)
+    nb = cols // 256
+    assert 1 <= t <= 5 and nbt in (4, 8) and 1 <= splits <= 8
+    assert (splits - 1) * bps < nb <= splits * bps
+    assert splits == -(-nb // bps)
 
 
-@pytest.mark.parametrize("rows,batch,kind", [(18944, 192, "dqtile"), (18944, 384, "dqtile"), (18944, 512, "dqreg"),
-                                             (3584, 512, "dqreg"), (300, 400, "dqreg"), (32768, 256, "dqtile")])
-def test_dq_kernel_choice(rows, batch, kind):
-    # the 256 x 128 tile kernel while its grid fills half to all of 256 CUs in one round
-    assert bench.dq_kernel_name(rows, batch, "blocks", "bf16").startswith(f"qmv::gemm_q4_k_{kind}<")
+@pytest.mark.parametrize("rows,cols,batch,route", [(18944, 3584, 64, False), (3584, 18944, 64, True),
+                                                   (18944, 3584, 128, True), (300, 768, 400, True),
+                                                   (255, 3584, 512, False), (3584, 18944, 32, False),
+                                                   (3584, 8192, 64, True), (3584, 7936, 64, False)])
+def test_dq_route(rows, cols, batch, route):
+    # from 128 rows, or from 64 against matrices of 8192 columns and more,
+    # against matrices of 256 rows and more
+    assert bench.dq_route(rows, cols, batch, "blocks") == route

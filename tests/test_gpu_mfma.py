@@ -1,8 +1,9 @@
 """Batched Q4_K x bf16 on the matrix-core path, and Q4_K x fp16 on its
 streaming kernel (5-16 rows with X in LDS) and tile kernels (17 rows up);
-from 192 rows against 256 weight rows and more, the two kernels on fp16
-weights dequantized on the chip (tiles shared in LDS, or per-wave fragments
-in registers, each in every tile form the launcher picks).
+from 128 rows (64 against 8192 columns and more) against 256 weight rows
+and more, the register-dequantized kernels (fp16 weight fragments formed per
+wave, activations converted once; every form the launcher picks, with K
+whole or in slices).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
@@ -11,13 +12,16 @@ fp32 GEMV; inputs whose products and sums are small integers are exact on both
 paths and are checked exactly.  Shapes cover the three kernels behind the call
 (batch <= 16 with X in LDS: one to eight 16-row tiles per workgroup and more
 workgroups than CUs; batch <= 32 or K too long for LDS: K split over waves;
-larger batches: 64 x 64 tiles; from 192 rows the dequantized-fp16 kernels),
+larger batches: 64 x 64 tiles; from 128 rows the register-dequantized kernels),
 ragged rows and batches, the smallest batch routed here (2: matrices wider
 than eight waves along K; narrower ones take the multi-row GEMV at batch 2,
 and at 3-4 those within one wave's K slice), and the full-size batched
 workload (18944 x 3584 at M = 4, 16, 64, 256 and 512, and 3584 x 18944 at
 M = 512) on sampled rows.
 """
+import os
+import sys
+
 import numpy as np
 import pytest
 import torch
@@ -26,6 +30,9 @@ import oracle
 from block_quantized_weight_qmv_amd import qmv
 from gpu_util import DEV, Weights, oracle_y, say, to_dev_x
 from synth import CONFIGS, gen_weights, gen_x, weight_seed, x_seed
+
+sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+from bench import dqreg_plan as bench_plan  # noqa: E402  (the form named in the test output)
 
 pytestmark = pytest.mark.gpu
 
@@ -59,12 +66,33 @@ def test_mfma_matches_oracle(rows, nblk, batch):
     assert np.all(err <= TOL), err
 
 
+# One shape per form of the register-dequantized kernels the launcher's model
+# picks (T tiles per wave, 64 or 128 activation rows per workgroup, K whole
+# or in slices summed afterwards), ragged where the form allows.
+DQREG_FORMS = [(256, 5, 128), (520, 14, 512), (4100, 1, 200), (520, 14, 384), (8200, 1, 200), (520, 14, 768),
+               (24000, 1, 200), (4100, 14, 256), (3000, 14, 160), (4100, 14, 200), (6000, 20, 160),
+               (24000, 1, 300), (3001, 14, 161), (4099, 14, 201), (257, 5, 129)]
+
+
+@pytest.mark.parametrize("rows,nblk,batch", DQREG_FORMS)
+def test_dqreg_forms_match_oracle(rows, nblk, batch):
+    cols = nblk * 256
+    say(f"dqreg form {bench_plan(rows, cols, batch)} q4_k {rows}x{cols} batch {batch}")
+    w = Weights("q4_k", rows, cols, seed=2100 + rows + nblk)
+    x = gen_x(batch, cols, "bf16", seed=210 + batch)
+    y = torch.full((batch, rows), 3.5, dtype=torch.float32, device=DEV)
+    w.gemv(to_dev_x(x, "bf16"), "bf16", batch, y=y)
+    err = oracle.normwise_rel_err(y.cpu().numpy(), oracle_y(w, x, "bf16"))
+    say(f"  normwise err max {err.max():.3e}")
+    assert np.all(err <= TOL), err
+
+
 @pytest.mark.parametrize("rows,batch", [(96, 64), (96, 128), (300, 384), (300, 400), (4100, 1000)])
 def test_mfma_integer_case_is_exact(rows, batch):
     # d = dmin = 1 and x in {-1, 0, 1}: every product and partial sum is an
     # integer below 2^24, so the fp32 result is exact on any summation order
-    # (on the dequantized-fp16 kernels, from 192 batch rows against 256
-    # weight rows, the fp16 weights sc u - m are exact integers too).
+    # (on the register-dequantized kernels the fp16 weights sc u - m are
+    # exact integers too, and the power-of-two activation scale is exact).
     cols = 4 * 256
     f = gen_weights("q4_k", rows, cols, 5)
     f["d_bits"][:] = 0x3C00
@@ -212,14 +240,12 @@ def test_mfma_f16_tile_graph_replay():
 @pytest.mark.parametrize("spread", ["wide", "large", "tiny", "rising", "falling", "zero_blocks"])
 @pytest.mark.parametrize("rows,nblk,batch", [(300, 9, 400), (18944, 3, 512), (4100, 3, 1000)])
 def test_dq_bf16_activation_range(layout, spread, rows, nblk, batch):
-    """From 192 rows the activations enter the matrix cores as fp16, scaled
-    per row by a power of two: on the LDS-tile kernel one that follows the
-    largest |x| seen along K and rescales the accumulators when a later block
-    raises it; on the register-fragment kernel one fixed per row from its
-    first block, the row's pass taken again from its maximum when a later
-    block would overflow fp16.  Rows far outside fp16's range, twelve decades
-    within a row, magnitudes rising or falling by 2^20 per block along K, and
-    all-zero blocks must all meet the gate, on one to five tiles per wave."""
+    """On the register-dequantized kernels the activations enter the matrix
+    cores as fp16, each row scaled by the power of two that brings its
+    largest |x| into [2^14, 2^15).  Rows far outside fp16's range, twelve
+    decades within a row, magnitudes rising or falling by 2^20 per block
+    along K, and all-zero blocks must all meet the gate, in forms with one to
+    five tiles per wave and K whole or in slices."""
     cols = nblk * 256
     w = Weights("q4_k", rows, cols, seed=1300)
     g = np.random.Generator(np.random.PCG64({"wide": 1, "large": 2, "tiny": 3, "rising": 4, "falling": 5,
@@ -258,9 +284,9 @@ def test_dq_bf16_activation_range(layout, spread, rows, nblk, batch):
 @pytest.mark.parametrize("x_dtype", ["bf16", "f16"])
 @pytest.mark.parametrize("rows,cols,batch", [(520, 6 * 256, 400), (4100, 2 * 256, 1000), (18944, 2 * 256, 512)])
 def test_dq_deterministic_and_graph_replay(x_dtype, rows, cols, batch):
-    # the dequantized-fp16 kernels (register fragments, LDS tiles, five tiles
-    # per wave): bitwise equal on a second call and on every replay of a
-    # captured graph
+    # the register-dequantized kernels (K in slices, 64-row activation
+    # tiles, five tiles per wave): bitwise equal on a second call and on
+    # every replay of a captured graph
     say(f"dq {x_dtype} determinism and graph replay {rows}x{cols} batch {batch}")
     w = Weights("q4_k", rows, cols, seed=1400)
     x = to_dev_x(gen_x(batch, cols, x_dtype, seed=140), x_dtype)
@@ -280,3 +306,41 @@ def test_dq_deterministic_and_graph_replay(x_dtype, rows, cols, batch):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(yg, y0)
+
+
+def test_dqreg_workspace_capture_and_growth():
+    """The register-dequantized kernels keep a workspace per stream: a call
+    that would have to allocate it under stream capture fails with
+    QMV_ERR_HIP and a message; after an eager call the same call captures,
+    and its graph stays valid (and exact) after a larger call on the stream
+    has grown the workspace."""
+    rows, cols, batch = 3584, 14 * 256, 128
+    w = Weights("q4_k", rows, cols, seed=2300)
+    x = to_dev_x(gen_x(batch, cols, "bf16", seed=230), "bf16")
+    s = torch.cuda.Stream()
+    y = torch.zeros(batch, rows, dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
+    with pytest.raises(qmv.QmvError, match="workspace"):
+        with torch.cuda.stream(s):
+            with torch.cuda.graph(g, stream=s):
+                w.gemv(x, "bf16", batch, y=y, stream=s)
+    torch.cuda.synchronize()
+    y0 = w.gemv(x, "bf16", batch)
+    with torch.cuda.stream(s):
+        w.gemv(x, "bf16", batch, y=y, stream=s)  # allocates this stream's workspace
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=s):
+            w.gemv(x, "bf16", batch, y=y, stream=s)
+        # a larger call on the same stream grows the workspace
+        big = 512
+        xb = to_dev_x(gen_x(big, cols, "bf16", seed=231), "bf16")
+        yb = w.gemv(xb, "bf16", big, stream=s)
+        torch.cuda.synchronize()
+    assert torch.equal(yb, w.gemv(xb, "bf16", big))
+    for _ in range(2):
+        y.fill_(0.0)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y0)

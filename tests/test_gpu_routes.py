@@ -6,8 +6,10 @@ figures and to pick the dominant kernel.  For every benchmarked launch plan,
 one eager step of bench.py is traced with rocprofv3 (kernel trace only) in a
 child process, and the GEMV dispatches of that step, in order, must carry the
 names the plan gives (the load-time repacks and the probes are left out).  A
-launch group served by the matrix-core kernels dispatches one kernel per
-matrix, named for that matrix's shape; every other group is one dispatch.
+launch group served by the matrix-core kernels dispatches per matrix, named
+for that matrix's shape (the register-dequantized kernel with its activation
+conversion before it and, with K in slices, the partial-output sum after
+it); every other group is one dispatch.
 """
 import csv
 import glob
@@ -62,12 +64,6 @@ def test_bench_kernel_names_are_dispatched(config, batch, x_dtype):
         r = subprocess.run(cmd, cwd=td, env=env, capture_output=True, text=True, timeout=240)
         assert r.returncode == 0, (r.returncode, r.stdout[-2000:], r.stderr[-2000:])
         got = _dispatched(td)
-    want = []
-    for g, k in zip(plan["groups"], plan["kname"]):
-        if k.startswith("qmv::gemm_q4_k_"):  # one matrix-core dispatch per matrix, each named for its shape
-            want += [bench.kernel_name(plan["fmt"], [plan["mats"][m][2]], plan["x_dtype"], plan["batch"], layout,
-                                       [plan["mats"][m][1]]) for m in g]
-        else:
-            want.append(k)
+    want = [k for _, _, k in plan["dispatches"]]
     say(f"  dispatched {got}")
     assert got == want, (got, want)
