@@ -265,8 +265,40 @@ int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x, int32_t x_dty
   return qmv_gemv_multi(fmt, x_dtype, batch, &item, 1, stream);
 }
 
+// qmv_gemv_multi; with fixed_scratch the batched kernels take the library's
+// fixed scratch instead of the stream's workspace (nothing is allocated).
+static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
+                               int32_t n, void* stream, bool fixed_scratch);
+
+int32_t qmv_gemv_noalloc(int32_t fmt, const qmv_weights* W, const void* x, int32_t x_dtype, float* y,
+                         int64_t rows, int64_t cols, int64_t batch, void* stream) {
+  if (!W) return fail(QMV_ERR_NULL, "weights descriptor is NULL");
+  if (fmt != W->fmt || rows != W->rows || cols != W->cols)
+    return fail(QMV_ERR_FORMAT, "call (fmt %d, %lld x %lld) disagrees with weights (fmt %d, %lld x %lld)",
+                fmt, (long long)rows, (long long)cols, W->fmt, (long long)W->rows,
+                (long long)W->cols);
+  const qmv_gemv_item item{W, x, y};
+  return gemv_multi_impl(fmt, x_dtype, batch, &item, 1, stream, true);
+}
+
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
                        int32_t n, void* stream) {
+  return gemv_multi_impl(fmt, x_dtype, batch, items, n, stream, false);
+}
+
+static int32_t batched_status(hipError_t e, bool fixed_scratch) {
+  if (e == hipErrorStreamCaptureUnsupported)
+    return fail(QMV_ERR_HIP, "qmv_gemv: the workspace of this stream must grow, which cannot happen "
+                             "under stream capture: make the same call once before capturing");
+  if (fixed_scratch && e == hipErrorOutOfMemory)
+    return fail(QMV_ERR_SIZE, "qmv_gemv_noalloc: this call needs more than the %llu bytes of the "
+                              "library's fixed scratch (fewer activation rows fit)",
+                (unsigned long long)qmv::kScratchBytes);
+  return qmv::from_hip(e, "qmv_gemv (batched matrix-core) launch");
+}
+
+static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
+                               int32_t n, void* stream, bool fixed_scratch) {
   if (!items) return fail(QMV_ERR_NULL, "items is NULL");
   if (n < 1) return fail(QMV_ERR_SHAPE, "item count %d < 1", n);
   if (n > qmv::kMaxItems)
@@ -370,10 +402,14 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
     };
     if (nn) e = rows(narrow, nn);
     if (e == hipSuccess && ns) e = rows(split, ns);
-    if (e == hipSuccess && nm) e = qmv::gemm_q4_k_mfma_items(mfma16, nm, true, batch, s);
+    if (e == hipSuccess && nm) {
+      e = qmv::gemm_q4_k_mfma_items(mfma16, nm, true, batch, s, fixed_scratch);
+      if (e != hipSuccess) return batched_status(e, fixed_scratch);
+    }
     if (e == hipSuccess && nw) {
       if (q4k_mfma) {
-        e = qmv::gemm_q4_k_mfma_items(wide, nw, false, batch, s);
+        e = qmv::gemm_q4_k_mfma_items(wide, nw, false, batch, s, fixed_scratch);
+        if (e != hipSuccess) return batched_status(e, fixed_scratch);
       } else {
         switch (fmt) {
           case QMV_Q4_K:
@@ -393,17 +429,11 @@ int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_ge
         }
       }
     }
-    if (e == hipErrorStreamCaptureUnsupported)
-      return qmv::fail(QMV_ERR_HIP, "qmv_gemv: the workspace of this stream must grow, which cannot happen "
-                                    "under stream capture: make the same call once before capturing");
     return qmv::from_hip(e, "qmv_gemv (multi-row) launch");
   }
   if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
-    e = qmv::gemm_q4_k_mfma_items(calls, n, false, batch, s);
-    if (e == hipErrorStreamCaptureUnsupported)
-      return qmv::fail(QMV_ERR_HIP, "qmv_gemv: the workspace of this stream must grow, which cannot happen "
-                                    "under stream capture: make the same call once before capturing");
-    return qmv::from_hip(e, "qmv_gemv (MFMA tiles) launch");
+    e = qmv::gemm_q4_k_mfma_items(calls, n, false, batch, s, fixed_scratch);
+    return batched_status(e, fixed_scratch);
   }
   switch (fmt) {
     case QMV_Q8_0: e = qmv::gemv_q8_0(calls, n, x_dtype, batch, s); break;

@@ -58,6 +58,7 @@
 // consecutive 16-byte pieces each) both land any eight lanes of a row of the
 // wave on eight different 16-byte bank groups of a 128-byte line.
 #include <algorithm>
+#include <mutex>
 #include <type_traits>
 #include <utility>
 
@@ -617,7 +618,34 @@ hipError_t gemm_q4_k_dqreg_ws(const qmv_weights& W, const void* x, bool f16x, fl
   return hipGetLastError();
 }
 
-hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t stream) {
+// The fixed workspace of qmv_gemv_noalloc, for callers that cannot allocate:
+// one copy per device, held from module load until the process ends.  In
+// host code `scratch` only names the symbol; its device address, per device,
+// comes from hipGetSymbolAddress on the first use there.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+hipError_t scratch_workspace(size_t bytes, void** out) {
+  if (bytes > kScratchBytes) return hipErrorOutOfMemory;
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* ptr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    ptr[dev] = p;
+  }
+  *out = ptr[dev];
+  return hipSuccess;
+}
+
+hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t stream,
+                                bool fixed_scratch) {
   DqregPlan plans[kMaxItems];
   bool reg[kMaxItems];
   size_t bytes = 0;
@@ -629,7 +657,7 @@ hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t
   }
   void* ws = nullptr;
   if (bytes) {
-    const hipError_t e = workspace(stream, bytes, &ws);
+    const hipError_t e = fixed_scratch ? scratch_workspace(bytes, &ws) : workspace(stream, bytes, &ws);
     if (e != hipSuccess) return e;
   }
   hipError_t e = hipSuccess;

@@ -109,7 +109,15 @@ hipError_t gemm_q4_k_dqreg_ws(const qmv_weights& W, const void* x, bool f16x, fl
 // so (with the workspace of stream s, sized for the largest; consecutive
 // calls on the same activations convert them once), else on the kernels of
 // gemm_q4_k_bf16 / gemm_q4_k_f16.
-hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t s);
+// With fixed_scratch, the workspace is the library's fixed device array of
+// kScratchBytes (scratch_workspace) and nothing is allocated; a call that
+// needs more fails with hipErrorOutOfMemory before any launch.
+hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t s,
+                                bool fixed_scratch = false);
+constexpr size_t kScratchBytes = QMV_NOALLOC_SCRATCH_BYTES;
+// The fixed device array of kScratchBytes on the current device (its
+// address looked up once per device); hipErrorOutOfMemory above that size.
+hipError_t scratch_workspace(size_t bytes, void** out);
 // Device workspace for stream s on the current device: at least `bytes`,
 // 256-byte aligned, one per (device, stream), kept until the process ends.
 // Growing it (hipMalloc of a new one; the old one stays allocated, so

@@ -65,6 +65,7 @@ _SIGS = {
     "qmv_create_weights_planes": (_i32, [_i32, _i64, _i64, _p, _u64, ctypes.POINTER(QmvWeights)]),
     "qmv_repack_planes": (_i32, [ctypes.POINTER(QmvWeights), _p, _u64, ctypes.POINTER(QmvWeights), _p]),
     "qmv_gemv": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
+    "qmv_gemv_noalloc": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
     "qmv_gemv_multi": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32, _p]),
     "qmv_dequant": (_i32, [ctypes.POINTER(QmvWeights), _p, _i32, _p]),
     "qmv_probe_read_outputs": (_i64, [_u64]),
@@ -291,6 +292,15 @@ def qmv_gemv(fmt, W: QmvWeights, x, x_dtype, y, rows: int, cols: int, batch: int
     _check_dev(y, "y", 0, batch * rows)
     _check(lib().qmv_gemv(_fmt(fmt), ctypes.byref(W), _ptr(x), _dtype(x_dtype), _ptr(y),
                           rows, cols, batch, _stream(stream, x, y)))
+
+
+def qmv_gemv_noalloc(fmt, W: QmvWeights, x, x_dtype, y, rows: int, cols: int, batch: int,
+                     stream=None) -> None:
+    xd = _dtype(x_dtype)
+    _check_dev(x, "x", xd, batch * cols)
+    _check_dev(y, "y", 0, batch * rows)
+    _check(lib().qmv_gemv_noalloc(_fmt(fmt), ctypes.byref(W), _ptr(x), _dtype(x_dtype), _ptr(y),
+                                  rows, cols, batch, _stream(stream, x, y)))
 
 
 def qmv_gemv_multi(fmt, x_dtype, batch: int, items, stream=None) -> None:

@@ -246,6 +246,26 @@ int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,
                  int32_t x_dtype, float* y, int64_t rows, int64_t cols,
                  int64_t batch, void* stream);
 
+/* qmv_gemv for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same arguments, checks, kernels and results, bit for bit, as
+ * qmv_gemv, but where the register-dequantized kernels need a workspace they
+ * take the library's fixed device array of QMV_NOALLOC_SCRATCH_BYTES
+ * (64 MiB, one per GPU, held from library load until the process ends)
+ * instead of allocating one; no path of this call allocates.  A call whose
+ * workspace would exceed it (activation rows x cols x 2 bytes, plus row
+ * scales and up to 8 partial outputs of rows x batch floats) fails with
+ * QMV_ERR_SIZE before any launch; the 7B decoder layer's matrices fit up to
+ * 512 activation rows.  Nothing in the array needs to start at zero.  Every
+ * call on one GPU shares the array and leaves it holding its own
+ * intermediates: calls that overlap on one GPU (several streams or
+ * threads, or graph replays of such calls) race and must be serialized by
+ * the caller. */
+#define QMV_NOALLOC_SCRATCH_BYTES (64ull << 20)
+int32_t qmv_gemv_noalloc(int32_t fmt, const qmv_weights* W, const void* x,
+                         int32_t x_dtype, float* y, int64_t rows,
+                         int64_t cols, int64_t batch, void* stream);
+
 /* One matrix of a multi-matrix GEMV launch. */
 typedef struct qmv_gemv_item {
   const qmv_weights* W; /* packed W_i (all items share the launch's format)  */
