@@ -416,12 +416,17 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
     for gi, g in enumerate(groups):
         if kname[gi].startswith("qmv::gemm"):
             ks = group_dispatches(fmt, [(mats[m][1], mats[m][2]) for m in g], x_dtype, batch, layout)
-            # each dispatch is credited to the matrix of the product kernel it serves
+            # each dispatch is credited to the matrix of the product kernel it
+            # serves: a conversion to the next product, a sum to the last one
             mi = 0
             for k in ks:
-                dispatches.append((gi, g[min(mi, len(g) - 1)], k))
                 if k.startswith("qmv::gemm"):
+                    dispatches.append((gi, g[mi], k))
                     mi += 1
+                elif k == "qmv::dqreg_sum":
+                    dispatches.append((gi, g[mi - 1], k))
+                else:
+                    dispatches.append((gi, g[mi], k))
         else:
             dispatches.append((gi, None, kname[gi]))
     workload = (cfg["name"] + (f"_m{batch}" if config == 5 or batch_given else "")
@@ -626,29 +631,37 @@ def summarize_trace(args) -> int:
     order = sorted(classes, key=len, reverse=True)
     durs = [[] for _ in disp]
     runs = []  # (class key, [dispatch durations per replay]) for ambiguous classes
+    def matches(key, at):
+        return at + len(key) <= len(toks) and all(toks[at + k][:2] == key[k] for k in range(len(key)))
+
+    def continues(at):
+        return at == len(toks) or any(matches(key, at) for key in order)
+
     p = unmatched = 0
     prev = None
     while p < len(toks):
         # a graph replays one pattern many times over: the pattern just seen
-        # first, then the longest
-        for key in ([prev] if prev else []) + order:
-            if p + len(key) <= len(toks) and all(toks[p + k][:2] == key[k] for k in range(len(key))):
-                prev = key
-                ds = [toks[p + k][2] for k in range(len(key))]
-                if len(classes[key]) == 1:
-                    for k, si in enumerate(classes[key][0]):
-                        durs[si].append(ds[k])
-                elif runs and runs[-1][0] == key and runs[-1][2] == p:
-                    runs[-1][1].append(ds)
-                    runs[-1][2] = p + len(key)
-                else:
-                    runs.append([key, [ds], p + len(key)])
-                p += len(key)
-                break
-        else:
+        # first, then the longest; a pattern is taken only if another (or the
+        # end of the trace) follows it, so that the tail of one replay and the
+        # head of the next are not read as a longer pattern
+        cands = [c for c in ([prev] if prev else []) + order if matches(c, p)]
+        key = next((c for c in cands if continues(p + len(c))), cands[0] if cands else None)
+        if key is None:
             unmatched += 1
             p += 1
             prev = None
+            continue
+        prev = key
+        ds = [toks[p + k][2] for k in range(len(key))]
+        if len(classes[key]) == 1:
+            for k, si in enumerate(classes[key][0]):
+                durs[si].append(ds[k])
+        elif runs and runs[-1][0] == key and runs[-1][2] == p:
+            runs[-1][1].append(ds)
+            runs[-1][2] = p + len(key)
+        else:
+            runs.append([key, [ds], p + len(key)])
+        p += len(key)
     ref = [statistics.median(d) if d else None for d in durs]
     for key, reps, _ in runs:
         run_med = [statistics.median(r[k] for r in reps) for k in range(len(key))]
