@@ -118,39 +118,47 @@ __device__ __forceinline__ uint32_t rg_pack(_Float16 a, _Float16 b) {
 // largest lands in [2^14, 2^15), so no value overflows fp16 and values down
 // to 2^-24 of the largest keep full fp16 precision; each value is rounded to
 // nearest once.  e = 0 for an all-zero row; e stays within [-126, 127].  One
-// workgroup per row: a pass for the maximum (four loads in flight per
-// thread), a pass for the conversion (the row is in L2 by then).  K a
-// multiple of 8, x and out 16-byte aligned.
+// workgroup per row; rows of up to 16384 columns are read once and held in
+// registers for both the maximum and the conversion, longer ones are read
+// twice (the second time from L2).  K a multiple of 8, x and out 16-byte
+// aligned.
 template <bool BF16>
 __global__ void __launch_bounds__(256) act_rows_f16(const uint16_t* x, int K, uint16_t* out, float* scale) {
+  constexpr int kHeld = 8;  // 16-byte pieces a thread keeps between the two passes (rows up to 16384 columns)
   __shared__ int wmax[4];
   const int tid = static_cast<int>(threadIdx.x), lane = tid & 63;
   const int row = static_cast<int>(blockIdx.x);
   const uint4* xr = reinterpret_cast<const uint4*>(x + static_cast<size_t>(row) * K);
   uint4* orow = reinterpret_cast<uint4*>(out + static_cast<size_t>(row) * K);
   const int n8 = K >> 3;
+  const bool held = n8 <= kHeld * 256;
+  uint4 v[kHeld];
+  if (held) {
+#pragma unroll
+    for (int u = 0; u < kHeld; ++u) v[u] = tid + 256 * u < n8 ? xr[tid + 256 * u] : make_uint4(0u, 0u, 0u, 0u);
+  }
   int e = 0;
   if constexpr (BF16) {
     u16x2_t m2 = {0, 0};
-    int i = tid;
-    for (; i + 3 * 256 < n8; i += 4 * 256) {
-      uint4 v[4];
+    auto fold = [&](const uint4& q) {
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, q.x & 0x7FFF7FFFu));
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, q.y & 0x7FFF7FFFu));
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, q.z & 0x7FFF7FFFu));
+      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, q.w & 0x7FFF7FFFu));
+    };
+    if (held) {
 #pragma unroll
-      for (int u = 0; u < 4; ++u) v[u] = xr[i + 256 * u];
+      for (int u = 0; u < kHeld; ++u) fold(v[u]);  // the zero fill adds nothing to a maximum
+    } else {
+      int i = tid;
+      for (; i + 3 * 256 < n8; i += 4 * 256) {
+        uint4 q[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].x & 0x7FFF7FFFu));
-        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].y & 0x7FFF7FFFu));
-        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].z & 0x7FFF7FFFu));
-        m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v[u].w & 0x7FFF7FFFu));
+        for (int u = 0; u < 4; ++u) q[u] = xr[i + 256 * u];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) fold(q[u]);
       }
-    }
-    for (; i < n8; i += 256) {
-      const uint4 v = xr[i];
-      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.x & 0x7FFF7FFFu));
-      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.y & 0x7FFF7FFFu));
-      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.z & 0x7FFF7FFFu));
-      m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, v.w & 0x7FFF7FFFu));
+      for (; i < n8; i += 256) fold(xr[i]);
     }
     int mx = max(static_cast<int>(m2.x), static_cast<int>(m2.y));
 #pragma unroll
@@ -163,23 +171,27 @@ __global__ void __launch_bounds__(256) act_rows_f16(const uint16_t* x, int K, ui
     e = e < -126 ? -126 : (e > 127 ? 127 : e);
   }
   const float s = __builtin_amdgcn_ldexpf(1.f, -e);
-  for (int i = tid; i < n8; i += 256) {
-    const uint4 v = xr[i];  // (x0 x1) (x2 x3) (x4 x5) (x6 x7)
-    uint4 o;
+  auto convert = [&](const uint4& q) {  // (x0 x1) (x2 x3) (x4 x5) (x6 x7)
     if constexpr (BF16) {
-      const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+      const uint32_t w[4] = {q.x, q.y, q.z, q.w};
       _Float16 h[8];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
         h[2 * k] = static_cast<_Float16>(__builtin_bit_cast(float, w[k] << 16) * s);
         h[2 * k + 1] = static_cast<_Float16>(__builtin_bit_cast(float, w[k] & 0xFFFF0000u) * s);
       }
-      o = make_uint4(rg_pack(h[0], h[2]), rg_pack(h[1], h[3]), rg_pack(h[4], h[6]), rg_pack(h[5], h[7]));
+      return make_uint4(rg_pack(h[0], h[2]), rg_pack(h[1], h[3]), rg_pack(h[4], h[6]), rg_pack(h[5], h[7]));
     } else {
-      o = make_uint4(__builtin_amdgcn_perm(v.y, v.x, 0x05040100u), __builtin_amdgcn_perm(v.y, v.x, 0x07060302u),
-                     __builtin_amdgcn_perm(v.w, v.z, 0x05040100u), __builtin_amdgcn_perm(v.w, v.z, 0x07060302u));
+      return make_uint4(__builtin_amdgcn_perm(q.y, q.x, 0x05040100u), __builtin_amdgcn_perm(q.y, q.x, 0x07060302u),
+                        __builtin_amdgcn_perm(q.w, q.z, 0x05040100u), __builtin_amdgcn_perm(q.w, q.z, 0x07060302u));
     }
-    orow[i] = o;
+  };
+  if (held) {
+#pragma unroll
+    for (int u = 0; u < kHeld; ++u)
+      if (tid + 256 * u < n8) orow[tid + 256 * u] = convert(v[u]);
+  } else {
+    for (int i = tid; i < n8; i += 256) orow[i] = convert(xr[i]);
   }
   if (tid == 0) scale[row] = __builtin_amdgcn_ldexpf(1.f, e);
 }
@@ -251,14 +263,17 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
       const uint32_t mw[2] = {h.z & 0x3F3F3F3Fu, ((h.w >> 4) & 0x0F0F0F0Fu) | ((h.z >> 2) & 0x30303030u)};
       const int sh = 16 * (g >> 1);  // sub-blocks 2 (g >> 1) + (0, 1) of each word
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh)
+      for (int hh = 0; hh < 2; ++hh) {
+        // shifted once, so that each value is one byte-to-float conversion
+        const uint32_t sw = scw[hh] >> sh, mh = mw[hh] >> sh;
 #pragma unroll
         for (int nib = 0; nib < 2; ++nib) {
-          const float sc = static_cast<float>((scw[hh] >> (sh + 8 * nib)) & 0xFFu);
-          const float mm = static_cast<float>((mw[hh] >> (sh + 8 * nib)) & 0xFFu);
+          const float sc = static_cast<float>((sw >> (8 * nib)) & 0xFFu);
+          const float mm = static_cast<float>((mh >> (8 * nib)) & 0xFFu);
           const h2_t v = {static_cast<_Float16>(d * sc), static_cast<_Float16>(-(dmin * mm))};
           scl[i][hh][nib] = __builtin_bit_cast(uint32_t, v);
         }
+      }
     }
   };
 
