@@ -87,13 +87,15 @@ def dq_route(rows: int, cols: int, batch: int, layout: str) -> bool:
     return wbytes < 2 ** 32 and 2 * batch * cols < 2 ** 32
 
 
-def dqreg_plan(rows: int, cols: int, batch: int, cus: int = DEVICE_CUS):
-    """(T, NB, slices, blocks per slice) of gemm_q4_k_dqreg: the launcher's
-    model, rounds of workgroups over the compute units times a workgroup's
-    time ((14 + 17 / T) ns per product of a wave at NB = 8, (20 + 16 / T) at
-    NB = 4, 5.5 us fixed), plus the sum of the partial outputs when K is
-    sliced (3 us and its bytes at 8 TB/s).  Ties keep the first in the order
-    NB = 8 then 4, smaller T, fewer slices."""
+def dqreg_plan(rows, cols: int, batch: int, cus: int = DEVICE_CUS):
+    """(T, NB, slices, blocks per slice) of gemm_q4_k_dqreg for one matrix of
+    `rows` rows, or a run of matrices (a list of row counts) in one launch:
+    the launcher's model, rounds of workgroups over the compute units times a
+    workgroup's time ((14 + 17 / T) ns per product of a wave at NB = 8,
+    (20 + 16 / T) at NB = 4, 5.5 us fixed), plus the sum of the partial
+    outputs when K is sliced (3 us and its bytes at 8 TB/s).  Ties keep the
+    first in the order NB = 8 then 4, smaller T, fewer slices."""
+    rows_list = list(rows) if isinstance(rows, (list, tuple)) else [rows]
     nb = cols // 256
     best = None
     for nbt in (8, 4):
@@ -103,19 +105,32 @@ def dqreg_plan(rows: int, cols: int, batch: int, cus: int = DEVICE_CUS):
                 splits = -(-nb // bps)
                 if splits != s:
                     continue
-                wgs = -(-rows // (64 * t)) * -(-batch // (16 * nbt)) * splits
+                tiles = sum(-(-r // (64 * t)) for r in rows_list)
+                wgs = tiles * -(-batch // (16 * nbt)) * splits
                 products = float(bps * 8 * nbt * t)
                 per = 20.0 + 16.0 / t if nbt == 4 else 14.0 + 17.0 / t
                 us = float(-(-wgs // cus)) * (products * per * 1e-3 + 5.5)
                 if splits > 1:
-                    us += 3.0 + float(splits + 1) * rows * batch * 4 / 8e6
+                    us += 3.0 + float(splits + 1) * sum(rows_list) * batch * 4 / 8e6
                 if best is None or us < best[0]:
                     best = (us, t, nbt, splits, bps)
     return best[1:]
 
 
-def dq_kernel_name(rows: int, cols: int, batch: int, layout: str) -> str:
-    """The register-dequantized kernel for one matrix of `rows` x `cols`."""
+def dq_run(mats, batch: int, layout: str):
+    """How many of the leading matrices (rows, cols) one register-dequantized
+    launch covers: those that route there with the first one's width, up to
+    four (0 if the first does not route there)."""
+    if not mats or not dq_route(mats[0][0], mats[0][1], batch, layout):
+        return 0
+    k = 1
+    while k < min(len(mats), 4) and mats[k][1] == mats[0][1] and dq_route(mats[k][0], mats[k][1], batch, layout):
+        k += 1
+    return k
+
+
+def dq_kernel_name(rows, cols: int, batch: int, layout: str) -> str:
+    """The register-dequantized kernel for one matrix or a run of matrices."""
     pl = "true" if layout == "planes" else "false"
     t, nbt = dqreg_plan(rows, cols, batch)[:2]
     d = 1 if t >= 3 else 2
@@ -123,25 +138,32 @@ def dq_kernel_name(rows: int, cols: int, batch: int, layout: str) -> str:
 
 
 def group_dispatches(fmt: str, mats, x_dtype: str, batch: int, layout: str):
-    """Kernels the matrices (rows, cols) of one launch on the matrix-core path
-    dispatch, in order: each register-dequantized matrix after the
-    activation conversion (skipped when the previous matrix was converted
-    from the same activations: a launch's matrices share them) and, with K
-    in slices, before the sum of its partial outputs."""
+    """(kernel, first matrix, matrices) of each dispatch the matrices (rows,
+    cols) of one launch on the matrix-core path make, in order: a run of up
+    to four register-dequantized matrices of one width is one product
+    launch, after the activation conversion (skipped when the previous run
+    converted the same activations: a launch's matrices share them) and,
+    with K in slices, before one sum of the partial outputs; the other
+    matrices take one matrix-core kernel each."""
     out = []
     prev = None
-    for rows, cols in mats:
-        k = kernel_name(fmt, [cols], x_dtype, batch, layout, [rows])
-        if k.startswith("qmv::gemm_q4_k_dqreg<"):
+    i = 0
+    while i < len(mats):
+        rows, cols = mats[i]
+        k = dq_run(mats[i:], batch, layout) if fmt == "q4_k" and x_dtype in ("f16", "bf16") else 0
+        if k:
+            run_rows = [m[0] for m in mats[i:i + k]]
             if prev != cols:
-                out.append(f"qmv::act_rows_f16<{'false' if x_dtype == 'f16' else 'true'}>")
-            out.append(k)
-            if dqreg_plan(rows, cols, batch)[2] > 1:
-                out.append("qmv::dqreg_sum")
+                out.append((f"qmv::act_rows_f16<{'false' if x_dtype == 'f16' else 'true'}>", i, k))
+            out.append((dq_kernel_name(run_rows, cols, batch, layout), i, k))
+            if dqreg_plan(run_rows, cols, batch)[2] > 1:
+                out.append(("qmv::dqreg_sum", i, k))
             prev = cols
+            i += k
         else:
-            out.append(k)
+            out.append((kernel_name(fmt, [cols], x_dtype, batch, layout, [rows]), i, 1))
             prev = None
+            i += 1
     return out
 
 
@@ -170,9 +192,10 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
         pol = "Q4KPlanesPolicy" if layout == "planes" else "Q4KPolicy"
         xt = "_Float16" if x_dtype == "f16" else "qmv::bf16_t"
         return f"qmv::gemv_rows_kernel<qmv::{pol}, {xt}, 1, 3, 256, 4>"
-    if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and rows_list is not None
-            and dq_route(rows_list[0], cols_list[0], batch, layout)):  # the register-dequantized kernels
-        return dq_kernel_name(rows_list[0], cols_list[0], batch, layout)
+    if fmt == "q4_k" and x_dtype in ("f16", "bf16") and rows_list is not None:  # the register-dequantized kernels
+        k = dq_run(list(zip(rows_list, cols_list)), batch, layout)
+        if k:
+            return dq_kernel_name(list(rows_list[:k]), cols_list[0], batch, layout)
     if fmt == "q4_k" and x_dtype == "f16" and batch >= 17:  # fp16 on the tile kernels
         pl = "true" if layout == "planes" else "false"
         mb = 1 if batch <= 32 else (2 if batch <= 64 else 4)
@@ -415,18 +438,9 @@ def workload_plan(config: int, batch: int | None, separate: bool, layout: str = 
     dispatches = []
     for gi, g in enumerate(groups):
         if kname[gi].startswith("qmv::gemm"):
-            ks = group_dispatches(fmt, [(mats[m][1], mats[m][2]) for m in g], x_dtype, batch, layout)
-            # each dispatch is credited to the matrix of the product kernel it
-            # serves: a conversion to the next product, a sum to the last one
-            mi = 0
-            for k in ks:
-                if k.startswith("qmv::gemm"):
-                    dispatches.append((gi, g[mi], k))
-                    mi += 1
-                elif k == "qmv::dqreg_sum":
-                    dispatches.append((gi, g[mi - 1], k))
-                else:
-                    dispatches.append((gi, g[mi], k))
+            # each dispatch is credited to the matrix it serves (None: several)
+            for k, i0, n in group_dispatches(fmt, [(mats[m][1], mats[m][2]) for m in g], x_dtype, batch, layout):
+                dispatches.append((gi, g[i0] if n == 1 else None, k))
         else:
             dispatches.append((gi, None, kname[gi]))
     workload = (cfg["name"] + (f"_m{batch}" if config == 5 or batch_given else "")

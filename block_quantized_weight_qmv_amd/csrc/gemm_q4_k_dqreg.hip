@@ -198,16 +198,27 @@ __global__ void __launch_bounds__(256) act_rows_f16(const uint16_t* x, int K, ui
 
 // T: 16-row weight tiles per wave.  NB: 16-row activation (B) tiles per
 // workgroup.  XD: activation loads run XD half blocks ahead (1 or 2).  CD:
-// code loads run CD half blocks ahead (1 or 2).  PL: plane layout.  x: the
-// activations in act_rows_f16's form; xs[m]: the factor of row m.  Blocks
-// kb0 = z bps .. min(kb0 + bps, K / 256) of the slice z = blockIdx.z; out:
-// y when there is one slice, else the partial outputs of slice z at
-// out + z zs ([M][N] each).  All byte offsets fit in 32 bits (checked by the
-// launcher).
+// code loads run CD half blocks ahead (1 or 2).  PL: plane layout.  mats:
+// one to kDqregMaxMats matrices of K columns against the same activations,
+// the row tiles of matrix i being blockIdx.x = tile0[i] .. tile0[i + 1];
+// x: the activations in act_rows_f16's form; xs[m]: the factor of row m.
+// Blocks kb0 = z bps .. min(kb0 + bps, K / 256) of the slice z = blockIdx.z;
+// out[i]: matrix i's y when there is one slice, else its partial outputs of
+// slice z at out[i] + z zs[i] ([M][N] each).  All byte offsets fit in 32
+// bits (checked by the launcher).
+struct DqregMats {
+  const uint8_t* w[kDqregMaxMats];
+  float* out[kDqregMaxMats];
+  size_t zs[kDqregMaxMats];
+  uint32_t pa[kDqregMaxMats];
+  int n[kDqregMaxMats];
+  int tile0[kDqregMaxMats + 1];
+  int count;
+};
+
 template <int T, int NB, int XD, int CD, bool PL>
 __global__ void __launch_bounds__(kRgThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
-gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, const float* xs, float* out,
-                size_t zs, int M, int bps) {
+gemm_q4_k_dqreg(const DqregMats mats, int K, const uint16_t* x, const float* xs, int M, int bps) {
   constexpr int kBatch = rg_batch(NB), kBufUnits = rg_buf_units(NB);
   constexpr int RS = NB / 4;  // activation rows staged per lane
   extern __shared__ __attribute__((aligned(16))) uint4 rg_lds[];
@@ -220,13 +231,20 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
   const int m0 = static_cast<int>(blockIdx.y) * kBatch;
   const int g = lane >> 4, r16 = lane & 15;
   const uint8_t* xbytes = reinterpret_cast<const uint8_t*>(x);
-  float* y = out + blockIdx.z * zs;
+  // this workgroup's matrix (blockIdx.x is uniform, so is mi)
+  int mi = 0;
+#pragma unroll
+  for (int k = 1; k < kDqregMaxMats; ++k) mi += k < mats.count && static_cast<int>(blockIdx.x) >= mats.tile0[k];
+  const uint8_t* w = mats.w[mi];
+  const uint32_t pa = mats.pa[mi];
+  const int N = mats.n[mi];
+  float* y = mats.out[mi] + blockIdx.z * mats.zs[mi];
 
   // Weight role: tile i of this wave is weight rows nw0 + 16 i .. + 16; lane
   // (g, r16) loads row nw0 + 16 i + r16 (rows past N re-read the last row,
   // results not stored): per block the header and, for half h, code piece
   // 16 (g & 1) of chunk 2h + (g >> 1).
-  const int nw0 = static_cast<int>(blockIdx.x) * (64 * T) + wave * (16 * T);
+  const int nw0 = (static_cast<int>(blockIdx.x) - mats.tile0[mi]) * (64 * T) + wave * (16 * T);
   uint32_t bidx[T];  // block index of the row's block 0
 #pragma unroll
   for (int i = 0; i < T; ++i) bidx[i] = static_cast<uint32_t>(min(nw0 + 16 * i + r16, N - 1)) * nb;
@@ -488,9 +506,20 @@ gemm_q4_k_dqreg(const uint8_t* w, uint32_t pa, int N, int K, const uint16_t* x, 
   }
 }
 
-// y[e] = the sum over s < S of part[s zs + e] in order of s, for e < n
-// (zs a multiple of 4; part and y 16-byte aligned).
-__global__ void __launch_bounds__(256) dqreg_sum(const float* part, int S, size_t zs, size_t n, float* y) {
+// For item i = blockIdx.y: y[e] = the sum over s < S of part[s zs + e] in
+// order of s, for e < n (zs a multiple of 4; part and y 16-byte aligned).
+struct DqregSums {
+  const float* part[kDqregMaxMats];
+  float* y[kDqregMaxMats];
+  size_t zs[kDqregMaxMats];
+  size_t n[kDqregMaxMats];
+};
+
+__global__ void __launch_bounds__(256) dqreg_sum(const DqregSums items, int S) {
+  const int it = static_cast<int>(blockIdx.y);
+  const float* part = items.part[it];
+  float* y = items.y[it];
+  const size_t zs = items.zs[it], n = items.n[it];
   const size_t n4 = n / 4, z4 = zs / 4;
   const f32x4_t* p = reinterpret_cast<const f32x4_t*>(part);
   f32x4_t* o = reinterpret_cast<f32x4_t*>(y);
@@ -522,32 +551,29 @@ size_t rg_align(size_t v) { return (v + 255) / 256 * 256; }
 size_t rg_slice_floats(int64_t rows, int64_t batch) { return rg_align(static_cast<size_t>(rows) * batch * 4) / 4; }
 
 template <int T, int NB>
-hipError_t launch_dqreg(const qmv_weights& W, const uint16_t* x16, const float* xs, float* out, size_t zs, int M,
-                        int splits, int bps, hipStream_t stream) {
+hipError_t launch_dqreg(const DqregMats& mats, int K, const uint16_t* x16, const float* xs, int M, int splits,
+                        int bps, bool pl, hipStream_t stream) {
   constexpr int D = rg_xd(T);
-  const int N = static_cast<int>(W.rows), K = static_cast<int>(W.cols);
-  const uint8_t* w = static_cast<const uint8_t*>(W.data);
-  const uint32_t pa = static_cast<uint32_t>(W.scales_offset);
-  const dim3 grid((N + 64 * T - 1) / (64 * T), (M + rg_batch(NB) - 1) / rg_batch(NB), splits);
+  const dim3 grid(mats.tile0[mats.count], (M + rg_batch(NB) - 1) / rg_batch(NB), splits);
   const size_t lds = rg_lds_bytes(NB);
-  if (W.layout == QMV_LAYOUT_PLANES)
-    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, D, D, true>), grid, dim3(kRgThreads), lds, stream, w, pa, N, K, x16,
-                       xs, out, zs, M, bps);
+  if (pl)
+    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, D, D, true>), grid, dim3(kRgThreads), lds, stream, mats, K, x16, xs, M,
+                       bps);
   else
-    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, D, D, false>), grid, dim3(kRgThreads), lds, stream, w, pa, N, K, x16,
-                       xs, out, zs, M, bps);
+    hipLaunchKernelGGL((gemm_q4_k_dqreg<T, NB, D, D, false>), grid, dim3(kRgThreads), lds, stream, mats, K, x16, xs,
+                       M, bps);
   return hipGetLastError();
 }
 
 template <int NB>
-hipError_t launch_dqreg_t(int t, const qmv_weights& W, const uint16_t* x16, const float* xs, float* out, size_t zs,
-                          int M, int splits, int bps, hipStream_t stream) {
+hipError_t launch_dqreg_t(int t, const DqregMats& mats, int K, const uint16_t* x16, const float* xs, int M,
+                          int splits, int bps, bool pl, hipStream_t stream) {
   switch (t) {
-    case 1: return launch_dqreg<1, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
-    case 2: return launch_dqreg<2, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
-    case 3: return launch_dqreg<3, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
-    case 4: return launch_dqreg<4, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
-    default: return launch_dqreg<5, NB>(W, x16, xs, out, zs, M, splits, bps, stream);
+    case 1: return launch_dqreg<1, NB>(mats, K, x16, xs, M, splits, bps, pl, stream);
+    case 2: return launch_dqreg<2, NB>(mats, K, x16, xs, M, splits, bps, pl, stream);
+    case 3: return launch_dqreg<3, NB>(mats, K, x16, xs, M, splits, bps, pl, stream);
+    case 4: return launch_dqreg<4, NB>(mats, K, x16, xs, M, splits, bps, pl, stream);
+    default: return launch_dqreg<5, NB>(mats, K, x16, xs, M, splits, bps, pl, stream);
   }
 }
 
@@ -558,12 +584,17 @@ hipError_t launch_dqreg_t(int t, const qmv_weights& W, const uint16_t* x16, cons
 // sum kernel, 3 us plus the partial outputs read and y written once at
 // 8 TB/s.  Fitted to kernel traces of the 7B layer's matrices at 128 to 512
 // rows (T = 1..5, 2 to 74 blocks per slice: within 10 %).
-double dqreg_cost(int64_t rows, int64_t batch, int64_t cus, int t, int nbt, int splits, int bps) {
-  const int64_t wgs = (rows + 64 * t - 1) / (64 * t) * ((batch + rg_batch(nbt) - 1) / rg_batch(nbt)) * splits;
+double dqreg_cost(const int64_t* rows, int n, int64_t batch, int64_t cus, int t, int nbt, int splits, int bps) {
+  int64_t tiles = 0, all_rows = 0;
+  for (int i = 0; i < n; ++i) {
+    tiles += (rows[i] + 64 * t - 1) / (64 * t);
+    all_rows += rows[i];
+  }
+  const int64_t wgs = tiles * ((batch + rg_batch(nbt) - 1) / rg_batch(nbt)) * splits;
   const double products = static_cast<double>(bps) * 8 * nbt * t;
   const double per = nbt == 4 ? 20.0 + 16.0 / t : 14.0 + 17.0 / t;
   double us = static_cast<double>((wgs + cus - 1) / cus) * (products * per * 1e-3 + 5.5);
-  if (splits > 1) us += 3.0 + static_cast<double>(splits + 1) * rows * batch * 4 / 8e6;
+  if (splits > 1) us += 3.0 + static_cast<double>(splits + 1) * all_rows * batch * 4 / 8e6;
   return us;
 }
 
@@ -577,7 +608,7 @@ bool dqreg_route(const qmv_weights& W, int64_t batch) {
   return wbytes < (1ull << 32) && 2 * static_cast<uint64_t>(batch) * W.cols < (1ull << 32);
 }
 
-DqregPlan dqreg_plan(int64_t rows, int64_t cols, int64_t batch) {
+DqregPlan dqreg_plan(const int64_t* rows, int n, int64_t cols, int64_t batch) {
   const int64_t cus = device_cus();
   const int nb = static_cast<int>(cols / 256);
   DqregPlan best{1, 8, 1, nb};
@@ -588,7 +619,7 @@ DqregPlan dqreg_plan(int64_t rows, int64_t cols, int64_t batch) {
         const int bps = (nb + s - 1) / s;
         const int splits = (nb + bps - 1) / bps;  // every slice holds at least one block
         if (splits != s) continue;
-        const double us = dqreg_cost(rows, batch, cus, t, nbt, splits, bps);
+        const double us = dqreg_cost(rows, n, batch, cus, t, nbt, splits, bps);
         if (best_us < 0 || us < best_us) {
           best = DqregPlan{t, nbt, splits, bps};
           best_us = us;
@@ -597,15 +628,16 @@ DqregPlan dqreg_plan(int64_t rows, int64_t cols, int64_t batch) {
   return best;
 }
 
-size_t dqreg_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, const DqregPlan& p) {
+size_t dqreg_workspace_bytes(const int64_t* rows, int n, int64_t cols, int64_t batch, const DqregPlan& p) {
   size_t b = rg_align(static_cast<size_t>(batch) * cols * 2) + rg_align(static_cast<size_t>(batch) * 4);
-  if (p.splits > 1) b += static_cast<size_t>(p.splits) * rg_slice_floats(rows, batch) * 4;
+  if (p.splits > 1)
+    for (int i = 0; i < n; ++i) b += static_cast<size_t>(p.splits) * rg_slice_floats(rows[i], batch) * 4;
   return b;
 }
 
-hipError_t gemm_q4_k_dqreg_ws(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
-                              const DqregPlan& p, void* ws, bool convert, hipStream_t stream) {
-  const int M = static_cast<int>(batch), N = static_cast<int>(W.rows), K = static_cast<int>(W.cols);
+hipError_t gemm_q4_k_dqreg_ws(const GemvCall* calls, int n, bool f16x, int64_t batch, const DqregPlan& p, void* ws,
+                              bool convert, hipStream_t stream) {
+  const int M = static_cast<int>(batch), K = static_cast<int>(calls[0].W->cols);
   uint8_t* base = static_cast<uint8_t*>(ws);
   uint16_t* x16 = reinterpret_cast<uint16_t*>(base);
   float* xs = reinterpret_cast<float*>(base + rg_align(static_cast<size_t>(M) * K * 2));
@@ -613,23 +645,43 @@ hipError_t gemm_q4_k_dqreg_ws(const qmv_weights& W, const void* x, bool f16x, fl
                                          rg_align(static_cast<size_t>(M) * 4));
   hipError_t e = hipSuccess;
   if (convert) {
+    const uint16_t* x = static_cast<const uint16_t*>(calls[0].x);
     if (f16x)
-      hipLaunchKernelGGL((act_rows_f16<false>), dim3(M), dim3(256), 0, stream, static_cast<const uint16_t*>(x), K,
-                         x16, xs);
+      hipLaunchKernelGGL((act_rows_f16<false>), dim3(M), dim3(256), 0, stream, x, K, x16, xs);
     else
-      hipLaunchKernelGGL((act_rows_f16<true>), dim3(M), dim3(256), 0, stream, static_cast<const uint16_t*>(x), K, x16,
-                         xs);
+      hipLaunchKernelGGL((act_rows_f16<true>), dim3(M), dim3(256), 0, stream, x, K, x16, xs);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  float* out = p.splits > 1 ? part : y;
-  const size_t zs = rg_slice_floats(N, M);
-  e = p.nb == 4 ? launch_dqreg_t<4>(p.t, W, x16, xs, out, zs, M, p.splits, p.bps, stream)
-                : launch_dqreg_t<8>(p.t, W, x16, xs, out, zs, M, p.splits, p.bps, stream);
+  DqregMats mats{};
+  DqregSums sums{};
+  mats.count = n;
+  size_t n_max = 0;
+  for (int i = 0; i < n; ++i) {
+    const qmv_weights& W = *calls[i].W;
+    mats.w[i] = static_cast<const uint8_t*>(W.data);
+    mats.pa[i] = static_cast<uint32_t>(W.scales_offset);
+    mats.n[i] = static_cast<int>(W.rows);
+    mats.tile0[i + 1] = mats.tile0[i] + static_cast<int>((W.rows + 64 * p.t - 1) / (64 * p.t));
+    mats.zs[i] = rg_slice_floats(W.rows, M);
+    if (p.splits > 1) {
+      mats.out[i] = part;
+      sums.part[i] = part;
+      sums.y[i] = calls[i].y;
+      sums.zs[i] = mats.zs[i];
+      sums.n[i] = static_cast<size_t>(M) * W.rows;
+      n_max = std::max(n_max, sums.n[i]);
+      part += static_cast<size_t>(p.splits) * mats.zs[i];
+    } else {
+      mats.out[i] = calls[i].y;
+    }
+  }
+  const bool pl = calls[0].W->layout == QMV_LAYOUT_PLANES;
+  e = p.nb == 4 ? launch_dqreg_t<4>(p.t, mats, K, x16, xs, M, p.splits, p.bps, pl, stream)
+                : launch_dqreg_t<8>(p.t, mats, K, x16, xs, M, p.splits, p.bps, pl, stream);
   if (e != hipSuccess || p.splits == 1) return e;
-  const size_t n = static_cast<size_t>(M) * N;
-  const int blocks = static_cast<int>(std::min<size_t>((n / 4 + 255) / 256 + 1, 4096));
-  hipLaunchKernelGGL(dqreg_sum, dim3(blocks), dim3(256), 0, stream, part, p.splits, zs, n, y);
+  const int blocks = static_cast<int>(std::min<size_t>((n_max / 4 + 255) / 256 + 1, 4096));
+  hipLaunchKernelGGL(dqreg_sum, dim3(blocks, n), dim3(256), 0, stream, sums, p.splits);
   return hipGetLastError();
 }
 
@@ -661,14 +713,29 @@ hipError_t scratch_workspace(size_t bytes, void** out) {
 
 hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t stream,
                                 bool fixed_scratch) {
-  DqregPlan plans[kMaxItems];
+  // runs of consecutive register-dequantized calls on the same activations
+  // and widths (up to kDqregMaxMats) share one conversion, one product
+  // launch and one sum launch
   bool reg[kMaxItems];
+  int run[kMaxItems];  // calls in the run starting at i (0 inside a run)
+  DqregPlan plans[kMaxItems];
   size_t bytes = 0;
-  for (int i = 0; i < n; ++i) {
-    reg[i] = dqreg_route(*calls[i].W, batch);
-    if (!reg[i]) continue;
-    plans[i] = dqreg_plan(calls[i].W->rows, calls[i].W->cols, batch);
-    bytes = std::max(bytes, dqreg_workspace_bytes(calls[i].W->rows, calls[i].W->cols, batch, plans[i]));
+  for (int i = 0; i < n; ++i) reg[i] = dqreg_route(*calls[i].W, batch);
+  for (int i = 0; i < n;) {
+    int k = 1;
+    if (reg[i])
+      while (i + k < n && k < kDqregMaxMats && reg[i + k] && calls[i + k].x == calls[i].x &&
+             calls[i + k].W->cols == calls[i].W->cols && calls[i + k].W->layout == calls[i].W->layout)
+        ++k;
+    run[i] = k;
+    for (int j = 1; j < k; ++j) run[i + j] = 0;
+    if (reg[i]) {
+      int64_t rows[kDqregMaxMats];
+      for (int j = 0; j < k; ++j) rows[j] = calls[i + j].W->rows;
+      plans[i] = dqreg_plan(rows, k, calls[i].W->cols, batch);
+      bytes = std::max(bytes, dqreg_workspace_bytes(rows, k, calls[i].W->cols, batch, plans[i]));
+    }
+    i += k;
   }
   void* ws = nullptr;
   if (bytes) {
@@ -676,14 +743,16 @@ hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t
     if (e != hipSuccess) return e;
   }
   hipError_t e = hipSuccess;
-  for (int i = 0; i < n && e == hipSuccess; ++i) {
+  const GemvCall* converted = nullptr;  // the run whose activations the workspace holds
+  for (int i = 0; i < n && e == hipSuccess; i += run[i]) {
     const GemvCall& c = calls[i];
     if (reg[i]) {
-      // the previous call left these activations converted in the workspace
-      const bool same = i > 0 && reg[i - 1] && calls[i - 1].x == c.x && calls[i - 1].W->cols == c.W->cols;
-      e = gemm_q4_k_dqreg_ws(*c.W, c.x, f16x, c.y, batch, plans[i], ws, !same, stream);
+      const bool same = converted && converted->x == c.x && converted->W->cols == c.W->cols;
+      e = gemm_q4_k_dqreg_ws(calls + i, run[i], f16x, batch, plans[i], ws, !same, stream);
+      converted = &c;
     } else {
       e = f16x ? gemm_q4_k_f16(*c.W, c.x, c.y, batch, stream) : gemm_q4_k_bf16(*c.W, c.x, c.y, batch, stream);
+      converted = nullptr;
     }
   }
   return e;

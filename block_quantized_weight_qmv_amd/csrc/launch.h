@@ -96,19 +96,24 @@ struct DqregPlan {
   int t, nb, splits, bps;
 };
 constexpr int kDqregMaxSplits = 8;
+// Matrices one launch of the register-dequantized kernels covers.
+constexpr int kDqregMaxMats = 4;
 bool dqreg_route(const qmv_weights& W, int64_t batch);
-DqregPlan dqreg_plan(int64_t rows, int64_t cols, int64_t batch);
-size_t dqreg_workspace_bytes(int64_t rows, int64_t cols, int64_t batch, const DqregPlan& p);
-// With the caller's workspace ws (dqreg_workspace_bytes, 256-byte aligned);
-// convert = false reuses the converted activations a previous call on the
-// same stream left in ws (same x, batch and cols).
-hipError_t gemm_q4_k_dqreg_ws(const qmv_weights& W, const void* x, bool f16x, float* y, int64_t batch,
-                              const DqregPlan& p, void* ws, bool convert, hipStream_t s);
+// The plan for n (1..kDqregMaxMats) matrices of rows[i] x cols in one launch.
+DqregPlan dqreg_plan(const int64_t* rows, int n, int64_t cols, int64_t batch);
+size_t dqreg_workspace_bytes(const int64_t* rows, int n, int64_t cols, int64_t batch, const DqregPlan& p);
+// The n calls (same x, cols and layout) in one launch, with the caller's
+// workspace ws (dqreg_workspace_bytes, 256-byte aligned); convert = false
+// reuses the converted activations a previous call on the same stream left
+// in ws (same x, batch and cols).
+hipError_t gemm_q4_k_dqreg_ws(const GemvCall* calls, int n, bool f16x, int64_t batch, const DqregPlan& p, void* ws,
+                              bool convert, hipStream_t s);
 // The matrix-core calls of one launch (Q4_K, bf16 or fp16 rows, batch >= 2)
 // in order: each on the register-dequantized kernels when dqreg_route says
-// so (with the workspace of stream s, sized for the largest; consecutive
-// calls on the same activations convert them once), else on the kernels of
-// gemm_q4_k_bf16 / gemm_q4_k_f16.
+// so (with the workspace of stream s, sized for the largest; runs of
+// consecutive such calls on the same activations, widths and layout, up to
+// kDqregMaxMats, share one conversion, one product launch and one sum),
+// else on the kernels of gemm_q4_k_bf16 / gemm_q4_k_f16.
 // With fixed_scratch, the workspace is the library's fixed device array of
 // kScratchBytes (scratch_workspace) and nothing is allocated; a call that
 // needs more fails with hipErrorOutOfMemory before any launch.
