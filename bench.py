@@ -70,16 +70,17 @@ def kernel_source_hash(kernel: str) -> str:
 
 # Compute units of the MI355X; the register-dequantized plans depend on it.
 DEVICE_CUS = 256
-# Q4_K x fp16/bf16 batches take the register-dequantized kernels from
-# DQ_MIN_BATCH rows, or from DQ_MIN_BATCH_LONGK rows against matrices of at
-# least DQ_LONGK columns, against matrices of at least DQ_MIN_ROWS rows.
-DQ_MIN_BATCH, DQ_MIN_BATCH_LONGK, DQ_LONGK, DQ_MIN_ROWS = 128, 64, 8192, 256
+# Q4_K x fp16/bf16 batches take the register-dequantized kernels for
+# matrices of at least DQ_MIN_ROWS rows: from DQ_MIN_BATCH_RUN rows for runs
+# of two or more matrices of a launch and for matrices of at least DQ_LONGK
+# columns, from DQ_MIN_BATCH rows for any matrix.
+DQ_MIN_BATCH, DQ_MIN_BATCH_RUN, DQ_LONGK, DQ_MIN_ROWS = 65, 32, 8192, 256
 
 
-def dq_route(rows: int, cols: int, batch: int, layout: str) -> bool:
-    """The launcher's dqreg_route for a Q4_K matrix and fp16/bf16 rows (byte
-    offsets of weights and activations within 32 bits)."""
-    if rows < DQ_MIN_ROWS or not (batch >= DQ_MIN_BATCH or (batch >= DQ_MIN_BATCH_LONGK and cols >= DQ_LONGK)):
+def dq_eligible(rows: int, cols: int, batch: int, layout: str) -> bool:
+    """The launcher's dqreg_eligible for a Q4_K matrix and fp16/bf16 rows
+    (byte offsets of weights and activations within 32 bits)."""
+    if rows < DQ_MIN_ROWS or batch < DQ_MIN_BATCH_RUN:
         return False
     nb = cols // 256
     a = -(-16 * rows * nb // 256) * 256  # the plane unit
@@ -119,13 +120,16 @@ def dqreg_plan(rows, cols: int, batch: int, cus: int = DEVICE_CUS):
 
 def dq_run(mats, batch: int, layout: str):
     """How many of the leading matrices (rows, cols) one register-dequantized
-    launch covers: those that route there with the first one's width, up to
-    four (0 if the first does not route there)."""
-    if not mats or not dq_route(mats[0][0], mats[0][1], batch, layout):
+    launch covers: those eligible with the first one's width, up to four; 0
+    if the first is not eligible, or is alone below DQ_MIN_BATCH rows with
+    fewer than DQ_LONGK columns."""
+    if not mats or not dq_eligible(mats[0][0], mats[0][1], batch, layout):
         return 0
     k = 1
-    while k < min(len(mats), 4) and mats[k][1] == mats[0][1] and dq_route(mats[k][0], mats[k][1], batch, layout):
+    while k < min(len(mats), 4) and mats[k][1] == mats[0][1] and dq_eligible(mats[k][0], mats[k][1], batch, layout):
         k += 1
+    if k == 1 and batch < DQ_MIN_BATCH and mats[0][1] < DQ_LONGK:
+        return 0
     return k
 
 

@@ -350,7 +350,9 @@ static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, cons
   // pass per two rows; Q4_K x bf16 above two rows keeps the matrix cores),
   // the wider ones the GEMV once per row; Q4_K x fp16 from five rows takes
   // the matrix cores with fp16 operands (gemm_q4_k_f16_fits).  Every item's
-  // result is the same as that of the item called alone.
+  // result is the same as that of the item called alone, except in runs of
+  // register-dequantized matrices (gemm_q4_k_mfma_items), whose shared K
+  // slicing can change the float32 summation order.
   const bool half_x = x_dtype == QMV_F16 || x_dtype == QMV_BF16;
   const int64_t wave_cols = fmt == QMV_Q8_0 ? 2048 : 4096;
   // Several small Q4_K matrices (the q, k, v of a layer) at 5..16 fp16/bf16

@@ -600,9 +600,8 @@ double dqreg_cost(const int64_t* rows, int n, int64_t batch, int64_t cus, int t,
 
 }  // namespace
 
-bool dqreg_route(const qmv_weights& W, int64_t batch) {
-  if (W.fmt != QMV_Q4_K || W.rows < kDqMinRows) return false;
-  if (batch < kDqMinBatch && !(batch >= kDqMinBatchLongK && W.cols >= kDqLongK)) return false;
+bool dqreg_eligible(const qmv_weights& W, int64_t batch) {
+  if (W.fmt != QMV_Q4_K || W.rows < kDqMinRows || batch < kDqMinBatchRun) return false;
   const uint64_t wbytes = W.layout == QMV_LAYOUT_PLANES ? 5 * W.scales_offset + 64 * (W.rows * (W.cols / 256))
                                                         : 144 * static_cast<uint64_t>(W.rows) * (W.cols / 256);
   return wbytes < (1ull << 32) && 2 * static_cast<uint64_t>(batch) * W.cols < (1ull << 32);
@@ -720,13 +719,17 @@ hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t
   int run[kMaxItems];  // calls in the run starting at i (0 inside a run)
   DqregPlan plans[kMaxItems];
   size_t bytes = 0;
-  for (int i = 0; i < n; ++i) reg[i] = dqreg_route(*calls[i].W, batch);
+  for (int i = 0; i < n; ++i) reg[i] = dqreg_eligible(*calls[i].W, batch);
   for (int i = 0; i < n;) {
     int k = 1;
-    if (reg[i])
+    if (reg[i]) {
       while (i + k < n && k < kDqregMaxMats && reg[i + k] && calls[i + k].x == calls[i].x &&
              calls[i + k].W->cols == calls[i].W->cols && calls[i + k].W->layout == calls[i].W->layout)
         ++k;
+      // a lone matrix below kDqMinBatch rows stays on the tile kernels
+      // unless its K is long
+      if (k == 1 && batch < kDqMinBatch && calls[i].W->cols < kDqLongK) reg[i] = false;
+    }
     run[i] = k;
     for (int j = 1; j < k; ++j) run[i + j] = 0;
     if (reg[i]) {

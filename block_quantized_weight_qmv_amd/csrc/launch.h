@@ -76,19 +76,24 @@ hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t bat
 constexpr int64_t kMfmaMinBatch = QMV_MFMA_MIN_BATCH;
 hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t batch,
                           hipStream_t s);
-// Q4_K x bf16/fp16 batches from kDqMinBatch rows, or from kDqMinBatchLongK
-// rows against matrices of at least kDqLongK columns, against matrices of at
-// least kDqMinRows rows whose byte offsets fit in 32 bits: the
-// register-dequantized kernels (gemm_q4_k_dqreg.hip; dqreg_route).  They
-// round each weight to fp16 (relative error near 2^-11), which the normwise
-// bound absorbs over a matrix of a few hundred rows (about 4e-4 on the 7B
-// FFN shapes) but not over a handful of rows, where one output's
-// cancellation sets the error; smaller matrices keep the exact-product
-// kernels.  Measured against the tile kernels on the 7B FFN shapes (bf16,
-// graph replays): 18944 x 3584 at 64 rows 26 (tile) against 39 us, at 128
-// rows 47 against 45 us; 3584 x 18944 at 64 rows 75 against 63 us, at 128
-// rows 169 against 66 us.
-constexpr int64_t kDqMinBatch = 128, kDqMinBatchLongK = 64, kDqLongK = 8192, kDqMinRows = 256;
+// Q4_K x bf16/fp16 batches on the register-dequantized kernels
+// (gemm_q4_k_dqreg.hip), for matrices of at least kDqMinRows rows whose byte
+// offsets fit in 32 bits (dqreg_eligible): from kDqMinBatchRun rows for runs
+// of two or more consecutive matrices of a launch on the same activations
+// (q+k+v, gate+up: one launch for the run) and for matrices of at least
+// kDqLongK columns, from kDqMinBatch rows for any matrix.  They round each
+// weight to fp16 (relative error near 2^-11), which the normwise bound
+// absorbs over a matrix of a few hundred rows (about 4e-4 on the 7B FFN
+// shapes) but not over a handful of rows, where one output's cancellation
+// sets the error; smaller matrices keep the exact-product kernels.
+// Measured against the tile kernels on the 7B decoder layer (bf16, graph
+// replays, whole layer): 32 rows 149.5 against 108.1 us, 48 rows 197.6
+// against 114.2, 64 rows 153.6 against 120.1, 96 rows 282.1 against 152.7;
+// a lone 3584 x 3584 matrix at 32 rows 12.9 (tile) against 15.5 us, the
+// 18944 x 3584 gate alone at 64 rows 26 (tile) against 39 us; above 64 rows
+// the tile kernels take 128-row tiles (the layer's o at 96 rows 35.7 us
+// against 24.5 at 128 rows on the register kernels).
+constexpr int64_t kDqMinBatch = 65, kDqMinBatchRun = 32, kDqLongK = 8192, kDqMinRows = 256;
 // The activations converted once into a workspace, T 16-row tiles per wave
 // against NB 16-row activation tiles per workgroup, K in `splits` slices of
 // `bps` blocks (partial outputs summed in slice order).
@@ -98,7 +103,7 @@ struct DqregPlan {
 constexpr int kDqregMaxSplits = 8;
 // Matrices one launch of the register-dequantized kernels covers.
 constexpr int kDqregMaxMats = 4;
-bool dqreg_route(const qmv_weights& W, int64_t batch);
+bool dqreg_eligible(const qmv_weights& W, int64_t batch);
 // The plan for n (1..kDqregMaxMats) matrices of rows[i] x cols in one launch.
 DqregPlan dqreg_plan(const int64_t* rows, int n, int64_t cols, int64_t batch);
 size_t dqreg_workspace_bytes(const int64_t* rows, int n, int64_t cols, int64_t batch, const DqregPlan& p);
@@ -109,8 +114,8 @@ size_t dqreg_workspace_bytes(const int64_t* rows, int n, int64_t cols, int64_t b
 hipError_t gemm_q4_k_dqreg_ws(const GemvCall* calls, int n, bool f16x, int64_t batch, const DqregPlan& p, void* ws,
                               bool convert, hipStream_t s);
 // The matrix-core calls of one launch (Q4_K, bf16 or fp16 rows, batch >= 2)
-// in order: each on the register-dequantized kernels when dqreg_route says
-// so (with the workspace of stream s, sized for the largest; runs of
+// in order: each on the register-dequantized kernels where the rules above
+// say so (with the workspace of stream s, sized for the largest; runs of
 // consecutive such calls on the same activations, widths and layout, up to
 // kDqregMaxMats, share one conversion, one product launch and one sum),
 // else on the kernels of gemm_q4_k_bf16 / gemm_q4_k_f16.

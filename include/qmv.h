@@ -222,9 +222,10 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * runs on the matrix cores with fp16 operands (exact products, fp32 sums).  Other Q4_K x bf16 calls with batch >= 2 run the
  * matrix-core path (weights read once for up to 16 activation rows, once per
  * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
- * independent of timing).  From 128 activation rows (from 64 against
- * matrices of 8192 columns and more) against at least 256 weight rows,
- * Q4_K x bf16/fp16 runs the register-dequantized kernels instead: the
+ * independent of timing).  Against matrices of at least 256 weight rows,
+ * from 65 activation rows (from 32 against matrices of 8192 columns and
+ * more, and for runs of matrices in qmv_gemv_multi below), Q4_K x
+ * bf16/fp16 runs the register-dequantized kernels instead: the
  * activations are converted once to fp16 (a bf16 row scaled by the power of
  * two that brings its largest |x| into [2^14, 2^15)), each weight is rounded
  * to fp16 (relative error near 2^-11), so the products are no longer exact;
@@ -286,11 +287,18 @@ typedef struct qmv_gemv_item {
  * (QMV_ERR_UNSUPPORTED otherwise).  Results equal n separate qmv_gemv calls
  * up to float32 summation order; where the calls would take the multi-row
  * GEMV or the matrix-core path, the launch routes each item as its own call
- * would, and results equal bit for bit -- except for two or more Q4_K
+ * would, and results equal bit for bit -- except (1) for two or more Q4_K
  * matrices of at most 4096 columns and 8192 rows in all at 5..16 fp16/bf16
  * rows, which share one multi-row launch (each output row then equals the
  * batch-1 result bit for bit) where a call of one of them alone would take
- * the matrix cores. */
+ * the matrix cores, and (2) from 32 fp16/bf16 rows, for runs of two to four
+ * consecutive Q4_K items of at least 256 rows on the same x pointer, with
+ * the same cols and layout, which share one register-dequantized launch
+ * (one activation conversion, one product kernel, one partial-output sum):
+ * each item meets the same error bound as its own call but may differ from
+ * it -- by the fp16 rounding of the weights where its own call would take
+ * the exact-product kernels (a lone matrix below 65 rows), else by float32
+ * summation order, since the run's K slicing follows all its rows. */
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch,
                        const qmv_gemv_item* items, int32_t n, void* stream);
 

@@ -155,11 +155,11 @@ def test_split_k_small_batches_name_the_split_kernel(config, batch, x_dtype):
                                           (16, "qmv::gemm_q4_k_stream<false, true>"),
                                           (17, "qmv::gemm_q4_k_tile<1, 1, 2, 5, false, true>"),
                                           (64, "qmv::gemm_q4_k_tile<1, 2, 2, 5, false, true>"),
-                                          (100, "qmv::gemm_q4_k_tile<1, 4, 2, 5, false, true>"),
+                                          (65, "qmv::gemm_q4_k_dqreg<"),
                                           (128, "qmv::gemm_q4_k_dqreg<"),
                                           (512, "qmv::gemm_q4_k_dqreg<")])
 def test_q4_k_f16_batches_name_the_f16_matrix_core_kernels(batch, kernel):
-    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (from 128
+    # Q4_K x fp16 from 5 rows: the matrix cores with fp16 operands (from 65
     # rows the register-dequantized kernels, in the form the plan picks)
     names = _library_kernels()
     layout = bench.default_layout(5, batch, "f16")
@@ -203,11 +203,18 @@ def test_dqreg_plan_is_well_formed(rows, cols, batch):
     assert splits == -(-nb // bps)
 
 
-@pytest.mark.parametrize("rows,cols,batch,route", [(18944, 3584, 64, False), (3584, 18944, 64, True),
-                                                   (18944, 3584, 128, True), (300, 768, 400, True),
-                                                   (255, 3584, 512, False), (3584, 18944, 32, False),
-                                                   (3584, 8192, 64, True), (3584, 7936, 64, False)])
-def test_dq_route(rows, cols, batch, route):
-    # from 128 rows, or from 64 against matrices of 8192 columns and more,
-    # against matrices of 256 rows and more
-    assert bench.dq_route(rows, cols, batch, "blocks") == route
+@pytest.mark.parametrize("mats,batch,run", [([(18944, 3584)], 64, 0), ([(3584, 18944)], 64, 1),
+                                           ([(18944, 3584)], 128, 1), ([(300, 768)], 400, 1),
+                                           ([(255, 3584)], 512, 0), ([(3584, 18944)], 32, 1),
+                                           ([(3584, 18944)], 31, 0), ([(3584, 8192)], 64, 1),
+                                           ([(3584, 7936)], 64, 0), ([(18944, 3584)] * 2, 32, 2),
+                                           ([(3584, 3584), (512, 3584), (512, 3584)], 64, 3),
+                                           ([(3584, 3584), (255, 3584), (512, 3584)], 64, 0),
+                                           ([(3584, 3584), (255, 3584), (512, 3584)], 128, 1),
+                                           ([(3584, 3584)] * 5, 256, 4), ([(3584, 3584), (3584, 1024)], 64, 0),
+                                           ([(18944, 3584)], 65, 1), ([(3584, 3584), (3584, 1024)], 96, 1)])
+def test_dq_run(mats, batch, run):
+    # runs of up to four matrices of one width from 32 rows, a lone matrix
+    # from 65 rows (from 32 against 8192 columns and more), matrices of 256
+    # rows and more
+    assert bench.dq_run(mats, batch, "blocks") == run
