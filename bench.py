@@ -74,7 +74,7 @@ DEVICE_CUS = 256
 # matrices of at least DQ_MIN_ROWS rows: from DQ_MIN_BATCH_RUN rows for runs
 # of two or more matrices of a launch and for matrices of at least DQ_LONGK
 # columns, from DQ_MIN_BATCH rows for any matrix.
-DQ_MIN_BATCH, DQ_MIN_BATCH_RUN, DQ_LONGK, DQ_MIN_ROWS = 65, 32, 8192, 256
+DQ_MIN_BATCH, DQ_MIN_BATCH_RUN, DQ_LONGK, DQ_MIN_ROWS = 65, 17, 8192, 256
 
 
 def dq_eligible(rows: int, cols: int, batch: int, layout: str) -> bool:

@@ -87,13 +87,14 @@ hipError_t gemm_q4_k_bf16(const qmv_weights& W, const void* x, float* y, int64_t
 // shapes) but not over a handful of rows, where one output's cancellation
 // sets the error; smaller matrices keep the exact-product kernels.
 // Measured against the tile kernels on the 7B decoder layer (bf16, graph
-// replays, whole layer): 32 rows 149.5 against 108.1 us, 48 rows 197.6
-// against 114.2, 64 rows 153.6 against 120.1, 96 rows 282.1 against 152.7;
+// replays, whole layer): 17 rows 151.1 against 101.5 us, 24 rows 152.3
+// against 103.7, 32 rows 149.5 against 108.1, 48 rows 197.6 against 114.2,
+// 64 rows 153.6 against 120.1, 96 rows 282.1 against 152.7;
 // a lone 3584 x 3584 matrix at 32 rows 12.9 (tile) against 15.5 us, the
 // 18944 x 3584 gate alone at 64 rows 26 (tile) against 39 us; above 64 rows
 // the tile kernels take 128-row tiles (the layer's o at 96 rows 35.7 us
 // against 24.5 at 128 rows on the register kernels).
-constexpr int64_t kDqMinBatch = 65, kDqMinBatchRun = 32, kDqLongK = 8192, kDqMinRows = 256;
+constexpr int64_t kDqMinBatch = 65, kDqMinBatchRun = 17, kDqLongK = 8192, kDqMinRows = 256;
 // The activations converted once into a workspace, T 16-row tiles per wave
 // against NB 16-row activation tiles per workgroup, K in `splits` slices of
 // `bps` blocks (partial outputs summed in slice order).

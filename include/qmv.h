@@ -223,7 +223,7 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * matrix-core path (weights read once for up to 16 activation rows, once per
  * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
  * independent of timing).  Against matrices of at least 256 weight rows,
- * from 65 activation rows (from 32 against matrices of 8192 columns and
+ * from 65 activation rows (from 17 against matrices of 8192 columns and
  * more, and for runs of matrices in qmv_gemv_multi below), Q4_K x
  * bf16/fp16 runs the register-dequantized kernels instead: the
  * activations are converted once to fp16 (a bf16 row scaled by the power of
@@ -291,7 +291,7 @@ typedef struct qmv_gemv_item {
  * matrices of at most 4096 columns and 8192 rows in all at 5..16 fp16/bf16
  * rows, which share one multi-row launch (each output row then equals the
  * batch-1 result bit for bit) where a call of one of them alone would take
- * the matrix cores, and (2) from 32 fp16/bf16 rows, for runs of two to four
+ * the matrix cores, and (2) from 17 fp16/bf16 rows, for runs of two to four
  * consecutive Q4_K items of at least 256 rows on the same x pointer, with
  * the same cols and layout, which share one register-dequantized launch
  * (one activation conversion, one product kernel, one partial-output sum):

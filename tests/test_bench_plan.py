@@ -205,8 +205,8 @@ def test_dqreg_plan_is_well_formed(rows, cols, batch):
 
 @pytest.mark.parametrize("mats,batch,run", [([(18944, 3584)], 64, 0), ([(3584, 18944)], 64, 1),
                                            ([(18944, 3584)], 128, 1), ([(300, 768)], 400, 1),
-                                           ([(255, 3584)], 512, 0), ([(3584, 18944)], 32, 1),
-                                           ([(3584, 18944)], 31, 0), ([(3584, 8192)], 64, 1),
+                                           ([(255, 3584)], 512, 0), ([(3584, 18944)], 17, 1),
+                                           ([(3584, 18944)], 16, 0), ([(3584, 8192)], 64, 1),
                                            ([(3584, 7936)], 64, 0), ([(18944, 3584)] * 2, 32, 2),
                                            ([(3584, 3584), (512, 3584), (512, 3584)], 64, 3),
                                            ([(3584, 3584), (255, 3584), (512, 3584)], 64, 0),
@@ -214,7 +214,7 @@ def test_dqreg_plan_is_well_formed(rows, cols, batch):
                                            ([(3584, 3584)] * 5, 256, 4), ([(3584, 3584), (3584, 1024)], 64, 0),
                                            ([(18944, 3584)], 65, 1), ([(3584, 3584), (3584, 1024)], 96, 1)])
 def test_dq_run(mats, batch, run):
-    # runs of up to four matrices of one width from 32 rows, a lone matrix
-    # from 65 rows (from 32 against 8192 columns and more), matrices of 256
+    # runs of up to four matrices of one width from 17 rows, a lone matrix
+    # from 65 rows (from 17 against 8192 columns and more), matrices of 256
     # rows and more
     assert bench.dq_run(mats, batch, "blocks") == run

@@ -160,10 +160,10 @@ def test_multi_small_q4_k_matrices_share_one_multi_row_launch(x_dtype, batch):
         assert np.all(oracle.normwise_rel_err(got, oracle_y(w, x_np, x_dtype)) <= TOL)
 
 
-@pytest.mark.parametrize("x_dtype,batch", [("bf16", 32), ("bf16", 128), ("f16", 64), ("bf16", 300)])
+@pytest.mark.parametrize("x_dtype,batch", [("bf16", 17), ("bf16", 32), ("bf16", 128), ("f16", 64), ("bf16", 300)])
 def test_multi_register_dequantized_runs(x_dtype, batch):
     """Consecutive Q4_K items of at least 256 rows on one activation share one
-    register-dequantized launch from 32 rows (a q+k+v-like run of three, then
+    register-dequantized launch from 17 rows (a q+k+v-like run of three, then
     a lone matrix of another width that runs alone): every item meets the
     oracle gate, as its own call does (below 65 rows a lone call of these
     matrices takes the exact-product kernels, so the two differ by the fp16

@@ -31,7 +31,7 @@ pytestmark = pytest.mark.gpu
 PLANS = [(1, None, None), (2, None, None), (3, None, None), (4, None, None), (6, None, None),
          (5, 1, None), (5, 4, None), (5, 16, None), (5, 64, None), (5, 256, None), (5, 512, None),
          (3, 8, "bf16"), (3, 8, "f16"), (5, 512, "f16"), (5, 100, "f16"), (2, 4, None), (3, 256, "bf16"),
-         (3, 32, "bf16"), (3, 64, "bf16"), (3, 128, "f16"), (3, 512, "bf16"), (5, 32, None)]
+         (3, 17, "bf16"), (3, 32, "bf16"), (3, 64, "bf16"), (3, 128, "f16"), (3, 512, "bf16"), (5, 32, None)]
 
 
 def _dispatched(trace_dir):
