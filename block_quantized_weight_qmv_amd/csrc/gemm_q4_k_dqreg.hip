@@ -8,20 +8,25 @@
 // tens of activation rows, it is cheaper to convert it to the matrix-core
 // type once than to apply its scales to every product.
 //
-// Three kernels per call, in stream order:
-// 1. act_rows_f16: the activations to fp16 once, into the workspace: bf16
+// Three kernels per run of one to four matrices on the same activations
+// (the consecutive items of a multi-matrix launch, e.g. q+k+v), in stream
+// order:
+// 1. act_rows_f16: the activations to fp16 once, into the workspace (not
+//    again for a following run on the same activations): bf16
 //    rows scaled by a power of two 2^-e per row (e from the row's largest
 //    |x|, which lands in [2^14, 2^15)), fp16 rows as given; each group of
 //    eight columns in the operand order (0, 2, 1, 3, 4, 6, 5, 7) below.
-// 2. gemm_q4_k_dqreg: the products over one of S slices of K (whole
-//    256-column blocks); with S = 1 straight into y, else into S partial
-//    outputs in the workspace.  Results are multiplied by 2^e at the end.
+// 2. gemm_q4_k_dqreg: the products of every matrix of the run (each
+//    workgroup finds its matrix by its row tile) over one of S slices of K
+//    (whole 256-column blocks); with S = 1 straight into y, else into S
+//    partial outputs in the workspace.  Results are multiplied by 2^e at the
+//    end.
 // 3. (S > 1) dqreg_sum: y = the sum of the partial outputs in slice order,
 //    so results are independent of timing.
 //
 // Workgroup: four waves, one per SIMD.  Wave w owns 16 T consecutive weight
-// rows (T tiles of 16) and all 16 NB activation rows of the workgroup's batch
-// tile.  Each wave dequantizes its own weight tiles straight into A operand
+// rows (T tiles of 16, T = 1..5) and all 16 NB activation rows of the
+// workgroup's batch tile (NB = 4 or 8).  Each wave dequantizes its own weight tiles straight into A operand
 // registers: weights never pass through LDS and are converted once.  The
 // fp16 activation tile is copied into LDS per half block (no arithmetic),
 // where all four waves read it as B operands.  Per 32-column step a wave
@@ -30,10 +35,11 @@
 // What sets the time (gfx950, measured): one wave issues about two
 // independent VALU instructions under each 16-cycle product for free; beyond
 // that the VALU issue sets the pace.  Forming an A operand costs about 16
-// VALU instructions (two per product at NB = 8).  Each B operand read (1 KB
-// per wave) serves T products, so T = 1 leaves the four waves bound by LDS
-// bandwidth.  The host picks T and S per shape from a model fitted to such
-// measurements and from how many workgroups fill the compute units.
+// VALU instructions (two per product at NB = 8, four at NB = 4).  Each B
+// operand read (1 KB per wave) serves T products, so T = 1 leaves the four
+// waves bound by LDS bandwidth.  The host picks T, NB and S per run from a
+// model fitted to such measurements and from how many workgroups fill the
+// compute units.
 //
 // K order.  A block is walked in two halves of four steps, half h covering
 // columns 128 h .. 128 h + 128 (code chunks c = 2h and 2h + 1: sub-blocks
