@@ -124,13 +124,13 @@ __device__ __forceinline__ uint32_t rg_pack(_Float16 a, _Float16 b) {
 // largest lands in [2^14, 2^15), so no value overflows fp16 and values down
 // to 2^-24 of the largest keep full fp16 precision; each value is rounded to
 // nearest once.  e = 0 for an all-zero row; e stays within [-126, 127].  One
-// workgroup per row; rows of up to 16384 columns are read once and held in
+// workgroup per row; rows of up to 20480 columns are read once and held in
 // registers for both the maximum and the conversion, longer ones are read
 // twice (the second time from L2).  K a multiple of 8, x and out 16-byte
 // aligned.
 template <bool BF16>
 __global__ void __launch_bounds__(256) act_rows_f16(const uint16_t* x, int K, uint16_t* out, float* scale) {
-  constexpr int kHeld = 8;  // 16-byte pieces a thread keeps between the two passes (rows up to 16384 columns)
+  constexpr int kHeld = 10;  // 16-byte pieces a thread keeps between the two passes (rows up to 20480 columns)
   __shared__ int wmax[4];
   const int tid = static_cast<int>(threadIdx.x), lane = tid & 63;
   const int row = static_cast<int>(blockIdx.x);
