@@ -9,8 +9,9 @@ timed region starts.  Distinct copies of the layer (>= 1.25 GiB in total) are
 cycled so that the 256 MB Infinity Cache cannot serve repeated reads.
 
 The step issues the layer's GEMVs in decode order, one launch per group of
-projections that read the same activation (qmv_gemv_multi): [q, k, v], [o],
-[gate, up], [down].  `--separate` issues one qmv_gemv per matrix instead.
+projections that read the same activation (qmv_gemv_multi_ws, with one
+caller-owned workspace sized by qmv_workspace_size): [q, k, v], [o],
+[gate, up], [down].  `--separate` issues one launch per matrix instead.
 
 Output: one JSON line.  `value` is algorithmic bytes (packed weights + x + y)
 per step divided by the measured time per step.  `roofline` covers the
@@ -903,14 +904,16 @@ def main() -> int:
     stream = torch.cuda.current_stream(dev)
     sp = stream.cuda_stream
 
+    # one workspace for every launch of the step (they run in stream order),
+    # sized for the launch that needs the most; allocated before any capture
+    ws_bytes = max(qmv.qmv_workspace_size(fmt, x_dtype, batch,
+                                          [(descs[0][m], xs_dev[m], ys[m]) for m in g])
+                   for g in groups)
+    ws = torch.empty(max(ws_bytes, 1), dtype=torch.uint8, device=dev)
+
     def launch(c, g, sptr):
-        if len(g) == 1:
-            m = g[0]
-            _, rows, cols = mats[m]
-            qmv.qmv_gemv(fmt, descs[c][m], xs_dev[m], x_dtype, ys[m], rows, cols, batch, sptr)
-        else:
-            qmv.qmv_gemv_multi(fmt, x_dtype, batch,
-                               [(descs[c][m], xs_dev[m], ys[m]) for m in g], sptr)
+        qmv.qmv_gemv_multi_ws(fmt, x_dtype, batch, [(descs[c][m], xs_dev[m], ys[m]) for m in g],
+                              ws, ws_bytes, sptr)
 
     # dominant kernel (plan["dom"]): the instantiation with the most algorithmic
     # bytes per step
@@ -937,11 +940,6 @@ def main() -> int:
     # rotation over weight copies and the launch order are unchanged -> its average
     # launch duration (the duration plus the small gap between graph nodes).
     cap = torch.cuda.Stream(dev)
-    # one eager step on the capture stream first: the batched kernels keep a
-    # workspace per stream, which is allocated outside graph capture
-    for g in groups:
-        launch(0, g, cap.cuda_stream)
-    torch.cuda.synchronize()
     spread = []   # (min, median, max) ms of each timed region's replays
 
     def timed_graph(gis):

@@ -10,8 +10,7 @@
 #include <stdarg.h>
 #include <stdio.h>
 
-#include <mutex>
-#include <vector>
+#include <algorithm>
 
 #include <hip/hip_runtime.h>
 
@@ -38,51 +37,21 @@ int32_t ok() {
 
 static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
-// Workspaces of the batched kernels, one per (device, stream).  Calls on one
-// stream run in order, so its workspace is never used by two calls at once;
-// calls on different streams never share one.  A workspace that grows is
-// replaced, not freed: graphs captured earlier keep valid addresses.
-namespace {
-struct Workspace {
-  int dev;
-  hipStream_t stream;
+// How a launch gets the workspace of the register-dequantized kernels: none
+// (those kernels are not used), the caller's buffer, or the library's fixed
+// scratch; with `need` set, nothing is launched and the bytes the launch
+// needs are stored there.
+struct WsMode {
   void* ptr;
-  size_t bytes;
+  uint64_t bytes;
+  bool fixed;
+  uint64_t* need;
 };
-std::mutex g_ws_mu;
-std::vector<Workspace> g_ws;
-}  // namespace
 
-hipError_t workspace(hipStream_t s, size_t bytes, void** out) {
-  int dev = 0;
-  hipError_t e = hipGetDevice(&dev);
-  if (e != hipSuccess) return e;
-  std::lock_guard<std::mutex> lock(g_ws_mu);
-  Workspace* ws = nullptr;
-  for (Workspace& w : g_ws)
-    if (w.dev == dev && w.stream == s) ws = &w;
-  if (ws && ws->bytes >= bytes) {
-    *out = ws->ptr;
-    return hipSuccess;
-  }
-  hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
-  e = hipStreamIsCapturing(s, &cap);
-  if (e != hipSuccess) return e;
-  if (cap != hipStreamCaptureStatusNone) return hipErrorStreamCaptureUnsupported;
-  const size_t grow = ws ? 2 * bytes : bytes;
-  const size_t want = (grow + (2u << 20) - 1) / (2u << 20) * (2u << 20);
-  void* p = nullptr;
-  e = hipMalloc(&p, want);
-  if (e != hipSuccess) return e;
-  if (ws) {
-    ws->ptr = p;
-    ws->bytes = want;
-  } else {
-    g_ws.push_back(Workspace{dev, s, p, want});
-  }
-  *out = p;
-  return hipSuccess;
-}
+// The workspace for a launch that needs `need` bytes of it (nullptr: the
+// register-dequantized kernels are not used).  Fails before any launch when
+// the caller's buffer or the fixed scratch is too small.
+static int32_t take_workspace(const WsMode& ws, uint64_t need, void** out);
 
 static int32_t from_hip(hipError_t e, const char* what) {
   if (e == hipSuccess) return ok();
@@ -133,6 +102,32 @@ static int32_t check_weights(const qmv_weights* W) {
 }  // namespace qmv
 
 using qmv::fail;
+
+namespace qmv {
+
+static int32_t take_workspace(const WsMode& ws, uint64_t need, void** out) {
+  if (out) *out = nullptr;
+  if (ws.need) {
+    *ws.need = need;
+    return ok();
+  }
+  if (need == 0) return ok();
+  if (ws.fixed) {
+    if (need > kScratchBytes)
+      return fail(QMV_ERR_SIZE, "qmv_gemv_noalloc: this call needs %llu bytes of workspace, more than the %llu "
+                                "of the library's fixed scratch (fewer activation rows fit)",
+                  (unsigned long long)need, (unsigned long long)kScratchBytes);
+    return from_hip(scratch_workspace(need, out), "qmv_gemv_noalloc: scratch lookup");
+  }
+  if (!ws.ptr) return ok();  // no workspace: the exact-product kernels
+  if (ws.bytes < need)
+    return fail(QMV_ERR_SIZE, "workspace holds %llu bytes, this launch needs %llu (qmv_workspace_size)",
+                (unsigned long long)ws.bytes, (unsigned long long)need);
+  *out = ws.ptr;
+  return ok();
+}
+
+}  // namespace qmv
 
 extern "C" {
 
@@ -265,10 +260,8 @@ int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x, int32_t x_dty
   return qmv_gemv_multi(fmt, x_dtype, batch, &item, 1, stream);
 }
 
-// qmv_gemv_multi; with fixed_scratch the batched kernels take the library's
-// fixed scratch instead of the stream's workspace (nothing is allocated).
 static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
-                               int32_t n, void* stream, bool fixed_scratch);
+                               int32_t n, void* stream, const qmv::WsMode& ws);
 
 int32_t qmv_gemv_noalloc(int32_t fmt, const qmv_weights* W, const void* x, int32_t x_dtype, float* y,
                          int64_t rows, int64_t cols, int64_t batch, void* stream) {
@@ -278,27 +271,36 @@ int32_t qmv_gemv_noalloc(int32_t fmt, const qmv_weights* W, const void* x, int32
                 fmt, (long long)rows, (long long)cols, W->fmt, (long long)W->rows,
                 (long long)W->cols);
   const qmv_gemv_item item{W, x, y};
-  return gemv_multi_impl(fmt, x_dtype, batch, &item, 1, stream, true);
+  return gemv_multi_impl(fmt, x_dtype, batch, &item, 1, stream, qmv::WsMode{nullptr, 0, true, nullptr});
 }
 
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
                        int32_t n, void* stream) {
-  return gemv_multi_impl(fmt, x_dtype, batch, items, n, stream, false);
+  return gemv_multi_impl(fmt, x_dtype, batch, items, n, stream, qmv::WsMode{nullptr, 0, false, nullptr});
 }
 
-static int32_t batched_status(hipError_t e, bool fixed_scratch) {
-  if (e == hipErrorStreamCaptureUnsupported)
-    return fail(QMV_ERR_HIP, "qmv_gemv: the workspace of this stream must grow, which cannot happen "
-                             "under stream capture: make the same call once before capturing");
-  if (fixed_scratch && e == hipErrorOutOfMemory)
-    return fail(QMV_ERR_SIZE, "qmv_gemv_noalloc: this call needs more than the %llu bytes of the "
-                              "library's fixed scratch (fewer activation rows fit)",
-                (unsigned long long)qmv::kScratchBytes);
-  return qmv::from_hip(e, "qmv_gemv (batched matrix-core) launch");
+int32_t qmv_gemv_multi_ws(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
+                          int32_t n, void* workspace, uint64_t workspace_bytes, void* stream) {
+  if (workspace_bytes && !workspace) return fail(QMV_ERR_NULL, "workspace is NULL");
+  if (workspace && (reinterpret_cast<uintptr_t>(workspace) & 255u))
+    return fail(QMV_ERR_ALIGN, "workspace not 256-byte aligned");
+  return gemv_multi_impl(fmt, x_dtype, batch, items, n, stream,
+                         qmv::WsMode{workspace, workspace_bytes, false, nullptr});
+}
+
+int32_t qmv_workspace_size(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
+                           int32_t n, uint64_t* bytes) {
+  if (!bytes) return fail(QMV_ERR_NULL, "bytes is NULL");
+  *bytes = 0;
+  uint64_t need = 0;
+  const int32_t st =
+      gemv_multi_impl(fmt, x_dtype, batch, items, n, nullptr, qmv::WsMode{nullptr, 0, false, &need});
+  if (st == QMV_OK) *bytes = need;
+  return st;
 }
 
 static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, const qmv_gemv_item* items,
-                               int32_t n, void* stream, bool fixed_scratch) {
+                               int32_t n, void* stream, const qmv::WsMode& ws) {
   if (!items) return fail(QMV_ERR_NULL, "items is NULL");
   if (n < 1) return fail(QMV_ERR_SHAPE, "item count %d < 1", n);
   if (n > qmv::kMaxItems)
@@ -367,9 +369,11 @@ static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, cons
       small = small && items[i].W->cols <= wave_cols;
       rows_sum += items[i].W->rows;
     }
-    if (small && rows_sum <= qmv::kRowsSmallMultiMaxRows)
+    if (small && rows_sum <= qmv::kRowsSmallMultiMaxRows) {
+      if (ws.need) return qmv::take_workspace(ws, 0, nullptr);
       return qmv::from_hip(qmv::gemv_q4_k_rows(calls, n, x_dtype, batch, planes, s),
                            "qmv_gemv (multi-row, several matrices) launch");
+    }
   }
   if (batch >= 2 &&
       !(fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch > qmv::kRowsMaxBf16Batch)) {
@@ -402,16 +406,18 @@ static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, cons
         default: return qmv::gemv_int4_g128_rows(c, k, x_dtype, batch, s);
       }
     };
+    // the register-dequantized kernels' workspace, checked before any launch
+    const uint64_t need = std::max(nm ? qmv::gemm_q4_k_mfma_items_workspace(mfma16, nm, batch) : 0,
+                                   q4k_mfma && nw ? qmv::gemm_q4_k_mfma_items_workspace(wide, nw, batch) : 0);
+    void* wsp = nullptr;
+    const int32_t wst = qmv::take_workspace(ws, need, &wsp);
+    if (wst != QMV_OK || ws.need) return wst;
     if (nn) e = rows(narrow, nn);
     if (e == hipSuccess && ns) e = rows(split, ns);
-    if (e == hipSuccess && nm) {
-      e = qmv::gemm_q4_k_mfma_items(mfma16, nm, true, batch, s, fixed_scratch);
-      if (e != hipSuccess) return batched_status(e, fixed_scratch);
-    }
+    if (e == hipSuccess && nm) e = qmv::gemm_q4_k_mfma_items(mfma16, nm, true, batch, s, wsp);
     if (e == hipSuccess && nw) {
       if (q4k_mfma) {
-        e = qmv::gemm_q4_k_mfma_items(wide, nw, false, batch, s, fixed_scratch);
-        if (e != hipSuccess) return batched_status(e, fixed_scratch);
+        e = qmv::gemm_q4_k_mfma_items(wide, nw, false, batch, s, wsp);
       } else {
         switch (fmt) {
           case QMV_Q4_K:
@@ -434,9 +440,13 @@ static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, cons
     return qmv::from_hip(e, "qmv_gemv (multi-row) launch");
   }
   if (fmt == QMV_Q4_K && x_dtype == QMV_BF16 && batch >= qmv::kMfmaMinBatch) {
-    e = qmv::gemm_q4_k_mfma_items(calls, n, false, batch, s, fixed_scratch);
-    return batched_status(e, fixed_scratch);
+    void* wsp = nullptr;
+    const int32_t st = qmv::take_workspace(ws, qmv::gemm_q4_k_mfma_items_workspace(calls, n, batch), &wsp);
+    if (st != QMV_OK || ws.need) return st;
+    return qmv::from_hip(qmv::gemm_q4_k_mfma_items(calls, n, false, batch, s, wsp),
+                         "qmv_gemv (matrix-core) launch");
   }
+  if (ws.need) return qmv::take_workspace(ws, 0, nullptr);
   switch (fmt) {
     case QMV_Q8_0: e = qmv::gemv_q8_0(calls, n, x_dtype, batch, s); break;
     case QMV_Q4_K:

@@ -716,14 +716,13 @@ hipError_t scratch_workspace(size_t bytes, void** out) {
   return hipSuccess;
 }
 
-hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t stream,
-                                bool fixed_scratch) {
-  // runs of consecutive register-dequantized calls on the same activations
-  // and widths (up to kDqregMaxMats) share one conversion, one product
-  // launch and one sum launch
-  bool reg[kMaxItems];
-  int run[kMaxItems];  // calls in the run starting at i (0 inside a run)
-  DqregPlan plans[kMaxItems];
+namespace {
+
+// The register-dequantized runs of a launch's matrix-core calls: reg[i] for
+// calls on those kernels, run[i] the calls in the run starting at i (0 inside
+// a run), plans[i] its plan; returns the workspace bytes the runs need (they
+// run one after another in one workspace).
+size_t plan_runs(const GemvCall* calls, int n, int64_t batch, bool* reg, int* run, DqregPlan* plans) {
   size_t bytes = 0;
   for (int i = 0; i < n; ++i) reg[i] = dqreg_eligible(*calls[i].W, batch);
   for (int i = 0; i < n;) {
@@ -746,10 +745,34 @@ hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t
     }
     i += k;
   }
-  void* ws = nullptr;
-  if (bytes) {
-    const hipError_t e = fixed_scratch ? scratch_workspace(bytes, &ws) : workspace(stream, bytes, &ws);
-    if (e != hipSuccess) return e;
+  return bytes;
+}
+
+}  // namespace
+
+size_t gemm_q4_k_mfma_items_workspace(const GemvCall* calls, int n, int64_t batch) {
+  bool reg[kMaxItems];
+  int run[kMaxItems];
+  DqregPlan plans[kMaxItems];
+  return plan_runs(calls, n, batch, reg, run, plans);
+}
+
+hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t stream,
+                                void* ws) {
+  // runs of consecutive register-dequantized calls on the same activations
+  // and widths (up to kDqregMaxMats) share one conversion, one product
+  // launch and one sum launch; without a workspace every call takes the
+  // kernels of gemm_q4_k_bf16 / gemm_q4_k_f16
+  bool reg[kMaxItems];
+  int run[kMaxItems];
+  DqregPlan plans[kMaxItems];
+  if (ws) {
+    plan_runs(calls, n, batch, reg, run, plans);
+  } else {
+    for (int i = 0; i < n; ++i) {
+      reg[i] = false;
+      run[i] = 1;
+    }
   }
   hipError_t e = hipSuccess;
   const GemvCall* converted = nullptr;  // the run whose activations the workspace holds

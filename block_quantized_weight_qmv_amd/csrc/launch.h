@@ -115,26 +115,21 @@ size_t dqreg_workspace_bytes(const int64_t* rows, int n, int64_t cols, int64_t b
 hipError_t gemm_q4_k_dqreg_ws(const GemvCall* calls, int n, bool f16x, int64_t batch, const DqregPlan& p, void* ws,
                               bool convert, hipStream_t s);
 // The matrix-core calls of one launch (Q4_K, bf16 or fp16 rows, batch >= 2)
-// in order: each on the register-dequantized kernels where the rules above
-// say so (with the workspace of stream s, sized for the largest; runs of
-// consecutive such calls on the same activations, widths and layout, up to
-// kDqregMaxMats, share one conversion, one product launch and one sum),
-// else on the kernels of gemm_q4_k_bf16 / gemm_q4_k_f16.
-// With fixed_scratch, the workspace is the library's fixed device array of
-// kScratchBytes (scratch_workspace) and nothing is allocated; a call that
-// needs more fails with hipErrorOutOfMemory before any launch.
-hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t s,
-                                bool fixed_scratch = false);
+// in order: with a device workspace ws (gemm_q4_k_mfma_items_workspace
+// bytes, 256-byte aligned), each on the register-dequantized kernels where
+// the rules above say so (runs of consecutive such calls on the same
+// activations, widths and layout, up to kDqregMaxMats, share one
+// conversion, one product launch and one sum), else on the kernels of
+// gemm_q4_k_bf16 / gemm_q4_k_f16; without one (ws = nullptr), every call on
+// the latter.
+hipError_t gemm_q4_k_mfma_items(const GemvCall* calls, int n, bool f16x, int64_t batch, hipStream_t s, void* ws);
+// Workspace bytes gemm_q4_k_mfma_items needs for these calls (0: none).
+size_t gemm_q4_k_mfma_items_workspace(const GemvCall* calls, int n, int64_t batch);
+// The fixed device array of qmv_gemv_noalloc, QMV_NOALLOC_SCRATCH_BYTES,
+// on the current device (its address looked up once per device).
 constexpr size_t kScratchBytes = QMV_NOALLOC_SCRATCH_BYTES;
-// The fixed device array of kScratchBytes on the current device (its
-// address looked up once per device); hipErrorOutOfMemory above that size.
 hipError_t scratch_workspace(size_t bytes, void** out);
-// Device workspace for stream s on the current device: at least `bytes`,
-// 256-byte aligned, one per (device, stream), kept until the process ends.
-// Growing it (hipMalloc of a new one; the old one stays allocated, so
-// graphs captured with it stay valid) is refused while s is capturing
-// (hipErrorStreamCaptureUnsupported).
-hipError_t workspace(hipStream_t s, size_t bytes, void** out);
+
 // Q4_K x fp16 on the matrix cores with fp16 operands: the kernels of the
 // bf16 path (streaming or K-split up to 16 rows, tiles from 17).  qmv_gemv
 // takes it from kMfmaMinF16Batch rows; below, the multi-row GEMV is faster.

@@ -67,6 +67,9 @@ _SIGS = {
     "qmv_gemv": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
     "qmv_gemv_noalloc": (_i32, [_i32, ctypes.POINTER(QmvWeights), _p, _i32, _p, _i64, _i64, _i64, _p]),
     "qmv_gemv_multi": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32, _p]),
+    "qmv_workspace_size": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32,
+                                  ctypes.POINTER(_u64)]),
+    "qmv_gemv_multi_ws": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32, _p, _u64, _p]),
     "qmv_dequant": (_i32, [ctypes.POINTER(QmvWeights), _p, _i32, _p]),
     "qmv_probe_read_outputs": (_i64, [_u64]),
     "qmv_probe_read": (_i32, [_p, _u64, _p, _p]),
@@ -303,19 +306,47 @@ def qmv_gemv_noalloc(fmt, W: QmvWeights, x, x_dtype, y, rows: int, cols: int, ba
                                   rows, cols, batch, _stream(stream, x, y)))
 
 
-def qmv_gemv_multi(fmt, x_dtype, batch: int, items, stream=None) -> None:
-    """items: sequence of (QmvWeights, x, y) triples; one launch for all of them."""
+def _items(x_dtype, batch: int, items, check: bool = True):
     arr = (QmvGemvItem * max(1, len(items)))()
     xd = _dtype(x_dtype)
     for i, (W, x, y) in enumerate(items):
-        _check_dev(x, f"item {i} x", xd, batch * W.cols)
-        _check_dev(y, f"item {i} y", 0, batch * W.rows)
+        if check:
+            _check_dev(x, f"item {i} x", xd, batch * W.cols)
+            _check_dev(y, f"item {i} y", 0, batch * W.rows)
         arr[i].W = ctypes.pointer(W)
         arr[i].x = _ptr(x)
         arr[i].y = _ptr(y)
+    return arr
+
+
+def qmv_gemv_multi(fmt, x_dtype, batch: int, items, stream=None) -> None:
+    """items: sequence of (QmvWeights, x, y) triples; one launch for all of them."""
+    arr = _items(x_dtype, batch, items)
     tensors = [t for _, x, y in items for t in (x, y)]
     _check(lib().qmv_gemv_multi(_fmt(fmt), _dtype(x_dtype), batch, arr, len(items),
                                 _stream(stream, *tensors)))
+
+
+def qmv_workspace_size(fmt, x_dtype, batch: int, items) -> int:
+    """Bytes of workspace qmv_gemv_multi_ws needs for these items (0: none)."""
+    arr = _items(x_dtype, batch, items, check=False)
+    n = _u64(0)
+    _check(lib().qmv_workspace_size(_fmt(fmt), _dtype(x_dtype), batch, arr, len(items),
+                                    ctypes.byref(n)))
+    return int(n.value)
+
+
+def qmv_gemv_multi_ws(fmt, x_dtype, batch: int, items, workspace, workspace_bytes: int,
+                      stream=None) -> None:
+    """qmv_gemv_multi with a caller-owned device workspace (None: no workspace)."""
+    arr = _items(x_dtype, batch, items)
+    tensors = [t for _, x, y in items for t in (x, y)]
+    if workspace is not None:
+        _check_dev(workspace, "workspace", None, workspace_bytes)
+        tensors.append(workspace)
+    _check(lib().qmv_gemv_multi_ws(_fmt(fmt), _dtype(x_dtype), batch, arr, len(items),
+                                   _ptr(workspace) if workspace is not None else None,
+                                   workspace_bytes, _stream(stream, *tensors)))
 
 
 def qmv_dequant(W: QmvWeights, out, out_dtype, stream=None) -> None:

@@ -4,8 +4,11 @@
  * C ABI of libqmv.so.  Plain C types only: integers, sizes and pointers.
  * Device pointers come from the caller (for example torch tensors'
  * data_ptr()); the library allocates no memory, creates no stream and never
- * synchronizes.  `stream` arguments are hipStream_t values passed as void*
- * (NULL = the legacy default stream).
+ * synchronizes (its one device array, the fixed scratch of qmv_gemv_noalloc,
+ * is part of the loaded code object).  Workspace, where a kernel needs one,
+ * comes from the caller too (qmv_workspace_size, qmv_gemv_multi_ws).
+ * `stream` arguments are hipStream_t values passed as void* (NULL = the
+ * legacy default stream).
  *
  * Operation (what every entry point computes):
  *   W is a rows x cols matrix stored as blocks of quantized codes plus
@@ -212,50 +215,35 @@ int32_t qmv_create_weights(int32_t fmt, int64_t rows, int64_t cols,
  * fmt, rows and cols must repeat the descriptor's (QMV_ERR_FORMAT otherwise),
  * x is [batch][cols] of x_dtype (QMV_F32, QMV_F16 or QMV_BF16), y is
  * [batch][rows] fp32; x and y device pointers, 16-byte aligned.  Enqueues on
- * `stream` and returns; legal inside HIP stream capture (see the workspace
- * of the register-dequantized kernels below).  batch >= 2 rows
+ * `stream` and returns; legal inside HIP stream capture.  batch >= 2 rows
  * (Q4_K x bf16: 2..4 rows) run the multi-row GEMV in every format: weights
  * read once per two or four activation rows (fp32: two) for cols <= 4096
  * (Q8_0: 2048), and, for fp16/bf16 rows, once per two rows up to eight times
  * that width (Q4_K x bf16: at two rows); each output row equals bit for bit
  * the batch-1 call on that activation row.  Q4_K x fp16 with 5 or more rows
- * runs on the matrix cores with fp16 operands (exact products, fp32 sums).  Other Q4_K x bf16 calls with batch >= 2 run the
- * matrix-core path (weights read once for up to 16 activation rows, once per
- * tile of 32, 64 or 128 rows above; exact products, fp32 sums, results
- * independent of timing).  Against matrices of at least 256 weight rows,
- * from 65 activation rows (from 17 against matrices of 8192 columns and
- * more, and for runs of matrices in qmv_gemv_multi below), Q4_K x
- * bf16/fp16 runs the register-dequantized kernels instead: the
- * activations are converted once to fp16 (a bf16 row scaled by the power of
- * two that brings its largest |x| into [2^14, 2^15)), each weight is rounded
- * to fp16 (relative error near 2^-11), so the products are no longer exact;
- * the normwise bound still holds over such matrices (about 4e-4 on the 7B
- * FFN shapes).  K may be cut into slices whose partial outputs are summed in
- * a fixed order, so results stay independent of timing.  These kernels use
- * a device workspace per (device, stream) that the library allocates
- * (hipMalloc) on the first call that needs it, or a larger one, and keeps
- * until the process ends (a grown-out one included, so graphs captured with
- * it stay valid); the converted activations and partial outputs go there.
- * Under stream capture it cannot be allocated: such a call fails with
- * QMV_ERR_HIP unless the same or a larger call ran on that stream before
- * the capture.  Graphs captured on one stream share its workspace: replay
- * them in order on one stream.  Otherwise each activation row is a GEMV over the
- * packed weights.  Q4_K, Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the
- * same arithmetic, in the same order, as the canonical layout on every one
- * of these paths, so results equal bit for bit. */
+ * runs on the matrix cores with fp16 operands (exact products, fp32 sums).
+ * Other Q4_K x bf16 calls with batch >= 2 run the matrix-core path (weights
+ * read once for up to 16 activation rows, once per tile of 32, 64 or 128
+ * rows above; exact products, fp32 sums, results independent of timing).
+ * Otherwise each activation row is a GEMV over the packed weights.  Q4_K,
+ * Q5_K and Q6_K weights in QMV_LAYOUT_PLANES run the same arithmetic, in the
+ * same order, as the canonical layout on every one of these paths, so
+ * results equal bit for bit.  This call uses no workspace; the faster
+ * register-dequantized kernels for large batches need one and run through
+ * qmv_gemv_multi_ws (or qmv_gemv_noalloc). */
 int32_t qmv_gemv(int32_t fmt, const qmv_weights* W, const void* x,
                  int32_t x_dtype, float* y, int64_t rows, int64_t cols,
                  int64_t batch, void* stream);
 
 /* qmv_gemv for callers that cannot allocate device memory (code under HIP
- * graph capture, tight serving loops, harnesses that forbid hipMalloc):
- * the same arguments, checks, kernels and results, bit for bit, as
- * qmv_gemv, but where the register-dequantized kernels need a workspace they
- * take the library's fixed device array of QMV_NOALLOC_SCRATCH_BYTES
- * (64 MiB, one per GPU, held from library load until the process ends)
- * instead of allocating one; no path of this call allocates.  A call whose
- * workspace would exceed it (activation rows x cols x 2 bytes, plus row
- * scales and up to 8 partial outputs of rows x batch floats) fails with
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc) and
+ * have no workspace to give: the same arguments and checks as qmv_gemv and
+ * the kernels and results, bit for bit, of qmv_gemv_multi_ws with this one
+ * item and a large enough workspace -- but the register-dequantized
+ * kernels take the library's fixed device array of QMV_NOALLOC_SCRATCH_BYTES
+ * (64 MiB, one per GPU, held from library load until the process ends) as
+ * their workspace.  No path of this call allocates.  A call whose workspace
+ * (qmv_workspace_size of that item) would exceed the array fails with
  * QMV_ERR_SIZE before any launch; the 7B decoder layer's matrices fit up to
  * 512 activation rows.  Nothing in the array needs to start at zero.  Every
  * call on one GPU shares the array and leaves it holding its own
@@ -287,20 +275,57 @@ typedef struct qmv_gemv_item {
  * (QMV_ERR_UNSUPPORTED otherwise).  Results equal n separate qmv_gemv calls
  * up to float32 summation order; where the calls would take the multi-row
  * GEMV or the matrix-core path, the launch routes each item as its own call
- * would, and results equal bit for bit -- except (1) for two or more Q4_K
+ * would, and results equal bit for bit -- except for two or more Q4_K
  * matrices of at most 4096 columns and 8192 rows in all at 5..16 fp16/bf16
  * rows, which share one multi-row launch (each output row then equals the
  * batch-1 result bit for bit) where a call of one of them alone would take
- * the matrix cores, and (2) from 17 fp16/bf16 rows, for runs of two to four
- * consecutive Q4_K items of at least 256 rows on the same x pointer, with
- * the same cols and layout, which share one register-dequantized launch
- * (one activation conversion, one product kernel, one partial-output sum):
- * each item meets the same error bound as its own call but may differ from
- * it -- by the fp16 rounding of the weights where its own call would take
- * the exact-product kernels (a lone matrix below 65 rows), else by float32
- * summation order, since the run's K slicing follows all its rows. */
+ * the matrix cores.  Uses no workspace. */
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch,
                        const qmv_gemv_item* items, int32_t n, void* stream);
+
+/* *bytes = the device workspace that qmv_gemv_multi_ws needs for exactly
+ * these arguments (the same fmt, x_dtype, batch and items, whose weight
+ * descriptors and shapes are read; x and y are only checked, never read):
+ * 0 when the launch takes no register-dequantized kernel.  Returns the
+ * status the launch would return for these arguments (bytes NULL:
+ * QMV_ERR_NULL), with *bytes = 0 on error.  No HIP call.  The size is (a
+ * run's cols x activation rows x 2 bytes, rounded up to 256) + (activation
+ * rows x 4, rounded up to 256), plus, where K is cut into S = 2..8 slices, S
+ * partial outputs of weight rows x activation rows x 4 bytes per matrix; at
+ * 512 bf16 rows the 7B FFN gate needs 3.7 MB, the down matrix (K in slices)
+ * 56 MB. */
+int32_t qmv_workspace_size(int32_t fmt, int32_t x_dtype, int64_t batch,
+                           const qmv_gemv_item* items, int32_t n,
+                           uint64_t* bytes);
+
+/* qmv_gemv_multi with a caller-owned device workspace, which lets large
+ * batches run the register-dequantized kernels: against Q4_K matrices of at
+ * least 256 weight rows, from 65 fp16/bf16 activation rows (from 17 against
+ * matrices of 8192 columns and more, and for runs of two to four
+ * consecutive items on the same x pointer with the same cols and layout).
+ * There the activations are converted once to fp16 (a bf16 row scaled by
+ * the power of two that brings its largest |x| into [2^14, 2^15)) and each
+ * weight is rounded to fp16 (relative error near 2^-11), so the products
+ * are no longer exact; the normwise bound still holds (about 4e-4 on the 7B
+ * FFN shapes).  K may be cut into slices whose partial outputs are summed in
+ * a fixed order, so results stay independent of timing.  A run shares one
+ * activation conversion, one product launch and one partial-output sum;
+ * its items meet the same bound as their own calls but may differ from them
+ * in float32 summation order, since the run's K slicing follows all its
+ * rows.  Every other item runs as in qmv_gemv_multi, bit for bit.
+ * workspace: device pointer, 256-byte aligned (QMV_ERR_ALIGN), NULL only
+ * with workspace_bytes 0 (QMV_ERR_NULL); workspace_bytes below
+ * qmv_workspace_size of the same arguments fails with QMV_ERR_SIZE before
+ * any launch.  NULL with 0 bytes means no workspace: qmv_gemv_multi's
+ * kernels.  The caller owns the buffer; the launch writes intermediates
+ * there (converted activations, row scales, partial outputs) that need no
+ * initial value, and stream order keeps them apart: launches that may run
+ * at the same time (other streams) need buffers of their own.  Enqueues
+ * only; legal inside HIP stream capture. */
+int32_t qmv_gemv_multi_ws(int32_t fmt, int32_t x_dtype, int64_t batch,
+                          const qmv_gemv_item* items, int32_t n,
+                          void* workspace, uint64_t workspace_bytes,
+                          void* stream);
 
 /* out = W as a dense [rows][cols] matrix of out_dtype (QMV_F32: the exact
  * value rounded once to fp32, bit-exact; QMV_F16 / QMV_BF16: that fp32 value

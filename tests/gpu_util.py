@@ -40,11 +40,29 @@ class Weights:
         sub = {k: v[ids] for k, v in f.items()}
         return oracle.pack(self.fmt, sub, len(ids), self.cols)
 
-    def gemv(self, x_dev, x_dtype, batch, y=None, stream=None):
+    def gemv(self, x_dev, x_dtype, batch, y=None, stream=None, ws=True):
+        """y = W x through qmv_gemv_multi_ws with a workspace of the size the
+        library asks for (the register-dequantized kernels where the launch
+        takes them), or through plain qmv_gemv (ws=False)."""
         if y is None:
             y = torch.empty(batch, self.rows, dtype=torch.float32, device=DEV)
-        qmv.qmv_gemv(self.fmt, self.desc, x_dev, x_dtype, y, self.rows, self.cols, batch, stream)
+        if not ws:
+            qmv.qmv_gemv(self.fmt, self.desc, x_dev, x_dtype, y, self.rows, self.cols, batch, stream)
+            return y
+        self._ws = gemv_ws(self.fmt, [(self.desc, x_dev, y)], x_dtype, batch, stream)
         return y
+
+
+def gemv_ws(fmt, items, x_dtype, batch, stream=None):
+    """qmv_gemv_multi_ws over `items` with a fresh workspace of the size the
+    library asks for; returns the workspace, which the caller holds until the
+    launch has run (a graph capture keeps it in the graph's own pool)."""
+    n = qmv.qmv_workspace_size(fmt, x_dtype, batch, items)
+    buf = torch.empty(n, dtype=torch.uint8, device=DEV) if n else None
+    qmv.qmv_gemv_multi_ws(fmt, x_dtype, batch, items, buf, n, stream)
+    if buf is not None and isinstance(stream, torch.cuda.Stream) and stream != torch.cuda.current_stream():
+        buf.record_stream(stream)  # not reused before the launch on `stream` has run
+    return buf
 
 
 def oracle_y(w: Weights, x_np, x_dtype, row_ids=None):

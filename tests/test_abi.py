@@ -110,6 +110,38 @@ def test_gemv_multi_validation_errors():
     _expect(-5, m, "q4_k", "f32", 1, [(a, FAKE, FAKE), (bad, FAKE, Y2)])
 
 
+def test_workspace_size_and_caller_workspace_errors():
+    """qmv_workspace_size needs no GPU; qmv_gemv_multi_ws refuses a missing,
+    misaligned or too small workspace before any HIP call."""
+    gate = _desc("q4_k", 18944, 3584)
+    down = _desc("q4_k", 3584, 18944)
+    small = _desc("q4_k", 64, 3584)
+    Y2 = FAKE + (1 << 30)
+    size = qmv.qmv_workspace_size
+    n = size("q4_k", "bf16", 512, [(gate, FAKE, FAKE)])
+    assert n >= 512 * 3584 * 2 + 512 * 4 and n % 256 == 0                # fp16 rows + row scales
+    # K in slices: the partial outputs too
+    assert size("q4_k", "bf16", 512, [(down, FAKE, FAKE)]) >= 512 * 18944 * 2 + 2 * 512 * 3584 * 4
+    assert size("q4_k", "f16", 512, [(gate, FAKE, FAKE)]) > 0
+    assert size("q4_k", "bf16", 32, [(down, FAKE, FAKE)]) > 0        # long K: from 17 rows
+    assert size("q4_k", "bf16", 32, [(gate, FAKE, FAKE)]) == 0       # a lone matrix: from 65 rows
+    assert size("q4_k", "bf16", 32, [(gate, FAKE, FAKE), (gate, FAKE, Y2)]) > 0  # a run: from 17
+    assert size("q4_k", "bf16", 512, [(small, FAKE, FAKE)]) == 0     # fewer than 256 weight rows
+    assert size("q4_k", "f32", 512, [(gate, FAKE, FAKE)]) == 0
+    assert size("q4_k", "bf16", 1, [(gate, FAKE, FAKE)]) == 0
+    assert size("q6_k", "bf16", 512, [(_desc("q6_k", 18944, 3584), FAKE, FAKE)]) == 0
+    _expect(-3, size, "q4_k", "bf16", 0, [(gate, FAKE, FAKE)])
+    _expect(-1, size, "q4_k", "bf16", 512, [(gate, None, FAKE)])
+    m = qmv.qmv_gemv_multi_ws
+    items = [(gate, FAKE, FAKE)]
+    _expect(-1, m, "q4_k", "bf16", 512, items, None, n)
+    _expect(-4, m, "q4_k", "bf16", 512, items, FAKE + 16, n)
+    _expect(-5, m, "q4_k", "bf16", 512, items, FAKE, n - 1)
+    _expect(-5, m, "q4_k", "bf16", 512, items, FAKE, 0)
+    # the fixed scratch of the allocation-free call holds 64 MiB
+    _expect(-5, qmv.qmv_gemv_noalloc, "q4_k", down, FAKE, "bf16", FAKE, 3584, 18944, 2048)
+
+
 def test_dequant_and_probe_validation_errors():
     w = _desc()
     _expect(-1, qmv.qmv_dequant, w, None, "f32")

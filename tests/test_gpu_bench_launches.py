@@ -19,7 +19,7 @@ import torch
 
 import oracle
 from block_quantized_weight_qmv_amd import qmv
-from gpu_util import DEV, Weights, say, to_dev_x
+from gpu_util import DEV, Weights, gemv_ws, say, to_dev_x
 from synth import gen_x, weight_seed, x_seed
 
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
@@ -59,12 +59,10 @@ def test_bench_launches_match_oracle(config, batch, x_dtype):
             descs.append(d)
         ys = [torch.full((b, mats[m][1]), 7.0, dtype=torch.float32, device=DEV) for m in g]
         say(f"  launch {plan['launch_names'][gi]} ({plan['kname'][gi]})")
-        if len(g) == 1:
-            m = g[0]
-            qmv.qmv_gemv(fmt, descs[0], xd, xd_name, ys[0], mats[m][1], mats[m][2], b)
-        else:
-            qmv.qmv_gemv_multi(fmt, xd_name, b, [(d, xd, y) for d, y in zip(descs, ys)])
+        # as the benchmark issues it: one launch with the workspace it asks for
+        wsbuf = gemv_ws(fmt, [(d, xd, y) for d, y in zip(descs, ys)], xd_name, b)
         torch.cuda.synchronize()
+        del wsbuf
         for w, m, y in zip(ws, g, ys):
             name, rows, cols = mats[m]
             got = y.cpu().numpy().astype(np.float64)

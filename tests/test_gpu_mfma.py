@@ -1,9 +1,11 @@
 """Batched Q4_K x bf16 on the matrix-core path, and Q4_K x fp16 on its
 streaming kernel (5-16 rows with X in LDS) and tile kernels (17 rows up);
-from 128 rows (64 against 8192 columns and more) against 256 weight rows
-and more, the register-dequantized kernels (fp16 weight fragments formed per
-wave, activations converted once; every form the launcher picks, with K
-whole or in slices).
+with a caller workspace, from 65 rows (17 against 8192 columns and more)
+against 256 weight rows and more, the register-dequantized kernels (fp16
+weight fragments formed per wave, activations converted once; every form
+the launcher picks, with K whole or in slices).  Calls through the test
+helper pass the workspace the library asks for; shapes the register path
+would take also run as plain calls (no workspace: the tile kernels).
 
 Gate: normwise relative error <= 2e-3 per batch row against the float64 oracle.
 The matrix cores take the 4-bit codes and the activations exactly and the
@@ -12,7 +14,7 @@ fp32 GEMV; inputs whose products and sums are small integers are exact on both
 paths and are checked exactly.  Shapes cover the three kernels behind the call
 (batch <= 16 with X in LDS: one to eight 16-row tiles per workgroup and more
 workgroups than CUs; batch <= 32 or K too long for LDS: K split over waves;
-larger batches: 64 x 64 tiles; from 128 rows the register-dequantized kernels),
+larger batches: 64 x 64 tiles; the register-dequantized kernels),
 ragged rows and batches, the smallest batch routed here (2: matrices wider
 than eight waves along K; narrower ones take the multi-row GEMV at batch 2,
 and at 3-4 those within one wave's K slice), and the full-size batched
@@ -28,7 +30,7 @@ import torch
 
 import oracle
 from block_quantized_weight_qmv_amd import qmv
-from gpu_util import DEV, Weights, oracle_y, say, to_dev_x
+from gpu_util import DEV, Weights, gemv_ws, oracle_y, say, to_dev_x
 from synth import CONFIGS, gen_weights, gen_x, weight_seed, x_seed
 
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
@@ -59,11 +61,19 @@ def test_mfma_matches_oracle(rows, nblk, batch):
     w = Weights("q4_k", rows, cols, seed=700 + rows + nblk)
     x = gen_x(batch, cols, "bf16", seed=71 + batch)
     y = torch.full((batch, rows), 3.5, dtype=torch.float32, device=DEV)
-    w.gemv(to_dev_x(x, "bf16"), "bf16", batch, y=y)
+    xd = to_dev_x(x, "bf16")
+    w.gemv(xd, "bf16", batch, y=y)
     y = y.cpu().numpy()
-    err = oracle.normwise_rel_err(y, oracle_y(w, x, "bf16"))
+    y64 = oracle_y(w, x, "bf16")
+    err = oracle.normwise_rel_err(y, y64)
     say(f"  normwise err max {err.max():.3e}")
     assert np.all(err <= TOL), err
+    if qmv.qmv_workspace_size("q4_k", "bf16", batch, [(w.desc, xd, y)]):
+        # with a workspace this took the register-dequantized kernels; the
+        # plain call takes the exact-product tile kernels
+        err = oracle.normwise_rel_err(w.gemv(xd, "bf16", batch, ws=False).cpu().numpy(), y64)
+        say(f"  plain call: normwise err max {err.max():.3e}")
+        assert np.all(err <= TOL), err
 
 
 # One shape per form of the register-dequantized kernels the launcher's model
@@ -171,11 +181,20 @@ def test_mfma_f16_matches_oracle(layout, rows, nblk, batch):
         desc.keep = buf
     x = gen_x(batch, cols, "f16", seed=91 + batch)
     y = torch.full((batch, rows), 3.5, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv("q4_k", desc, to_dev_x(x, "f16"), "f16", y, rows, cols, batch)
-    y = y.cpu().numpy()
-    err = oracle.normwise_rel_err(y, oracle_y(w, x, "f16"))
+    xd = to_dev_x(x, "f16")
+    qmv.qmv_gemv("q4_k", desc, xd, "f16", y, rows, cols, batch)
+    y64 = oracle_y(w, x, "f16")
+    err = oracle.normwise_rel_err(y.cpu().numpy(), y64)
     say(f"  normwise err max {err.max():.3e}")
     assert np.all(err <= TOL), err
+    if qmv.qmv_workspace_size("q4_k", "f16", batch, [(desc, xd, y)]):
+        # with a workspace: the register-dequantized kernels
+        y.fill_(3.5)
+        ws = gemv_ws("q4_k", [(desc, xd, y)], "f16", batch)
+        err = oracle.normwise_rel_err(y.cpu().numpy(), y64)
+        del ws
+        say(f"  with a workspace: normwise err max {err.max():.3e}")
+        assert np.all(err <= TOL), err
 
 
 def test_mfma_f16_integer_case_is_exact():
@@ -273,8 +292,9 @@ def test_dq_bf16_activation_range(layout, spread, rows, nblk, batch):
         desc = qmv.qmv_repack_planes(w.desc, keep)
     say(f"dq bf16 activation range {spread} ({layout}) {rows}x{cols} batch {batch}")
     y = torch.full((batch, rows), 3.5, dtype=torch.float32, device=DEV)
-    qmv.qmv_gemv("q4_k", desc, to_dev_x(x, "bf16"), "bf16", y, rows, cols, batch)
+    ws = gemv_ws("q4_k", [(desc, to_dev_x(x, "bf16"), y)], "bf16", batch)
     got = y.cpu().numpy()
+    del ws
     assert np.all(np.isfinite(got))
     err = oracle.normwise_rel_err(got, oracle_y(w, x, "bf16"))
     say(f"  normwise err max {err.max():.3e}")
@@ -308,39 +328,47 @@ def test_dq_deterministic_and_graph_replay(x_dtype, rows, cols, batch):
         assert torch.equal(yg, y0)
 
 
-def test_dqreg_workspace_capture_and_growth():
-    """The register-dequantized kernels keep a workspace per stream: a call
-    that would have to allocate it under stream capture fails with
-    QMV_ERR_HIP and a message; after an eager call the same call captures,
-    and its graph stays valid (and exact) after a larger call on the stream
-    has grown the workspace."""
+def test_dqreg_caller_workspace():
+    """The register-dequantized kernels run only with a workspace from the
+    caller: qmv_workspace_size names its bytes, one byte fewer fails with
+    QMV_ERR_SIZE before anything is launched (y keeps its values), no
+    workspace gives the exact-product kernels of plain qmv_gemv (bit for
+    bit), and a capture on a fresh stream needs no earlier call: every
+    replay equals the eager result, also after a larger call has used
+    another workspace."""
     rows, cols, batch = 3584, 14 * 256, 128
     w = Weights("q4_k", rows, cols, seed=2300)
     x = to_dev_x(gen_x(batch, cols, "bf16", seed=230), "bf16")
-    s = torch.cuda.Stream()
-    y = torch.zeros(batch, rows, dtype=torch.float32, device=DEV)
-    g = torch.cuda.CUDAGraph()
-    with pytest.raises(qmv.QmvError, match="workspace"):
-        with torch.cuda.stream(s):
-            with torch.cuda.graph(g, stream=s):
-                w.gemv(x, "bf16", batch, y=y, stream=s)
+    y = torch.full((batch, rows), 7.0, dtype=torch.float32, device=DEV)
+    items = [(w.desc, x, y)]
+    n = qmv.qmv_workspace_size("q4_k", "bf16", batch, items)
+    assert n >= cols * batch * 2 + rows * batch * 4
+    ws = torch.empty(n, dtype=torch.uint8, device=DEV)
+    with pytest.raises(qmv.QmvError, match="workspace") as e:
+        qmv.qmv_gemv_multi_ws("q4_k", "bf16", batch, items, ws, n - 1)
+    assert e.value.status == -5
     torch.cuda.synchronize()
+    assert bool((y == 7.0).all())
+    plain = w.gemv(x, "bf16", batch, ws=False)
+    qmv.qmv_gemv_multi_ws("q4_k", "bf16", batch, items, None, 0)
+    assert torch.equal(y, plain)
     y0 = w.gemv(x, "bf16", batch)
+    assert not torch.equal(y0, plain)  # fp16 weights on the register path
+    s = torch.cuda.Stream()
+    yg = torch.zeros(batch, rows, dtype=torch.float32, device=DEV)
+    g = torch.cuda.CUDAGraph()
     with torch.cuda.stream(s):
-        w.gemv(x, "bf16", batch, y=y, stream=s)  # allocates this stream's workspace
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g, stream=s):
-            w.gemv(x, "bf16", batch, y=y, stream=s)
-        # a larger call on the same stream grows the workspace
-        big = 512
-        xb = to_dev_x(gen_x(big, cols, "bf16", seed=231), "bf16")
-        yb = w.gemv(xb, "bf16", big, stream=s)
-        torch.cuda.synchronize()
-    assert torch.equal(yb, w.gemv(xb, "bf16", big))
-    for _ in range(2):
-        y.fill_(0.0)
+            qmv.qmv_gemv_multi_ws("q4_k", "bf16", batch, [(w.desc, x, yg)], ws, n, stream=s)
+    big = 512
+    xb = to_dev_x(gen_x(big, cols, "bf16", seed=231), "bf16")
+    yb = w.gemv(xb, "bf16", big)
+    for _ in range(3):
+        yg.fill_(0.0)
         torch.cuda.synchronize()
         g.replay()
         torch.cuda.synchronize()
-        assert torch.equal(y, y0)
+        assert torch.equal(yg, y0)
+    err = oracle.normwise_rel_err(yb.cpu().numpy()[::37], oracle_y(w, gen_x(big, cols, "bf16", seed=231)[::37],
+                                                                    "bf16"))
+    assert np.all(err <= TOL), err

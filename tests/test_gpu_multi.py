@@ -12,7 +12,7 @@ import torch
 
 import oracle
 from block_quantized_weight_qmv_amd import qmv
-from gpu_util import DEV, Weights, oracle_y, say, to_dev_x
+from gpu_util import DEV, Weights, gemv_ws, oracle_y, say, to_dev_x
 from synth import gen_x
 
 pytestmark = pytest.mark.gpu
@@ -162,12 +162,14 @@ def test_multi_small_q4_k_matrices_share_one_multi_row_launch(x_dtype, batch):
 
 @pytest.mark.parametrize("x_dtype,batch", [("bf16", 17), ("bf16", 32), ("bf16", 128), ("f16", 64), ("bf16", 300)])
 def test_multi_register_dequantized_runs(x_dtype, batch):
-    """Consecutive Q4_K items of at least 256 rows on one activation share one
-    register-dequantized launch from 17 rows (a q+k+v-like run of three, then
+    """With a workspace, consecutive Q4_K items of at least 256 rows on one
+    activation share one register-dequantized launch from 17 rows (a q+k+v-like run of three, then
     a lone matrix of another width that runs alone): every item meets the
     oracle gate, as its own call does (below 65 rows a lone call of these
     matrices takes the exact-product kernels, so the two differ by the fp16
-    rounding of the weights; above, by float32 summation order)."""
+    rounding of the weights; above, by float32 summation order).  Without a
+    workspace the launch gives each item its plain call's result, bit for
+    bit."""
     items = [(520, 14), (256, 14), (300, 14), (257, 9)]
     ws = [Weights("q4_k", r, n * 256, seed=1700 + 13 * i) for i, (r, n) in enumerate(items)]
     x14 = gen_x(batch, 14 * 256, x_dtype, seed=1800 + batch)
@@ -176,12 +178,17 @@ def test_multi_register_dequantized_runs(x_dtype, batch):
     ys = [torch.full((batch, w.rows), -3.0, dtype=torch.float32, device=DEV) for w in ws]
     xs = [xd14, xd14, xd14, xd9]
     say(f"multi q4_k {x_dtype} batch {batch}: run of three on one activation, one more")
-    qmv.qmv_gemv_multi("q4_k", x_dtype, batch, [(w.desc, x, y) for w, x, y in zip(ws, xs, ys)])
+    buf = gemv_ws("q4_k", [(w.desc, x, y) for w, x, y in zip(ws, xs, ys)], x_dtype, batch)
     torch.cuda.synchronize()
-    for w, x_np, xd, y in zip(ws, [x14, x14, x14, x9], xs, ys):
+    del buf
+    # without a workspace every item takes the exact-product kernels of its own plain call
+    yp = [torch.full_like(y, -5.0) for y in ys]
+    qmv.qmv_gemv_multi("q4_k", x_dtype, batch, [(w.desc, x, y) for w, x, y in zip(ws, xs, yp)])
+    for w, x_np, xd, y, y_plain in zip(ws, [x14, x14, x14, x9], xs, ys, yp):
         got = y.cpu().numpy()
         err = oracle.normwise_rel_err(got, oracle_y(w, x_np, x_dtype))
         assert np.all(err <= TOL), (w.rows, w.cols, err.max())
         alone = w.gemv(xd, x_dtype, batch).cpu().numpy()
         apart = oracle.normwise_rel_err(got, alone.astype(np.float64))
         assert np.all(apart <= (2 * TOL if batch < 65 else 1e-5)), (w.rows, w.cols, apart.max())
+        assert torch.equal(y_plain, w.gemv(xd, x_dtype, batch, ws=False)), (w.rows, w.cols)
