@@ -14,9 +14,14 @@ caller-owned workspace sized by qmv_workspace_size): [q, k, v], [o],
 [gate, up], [down].  `--separate` issues one launch per matrix instead.
 
 Output: one JSON line.  `value` is algorithmic bytes (packed weights + x + y)
-per step divided by the measured time per step.  `roofline` covers the
-dominant kernel (most bytes per step): a graph of the same K steps restricted
-to that kernel's launches, replayed between HIP events on the replay stream.
+per step divided by the measured time per step.  For the default workload the
+line also carries `batched`: the same measurement, run first in child
+processes, of the batched bf16 workloads (the FFN gate at 64 and 512 rows,
+the whole layer at 17, 64, 128 and 512 rows, with one caller workspace),
+their step and launch times and their dominant kernel's roofline.
+`roofline` covers the dominant kernel (most bytes per step): a graph of the
+same K steps restricted to that kernel's launches, replayed between HIP
+events on the replay stream.
 `cpu_baseline` times the CPU oracle (float64 decode + dot) on a bounded sample
 of the same matrices.
 
@@ -799,6 +804,42 @@ def _layout(args) -> str:
             else args.layout)
 
 
+# Batched workloads reported beside the decode line: (configuration, rows).
+# Configuration 5 is the 7B FFN gate matrix (18944 x 3584), configuration 3
+# the whole 7B decoder layer (its down projection is 3584 x 18944), both
+# with bf16 rows here.
+BATCHED_RUNS = [(5, 64), (5, 512), (3, 17), (3, 64), (3, 128), (3, 512)]
+
+
+def batched_lines(args) -> list:
+    """Time each batched workload in a child run of this script (one GPU
+    process at a time) and keep the figures of its line: step time, launch
+    times and the dominant kernel's roofline."""
+    import subprocess
+    out = []
+    for config, batch in BATCHED_RUNS:
+        cmd = [sys.executable, "-u", os.path.abspath(__file__), "--config", str(config), "--batch", str(batch),
+               "--x-dtype", "bf16", "--steps", "50", "--warmup", "5", "--no-cpu-baseline", "--batched", "off",
+               "--settle-ms", str(args.settle_ms), "--replays", str(args.replays)]
+        print(f"batched workload: config {config}, {batch} bf16 rows", file=sys.stderr, flush=True)
+        r = subprocess.run(cmd, capture_output=True, text=True, timeout=600)
+        lines = [ln for ln in r.stdout.splitlines() if ln.startswith("{")]
+        if r.returncode != 0 or not lines:
+            msg = f"exit {r.returncode}: {r.stderr[-1500:]}"
+            print(f"batched workload failed: {msg}", file=sys.stderr, flush=True)
+            out.append({"config": config, "batch": batch, "x_dtype": "bf16", "error": msg})
+            continue
+        d = json.loads(lines[-1])
+        rf = d["roofline"]
+        out.append({"workload": d["config"]["workload"], "batch": batch, "x_dtype": "bf16",
+                    "layout": d["config"]["layout"], "launches": d["config"]["launches"],
+                    "steps": d["steps"], "ms_per_step": d["ms_per_step"],
+                    "per_launch_us": {k: v["us"] for k, v in (d["per_launch"] or {}).items()},
+                    "roofline": {k: rf[k] for k in ("bound", "achieved", "peak", "unit", "frac", "kernel",
+                                                    "avg_launch_us")}})
+    return out
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -832,6 +873,10 @@ def main() -> int:
                          "(grouped by kernel and grid) and the dominant kernel's roofline fraction")
     ap.add_argument("--summarize-sq", nargs="+", metavar="DIR",
                     help="rocprofv3 --pmc output dirs (SQ counters) of the eager pass: per-launch table")
+    ap.add_argument("--batched", choices=["auto", "on", "off"], default="auto",
+                    help="also time the batched bf16 workloads (the FFN gate at 64 and 512 rows, the "
+                         "layer at 17, 64, 128 and 512 rows), each in a child run before this one, and add "
+                         "their figures to the line as \"batched\" (auto: for the default workload)")
     args = ap.parse_args()
     if args.summarize_counters:
         return summarize_counters(args)
@@ -846,6 +891,12 @@ def main() -> int:
               "each would hold rows/P of every matrix, take the whole activation and all-gather "
               "y). Run with --gpus 1.", file=sys.stderr)
         return 2
+
+    batched = None
+    default_run = (args.config == 3 and args.batch is None and args.x_dtype is None and not args.separate
+                   and not args.eager_pass and args.layout == "auto")
+    if args.batched == "on" or (args.batched == "auto" and default_run):
+        batched = batched_lines(args)  # child runs first: this process has not touched the GPU yet
 
     import numpy as np
     import torch
@@ -1065,6 +1116,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(mats, fmt, x_dtype, fields_list, xs, args.cpu_sample_rows)
+    if batched is not None:
+        rec["batched"] = batched
     print(json.dumps(rec), flush=True)
     return 0
 
