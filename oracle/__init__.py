@@ -19,6 +19,9 @@ What it computes, and from which passage:
   reference is the correctness gate for every GPU kernel; fused kernels are
   checked against an unfused chain.  The oracle's GEMV is the unfused chain:
   dequantize to float64, then a float64 matrix-vector product.
+* hipfire, Qwen2 decoder "Key Technical Specifications": the FFN is SwiGLU.
+  The oracle's SwiGLU input h = silu(W_gate x) * (W_up x) is that unfused
+  chain again: two float64 GEMVs, then silu(g) = g / (1 + exp(-g)) times u.
 
 Everything is plain numpy in float64.  The decoders are deliberately
 unblocked and unfused so they can be checked against the layout tables by eye.
@@ -36,7 +39,7 @@ from .formats import (BLOCK_BYTES, FORMATS, QK, dequant32, dequant64, pack,
 from .fp import bf16_bits_to_f64, f32_to_bf16_bits_rne, fp16_bits_to_f64
 from .gemv import (elementwise_bound, elementwise_bound_rows, gamma, gemv64, gemv64_and_bound,
                    gemv64_rows,
-                   normwise_rel_err, x_to_f64)
+                   normwise_rel_err, silu64, swiglu64, x_to_f64)
 
 __all__ = [
     "BLOCK_BYTES", "FORMATS", "QK", "dequant32", "dequant64", "pack", "packed_size",
@@ -44,5 +47,5 @@ __all__ = [
     "fp16_bits_to_f64", "elementwise_bound", "elementwise_bound_rows", "gamma", "gemv64",
     "gemv64_and_bound",
     "gemv64_rows",
-    "normwise_rel_err", "x_to_f64",
+    "normwise_rel_err", "silu64", "swiglu64", "x_to_f64",
 ]

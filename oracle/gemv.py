@@ -138,3 +138,31 @@ def elementwise_bound_rows(fmt: str, data, rows: int, cols: int, x, x_dtype: str
     w = np.stack([dequant64(fmt, row_slice(fmt, data, rows, cols, int(r), int(r) + 1), 1, cols)[0]
                   for r in ids])
     return gamma(cols + 1) * (x64 @ np.abs(w).T)
+
+
+def silu64(g) -> np.ndarray:
+    """silu(g) = g / (1 + exp(-g)) in float64, elementwise.
+
+    hipfire's Qwen2 decoder ("Key Technical Specifications") names a SwiGLU
+    FFN; silu is the gate nonlinearity of SwiGLU.  For g below about -709,
+    exp(-g) overflows to +inf and the quotient is -0, the limit of silu."""
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):
+        return g / (1.0 + np.exp(-g))
+
+
+def swiglu64(fmt: str, gate_data, up_data, rows: int, cols: int, x, x_dtype: str,
+             row_ids=None) -> np.ndarray:
+    """h64 = silu(W_gate x) * (W_up x), float64 [batch, rows] (or the listed rows).
+
+    The SwiGLU FFN input of hipfire's Qwen2 decoder, computed by the unfused
+    chain that hipEngine 0.3.0 ("Core principles") keeps beside every fused
+    composite: the two GEMVs of the oracle, then the elementwise product of
+    silu of the gate with the up projection, all in float64."""
+    if row_ids is None:
+        g = gemv64(fmt, gate_data, rows, cols, x, x_dtype)
+        u = gemv64(fmt, up_data, rows, cols, x, x_dtype)
+    else:
+        g = gemv64_rows(fmt, gate_data, rows, cols, x, x_dtype, row_ids)
+        u = gemv64_rows(fmt, up_data, rows, cols, x, x_dtype, row_ids)
+    return silu64(g) * u

@@ -13,6 +13,8 @@ oracle disagrees with:
 * invariants: zero scale -> zero weights, weights affine in the code with slope
   d*sc, the zero point of each format;
 * brute force: the float64 GEMV against an exact rational sum;
+* silu against closed forms from the math module, and the SwiGLU chain on
+  hand-made matrices whose GEMVs are exact integers;
 * the byte counts of the decode workloads (34, 144 and 210 bytes per block)
   and of GGUF's Q5_K block (176 bytes).
 
@@ -349,11 +351,46 @@ def pin_elementwise_bound():
                 assert np.all(np.abs(y32.astype(np.float64) - y64[bi]) <= bound[bi]), fmt
 
 
+def pin_swiglu():
+    """silu against closed forms built with the math module, and the SwiGLU
+    chain against hand-made Q8_0 matrices whose GEMVs are exact integers:
+    h[b, r] = silu(g[b, r]) * u[b, r] with gate and up not interchangeable
+    (silu(2) * 3 != silu(3) * 2), rows paired by index and batch rows apart."""
+    import math
+    pts = [0.0, 1.0, -1.0, 2.5, -7.0, 30.0]
+    want = [p / (1.0 + math.exp(-p)) for p in pts]
+    got = oracle.silu64(np.array(pts))
+    assert np.allclose(got, want, rtol=1e-15, atol=0)
+    assert got[0] == 0.0 and abs(got[1] - 0.7310585786300049) < 1e-15
+    big = oracle.silu64(np.array([-800.0, 800.0, np.nan]))
+    assert big[0] == 0.0 and np.signbit(big[0]) and big[1] == 800.0 and np.isnan(big[2])
+    # gate row r has code gq[r] at column 0 and up row r has uq[r] there (d = 1),
+    # so with x = (x0, 0, ..., 0): g = gq[r] * x0, u = uq[r] * x0
+    rows, cols = 3, 32
+    gq, uq = [2, -1, 0], [3, 5, -4]
+    gf = {"d_bits": np.full((rows, 1), 0x3C00, np.uint16), "q": np.zeros((rows, cols), np.int8)}
+    uf = {"d_bits": np.full((rows, 1), 0x3C00, np.uint16), "q": np.zeros((rows, cols), np.int8)}
+    gf["q"][:, 0] = gq
+    uf["q"][:, 0] = uq
+    gd, ud = oracle.pack("q8_0", gf, rows, cols), oracle.pack("q8_0", uf, rows, cols)
+    x = np.zeros((2, cols), np.float32)
+    x[:, 0] = [1.0, -0.5]
+    h = oracle.swiglu64("q8_0", gd, ud, rows, cols, x, "f32")
+    assert h.shape == (2, rows)
+    for b, x0 in enumerate((1.0, -0.5)):
+        for r in range(rows):
+            g, u = gq[r] * x0, uq[r] * x0
+            assert abs(h[b, r] - g / (1.0 + math.exp(-g)) * u) <= 1e-15 * max(1.0, abs(g * u)), (b, r)
+    assert abs(h[0, 0] - 3 * 2 / (1 + math.exp(-2))) < 1e-14        # 5.2848..., not silu(3) * 2
+    # sampled rows equal the full result
+    assert np.array_equal(oracle.swiglu64("q8_0", gd, ud, rows, cols, x, "f32", [2, 0]), h[:, [2, 0]])
+
+
 ALL_PINS = (
     [("fp16_decode", pin_fp16_decode, ()), ("bf16_decode", pin_bf16_decode, ()),
      ("bf16_rne", pin_bf16_rne, ()), ("packed_sizes", pin_packed_sizes, ()),
      ("x_to_f64", pin_x_to_f64, ()), ("normwise_gate", pin_normwise_gate, ()),
-     ("elementwise_bound", pin_elementwise_bound, ())]
+     ("elementwise_bound", pin_elementwise_bound, ()), ("swiglu", pin_swiglu, ())]
     + [(f"golden[{n}]", pin_golden, (n,)) for n in all_names()]
     + [(f"{p.__name__[4:]}[{fmt}]", p, (fmt,)) for fmt in FMTS
        for p in (pin_roundtrip, pin_single_rounding, pin_zero_scale, pin_affine_in_code,

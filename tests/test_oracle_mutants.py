@@ -157,10 +157,21 @@ def _bound_gamma_k(fmt, data, rows, cols, x, x_dtype, row_chunk=4096):
     return BOUND_ORIG(fmt, data, rows, cols, x, x_dtype) * (G.gamma(cols) / G.gamma(cols + 1))
 
 
+def _swiglu_swapped(fmt, gate_data, up_data, rows, cols, x, x_dtype, row_ids=None):
+    return SWIGLU_ORIG(fmt, up_data, gate_data, rows, cols, x, x_dtype, row_ids)
+
+
+def _silu_sigmoid(g):
+    g = np.asarray(g, np.float64)
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-g))
+
+
 X_ORIG = G.x_to_f64
 BOUND_ORIG = G.elementwise_bound
 FP_ORIG = FP.fp16_bits_to_f64
 Q4K_SCALES_ORIG = F.q4_k_bytes_to_scales
+SWIGLU_ORIG = G.swiglu64
 
 MUTANTS = {
     "q4_k nibbles swapped": [(F, "q4_k_qs_to_codes", _q4k_codes_swapped)],
@@ -187,6 +198,8 @@ MUTANTS = {
     "activations f16 and bf16 swapped": [(G, "x_to_f64", _x_to_f64_swapped), (oracle, "x_to_f64", _x_to_f64_swapped)],
     "bound without |W|": [(oracle, "elementwise_bound", _bound_signed)],
     "bound gamma_K": [(oracle, "elementwise_bound", _bound_gamma_k)],
+    "swiglu gate and up swapped": [(G, "swiglu64", _swiglu_swapped), (oracle, "swiglu64", _swiglu_swapped)],
+    "swiglu sigmoid in place of silu": [(G, "silu64", _silu_sigmoid), (oracle, "silu64", _silu_sigmoid)],
 }
 
 
