@@ -19,6 +19,8 @@ line also carries `batched`: the same measurement, run first in child
 processes, of the batched bf16 workloads (the FFN gate at 64 and 512 rows,
 the whole layer at 17, 64, 128 and 512 rows, with one caller workspace),
 their step and launch times and their dominant kernel's roofline.
+`swiglu_fused` times gate and up as one launch that writes silu(gate) * up
+(qmv_gemv_swiglu) next to the unfused gate+up launch.
 `roofline` covers the dominant kernel (most bytes per step): a graph of the
 same K steps restricted to that kernel's launches, replayed between HIP
 events on the replay stream.
@@ -993,12 +995,14 @@ def main() -> int:
     cap = torch.cuda.Stream(dev)
     spread = []   # (min, median, max) ms of each timed region's replays
 
-    def timed_graph(gis):
+    def timed_graph(gis, fn=None):
         g = torch.cuda.CUDAGraph()
         torch.cuda.synchronize()
         with torch.cuda.graph(g, stream=cap):
             for s in range(args.steps):
                 c = (args.warmup + s) % copies
+                if fn is not None:
+                    fn(c, cap.cuda_stream)
                 for gi in gis:
                     launch(c, groups[gi], cap.cuda_stream)
         g.replay()                    # untimed: first-touch costs
@@ -1049,6 +1053,27 @@ def main() -> int:
                                round(spread[-1][2] * 1e3 / args.steps, 3)]}
     else:
         per_launch = None
+    # The SwiGLU epilogue: gate and up as one launch writing silu(g) * u
+    # (qmv_gemv_swiglu), against the unfused gate+up launch above (decode
+    # steps, one activation row).
+    fused = None
+    if "gate" in names and "up" in names and not args.separate and batch == 1:
+        mg, mu = names.index("gate"), names.index("up")
+        _, grows, gcols = mats[mg]
+        if gcols <= (2048 if fmt == "q8_0" else 4096):
+            hbuf = torch.empty(batch, grows, dtype=torch.float32, device=dev)
+
+            def swiglu_launch(c, sptr):
+                qmv.qmv_gemv_swiglu(fmt, descs[c][mg], descs[c][mu], xs_dev[mg], x_dtype, hbuf,
+                                    grows, gcols, batch, sptr)
+            el = timed_graph([], swiglu_launch)
+            us = el * 1e3 / args.steps
+            gb = gbytes[[i for i, g in enumerate(groups) if mg in g][0]]
+            fused = {"launch": "gate+up -> silu(gate) * up", "us": round(us, 3),
+                     "GBps": round((gb - batch * grows * 4) / (us * 1e-6) / 1e9, 1),
+                     "us_min_max": [round(spread[-1][0] * 1e3 / args.steps, 3),
+                                    round(spread[-1][2] * 1e3 / args.steps, 3)],
+                     "unfused_gate_up_us": (per_launch or {}).get("gate+up", {}).get("us")}
     dom_avg_us = kern[dom]["avg_launch_us"]
     dom_bytes_per_launch = kern[dom]["bytes_per_launch"]
     dom_flops_per_launch = sum(gflops[gi] for gi in by_kernel[dom]) / len(by_kernel[dom])
@@ -1116,6 +1141,8 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = cpu_baseline(mats, fmt, x_dtype, fields_list, xs, args.cpu_sample_rows)
+    if fused is not None:
+        rec["swiglu_fused"] = fused
     if batched is not None:
         rec["batched"] = batched
     print(json.dumps(rec), flush=True)

@@ -11,6 +11,7 @@
 #include <stdio.h>
 
 #include <algorithm>
+#include <initializer_list>
 
 #include <hip/hip_runtime.h>
 
@@ -464,6 +465,51 @@ static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, cons
     default: e = qmv::gemv_int4_g128(calls, n, x_dtype, batch, s); break;
   }
   return qmv::from_hip(e, "qmv_gemv launch");
+}
+
+int32_t qmv_gemv_swiglu(int32_t fmt, const qmv_weights* Wg, const qmv_weights* Wu, const void* x,
+                        int32_t x_dtype, float* h, int64_t rows, int64_t cols, int64_t batch, void* stream) {
+  for (const qmv_weights* W : {Wg, Wu}) {
+    const int32_t st = qmv::check_weights(W);
+    if (st != QMV_OK) return st;
+    if (fmt != W->fmt || rows != W->rows || cols != W->cols)
+      return fail(QMV_ERR_FORMAT, "call (fmt %d, %lld x %lld) disagrees with weights (fmt %d, %lld x %lld)",
+                  fmt, (long long)rows, (long long)cols, W->fmt, (long long)W->rows, (long long)W->cols);
+  }
+  if (Wg->layout != Wu->layout)
+    return fail(QMV_ERR_UNSUPPORTED, "gate layout %d, up layout %d", Wg->layout, Wu->layout);
+  if (!x || !h) return fail(QMV_ERR_NULL, "x or h is NULL");
+  if (!qmv::aligned16(x) || !qmv::aligned16(h)) return fail(QMV_ERR_ALIGN, "x or h not 16-byte aligned");
+  if (batch < 1) return fail(QMV_ERR_SHAPE, "batch %lld < 1", (long long)batch);
+  if (batch > qmv::kMaxBatch)
+    return fail(QMV_ERR_UNSUPPORTED, "batch %lld above %lld", (long long)batch, (long long)qmv::kMaxBatch);
+  if (x_dtype != QMV_F32 && x_dtype != QMV_F16 && x_dtype != QMV_BF16)
+    return fail(QMV_ERR_UNSUPPORTED, "activation dtype %d", x_dtype);
+  const int64_t slice = fmt == QMV_Q8_0 ? 2048 : 4096;  // one wave's K slice
+  if (cols > slice)
+    return fail(QMV_ERR_UNSUPPORTED, "cols %lld above %lld: the fused gate/up launch needs every row within "
+                "one wave's K slice (call qmv_gemv_multi for gate and up instead)", (long long)cols,
+                (long long)slice);
+  if (rows > INT32_MAX / 2) return fail(QMV_ERR_UNSUPPORTED, "rows %lld too large", (long long)rows);
+  const uintptr_t x0 = reinterpret_cast<uintptr_t>(x);
+  const uintptr_t x1 = x0 + static_cast<uintptr_t>(batch * cols) * (x_dtype == QMV_F32 ? 4 : 2);
+  const uintptr_t h0 = reinterpret_cast<uintptr_t>(h);
+  const uintptr_t h1 = h0 + static_cast<uintptr_t>(batch * rows) * 4;
+  if (x0 < h1 && h0 < x1) return fail(QMV_ERR_SHAPE, "h overlaps x");
+  qmv_weights pair = *Wg;  // launch rows 2i, 2i + 1 = gate row i, up row i
+  pair.rows = 2 * rows;
+  const qmv::GemvCall gate{&pair, x, h};
+  const bool planes = Wg->layout == QMV_LAYOUT_PLANES;
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (fmt) {
+    case QMV_Q8_0: e = qmv::gemv_q8_0_glu(gate, Wu->data, x_dtype, batch, s); break;
+    case QMV_Q4_K: e = qmv::gemv_q4_k_glu(gate, Wu->data, x_dtype, batch, planes, s); break;
+    case QMV_Q5_K: e = qmv::gemv_q5_k_glu(gate, Wu->data, x_dtype, batch, planes, s); break;
+    case QMV_Q6_K: e = qmv::gemv_q6_k_glu(gate, Wu->data, x_dtype, batch, planes, s); break;
+    default: e = qmv::gemv_int4_g128_glu(gate, Wu->data, x_dtype, batch, s); break;
+  }
+  return qmv::from_hip(e, "qmv_gemv_swiglu launch");
 }
 
 int32_t qmv_dequant(const qmv_weights* W, void* out, int32_t out_dtype, void* stream) {

@@ -242,6 +242,12 @@ hipError_t gemv_q4_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t b
   return launch_gemv<Q4KPlanesPolicy>(calls, n, x_dtype, batch, s);
 }
 
+hipError_t gemv_q4_k_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, bool planes,
+                         hipStream_t s) {
+  return planes ? launch_gemv_glu<Q4KPlanesPolicy>(gate, up, x_dtype, batch, s)
+                : launch_gemv_glu<Q4KPolicy>(gate, up, x_dtype, batch, s);
+}
+
 hipError_t gemv_q4_k_rows(const GemvCall* calls, int n, int x_dtype, int64_t batch, bool planes,
                           hipStream_t s) {
   return planes ? launch_gemv_rows<Q4KPlanesPolicy>(calls, n, x_dtype, batch, s)

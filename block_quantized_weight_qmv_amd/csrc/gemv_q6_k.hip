@@ -275,4 +275,10 @@ hipError_t gemv_q6_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t b
   return launch_gemv<Q6KPlanesPolicy>(calls, n, x_dtype, batch, s);
 }
 
+hipError_t gemv_q6_k_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, bool planes,
+                         hipStream_t s) {
+  return planes ? launch_gemv_glu<Q6KPlanesPolicy>(gate, up, x_dtype, batch, s)
+                : launch_gemv_glu<Q6KPolicy>(gate, up, x_dtype, batch, s);
+}
+
 }  // namespace qmv

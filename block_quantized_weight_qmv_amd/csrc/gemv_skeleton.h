@@ -96,9 +96,35 @@ __device__ __forceinline__ void load_tile(const P& pol, typename P::Frag* f, int
   for (int r = 0; r < R; ++r) pol.load(min(row0 + r, r_last), f[r]);
 }
 
+// A tile of the gate/up launch (GLU): launch rows 2i and 2i + 1 are row i of
+// the gate matrix (pol) and of the up matrix (pol_up); row0 is even.
+template <class P, int R, bool GLU>
+__device__ __forceinline__ void load_tile_of(const P& pol, const P& pol_up, typename P::Frag* f, int row0,
+                                             int r_last) {
+  if constexpr (GLU) {
+    const int i = min(row0, r_last) >> 1;
+    pol.load(i, f[0]);
+    pol_up.load(i, f[1]);
+  } else {
+    load_tile<P, R>(pol, f, row0, r_last);
+  }
+}
+
+// silu(g) = g / (1 + e^-g), the gate nonlinearity of a SwiGLU FFN, as
+// g * rcp(1 + 2^(-g log2 e)) with the hardware exp2 and reciprocal (each
+// about 1 ulp; six instructions per tile against about 25 for expf and an
+// IEEE division, on a path bound by VALU issue).  The rounded product
+// -g log2 e adds about |g| 2^-24 relative error to e^-g, which reaches h only
+// in proportion e^-g / (1 + e^-g): where g is very negative and silu(g) is
+// already tiny.  Below about -88, e^-g overflows to +inf and the result is
+// -0, the limit.
+__device__ __forceinline__ float silu(float g) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
+}
+
 // Reduce a tile and store its rows: to y when this wave covers all of K, else
 // this wave's K-slice sums to its LDS column `part` (indexed by row - r_begin).
-template <class P, typename XT, int R>
+template <class P, typename XT, int R, bool GLU = false>
 __device__ __forceinline__ void finish_tile(const P& pol, const typename P::Frag* f,
                                             const typename P::template XSliceT<XT>& xs, float* y, int row0,
                                             int r_begin, int r_end, int kw, int lane, float* part) {
@@ -106,6 +132,13 @@ __device__ __forceinline__ void finish_tile(const P& pol, const typename P::Frag
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = pol.template dot<XT>(f[r], xs);
   const float t = reduce_rows<R>(acc, lane);
+  if constexpr (GLU) {
+    // even lanes hold the gate row's total, odd lanes the up row's; lane 0
+    // takes lane 1's and writes h[i] = silu(g) * u for the pair's row i
+    const float u = dpp<0xB1>(t);  // quad_perm [1,0,3,2]
+    if (lane == 0 && row0 < r_end) y[row0 >> 1] = silu(t) * u;
+    return;
+  }
   if (lane < R && row0 + lane < r_end) {
     // The LDS write is a relaxed atomic store (a plain ds_write) so that the
     // compiler cannot merge the two stores into one generic-pointer store:
@@ -122,9 +155,10 @@ __device__ __forceinline__ void finish_tile(const P& pol, const typename P::Frag
 // One matrix of a launch, as laid out by plan_gemv (host).
 struct GemvItem {
   const uint8_t* w;
+  const uint8_t* w_up;  // gate/up launches (GLU): the up matrix, w the gate
   uint64_t scales_offset;
   const void* x;      // [batch][cols]
-  float* y;           // [batch][rows]
+  float* y;           // [batch][rows]; GLU: h, [batch][rows / 2]
   int rows, cols;
   int kw;             // waves along K
   int sets_per_wg;    // row sets per workgroup (kw waves each)
@@ -138,9 +172,15 @@ struct GemvLaunch {
   GemvItem item[kMaxItems];
 };
 
-template <class P, typename XT, int R, int D, int MAXT, bool SX>
-__global__ void __launch_bounds__(MAXT)
-gemv_kernel(const GemvLaunch args) {
+// The body of gemv_kernel and gemv_glu_kernel.  GLU: the gate and up
+// matrices of a SwiGLU FFN as one launch of 2 x rows rows, rows 2i and
+// 2i + 1 being gate row i and up row i, so that each two-row tile holds both
+// projections of one output and its epilogue writes h = silu(gate . x) *
+// (up . x) in place of the two results (only with SX and R = 2: every row
+// within one wave's K slice).
+template <class P, typename XT, int R, int D, int MAXT, bool SX, bool GLU>
+__device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
+  static_assert(!GLU || (SX && R == 2), "gate/up tiles are two rows within one wave's K slice");
   // This workgroup's matrix (wave-uniform scan over at most kMaxItems).
   int it = 0;
 #pragma unroll 1
@@ -158,7 +198,7 @@ gemv_kernel(const GemvLaunch args) {
   // waves to the x copy and give them no rows.
   if (!SX && set >= m.nsets) return;
   const XT* x = static_cast<const XT*>(m.x) + static_cast<size_t>(blockIdx.y) * m.cols;
-  float* y = m.y + static_cast<size_t>(blockIdx.y) * m.rows;
+  float* y = m.y + static_cast<size_t>(blockIdx.y) * (GLU ? m.rows / 2 : m.rows);
   int r_begin = set * m.q + R * min(set, m.rem);
   int r_end = min(r_begin + m.q + (set < m.rem ? R : 0), m.rows);
   if (SX && set >= m.nsets) r_begin = r_end = m.rows;  // tile loads clamp to the last row
@@ -169,6 +209,7 @@ gemv_kernel(const GemvLaunch args) {
   extern __shared__ float part_lds[];
   float* part = part_lds + wave * args.part_stride;
   const P pol(m.w, m.scales_offset, m.cols, kslot, lane);
+  const P pol_up(GLU ? m.w_up : m.w, m.scales_offset, m.cols, kslot, lane);  // GLU only
 
   uint4 raw[P::kXElems * sizeof(XT) / 16];
   typename P::Frag f[D][R];
@@ -194,7 +235,7 @@ gemv_kernel(const GemvLaunch args) {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
+    for (int j = 0; j < D; ++j) load_tile_of<P, R, GLU>(pol, pol_up, f[j], r_begin + j * R, r_last);
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     u32x4* xl = reinterpret_cast<u32x4*>(part_lds);
@@ -207,7 +248,7 @@ gemv_kernel(const GemvLaunch args) {
     pol.load_x_raw(XGlobal<XT>{x}, raw);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < D; ++j) load_tile<P, R>(pol, f[j], r_begin + j * R, r_last);
+    for (int j = 0; j < D; ++j) load_tile_of<P, R, GLU>(pol, pol_up, f[j], r_begin + j * R, r_last);
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -236,8 +277,8 @@ gemv_kernel(const GemvLaunch args) {
   for (int t = D; t < ntiles; t += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-      finish_tile<P, XT, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
-      load_tile<P, R>(pol, f[j], r0 + (j + D) * R, r_last);
+      finish_tile<P, XT, R, GLU>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
+      load_tile_of<P, R, GLU>(pol, pol_up, f[j], r0 + (j + D) * R, r_last);
       __asm__ __volatile__("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -245,7 +286,7 @@ gemv_kernel(const GemvLaunch args) {
   }
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (r0 + j * R < r_end) finish_tile<P, XT, R>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
+    if (r0 + j * R < r_end) finish_tile<P, XT, R, GLU>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
 
   // K split: after one barrier, the kw waves of the set add the columns of
   // their set in slot order, row by row (waves that left early count as
@@ -259,6 +300,19 @@ gemv_kernel(const GemvLaunch args) {
       y[r_begin + j] = v;
     }
   }
+}
+
+template <class P, typename XT, int R, int D, int MAXT, bool SX>
+__global__ void __launch_bounds__(MAXT)
+gemv_kernel(const GemvLaunch args) {
+  gemv_body<P, XT, R, D, MAXT, SX, false>(args);
+}
+
+// The gate/up launch of a SwiGLU FFN (gemv_body with GLU).
+template <class P, typename XT, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+gemv_glu_kernel(const GemvLaunch args) {
+  gemv_body<P, XT, 2, 2, MAXT, true, true>(args);
 }
 
 // Batches of activation rows against matrices within one wave's K slice: the
@@ -627,6 +681,7 @@ inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_wav
     GemvItem& m = L->item[i];
     const qmv_weights* W = calls[i].W;
     m.w = static_cast<const uint8_t*>(W->data);
+    m.w_up = nullptr;
     m.scales_offset = W->scales_offset;
     m.x = calls[i].x;
     m.y = calls[i].y;
@@ -683,10 +738,15 @@ inline size_t sx_lds_bytes(const GemvCall* calls, int n) {
   return static_cast<size_t>(chunks) * 16;
 }
 
-template <class P, typename XT, int R, int D, int MAXT, bool SX>
+template <class P, typename XT, int R, int D, int MAXT, bool SX, bool GLU = false>
 hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream,
-                      int waves_per_simd) {
-  auto kernel = gemv_kernel<P, XT, R, D, MAXT, SX>;
+                      int waves_per_simd, const void* w_up = nullptr) {
+  const auto kernel = [] {
+    if constexpr (GLU)
+      return gemv_glu_kernel<P, XT, MAXT>;
+    else
+      return gemv_kernel<P, XT, R, D, MAXT, SX>;
+  }();
   const int block = 64 * waves;
   if (SX && block != MAXT) return hipErrorInvalidValue;  // the x copy assumes MAXT threads
   const int cus = device_cus();
@@ -710,6 +770,7 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   if (target > resident) target = resident;
   GemvLaunch L;
   const int grid = plan_gemv<P, R>(calls, n, waves, target, &L);
+  if (GLU) L.item[0].w_up = static_cast<const uint8_t*>(w_up);
   size_t lds = static_cast<size_t>(waves) * L.part_stride * sizeof(float);
   if (SX) lds = sx_lds_bytes<XT>(calls, n);
   hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(block), lds, stream,
@@ -917,6 +978,25 @@ hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStr
   if (waves <= 4) return launch_cfg<P, XT, 2, 2, 256, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
   if (waves <= 8) return launch_cfg<P, XT, 2, 2, 512, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
   return launch_cfg<P, XT, 1, 2, 1024, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
+}
+
+// The gate/up launch of a SwiGLU FFN (GLU): `gate` describes the gate
+// matrix with twice its rows (rows 2i, 2i + 1 = gate row i, up row i) and
+// gate.y is h; `up` is the up matrix's data, of the same format, layout and
+// shape.  Every row within one wave's K slice (checked by the caller).
+template <class P>
+hipError_t launch_gemv_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch,
+                           hipStream_t stream) {
+  if (max_kw<P>(&gate, 1) != 1 || (gate.W->rows & 1)) return hipErrorInvalidValue;
+  switch (x_dtype) {
+    case QMV_F32:
+      return launch_cfg<P, float, 2, 2, 256, true, true>(&gate, 1, 4, batch, stream, kMaxWavesPerSimd, up);
+    case QMV_F16:
+      return launch_cfg<P, _Float16, 2, 2, 256, true, true>(&gate, 1, 4, batch, stream, kMaxWavesPerSimd, up);
+    case QMV_BF16:
+      return launch_cfg<P, bf16_t, 2, 2, 256, true, true>(&gate, 1, 4, batch, stream, kMaxWavesPerSimd, up);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 template <class P>

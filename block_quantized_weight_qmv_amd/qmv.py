@@ -70,6 +70,8 @@ _SIGS = {
     "qmv_workspace_size": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32,
                                   ctypes.POINTER(_u64)]),
     "qmv_gemv_multi_ws": (_i32, [_i32, _i32, _i64, ctypes.POINTER(QmvGemvItem), _i32, _p, _u64, _p]),
+    "qmv_gemv_swiglu": (_i32, [_i32, ctypes.POINTER(QmvWeights), ctypes.POINTER(QmvWeights), _p, _i32, _p,
+                               _i64, _i64, _i64, _p]),
     "qmv_dequant": (_i32, [ctypes.POINTER(QmvWeights), _p, _i32, _p]),
     "qmv_probe_read_outputs": (_i64, [_u64]),
     "qmv_probe_read": (_i32, [_p, _u64, _p, _p]),
@@ -347,6 +349,16 @@ def qmv_gemv_multi_ws(fmt, x_dtype, batch: int, items, workspace, workspace_byte
     _check(lib().qmv_gemv_multi_ws(_fmt(fmt), _dtype(x_dtype), batch, arr, len(items),
                                    _ptr(workspace) if workspace is not None else None,
                                    workspace_bytes, _stream(stream, *tensors)))
+
+
+def qmv_gemv_swiglu(fmt, Wg: QmvWeights, Wu: QmvWeights, x, x_dtype, h, rows: int, cols: int, batch: int,
+                    stream=None) -> None:
+    """h = silu(Wg x) * (Wu x) in one launch (h: [batch][rows] fp32)."""
+    xd = _dtype(x_dtype)
+    _check_dev(x, "x", xd, batch * cols)
+    _check_dev(h, "h", 0, batch * rows)
+    _check(lib().qmv_gemv_swiglu(_fmt(fmt), ctypes.byref(Wg), ctypes.byref(Wu), _ptr(x), xd, _ptr(h),
+                                 rows, cols, batch, _stream(stream, x, h)))
 
 
 def qmv_dequant(W: QmvWeights, out, out_dtype, stream=None) -> None:

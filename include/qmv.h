@@ -327,6 +327,34 @@ int32_t qmv_gemv_multi_ws(int32_t fmt, int32_t x_dtype, int64_t batch,
                           void* workspace, uint64_t workspace_bytes,
                           void* stream);
 
+/* h = silu(W_gate x) * (W_up x), elementwise, for `batch` activation rows:
+ * the input of a SwiGLU FFN's down projection (hipfire, the Qwen2 decoder's
+ * "Key Technical Specifications": a SwiGLU FFN), silu(g) = g / (1 + e^-g),
+ * in one launch whose epilogue combines the two projections of each output,
+ * so neither g nor u is written to memory.  The unfused chain stays
+ * available and is the correctness baseline (hipEngine 0.3.0, "Core
+ * principles": fused composites coexist with a numerically equivalent
+ * unfused chain): qmv_gemv_multi over the two matrices, then silu(g) * u.
+ * Wg and Wu are the gate and up matrices, of format fmt, both rows x cols
+ * and in one layout (QMV_ERR_FORMAT / QMV_ERR_UNSUPPORTED otherwise); x is
+ * [batch][cols] of x_dtype (QMV_F32, QMV_F16 or QMV_BF16), h is
+ * [batch][rows] fp32, overwritten; both device pointers, 16-byte aligned,
+ * not overlapping (QMV_ERR_SHAPE).  Every row must lie within one wave's K
+ * slice: cols <= 4096 (Q8_0: 2048), else QMV_ERR_UNSUPPORTED.  Each
+ * activation row is one pass over both matrices (the batch-1 GEMV per
+ * row), each output pair (g, u) is computed with the arithmetic of the
+ * GEMV's two-row tiles, and silu(g) = g * rcp(1 + 2^(-g log2 e)) uses the
+ * hardware exp2 and reciprocal (about 1 ulp each): h differs from
+ * silu(g) * u of the same kernel's g and u only in the rounding of the
+ * epilogue (relative error within a few ulp, plus about |g| 2^-24 where g is
+ * very negative and h tiny; -0 below g = -88).
+ * Enqueues on `stream` and returns; no workspace; legal inside HIP stream
+ * capture. */
+int32_t qmv_gemv_swiglu(int32_t fmt, const qmv_weights* Wg,
+                        const qmv_weights* Wu, const void* x, int32_t x_dtype,
+                        float* h, int64_t rows, int64_t cols, int64_t batch,
+                        void* stream);
+
 /* out = W as a dense [rows][cols] matrix of out_dtype (QMV_F32: the exact
  * value rounded once to fp32, bit-exact; QMV_F16 / QMV_BF16: that fp32 value
  * rounded to nearest-even).  out is a 16-byte aligned device pointer to

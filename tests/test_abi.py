@@ -142,6 +142,29 @@ def test_workspace_size_and_caller_workspace_errors():
     _expect(-5, qmv.qmv_gemv_noalloc, "q4_k", down, FAKE, "bf16", FAKE, 3584, 18944, 2048)
 
 
+def test_swiglu_validation_errors():
+    g, u = _desc("q4_k", 8, 512), _desc("q4_k", 8, 512)
+    f = qmv.qmv_gemv_swiglu
+    H = FAKE + 4096
+    _expect(-2, f, "q6_k", g, u, FAKE, "f32", H, 8, 512, 1)                 # fmt disagrees
+    _expect(-2, f, "q4_k", g, _desc("q4_k", 9, 512), FAKE, "f32", H, 8, 512, 1)
+    _expect(-2, f, "q4_k", g, u, FAKE, "f32", H, 8, 256, 1)
+    pl = qmv.qmv_create_weights_planes("q4_k", 8, 512, FAKE, qmv.qmv_planes_size("q4_k", 8, 512))
+    _expect(-6, f, "q4_k", g, pl, FAKE, "f32", H, 8, 512, 1)                # layouts differ
+    _expect(-1, f, "q4_k", g, u, None, "f32", H, 8, 512, 1)
+    _expect(-4, f, "q4_k", g, u, FAKE, "f32", H + 4, 8, 512, 1)
+    _expect(-3, f, "q4_k", g, u, FAKE, "f32", H, 8, 512, 0)
+    _expect(-6, f, "q4_k", g, u, FAKE, 7, H, 8, 512, 1)
+    _expect(-3, f, "q4_k", g, u, FAKE, "f32", FAKE + 16, 8, 512, 1)          # h overlaps x
+    w17 = _desc("q4_k", 8, 17 * 256)                                         # past one wave's K slice
+    _expect(-6, f, "q4_k", w17, w17, FAKE, "f32", FAKE + (1 << 20), 8, 17 * 256, 1)
+    q8 = _desc("q8_0", 8, 2080)
+    _expect(-6, f, "q8_0", q8, q8, FAKE, "f32", FAKE + (1 << 20), 8, 2080, 1)
+    bad = _desc()
+    bad.nbytes += 144
+    _expect(-5, f, "q4_k", g, bad, FAKE, "f32", H, 8, 512, 1)
+
+
 def test_dequant_and_probe_validation_errors():
     w = _desc()
     _expect(-1, qmv.qmv_dequant, w, None, "f32")
