@@ -51,6 +51,8 @@ CSRC = os.path.join(ROOT, "block_quantized_weight_qmv_amd", "csrc")
 _KERNEL_SOURCES = {
     "gemv_kernel": ["gemv_skeleton.h", "device_util.h"],
     "gemv_rows_kernel": ["gemv_skeleton.h", "device_util.h"],
+    "gemv_pair_kernel": ["gemv_skeleton.h", "device_util.h"],
+    "gemv_glu_kernel": ["gemv_skeleton.h", "device_util.h"],
     "gemm_q4_k_stream": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_ksplit": ["gemm_q4_k_mfma.hip", "device_util.h"],
     "gemm_q4_k_tile": ["gemm_q4_k_mfma.hip", "device_util.h"],
@@ -196,7 +198,9 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     5-16 fp16/bf16 rows (rows_list summing to at most 8192) -> one multi-row
     launch; Q4_K x fp16/bf16 from 128 rows (from 64 against 8192 columns and
     more) against matrices of at least 256 rows -> gemm_q4_k_dqreg in the
-    form dqreg_plan picks; the first matrix of a group names the group)."""
+    form dqreg_plan picks; one activation row against two matrices of one
+    shape within one wave's K slice (gate, up) -> the paired kernel; the
+    first matrix of a group names the group)."""
     nb_max = max(cols_list) // 256
     if (fmt == "q4_k" and x_dtype in ("f16", "bf16") and 5 <= batch <= 16 and len(cols_list) >= 2
             and max(cols_list) <= 4096 and rows_list is not None and sum(rows_list) <= 8192):
@@ -254,6 +258,10 @@ def kernel_name(fmt: str, cols_list, x_dtype: str, batch: int = 1, layout: str =
     xt = {"f32": "float", "f16": "_Float16", "bf16": "qmv::bf16_t"}[x_dtype]
     if len(cols_list) == 1 and 2 <= kw <= 8:   # one matrix split along K: slices in LDS
         return f"qmv::gemv_lx_kernel<qmv::{pol}, {xt}, 2, 2, 512>"
+    if (batch == 1 and kw == 1 and len(cols_list) == 2 and cols_list[0] == cols_list[1]
+            and rows_list is not None and rows_list[0] == rows_list[1]):
+        # two matrices of one shape on one activation (gate, up): rows paired per tile
+        return f"qmv::gemv_pair_kernel<qmv::{pol}, {xt}, 256>"
     if kw == 1:   # the shared-activation kernel; INT4 with one-row tiles, three in flight
         cfg = "1, 3, 256, true" if fmt == "int4_g128" else "2, 2, 256, true"
     else:
@@ -473,6 +481,10 @@ _F16_FORMS = [
      lambda m: f"qmv::gemv_rows_kernel<qmv::{m[1]}, _Float16, {m[2]}, {m[3]}, {m[4]}, {m[5]}>"),
     (r"_ZN3qmv22gemv_rows_split_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi",
      lambda m: f"qmv::gemv_rows_split_kernel<qmv::{m[1]}, _Float16, {m[2]}, {m[3]}, {m[4]}>"),
+    (r"_ZN3qmv16gemv_pair_kernelINS_\d+(\w+?)EDF16_Li(\d+)EEEvNS_10GemvLaunchE",
+     lambda m: f"qmv::gemv_pair_kernel<qmv::{m[1]}, _Float16, {m[2]}>"),
+    (r"_ZN3qmv15gemv_glu_kernelINS_\d+(\w+?)EDF16_Li(\d+)EEEvNS_10GemvLaunchE",
+     lambda m: f"qmv::gemv_glu_kernel<qmv::{m[1]}, _Float16, {m[2]}>"),
 ]
 
 

@@ -106,6 +106,19 @@ using qmv::fail;
 
 namespace qmv {
 
+// A paired launch of two matrices of one format, layout and shape (`a` with
+// twice its rows; launch.h): both outputs, or with glu the SwiGLU input.
+static hipError_t pair_launch(int32_t fmt, const GemvCall& a, const void* b_w, float* b_y, int32_t x_dtype,
+                              int64_t batch, bool planes, bool glu, hipStream_t s) {
+  switch (fmt) {
+    case QMV_Q8_0: return gemv_q8_0_pair(a, b_w, b_y, x_dtype, batch, glu, s);
+    case QMV_Q4_K: return gemv_q4_k_pair(a, b_w, b_y, x_dtype, batch, planes, glu, s);
+    case QMV_Q5_K: return gemv_q5_k_pair(a, b_w, b_y, x_dtype, batch, planes, glu, s);
+    case QMV_Q6_K: return gemv_q6_k_pair(a, b_w, b_y, x_dtype, batch, planes, glu, s);
+    default: return gemv_int4_g128_pair(a, b_w, b_y, x_dtype, batch, glu, s);
+  }
+}
+
 static int32_t take_workspace(const WsMode& ws, uint64_t need, void** out) {
   if (out) *out = nullptr;
   if (ws.need) {
@@ -448,6 +461,19 @@ static int32_t gemv_multi_impl(int32_t fmt, int32_t x_dtype, int64_t batch, cons
                          "qmv_gemv (matrix-core) launch");
   }
   if (ws.need) return qmv::take_workspace(ws, 0, nullptr);
+  // Two matrices of one shape on one activation within one wave's K slice
+  // (gate and up): one launch whose two-row tiles pair row i of each
+  // (7B gate+up, Q4_K planes, fp32 x: 15.3 against 15.5 us as two items;
+  // INT4, fp16 x: 13.2 against 13.9 us).
+  if (batch == 1 && n == 2 && items[0].x == items[1].x && items[0].W->rows == items[1].W->rows &&
+      items[0].W->cols == items[1].W->cols && items[0].W->cols <= wave_cols &&
+      items[0].W->rows <= INT32_MAX / 2) {
+    qmv_weights pair = *items[0].W;
+    pair.rows = 2 * items[0].W->rows;
+    const qmv::GemvCall a{&pair, items[0].x, items[0].y};
+    return qmv::from_hip(qmv::pair_launch(fmt, a, items[1].W->data, items[1].y, x_dtype, batch, planes, false, s),
+                         "qmv_gemv (paired matrices) launch");
+  }
   switch (fmt) {
     case QMV_Q8_0: e = qmv::gemv_q8_0(calls, n, x_dtype, batch, s); break;
     case QMV_Q4_K:
@@ -499,17 +525,9 @@ int32_t qmv_gemv_swiglu(int32_t fmt, const qmv_weights* Wg, const qmv_weights* W
   qmv_weights pair = *Wg;  // launch rows 2i, 2i + 1 = gate row i, up row i
   pair.rows = 2 * rows;
   const qmv::GemvCall gate{&pair, x, h};
-  const bool planes = Wg->layout == QMV_LAYOUT_PLANES;
-  const hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (fmt) {
-    case QMV_Q8_0: e = qmv::gemv_q8_0_glu(gate, Wu->data, x_dtype, batch, s); break;
-    case QMV_Q4_K: e = qmv::gemv_q4_k_glu(gate, Wu->data, x_dtype, batch, planes, s); break;
-    case QMV_Q5_K: e = qmv::gemv_q5_k_glu(gate, Wu->data, x_dtype, batch, planes, s); break;
-    case QMV_Q6_K: e = qmv::gemv_q6_k_glu(gate, Wu->data, x_dtype, batch, planes, s); break;
-    default: e = qmv::gemv_int4_g128_glu(gate, Wu->data, x_dtype, batch, s); break;
-  }
-  return qmv::from_hip(e, "qmv_gemv_swiglu launch");
+  return qmv::from_hip(qmv::pair_launch(fmt, gate, Wu->data, nullptr, x_dtype, batch,
+                                       Wg->layout == QMV_LAYOUT_PLANES, true, static_cast<hipStream_t>(stream)),
+                       "qmv_gemv_swiglu launch");
 }
 
 int32_t qmv_dequant(const qmv_weights* W, void* out, int32_t out_dtype, void* stream) {

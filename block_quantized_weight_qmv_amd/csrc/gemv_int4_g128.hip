@@ -236,9 +236,9 @@ hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t bat
   return launch_gemv<Int4G128Policy>(calls, n, x_dtype, batch, s);
 }
 
-hipError_t gemv_int4_g128_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch,
-                              hipStream_t s) {
-  return launch_gemv_glu<Int4G128Policy>(gate, up, x_dtype, batch, s);
+hipError_t gemv_int4_g128_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                               bool glu, hipStream_t s) {
+  return launch_gemv_pair<Int4G128Policy>(a, b_w, b_y, x_dtype, batch, glu, s);
 }
 
 }  // namespace qmv

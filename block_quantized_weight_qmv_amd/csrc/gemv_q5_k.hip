@@ -267,10 +267,10 @@ hipError_t gemv_q5_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t b
   return launch_gemv<Q5KPlanesPolicy>(calls, n, x_dtype, batch, s);
 }
 
-hipError_t gemv_q5_k_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, bool planes,
-                         hipStream_t s) {
-  return planes ? launch_gemv_glu<Q5KPlanesPolicy>(gate, up, x_dtype, batch, s)
-                : launch_gemv_glu<Q5KPolicy>(gate, up, x_dtype, batch, s);
+hipError_t gemv_q5_k_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                          bool planes, bool glu, hipStream_t s) {
+  return planes ? launch_gemv_pair<Q5KPlanesPolicy>(a, b_w, b_y, x_dtype, batch, glu, s)
+                : launch_gemv_pair<Q5KPolicy>(a, b_w, b_y, x_dtype, batch, glu, s);
 }
 
 }  // namespace qmv

@@ -275,10 +275,10 @@ hipError_t gemv_q6_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t b
   return launch_gemv<Q6KPlanesPolicy>(calls, n, x_dtype, batch, s);
 }
 
-hipError_t gemv_q6_k_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, bool planes,
-                         hipStream_t s) {
-  return planes ? launch_gemv_glu<Q6KPlanesPolicy>(gate, up, x_dtype, batch, s)
-                : launch_gemv_glu<Q6KPolicy>(gate, up, x_dtype, batch, s);
+hipError_t gemv_q6_k_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                          bool planes, bool glu, hipStream_t s) {
+  return planes ? launch_gemv_pair<Q6KPlanesPolicy>(a, b_w, b_y, x_dtype, batch, glu, s)
+                : launch_gemv_pair<Q6KPolicy>(a, b_w, b_y, x_dtype, batch, glu, s);
 }
 
 }  // namespace qmv

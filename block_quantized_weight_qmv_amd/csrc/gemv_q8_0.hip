@@ -169,8 +169,9 @@ hipError_t gemv_q8_0(const GemvCall* calls, int n, int x_dtype, int64_t batch, h
   return launch_gemv<Q80Policy>(calls, n, x_dtype, batch, s);
 }
 
-hipError_t gemv_q8_0_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, hipStream_t s) {
-  return launch_gemv_glu<Q80Policy>(gate, up, x_dtype, batch, s);
+hipError_t gemv_q8_0_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch, bool glu,
+                          hipStream_t s) {
+  return launch_gemv_pair<Q80Policy>(a, b_w, b_y, x_dtype, batch, glu, s);
 }
 
 }  // namespace qmv

@@ -96,12 +96,20 @@ __device__ __forceinline__ void load_tile(const P& pol, typename P::Frag* f, int
   for (int r = 0; r < R; ++r) pol.load(min(row0 + r, r_last), f[r]);
 }
 
-// A tile of the gate/up launch (GLU): launch rows 2i and 2i + 1 are row i of
-// the gate matrix (pol) and of the up matrix (pol_up); row0 is even.
-template <class P, int R, bool GLU>
+// Paired launches: two matrices of one shape and one activation as a single
+// launch of 2 x rows rows, rows 2i and 2i + 1 being row i of the first
+// matrix (w) and of the second (w_up), so each two-row tile holds both
+// matrices' row i.  kPairOut writes both results (y, y_up); kPairGlu, the
+// gate and up projections of a SwiGLU FFN, writes h = silu(gate . x) *
+// (up . x) to y in their place.
+constexpr int kPairNone = 0, kPairOut = 1, kPairGlu = 2;
+
+// A tile of a paired launch: rows 2i and 2i + 1 are row i of the first
+// matrix (pol) and of the second (pol_up); row0 is even.
+template <class P, int R, int PM>
 __device__ __forceinline__ void load_tile_of(const P& pol, const P& pol_up, typename P::Frag* f, int row0,
                                              int r_last) {
-  if constexpr (GLU) {
+  if constexpr (PM != kPairNone) {
     const int i = min(row0, r_last) >> 1;
     pol.load(i, f[0]);
     pol_up.load(i, f[1]);
@@ -124,19 +132,25 @@ __device__ __forceinline__ float silu(float g) {
 
 // Reduce a tile and store its rows: to y when this wave covers all of K, else
 // this wave's K-slice sums to its LDS column `part` (indexed by row - r_begin).
-template <class P, typename XT, int R, bool GLU = false>
+template <class P, typename XT, int R, int PM = kPairNone>
 __device__ __forceinline__ void finish_tile(const P& pol, const typename P::Frag* f,
                                             const typename P::template XSliceT<XT>& xs, float* y, int row0,
-                                            int r_begin, int r_end, int kw, int lane, float* part) {
+                                            int r_begin, int r_end, int kw, int lane, float* part,
+                                            float* y_up = nullptr) {
   float acc[R];
 #pragma unroll
   for (int r = 0; r < R; ++r) acc[r] = pol.template dot<XT>(f[r], xs);
   const float t = reduce_rows<R>(acc, lane);
-  if constexpr (GLU) {
-    // even lanes hold the gate row's total, odd lanes the up row's; lane 0
-    // takes lane 1's and writes h[i] = silu(g) * u for the pair's row i
+  // paired launches: even lanes hold the first matrix's row total, odd lanes
+  // the second's
+  if constexpr (PM == kPairGlu) {
+    // lane 0 takes lane 1's and writes h[i] = silu(g) * u for the pair's row i
     const float u = dpp<0xB1>(t);  // quad_perm [1,0,3,2]
     if (lane == 0 && row0 < r_end) y[row0 >> 1] = silu(t) * u;
+    return;
+  }
+  if constexpr (PM == kPairOut) {
+    if (lane < 2 && row0 < r_end) (lane ? y_up : y)[row0 >> 1] = t;
     return;
   }
   if (lane < R && row0 + lane < r_end) {
@@ -155,10 +169,11 @@ __device__ __forceinline__ void finish_tile(const P& pol, const typename P::Frag
 // One matrix of a launch, as laid out by plan_gemv (host).
 struct GemvItem {
   const uint8_t* w;
-  const uint8_t* w_up;  // gate/up launches (GLU): the up matrix, w the gate
+  const uint8_t* w_up;  // paired launches: the second matrix
   uint64_t scales_offset;
   const void* x;      // [batch][cols]
-  float* y;           // [batch][rows]; GLU: h, [batch][rows / 2]
+  float* y;           // [batch][rows]; paired: [batch][rows / 2] (kPairGlu: h)
+  float* y_up;        // kPairOut: the second matrix's [batch][rows / 2]
   int rows, cols;
   int kw;             // waves along K
   int sets_per_wg;    // row sets per workgroup (kw waves each)
@@ -172,15 +187,12 @@ struct GemvLaunch {
   GemvItem item[kMaxItems];
 };
 
-// The body of gemv_kernel and gemv_glu_kernel.  GLU: the gate and up
-// matrices of a SwiGLU FFN as one launch of 2 x rows rows, rows 2i and
-// 2i + 1 being gate row i and up row i, so that each two-row tile holds both
-// projections of one output and its epilogue writes h = silu(gate . x) *
-// (up . x) in place of the two results (only with SX and R = 2: every row
-// within one wave's K slice).
-template <class P, typename XT, int R, int D, int MAXT, bool SX, bool GLU>
+// The body of gemv_kernel, gemv_pair_kernel and gemv_glu_kernel (PM: the
+// paired modes above, only with SX and R = 2: every row within one wave's K
+// slice).
+template <class P, typename XT, int R, int D, int MAXT, bool SX, int PM>
 __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
-  static_assert(!GLU || (SX && R == 2), "gate/up tiles are two rows within one wave's K slice");
+  static_assert(PM == kPairNone || (SX && R == 2), "paired tiles are two rows within one wave's K slice");
   // This workgroup's matrix (wave-uniform scan over at most kMaxItems).
   int it = 0;
 #pragma unroll 1
@@ -198,7 +210,8 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
   // waves to the x copy and give them no rows.
   if (!SX && set >= m.nsets) return;
   const XT* x = static_cast<const XT*>(m.x) + static_cast<size_t>(blockIdx.y) * m.cols;
-  float* y = m.y + static_cast<size_t>(blockIdx.y) * (GLU ? m.rows / 2 : m.rows);
+  float* y = m.y + static_cast<size_t>(blockIdx.y) * (PM != kPairNone ? m.rows / 2 : m.rows);
+  float* y_up = PM == kPairOut ? m.y_up + static_cast<size_t>(blockIdx.y) * (m.rows / 2) : nullptr;
   int r_begin = set * m.q + R * min(set, m.rem);
   int r_end = min(r_begin + m.q + (set < m.rem ? R : 0), m.rows);
   if (SX && set >= m.nsets) r_begin = r_end = m.rows;  // tile loads clamp to the last row
@@ -209,7 +222,7 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
   extern __shared__ float part_lds[];
   float* part = part_lds + wave * args.part_stride;
   const P pol(m.w, m.scales_offset, m.cols, kslot, lane);
-  const P pol_up(GLU ? m.w_up : m.w, m.scales_offset, m.cols, kslot, lane);  // GLU only
+  const P pol_up(PM != kPairNone ? m.w_up : m.w, m.scales_offset, m.cols, kslot, lane);  // paired only
 
   uint4 raw[P::kXElems * sizeof(XT) / 16];
   typename P::Frag f[D][R];
@@ -235,7 +248,7 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
     }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < D; ++j) load_tile_of<P, R, GLU>(pol, pol_up, f[j], r_begin + j * R, r_last);
+    for (int j = 0; j < D; ++j) load_tile_of<P, R, PM>(pol, pol_up, f[j], r_begin + j * R, r_last);
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
     u32x4* xl = reinterpret_cast<u32x4*>(part_lds);
@@ -248,7 +261,7 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
     pol.load_x_raw(XGlobal<XT>{x}, raw);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int j = 0; j < D; ++j) load_tile_of<P, R, GLU>(pol, pol_up, f[j], r_begin + j * R, r_last);
+    for (int j = 0; j < D; ++j) load_tile_of<P, R, PM>(pol, pol_up, f[j], r_begin + j * R, r_last);
     __asm__ __volatile__("" ::: "memory");
     __builtin_amdgcn_sched_barrier(0);
   }
@@ -277,8 +290,8 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
   for (int t = D; t < ntiles; t += D) {
 #pragma unroll
     for (int j = 0; j < D; ++j) {
-      finish_tile<P, XT, R, GLU>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
-      load_tile_of<P, R, GLU>(pol, pol_up, f[j], r0 + (j + D) * R, r_last);
+      finish_tile<P, XT, R, PM>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part, y_up);
+      load_tile_of<P, R, PM>(pol, pol_up, f[j], r0 + (j + D) * R, r_last);
       __asm__ __volatile__("" ::: "memory");
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -286,7 +299,8 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
   }
 #pragma unroll
   for (int j = 0; j < D; ++j)
-    if (r0 + j * R < r_end) finish_tile<P, XT, R, GLU>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part);
+    if (r0 + j * R < r_end)
+      finish_tile<P, XT, R, PM>(pol, f[j], xs, y, r0 + j * R, r_begin, r_end, kw, lane, part, y_up);
 
   // K split: after one barrier, the kw waves of the set add the columns of
   // their set in slot order, row by row (waves that left early count as
@@ -305,14 +319,21 @@ __device__ __forceinline__ void gemv_body(const GemvLaunch& args) {
 template <class P, typename XT, int R, int D, int MAXT, bool SX>
 __global__ void __launch_bounds__(MAXT)
 gemv_kernel(const GemvLaunch args) {
-  gemv_body<P, XT, R, D, MAXT, SX, false>(args);
+  gemv_body<P, XT, R, D, MAXT, SX, kPairNone>(args);
 }
 
-// The gate/up launch of a SwiGLU FFN (gemv_body with GLU).
+// Two matrices of one shape on one activation, paired row by row (kPairOut).
+template <class P, typename XT, int MAXT>
+__global__ void __launch_bounds__(MAXT)
+gemv_pair_kernel(const GemvLaunch args) {
+  gemv_body<P, XT, 2, 2, MAXT, true, kPairOut>(args);
+}
+
+// The gate/up launch of a SwiGLU FFN (kPairGlu).
 template <class P, typename XT, int MAXT>
 __global__ void __launch_bounds__(MAXT)
 gemv_glu_kernel(const GemvLaunch args) {
-  gemv_body<P, XT, 2, 2, MAXT, true, true>(args);
+  gemv_body<P, XT, 2, 2, MAXT, true, kPairGlu>(args);
 }
 
 // Batches of activation rows against matrices within one wave's K slice: the
@@ -682,6 +703,7 @@ inline int plan_gemv(const GemvCall* calls, int n, int waves, int64_t target_wav
     const qmv_weights* W = calls[i].W;
     m.w = static_cast<const uint8_t*>(W->data);
     m.w_up = nullptr;
+    m.y_up = nullptr;
     m.scales_offset = W->scales_offset;
     m.x = calls[i].x;
     m.y = calls[i].y;
@@ -738,12 +760,14 @@ inline size_t sx_lds_bytes(const GemvCall* calls, int n) {
   return static_cast<size_t>(chunks) * 16;
 }
 
-template <class P, typename XT, int R, int D, int MAXT, bool SX, bool GLU = false>
+template <class P, typename XT, int R, int D, int MAXT, bool SX, int PM = kPairNone>
 hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hipStream_t stream,
-                      int waves_per_simd, const void* w_up = nullptr) {
+                      int waves_per_simd, const void* w_up = nullptr, float* y_up = nullptr) {
   const auto kernel = [] {
-    if constexpr (GLU)
+    if constexpr (PM == kPairGlu)
       return gemv_glu_kernel<P, XT, MAXT>;
+    else if constexpr (PM == kPairOut)
+      return gemv_pair_kernel<P, XT, MAXT>;
     else
       return gemv_kernel<P, XT, R, D, MAXT, SX>;
   }();
@@ -770,7 +794,10 @@ hipError_t launch_cfg(const GemvCall* calls, int n, int waves, int64_t batch, hi
   if (target > resident) target = resident;
   GemvLaunch L;
   const int grid = plan_gemv<P, R>(calls, n, waves, target, &L);
-  if (GLU) L.item[0].w_up = static_cast<const uint8_t*>(w_up);
+  if (PM != kPairNone) {
+    L.item[0].w_up = static_cast<const uint8_t*>(w_up);
+    L.item[0].y_up = y_up;
+  }
   size_t lds = static_cast<size_t>(waves) * L.part_stride * sizeof(float);
   if (SX) lds = sx_lds_bytes<XT>(calls, n);
   hipLaunchKernelGGL(kernel, dim3(grid, static_cast<unsigned>(batch)), dim3(block), lds, stream,
@@ -980,23 +1007,31 @@ hipError_t launch_gemv_typed(const GemvCall* calls, int n, int64_t batch, hipStr
   return launch_cfg<P, XT, 1, 2, 1024, false>(calls, n, waves, batch, stream, kMaxWavesPerSimd);
 }
 
-// The gate/up launch of a SwiGLU FFN (GLU): `gate` describes the gate
-// matrix with twice its rows (rows 2i, 2i + 1 = gate row i, up row i) and
-// gate.y is h; `up` is the up matrix's data, of the same format, layout and
-// shape.  Every row within one wave's K slice (checked by the caller).
-template <class P>
-hipError_t launch_gemv_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch,
-                           hipStream_t stream) {
-  if (max_kw<P>(&gate, 1) != 1 || (gate.W->rows & 1)) return hipErrorInvalidValue;
+// A paired launch: `a` describes the first matrix with twice its rows (rows
+// 2i, 2i + 1 = row i of the first and of the second matrix) and a.y its
+// output (glu: h); `b_w` is the second matrix's data, of the same format,
+// layout and shape, and `b_y` its output (kPairOut only).  Every row within
+// one wave's K slice (checked by the caller).
+template <class P, int PM>
+hipError_t launch_gemv_pair_mode(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                                 hipStream_t stream) {
+  if (max_kw<P>(&a, 1) != 1 || (a.W->rows & 1)) return hipErrorInvalidValue;
   switch (x_dtype) {
     case QMV_F32:
-      return launch_cfg<P, float, 2, 2, 256, true, true>(&gate, 1, 4, batch, stream, kMaxWavesPerSimd, up);
+      return launch_cfg<P, float, 2, 2, 256, true, PM>(&a, 1, 4, batch, stream, kMaxWavesPerSimd, b_w, b_y);
     case QMV_F16:
-      return launch_cfg<P, _Float16, 2, 2, 256, true, true>(&gate, 1, 4, batch, stream, kMaxWavesPerSimd, up);
+      return launch_cfg<P, _Float16, 2, 2, 256, true, PM>(&a, 1, 4, batch, stream, kMaxWavesPerSimd, b_w, b_y);
     case QMV_BF16:
-      return launch_cfg<P, bf16_t, 2, 2, 256, true, true>(&gate, 1, 4, batch, stream, kMaxWavesPerSimd, up);
+      return launch_cfg<P, bf16_t, 2, 2, 256, true, PM>(&a, 1, 4, batch, stream, kMaxWavesPerSimd, b_w, b_y);
     default: return hipErrorInvalidValue;
   }
+}
+
+template <class P>
+hipError_t launch_gemv_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                            bool glu, hipStream_t stream) {
+  return glu ? launch_gemv_pair_mode<P, kPairGlu>(a, b_w, nullptr, x_dtype, batch, stream)
+             : launch_gemv_pair_mode<P, kPairOut>(a, b_w, b_y, x_dtype, batch, stream);
 }
 
 template <class P>

@@ -68,20 +68,23 @@ hipError_t gemv_q6_k_planes(const GemvCall* calls, int n, int x_dtype, int64_t b
 hipError_t gemv_int4_g128(const GemvCall* calls, int n, int x_dtype, int64_t batch,
                           hipStream_t s);
 
-// The gate and up projections of a SwiGLU FFN in one launch whose epilogue
-// writes h = silu(gate . x) * (up . x) (gemv_kernel with GLU): `gate`
-// describes the gate matrix with twice its rows and gate.y is h; `up` is the
-// up matrix's data, same format, layout and shape.  Matrices within one
-// wave's K slice only (4096 columns; Q8_0 2048).
-hipError_t gemv_q8_0_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, hipStream_t s);
-hipError_t gemv_q4_k_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, bool planes,
-                         hipStream_t s);
-hipError_t gemv_q5_k_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, bool planes,
-                         hipStream_t s);
-hipError_t gemv_q6_k_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch, bool planes,
-                         hipStream_t s);
-hipError_t gemv_int4_g128_glu(const GemvCall& gate, const void* up, int x_dtype, int64_t batch,
-                              hipStream_t s);
+// Two matrices of one format, layout and shape on one activation as one
+// launch whose two-row tiles pair row i of each (gemv_pair_kernel): `a`
+// describes the first matrix with twice its rows, a.y its output; b_w is
+// the second matrix's data and b_y its output.  glu: the gate and up
+// projections of a SwiGLU FFN, whose epilogue writes h = silu(gate . x) *
+// (up . x) to a.y in place of both (gemv_glu_kernel; b_y unused).  Matrices
+// within one wave's K slice only (4096 columns; Q8_0 2048).
+hipError_t gemv_q8_0_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch, bool glu,
+                          hipStream_t s);
+hipError_t gemv_q4_k_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                          bool planes, bool glu, hipStream_t s);
+hipError_t gemv_q5_k_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                          bool planes, bool glu, hipStream_t s);
+hipError_t gemv_q6_k_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                          bool planes, bool glu, hipStream_t s);
+hipError_t gemv_int4_g128_pair(const GemvCall& a, const void* b_w, float* b_y, int x_dtype, int64_t batch,
+                               bool glu, hipStream_t s);
 
 // Batched Q4_K x bf16 on MFMA (gemm_q4_k_mfma.hip); the GEMV entry points use
 // it for batches of at least kMfmaMinBatch rows.

@@ -279,7 +279,11 @@ typedef struct qmv_gemv_item {
  * matrices of at most 4096 columns and 8192 rows in all at 5..16 fp16/bf16
  * rows, which share one multi-row launch (each output row then equals the
  * batch-1 result bit for bit) where a call of one of them alone would take
- * the matrix cores.  Uses no workspace. */
+ * the matrix cores.  One activation row against exactly two matrices of one
+ * shape within one wave's K slice on the same x pointer (gate and up) runs
+ * as one launch whose two-row tiles pair row i of both: results equal the
+ * lone calls bit for bit, except INT4 (its lone call runs one-row tiles),
+ * which differs in float32 summation order.  Uses no workspace. */
 int32_t qmv_gemv_multi(int32_t fmt, int32_t x_dtype, int64_t batch,
                        const qmv_gemv_item* items, int32_t n, void* stream);
 

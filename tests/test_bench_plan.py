@@ -35,6 +35,7 @@ def _library_kernels():
     f16_rows = re.compile(r"_ZN3qmv16gemv_rows_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi")
     f16_split = re.compile(r"_ZN3qmv22gemv_rows_split_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLaunchEi")
     f16_lx = re.compile(r"_ZN3qmv14gemv_lx_kernelINS_\d+(\w+?)EDF16_Li(\d+)ELi(\d+)ELi(\d+)EEEvNS_10GemvLxArgsE")
+    f16_pair = re.compile(r"_ZN3qmv16gemv_pair_kernelINS_\d+(\w+?)EDF16_Li(\d+)EEEvNS_10GemvLaunchE")
     for line in out.splitlines():
         m = f16.search(line)
         if m:
@@ -50,13 +51,17 @@ def _library_kernels():
         if m:
             names.add(f"qmv::gemv_lx_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, {m.group(4)}>")
             continue
+        m = f16_pair.search(line)
+        if m:
+            names.add(f"qmv::gemv_pair_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}>")
+            continue
         m = f16_rows.search(line)
         if m:
             names.add(f"qmv::gemv_rows_kernel<qmv::{m.group(1)}, _Float16, {m.group(2)}, {m.group(3)}, "
                       f"{m.group(4)}, {m.group(5)}>")
             continue
         if ("qmv::gemv_kernel<" in line or "qmv::gemv_rows_kernel<" in line or "qmv::gemv_rows_split_kernel<" in line
-                or "qmv::gemv_lx_kernel<" in line
+                or "qmv::gemv_lx_kernel<" in line or "qmv::gemv_pair_kernel<" in line
                 or "qmv::gemm_q4_k_bf16_" in line or "qmv::gemm_q4_k_stream<" in line
                 or "qmv::gemm_q4_k_tile<" in line or "qmv::gemm_q4_k_ksplit<" in line
                 or "qmv::act_rows_f16<" in line or "qmv::gemm_q4_k_dqreg<" in line or "qmv::dqreg_sum" in line):

@@ -192,3 +192,52 @@ def test_multi_register_dequantized_runs(x_dtype, batch):
         apart = oracle.normwise_rel_err(got, alone.astype(np.float64))
         assert np.all(apart <= (2 * TOL if batch < 65 else 1e-5)), (w.rows, w.cols, apart.max())
         assert torch.equal(y_plain, w.gemv(xd, x_dtype, batch, ws=False)), (w.rows, w.cols)
+
+
+PAIR_CASES = [("q8_0", "blocks"), ("q4_k", "blocks"), ("q4_k", "planes"), ("q5_k", "planes"), ("q6_k", "blocks"),
+              ("q6_k", "planes"), ("int4_g128", "blocks")]
+
+
+@pytest.mark.parametrize("x_dtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("rows,eighths", [(1, 8), (67, 3), (4100, 8)])
+@pytest.mark.parametrize("fmt,layout", PAIR_CASES)
+def test_multi_pair_of_one_shape(fmt, layout, rows, eighths, x_dtype):
+    """Two matrices of one shape on one activation row (gate and up) run as
+    one launch whose two-row tiles pair row i of each: every output against
+    the oracle, and against each matrix called alone -- bit for bit where
+    the lone call also runs two-row tiles (every format but INT4, whose lone
+    call runs one-row tiles and so another reduction order)."""
+    qk = oracle.QK[fmt]
+    slice_cols = 2048 if fmt == "q8_0" else 4096
+    cols = max(qk, slice_cols * eighths // 8 // qk * qk)
+    ws = [Weights(fmt, rows, cols, seed=2600 + 5 * i + rows) for i in range(2)]
+    keep, descs = [], []
+    for w in ws:
+        d = w.desc
+        if layout == "planes":
+            buf = torch.empty(qmv.qmv_planes_size(fmt, rows, cols), dtype=torch.uint8, device=DEV)
+            d = qmv.qmv_repack_planes(w.desc, buf)
+            keep.append(buf)
+        descs.append(d)
+    x = gen_x(1, cols, x_dtype, seed=2700 + rows)
+    xd = to_dev_x(x, x_dtype)
+    off = (rows + 4 + 3) // 4 * 4  # the second output 16-byte aligned, a canary gap between
+    ybuf = torch.full((off + rows + 4,), 7.25, dtype=torch.float32, device=DEV)
+    ys = [ybuf[:rows], ybuf[off:off + rows]]
+    say(f"multi pair {fmt} {layout} {rows}x{cols} x {x_dtype}")
+    qmv.qmv_gemv_multi(fmt, x_dtype, 1, [(d, xd, y) for d, y in zip(descs, ys)])
+    torch.cuda.synchronize()
+    host = ybuf.cpu().numpy()
+    assert np.all(host[rows:off] == 7.25) and np.all(host[off + rows:] == 7.25)
+    for w, d, y in zip(ws, descs, ys):
+        got = y.cpu().numpy().reshape(1, rows)
+        err = oracle.normwise_rel_err(got, oracle_y(w, x, x_dtype))
+        assert np.all(err <= TOL), err
+        alone = torch.empty(1, rows, dtype=torch.float32, device=DEV)
+        qmv.qmv_gemv(fmt, d, xd, x_dtype, alone, rows, cols, 1)
+        alone = alone.cpu().numpy()
+        if fmt == "int4_g128":
+            np.testing.assert_allclose(got, alone, rtol=1e-5, atol=1e-5 * np.abs(alone).max())
+        else:
+            np.testing.assert_array_equal(got, alone)
+    del keep
