@@ -82,3 +82,19 @@ def test_dequant_and_create_checks():
     n = qmv.qmv_packed_size("q4_k", 8, 512)
     assert _status(qmv.qmv_create_weights, "q4_k", 8, 512, torch.zeros(n, dtype=torch.uint8)) == -6
     assert _status(qmv.qmv_create_weights, "q4_k", 8, 512, DevTensor(torch.uint8, n - 16), n) == -5
+
+
+def test_swiglu_and_caller_workspace_checks():
+    w = _w()
+    x, h = DevTensor(torch.float32, 512), DevTensor(torch.float32, 8)
+    with pytest.raises(qmv.QmvError, match="not on a GPU"):
+        qmv.qmv_gemv_swiglu("q4_k", w, w, torch.zeros(512), "f32", h, 8, 512, 1)
+    with pytest.raises(qmv.QmvError, match="needs 8"):
+        qmv.qmv_gemv_swiglu("q4_k", w, w, x, "f32", DevTensor(torch.float32, 7), 8, 512, 1)
+    with pytest.raises(qmv.QmvError, match="dtype"):
+        qmv.qmv_gemv_swiglu("q4_k", w, w, DevTensor(torch.float16, 512), "f32", h, 8, 512, 1)
+    ok = (w, x, h)
+    with pytest.raises(qmv.QmvError, match="workspace: holds 100"):
+        qmv.qmv_gemv_multi_ws("q4_k", "f32", 1, [ok], DevTensor(torch.uint8, 100), 256)
+    with pytest.raises(qmv.QmvError, match="not on a GPU"):
+        qmv.qmv_gemv_multi_ws("q4_k", "f32", 1, [ok], torch.zeros(256, dtype=torch.uint8), 256)
