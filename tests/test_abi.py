@@ -260,3 +260,40 @@ def test_create_weights_planes():
     _expect(-3, c, "q4_k", 8, 500, FAKE, n)
     _expect(-5, c, "q4_k", 8, 512, FAKE, n - 16)
     _expect(-4, c, "q4_k", 8, 512, FAKE + 8, n)
+
+
+def test_header_is_plain_c_and_links():
+    """include/qmv.h compiles as C99 with every warning on, and a C program
+    that calls entry points which need no GPU links against libqmv.so and
+    runs: the boundary is a plain C ABI."""
+    import shutil
+    import subprocess
+    import tempfile
+    if shutil.which("gcc") is None:
+        pytest.skip("gcc not available")
+    src = r'''
+#include <stdio.h>
+#include "qmv.h"
+int main(void) {
+  qmv_weights w;
+  uint64_t n = qmv_packed_size(QMV_Q4_K, 8, 512), ws = 1;
+  qmv_gemv_item it;
+  if (n != 8 * 2 * 144) return 1;
+  if (qmv_create_weights(QMV_Q4_K, 8, 512, (const void*)(uintptr_t)0x7F0000000000ull, n, &w) != QMV_OK) return 2;
+  it.W = &w; it.x = (const void*)(uintptr_t)0x7F0000100000ull; it.y = (float*)(uintptr_t)0x7F0000200000ull;
+  if (qmv_workspace_size(QMV_Q4_K, QMV_BF16, 1, &it, 1, &ws) != QMV_OK || ws != 0) return 3;
+  if (qmv_gemv_swiglu(QMV_Q4_K, &w, &w, 0, QMV_F32, it.y, 8, 512, 1, 0) != QMV_ERR_NULL) return 4;
+  printf("%s\n", qmv_status_string(QMV_ERR_SIZE));
+  return 0;
+}
+'''
+    lib = qmv.lib()._name
+    with tempfile.TemporaryDirectory() as d:
+        c = os.path.join(d, "t.c")
+        exe = os.path.join(d, "t")
+        open(c, "w").write(src)
+        subprocess.run(["gcc", "-std=c99", "-Wall", "-Wextra", "-pedantic", "-Werror", "-I", os.path.join(ROOT, "include"),
+                        c, lib, "-Wl,-rpath," + os.path.dirname(lib), "-o", exe], check=True)
+        r = subprocess.run([exe], capture_output=True, text=True)
+        assert r.returncode == 0, (r.returncode, r.stderr)
+        assert r.stdout.strip() != ""
