@@ -199,14 +199,16 @@ PAIR_CASES = [("q8_0", "blocks"), ("q4_k", "blocks"), ("q4_k", "planes"), ("q5_k
 
 
 @pytest.mark.parametrize("x_dtype", ["f32", "f16", "bf16"])
-@pytest.mark.parametrize("rows,eighths", [(1, 8), (67, 3), (4100, 8)])
+@pytest.mark.parametrize("rows,eighths,batch", [(1, 8, 1), (67, 3, 1), (4100, 8, 1), (67, 3, 2), (130, 8, 2),
+                                                (1, 8, 3), (67, 5, 3), (300, 8, 4)])
 @pytest.mark.parametrize("fmt,layout", PAIR_CASES)
-def test_multi_pair_of_one_shape(fmt, layout, rows, eighths, x_dtype):
-    """Two matrices of one shape on one activation row (gate and up) run as
-    one launch whose two-row tiles pair row i of each: every output against
-    the oracle, and against each matrix called alone -- bit for bit where
-    the lone call also runs two-row tiles (every format but INT4, whose lone
-    call runs one-row tiles and so another reduction order)."""
+def test_multi_pair_of_one_shape(fmt, layout, rows, eighths, batch, x_dtype):
+    """Two matrices of one shape on the same activation rows (gate and up):
+    at one row they run as one launch whose two-row tiles pair row i of
+    each; at two or more rows as two items of the multi-row GEMV.  Every
+    output against the oracle, and against each matrix called alone -- bit
+    for bit, except INT4 at one row, whose lone call runs one-row tiles and
+    so another reduction order."""
     qk = oracle.QK[fmt]
     slice_cols = 2048 if fmt == "q8_0" else 4096
     cols = max(qk, slice_cols * eighths // 8 // qk * qk)
@@ -219,24 +221,25 @@ def test_multi_pair_of_one_shape(fmt, layout, rows, eighths, x_dtype):
             d = qmv.qmv_repack_planes(w.desc, buf)
             keep.append(buf)
         descs.append(d)
-    x = gen_x(1, cols, x_dtype, seed=2700 + rows)
+    x = gen_x(batch, cols, x_dtype, seed=2700 + rows)
     xd = to_dev_x(x, x_dtype)
-    off = (rows + 4 + 3) // 4 * 4  # the second output 16-byte aligned, a canary gap between
-    ybuf = torch.full((off + rows + 4,), 7.25, dtype=torch.float32, device=DEV)
-    ys = [ybuf[:rows], ybuf[off:off + rows]]
-    say(f"multi pair {fmt} {layout} {rows}x{cols} x {x_dtype}")
-    qmv.qmv_gemv_multi(fmt, x_dtype, 1, [(d, xd, y) for d, y in zip(descs, ys)])
+    n = batch * rows
+    off = (n + 4 + 3) // 4 * 4  # the second output 16-byte aligned, a canary gap between
+    ybuf = torch.full((off + n + 4,), 7.25, dtype=torch.float32, device=DEV)
+    ys = [ybuf[:n], ybuf[off:off + n]]
+    say(f"multi pair {fmt} {layout} {rows}x{cols} batch {batch} x {x_dtype}")
+    qmv.qmv_gemv_multi(fmt, x_dtype, batch, [(d, xd, y) for d, y in zip(descs, ys)])
     torch.cuda.synchronize()
     host = ybuf.cpu().numpy()
-    assert np.all(host[rows:off] == 7.25) and np.all(host[off + rows:] == 7.25)
+    assert np.all(host[n:off] == 7.25) and np.all(host[off + n:] == 7.25)
     for w, d, y in zip(ws, descs, ys):
-        got = y.cpu().numpy().reshape(1, rows)
+        got = y.cpu().numpy().reshape(batch, rows)
         err = oracle.normwise_rel_err(got, oracle_y(w, x, x_dtype))
         assert np.all(err <= TOL), err
-        alone = torch.empty(1, rows, dtype=torch.float32, device=DEV)
-        qmv.qmv_gemv(fmt, d, xd, x_dtype, alone, rows, cols, 1)
+        alone = torch.empty(batch, rows, dtype=torch.float32, device=DEV)
+        qmv.qmv_gemv(fmt, d, xd, x_dtype, alone, rows, cols, batch)
         alone = alone.cpu().numpy()
-        if fmt == "int4_g128":
+        if fmt == "int4_g128" and batch == 1:
             np.testing.assert_allclose(got, alone, rtol=1e-5, atol=1e-5 * np.abs(alone).max())
         else:
             np.testing.assert_array_equal(got, alone)
